@@ -1,0 +1,217 @@
+/*
+ * pkv.h -- C ABI of libpkv.so: paged KV-cache decode attention for MI355X (gfx950).
+ *
+ * What the library computes is set by four web pages on continuous batching and
+ * PagedAttention, cited below as
+ *   [CB]  "Batching Continuo y PagedAttention" (cruxr.ai)
+ *   [IPX] iplexlaw.co.kr commentary on the vLLM PagedAttention paper (arXiv v1)
+ *   [OS]  "PagedAttention: gestionar la KV cache como memoria de un sistema operativo"
+ *         (josueisai.com)
+ *   [UL]  "Continuous Batching" (Ultralytics glossary)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Pool layout ("paged KV cache"): k_cache and v_cache are each
+ *        [num_blocks][num_kv_heads][block_size][head_dim]
+ *    row-major, elements of `dtype`.  One block holds the keys (values) of
+ *    block_size consecutive tokens of one sequence for every KV head
+ *    ([CB] "PagedAttention: Memoria virtual para la KV cache": fixed-size blocks
+ *    of P tokens, P = 16; [OS] "La idea prestada: paginación").
+ *  - A slot is  block * block_size + offset;  slot -1 means "no token".
+ *  - Block table: int32 [num_seqs][max_blocks_per_seq]; entry i of row s is the
+ *    physical block that holds tokens 16i..16i+15 of sequence s
+ *    ([CB] same section: the per-request page table; [IPX] "Separar orden lógico y
+ *    ubicación física").  Entries past ceil(ctx/16) are never read.
+ *  - Device calls take caller-owned device pointers (e.g. torch tensors) and a
+ *    hipStream_t passed as void* (NULL = the null stream).  They only enqueue
+ *    work: they return as soon as the kernels are launched, never synchronise
+ *    and never allocate device memory.  Host-checkable arguments are validated
+ *    before anything is launched; on error nothing is enqueued.
+ *  - Data that lives on the device (slots, block ids, context lengths) is not
+ *    visible to the host.  Kernels never touch memory outside the buffers
+ *    described by the size arguments: out-of-range slots and block ids are
+ *    skipped, and attention rows they affect are written as NaN (see each call).
+ *  - Supported: block_size 16; head_dim 64 or 128; dtype PKV_F32 or PKV_BF16
+ *    (the same dtype for q, K and V); num_heads a multiple of num_kv_heads.
+ *  - Calls that enqueue work on one stream are ordered by that stream.  For one
+ *    decode step the caller enqueues pkv_copy_blocks, then pkv_append, then the
+ *    attention calls: copies must read shared blocks before this step writes.
+ *  - Errors: every call returns a pkv_status; pkv_last_error() gives the text of
+ *    the last failure on the calling thread.  No C++ exception crosses the ABI.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1,    /* a host-checkable argument is wrong; nothing done     */
+  PKV_ERR_OUT_OF_BLOCKS = 2,  /* the free pool is too small; allocator state unchanged */
+  PKV_ERR_UNSUPPORTED = 3,    /* valid but not built (e.g. head_dim 96)                */
+  PKV_ERR_HIP = 4,            /* a HIP runtime call failed (text in pkv_last_error)    */
+  PKV_ERR_UNKNOWN_SEQ = 5     /* sequence id not live in this allocator                */
+} pkv_status;
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+/* Text of the last non-OK status returned on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* Library version string. */
+const char* pkv_version(void);
+
+/* ------------------------------------------------------------------------
+ * Cache write.  [OS] "Cómo funciona por dentro": each new token's key and value
+ * are written into the last block of its sequence's table; [CB] "PagedAttention:
+ * Memoria virtual para la KV cache": blocks fill token by token.
+ *
+ *   for t in [0, num_tokens), h in [0, num_kv_heads):
+ *     if 0 <= slot_mapping[t] < num_blocks*block_size:
+ *       k_cache[slot/bs][h][slot%bs][:] = k[t][h][:]   (same for v)
+ *
+ * k, v: device [num_tokens][num_kv_heads][head_dim] in the pool dtype (a pure
+ * byte copy: no conversion).  slot_mapping: device int64 [num_tokens].  Slots
+ * outside the pool (including -1) are skipped.  Two tokens with the same slot in
+ * one call race (the allocator never produces that).  num_tokens may be 0.
+ * ------------------------------------------------------------------------ */
+pkv_status pkv_append(void* k_cache, void* v_cache, const void* k, const void* v,
+                      const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      pkv_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Copy-on-write block copy.  [IPX] "Dos respuestas a una entrada": a shared
+ * block that still has room is copied before a writer changes it;
+ * [CB] "PagedAttention: Memoria virtual para la KV cache": copy-on-write sharing
+ * as in Unix fork().
+ *
+ *   for i in [0, num_pairs): k_cache[dst_i] = k_cache[src_i]; v_cache[dst_i] = v_cache[src_i]
+ *
+ * with (src_i, dst_i) = (src_dst[2i], src_dst[2i+1]), device int32, whole blocks
+ * (all heads, all slots).  Destinations must be distinct and not among the
+ * sources (the allocator guarantees it), so every copy reads the pre-call pool.
+ * Pairs with an id outside [0, num_blocks) are skipped.  num_pairs may be 0.
+ * ------------------------------------------------------------------------ */
+pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst,
+                           int32_t num_pairs, int32_t num_blocks, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, pkv_dtype dtype,
+                           void* stream);
+
+/* ------------------------------------------------------------------------
+ * Decode attention.  [OS] "Cómo funciona por dentro": the kernel follows the
+ * block table to each block, scores the query against the block's keys and
+ * forms one softmax-weighted sum of the values; [IPX] "Separar orden lógico y
+ * ubicación física": attention follows the table in logical order; [UL] "Cómo
+ * funciona la planificación a nivel de iteración": attention runs per sequence
+ * because every sequence has its own context length.
+ *
+ *   for s, h:  g = h / (num_heads/num_kv_heads);  n = context_lens[s]
+ *     K_j, V_j = key/value of token j < n of sequence s, KV head g, found at
+ *                block_tables[s][j/16], offset j%16
+ *     out[s][h][:] = sum_j softmax_j(scale * <q[s][h], K_j>) V_j      (0 if n == 0)
+ *
+ * q: device [num_seqs][num_heads][head_dim] in `dtype`; out: device float32
+ * [num_seqs][num_heads][head_dim]; context_lens: device int32 [num_seqs].
+ * Scores, softmax and accumulation are float32.  max_context_len must be >= every
+ * context length (it sizes the context split); a row whose length exceeds it or
+ * max_blocks_per_seq*block_size, or whose table names a block outside
+ * [0, num_blocks), is written as NaN.
+ * workspace: device scratch of at least pkv_attention_workspace_bytes(...) bytes
+ * for the split-context partial results (may be NULL when that size is 0).  The
+ * library only reads/writes it during the call's kernels; no initialisation needed.
+ * ------------------------------------------------------------------------ */
+size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                     int32_t max_context_len);
+
+pkv_status pkv_attention_decode(float* out, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                int32_t max_context_len, float scale, pkv_dtype dtype,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Tokens per context partition of the split-context decode (a multiple of 16 in
+ * [16, 8192]; default 256).  Process-wide; set it before sizing workspaces.
+ * Results do not depend on it beyond float32 rounding. */
+pkv_status pkv_set_decode_partition_tokens(int32_t tokens);
+int32_t pkv_get_decode_partition_tokens(void);
+
+/* ------------------------------------------------------------------------
+ * Host block allocator.  [CB] "PagedAttention: Memoria virtual para la KV
+ * cache" and "Juntándolo todo: Arquitectura de vLLM": a request gets a block when
+ * first scheduled, a new block from the free pool when its last block is full,
+ * and returns all blocks when it finishes; admission needs enough free blocks.
+ * [OS] "Cómo funciona por dentro": the next free block, wherever it is.
+ * [IPX] "Dos respuestas a una entrada": shared prompt blocks with refcounts,
+ * copy-on-write of a shared block that still has room, full shared blocks stay
+ * shared, unreferenced blocks are freed.
+ *
+ * Policy (fixed so that results are reproducible): the free list is FIFO --
+ * blocks are taken from the front, freed blocks are appended at the back in
+ * block-table order; the initial order is `initial_free_order` (a permutation of
+ * [0, num_blocks)) or ascending ids.  Appending to a sequence whose last block is
+ * partially filled and shared (refcount > 1) first moves it to a fresh block and
+ * reports the (old, new) pair, which the caller copies with pkv_copy_blocks
+ * before writing.  Sequence ids are 0, 1, 2, ... in creation order (create and
+ * fork), never reused.  Calls are atomic: on any error the state is unchanged.
+ * Not thread-safe: use one allocator from one thread.
+ * ------------------------------------------------------------------------ */
+typedef struct pkv_allocator pkv_allocator;
+
+pkv_status pkv_allocator_create(int32_t num_blocks, int32_t block_size,
+                                const int32_t* initial_free_order /* host, nullable */,
+                                pkv_allocator** out);
+void pkv_allocator_destroy(pkv_allocator* a);
+int32_t pkv_allocator_num_free(const pkv_allocator* a);
+
+pkv_status pkv_seq_create(pkv_allocator* a, int64_t* seq_id);
+
+/* Reserve slots for n_tokens new tokens of seq.  slots_out: host int64
+ * [n_tokens].  cow_src_dst_out: host int32 [2]; *n_cow_out is 0 or 1. */
+pkv_status pkv_seq_append_slots(pkv_allocator* a, int64_t seq, int32_t n_tokens,
+                                int64_t* slots_out, int32_t* cow_src_dst_out,
+                                int32_t* n_cow_out);
+
+/* Batched form for one scheduler step: appends n_tokens[i] tokens to seqs[i]
+ * for i in [0, count) (distinct sequences), writing all slots consecutively into
+ * slots_out (host int64 [sum n_tokens]) and the copy pairs into cow_src_dst_out
+ * (host int32 [count][2]; *n_cow_out pairs).  All-or-nothing. */
+pkv_status pkv_seq_append_slots_batch(pkv_allocator* a, const int64_t* seqs,
+                                      const int32_t* n_tokens, int32_t count,
+                                      int64_t* slots_out, int32_t* cow_src_dst_out,
+                                      int32_t* n_cow_out);
+
+/* New sequence sharing every block of parent (refcounts + 1). */
+pkv_status pkv_seq_fork(pkv_allocator* a, int64_t parent, int64_t* child);
+
+/* Drop seq; blocks whose refcount reaches 0 return to the back of the free list. */
+pkv_status pkv_seq_free(pkv_allocator* a, int64_t seq);
+
+/* Copy seq's block table (up to cap entries) to out; *n_blocks = table length,
+ * *n_tokens = context length.  Fails if cap < table length. */
+pkv_status pkv_seq_block_table(const pkv_allocator* a, int64_t seq, int32_t* out, int32_t cap,
+                               int32_t* n_blocks, int32_t* n_tokens);
+
+/* Dense tables for a batch: tables_out host int32 [count][max_blocks] (unused
+ * entries 0), context_lens_out host int32 [count]. */
+pkv_status pkv_block_tables(const pkv_allocator* a, const int64_t* seqs, int32_t count,
+                            int32_t max_blocks, int32_t* tables_out, int32_t* context_lens_out);
+
+pkv_status pkv_block_refcount(const pkv_allocator* a, int32_t block, int32_t* rc);
+
+/* Free blocks that appending n_tokens to seq would take (admission check). */
+pkv_status pkv_seq_blocks_needed(const pkv_allocator* a, int64_t seq, int32_t n_tokens,
+                                 int32_t* needed);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,233 @@
+"""ctypes binding of libpkv.so (argument marshalling only).
+
+Every function has the name of the C call it wraps (include/pkv.h).  Device
+buffers are torch tensors on the GPU: the binding passes ``tensor.data_ptr()``,
+shapes read off the tensors, and torch's current HIP stream, and raises
+``PkvError`` for any non-OK status.  All computation happens in the library's
+HIP kernels; if the library is missing, importing this module fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch  # loads torch's HIP runtime first; libpkv.so binds to the same one
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m paged_kv_cache_171_amd.build`")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_OUT_OF_BLOCKS, PKV_ERR_UNSUPPORTED, PKV_ERR_HIP, PKV_ERR_UNKNOWN_SEQ = range(6)
+PKV_F32, PKV_BF16 = 0, 1
+STATUS_NAMES = {0: "PKV_OK", 1: "PKV_ERR_INVALID_ARG", 2: "PKV_ERR_OUT_OF_BLOCKS",
+                3: "PKV_ERR_UNSUPPORTED", 4: "PKV_ERR_HIP", 5: "PKV_ERR_UNKNOWN_SEQ"}
+
+_c_i32, _c_i64, _c_f32, _c_p, _c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+_P_I32 = ctypes.POINTER(ctypes.c_int32)
+_P_I64 = ctypes.POINTER(ctypes.c_int64)
+
+_SIGS = {
+    "pkv_last_error": (ctypes.c_char_p, []),
+    "pkv_version": (ctypes.c_char_p, []),
+    "pkv_append": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_p]),
+    "pkv_copy_blocks": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_p]),
+    "pkv_attention_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32]),
+    "pkv_attention_decode": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32,
+                                      _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_p, _c_sz, _c_p]),
+    "pkv_set_decode_partition_tokens": (_c_i32, [_c_i32]),
+    "pkv_get_decode_partition_tokens": (_c_i32, []),
+    "pkv_allocator_create": (_c_i32, [_c_i32, _c_i32, _c_p, ctypes.POINTER(_c_p)]),
+    "pkv_allocator_destroy": (None, [_c_p]),
+    "pkv_allocator_num_free": (_c_i32, [_c_p]),
+    "pkv_seq_create": (_c_i32, [_c_p, _P_I64]),
+    "pkv_seq_append_slots": (_c_i32, [_c_p, _c_i64, _c_i32, _c_p, _c_p, _P_I32]),
+    "pkv_seq_append_slots_batch": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_p, _c_p, _P_I32]),
+    "pkv_seq_fork": (_c_i32, [_c_p, _c_i64, _P_I64]),
+    "pkv_seq_free": (_c_i32, [_c_p, _c_i64]),
+    "pkv_seq_block_table": (_c_i32, [_c_p, _c_i64, _c_p, _c_i32, _P_I32, _P_I32]),
+    "pkv_block_tables": (_c_i32, [_c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p]),
+    "pkv_block_refcount": (_c_i32, [_c_p, _c_i32, _P_I32]),
+    "pkv_seq_blocks_needed": (_c_i32, [_c_p, _c_i64, _c_i32, _P_I32]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+LIB = _lib
+LIB_PATH = _LIB_PATH
+EXPORTED = tuple(_SIGS)
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+def _check(st: int) -> None:
+    if st != PKV_OK:
+        raise PkvError(st, _lib.pkv_last_error().decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return PKV_F32
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError("expected contiguous GPU tensors")
+
+
+def pkv_version() -> str:
+    return _lib.pkv_version().decode()
+
+
+def pkv_append(k_cache: torch.Tensor, v_cache: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+               slot_mapping: torch.Tensor, stream=None) -> None:
+    """k_cache/v_cache [NB, Hkv, 16, d]; k/v [T, Hkv, d] (pool dtype); slot_mapping int64 [T]."""
+    _dev(k_cache, v_cache, k, v, slot_mapping)
+    assert slot_mapping.dtype == torch.int64 and k.dtype == k_cache.dtype == v.dtype == v_cache.dtype
+    nb, hkv, bs, d = k_cache.shape
+    _check(_lib.pkv_append(k_cache.data_ptr(), v_cache.data_ptr(), k.data_ptr(), v.data_ptr(),
+                           slot_mapping.data_ptr(), k.shape[0], nb, hkv, d, bs,
+                           _dtype_code(k_cache), _stream(stream)))
+
+
+def pkv_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src_dst: torch.Tensor, stream=None) -> None:
+    """src_dst: int32 [n, 2] on the GPU."""
+    _dev(k_cache, v_cache, src_dst)
+    assert src_dst.dtype == torch.int32
+    nb, hkv, bs, d = k_cache.shape
+    _check(_lib.pkv_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), src_dst.data_ptr(),
+                                src_dst.shape[0] if src_dst.dim() == 2 else src_dst.numel() // 2,
+                                nb, hkv, d, bs, _dtype_code(k_cache), _stream(stream)))
+
+
+def pkv_attention_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int) -> int:
+    return int(_lib.pkv_attention_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len))
+
+
+def pkv_set_decode_partition_tokens(tokens: int) -> None:
+    _check(_lib.pkv_set_decode_partition_tokens(tokens))
+
+
+def pkv_get_decode_partition_tokens() -> int:
+    return int(_lib.pkv_get_decode_partition_tokens())
+
+
+def workspace_for(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
+                  device="cuda") -> torch.Tensor:
+    """A device buffer big enough for pkv_attention_decode's split-context partials."""
+    n = pkv_attention_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def pkv_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                         scale: float, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """out fp32 [S, Hq, d]; q [S, Hq, d]; block_tables int32 [S, MB]; context_lens int32 [S]."""
+    _dev(out, q, k_cache, v_cache, block_tables, context_lens)
+    assert out.dtype == torch.float32 and block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+    S, hq, d = q.shape
+    nb, hkv, bs, _ = k_cache.shape
+    if workspace is None:
+        workspace = workspace_for(S, hq, d, max_context_len, device=q.device)
+    _check(_lib.pkv_attention_decode(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                     block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
+                                     S, hq, hkv, d, bs, nb, int(max_context_len), float(scale),
+                                     _dtype_code(k_cache), workspace.data_ptr(), workspace.numel(),
+                                     _stream(stream)))
+
+
+class BlockAllocator:
+    """Host block allocator (pkv_allocator_* / pkv_seq_* calls)."""
+
+    def __init__(self, num_blocks: int, block_size: int = 16, initial_free_order: Optional[Sequence[int]] = None):
+        h = _c_p()
+        order = None
+        if initial_free_order is not None:
+            order = np.ascontiguousarray(np.asarray(initial_free_order, dtype=np.int32))
+        _check(_lib.pkv_allocator_create(num_blocks, block_size,
+                                         order.ctypes.data if order is not None else None, ctypes.byref(h)))
+        self._h = h
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            _lib.pkv_allocator_destroy(h)
+            self._h = None
+
+    @property
+    def num_free(self) -> int:
+        return int(_lib.pkv_allocator_num_free(self._h))
+
+    def seq_create(self) -> int:
+        sid = _c_i64()
+        _check(_lib.pkv_seq_create(self._h, ctypes.byref(sid)))
+        return sid.value
+
+    def seq_append_slots(self, seq: int, n: int) -> Tuple[np.ndarray, List[Tuple[int, int]]]:
+        slots = np.empty(max(n, 1), dtype=np.int64)
+        cow = np.zeros(2, dtype=np.int32)
+        ncow = _c_i32()
+        _check(_lib.pkv_seq_append_slots(self._h, seq, n, slots.ctypes.data, cow.ctypes.data, ctypes.byref(ncow)))
+        return slots[:n], [(int(cow[0]), int(cow[1]))] if ncow.value else []
+
+    def seq_append_slots_batch(self, seqs: Sequence[int], n_tokens: Sequence[int]):
+        seqs_a = np.ascontiguousarray(seqs, dtype=np.int64)
+        n_a = np.ascontiguousarray(n_tokens, dtype=np.int32)
+        slots = np.empty(max(int(n_a.sum()), 1), dtype=np.int64)
+        cow = np.zeros((max(len(seqs_a), 1), 2), dtype=np.int32)
+        ncow = _c_i32()
+        _check(_lib.pkv_seq_append_slots_batch(self._h, seqs_a.ctypes.data, n_a.ctypes.data, len(seqs_a),
+                                               slots.ctypes.data, cow.ctypes.data, ctypes.byref(ncow)))
+        return slots[:int(n_a.sum())], cow[:ncow.value]
+
+    def seq_fork(self, parent: int) -> int:
+        c = _c_i64()
+        _check(_lib.pkv_seq_fork(self._h, parent, ctypes.byref(c)))
+        return c.value
+
+    def seq_free(self, seq: int) -> None:
+        _check(_lib.pkv_seq_free(self._h, seq))
+
+    def seq_block_table(self, seq: int, cap: int = 1 << 20) -> Tuple[List[int], int]:
+        out = np.empty(cap, dtype=np.int32)
+        nb, nt = _c_i32(), _c_i32()
+        _check(_lib.pkv_seq_block_table(self._h, seq, out.ctypes.data, cap, ctypes.byref(nb), ctypes.byref(nt)))
+        return [int(x) for x in out[:nb.value]], nt.value
+
+    def block_tables(self, seqs: Sequence[int], max_blocks: int) -> Tuple[np.ndarray, np.ndarray]:
+        seqs_a = np.ascontiguousarray(seqs, dtype=np.int64)
+        tables = np.empty((len(seqs_a), max_blocks), dtype=np.int32)
+        lens = np.empty(len(seqs_a), dtype=np.int32)
+        _check(_lib.pkv_block_tables(self._h, seqs_a.ctypes.data, len(seqs_a), max_blocks,
+                                     tables.ctypes.data, lens.ctypes.data))
+        return tables, lens
+
+    def block_refcount(self, block: int) -> int:
+        rc = _c_i32()
+        _check(_lib.pkv_block_refcount(self._h, block, ctypes.byref(rc)))
+        return rc.value
+
+    def seq_blocks_needed(self, seq: int, n: int) -> int:
+        r = _c_i32()
+        _check(_lib.pkv_seq_blocks_needed(self._h, seq, n, ctypes.byref(r)))
+        return r.value

@@ -1,0 +1,42 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/pkv.h"
+
+// Record `msg` as this thread's last error and return `st`.
+pkv_status pkv_fail(pkv_status st, const char* msg);
+pkv_status pkv_failf(pkv_status st, const char* fmt, ...);
+
+// Kernel launchers (pkv_kernels.hip).  Arguments are already validated; each
+// returns hipSuccess or the launch error as an int.
+int pkv_launch_append(void* k_cache, void* v_cache, const void* k, const void* v,
+                      const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                      int32_t num_kv_heads, int32_t row_bytes, void* stream);
+int pkv_launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst, int32_t num_pairs,
+                           int32_t num_blocks, int64_t block_bytes, void* stream);
+
+struct pkv_decode_args {
+  float* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* part_ml;      // [S][Hq][NP][2]  (running max in log2 units, sum)
+  float* part_acc;     // [S][Hq][NP][d]
+  int32_t max_blocks_per_seq;
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t num_blocks;
+  int32_t max_context_len;
+  int32_t partition_tokens;
+  int32_t num_partitions;  // NP = ceil(max_context_len / partition_tokens)
+  float scale_log2;        // scale * log2(e)
+  int dtype;               // pkv_dtype
+};
+int pkv_launch_decode(const pkv_decode_args& a, void* stream);

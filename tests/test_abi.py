@@ -1,0 +1,123 @@
+"""The C ABI library loads, exports every declared call, and rejects bad
+host-checkable arguments before launching anything (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def P():
+    import paged_kv_cache_171_amd as P
+    return P
+
+
+def test_every_declared_call_is_exported(P):
+    names = _declared()
+    assert len(names) >= 20
+    lib = ctypes.CDLL(P.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    # and the binding wraps each of them
+    assert set(names) <= set(P.EXPORTED), set(names) - set(P.EXPORTED)
+
+
+def test_version_and_empty_error(P):
+    assert "gfx950" in P.pkv_version()
+
+
+def _lib(P):
+    return P.binding.LIB
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), 3), (dict(block_size=32), 3), (dict(num_kv_heads=0), 1),
+    (dict(dtype=7), 1), (dict(num_tokens=-1), 1), (dict(num_blocks=0), 1),
+    (dict(k=None), 1),
+])
+def test_append_rejects_bad_arguments(P, kw, code):
+    args = dict(k_cache=16, v_cache=32, k=48, v=64, slot=80, num_tokens=4, num_blocks=8,
+                num_kv_heads=2, head_dim=64, block_size=16, dtype=1)
+    args.update(kw)
+    st = _lib(P).pkv_append(args["k_cache"], args["v_cache"], args["k"], args["v"], args["slot"],
+                            args["num_tokens"], args["num_blocks"], args["num_kv_heads"], args["head_dim"],
+                            args["block_size"], args["dtype"], None)
+    assert st == code
+    assert _lib(P).pkv_last_error().decode().startswith("pkv_append")
+
+
+def test_append_with_no_tokens_is_a_no_op(P):
+    assert _lib(P).pkv_append(None, None, None, None, None, 0, 8, 2, 64, 16, 1, None) == 0
+
+
+def test_misaligned_pointer_is_rejected(P):
+    st = _lib(P).pkv_append(17, 32, 48, 64, 80, 4, 8, 2, 64, 16, 1, None)
+    assert st == P.PKV_ERR_INVALID_ARG and "aligned" in _lib(P).pkv_last_error().decode()
+
+
+def test_copy_blocks_rejects_bad_arguments(P):
+    L = _lib(P)
+    assert L.pkv_copy_blocks(16, 32, 48, -1, 8, 2, 64, 16, 1, None) == P.PKV_ERR_INVALID_ARG
+    assert L.pkv_copy_blocks(16, 32, None, 3, 8, 2, 64, 16, 1, None) == P.PKV_ERR_INVALID_ARG
+    assert L.pkv_copy_blocks(None, None, None, 0, 8, 2, 64, 16, 1, None) == P.PKV_OK
+
+
+def _decode(P, **kw):
+    a = dict(out=256, q=512, k=768, v=1024, tables=1280, mb=4, lens=1536, S=2, Hq=4, Hkv=2, d=64, bs=16,
+             nb=8, maxctx=64, scale=0.125, dtype=1, ws=None, wsb=0)
+    a.update(kw)
+    return _lib(P).pkv_attention_decode(a["out"], a["q"], a["k"], a["v"], a["tables"], a["mb"], a["lens"],
+                                        a["S"], a["Hq"], a["Hkv"], a["d"], a["bs"], a["nb"], a["maxctx"],
+                                        a["scale"], a["dtype"], a["ws"], a["wsb"], None)
+
+
+def test_decode_rejects_bad_arguments(P):
+    assert _decode(P, Hq=5) == P.PKV_ERR_INVALID_ARG            # not a multiple of Hkv
+    assert _decode(P, d=80) == P.PKV_ERR_UNSUPPORTED
+    assert _decode(P, scale=float("nan")) == P.PKV_ERR_INVALID_ARG
+    assert _decode(P, mb=0) == P.PKV_ERR_INVALID_ARG
+    assert _decode(P, q=None) == P.PKV_ERR_INVALID_ARG
+    assert _decode(P, S=0, q=None) == P.PKV_OK                  # nothing to do
+    # a long context needs a split-context workspace
+    need = P.pkv_attention_workspace_bytes(2, 4, 64, 5000)
+    assert need > 0
+    assert _decode(P, maxctx=5000, mb=400) == P.PKV_ERR_INVALID_ARG
+    assert "workspace" in _lib(P).pkv_last_error().decode()
+
+
+def test_workspace_size_follows_partition_tokens(P):
+    old = P.pkv_get_decode_partition_tokens()
+    try:
+        P.pkv_set_decode_partition_tokens(64)
+        assert P.pkv_attention_workspace_bytes(3, 4, 128, 64) == 0          # one partition
+        n = P.pkv_attention_workspace_bytes(3, 4, 128, 65)                  # two partitions
+        assert n >= 3 * 4 * 2 * (128 + 2) * 4
+        with pytest.raises(P.PkvError):
+            P.pkv_set_decode_partition_tokens(40)
+    finally:
+        P.pkv_set_decode_partition_tokens(old)
+
+
+def test_allocator_errors_are_status_codes(P):
+    with pytest.raises(P.PkvError) as e:
+        P.BlockAllocator(4, 16, [0, 1, 1, 2])
+    assert e.value.status == P.PKV_ERR_INVALID_ARG
+    a = P.BlockAllocator(2, 16)
+    s = a.seq_create()
+    with pytest.raises(P.PkvError) as e:
+        a.seq_append_slots(s, 33)
+    assert e.value.status == P.PKV_ERR_OUT_OF_BLOCKS
+    assert a.num_free == 2
+    with pytest.raises(P.PkvError) as e:
+        a.seq_free(99)
+    assert e.value.status == P.PKV_ERR_UNKNOWN_SEQ

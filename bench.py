@@ -1,0 +1,263 @@
+"""Benchmark: one decode step of the 13B-shaped batch through libpkv on one GPU.
+
+A step is one pass of the hot path over the batch: the host allocator reserves
+one new slot per sequence (and names any copy-on-write pairs), the slot map,
+block tables and context lengths go to the device, and then for each of the 40
+layers the new token's K/V is written into that layer's paged pool
+(pkv_append) and paged decode attention runs over it (pkv_attention_decode).
+
+Workload: 64 sequences, 40 MHA heads, head_dim 128, bf16, context lengths
+lognormal (median 200, sigma 1.0) clipped to [1, 2048], 16-token blocks shuffled
+over a pool of 1.2x the blocks needed, one pool per layer (40 pools, ~21 GB, far
+larger than the 256 MB last-level cache).  Pool contents, queries and new K/V
+are synthetic N(0, 1) bf16 drawn on the device; the inputs are resident in HBM
+before the timed region starts.
+
+Prints one JSON line: decode tokens/s (value), effective KV GB/s and the
+fraction of the 8 TB/s HBM peak, a roofline object for the decode kernel, and
+the CPU oracle's rate on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "paged decode attention: KV GB/s and % of HBM peak; decode tokens/s per step"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_13b_counters.md")
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_171_amd", "csrc", "pkv_kernels.hip")
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per decode launch from the committed counter summary, if it was
+    taken on the current kernel source (else None)."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    text = open(COUNTERS_FILE).read()
+    h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not h or not t or h.group(1) != kernel_source_hash():
+        return None
+    return float(t.group(1))
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=40)
+    ap.add_argument("--seed", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time for the oracle sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(seed: int, target_s: float):
+    """The oracle (float64 numpy, one BLAS thread) on a bounded sample: the same
+    64-sequence batch, one layer at a time, repeated until ~target_s seconds."""
+    from threadpoolctl import threadpool_limits
+    import pkv_workloads as W
+    from oracle import pkv_oracle as O
+
+    w = W.shaped_13b(seed=seed)
+    r = O.replay(w.ops, w.k_rows, w.v_rows, w.num_blocks, w.num_kv_heads, w.head_dim, w.initial_free_order)
+    tables = [r.alloc.block_table(s) for s in w.decode_seqs]
+    lens = [r.alloc.num_tokens(s) for s in w.decode_seqs]
+    layers = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            O.decode_attention(w.q, r.k_pool, r.v_pool, tables, lens, w.scale)
+            layers += 1
+            el = time.perf_counter() - t0
+            if el >= target_s or layers >= 40:
+                break
+    per_layer = el / layers
+    tok_s = len(lens) / (per_layer * 40)
+    return {"value": tok_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{layers} of the 40 layers of one decode step (64 seqs, {sum(lens)} cached tokens, "
+                      f"40 heads x 128, bf16 inputs, float64 math), {el:.1f} s; scaled to a 40-layer step"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_171_amd as PK
+    from paged_kv_cache_171_amd import binding as B
+    import pkv_workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L, S, H, D, P = args.layers, 64, 40, 128, 16
+
+    lens0 = W.shaped_13b_lengths(seed=args.seed, num_seqs=S)
+    total_steps = args.warmup + args.steps
+    need = sum(-(-int(c) // P) for c in lens0)
+    NB = int(math.ceil(1.2 * need))
+    perm = np.random.default_rng(args.seed + 1000).permutation(NB).astype(np.int32)
+    MB = -(-(int(lens0.max()) + total_steps) // P)
+
+    # host allocator with the prompt tokens of every sequence already cached
+    alloc = PK.BlockAllocator(NB, P, perm)
+    seqs = [alloc.seq_create() for _ in range(S)]
+    for s, c in zip(seqs, lens0):
+        alloc.seq_append_slots(s, int(c) - 1)
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+    k_pools = [randn(NB, H, P, D) for _ in range(L)]
+    v_pools = [randn(NB, H, P, D) for _ in range(L)]
+    q = [randn(S, H, D) for _ in range(L)]
+    k_new = [randn(S, H, D) for _ in range(L)]
+    v_new = [randn(S, H, D) for _ in range(L)]
+    out = [torch.empty(S, H, D, dtype=torch.float32, device=dev) for _ in range(L)]
+    max_ctx_cap = int(lens0.max()) + total_steps
+    ws_bytes = PK.pkv_attention_workspace_bytes(S, H, D, max_ctx_cap)
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    plan_bytes = PK.pkv_decode_plan_bytes(S, max_ctx_cap)
+    plan = torch.zeros(max(plan_bytes, 256), dtype=torch.uint8, device=dev)
+    tables_h = torch.zeros(S, MB, dtype=torch.int32).pin_memory()
+    lens_h = torch.zeros(S, dtype=torch.int32).pin_memory()
+    slots_h = torch.zeros(S, dtype=torch.int64).pin_memory()
+    tables_d = torch.zeros(S, MB, dtype=torch.int32, device=dev)
+    lens_d = torch.zeros(S, dtype=torch.int32, device=dev)
+    slots_d = torch.zeros(S, dtype=torch.int64, device=dev)
+    pairs_d = torch.zeros(S, 2, dtype=torch.int32, device=dev)
+    pairs_h = torch.zeros(S, 2, dtype=torch.int32).pin_memory()
+    scale = 1.0 / math.sqrt(D)
+    torch.cuda.synchronize()
+
+    lib = B.LIB
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    ones = np.ones(S, dtype=np.int32)
+    kp = [(k_pools[l].data_ptr(), v_pools[l].data_ptr()) for l in range(L)]
+    kvn = [(k_new[l].data_ptr(), v_new[l].data_ptr()) for l in range(L)]
+    qp = [q[l].data_ptr() for l in range(L)]
+    op = [out[l].data_ptr() for l in range(L)]
+    BF16 = PK.PKV_BF16
+
+    def step(events=None):
+        # (a1) host: reserve one slot per sequence, refresh the tables
+        slots, pairs = alloc.seq_append_slots_batch(seqs, ones)
+        t, ln = alloc.block_tables(seqs, MB)
+        slots_h.numpy()[:] = slots
+        tables_h.numpy()[:] = t
+        lens_h.numpy()[:] = ln
+        slots_d.copy_(slots_h, non_blocking=True)
+        tables_d.copy_(tables_h, non_blocking=True)
+        lens_d.copy_(lens_h, non_blocking=True)
+        max_ctx = int(ln.max())
+        # the decode plan depends only on this step's lengths: built once, used by every layer
+        B._check(lib.pkv_decode_plan(plan.data_ptr(), plan.numel(), lens_d.data_ptr(), S, MB, max_ctx, sp))
+        n_pairs = len(pairs)
+        if n_pairs:
+            pairs_h.numpy()[:n_pairs] = pairs
+            pairs_d.copy_(pairs_h, non_blocking=True)
+        for l in range(L):
+            if n_pairs:   # (a2) copy-on-write (none arise in this workload)
+                B._check(lib.pkv_copy_blocks(kp[l][0], kp[l][1], pairs_d.data_ptr(), n_pairs, NB, H, D, P, BF16, sp))
+            # (a3) write this step's K/V
+            B._check(lib.pkv_append(kp[l][0], kp[l][1], kvn[l][0], kvn[l][1], slots_d.data_ptr(), S, NB, H, D, P,
+                                    BF16, sp))
+            # (a4, a5) paged decode attention and the partition merge
+            if events is not None:
+                events[l][0].record(stream)
+            B._check(lib.pkv_attention_decode_planned(op[l], qp[l], kp[l][0], kp[l][1], tables_d.data_ptr(), MB,
+                                                      lens_d.data_ptr(), S, H, H, D, P, NB, max_ctx, scale, BF16,
+                                                      plan.data_ptr(), plan.numel(), ws.data_ptr(), ws.numel(),
+                                                      sp))
+            if events is not None:
+                events[l][1].record(stream)
+        return ln
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(L)]
+          for _ in range(args.steps)]
+    step_lens = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step_lens.append(step(ev[k]))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # algorithmic bytes of one decode launch: K and V of every live token once,
+    # plus q, the fp32 output, the table entries in use and the lengths
+    kv_bytes = [int(ln.sum()) * 2 * H * D * 2 for ln in step_lens]
+    other = [S * H * D * 2 + S * H * D * 4 + int(sum(-(-int(c) // P) for c in ln)) * 4 + S * 4 for ln in step_lens]
+    dec_ms = [sum(ev[k][l][0].elapsed_time(ev[k][l][1]) for l in range(L)) for k in range(args.steps)]
+    launches = args.steps * L
+    alg_bytes_total = sum((kv + o) * L for kv, o in zip(kv_bytes, other))
+    dec_s_total = sum(dec_ms) / 1e3
+    achieved = alg_bytes_total / dec_s_total / 1e9
+    avg_launch_us = dec_s_total / launches * 1e6
+    step_s = ms_per_step / 1e3
+    kv_gbps = (sum(kv_bytes) / args.steps) * L / step_s / 1e9
+
+    traffic = stored_traffic()
+    res = {
+        "metric": METRIC,
+        "value": round(S / step_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "13b-shaped decode step: 64 seqs, 40 MHA heads x head_dim 128, bf16 K/V/q, "
+                        "lognormal ctx (median 200, sigma 1) clipped [1,2048], block 16, pool 1.2x shuffled, "
+                        f"{L} layer pools",
+            "global_batch": S, "layers": L, "mean_ctx": round(float(np.mean([ln.mean() for ln in step_lens])), 1),
+            "partition_tokens": 512, "parallelism": "none (1 GPU)"},
+        "kv_gbps_step": round(kv_gbps, 1),
+        "hbm_peak_frac_step": round(kv_gbps / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "kernel": "decode_valu_kernel<bf16,128> + merge_partitions_kernel<128>",
+                     "avg_launch_us": round(avg_launch_us, 2),
+                     "alg_bytes_per_launch": round(alg_bytes_total / launches)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

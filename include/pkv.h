@@ -123,8 +123,10 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst,
  * max_blocks_per_seq*block_size, or whose table names a block outside
  * [0, num_blocks), is written as NaN.
  * workspace: device scratch of at least pkv_attention_workspace_bytes(...) bytes
- * for the split-context partial results (may be NULL when that size is 0).  The
- * library only reads/writes it during the call's kernels; no initialisation needed.
+ * for the decode plan and the partial results of contexts longer than one
+ * 512-token partition.  No
+ * initialisation is needed; its contents are meaningless between calls.  Calls
+ * that share one workspace must not overlap in time (e.g. run them on one stream).
  * ------------------------------------------------------------------------ */
 size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                      int32_t max_context_len);
@@ -137,11 +139,35 @@ pkv_status pkv_attention_decode(float* out, const void* q, const void* k_cache,
                                 int32_t max_context_len, float scale, pkv_dtype dtype,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
-/* Tokens per context partition of the split-context decode (a multiple of 16 in
- * [16, 8192]; default 256).  Process-wide; set it before sizing workspaces.
- * Results do not depend on it beyond float32 rounding. */
-pkv_status pkv_set_decode_partition_tokens(int32_t tokens);
-int32_t pkv_get_decode_partition_tokens(void);
+/* ------------------------------------------------------------------------
+ * Decode plan.  Decode work is cut into units (sequence, 512-token partition);
+ * the plan lists them longest first for the decode kernel's dispatch order.  It
+ * depends only on the context lengths and sizes, so a caller may build it once
+ * per step and reuse it for every layer (pkv_attention_decode_planned);
+ * pkv_attention_decode builds it in its workspace on every call.
+ *
+ * plan: device buffer of at least pkv_decode_plan_bytes(num_seqs,
+ * max_context_len) bytes, 16-byte aligned.  Rows with a context length of 0
+ * or an invalid one (see pkv_attention_decode) get no unit.  A plan records
+ * num_seqs, max_context_len and max_blocks_per_seq; a decode call with other
+ * values writes NaN rows instead of using it.
+ * ------------------------------------------------------------------------ */
+size_t pkv_decode_plan_bytes(int32_t num_seqs, int32_t max_context_len);
+
+pkv_status pkv_decode_plan(void* plan, size_t plan_bytes, const int32_t* context_lens, int32_t num_seqs,
+                           int32_t max_blocks_per_seq, int32_t max_context_len, void* stream);
+
+/* pkv_attention_decode with a plan built by pkv_decode_plan from the same
+ * context_lens, num_seqs, max_blocks_per_seq and max_context_len (and not
+ * changed since).  Same arguments and results otherwise; the workspace of
+ * pkv_attention_workspace_bytes(...) is enough. */
+pkv_status pkv_attention_decode_planned(float* out, const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                        int32_t num_blocks, int32_t max_context_len, float scale,
+                                        pkv_dtype dtype, const void* plan, size_t plan_bytes,
+                                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Host block allocator.  [CB] "PagedAttention: Memoria virtual para la KV

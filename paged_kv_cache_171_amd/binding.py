@@ -37,8 +37,11 @@ _SIGS = {
     "pkv_attention_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32]),
     "pkv_attention_decode": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32,
                                       _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_p, _c_sz, _c_p]),
-    "pkv_set_decode_partition_tokens": (_c_i32, [_c_i32]),
-    "pkv_get_decode_partition_tokens": (_c_i32, []),
+    "pkv_decode_plan_bytes": (_c_sz, [_c_i32, _c_i32]),
+    "pkv_decode_plan": (_c_i32, [_c_p, _c_sz, _c_p, _c_i32, _c_i32, _c_i32, _c_p]),
+    "pkv_attention_decode_planned": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32,
+                                              _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_p, _c_sz, _c_p,
+                                              _c_sz, _c_p]),
     "pkv_allocator_create": (_c_i32, [_c_i32, _c_i32, _c_p, ctypes.POINTER(_c_p)]),
     "pkv_allocator_destroy": (None, [_c_p]),
     "pkv_allocator_num_free": (_c_i32, [_c_p]),
@@ -122,12 +125,24 @@ def pkv_attention_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, 
     return int(_lib.pkv_attention_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len))
 
 
-def pkv_set_decode_partition_tokens(tokens: int) -> None:
-    _check(_lib.pkv_set_decode_partition_tokens(tokens))
+def pkv_decode_plan_bytes(num_seqs: int, max_context_len: int) -> int:
+    return int(_lib.pkv_decode_plan_bytes(num_seqs, max_context_len))
 
 
-def pkv_get_decode_partition_tokens() -> int:
-    return int(_lib.pkv_get_decode_partition_tokens())
+def pkv_decode_plan(plan: torch.Tensor, context_lens: torch.Tensor, max_blocks_per_seq: int,
+                    max_context_len: int, stream=None) -> None:
+    """plan: device uint8 buffer; context_lens: int32 [S] on the GPU."""
+    _dev(plan, context_lens)
+    _check(_lib.pkv_decode_plan(plan.data_ptr(), plan.numel() * plan.element_size(), context_lens.data_ptr(),
+                                context_lens.numel(), max_blocks_per_seq, int(max_context_len), _stream(stream)))
+
+
+def plan_for(context_lens: torch.Tensor, max_blocks_per_seq: int, max_context_len: int) -> torch.Tensor:
+    """A device plan for these lengths (pkv_decode_plan into a fresh buffer)."""
+    n = pkv_decode_plan_bytes(context_lens.numel(), max_context_len)
+    plan = torch.empty(max(n, 16), dtype=torch.uint8, device=context_lens.device)
+    pkv_decode_plan(plan, context_lens, max_blocks_per_seq, max_context_len)
+    return plan
 
 
 def workspace_for(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
@@ -139,19 +154,25 @@ def workspace_for(num_seqs: int, num_heads: int, head_dim: int, max_context_len:
 
 def pkv_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                          block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
-                         scale: float, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
-    """out fp32 [S, Hq, d]; q [S, Hq, d]; block_tables int32 [S, MB]; context_lens int32 [S]."""
+                         scale: float, workspace: Optional[torch.Tensor] = None, stream=None,
+                         plan: Optional[torch.Tensor] = None) -> None:
+    """out fp32 [S, Hq, d]; q [S, Hq, d]; block_tables int32 [S, MB]; context_lens int32 [S].
+    With ``plan`` (from pkv_decode_plan / plan_for) this calls pkv_attention_decode_planned."""
     _dev(out, q, k_cache, v_cache, block_tables, context_lens)
     assert out.dtype == torch.float32 and block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
     S, hq, d = q.shape
     nb, hkv, bs, _ = k_cache.shape
     if workspace is None:
         workspace = workspace_for(S, hq, d, max_context_len, device=q.device)
-    _check(_lib.pkv_attention_decode(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                                     block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
-                                     S, hq, hkv, d, bs, nb, int(max_context_len), float(scale),
-                                     _dtype_code(k_cache), workspace.data_ptr(), workspace.numel(),
-                                     _stream(stream)))
+    args = (out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+            block_tables.shape[1], context_lens.data_ptr(), S, hq, hkv, d, bs, nb, int(max_context_len),
+            float(scale), _dtype_code(k_cache))
+    if plan is None:
+        _check(_lib.pkv_attention_decode(*args, workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    else:
+        _dev(plan)
+        _check(_lib.pkv_attention_decode_planned(*args, plan.data_ptr(), plan.numel(), workspace.data_ptr(),
+                                                 workspace.numel(), _stream(stream)))
 
 
 class BlockAllocator:

@@ -12,7 +12,6 @@
 
 namespace {
 thread_local std::string g_last_error;
-int32_t g_partition_tokens = 256;
 
 constexpr int kBlock = 16;
 
@@ -36,13 +35,23 @@ pkv_status hip_status(const char* fn, int err) {
                    hipGetErrorString(static_cast<hipError_t>(err)));
 }
 
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
 int32_t num_partitions(int32_t max_context_len) {
-  const int32_t pt = g_partition_tokens;
-  const int32_t np = (max_context_len + pt - 1) / pt;
+  const int32_t np = (max_context_len + kPartTokens - 1) / kPartTokens;
   return np < 1 ? 1 : np;
 }
 
-size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+size_t plan_bytes(int32_t num_seqs, int32_t max_context_len) {
+  return (4 + 2 * static_cast<size_t>(num_seqs) * num_partitions(max_context_len)) * sizeof(int32_t);
+}
+
+size_t partial_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len) {
+  const int32_t np = num_partitions(max_context_len);
+  if (np <= 1) return 0;
+  const size_t units = static_cast<size_t>(num_seqs) * num_heads * np;
+  return align256(units * 2 * sizeof(float)) + units * head_dim * sizeof(float);
+}
 }  // namespace
 
 pkv_status pkv_fail(pkv_status st, const char* msg) {
@@ -103,33 +112,42 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst,
                                                block_bytes, stream));
 }
 
-pkv_status pkv_set_decode_partition_tokens(int32_t tokens) {
-  if (tokens < kBlock || tokens > 8192 || tokens % kBlock != 0)
-    return pkv_failf(PKV_ERR_INVALID_ARG,
-                     "pkv_set_decode_partition_tokens: %d is not a multiple of 16 in [16, 8192]", tokens);
-  g_partition_tokens = tokens;
-  return PKV_OK;
+size_t pkv_decode_plan_bytes(int32_t num_seqs, int32_t max_context_len) {
+  if (num_seqs <= 0 || max_context_len < 0) return 0;
+  return plan_bytes(num_seqs, max_context_len);
 }
 
-int32_t pkv_get_decode_partition_tokens(void) { return g_partition_tokens; }
+pkv_status pkv_decode_plan(void* plan, size_t plan_bytes_given, const int32_t* context_lens, int32_t num_seqs,
+                           int32_t max_blocks_per_seq, int32_t max_context_len, void* stream) {
+  const char* fn = "pkv_decode_plan";
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0)
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  if (num_seqs == 0) return PKV_OK;
+  if (!plan || !context_lens) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (reinterpret_cast<uintptr_t>(plan) & 15u) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: plan must be 16-byte aligned", fn);
+  if (static_cast<int64_t>(num_seqs) * num_partitions(max_context_len) > 0x3FFFFFFF)
+    return pkv_failf(PKV_ERR_UNSUPPORTED, "%s: too many work units", fn);
+  if (plan_bytes_given < plan_bytes(num_seqs, max_context_len))
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: plan buffer of %zu bytes is smaller than the %zu needed", fn,
+                     plan_bytes_given, plan_bytes(num_seqs, max_context_len));
+  return hip_status(fn, pkv_launch_plan(static_cast<int32_t*>(plan), context_lens, num_seqs, max_blocks_per_seq,
+                                        max_context_len, stream));
+}
 
 size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                      int32_t max_context_len) {
-  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
-  const int32_t np = num_partitions(max_context_len);
-  if (np <= 1) return 0;
-  const size_t units = static_cast<size_t>(num_seqs) * num_heads * np;
-  return align256(units * 2 * sizeof(float)) + units * head_dim * sizeof(float);
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
+  return align256(plan_bytes(num_seqs, max_context_len)) +
+         partial_bytes(num_seqs, num_heads, head_dim, max_context_len);
 }
 
-pkv_status pkv_attention_decode(float* out, const void* q, const void* k_cache,
-                                const void* v_cache, const int32_t* block_tables,
-                                int32_t max_blocks_per_seq, const int32_t* context_lens,
-                                int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                                int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                                int32_t max_context_len, float scale, pkv_dtype dtype,
-                                void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "pkv_attention_decode";
+static pkv_status decode_impl(const char* fn, float* out, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              int32_t max_context_len, float scale, pkv_dtype dtype, const void* plan,
+                              size_t plan_bytes_given, void* workspace, size_t workspace_bytes,
+                              bool build_plan, void* stream) {
   pkv_status st = check_common(fn, num_kv_heads, head_dim, block_size, dtype);
   if (st != PKV_OK) return st;
   if (num_seqs < 0) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: num_seqs < 0", fn);
@@ -145,16 +163,31 @@ pkv_status pkv_attention_decode(float* out, const void* q, const void* k_cache,
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: NULL pointer", fn);
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: out, q and cache pointers must be 16-byte aligned", fn);
-  const size_t need = pkv_attention_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len);
+  const int32_t np = num_partitions(max_context_len);
+  const int64_t grid = static_cast<int64_t>(num_seqs) * num_heads * np;
+  if (grid > 0x7FFFFFFF || static_cast<int64_t>(num_seqs) * np > 0x3FFFFFFF)
+    return pkv_failf(PKV_ERR_UNSUPPORTED, "%s: launch grid too large", fn);
+  const size_t pb = plan_bytes(num_seqs, max_context_len);
+  const size_t part = partial_bytes(num_seqs, num_heads, head_dim, max_context_len);
+  const size_t need = (build_plan ? align256(pb) : 0) + part;
   if (workspace_bytes < need)
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: workspace of %zu bytes is smaller than the %zu needed", fn,
                      workspace_bytes, need);
   if (need > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: workspace must be a 256-byte aligned device buffer", fn);
-  const int32_t np = num_partitions(max_context_len);
-  const int64_t grid = static_cast<int64_t>(num_seqs) * num_heads * np;
-  if (grid > 0x7FFFFFFF) return pkv_failf(PKV_ERR_UNSUPPORTED, "%s: launch grid too large", fn);
-
+  char* ws = static_cast<char*>(workspace);
+  if (build_plan) {
+    plan = ws;
+    ws += align256(pb);
+    const int err = pkv_launch_plan(static_cast<int32_t*>(const_cast<void*>(plan)), context_lens, num_seqs,
+                                    max_blocks_per_seq, max_context_len, stream);
+    if (err) return hip_status(fn, err);
+  } else {
+    if (!plan) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: plan is NULL", fn);
+    if (plan_bytes_given < pb)
+      return pkv_failf(PKV_ERR_INVALID_ARG, "%s: plan of %zu bytes is smaller than the %zu these sizes need", fn,
+                       plan_bytes_given, pb);
+  }
   pkv_decode_args a{};
   a.out = out;
   a.q = q;
@@ -162,10 +195,10 @@ pkv_status pkv_attention_decode(float* out, const void* q, const void* k_cache,
   a.v_cache = v_cache;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
+  a.plan = static_cast<const int32_t*>(plan);
   const size_t units = static_cast<size_t>(num_seqs) * num_heads * np;
-  a.part_ml = need ? static_cast<float*>(workspace) : nullptr;
-  a.part_acc = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + align256(units * 2 * sizeof(float)))
-                    : nullptr;
+  a.part_ml = part ? reinterpret_cast<float*>(ws) : nullptr;
+  a.part_acc = part ? reinterpret_cast<float*>(ws + align256(units * 2 * sizeof(float))) : nullptr;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
@@ -173,11 +206,34 @@ pkv_status pkv_attention_decode(float* out, const void* q, const void* k_cache,
   a.head_dim = head_dim;
   a.num_blocks = num_blocks;
   a.max_context_len = max_context_len;
-  a.partition_tokens = g_partition_tokens;
   a.num_partitions = np;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.dtype = dtype;
   return hip_status(fn, pkv_launch_decode(a, stream));
+}
+
+pkv_status pkv_attention_decode(float* out, const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                int32_t max_context_len, float scale, pkv_dtype dtype, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  return decode_impl("pkv_attention_decode", out, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                     context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_context_len, scale, dtype, nullptr, 0, workspace, workspace_bytes, true, stream);
+}
+
+pkv_status pkv_attention_decode_planned(float* out, const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                        int32_t num_blocks, int32_t max_context_len, float scale,
+                                        pkv_dtype dtype, const void* plan, size_t plan_bytes_given,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl("pkv_attention_decode_planned", out, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                     context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                     max_context_len, scale, dtype, plan, plan_bytes_given, workspace, workspace_bytes, false,
+                     stream);
 }
 
 }  // extern "C"

@@ -18,6 +18,9 @@ int pkv_launch_append(void* k_cache, void* v_cache, const void* k, const void* v
 int pkv_launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst, int32_t num_pairs,
                            int32_t num_blocks, int64_t block_bytes, void* stream);
 
+// Tokens per context partition of the decode work split (a multiple of 16).
+constexpr int32_t kPartTokens = 512;
+
 struct pkv_decode_args {
   float* out;
   const void* q;
@@ -25,6 +28,7 @@ struct pkv_decode_args {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  const int32_t* plan; // unit list built by the plan kernel
   float* part_ml;      // [S][Hq][NP][2]  (running max in log2 units, sum)
   float* part_acc;     // [S][Hq][NP][d]
   int32_t max_blocks_per_seq;
@@ -34,9 +38,10 @@ struct pkv_decode_args {
   int32_t head_dim;
   int32_t num_blocks;
   int32_t max_context_len;
-  int32_t partition_tokens;
-  int32_t num_partitions;  // NP = ceil(max_context_len / partition_tokens)
+  int32_t num_partitions;  // NP = ceil(max_context_len / kPartTokens)
   float scale_log2;        // scale * log2(e)
   int dtype;               // pkv_dtype
 };
 int pkv_launch_decode(const pkv_decode_args& a, void* stream);
+int pkv_launch_plan(int32_t* plan, const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                    int32_t max_context_len, void* stream);

@@ -106,6 +106,24 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Global-memory (address space 1) pointers.  uniform_gptr moves a pointer that
+// every lane agrees on into scalar registers, so loads use the scalar-base +
+// 32-bit lane-offset form of global_load.
+typedef const __attribute__((address_space(1))) char* gptr_t;
+typedef const __attribute__((address_space(1))) u32x4* gptr4_t;
+typedef const __attribute__((address_space(1))) int32_t* gptri_t;
+
+__device__ __forceinline__ gptr_t uniform_gptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<gptr_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ u32x4 load16_nt(gptr_t base, uint32_t off) {
+  return __builtin_nontemporal_load(reinterpret_cast<gptr4_t>(base + off));
+}
+
 // Storage element traits: 16 bytes of storage -> EPL float32 values.
 template <typename T> struct Elem;
 template <> struct Elem<float> {
@@ -132,32 +150,140 @@ template <> struct Elem<uint16_t> {  // bf16 bits
 // [OS] "Cómo funciona por dentro": follow the block table, score the query
 // against each block's keys, then one softmax-weighted sum of the values.
 // [OS] "Qué significa esto para lo que pagas": decode is memory-bound, so the
-// kernel is built around streaming K/V tiles from HBM once, at full width.
+// kernel is built around streaming every K/V tile from HBM exactly once.
 //
-// Workgroup = (sequence s, query head h, context partition p) with 4 waves;
-// partition p holds blocks [p*BPP, (p+1)*BPP) of the sequence, and wave w takes
-// every 4th of them.  A wave reads a (block, head) tile with NLD 1 KiB loads:
+// Work units.  A sequence's context is cut into partitions of kPartTokens
+// tokens; a unit is (sequence s, partition p) and one workgroup handles one unit
+// for one query head.  The plan (plan_kernel) lists the units longest first --
+// every full partition, then the remainders by decreasing size -- so that the
+// workgroups dispatched last are the short ones and the ragged batches of
+// continuous batching ([UL] "Cómo funciona la planificación a nivel de
+// iteración") do not leave a long unit running alone at the end.  The grid is
+// units x heads with the head fastest, so the workgroups that run together
+// read the tiles of all heads of the same blocks.
+//
+// Inside a workgroup.  The unit's blocks are dealt to the 4 waves in turn.  A
+// (block, head) tile is 16 * D contiguous elements read with NLD 1 KiB loads:
 // lane l reads 16 bytes at l*16 of each KiB, i.e. token i*TPL + l/LPR of the
-// tile, dims (l%LPR)*EPL ... +EPL -- the same dims of q that the lane holds.
-// The dot product is a group_sum over the LPR lanes of a token row (DPP, no
-// LDS), so the score of a token lands in every lane of its row, which is
-// exactly the set of lanes that holds that token's V row for the P*V step.
-// Each row keeps its own running max / sum / accumulator (online softmax in
-// base 2, q pre-scaled by scale*log2 e); rows, then waves (through LDS), are
-// merged with the log-sum-exp rule at the end.  K/V tiles go straight to
-// registers: every element is used once by one lane, so staging through LDS
-// would only add traffic.  Masked tokens (past the context) are removed by
-// select, never by multiplying with 0, so NaN in unused slots cannot leak.
+// tile, dims (l%LPR)*EPL ... +EPL -- the dims of q the lane holds.  The dot
+// product is a group_sum over the LPR lanes of a token row (DPP, no LDS), so a
+// token's score lands in every lane of its row -- the lanes that hold that
+// token's V row for the P*V step.  Each row keeps its own online-softmax state
+// (base 2, q pre-scaled by scale*log2 e); rows, then waves (through LDS), are
+// merged with the log-sum-exp rule.  K/V go straight to registers: every
+// element is used once by one lane, so staging through LDS would only add
+// traffic.  Masked tokens (past the context) are removed by select, never by
+// multiplying with 0, so NaN in unused slots cannot leak.  A unit of a
+// sequence with one partition writes the output row; otherwise it writes a
+// partial (max, sum, unnormalised accumulator) for merge_partitions_kernel.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 struct DecodeShape {
   static constexpr int kEpl = Elem<T>::kEpl;            // elements per lane per load
   static constexpr int kLpr = D / kEpl;                 // lanes per token row
-  static constexpr int kTpl = 64 / kLpr;                // tokens per load
-  static constexpr int kNld = kBlock / kTpl;            // loads per tile
+  static constexpr int kTpl = 64 / kLpr;                // tokens per 1 KiB load
+  static constexpr int kNld = kBlock / kTpl;            // KiB per tile
   static constexpr int kBpi = kNld <= 4 ? 2 : 1;        // tiles in flight per wave
   static_assert(kLpr == 8 || kLpr == 16 || kLpr == 32, "unsupported shape");
 };
+
+// Plan header (int32): n_units, num_seqs, max_context_len, max_blocks_per_seq;
+// then (s, p) per unit.
+constexpr int kPlanHdr = 4;
+
+// A length that takes part in attention (others give a 0 row or a NaN row).
+__device__ __forceinline__ bool len_ok(int32_t ctx, int32_t max_context_len, int32_t max_blocks_per_seq) {
+  return ctx > 0 && ctx <= max_context_len && ctx <= max_blocks_per_seq * kBlock;
+}
+
+__device__ __forceinline__ bool plan_matches(const int32_t* plan, const pkv_decode_args& a) {
+  return plan[1] == a.num_seqs && plan[2] == a.max_context_len && plan[3] == a.max_blocks_per_seq;
+}
+
+// ---------------------------------------------------------------------------
+// Plan: one workgroup turns the context lengths into the unit list.  Full
+// partitions come first (sequence order), then remainders sorted by size,
+// largest first (a counting sort over the kPartTokens possible sizes; the
+// order inside one size is whatever the LDS atomics give, which changes no
+// result: every unit computes the same partial whenever it runs).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void plan_kernel(int32_t* __restrict__ plan,
+                                                    const int32_t* __restrict__ context_lens,
+                                                    int32_t num_seqs, int32_t max_blocks_per_seq,
+                                                    int32_t max_context_len) {
+  __shared__ int32_t bucket[kPartTokens];   // remainder size -> count, then -> next slot
+  __shared__ int32_t scan[1024];
+  __shared__ int32_t sm_full;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kPartTokens; i += 1024) bucket[i] = 0;
+  if (tid == 0) sm_full = 0;
+  __syncthreads();
+  int32_t full = 0;
+  for (int32_t s = tid; s < num_seqs; s += 1024) {
+    const int32_t ctx = context_lens[s];
+    if (!len_ok(ctx, max_context_len, max_blocks_per_seq)) continue;
+    full += ctx / kPartTokens;
+    if (ctx % kPartTokens) atomicAdd(&bucket[ctx % kPartTokens], 1);
+  }
+  atomicAdd(&sm_full, full);
+  __syncthreads();
+  const int32_t n_full = sm_full;
+  // bucket r's first slot = n_full + (remainders larger than r): a running sum
+  // over r from large to small, one thread per bucket, in chunks of 1024.
+  int32_t carry = n_full;
+  for (int32_t base = kPartTokens - 1; base >= 0; base -= 1024) {
+    const int32_t r = base - tid;
+    const int32_t c = r >= 1 ? bucket[r] : 0;
+    scan[tid] = c;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int32_t y = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += y;
+      __syncthreads();
+    }
+    if (r >= 1) bucket[r] = carry + scan[tid] - c;
+    const int32_t chunk_total = scan[1023];
+    __syncthreads();
+    carry += chunk_total;
+  }
+  const int32_t n_units = carry;
+  // full units at exclusive prefix positions, remainder units at their bucket slot
+  int32_t run = 0;
+  for (int32_t base = 0; base < num_seqs; base += 1024) {
+    const int32_t s = base + tid;
+    int32_t ctx = s < num_seqs ? context_lens[s] : 0;
+    const bool ok = s < num_seqs && len_ok(ctx, max_context_len, max_blocks_per_seq);
+    const int32_t nf = ok ? ctx / kPartTokens : 0;
+    scan[tid] = nf;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int32_t y = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += y;
+      __syncthreads();
+    }
+    const int32_t first = run + scan[tid] - nf;
+    for (int32_t p = 0; p < nf; ++p) {
+      plan[kPlanHdr + 2 * (first + p)] = s;
+      plan[kPlanHdr + 2 * (first + p) + 1] = p;
+    }
+    if (ok && ctx % kPartTokens) {
+      const int32_t slot = atomicAdd(&bucket[ctx % kPartTokens], 1);
+      plan[kPlanHdr + 2 * slot] = s;
+      plan[kPlanHdr + 2 * slot + 1] = nf;
+    }
+    const int32_t chunk_total = scan[1023];
+    __syncthreads();
+    run += chunk_total;
+  }
+  if (tid == 0) {
+    plan[0] = n_units;
+    plan[1] = num_seqs;
+    plan[2] = max_context_len;
+    plan[3] = max_blocks_per_seq;
+  }
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_valu_kernel(pkv_decode_args a) {
@@ -169,41 +295,29 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(pkv_decode_args a) {
   __shared__ int sm_bad[kWaves];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
   const int row = lane / LPR;
   const int col = lane % LPR;
 
-  // blockIdx -> (p, s, h): partitions from the last to the first so that the
-  // workgroups dispatched last are the short remainders.
   const int32_t Hq = a.num_heads;
-  int64_t bid = blockIdx.x;
-  const int32_t h = static_cast<int32_t>(bid % Hq); bid /= Hq;
-  const int32_t s = static_cast<int32_t>(bid % a.num_seqs); bid /= a.num_seqs;
-  const int32_t p = a.num_partitions - 1 - static_cast<int32_t>(bid);
-
+  const int32_t u = static_cast<int32_t>(blockIdx.x / Hq);
+  const int32_t h = static_cast<int32_t>(blockIdx.x - static_cast<uint32_t>(u) * Hq);
+  const int32_t* plan = a.plan;
+  if (!plan_matches(plan, a) || u >= plan[0]) return;
+  const int32_t s = plan[kPlanHdr + 2 * u];
+  const int32_t p = plan[kPlanHdr + 2 * u + 1];
   const int32_t ctx = a.context_lens[s];
-  const int32_t cap = a.max_blocks_per_seq * kBlock;
-  const bool bad_len = ctx < 0 || ctx > a.max_context_len || ctx > cap;
-  const int64_t orow = (static_cast<int64_t>(s) * Hq + h) * D;
-  if (bad_len || ctx == 0) {
-    // Only partition 0 owns the output row; it writes NaN (bad length) or 0.
-    if (p == 0 && threadIdx.x < D) a.out[orow + threadIdx.x] = bad_len ? __builtin_nanf("") : 0.0f;
-    return;
-  }
-  const int32_t pt = a.partition_tokens;
-  const int32_t tok0 = p * pt;
-  if (tok0 >= ctx) return;                                  // empty partition
-  const int32_t np_s = (ctx + pt - 1) / pt;
+  const int32_t np_s = (ctx + kPartTokens - 1) / kPartTokens;
   const int32_t nblk = (ctx + kBlock - 1) / kBlock;
-  const int32_t blk_begin = tok0 / kBlock;
-  const int32_t blk_end = min(nblk, (tok0 + pt) / kBlock);
+  const int32_t blk_begin = p * (kPartTokens / kBlock);
+  const int32_t blk_end = min(nblk, blk_begin + kPartTokens / kBlock);
+  const int64_t orow = (static_cast<int64_t>(s) * Hq + h) * D;
 
-  const int32_t g = h / (Hq / a.num_kv_heads);
-  const int64_t tile_elems = static_cast<int64_t>(kBlock) * D;
-  const int64_t head_off = static_cast<int64_t>(g) * tile_elems;
-  const int64_t block_stride = static_cast<int64_t>(a.num_kv_heads) * tile_elems;
-  const T* __restrict__ kc = reinterpret_cast<const T*>(a.k_cache);
-  const T* __restrict__ vc = reinterpret_cast<const T*>(a.v_cache);
+  constexpr int64_t kTileBytes = static_cast<int64_t>(kBlock) * D * sizeof(T);
+  const int64_t block_bytes = static_cast<int64_t>(a.num_kv_heads) * kTileBytes;
+  const int64_t head_off = static_cast<int64_t>(h / (Hq / a.num_kv_heads)) * kTileBytes;
+  const char* __restrict__ kc = reinterpret_cast<const char*>(a.k_cache);
+  const char* __restrict__ vc = reinterpret_cast<const char*>(a.v_cache);
   const int32_t* __restrict__ table = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq;
 
   // q slice of this lane, pre-scaled into base-2 units
@@ -221,27 +335,37 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(pkv_decode_args a) {
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
   bool bad = false;
 
+  // The block ids of the next iteration are fetched (scalar loads) while the
+  // current iteration's tiles are in flight.
+  int32_t nxt[BPI];
+#pragma unroll
+  for (int bi = 0; bi < BPI; ++bi) {
+    const int32_t j = blk_begin + wave + bi * kWaves;
+    nxt[bi] = j < blk_end ? table[j] : 0;
+  }
   for (int32_t j0 = blk_begin + wave; j0 < blk_end; j0 += kWaves * BPI) {
     u32x4 kt[BPI][NLD], vt[BPI][NLD];
     int32_t tb[BPI];
 #pragma unroll
     for (int bi = 0; bi < BPI; ++bi) {
       const int32_t j = j0 + bi * kWaves;
-      int32_t b = 0;
+      int32_t b = nxt[bi];
       tb[bi] = -1;
       if (j < blk_end) {
-        b = table[j];
         if (static_cast<uint32_t>(b) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; b = 0; }
         tb[bi] = j * kBlock;
-      }
-      const u32x4* kp = reinterpret_cast<const u32x4*>(kc + b * block_stride + head_off);
-      const u32x4* vp = reinterpret_cast<const u32x4*>(vc + b * block_stride + head_off);
-      if (j < blk_end) {
+        const u32x4* kp = reinterpret_cast<const u32x4*>(kc + b * block_bytes + head_off);
+        const u32x4* vp = reinterpret_cast<const u32x4*>(vc + b * block_bytes + head_off);
 #pragma unroll
         for (int i = 0; i < NLD; ++i) kt[bi][i] = __builtin_nontemporal_load(kp + i * 64 + lane);
 #pragma unroll
         for (int i = 0; i < NLD; ++i) vt[bi][i] = __builtin_nontemporal_load(vp + i * 64 + lane);
       }
+    }
+#pragma unroll
+    for (int bi = 0; bi < BPI; ++bi) {
+      const int32_t j = j0 + kWaves * BPI + bi * kWaves;
+      nxt[bi] = j < blk_end ? table[j] : 0;
     }
 #pragma unroll
     for (int bi = 0; bi < BPI; ++bi) {
@@ -291,7 +415,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(pkv_decode_args a) {
     }
   }
 
-  // merge the TPL rows of the wave (lanes that hold the same dims)
+  // merge the rows of the wave (lanes that hold the same dims) ...
 #pragma unroll
   for (int off = LPR; off < 64; off <<= 1) {
     const float mo = __shfl_xor(m, off);
@@ -306,25 +430,24 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(pkv_decode_args a) {
     }
     m = mx;
   }
-  if (lane == 0) sm_bad[wave] = bad ? 1 : 0;
+  // ... then the four waves, through LDS
   if (lane < LPR) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) sm_acc[wave][col * EPL + e] = acc[e];
   }
-  if (lane == 0) { sm_ml[wave][0] = m; sm_ml[wave][1] = l; }
+  if (lane == 0) { sm_ml[wave][0] = m; sm_ml[wave][1] = l; sm_bad[wave] = bad ? 1 : 0; }
   __syncthreads();
-
   if (threadIdx.x < D) {
     const int t = threadIdx.x;
     float M = sm_ml[0][0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_ml[w][0]);
+    for (int v = 1; v < kWaves; ++v) M = fmaxf(M, sm_ml[v][0]);
     float L = 0.f, o = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = fast_exp2(sm_ml[w][0] - M);
-      L += sm_ml[w][1] * f;
-      o += sm_acc[w][t] * f;
+    for (int v = 0; v < kWaves; ++v) {
+      const float f = fast_exp2(sm_ml[v][0] - M);
+      L += sm_ml[v][1] * f;
+      o += sm_acc[v][t] * f;
     }
     if (sm_bad[0] | sm_bad[1] | sm_bad[2] | sm_bad[3]) { o = __builtin_nanf(""); L = __builtin_nanf(""); }
     if (np_s == 1) {
@@ -338,26 +461,34 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(pkv_decode_args a) {
 }
 
 // ---------------------------------------------------------------------------
-// Partition merge: for every (s, h) whose context spans more than one
-// partition, M = max_p m_p, L = sum_p l_p 2^(m_p - M), out = sum_p acc_p 2^(m_p - M) / L.
-// This is the log-sum-exp identity that makes the split softmax equal the
-// unsplit one.  One thread per output element.
+// Partition merge, one workgroup per (s, h): for a context of more than one
+// partition,  M = max_p m_p,  L = sum_p l_p 2^(m_p - M),
+// out = sum_p acc_p 2^(m_p - M) / L  -- the log-sum-exp identity that makes the
+// split softmax equal the unsplit one.  It also writes the rows no unit owns:
+// 0 for an empty context, NaN for an invalid one (or a plan built for other
+// arguments).  A separate launch keeps the decode kernel free of
+// cross-workgroup synchronisation: device-scope fences write back and
+// invalidate a whole XCD L2, far costlier than a second launch.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(D) void merge_partitions_kernel(pkv_decode_args a) {
   const int64_t sh = blockIdx.x;                       // s * Hq + h
   const int32_t s = static_cast<int32_t>(sh / a.num_heads);
   const int32_t ctx = a.context_lens[s];
-  const int32_t cap = a.max_blocks_per_seq * kBlock;
-  if (ctx <= 0 || ctx > a.max_context_len || ctx > cap) return;   // written by the decode kernel
-  const int32_t np_s = (ctx + a.partition_tokens - 1) / a.partition_tokens;
+  const int t = threadIdx.x;
+  const bool plan_ok = plan_matches(a.plan, a);
+  if (!plan_ok || !len_ok(ctx, a.max_context_len, a.max_blocks_per_seq)) {
+    if (!plan_ok || ctx != 0) a.out[sh * D + t] = __builtin_nanf("");
+    else a.out[sh * D + t] = 0.f;
+    return;
+  }
+  const int32_t np_s = (ctx + kPartTokens - 1) / kPartTokens;
   if (np_s <= 1) return;
   const float* ml = a.part_ml + sh * a.num_partitions * 2;
   const float* acc = a.part_acc + sh * a.num_partitions * D;
   float M = ml[0];
   for (int32_t p = 1; p < np_s; ++p) M = fmaxf(M, ml[2 * p]);
   float L = 0.f, o = 0.f;
-  const int t = threadIdx.x;
   for (int32_t p = 0; p < np_s; ++p) {
     const float f = fast_exp2(ml[2 * p] - M);
     L += ml[2 * p + 1] * f;
@@ -368,19 +499,24 @@ __global__ __launch_bounds__(D) void merge_partitions_kernel(pkv_decode_args a) 
 
 template <typename T, int D>
 int launch_decode_typed(const pkv_decode_args& a, hipStream_t st) {
-  const int64_t grid = static_cast<int64_t>(a.num_seqs) * a.num_heads * a.num_partitions;
+  const int64_t grid = static_cast<int64_t>(a.num_seqs) * a.num_partitions * a.num_heads;
   hipLaunchKernelGGL((decode_valu_kernel<T, D>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.num_partitions > 1) {
-    hipLaunchKernelGGL((merge_partitions_kernel<D>), dim3(static_cast<uint32_t>(a.num_seqs) * a.num_heads),
-                       dim3(D), 0, st, a);
-    e = hipGetLastError();
-  }
-  return e;
+  hipLaunchKernelGGL((merge_partitions_kernel<D>), dim3(static_cast<uint32_t>(a.num_seqs) * a.num_heads), dim3(D),
+                     0, st, a);
+  return hipGetLastError();
 }
 
 }  // namespace
+
+int pkv_launch_plan(int32_t* plan, const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                    int32_t max_context_len, void* stream) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, static_cast<hipStream_t>(stream), plan, context_lens,
+                     num_seqs, max_blocks_per_seq, max_context_len);
+  return hipGetLastError();
+}
+
 
 int pkv_launch_append(void* k_cache, void* v_cache, const void* k, const void* v,
                       const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,

@@ -24,13 +24,6 @@ from pkv_gpu_driver import GpuReplay, pool_to_host, rows_to_device  # noqa: E402
 TOL = {"f32": 1e-5, "bf16": 2e-3}
 
 
-@pytest.fixture(autouse=True)
-def _partition_default():
-    old = PK.pkv_get_decode_partition_tokens()
-    yield
-    PK.pkv_set_decode_partition_tokens(old)
-
-
 def _oracle(w, pool_fill=None):
     return O.replay(w.ops, w.k_rows, w.v_rows, w.num_blocks, w.num_kv_heads, w.head_dim,
                     w.initial_free_order, pool_fill=pool_fill)
@@ -67,21 +60,20 @@ def test_tiny_workload_bit_exact_state_and_attention():
 
 
 SMALL = [
-    # seed, S, max_ctx, Hq, Hkv, d, dtype, partition tokens
-    (11, 7, 70, 4, 4, 64, "f32", 256),
-    (12, 9, 300, 2, 2, 128, "f32", 64),
-    (13, 5, 200, 8, 2, 128, "bf16", 16),
-    (14, 12, 520, 4, 4, 128, "bf16", 256),
-    (15, 6, 129, 4, 1, 64, "bf16", 32),
-    (16, 10, 1000, 2, 2, 64, "f32", 128),
-    (17, 3, 33, 16, 16, 128, "bf16", 16),
+    # seed, S, max_ctx, Hq, Hkv, d, dtype  (512-token partitions: > 512 exercises the merge)
+    (11, 7, 70, 4, 4, 64, "f32"),
+    (12, 9, 1300, 2, 2, 128, "f32"),
+    (13, 5, 1100, 8, 2, 128, "bf16"),
+    (14, 12, 520, 4, 4, 128, "bf16"),
+    (15, 6, 1700, 4, 1, 64, "bf16"),
+    (16, 10, 2100, 2, 2, 64, "f32"),
+    (17, 3, 33, 16, 16, 128, "bf16"),
 ]
 
 
-@pytest.mark.parametrize("seed,S,max_ctx,hq,hkv,d,dtype,pt", SMALL)
-def test_small_ragged_batches(seed, S, max_ctx, hq, hkv, d, dtype, pt):
-    print(f"case: small seed={seed} S={S} ctx<={max_ctx} H={hq}/{hkv} d={d} {dtype} pt={pt}", flush=True)
-    PK.pkv_set_decode_partition_tokens(pt)
+@pytest.mark.parametrize("seed,S,max_ctx,hq,hkv,d,dtype", SMALL)
+def test_small_ragged_batches(seed, S, max_ctx, hq, hkv, d, dtype):
+    print(f"case: small seed={seed} S={S} ctx<={max_ctx} H={hq}/{hkv} d={d} {dtype}", flush=True)
     w = W.random_small(seed, S, max_ctx, hq, hkv, d, dtype)
     g, r = GpuReplay(w), _oracle(w)
     _check_state(g, r, w)
@@ -157,11 +149,10 @@ def test_context_of_one_returns_the_value_row_and_zero_context_gives_zeros():
     assert np.array_equal(out0[0], out[0])
 
 
-@pytest.mark.parametrize("pt", [16, 256])
-def test_physical_block_relabelling_gives_bit_identical_outputs(pt):
-    PK.pkv_set_decode_partition_tokens(pt)
-    w = W.random_small(23, 6, 150, 4, 4, 128, "bf16")
-    print(f"case: relabel pt={pt}", flush=True)
+@pytest.mark.parametrize("max_ctx", [150, 1500])
+def test_physical_block_relabelling_gives_bit_identical_outputs(max_ctx):
+    w = W.random_small(23, 6, max_ctx, 4, 4, 128, "bf16")
+    print(f"case: relabel max_ctx={max_ctx}", flush=True)
     g = GpuReplay(w)
     out, tables, lens = g.decode()
     pi = torch.from_numpy(np.random.default_rng(0).permutation(w.num_blocks)).cuda()
@@ -203,8 +194,7 @@ def test_forked_samples_give_the_same_outputs_as_unshared_copies():
 
 
 def test_bad_rows_are_nan_and_leave_other_rows_alone():
-    PK.pkv_set_decode_partition_tokens(32)
-    w = W.random_small(24, 5, 100, 2, 2, 64, "f32")
+    w = W.random_small(24, 5, 1100, 2, 2, 64, "f32")
     print("case: bad rows", flush=True)
     g = GpuReplay(w)
     out, tables, lens = g.decode()
@@ -216,6 +206,7 @@ def test_bad_rows_are_nan_and_leave_other_rows_alone():
     l2[3] = mcl + 1                      # longer than max_context_len
     out2, _, _ = g.decode(tables=t2, lens=l2, max_context_len=mcl)
     assert np.isnan(out2[1]).all() and np.isnan(out2[2]).all() and np.isnan(out2[3]).all()
+    # the other rows are computed exactly as before
     assert np.array_equal(out2[0], out[0]) and np.array_equal(out2[4], out[4])
 
 
@@ -229,3 +220,73 @@ def test_append_skips_negative_and_out_of_pool_slots():
     PK.pkv_append(g.k_pool, g.v_pool, rows, rows, sl)
     torch.cuda.synchronize()
     assert np.array_equal(pool_to_host(g.k_pool), before_k)
+
+
+def test_workspace_reuse_across_calls_and_shapes():
+    """One workspace (never cleared) serves consecutive calls with different batches."""
+    print("case: workspace reuse", flush=True)
+    ws = PK.workspace_for(16, 8, 128, 1600)
+    results = []
+    for seed, S, mx in ((41, 9, 1600), (42, 16, 700), (41, 9, 1600)):
+        w = W.random_small(seed, S, mx, 8, 2, 128, "bf16")
+        g = GpuReplay(w)
+        tables, lens = g.tables(w.decode_seqs)
+        out = torch.empty((S, 8, 128), dtype=torch.float32, device="cuda")
+        PK.pkv_attention_decode(out, rows_to_device(w.q, "cuda"), g.k_pool, g.v_pool,
+                                torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
+                                int(lens.max()), float(w.scale), workspace=ws)
+        torch.cuda.synchronize()
+        r = _oracle(w)
+        ref = O.decode_attention(w.q, r.k_pool, r.v_pool, [r.alloc.block_table(s) for s in w.decode_seqs],
+                                 [r.alloc.num_tokens(s) for s in w.decode_seqs], w.scale)
+        o = out.cpu().numpy()
+        assert float(np.abs(o - ref).max()) <= TOL["bf16"]
+        results.append(o)
+    assert np.array_equal(results[0], results[2])
+
+
+def test_planned_decode_matches_self_planned_and_reuses_the_plan():
+    """One plan per step serves every layer: the planned call gives the same bits
+    as the self-planning call, on two different pools with the same tables."""
+    w = W.random_small(51, 11, 1400, 8, 8, 128, "bf16")
+    print("case: planned decode", flush=True)
+    g = GpuReplay(w)
+    tables, lens = g.tables(w.decode_seqs)
+    td, ld = torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
+    mcl = int(lens.max())
+    plan = PK.plan_for(ld, tables.shape[1], mcl)
+    q = rows_to_device(w.q, "cuda")
+    pools = [(g.k_pool, g.v_pool), (g.v_pool, g.k_pool)]   # a second "layer": K and V swapped
+    for kp, vp in pools:
+        o1 = torch.empty((len(lens), 8, 128), dtype=torch.float32, device="cuda")
+        o2 = torch.empty_like(o1)
+        PK.pkv_attention_decode(o1, q, kp, vp, td, ld, mcl, float(w.scale))
+        PK.pkv_attention_decode(o2, q, kp, vp, td, ld, mcl, float(w.scale), plan=plan)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2)
+
+
+def test_plan_built_for_other_sizes_gives_nan_rows():
+    w = W.random_small(52, 4, 300, 2, 2, 64, "f32")
+    print("case: plan mismatch", flush=True)
+    g = GpuReplay(w)
+    tables, lens = g.tables(w.decode_seqs)
+    td, ld = torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
+    mcl = int(lens.max())
+    plan = PK.plan_for(ld, tables.shape[1], mcl + 1)           # built with another max_context_len
+    o = torch.zeros((4, 2, 64), dtype=torch.float32, device="cuda")
+    PK.pkv_attention_decode(o, rows_to_device(w.q, "cuda"), g.k_pool, g.v_pool, td, ld, mcl, float(w.scale),
+                            plan=plan)
+    torch.cuda.synchronize()
+    assert torch.isnan(o).all()
+
+
+@pytest.mark.parametrize("ctxs", [[512, 513, 1024, 1, 16, 17, 1536], [4096, 3, 700]])
+def test_partition_boundaries(ctxs):
+    """Context lengths on and next to the 512-token partition edges."""
+    print(f"case: partition edges {ctxs}", flush=True)
+    rng = np.random.default_rng(sum(ctxs))
+    w = W._plain_decode("edges", 77, ctxs, 4, 4, 128, "bf16")
+    g, r = GpuReplay(w), _oracle(w)
+    err = _attn_err(g, r, w)
+    assert err <= TOL["bf16"], err

@@ -43,17 +43,20 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def stored_traffic():
+def stored_traffic(alg_bytes_per_launch: float):
     """HBM bytes per decode launch from the committed counter summary, if it was
-    taken on the current kernel source (else None)."""
+    taken on the current kernel source (else None).  The summary holds the
+    counter bytes of its own run and that run's algorithmic bytes; the traffic
+    is scaled by the ratio of algorithmic bytes to this run's launches."""
     if not os.path.exists(COUNTERS_FILE):
         return None
     text = open(COUNTERS_FILE).read()
     h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not h or not t or h.group(1) != kernel_source_hash():
+    a = re.search(r"alg_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not h or not t or not a or h.group(1) != kernel_source_hash():
         return None
-    return float(t.group(1))
+    return round(float(t.group(1)) * alg_bytes_per_launch / float(a.group(1)))
 
 
 def parse():
@@ -65,7 +68,28 @@ def parse():
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time for the oracle sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run pkv_copy_blocks over 4096 whole blocks (a plain copy of known size, "
+                         "used to scale the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def copy_probe():
+    """Copy 4096 whole 40-head bf16 blocks of K and of V (2 x 640 MiB read,
+    2 x 640 MiB written) three times with pkv_copy_blocks."""
+    import torch
+    import paged_kv_cache_171_amd as PK
+    dev = torch.device("cuda:0")
+    n, H, D, P = 4096, 40, 128, 16
+    k = torch.zeros(2 * n, H, P, D, dtype=torch.bfloat16, device=dev)
+    v = torch.zeros_like(k)
+    pairs = torch.stack([torch.arange(n), torch.arange(n, 2 * n)], 1).to(torch.int32).to(dev)
+    for _ in range(3):
+        PK.pkv_copy_blocks(k, v, pairs)
+    torch.cuda.synchronize()
+    block_bytes = H * P * D * 2
+    print(json.dumps({"copy_probe": "pkv_copy_blocks", "pairs": n, "read_bytes": 2 * n * block_bytes,
+                      "write_bytes": 2 * n * block_bytes, "launches": 3}), flush=True)
 
 
 def cpu_baseline(seed: int, target_s: float):
@@ -101,6 +125,9 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
 
     import torch
     import paged_kv_cache_171_amd as PK
@@ -225,7 +252,7 @@ def main():
     step_s = ms_per_step / 1e3
     kv_gbps = (sum(kv_bytes) / args.steps) * L / step_s / 1e9
 
-    traffic = stored_traffic()
+    traffic = stored_traffic(alg_bytes_total / launches)
     res = {
         "metric": METRIC,
         "value": round(S / step_s, 1),

@@ -118,7 +118,9 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst,
  *
  * q: device [num_seqs][num_heads][head_dim] in `dtype`; out: device float32
  * [num_seqs][num_heads][head_dim]; context_lens: device int32 [num_seqs].
- * Scores, softmax and accumulation are float32.  max_context_len must be >= every
+ * Scores, softmax and accumulation are float32 (bf16 query-head groups of 2..16
+ * heads per KV head run on the matrix cores with the probabilities carried as
+ * a bf16 pair, ~16 significant bits).  max_context_len must be >= every
  * context length (it sizes the context split); a row whose length exceeds it or
  * max_blocks_per_seq*block_size, or whose table names a block outside
  * [0, num_blocks), is written as NaN.
@@ -168,6 +170,36 @@ pkv_status pkv_attention_decode_planned(float* out, const void* q, const void* k
                                         int32_t num_blocks, int32_t max_context_len, float scale,
                                         pkv_dtype dtype, const void* plan, size_t plan_bytes,
                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Causal chunked-prefill attention.  [UL] "Cómo funciona la planificación a
+ * nivel de iteración" and "Límites y técnicas complementarias": a long prompt
+ * is prefilled in chunks that run in the same step as other sequences' decode.
+ * Sequence s owns query tokens query_start_loc[s] .. query_start_loc[s+1]-1;
+ * with n_s of them they are the last n_s tokens of its context (their K/V
+ * already written with pkv_append), so query i sits at position
+ * p_i = context_lens[s] - n_s + i and attends keys 0..p_i:
+ *
+ *   for s, i < n_s, h:  g = h / (num_heads/num_kv_heads)
+ *     out[qsl[s]+i][h][:] = sum_{j<=p_i} softmax_j(scale * <q[qsl[s]+i][h], K_j>) V_j
+ *
+ * q: device [num_query_tokens][num_heads][head_dim] bf16; out: device float32
+ * of the same shape; query_start_loc: device int32 [num_seqs+1].  bf16 only
+ * (PKV_ERR_UNSUPPORTED otherwise); matrix-core (MFMA) kernel with float32
+ * scores, softmax and accumulation.  max_query_len must be >= every n_s (it
+ * sizes the grid).  A sequence whose query range is not inside
+ * [0, num_query_tokens] or is longer than max_query_len is skipped (its rows
+ * are not written); one whose context is shorter than n_s, longer than
+ * max_context_len or max_blocks_per_seq*block_size, or whose table names a
+ * block outside [0, num_blocks), gets NaN rows.  No workspace.
+ * ------------------------------------------------------------------------ */
+pkv_status pkv_attention_prefill_chunk(float* out, const void* q, const int32_t* query_start_loc,
+                                       int32_t num_query_tokens, int32_t max_query_len, const void* k_cache,
+                                       const void* v_cache, const int32_t* block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size, int32_t num_blocks, int32_t max_context_len,
+                                       float scale, pkv_dtype dtype, void* stream);
 
 /* ------------------------------------------------------------------------
  * Host block allocator.  [CB] "PagedAttention: Memoria virtual para la KV

@@ -42,6 +42,9 @@ _SIGS = {
     "pkv_attention_decode_planned": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32,
                                               _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_p, _c_sz, _c_p,
                                               _c_sz, _c_p]),
+    "pkv_attention_prefill_chunk": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_i32, _c_p,
+                                             _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
+                                             _c_i32, _c_p]),
     "pkv_allocator_create": (_c_i32, [_c_i32, _c_i32, _c_p, ctypes.POINTER(_c_p)]),
     "pkv_allocator_destroy": (None, [_c_p]),
     "pkv_allocator_num_free": (_c_i32, [_c_p]),
@@ -173,6 +176,24 @@ def pkv_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tens
         _dev(plan)
         _check(_lib.pkv_attention_decode_planned(*args, plan.data_ptr(), plan.numel(), workspace.data_ptr(),
                                                  workspace.numel(), _stream(stream)))
+
+
+def pkv_attention_prefill_chunk(out: torch.Tensor, q: torch.Tensor, query_start_loc: torch.Tensor,
+                                max_query_len: int, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                                scale: float, stream=None) -> None:
+    """out fp32 [Tq, Hq, d]; q bf16 [Tq, Hq, d]; query_start_loc int32 [S+1]; block_tables int32 [S, MB];
+    context_lens int32 [S] (each sequence's chunk is the last tokens of its context)."""
+    _dev(out, q, query_start_loc, k_cache, v_cache, block_tables, context_lens)
+    assert out.dtype == torch.float32 and query_start_loc.dtype == torch.int32
+    assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+    tq, hq, d = q.shape
+    nb, hkv, bs, _ = k_cache.shape
+    _check(_lib.pkv_attention_prefill_chunk(out.data_ptr(), q.data_ptr(), query_start_loc.data_ptr(), tq,
+                                            int(max_query_len), k_cache.data_ptr(), v_cache.data_ptr(),
+                                            block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
+                                            context_lens.numel(), hq, hkv, d, bs, nb, int(max_context_len),
+                                            float(scale), _dtype_code(k_cache), _stream(stream)))
 
 
 class BlockAllocator:

@@ -236,4 +236,53 @@ pkv_status pkv_attention_decode_planned(float* out, const void* q, const void* k
                      stream);
 }
 
+pkv_status pkv_attention_prefill_chunk(float* out, const void* q, const int32_t* query_start_loc,
+                                       int32_t num_query_tokens, int32_t max_query_len, const void* k_cache,
+                                       const void* v_cache, const int32_t* block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size, int32_t num_blocks, int32_t max_context_len,
+                                       float scale, pkv_dtype dtype, void* stream) {
+  const char* fn = "pkv_attention_prefill_chunk";
+  pkv_status st = check_common(fn, num_kv_heads, head_dim, block_size, dtype);
+  if (st != PKV_OK) return st;
+  if (dtype != PKV_BF16) return pkv_failf(PKV_ERR_UNSUPPORTED, "%s: only bf16 is built", fn);
+  if (num_seqs < 0 || num_query_tokens < 0 || max_query_len < 0 || max_context_len < 0)
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (num_heads <= 0 || num_heads % num_kv_heads != 0)
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: num_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                     fn, num_heads, num_kv_heads);
+  if (num_blocks <= 0) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: num_blocks must be > 0", fn);
+  if (max_blocks_per_seq <= 0) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: max_blocks_per_seq must be > 0", fn);
+  if (!std::isfinite(scale)) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+  if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0) return PKV_OK;
+  if (!out || !q || !query_start_loc || !k_cache || !v_cache || !block_tables || !context_lens)
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: out, q and cache pointers must be 16-byte aligned", fn);
+  const int64_t group = num_heads / num_kv_heads;
+  const int64_t tiles = (static_cast<int64_t>(max_query_len) * group + kPrefillRowsPerWg - 1) / kPrefillRowsPerWg;
+  if (static_cast<int64_t>(num_seqs) * num_kv_heads * tiles > 0x7FFFFFFF)
+    return pkv_failf(PKV_ERR_UNSUPPORTED, "%s: launch grid too large", fn);
+  pkv_prefill_args a{};
+  a.out = out;
+  a.q = q;
+  a.query_start_loc = query_start_loc;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_query_tokens = num_query_tokens;
+  a.max_query_len = max_query_len;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.max_context_len = max_context_len;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(fn, pkv_launch_prefill(a, stream));
+}
+
 }  // extern "C"

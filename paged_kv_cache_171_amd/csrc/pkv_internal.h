@@ -42,6 +42,35 @@ struct pkv_decode_args {
   float scale_log2;        // scale * log2(e)
   int dtype;               // pkv_dtype
 };
+// Decode: the main kernel (VALU, or MFMA for bf16 query-head groups of 2..16
+// heads) and then the partition merge.
 int pkv_launch_decode(const pkv_decode_args& a, void* stream);
+constexpr int32_t kMaxMfmaGroup = 16;
+// The MFMA kernel for bf16 query-head groups (pkv_mfma.hip); the caller launches the merge.
+int pkv_launch_decode_group(const pkv_decode_args& a, void* stream);
 int pkv_launch_plan(int32_t* plan, const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
                     int32_t max_context_len, void* stream);
+
+// Causal chunked-prefill attention (pkv_mfma.hip).
+struct pkv_prefill_args {
+  float* out;                     // [num_query_tokens][Hq][d]
+  const void* q;                  // [num_query_tokens][Hq][d]
+  const int32_t* query_start_loc; // [num_seqs + 1]
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t num_query_tokens;
+  int32_t max_query_len;
+  int32_t max_blocks_per_seq;
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t num_blocks;
+  int32_t max_context_len;
+  float scale_log2;
+};
+// Query rows (token, head of a KV group) per prefill workgroup.
+constexpr int32_t kPrefillRowsPerWg = 128;
+int pkv_launch_prefill(const pkv_prefill_args& a, void* stream);

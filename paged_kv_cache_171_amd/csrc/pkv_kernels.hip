@@ -9,20 +9,19 @@
 //
 // Pool layout: [num_blocks][num_kv_heads][16][head_dim].  One (block, KV head)
 // tile is 16 * head_dim contiguous elements (4 KiB for bf16, head_dim 128).
-#include <hip/hip_runtime.h>
-
-#include <cfloat>
-#include <cstdint>
-
-#include "pkv_internal.h"
+#include "pkv_device.h"
 
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+using pkvd::u32x4;
+using pkvd::kBlock;
+using pkvd::kNegBig;
+using pkvd::kPlanHdr;
+using pkvd::fast_exp2;
+using pkvd::len_ok;
+using pkvd::plan_matches;
 
-constexpr int kBlock = 16;        // tokens per block ([CB]: P = 16)
 constexpr int kWaves = 4;         // waves per decode workgroup
-constexpr float kNegBig = -FLT_MAX;
 
 // ---------------------------------------------------------------------------
 // Cache write ([OS] "Cómo funciona por dentro": a token's K/V go to the slot its
@@ -103,8 +102,6 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (LPR >= 32) x += __shfl_xor(x, 16);
   return x;
 }
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Global-memory (address space 1) pointers.  uniform_gptr moves a pointer that
 // every lane agrees on into scalar registers, so loads use the scalar-base +
@@ -187,18 +184,8 @@ struct DecodeShape {
   static_assert(kLpr == 8 || kLpr == 16 || kLpr == 32, "unsupported shape");
 };
 
-// Plan header (int32): n_units, num_seqs, max_context_len, max_blocks_per_seq;
-// then (s, p) per unit.
-constexpr int kPlanHdr = 4;
-
-// A length that takes part in attention (others give a 0 row or a NaN row).
-__device__ __forceinline__ bool len_ok(int32_t ctx, int32_t max_context_len, int32_t max_blocks_per_seq) {
-  return ctx > 0 && ctx <= max_context_len && ctx <= max_blocks_per_seq * kBlock;
-}
-
-__device__ __forceinline__ bool plan_matches(const int32_t* plan, const pkv_decode_args& a) {
-  return plan[1] == a.num_seqs && plan[2] == a.max_context_len && plan[3] == a.max_blocks_per_seq;
-}
+// Plan layout (int32): header n_units, num_seqs, max_context_len,
+// max_blocks_per_seq; then (s, p) per unit.
 
 // ---------------------------------------------------------------------------
 // Plan: one workgroup turns the context lengths into the unit list.  Full
@@ -498,13 +485,9 @@ __global__ __launch_bounds__(D) void merge_partitions_kernel(pkv_decode_args a) 
 }
 
 template <typename T, int D>
-int launch_decode_typed(const pkv_decode_args& a, hipStream_t st) {
+int launch_decode_valu(const pkv_decode_args& a, hipStream_t st) {
   const int64_t grid = static_cast<int64_t>(a.num_seqs) * a.num_partitions * a.num_heads;
   hipLaunchKernelGGL((decode_valu_kernel<T, D>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((merge_partitions_kernel<D>), dim3(static_cast<uint32_t>(a.num_seqs) * a.num_heads), dim3(D),
-                     0, st, a);
   return hipGetLastError();
 }
 
@@ -545,10 +528,21 @@ int pkv_launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst,
 
 int pkv_launch_decode(const pkv_decode_args& a, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (a.dtype == PKV_BF16) {
-    if (a.head_dim == 128) return launch_decode_typed<uint16_t, 128>(a, st);
-    return launch_decode_typed<uint16_t, 64>(a, st);
+  const int32_t group = a.num_heads / a.num_kv_heads;
+  int err;
+  if (a.dtype == PKV_BF16 && group >= 2 && group <= kMaxMfmaGroup) {
+    err = pkv_launch_decode_group(a, stream);          // query-head groups: MFMA kernel
+  } else if (a.dtype == PKV_BF16) {
+    err = a.head_dim == 128 ? launch_decode_valu<uint16_t, 128>(a, st) : launch_decode_valu<uint16_t, 64>(a, st);
+  } else {
+    err = a.head_dim == 128 ? launch_decode_valu<float, 128>(a, st) : launch_decode_valu<float, 64>(a, st);
   }
-  if (a.head_dim == 128) return launch_decode_typed<float, 128>(a, st);
-  return launch_decode_typed<float, 64>(a, st);
+  if (err != hipSuccess) return err;
+  const uint32_t rows = static_cast<uint32_t>(a.num_seqs) * a.num_heads;
+  if (a.head_dim == 128) {
+    hipLaunchKernelGGL((merge_partitions_kernel<128>), dim3(rows), dim3(128), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((merge_partitions_kernel<64>), dim3(rows), dim3(64), 0, st, a);
+  }
+  return hipGetLastError();
 }

@@ -1,0 +1,539 @@
+// MFMA kernels for gfx950 (CDNA4, wave64): attention of query-head groups that
+// share one KV head, where the work is a real dense contraction.
+//
+//   decode_group_mfma_kernel   -- decode with grouped-query heads (G = Hq/Hkv in
+//                                 2..16 query heads read the same K/V tiles)
+//   prefill_chunk_mfma_kernel  -- causal attention of a prefill chunk: every
+//                                 (query token, head) row of a KV group against
+//                                 its sequence's paged context
+//
+// Pages cited:
+//   [OS]  "PagedAttention: gestionar la KV cache como memoria de un sistema
+//         operativo" (josueisai.com), "Cómo funciona por dentro": attention follows
+//         the block table, scores each block, then one softmax-weighted sum.
+//   [UL]  "Continuous Batching" (Ultralytics glossary), "Cómo funciona la
+//         planificación a nivel de iteración" and "Límites y técnicas
+//         complementarias": long prompts are prefilled in chunks that share a
+//         step with other sequences' decode.
+//
+// Matrix-core layout (v_mfma_f32_16x16x32_bf16, checked on the device): lane l
+// with n = l % 16 and g = l / 16 supplies row n of A and column n of B, each as
+// 8 bf16 of the k-slots of group g, and receives D[4g + j][n], j = 0..3.
+//
+// Both kernels compute the transposed products
+//     S^T = K Q^T        (A = 16 keys of a block x 32 dims, B = Q^T)
+//     O^T += V^T P^T     (A = V^T: 16 dims x 32 keys, B = P^T)
+// so that every per-row quantity (running max, sum, the row's output) lives in
+// the lanes whose n is that row, and the P^T operand is exactly the S^T result
+// of two blocks: lane (n, g) holds keys 4g..4g+3 of each block for row n.
+// V is stored token-major in the pool, so V^T is formed with the gfx950
+// transposed LDS read ds_read_tr16_b64: within each 16-lane group, lane i gets
+// element i % 4 of the 4-element segments addressed by lanes 4j + i/4
+// (j = 0..3).  Lane s of group g therefore points at V[key 4g + s/4][dims
+// 16c + 4(s%4) ..], and receives V[key 4g + j][dim 16c + s] for j = 0..3.
+//
+// P is split into a bf16 high part and a bf16 remainder, two MFMAs each, so
+// that the probabilities keep ~16 significant bits: a plain bf16 P would put an
+// error of up to 2^-9 |v| on short contexts.  Masked keys are removed by select
+// (score -inf, V row 0), never by multiplying, so NaN in unused slots cannot
+// reach the output.
+#include "pkv_device.h"
+
+namespace {
+
+using pkvd::u32x4;
+using pkvd::kBlock;
+using pkvd::kNegBig;
+using pkvd::kPlanHdr;
+using pkvd::fast_exp2;
+using pkvd::len_ok;
+using pkvd::plan_matches;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kWaves = 4;
+
+__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& w) { return __builtin_bit_cast(bf16x8, w); }
+
+__device__ __forceinline__ u32x4 load16_nt(const char* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// Transposed read of one 4-key x 16-dim piece of V from LDS (see the header).
+__device__ __forceinline__ s16x4 lds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+
+__device__ __forceinline__ bf16x8 join(const s16x4& lo, const s16x4& hi) {
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// ---------------------------------------------------------------------------
+// Decode for a query-head group.  One workgroup per (unit, KV head), where a
+// unit is a (sequence, 512-token partition) of the plan (longest first).  The
+// G query heads of the group are the 16 MFMA rows (rows >= G hold q = 0 and are
+// never written).  The unit's blocks are dealt to the 4 waves in pairs; a wave
+// loads a pair's K tiles straight into the A-operand layout (lane (n, g) reads
+// 16 B of key n at dims 32c + 8g), the V tiles with 1 KiB coalesced loads into
+// its own LDS area (token rows, padded), and forms V^T with transposed reads.
+// Each wave keeps an online softmax per row; the waves are merged through LDS
+// with the log-sum-exp rule, and the unit writes the output rows (one-partition
+// sequences) or (max, sum, accumulator) partials for the merge kernel -- the
+// same partial format as the VALU decode kernel.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void decode_group_mfma_kernel(pkv_decode_args a) {
+  constexpr int KC = D / 32;            // 32-dim chunks of q.k
+  constexpr int DC = D / 16;            // 16-dim chunks of the output
+  constexpr int RB = D * 2;             // bytes per key row
+  constexpr int VROW = RB + 32;         // padded LDS row of V
+  constexpr int NLD = 16 * RB / 1024;   // 1 KiB loads per V tile
+  constexpr int OROW = D + 4;           // padded LDS row (floats) of the wave merge
+  constexpr int kVBytes = kWaves * 2 * kBlock * VROW;
+  constexpr int kOBytes = kWaves * 16 * OROW * 4;
+  constexpr int kSmem = kVBytes > kOBytes ? kVBytes : kOBytes;
+  constexpr int64_t kTile = static_cast<int64_t>(kBlock) * RB;
+  __shared__ __align__(16) char smem[kSmem];
+  __shared__ float sm_ml[kWaves][16][2];
+  __shared__ int sm_bad[kWaves];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;
+  const int g = lane >> 4;
+
+  const int32_t Hq = a.num_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
+  const int32_t u = static_cast<int32_t>(blockIdx.x / static_cast<uint32_t>(Hkv));
+  const int32_t kvh = static_cast<int32_t>(blockIdx.x - static_cast<uint32_t>(u) * Hkv);
+  const int32_t* plan = a.plan;
+  if (!plan_matches(plan, a) || u >= plan[0]) return;
+  const int32_t s = plan[kPlanHdr + 2 * u];
+  const int32_t p = plan[kPlanHdr + 2 * u + 1];
+  const int32_t ctx = a.context_lens[s];
+  const int32_t np_s = (ctx + kPartTokens - 1) / kPartTokens;
+  const int32_t nblk = (ctx + kBlock - 1) / kBlock;
+  const int32_t blk_begin = p * (kPartTokens / kBlock);
+  const int32_t blk_end = min(nblk, blk_begin + kPartTokens / kBlock);
+
+  const int64_t block_bytes = static_cast<int64_t>(Hkv) * kTile;
+  const char* __restrict__ kc = reinterpret_cast<const char*>(a.k_cache) + kvh * kTile;
+  const char* __restrict__ vc = reinterpret_cast<const char*>(a.v_cache) + kvh * kTile;
+  const int32_t* __restrict__ table = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq;
+
+  // Q^T as the B operand: lane (n, g) holds dims 32c + 8g .. +8 of head kvh*G + n.
+  bf16x8 qb[KC];
+  {
+    const int hr = n < G ? n : 0;
+    const char* qrow = reinterpret_cast<const char*>(a.q) +
+                       ((static_cast<int64_t>(s) * Hq + kvh * G + hr) * D) * 2;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 64 * c + 16 * g);
+      if (n >= G) w = u32x4{0, 0, 0, 0};
+      qb[c] = as_bf16x8(w);
+    }
+  }
+
+  f32x4 o[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = kNegBig, lsum = 0.f;
+  bool bad = false;
+  char* vs = smem + wave * (2 * kBlock * VROW);
+
+  int32_t nxt[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int32_t j = blk_begin + 2 * wave + b;
+    nxt[b] = j < blk_end ? table[j] : 0;
+  }
+  for (int32_t j0 = blk_begin + 2 * wave; j0 < blk_end; j0 += 2 * kWaves) {
+    u32x4 kt[2][KC], vt[2][NLD];
+    bool have[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      have[b] = j0 + b < blk_end;
+      if (have[b]) {
+        int32_t id = nxt[b];
+        if (static_cast<uint32_t>(id) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; id = 0; }
+        const char* kp = kc + id * block_bytes;
+        const char* vp = vc + id * block_bytes;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) kt[b][c] = load16_nt(kp + n * RB + 64 * c + 16 * g);
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) vt[b][i] = load16_nt(vp + 1024 * i + 16 * lane);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int32_t j = j0 + 2 * kWaves + b;
+      nxt[b] = j < blk_end ? table[j] : 0;
+    }
+
+    // scores S^T (keys x rows), base-2 units, masked keys -inf
+    float sc[2][4];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      if (have[b]) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < KC; ++c) acc = mfma(as_bf16x8(kt[b][c]), qb[c], acc);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int32_t t = (j0 + b) * kBlock + 4 * g + jj;
+          sc[b][jj] = t < ctx ? acc[jj] * a.scale_log2 : -INFINITY;
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) sc[b][jj] = -INFINITY;
+      }
+    }
+    float mx = sc[0][0];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) mx = fmaxf(mx, sc[b][jj]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(m, mx);
+    const float alpha = fast_exp2(m - mnew);
+    m = mnew;
+    bf16x8 ph, pl;
+    float ps = 0.f;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float pr = fast_exp2(sc[b][jj] - m);
+        ps += pr;
+        const __bf16 hi = static_cast<__bf16>(pr);
+        ph[4 * b + jj] = hi;
+        pl[4 * b + jj] = static_cast<__bf16>(pr - static_cast<float>(hi));
+      }
+    lsum = lsum * alpha + ps;
+
+    // V tiles into this wave's LDS rows; keys past the context (or a missing
+    // second block) are stored as 0.  LDS operations of one wave execute in
+    // order, so the transposed reads below see these writes, and the next
+    // iteration's writes come after these reads.
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const int off = 1024 * i + 16 * lane;
+        const int tok = off / RB, col = off % RB;
+        u32x4 w = vt[b][i];
+        if (!have[b] || (j0 + b) * kBlock + tok >= ctx) w = u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4*>(vs + (b * kBlock + tok) * VROW + col) = w;
+      }
+    __builtin_amdgcn_wave_barrier();
+
+    // O^T += V^T P^T, one 16-dim chunk at a time
+    const char* tr0 = vs + (4 * g + (n >> 2)) * VROW + 8 * (n & 3);
+    const char* tr1 = tr0 + kBlock * VROW;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      const bf16x8 va = join(lds_read_tr(tr0 + 32 * c), lds_read_tr(tr1 + 32 * c));
+      f32x4 acc = o[c] * alpha;
+      acc = mfma(va, ph, acc);
+      o[c] = mfma(va, pl, acc);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+
+  // merge the four waves through LDS (the V areas are reused)
+  __syncthreads();
+  float* so = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int c = 0; c < DC; ++c)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) so[(wave * 16 + n) * OROW + 16 * c + 4 * g + jj] = o[c][jj];
+  if (g == 0) { sm_ml[wave][n][0] = m; sm_ml[wave][n][1] = lsum; }
+  if (lane == 0) sm_bad[wave] = bad ? 1 : 0;
+  __syncthreads();
+  const bool any_bad = (sm_bad[0] | sm_bad[1] | sm_bad[2] | sm_bad[3]) != 0;
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    const int r = idx / D, d = idx - (idx / D) * D;
+    float M = sm_ml[0][r][0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_ml[w][r][0]);
+    float L = 0.f, acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = fast_exp2(sm_ml[w][r][0] - M);
+      L += sm_ml[w][r][1] * f;
+      acc += so[(w * 16 + r) * OROW + d] * f;
+    }
+    if (any_bad) { acc = __builtin_nanf(""); L = __builtin_nanf(""); }
+    const int32_t h = kvh * G + r;
+    if (np_s == 1) {
+      a.out[(static_cast<int64_t>(s) * Hq + h) * D + d] = acc / L;
+    } else {
+      const int64_t pidx = (static_cast<int64_t>(s) * Hq + h) * a.num_partitions + p;
+      a.part_acc[pidx * D + d] = acc;
+      if (d == 0) { a.part_ml[2 * pidx] = M; a.part_ml[2 * pidx + 1] = L; }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Causal chunked prefill.  Sequence s owns query tokens q0..q1-1 (n = q1 - q0
+// of them, the last n tokens of its context of ctx tokens, already written to
+// the cache); query i sits at position ctx - n + i and attends keys 0..ctx-n+i.
+// The rows of KV head kvh are (query i, head kvh*G + r) for r < G, numbered
+// token-major so that a 16-row MFMA tile spans few positions; a workgroup takes
+// 128 consecutive rows (4 waves x 2 tiles).  The workgroup walks the keys two
+// blocks (32 keys) at a time: all 256 threads stage the pair's K and V tiles
+// into LDS (double-buffered, one barrier per pair), and every wave reads K in
+// the A-operand layout and V^T with transposed reads, shared by its two row
+// tiles.  Pairs past a tile's last causal position are skipped for that tile.
+// Workgroup b takes group (s, kvh) = b % (S*Hkv) and row tile b / (S*Hkv), so
+// when S*Hkv is a multiple of 8 the tiles of one group share an XCD (dispatch
+// is round-robin over the 8 XCDs) and read the same K/V from that XCD's L2.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void prefill_chunk_mfma_kernel(pkv_prefill_args a) {
+  constexpr int KC = D / 32;
+  constexpr int DC = D / 16;
+  constexpr int RB = D * 2;
+  constexpr int KROW = RB + 16;          // padded LDS row of K
+  constexpr int VROW = RB + 32;          // padded LDS row of V
+  constexpr int kTiles = 2;              // 16-row tiles per wave
+  constexpr int64_t kTile = static_cast<int64_t>(kBlock) * RB;
+  constexpr int kChunks = 4 * kBlock * RB / 16;   // 16-byte chunks of a pair's K and V tiles
+  constexpr int kPerThread = kChunks / 256;
+  static_assert(kChunks % 256 == 0, "pair staging");
+  __shared__ __align__(16) char sk[2][2 * kBlock * KROW];
+  __shared__ __align__(16) char sv[2][2 * kBlock * VROW];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;
+  const int g = lane >> 4;
+
+  const int32_t Hq = a.num_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
+  const int32_t SG = a.num_seqs * Hkv;
+  const int32_t sg = static_cast<int32_t>(blockIdx.x % static_cast<uint32_t>(SG));
+  const int32_t rt = static_cast<int32_t>(blockIdx.x / static_cast<uint32_t>(SG));
+  const int32_t s = sg / Hkv, kvh = sg - (sg / Hkv) * Hkv;
+  const int32_t q0 = a.query_start_loc[s], q1 = a.query_start_loc[s + 1];
+  if (q0 < 0 || q1 < q0 || q1 > a.num_query_tokens || q1 - q0 > a.max_query_len) return;   // nowhere safe to write
+  const int32_t nq = q1 - q0;
+  const int32_t rows = nq * G;
+  const int32_t r0 = rt * kPrefillRowsPerWg;
+  if (r0 >= rows) return;
+  const int32_t r_end = min(rows, r0 + kPrefillRowsPerWg);
+  const int32_t ctx = a.context_lens[s];
+  if (ctx < nq || !len_ok(ctx, a.max_context_len, a.max_blocks_per_seq)) {
+    for (int idx = threadIdx.x; idx < (r_end - r0) * D; idx += 256) {
+      const int32_t r = r0 + idx / D, d = idx % D;
+      a.out[((static_cast<int64_t>(q0) + r / G) * Hq + kvh * G + r % G) * D + d] = __builtin_nanf("");
+    }
+    return;
+  }
+  const int32_t first_pos = ctx - nq;            // position of query 0
+  const int32_t* __restrict__ table = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq;
+  const int64_t block_bytes = static_cast<int64_t>(Hkv) * kTile;
+  const char* __restrict__ kc = reinterpret_cast<const char*>(a.k_cache) + kvh * kTile;
+  const char* __restrict__ vc = reinterpret_cast<const char*>(a.v_cache) + kvh * kTile;
+
+  // this lane's rows (one per tile) and their key limits; invalid rows: limit 0, q = 0
+  bf16x8 qb[kTiles][KC];
+  int32_t lim[kTiles];
+  int32_t tile_lim[kTiles];      // keys any row of the tile needs (uniform)
+#pragma unroll
+  for (int tt = 0; tt < kTiles; ++tt) {
+    const int32_t rbase = r0 + wave * 32 + tt * 16;
+    const int32_t r = rbase + n;
+    const bool valid = r < r_end;
+    const int32_t i = valid ? r / G : 0;
+    lim[tt] = valid ? first_pos + i + 1 : 0;
+    const int32_t rlast = min(r_end, rbase + 16) - 1;
+    tile_lim[tt] = rlast >= rbase ? first_pos + rlast / G + 1 : 0;
+    const char* qrow = reinterpret_cast<const char*>(a.q) +
+                       ((static_cast<int64_t>(q0) + i) * Hq + kvh * G + (valid ? r % G : 0)) * D * 2;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 64 * c + 16 * g);
+      if (!valid) w = u32x4{0, 0, 0, 0};
+      qb[tt][c] = as_bf16x8(w);
+    }
+  }
+  const int32_t wg_lim = first_pos + (r_end - 1) / G + 1;      // keys the workgroup needs
+  const int32_t npairs = (wg_lim + 2 * kBlock - 1) / (2 * kBlock);
+  const int32_t nblk = (ctx + kBlock - 1) / kBlock;
+
+  f32x4 o[kTiles][DC];
+  float m[kTiles], lsum[kTiles];
+#pragma unroll
+  for (int tt = 0; tt < kTiles; ++tt) {
+    m[tt] = kNegBig;
+    lsum[tt] = 0.f;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) o[tt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  bool bad = false;
+
+  // staging: thread chunk q -> tile q / (kBlock*RB/16) in {K0, K1, V0, V1}
+  u32x4 stage[kPerThread];
+  auto load_pair = [&](int32_t pp) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int q = threadIdx.x + 256 * i;
+      const int which = q / (kBlock * RB / 16);
+      const int off = (q % (kBlock * RB / 16)) * 16;
+      const int32_t j = 2 * pp + (which & 1);
+      u32x4 w = u32x4{0, 0, 0, 0};
+      if (j < nblk) {
+        int32_t id = table[j];
+        if (static_cast<uint32_t>(id) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; id = 0; }
+        const char* base = (which < 2 ? kc : vc) + id * block_bytes;
+        w = load16_nt(base + off);
+      }
+      stage[i] = w;
+    }
+  };
+  auto store_pair = [&](int32_t pp, int buf) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int q = threadIdx.x + 256 * i;
+      const int which = q / (kBlock * RB / 16);
+      const int off = (q % (kBlock * RB / 16)) * 16;
+      const int tok = off / RB, col = off % RB;
+      const int b = which & 1;
+      u32x4 w = stage[i];
+      if (which < 2) {
+        *reinterpret_cast<u32x4*>(&sk[buf][(b * kBlock + tok) * KROW + col]) = w;
+      } else {
+        if ((2 * pp + b) * kBlock + tok >= ctx) w = u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4*>(&sv[buf][(b * kBlock + tok) * VROW + col]) = w;
+      }
+    }
+  };
+
+  load_pair(0);
+  store_pair(0, 0);
+  __syncthreads();
+  for (int32_t pp = 0; pp < npairs; ++pp) {
+    const int buf = pp & 1;
+    if (pp + 1 < npairs) load_pair(pp + 1);
+    const int32_t key0 = pp * 2 * kBlock;
+    if (key0 < tile_lim[0] || key0 < tile_lim[1]) {
+      // K in the A-operand layout: key 16b + n, dims 32c + 8g
+      bf16x8 ka[2][KC];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+          ka[b][c] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sk[buf][(b * kBlock + n) * KROW + 64 * c + 16 * g]));
+      bf16x8 va[DC];
+      const char* tr0 = &sv[buf][(4 * g + (n >> 2)) * VROW + 8 * (n & 3)];
+#pragma unroll
+      for (int c = 0; c < DC; ++c)
+        va[c] = join(lds_read_tr(tr0 + 32 * c), lds_read_tr(tr0 + kBlock * VROW + 32 * c));
+#pragma unroll
+      for (int tt = 0; tt < kTiles; ++tt) {
+        if (key0 >= tile_lim[tt]) continue;
+        float sc[2][4];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < KC; ++c) acc = mfma(ka[b][c], qb[tt][c], acc);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int32_t t = key0 + b * kBlock + 4 * g + jj;
+            sc[b][jj] = t < lim[tt] ? acc[jj] * a.scale_log2 : -INFINITY;
+          }
+        }
+        float mx = sc[0][0];
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) mx = fmaxf(mx, sc[b][jj]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(m[tt], mx);
+        const float alpha = fast_exp2(m[tt] - mnew);
+        m[tt] = mnew;
+        bf16x8 ph, pl;
+        float ps = 0.f;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const float pr = fast_exp2(sc[b][jj] - mnew);
+            ps += pr;
+            const __bf16 hi = static_cast<__bf16>(pr);
+            ph[4 * b + jj] = hi;
+            pl[4 * b + jj] = static_cast<__bf16>(pr - static_cast<float>(hi));
+          }
+        lsum[tt] = lsum[tt] * alpha + ps;
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+          f32x4 acc = o[tt][c] * alpha;
+          acc = mfma(va[c], ph, acc);
+          o[tt][c] = mfma(va[c], pl, acc);
+        }
+      }
+    }
+    if (pp + 1 < npairs) store_pair(pp + 1, buf ^ 1);
+    __syncthreads();
+  }
+
+  // a bad block id anywhere in the workgroup's range poisons its rows
+  const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0;
+#pragma unroll
+  for (int tt = 0; tt < kTiles; ++tt) {
+    float L = lsum[tt];
+    L += __shfl_xor(L, 16);
+    L += __shfl_xor(L, 32);
+    const int32_t r = r0 + wave * 32 + tt * 16 + n;
+    if (r >= r_end) continue;
+    const float inv = any_bad ? __builtin_nanf("") : 1.f / L;
+    float* orow = a.out + ((static_cast<int64_t>(q0) + r / G) * Hq + kvh * G + r % G) * D;
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      const f32x4 v = o[tt][c] * inv;
+      *reinterpret_cast<f32x4*>(orow + 16 * c + 4 * g) = v;
+    }
+  }
+}
+
+}  // namespace
+
+int pkv_launch_decode_group(const pkv_decode_args& a, void* stream) {
+  const int64_t grid = static_cast<int64_t>(a.num_seqs) * a.num_partitions * a.num_kv_heads;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (a.head_dim == 128) {
+    hipLaunchKernelGGL((decode_group_mfma_kernel<128>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((decode_group_mfma_kernel<64>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+int pkv_launch_prefill(const pkv_prefill_args& a, void* stream) {
+  const int32_t group = a.num_heads / a.num_kv_heads;
+  const int64_t tiles = (static_cast<int64_t>(a.max_query_len) * group + kPrefillRowsPerWg - 1) / kPrefillRowsPerWg;
+  const int64_t grid = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * tiles;
+  if (grid == 0) return hipSuccess;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (a.head_dim == 128) {
+    hipLaunchKernelGGL((prefill_chunk_mfma_kernel<128>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((prefill_chunk_mfma_kernel<64>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}

@@ -251,4 +251,17 @@ def random_small(seed: int, num_seqs: int, max_ctx: int, hq: int, hkv: int, d: i
                          pool_factor=pool_factor)
 
 
+def random_prefill(seed: int, ctxs, n_queries, hq: int, hkv: int, d: int, pool_factor: float = 1.3) -> Workload:
+    """Chunked-prefill parity cases: sequence s has ctxs[s] cached tokens, the last
+    n_queries[s] of which are its chunk's queries (bf16).  Every sequence also
+    carries one decode query."""
+    w = _plain_decode(f"prefill{seed}", seed + 104729, ctxs, hq, hkv, d, "bf16", pool_factor=pool_factor)
+    rng = np.random.default_rng(seed + 31337)
+    nq = np.asarray(n_queries, dtype=np.int32)
+    w.chunk_seqs = list(range(len(ctxs)))
+    w.chunk_q = _normal(rng, (int(nq.sum()), hq, d), "bf16")
+    w.chunk_query_start_loc = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    return w
+
+
 WORKLOADS = {1: tiny, 2: shaped_13b, 3: gqa, 4: parallel_sampling, 5: long_mix}

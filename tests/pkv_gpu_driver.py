@@ -85,3 +85,23 @@ class GpuReplay:
                                 mcl, float(w.scale))
         torch.cuda.synchronize()
         return out.cpu().numpy(), tables, lens
+
+    def prefill(self, seqs=None, q=None, qsl=None, tables=None, lens=None, max_context_len=None,
+                max_query_len=None):
+        w = self.w
+        seqs = w.chunk_seqs if seqs is None else seqs
+        q = w.chunk_q if q is None else q
+        qsl = w.chunk_query_start_loc if qsl is None else qsl
+        if tables is None:
+            tables, lens = self.tables(seqs)
+        mcl = int(max(lens)) if max_context_len is None else max_context_len
+        mql = int(np.max(np.diff(qsl))) if max_query_len is None else max_query_len
+        qd = rows_to_device(q, self.dev)
+        out = torch.full((q.shape[0], w.num_heads, w.head_dim), -7.0, dtype=torch.float32, device=self.dev)
+        PK.pkv_attention_prefill_chunk(out, qd, torch.from_numpy(np.ascontiguousarray(qsl, dtype=np.int32)).to(self.dev),
+                                       mql, self.k_pool, self.v_pool,
+                                       torch.from_numpy(np.ascontiguousarray(tables)).to(self.dev),
+                                       torch.from_numpy(np.ascontiguousarray(lens, dtype=np.int32)).to(self.dev),
+                                       mcl, float(w.scale))
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), tables, lens

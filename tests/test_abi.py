@@ -128,3 +128,27 @@ def test_allocator_errors_are_status_codes(P):
     with pytest.raises(P.PkvError) as e:
         a.seq_free(99)
     assert e.value.status == P.PKV_ERR_UNKNOWN_SEQ
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=0), 3), (dict(head_dim=96), 3), (dict(block_size=8), 3), (dict(num_heads=6, num_kv_heads=4), 1),
+    (dict(q=None), 1), (dict(max_query_len=-1), 1), (dict(out=17), 1), (dict(num_blocks=0), 1),
+    (dict(scale=float("inf")), 1),
+])
+def test_prefill_rejects_bad_arguments(P, kw, code):
+    args = dict(out=16, q=32, qsl=48, tq=8, mql=4, k_cache=64, v_cache=80, tables=96, mb=4, lens=112, num_seqs=2,
+                num_heads=8, num_kv_heads=2, head_dim=128, block_size=16, num_blocks=8, mcl=64, scale=0.1,
+                dtype=1, max_query_len=4)
+    args.update(kw)
+    st = _lib(P).pkv_attention_prefill_chunk(
+        args["out"], args["q"], args["qsl"], args["tq"], args["max_query_len"], args["k_cache"], args["v_cache"],
+        args["tables"], args["mb"], args["lens"], args["num_seqs"], args["num_heads"], args["num_kv_heads"],
+        args["head_dim"], args["block_size"], args["num_blocks"], args["mcl"], args["scale"], args["dtype"], None)
+    assert st == code
+    assert _lib(P).pkv_last_error().decode().startswith("pkv_attention_prefill_chunk")
+
+
+def test_prefill_with_no_queries_is_a_no_op(P):
+    lib = _lib(P)
+    assert lib.pkv_attention_prefill_chunk(None, None, None, 0, 0, None, None, None, 4, None, 3, 8, 2, 128, 16,
+                                           8, 64, 0.1, 1, None) == 0

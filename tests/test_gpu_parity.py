@@ -290,3 +290,97 @@ def test_partition_boundaries(ctxs):
     g, r = GpuReplay(w), _oracle(w)
     err = _attn_err(g, r, w)
     assert err <= TOL["bf16"], err
+
+
+# ---------------------------------------------------------------------------
+# Query-head groups (MFMA decode kernel for bf16 groups of 2..16 heads; the
+# VALU kernel above 16) and causal chunked prefill (MFMA kernel).
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed,S,max_ctx,hq,hkv,d", [
+    (71, 9, 1300, 16, 1, 128),    # G = 16: the whole MFMA row tile
+    (72, 7, 600, 6, 2, 64),       # G = 3
+    (73, 5, 900, 32, 1, 128),     # G = 32: VALU kernel
+    (74, 12, 40, 16, 8, 128),     # G = 2, short contexts (P rounding matters most)
+])
+def test_query_head_groups(seed, S, max_ctx, hq, hkv, d):
+    print(f"case: groups seed={seed} H={hq}/{hkv} d={d}", flush=True)
+    w = W.random_small(seed, S, max_ctx, hq, hkv, d, "bf16")
+    g, r = GpuReplay(w), _oracle(w)
+    err = _attn_err(g, r, w)
+    assert err <= TOL["bf16"], err
+
+
+def _prefill_ref(r, w, rows=None):
+    tables = [r.alloc.block_table(s) for s in w.chunk_seqs]
+    lens = [r.alloc.num_tokens(s) for s in w.chunk_seqs]
+    return O.prefill_chunk_attention(w.chunk_q, w.chunk_query_start_loc, r.k_pool, r.v_pool, tables, lens, w.scale)
+
+
+PREFILL = [
+    # seed, contexts, chunk lengths, Hq, Hkv, d
+    (61, [60, 300, 700], [37, 64, 100], 8, 2, 128),
+    (62, [16, 33, 129, 1], [16, 1, 129, 1], 4, 4, 64),      # whole prompt, single query, MHA
+    (63, [1000], [200], 16, 2, 128),
+    (64, [90, 45], [90, 5], 32, 1, 128),                    # MQA: 32 heads per KV head
+]
+
+
+@pytest.mark.parametrize("seed,ctxs,nqs,hq,hkv,d", PREFILL)
+def test_prefill_chunks(seed, ctxs, nqs, hq, hkv, d):
+    print(f"case: prefill seed={seed} ctx={ctxs} n={nqs} H={hq}/{hkv} d={d}", flush=True)
+    w = W.random_prefill(seed, ctxs, nqs, hq, hkv, d)
+    g, r = GpuReplay(w), _oracle(w)
+    out, _, _ = g.prefill()
+    ref = _prefill_ref(r, w)
+    assert np.isfinite(out).all()
+    err = float(np.abs(out - ref).max())
+    assert err <= TOL["bf16"], err
+
+
+def test_prefill_nan_in_unused_slots_never_reaches_the_output():
+    w = W.random_prefill(65, [70, 33], [20, 33], 8, 2, 128)
+    print("case: prefill nan poison", flush=True)
+    g = GpuReplay(w, pool_fill=float("nan"))
+    r = _oracle(w, pool_fill=np.uint16(0x7FC0))
+    out, _, _ = g.prefill()
+    err = float(np.abs(out - _prefill_ref(r, w)).max())
+    assert err <= TOL["bf16"], err
+
+
+def test_prefill_bad_rows():
+    """A chunk longer than its context gets NaN rows; a query range outside the
+    query buffer is not written; other sequences are computed as before."""
+    w = W.random_prefill(66, [50, 80, 64], [10, 20, 30], 8, 2, 128)
+    print("case: prefill bad rows", flush=True)
+    g = GpuReplay(w)
+    out, tables, lens = g.prefill()
+    l2 = np.array(lens).copy()
+    l2[0] = 5                                   # context shorter than the 10-query chunk
+    out2, _, _ = g.prefill(tables=tables, lens=l2, max_context_len=int(max(lens)))
+    qsl = w.chunk_query_start_loc
+    assert np.isnan(out2[qsl[0]:qsl[1]]).all()
+    assert np.array_equal(out2[qsl[1]:], out[qsl[1]:])
+    qsl3 = qsl.copy()
+    qsl3[3] = qsl3[3] + 5                       # last range runs past the buffer: skipped
+    out3, _, _ = g.prefill(qsl=qsl3, tables=tables, lens=lens, max_query_len=35)
+    assert (out3[qsl[2]:] == -7.0).all()
+    assert np.array_equal(out3[:qsl[2]], out[:qsl[2]])
+
+
+def test_long_context_prefill_chunks_sampled():
+    w = W.long_mix()
+    print("case: long mix prefill 4x512 on 8192", flush=True)
+    g, r = GpuReplay(w), _oracle(w)
+    out, _, _ = g.prefill()
+    assert np.isfinite(out).all()
+    qsl = w.chunk_query_start_loc
+    err = 0.0
+    for c, s in enumerate(w.chunk_seqs):
+        table, ctx = r.alloc.block_table(s), r.alloc.num_tokens(s)
+        n = qsl[c + 1] - qsl[c]
+        for i in (0, 1, 255, n - 2, n - 1):
+            # a chunk query equals a decode query over the prefix ending at its position
+            ref = O.decode_attention(w.chunk_q[qsl[c] + i][None], r.k_pool, r.v_pool, [table], [ctx - n + i + 1],
+                                     w.scale)
+            err = max(err, float(np.abs(out[qsl[c] + i] - ref[0]).max()))
+    assert err <= TOL["bf16"], err

@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time for the oracle sample")
+    ap.add_argument("--workload", default="13b", choices=["13b", "gqa", "fork", "long"],
+                    help="13b: the headline decode step (default).  gqa / fork / long: kernel measurements on the "
+                         "grouped-query, parallel-sampling and long-context + chunked-prefill batches")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run pkv_copy_blocks over 4096 whole blocks (a plain copy of known size, "
                          "used to scale the FETCH_SIZE / WRITE_SIZE counters)")
@@ -119,6 +122,128 @@ def cpu_baseline(seed: int, target_s: float):
                       f"40 heads x 128, bf16 inputs, float64 math), {el:.1f} s; scaled to a 40-layer step"}
 
 
+def _timed(fn, reps, stream):
+    """Average duration (us) of fn() over reps calls, HIP events on `stream`."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / reps * 1e3
+
+
+def secondary(args):
+    """Kernel measurements on the other batches (one JSON line each; not the headline).
+
+    gqa:  256 seqs, 64 query / 8 KV heads, d 128, bf16, ctx U[128, 4096], pool 1.2x
+          shuffled, 8 layer pools: decode (MFMA group kernel) per layer.
+    fork: 32 groups x 8 samples of a 1000-token prompt, tails U[1, 512], 40 heads,
+          4 layer pools: the copy-on-write copies, then decode over the shared blocks.
+    long: 16 seqs at ctx 32768 (split over 64 partitions each) + 4 prefill chunks of
+          512 causal queries ending 8192-token contexts, 32 / 8 heads, 4 layer pools.
+    """
+    import torch
+    import paged_kv_cache_171_amd as PK
+    import pkv_workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    P, D = 16, 128
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+    name = args.workload
+    w = {"gqa": lambda: W.gqa(with_rows=False), "fork": lambda: W.parallel_sampling(with_rows=False),
+         "long": lambda: W.long_mix(with_rows=False)}[name]()
+    L = {"gqa": 8, "fork": 4, "long": 4}[name]
+    Hq, Hkv, NB = w.num_heads, w.num_kv_heads, w.num_blocks
+    alloc = PK.BlockAllocator(NB, P, w.initial_free_order)
+    pairs = []
+    for op in w.ops:                      # the allocator script: tables, slots and copy pairs
+        if op[0] == "create":
+            alloc.seq_create()
+        elif op[0] == "fork":
+            alloc.seq_fork(op[1])
+        elif op[0] == "append":
+            pairs += alloc.seq_append_slots(op[1], op[2])[1]
+    seqs = w.decode_seqs
+    lens_h = np.array([alloc.seq_block_table(s)[1] for s in seqs], dtype=np.int32)
+    MB = int(-(-lens_h.max() // P))
+    tables_h, _ = alloc.block_tables(seqs, MB)
+    pools = [(randn(NB, Hkv, P, D), randn(NB, Hkv, P, D)) for _ in range(L)]
+    q = randn(len(seqs), Hq, D)
+    out = torch.empty(len(seqs), Hq, D, dtype=torch.float32, device=dev)
+    td, ld = torch.from_numpy(tables_h).to(dev), torch.from_numpy(lens_h).to(dev)
+    mcl = int(lens_h.max())
+    ws = PK.workspace_for(len(seqs), Hq, D, mcl, device=dev)
+    plan = PK.plan_for(ld, MB, mcl)
+    scale = 1.0 / math.sqrt(D)
+    reps = max(args.steps, 3)
+
+    def decode_all():
+        for kp, vp in pools:
+            PK.pkv_attention_decode(out, q, kp, vp, td, ld, mcl, scale, workspace=ws, plan=plan)
+
+    for _ in range(max(args.warmup, 1)):
+        decode_all()
+    torch.cuda.synchronize()
+    dec_us = _timed(decode_all, reps, stream) / L
+    kv_logical = int(lens_h.sum()) * 2 * Hkv * D * 2
+    res = {"workload": name, "layers": L, "num_seqs": len(seqs), "heads": f"{Hq}/{Hkv}", "head_dim": D,
+           "mean_ctx": round(float(lens_h.mean()), 1), "decode_us_per_layer": round(dec_us, 2),
+           "decode_kv_gbps": round(kv_logical / dec_us / 1e3, 1),
+           "decode_hbm_peak_frac": round(kv_logical / dec_us / 1e3 / HBM_PEAK_GBPS, 4),
+           "decode_tokens_per_s_per_layer": round(len(seqs) / dec_us * 1e6, 1),
+           "kernel": "decode_group_mfma_kernel" if 2 <= Hq // Hkv <= 16 else "decode_valu_kernel"}
+    if name == "fork":
+        unique = len({int(b) for s, c in zip(range(len(seqs)), lens_h) for b in tables_h[s, :-(-int(c) // P)]})
+        res["kv_unique_bytes"] = unique * P * 2 * Hkv * D * 2
+        res["kv_logical_bytes"] = kv_logical
+        sd = torch.tensor(pairs, dtype=torch.int32, device=dev)
+        kp, vp = pools[0]
+
+        def cow():
+            PK.pkv_copy_blocks(kp, vp, sd)
+        cow()
+        torch.cuda.synchronize()
+        cow_us = _timed(cow, reps, stream)
+        cow_bytes = 2 * 2 * len(pairs) * Hkv * P * D * 2
+        res.update({"cow_pairs": len(pairs), "cow_us": round(cow_us, 2),
+                    "cow_gbps_read_plus_write": round(cow_bytes / cow_us / 1e3, 1)})
+    if name == "long":
+        cs = w.chunk_seqs
+        clens = np.array([alloc.seq_block_table(s)[1] for s in cs], dtype=np.int32)
+        cmb = int(-(-clens.max() // P))
+        ct, _ = alloc.block_tables(cs, cmb)
+        qsl = torch.from_numpy(w.chunk_query_start_loc).to(dev)
+        nq = np.diff(w.chunk_query_start_loc)
+        cq = randn(int(nq.sum()), Hq, D)
+        cout = torch.empty(int(nq.sum()), Hq, D, dtype=torch.float32, device=dev)
+        ctd, cld = torch.from_numpy(ct).to(dev), torch.from_numpy(clens).to(dev)
+
+        def prefill_all():
+            for kp, vp in pools:
+                PK.pkv_attention_prefill_chunk(cout, cq, qsl, int(nq.max()), kp, vp, ctd, cld, int(clens.max()),
+                                               scale)
+        prefill_all()
+        torch.cuda.synchronize()
+        pf_us = _timed(prefill_all, reps, stream) / L
+        # causal flops: q.k and p.v, 2 flops per multiply-add, per (query, head, visible key, dim)
+        keys = sum(int(c) * int(n) - int(n) * (int(n) - 1) // 2 for c, n in zip(clens, nq))
+        flops = 4 * Hq * D * keys
+        res.update({"prefill_us_per_layer": round(pf_us, 2), "prefill_tflops": round(flops / pf_us / 1e6, 1),
+                    "prefill_mfma_peak_frac": round(flops / pf_us / 1e6 / 2500.0, 4),
+                    "prefill_tokens_per_s_per_layer": round(int(nq.sum()) / pf_us * 1e6, 1),
+                    "prefill_kernel": "prefill_chunk_mfma_kernel"})
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -127,6 +252,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.workload != "13b":
+        secondary(args)
         return
 
     import torch

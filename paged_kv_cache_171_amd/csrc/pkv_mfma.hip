@@ -81,24 +81,45 @@ __device__ __forceinline__ bf16x8 join(const s16x4& lo, const s16x4& hi) {
 // Decode for a query-head group.  One workgroup per (unit, KV head), where a
 // unit is a (sequence, 512-token partition) of the plan (longest first).  The
 // G query heads of the group are the 16 MFMA rows (rows >= G hold q = 0 and are
-// never written).  The unit's blocks are dealt to the 4 waves in pairs; a wave
-// loads a pair's K tiles straight into the A-operand layout (lane (n, g) reads
-// 16 B of key n at dims 32c + 8g), the V tiles with 1 KiB coalesced loads into
-// its own LDS area (token rows, padded), and forms V^T with transposed reads.
+// never written).  The unit's blocks are dealt to the 4 waves in turn; per
+// block a wave
+//   - loads the K tile straight into the A-operand layout (lane (n, g) reads
+//     16 B of key n at dims 32c + 8g) and forms S^T = K Q^T (D/32 MFMAs),
+//   - moves the V tile into its own 16-row LDS tile by direct global->LDS
+//     loads (no registers), with the 16-byte slots of row r XOR-swizzled by
+//     2*(r / (256/row bytes) mod (slots/2)) so that the transposed reads hit
+//     every bank pair at most twice; rows of keys past the context are filled
+//     from key 0 of the block (finite data) and get probability 0,
+//   - forms V^T with one transposed read per 16 dims and accumulates
+//     O^T += V^T P^T with 16x16x16 MFMAs (P^T is exactly the S^T of the block).
 // Each wave keeps an online softmax per row; the waves are merged through LDS
 // with the log-sum-exp rule, and the unit writes the output rows (one-partition
 // sequences) or (max, sum, accumulator) partials for the merge kernel -- the
 // same partial format as the VALU decode kernel.
 // ---------------------------------------------------------------------------
+typedef short s16x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(const s16x4v& a, const s16x4v& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// 16-byte slot k of V row r lives at slot k ^ vswz(r) of the LDS tile.
 template <int D>
-__global__ __launch_bounds__(256) void decode_group_mfma_kernel(pkv_decode_args a) {
+__device__ __forceinline__ int vswz(int r) {
+  constexpr int kSlots = D * 2 / 16;            // 16-byte slots per row
+  constexpr int kRowsPerLine = 256 / (D * 2);   // rows per 256-byte bank line
+  return 2 * ((r / kRowsPerLine) % (kSlots / 2));
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 4) void decode_group_mfma_kernel(pkv_decode_args a) {
   constexpr int KC = D / 32;            // 32-dim chunks of q.k
   constexpr int DC = D / 16;            // 16-dim chunks of the output
   constexpr int RB = D * 2;             // bytes per key row
-  constexpr int VROW = RB + 32;         // padded LDS row of V
-  constexpr int NLD = 16 * RB / 1024;   // 1 KiB loads per V tile
+  constexpr int kSlots = RB / 16;
+  constexpr int NLD = kBlock * RB / 1024;   // 1 KiB direct-to-LDS loads per V tile
   constexpr int OROW = D + 4;           // padded LDS row (floats) of the wave merge
-  constexpr int kVBytes = kWaves * 2 * kBlock * VROW;
+  constexpr int kVBytes = kWaves * 2 * kBlock * RB;     // two V tiles per wave
   constexpr int kOBytes = kWaves * 16 * OROW * 4;
   constexpr int kSmem = kVBytes > kOBytes ? kVBytes : kOBytes;
   constexpr int64_t kTile = static_cast<int64_t>(kBlock) * RB;
@@ -129,6 +150,8 @@ __global__ __launch_bounds__(256) void decode_group_mfma_kernel(pkv_decode_args 
   const char* __restrict__ vc = reinterpret_cast<const char*>(a.v_cache) + kvh * kTile;
   const int32_t* __restrict__ table = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq;
 
+  char* vs = smem + wave * (2 * kBlock * RB);      // this wave's two V tiles
+
   // Q^T as the B operand: lane (n, g) holds dims 32c + 8g .. +8 of head kvh*G + n.
   bf16x8 qb[KC];
   {
@@ -143,116 +166,101 @@ __global__ __launch_bounds__(256) void decode_group_mfma_kernel(pkv_decode_args 
     }
   }
 
+  // per-lane pieces of the V tile traffic: DMA source offset (swizzled) and
+  // transposed-read address (key row 4g + n/4, dims 4(n%4) of each 16-dim chunk)
+  int dma_off[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int r = (1024 * i + 16 * lane) / RB, k = ((1024 * i + 16 * lane) % RB) / 16;
+    dma_off[i] = r * RB + 16 * (k ^ vswz<D>(r));
+  }
+  const int tr_row = 4 * g + (n >> 2);
+  const int tr_sw = vswz<D>(tr_row);
+  const int tr_k0 = (n & 3) >> 1;       // slot of dims 4(n%4) within a 32-byte chunk pair
+
   f32x4 o[DC];
 #pragma unroll
   for (int c = 0; c < DC; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = kNegBig, lsum = 0.f;
   bool bad = false;
-  char* vs = smem + wave * (2 * kBlock * VROW);
 
-  int32_t nxt[2];
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int32_t j = blk_begin + 2 * wave + b;
-    nxt[b] = j < blk_end ? table[j] : 0;
-  }
-  for (int32_t j0 = blk_begin + 2 * wave; j0 < blk_end; j0 += 2 * kWaves) {
-    u32x4 kt[2][KC], vt[2][NLD];
-    bool have[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      have[b] = j0 + b < blk_end;
-      if (have[b]) {
-        int32_t id = nxt[b];
-        if (static_cast<uint32_t>(id) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; id = 0; }
-        const char* kp = kc + id * block_bytes;
-        const char* vp = vc + id * block_bytes;
-#pragma unroll
-        for (int c = 0; c < KC; ++c) kt[b][c] = load16_nt(kp + n * RB + 64 * c + 16 * g);
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) vt[b][i] = load16_nt(vp + 1024 * i + 16 * lane);
-      }
-    }
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int32_t j = j0 + 2 * kWaves + b;
-      nxt[b] = j < blk_end ? table[j] : 0;
-    }
+  // The wave's block ids (at most kPartTokens/16/4 = 8 of them), one per lane,
+  // fetched once before the loop; each block takes its id with a lane read.
+  const int32_t nit = (blk_end - blk_begin - wave + kWaves - 1) / kWaves;
+  const int32_t my_ids = lane < nit ? table[blk_begin + wave + kWaves * lane] : 0;
 
-    // scores S^T (keys x rows), base-2 units, masked keys -inf
-    float sc[2][4];
+  // Loads of block `it`: K into registers, V into an LDS tile.  V rows of keys
+  // past the context are copied from key 0 of the block instead (finite data;
+  // their probabilities are 0), so the copies need no branches.
+  auto issue = [&](int32_t it, u32x4 (&kt)[KC], char* tile) {
+    const int32_t j = blk_begin + wave + kWaves * it;
+    int32_t id = __builtin_amdgcn_readlane(my_ids, it);
+    if (static_cast<uint32_t>(id) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; id = 0; }
+    const char* kp = kc + id * block_bytes;
+    const char* vp = vc + id * block_bytes;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      if (have[b]) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < KC; ++c) kt[c] = load16_nt(kp + n * RB + 64 * c + 16 * g);
+    const int32_t valid_rows = min(kBlock, ctx - j * kBlock);
 #pragma unroll
-        for (int c = 0; c < KC; ++c) acc = mfma(as_bf16x8(kt[b][c]), qb[c], acc);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int32_t t = (j0 + b) * kBlock + 4 * g + jj;
-          sc[b][jj] = t < ctx ? acc[jj] * a.scale_log2 : -INFINITY;
-        }
-      } else {
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) sc[b][jj] = -INFINITY;
-      }
+    for (int i = 0; i < NLD; ++i) {
+      const int src = (1024 * i + 16 * lane) / RB < valid_rows ? dma_off[i] : dma_off[i] % RB;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vp + src),
+                                       (__attribute__((address_space(3))) void*)(tile + 1024 * i), 16, 0, 0);
     }
-    float mx = sc[0][0];
+  };
+  // Online-softmax update of block `it` from its K registers and V tile.
+  auto compute = [&](int32_t it, const u32x4 (&kt)[KC], const char* tile) {
+    const int32_t j = blk_begin + wave + kWaves * it;
+    const int32_t valid_rows = min(kBlock, ctx - j * kBlock);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int c = 0; c < KC; ++c) acc = mfma(as_bf16x8(kt[c]), qb[c], acc);
+    float sc[4];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) mx = fmaxf(mx, sc[b][jj]);
+    for (int jj = 0; jj < 4; ++jj) sc[jj] = 4 * g + jj < valid_rows ? acc[jj] * a.scale_log2 : -INFINITY;
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mnew = fmaxf(m, mx);
     const float alpha = fast_exp2(m - mnew);
     m = mnew;
-    bf16x8 ph, pl;
+    s16x4v ph, pl;
     float ps = 0.f;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float pr = fast_exp2(sc[b][jj] - m);
-        ps += pr;
-        const __bf16 hi = static_cast<__bf16>(pr);
-        ph[4 * b + jj] = hi;
-        pl[4 * b + jj] = static_cast<__bf16>(pr - static_cast<float>(hi));
-      }
+    for (int jj = 0; jj < 4; ++jj) {
+      const float pr = fast_exp2(sc[jj] - mnew);
+      ps += pr;
+      const __bf16 hi = static_cast<__bf16>(pr);
+      const __bf16 lo = static_cast<__bf16>(pr - static_cast<float>(hi));
+      ph[jj] = __builtin_bit_cast(short, hi);
+      pl[jj] = __builtin_bit_cast(short, lo);
+    }
     lsum = lsum * alpha + ps;
-
-    // V tiles into this wave's LDS rows; keys past the context (or a missing
-    // second block) are stored as 0.  LDS operations of one wave execute in
-    // order, so the transposed reads below see these writes, and the next
-    // iteration's writes come after these reads.
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        const int off = 1024 * i + 16 * lane;
-        const int tok = off / RB, col = off % RB;
-        u32x4 w = vt[b][i];
-        if (!have[b] || (j0 + b) * kBlock + tok >= ctx) w = u32x4{0, 0, 0, 0};
-        *reinterpret_cast<u32x4*>(vs + (b * kBlock + tok) * VROW + col) = w;
-      }
-    __builtin_amdgcn_wave_barrier();
-
-    // O^T += V^T P^T, one 16-dim chunk at a time
-    const char* tr0 = vs + (4 * g + (n >> 2)) * VROW + 8 * (n & 3);
-    const char* tr1 = tr0 + kBlock * VROW;
+    const char* trb = tile + tr_row * RB + 8 * (n & 1);
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
-      const bf16x8 va = join(lds_read_tr(tr0 + 32 * c), lds_read_tr(tr1 + 32 * c));
-      f32x4 acc = o[c] * alpha;
-      acc = mfma(va, ph, acc);
-      o[c] = mfma(va, pl, acc);
+      const s16x4 vt = lds_read_tr(trb + 16 * ((2 * c + tr_k0) ^ tr_sw));
+      f32x4 t = o[c] * alpha;
+      t = mfma16(vt, ph, t);
+      o[c] = mfma16(vt, pl, t);
     }
-    __builtin_amdgcn_wave_barrier();
+  };
+  // Two blocks per step: both blocks' K and V loads are issued, then both are
+  // computed, so a wave keeps 2 x (K + V) tiles in flight.
+  u32x4 ktA[KC], ktB[KC];
+  char* tileA = vs;
+  char* tileB = vs + kBlock * RB;
+  for (int32_t it = 0; it < nit; it += 2) {
+    issue(it, ktA, tileA);
+    if (it + 1 < nit) issue(it + 1, ktB, tileB);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    compute(it, ktA, tileA);
+    if (it + 1 < nit) compute(it + 1, ktB, tileB);
   }
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
 
-  // merge the four waves through LDS (the V areas are reused)
+  // merge the four waves through LDS (the V tiles are reused)
   __syncthreads();
   float* so = reinterpret_cast<float*>(smem);
 #pragma unroll
@@ -285,6 +293,7 @@ __global__ __launch_bounds__(256) void decode_group_mfma_kernel(pkv_decode_args 
       if (d == 0) { a.part_ml[2 * pidx] = M; a.part_ml[2 * pidx + 1] = L; }
     }
   }
+  (void)kSlots;
 }
 
 // ---------------------------------------------------------------------------

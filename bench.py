@@ -182,7 +182,7 @@ def secondary(args):
     td, ld = torch.from_numpy(tables_h).to(dev), torch.from_numpy(lens_h).to(dev)
     mcl = int(lens_h.max())
     ws = PK.workspace_for(len(seqs), Hq, D, mcl, device=dev)
-    plan = PK.plan_for(ld, MB, mcl)
+    plan = PK.plan_for(ld, Hq, Hkv, MB, mcl, PK.PKV_BF16)
     scale = 1.0 / math.sqrt(D)
     reps = max(args.steps, 3)
 
@@ -330,7 +330,8 @@ def main():
         lens_d.copy_(lens_h, non_blocking=True)
         max_ctx = int(ln.max())
         # the decode plan depends only on this step's lengths: built once, used by every layer
-        B._check(lib.pkv_decode_plan(plan.data_ptr(), plan.numel(), lens_d.data_ptr(), S, MB, max_ctx, sp))
+        B._check(lib.pkv_decode_plan(plan.data_ptr(), plan.numel(), lens_d.data_ptr(), S, H, H, MB, max_ctx, BF16,
+                                     sp))
         n_pairs = len(pairs)
         if n_pairs:
             pairs_h.numpy()[:n_pairs] = pairs
@@ -399,7 +400,7 @@ def main():
                         "lognormal ctx (median 200, sigma 1) clipped [1,2048], block 16, pool 1.2x shuffled, "
                         f"{L} layer pools",
             "global_batch": S, "layers": L, "mean_ctx": round(float(np.mean([ln.mean() for ln in step_lens])), 1),
-            "partition_tokens": 512, "parallelism": "none (1 GPU)"},
+            "partition_tokens": 1024, "parallelism": "none (1 GPU)"},
         "kv_gbps_step": round(kv_gbps, 1),
         "hbm_peak_frac_step": round(kv_gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -125,10 +125,11 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst,
  * max_blocks_per_seq*block_size, or whose table names a block outside
  * [0, num_blocks), is written as NaN.
  * workspace: device scratch of at least pkv_attention_workspace_bytes(...) bytes
- * for the decode plan and the partial results of contexts longer than one
- * 512-token partition.  No
- * initialisation is needed; its contents are meaningless between calls.  Calls
- * that share one workspace must not overlap in time (e.g. run them on one stream).
+ * for the decode plan and the partial results of split contexts (the context
+ * is cut into partitions of 1024 tokens, 4096 for the matrix-core group
+ * kernel; a second kernel merges split contexts).  No initialisation is needed; its contents are meaningless
+ * between calls.  Calls that share one workspace must not overlap in time
+ * (e.g. run them on one stream).
  * ------------------------------------------------------------------------ */
 size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                      int32_t max_context_len);
@@ -142,27 +143,30 @@ pkv_status pkv_attention_decode(float* out, const void* q, const void* k_cache,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
- * Decode plan.  Decode work is cut into units (sequence, 512-token partition);
- * the plan lists them longest first for the decode kernel's dispatch order.  It
- * depends only on the context lengths and sizes, so a caller may build it once
- * per step and reuse it for every layer (pkv_attention_decode_planned);
+ * Decode plan.  Decode work is cut into units (sequence, context partition);
+ * the plan lists them longest first for the decode kernel's dispatch order.
+ * It depends only on the context lengths and sizes, so a caller may build it
+ * once per step and reuse it for every layer (pkv_attention_decode_planned);
  * pkv_attention_decode builds it in its workspace on every call.
  *
  * plan: device buffer of at least pkv_decode_plan_bytes(num_seqs,
- * max_context_len) bytes, 16-byte aligned.  Rows with a context length of 0
- * or an invalid one (see pkv_attention_decode) get no unit.  A plan records
- * num_seqs, max_context_len and max_blocks_per_seq; a decode call with other
- * values writes NaN rows instead of using it.
+ * max_context_len) bytes, 16-byte aligned.  num_heads, num_kv_heads and dtype
+ * choose the partition size (they must be those of the decode calls).  A
+ * sequence with a context length of 0 or an invalid one (see
+ * pkv_attention_decode) gets a unit that writes its 0 or NaN rows.  A plan
+ * records num_seqs, max_context_len, max_blocks_per_seq and the partition
+ * size; a decode call with other values writes NaN rows instead of using it.
  * ------------------------------------------------------------------------ */
 size_t pkv_decode_plan_bytes(int32_t num_seqs, int32_t max_context_len);
 
 pkv_status pkv_decode_plan(void* plan, size_t plan_bytes, const int32_t* context_lens, int32_t num_seqs,
-                           int32_t max_blocks_per_seq, int32_t max_context_len, void* stream);
+                           int32_t num_heads, int32_t num_kv_heads, int32_t max_blocks_per_seq,
+                           int32_t max_context_len, pkv_dtype dtype, void* stream);
 
 /* pkv_attention_decode with a plan built by pkv_decode_plan from the same
- * context_lens, num_seqs, max_blocks_per_seq and max_context_len (and not
- * changed since).  Same arguments and results otherwise; the workspace of
- * pkv_attention_workspace_bytes(...) is enough. */
+ * context_lens, num_seqs, heads, dtype, max_blocks_per_seq and max_context_len
+ * (and not changed since).  Same arguments and results otherwise; the
+ * workspace of pkv_attention_workspace_bytes(...) is enough. */
 pkv_status pkv_attention_decode_planned(float* out, const void* q, const void* k_cache, const void* v_cache,
                                         const int32_t* block_tables, int32_t max_blocks_per_seq,
                                         const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,

@@ -38,7 +38,7 @@ _SIGS = {
     "pkv_attention_decode": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32,
                                       _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_p, _c_sz, _c_p]),
     "pkv_decode_plan_bytes": (_c_sz, [_c_i32, _c_i32]),
-    "pkv_decode_plan": (_c_i32, [_c_p, _c_sz, _c_p, _c_i32, _c_i32, _c_i32, _c_p]),
+    "pkv_decode_plan": (_c_i32, [_c_p, _c_sz, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_p]),
     "pkv_attention_decode_planned": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32,
                                               _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_p, _c_sz, _c_p,
                                               _c_sz, _c_p]),
@@ -132,19 +132,21 @@ def pkv_decode_plan_bytes(num_seqs: int, max_context_len: int) -> int:
     return int(_lib.pkv_decode_plan_bytes(num_seqs, max_context_len))
 
 
-def pkv_decode_plan(plan: torch.Tensor, context_lens: torch.Tensor, max_blocks_per_seq: int,
-                    max_context_len: int, stream=None) -> None:
-    """plan: device uint8 buffer; context_lens: int32 [S] on the GPU."""
+def pkv_decode_plan(plan: torch.Tensor, context_lens: torch.Tensor, num_heads: int, num_kv_heads: int,
+                    max_blocks_per_seq: int, max_context_len: int, dtype: int, stream=None) -> None:
+    """plan: device uint8 buffer; context_lens: int32 [S] on the GPU; dtype PKV_F32 / PKV_BF16."""
     _dev(plan, context_lens)
     _check(_lib.pkv_decode_plan(plan.data_ptr(), plan.numel() * plan.element_size(), context_lens.data_ptr(),
-                                context_lens.numel(), max_blocks_per_seq, int(max_context_len), _stream(stream)))
+                                context_lens.numel(), num_heads, num_kv_heads, max_blocks_per_seq,
+                                int(max_context_len), int(dtype), _stream(stream)))
 
 
-def plan_for(context_lens: torch.Tensor, max_blocks_per_seq: int, max_context_len: int) -> torch.Tensor:
+def plan_for(context_lens: torch.Tensor, num_heads: int, num_kv_heads: int, max_blocks_per_seq: int,
+             max_context_len: int, dtype: int) -> torch.Tensor:
     """A device plan for these lengths (pkv_decode_plan into a fresh buffer)."""
     n = pkv_decode_plan_bytes(context_lens.numel(), max_context_len)
     plan = torch.empty(max(n, 16), dtype=torch.uint8, device=context_lens.device)
-    pkv_decode_plan(plan, context_lens, max_blocks_per_seq, max_context_len)
+    pkv_decode_plan(plan, context_lens, num_heads, num_kv_heads, max_blocks_per_seq, max_context_len, dtype)
     return plan
 
 

@@ -37,13 +37,18 @@ pkv_status hip_status(const char* fn, int err) {
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Partial-result slots per (sequence, head): enough for the smallest partition.
 int32_t num_partitions(int32_t max_context_len) {
-  const int32_t np = (max_context_len + kPartTokens - 1) / kPartTokens;
+  const int32_t np = (max_context_len + kMinPartTokens - 1) / kMinPartTokens;
   return np < 1 ? 1 : np;
 }
 
+// Header and (s, p) per unit: at most num_partitions per sequence, or one
+// rowless unit.
+constexpr size_t kPlanHdrWords = 8;
 size_t plan_bytes(int32_t num_seqs, int32_t max_context_len) {
-  return (4 + 2 * static_cast<size_t>(num_seqs) * num_partitions(max_context_len)) * sizeof(int32_t);
+  return (kPlanHdrWords + 2 * static_cast<size_t>(num_seqs) * (num_partitions(max_context_len) + 1)) *
+         sizeof(int32_t);
 }
 
 size_t partial_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len) {
@@ -118,20 +123,26 @@ size_t pkv_decode_plan_bytes(int32_t num_seqs, int32_t max_context_len) {
 }
 
 pkv_status pkv_decode_plan(void* plan, size_t plan_bytes_given, const int32_t* context_lens, int32_t num_seqs,
-                           int32_t max_blocks_per_seq, int32_t max_context_len, void* stream) {
+                           int32_t num_heads, int32_t num_kv_heads, int32_t max_blocks_per_seq,
+                           int32_t max_context_len, pkv_dtype dtype, void* stream) {
   const char* fn = "pkv_decode_plan";
   if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0)
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+  if (num_kv_heads <= 0 || num_heads <= 0 || num_heads % num_kv_heads != 0)
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: num_heads (%d) must be a positive multiple of num_kv_heads (%d)", fn,
+                     num_heads, num_kv_heads);
   if (num_seqs == 0) return PKV_OK;
   if (!plan || !context_lens) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: NULL pointer", fn);
   if (reinterpret_cast<uintptr_t>(plan) & 15u) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: plan must be 16-byte aligned", fn);
-  if (static_cast<int64_t>(num_seqs) * num_partitions(max_context_len) > 0x3FFFFFFF)
+  if (static_cast<int64_t>(num_seqs) * (num_partitions(max_context_len) + 1) > 0x3FFFFFFF)
     return pkv_failf(PKV_ERR_UNSUPPORTED, "%s: too many work units", fn);
-  if (plan_bytes_given < plan_bytes(num_seqs, max_context_len))
+  const size_t need = plan_bytes(num_seqs, max_context_len);
+  if (plan_bytes_given < need)
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: plan buffer of %zu bytes is smaller than the %zu needed", fn,
-                     plan_bytes_given, plan_bytes(num_seqs, max_context_len));
+                     plan_bytes_given, need);
   return hip_status(fn, pkv_launch_plan(static_cast<int32_t*>(plan), context_lens, num_seqs, max_blocks_per_seq,
-                                        max_context_len, stream));
+                                        max_context_len, pkv_part_tokens(dtype, num_heads, num_kv_heads), stream));
 }
 
 size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
@@ -165,8 +176,9 @@ static pkv_status decode_impl(const char* fn, float* out, const void* q, const v
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: out, q and cache pointers must be 16-byte aligned", fn);
   const int32_t np = num_partitions(max_context_len);
   const int64_t grid = static_cast<int64_t>(num_seqs) * num_heads * np;
-  if (grid > 0x7FFFFFFF || static_cast<int64_t>(num_seqs) * np > 0x3FFFFFFF)
+  if (grid > 0x7FFFFFFF || static_cast<int64_t>(num_seqs) * (np + 1) > 0x3FFFFFFF)
     return pkv_failf(PKV_ERR_UNSUPPORTED, "%s: launch grid too large", fn);
+  const int32_t part_tokens = pkv_part_tokens(dtype, num_heads, num_kv_heads);
   const size_t pb = plan_bytes(num_seqs, max_context_len);
   const size_t part = partial_bytes(num_seqs, num_heads, head_dim, max_context_len);
   const size_t need = (build_plan ? align256(pb) : 0) + part;
@@ -180,7 +192,7 @@ static pkv_status decode_impl(const char* fn, float* out, const void* q, const v
     plan = ws;
     ws += align256(pb);
     const int err = pkv_launch_plan(static_cast<int32_t*>(const_cast<void*>(plan)), context_lens, num_seqs,
-                                    max_blocks_per_seq, max_context_len, stream);
+                                    max_blocks_per_seq, max_context_len, part_tokens, stream);
     if (err) return hip_status(fn, err);
   } else {
     if (!plan) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: plan is NULL", fn);
@@ -207,6 +219,7 @@ static pkv_status decode_impl(const char* fn, float* out, const void* q, const v
   a.num_blocks = num_blocks;
   a.max_context_len = max_context_len;
   a.num_partitions = np;
+  a.part_tokens = part_tokens;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.dtype = dtype;
   return hip_status(fn, pkv_launch_decode(a, stream));

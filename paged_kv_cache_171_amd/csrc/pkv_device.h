@@ -14,7 +14,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = 16;            // tokens per block (the pages' P = 16)
 constexpr float kNegBig = -FLT_MAX;   // finite "minus infinity" for running maxima
-constexpr int kPlanHdr = 4;           // plan header: n_units, num_seqs, max_context_len, max_blocks_per_seq
+// Plan layout (int32): a header of kPlanHdr words -- n_units, num_seqs,
+// max_context_len, max_blocks_per_seq, part_tokens, 0, 0, 0 -- then (s, p) per
+// unit; p = -1 marks a sequence with no attention work (empty or invalid
+// context).
+constexpr int kPlanHdr = 8;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -25,7 +29,24 @@ __device__ __forceinline__ bool len_ok(int32_t ctx, int32_t max_context_len, int
 
 // The plan was built for these sizes.
 __device__ __forceinline__ bool plan_matches(const int32_t* plan, const pkv_decode_args& a) {
-  return plan[1] == a.num_seqs && plan[2] == a.max_context_len && plan[3] == a.max_blocks_per_seq;
+  return plan[1] == a.num_seqs && plan[2] == a.max_context_len && plan[3] == a.max_blocks_per_seq &&
+         plan[4] == a.part_tokens;
+}
+
+__device__ __forceinline__ const int32_t* plan_units(const int32_t* plan) { return plan + kPlanHdr; }
+
+// Log-sum-exp merge of the n partials (m in log2 units, l, acc) of one output
+// element: sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M), M = max_p m_p.
+__device__ __forceinline__ float merge_partials(const float* ml, const float* acc, int32_t n, int32_t stride) {
+  float M = ml[0];
+  for (int32_t q = 1; q < n; ++q) M = fmaxf(M, ml[2 * q]);
+  float L = 0.f, o = 0.f;
+  for (int32_t q = 0; q < n; ++q) {
+    const float f = fast_exp2(ml[2 * q] - M);
+    L += ml[2 * q + 1] * f;
+    o += acc[static_cast<int64_t>(q) * stride] * f;
+  }
+  return o / L;
 }
 
 }  // namespace pkvd

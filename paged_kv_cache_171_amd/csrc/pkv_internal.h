@@ -18,8 +18,16 @@ int pkv_launch_append(void* k_cache, void* v_cache, const void* k, const void* v
 int pkv_launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst, int32_t num_pairs,
                            int32_t num_blocks, int64_t block_bytes, void* stream);
 
-// Tokens per context partition of the decode work split (a multiple of 16).
-constexpr int32_t kPartTokens = 512;
+// Context partitions of the decode work split (multiples of 16 tokens): 1024
+// tokens for the VALU kernel, 4096 for the MFMA group kernel (which reads
+// Hq/Hkv heads per tile and gains more from long units than from balance).
+constexpr int32_t kMinPartTokens = 1024;
+constexpr int32_t kMaxPartTokens = 4096;
+constexpr int32_t kMaxMfmaGroup = 16;
+inline int32_t pkv_part_tokens(int dtype, int32_t num_heads, int32_t num_kv_heads) {
+  const int32_t group = num_heads / num_kv_heads;
+  return (dtype == PKV_BF16 && group >= 2 && group <= kMaxMfmaGroup) ? kMaxPartTokens : kMinPartTokens;
+}
 
 struct pkv_decode_args {
   float* out;
@@ -38,18 +46,17 @@ struct pkv_decode_args {
   int32_t head_dim;
   int32_t num_blocks;
   int32_t max_context_len;
-  int32_t num_partitions;  // NP = ceil(max_context_len / kPartTokens)
+  int32_t num_partitions;  // NP = ceil(max_context_len / kMinPartTokens): partial slots per row
+  int32_t part_tokens;     // tokens per partition for this launch
   float scale_log2;        // scale * log2(e)
   int dtype;               // pkv_dtype
 };
 // Decode: the main kernel (VALU, or MFMA for bf16 query-head groups of 2..16
-// heads) and then the partition merge.
+// heads, pkv_mfma.hip), then the partition merge when a context can be split.
 int pkv_launch_decode(const pkv_decode_args& a, void* stream);
-constexpr int32_t kMaxMfmaGroup = 16;
-// The MFMA kernel for bf16 query-head groups (pkv_mfma.hip); the caller launches the merge.
 int pkv_launch_decode_group(const pkv_decode_args& a, void* stream);
 int pkv_launch_plan(int32_t* plan, const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
-                    int32_t max_context_len, void* stream);
+                    int32_t max_context_len, int32_t part_tokens, void* stream);
 
 // Causal chunked-prefill attention (pkv_mfma.hip).
 struct pkv_prefill_args {

@@ -149,9 +149,9 @@ template <> struct Elem<uint16_t> {  // bf16 bits
 // [OS] "Qué significa esto para lo que pagas": decode is memory-bound, so the
 // kernel is built around streaming every K/V tile from HBM exactly once.
 //
-// Work units.  A sequence's context is cut into partitions of kPartTokens
-// tokens; a unit is (sequence s, partition p) and one workgroup handles one unit
-// for one query head.  The plan (plan_kernel) lists the units longest first --
+// Work units.  A sequence's context is cut into partitions of part_tokens
+// tokens (1024 here); a unit is (sequence s, partition p) and one workgroup
+// handles one unit for one query head.  The plan (plan_kernel) lists the units longest first --
 // every full partition, then the remainders by decreasing size -- so that the
 // workgroups dispatched last are the short ones and the ragged batches of
 // continuous batching ([UL] "Cómo funciona la planificación a nivel de
@@ -184,33 +184,33 @@ struct DecodeShape {
   static_assert(kLpr == 8 || kLpr == 16 || kLpr == 32, "unsupported shape");
 };
 
-// Plan layout (int32): header n_units, num_seqs, max_context_len,
-// max_blocks_per_seq; then (s, p) per unit.
-
 // ---------------------------------------------------------------------------
 // Plan: one workgroup turns the context lengths into the unit list.  Full
 // partitions come first (sequence order), then remainders sorted by size,
-// largest first (a counting sort over the kPartTokens possible sizes; the
+// largest first (a counting sort over the part_tokens possible sizes; the
 // order inside one size is whatever the LDS atomics give, which changes no
-// result: every unit computes the same partial whenever it runs).
+// result: every unit computes the same partial whenever it runs), then one
+// (s, -1) unit per sequence with an empty or invalid context, whose rows the
+// decode kernel writes as 0 or NaN.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void plan_kernel(int32_t* __restrict__ plan,
                                                     const int32_t* __restrict__ context_lens,
                                                     int32_t num_seqs, int32_t max_blocks_per_seq,
-                                                    int32_t max_context_len) {
-  __shared__ int32_t bucket[kPartTokens];   // remainder size -> count, then -> next slot
+                                                    int32_t max_context_len, int32_t part) {
+  __shared__ int32_t bucket[kMaxPartTokens];   // remainder size -> count, then -> next slot
   __shared__ int32_t scan[1024];
-  __shared__ int32_t sm_full;
+  __shared__ int32_t sm_full, sm_special;
   const int tid = threadIdx.x;
-  for (int i = tid; i < kPartTokens; i += 1024) bucket[i] = 0;
-  if (tid == 0) sm_full = 0;
+  int32_t* units = plan + kPlanHdr;
+  for (int i = tid; i < part; i += 1024) bucket[i] = 0;
+  if (tid == 0) { sm_full = 0; sm_special = 0; }
   __syncthreads();
   int32_t full = 0;
   for (int32_t s = tid; s < num_seqs; s += 1024) {
     const int32_t ctx = context_lens[s];
     if (!len_ok(ctx, max_context_len, max_blocks_per_seq)) continue;
-    full += ctx / kPartTokens;
-    if (ctx % kPartTokens) atomicAdd(&bucket[ctx % kPartTokens], 1);
+    full += ctx / part;
+    if (ctx % part) atomicAdd(&bucket[ctx % part], 1);
   }
   atomicAdd(&sm_full, full);
   __syncthreads();
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(int32_t* __restrict__ plan,
   // bucket r's first slot = n_full + (remainders larger than r): a running sum
   // over r from large to small, one thread per bucket, in chunks of 1024.
   int32_t carry = n_full;
-  for (int32_t base = kPartTokens - 1; base >= 0; base -= 1024) {
+  for (int32_t base = part - 1; base >= 0; base -= 1024) {
     const int32_t r = base - tid;
     const int32_t c = r >= 1 ? bucket[r] : 0;
     scan[tid] = c;
@@ -234,14 +234,15 @@ __global__ __launch_bounds__(1024) void plan_kernel(int32_t* __restrict__ plan,
     __syncthreads();
     carry += chunk_total;
   }
-  const int32_t n_units = carry;
-  // full units at exclusive prefix positions, remainder units at their bucket slot
+  const int32_t n_regular = carry;
+  // full units at exclusive prefix positions, remainder units at their bucket
+  // slot, rowless sequences after all of them
   int32_t run = 0;
   for (int32_t base = 0; base < num_seqs; base += 1024) {
     const int32_t s = base + tid;
-    int32_t ctx = s < num_seqs ? context_lens[s] : 0;
+    const int32_t ctx = s < num_seqs ? context_lens[s] : 0;
     const bool ok = s < num_seqs && len_ok(ctx, max_context_len, max_blocks_per_seq);
-    const int32_t nf = ok ? ctx / kPartTokens : 0;
+    const int32_t nf = ok ? ctx / part : 0;
     scan[tid] = nf;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
@@ -251,24 +252,34 @@ __global__ __launch_bounds__(1024) void plan_kernel(int32_t* __restrict__ plan,
       __syncthreads();
     }
     const int32_t first = run + scan[tid] - nf;
-    for (int32_t p = 0; p < nf; ++p) {
-      plan[kPlanHdr + 2 * (first + p)] = s;
-      plan[kPlanHdr + 2 * (first + p) + 1] = p;
+    for (int32_t q = 0; q < nf; ++q) {
+      units[2 * (first + q)] = s;
+      units[2 * (first + q) + 1] = q;
     }
-    if (ok && ctx % kPartTokens) {
-      const int32_t slot = atomicAdd(&bucket[ctx % kPartTokens], 1);
-      plan[kPlanHdr + 2 * slot] = s;
-      plan[kPlanHdr + 2 * slot + 1] = nf;
+    if (ok && ctx % part) {
+      const int32_t slot = atomicAdd(&bucket[ctx % part], 1);
+      units[2 * slot] = s;
+      units[2 * slot + 1] = nf;
+    }
+    if (s < num_seqs && !ok) {
+      const int32_t slot = n_regular + atomicAdd(&sm_special, 1);
+      units[2 * slot] = s;
+      units[2 * slot + 1] = -1;
     }
     const int32_t chunk_total = scan[1023];
     __syncthreads();
     run += chunk_total;
   }
+  __syncthreads();
   if (tid == 0) {
-    plan[0] = n_units;
+    plan[0] = n_regular + sm_special;
     plan[1] = num_seqs;
     plan[2] = max_context_len;
     plan[3] = max_blocks_per_seq;
+    plan[4] = part;
+    plan[5] = 0;
+    plan[6] = 0;
+    plan[7] = 0;
   }
 }
 
@@ -290,15 +301,28 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(pkv_decode_args a) {
   const int32_t u = static_cast<int32_t>(blockIdx.x / Hq);
   const int32_t h = static_cast<int32_t>(blockIdx.x - static_cast<uint32_t>(u) * Hq);
   const int32_t* plan = a.plan;
-  if (!plan_matches(plan, a) || u >= plan[0]) return;
-  const int32_t s = plan[kPlanHdr + 2 * u];
-  const int32_t p = plan[kPlanHdr + 2 * u + 1];
+  if (!plan_matches(plan, a)) {
+    // a plan built for other sizes: every row is NaN
+    if (u < a.num_seqs && threadIdx.x < D)
+      a.out[(static_cast<int64_t>(u) * Hq + h) * D + threadIdx.x] = __builtin_nanf("");
+    return;
+  }
+  if (u >= plan[0]) return;
+  const int32_t* units = pkvd::plan_units(plan);
+  const int32_t s = units[2 * u];
+  const int32_t p = units[2 * u + 1];
   const int32_t ctx = a.context_lens[s];
-  const int32_t np_s = (ctx + kPartTokens - 1) / kPartTokens;
-  const int32_t nblk = (ctx + kBlock - 1) / kBlock;
-  const int32_t blk_begin = p * (kPartTokens / kBlock);
-  const int32_t blk_end = min(nblk, blk_begin + kPartTokens / kBlock);
   const int64_t orow = (static_cast<int64_t>(s) * Hq + h) * D;
+  if (p < 0) {
+    // no attention work: an empty context gives 0, an invalid one NaN
+    if (threadIdx.x < D) a.out[orow + threadIdx.x] = ctx == 0 ? 0.f : __builtin_nanf("");
+    return;
+  }
+  const int32_t part = a.part_tokens;
+  const int32_t np_s = (ctx + part - 1) / part;
+  const int32_t nblk = (ctx + kBlock - 1) / kBlock;
+  const int32_t blk_begin = p * (part / kBlock);
+  const int32_t blk_end = min(nblk, blk_begin + part / kBlock);
 
   constexpr int64_t kTileBytes = static_cast<int64_t>(kBlock) * D * sizeof(T);
   const int64_t block_bytes = static_cast<int64_t>(a.num_kv_heads) * kTileBytes;
@@ -424,12 +448,12 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(pkv_decode_args a) {
   }
   if (lane == 0) { sm_ml[wave][0] = m; sm_ml[wave][1] = l; sm_bad[wave] = bad ? 1 : 0; }
   __syncthreads();
-  if (threadIdx.x < D) {
-    const int t = threadIdx.x;
-    float M = sm_ml[0][0];
+  float M = 0.f, L = 0.f, o = 0.f;
+  const int t = threadIdx.x;
+  if (t < D) {
+    M = sm_ml[0][0];
 #pragma unroll
     for (int v = 1; v < kWaves; ++v) M = fmaxf(M, sm_ml[v][0]);
-    float L = 0.f, o = 0.f;
 #pragma unroll
     for (int v = 0; v < kWaves; ++v) {
       const float f = fast_exp2(sm_ml[v][0] - M);
@@ -437,56 +461,46 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(pkv_decode_args a) {
       o += sm_acc[v][t] * f;
     }
     if (sm_bad[0] | sm_bad[1] | sm_bad[2] | sm_bad[3]) { o = __builtin_nanf(""); L = __builtin_nanf(""); }
-    if (np_s == 1) {
-      a.out[orow + t] = o / L;
-    } else {
-      const int64_t pidx = (static_cast<int64_t>(s) * Hq + h) * a.num_partitions + p;
-      a.part_acc[pidx * D + t] = o;
-      if (t == 0) { a.part_ml[2 * pidx] = M; a.part_ml[2 * pidx + 1] = L; }
-    }
+  }
+  if (np_s == 1) {
+    if (t < D) a.out[orow + t] = o / L;
+    return;
+  }
+  // a split context: this partition's (max, sum, accumulator) for the merge kernel
+  const int64_t pidx = (static_cast<int64_t>(s) * Hq + h) * a.num_partitions + p;
+  if (t < D) {
+    a.part_acc[pidx * D + t] = o;
+    if (t == 0) { a.part_ml[2 * pidx] = M; a.part_ml[2 * pidx + 1] = L; }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Partition merge, one workgroup per (s, h): for a context of more than one
-// partition,  M = max_p m_p,  L = sum_p l_p 2^(m_p - M),
-// out = sum_p acc_p 2^(m_p - M) / L  -- the log-sum-exp identity that makes the
-// split softmax equal the unsplit one.  It also writes the rows no unit owns:
-// 0 for an empty context, NaN for an invalid one (or a plan built for other
-// arguments).  A separate launch keeps the decode kernel free of
-// cross-workgroup synchronisation: device-scope fences write back and
-// invalidate a whole XCD L2, far costlier than a second launch.
+// Partition merge, one workgroup per (s, h), for contexts cut into more than
+// one partition:  M = max_p m_p,  out = sum_p acc_p 2^(m_p - M) / sum_p l_p
+// 2^(m_p - M) -- the log-sum-exp identity that makes the split softmax equal
+// the unsplit one.  A separate launch keeps the decode kernel free of
+// cross-workgroup synchronisation: a device-scope release/acquire per split
+// unit writes back and invalidates an XCD L2 and costs far more (measured 2x on
+// the 13B-shaped batch) than this launch, whose kernel boundary publishes all
+// partials at once.  It is launched only when some context can be split.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(D) void merge_partitions_kernel(pkv_decode_args a) {
   const int64_t sh = blockIdx.x;                       // s * Hq + h
   const int32_t s = static_cast<int32_t>(sh / a.num_heads);
+  if (!plan_matches(a.plan, a)) return;                // the decode kernel wrote NaN rows
   const int32_t ctx = a.context_lens[s];
-  const int t = threadIdx.x;
-  const bool plan_ok = plan_matches(a.plan, a);
-  if (!plan_ok || !len_ok(ctx, a.max_context_len, a.max_blocks_per_seq)) {
-    if (!plan_ok || ctx != 0) a.out[sh * D + t] = __builtin_nanf("");
-    else a.out[sh * D + t] = 0.f;
-    return;
-  }
-  const int32_t np_s = (ctx + kPartTokens - 1) / kPartTokens;
+  if (!len_ok(ctx, a.max_context_len, a.max_blocks_per_seq)) return;
+  const int32_t np_s = (ctx + a.part_tokens - 1) / a.part_tokens;
   if (np_s <= 1) return;
-  const float* ml = a.part_ml + sh * a.num_partitions * 2;
-  const float* acc = a.part_acc + sh * a.num_partitions * D;
-  float M = ml[0];
-  for (int32_t p = 1; p < np_s; ++p) M = fmaxf(M, ml[2 * p]);
-  float L = 0.f, o = 0.f;
-  for (int32_t p = 0; p < np_s; ++p) {
-    const float f = fast_exp2(ml[2 * p] - M);
-    L += ml[2 * p + 1] * f;
-    o += acc[static_cast<int64_t>(p) * D + t] * f;
-  }
-  a.out[sh * D + t] = o / L;
+  const int64_t prow = sh * a.num_partitions;
+  a.out[sh * D + threadIdx.x] = pkvd::merge_partials(a.part_ml + 2 * prow, a.part_acc + prow * D + threadIdx.x, np_s, D);
 }
 
 template <typename T, int D>
 int launch_decode_valu(const pkv_decode_args& a, hipStream_t st) {
-  const int64_t grid = static_cast<int64_t>(a.num_seqs) * a.num_partitions * a.num_heads;
+  const int64_t np = (a.max_context_len + a.part_tokens - 1) / a.part_tokens;
+  const int64_t grid = static_cast<int64_t>(a.num_seqs) * (np < 1 ? 1 : np) * a.num_heads;
   hipLaunchKernelGGL((decode_valu_kernel<T, D>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
@@ -494,9 +508,9 @@ int launch_decode_valu(const pkv_decode_args& a, hipStream_t st) {
 }  // namespace
 
 int pkv_launch_plan(int32_t* plan, const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
-                    int32_t max_context_len, void* stream) {
+                    int32_t max_context_len, int32_t part_tokens, void* stream) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, static_cast<hipStream_t>(stream), plan, context_lens,
-                     num_seqs, max_blocks_per_seq, max_context_len);
+                     num_seqs, max_blocks_per_seq, max_context_len, part_tokens);
   return hipGetLastError();
 }
 
@@ -531,13 +545,13 @@ int pkv_launch_decode(const pkv_decode_args& a, void* stream) {
   const int32_t group = a.num_heads / a.num_kv_heads;
   int err;
   if (a.dtype == PKV_BF16 && group >= 2 && group <= kMaxMfmaGroup) {
-    err = pkv_launch_decode_group(a, stream);          // query-head groups: MFMA kernel
+    err = pkv_launch_decode_group(a, stream);
   } else if (a.dtype == PKV_BF16) {
     err = a.head_dim == 128 ? launch_decode_valu<uint16_t, 128>(a, st) : launch_decode_valu<uint16_t, 64>(a, st);
   } else {
     err = a.head_dim == 128 ? launch_decode_valu<float, 128>(a, st) : launch_decode_valu<float, 64>(a, st);
   }
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || a.max_context_len <= a.part_tokens) return err;   // no context can be split
   const uint32_t rows = static_cast<uint32_t>(a.num_seqs) * a.num_heads;
   if (a.head_dim == 128) {
     hipLaunchKernelGGL((merge_partitions_kernel<128>), dim3(rows), dim3(128), 0, st, a);

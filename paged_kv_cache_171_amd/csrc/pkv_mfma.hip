@@ -136,14 +136,29 @@ __global__ __launch_bounds__(256, 4) void decode_group_mfma_kernel(pkv_decode_ar
   const int32_t u = static_cast<int32_t>(blockIdx.x / static_cast<uint32_t>(Hkv));
   const int32_t kvh = static_cast<int32_t>(blockIdx.x - static_cast<uint32_t>(u) * Hkv);
   const int32_t* plan = a.plan;
-  if (!plan_matches(plan, a) || u >= plan[0]) return;
-  const int32_t s = plan[kPlanHdr + 2 * u];
-  const int32_t p = plan[kPlanHdr + 2 * u + 1];
+  if (!plan_matches(plan, a)) {
+    // a plan built for other sizes: every row is NaN
+    if (u < a.num_seqs)
+      for (int idx = threadIdx.x; idx < G * D; idx += 256)
+        a.out[(static_cast<int64_t>(u) * Hq + kvh * G) * D + idx] = __builtin_nanf("");
+    return;
+  }
+  if (u >= plan[0]) return;
+  const int32_t* units = pkvd::plan_units(plan);
+  const int32_t s = units[2 * u];
+  const int32_t p = units[2 * u + 1];
   const int32_t ctx = a.context_lens[s];
-  const int32_t np_s = (ctx + kPartTokens - 1) / kPartTokens;
+  if (p < 0) {
+    // no attention work: an empty context gives 0, an invalid one NaN
+    for (int idx = threadIdx.x; idx < G * D; idx += 256)
+      a.out[(static_cast<int64_t>(s) * Hq + kvh * G) * D + idx] = ctx == 0 ? 0.f : __builtin_nanf("");
+    return;
+  }
+  const int32_t part = a.part_tokens;
+  const int32_t np_s = (ctx + part - 1) / part;
   const int32_t nblk = (ctx + kBlock - 1) / kBlock;
-  const int32_t blk_begin = p * (kPartTokens / kBlock);
-  const int32_t blk_end = min(nblk, blk_begin + kPartTokens / kBlock);
+  const int32_t blk_begin = p * (part / kBlock);
+  const int32_t blk_end = min(nblk, blk_begin + part / kBlock);
 
   const int64_t block_bytes = static_cast<int64_t>(Hkv) * kTile;
   const char* __restrict__ kc = reinterpret_cast<const char*>(a.k_cache) + kvh * kTile;
@@ -184,7 +199,7 @@ __global__ __launch_bounds__(256, 4) void decode_group_mfma_kernel(pkv_decode_ar
   float m = kNegBig, lsum = 0.f;
   bool bad = false;
 
-  // The wave's block ids (at most kPartTokens/16/4 = 8 of them), one per lane,
+  // The wave's block ids (at most kMaxPartTokens/16/4 = 64 of them), one per lane,
   // fetched once before the loop; each block takes its id with a lane read.
   const int32_t nit = (blk_end - blk_begin - wave + kWaves - 1) / kWaves;
   const int32_t my_ids = lane < nit ? table[blk_begin + wave + kWaves * lane] : 0;
@@ -523,7 +538,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_mfma_kernel(pkv_prefill_arg
 }  // namespace
 
 int pkv_launch_decode_group(const pkv_decode_args& a, void* stream) {
-  const int64_t grid = static_cast<int64_t>(a.num_seqs) * a.num_partitions * a.num_kv_heads;
+  const int64_t np = (a.max_context_len + a.part_tokens - 1) / a.part_tokens;
+  const int64_t grid = static_cast<int64_t>(a.num_seqs) * (np < 1 ? 1 : np) * a.num_kv_heads;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (a.head_dim == 128) {
     hipLaunchKernelGGL((decode_group_mfma_kernel<128>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st, a);

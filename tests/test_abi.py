@@ -89,30 +89,33 @@ def test_decode_rejects_bad_arguments(P):
     assert _decode(P, q=None) == P.PKV_ERR_INVALID_ARG
     assert _decode(P, S=0, q=None) == P.PKV_OK                  # nothing to do
     # the plan and the split-context partials need a workspace
-    need = P.pkv_attention_workspace_bytes(2, 4, 64, 5000)
+    need = P.pkv_attention_workspace_bytes(2, 4, 64, 5000)      # 5 partitions of 1024
     assert need > 0
     assert _decode(P, maxctx=5000, mb=400) == P.PKV_ERR_INVALID_ARG
     assert "workspace" in _lib(P).pkv_last_error().decode()
 
 
 def test_workspace_and_plan_sizes(P):
-    # plan: 4 header ints + (s, p) per unit; 512-token partitions
-    assert P.pkv_decode_plan_bytes(3, 64) == (4 + 2 * 3 * 1) * 4
-    assert P.pkv_decode_plan_bytes(3, 1025) == (4 + 2 * 3 * 3) * 4
+    # plan: 8 header ints + (s, p) for up to ceil(max_ctx / 1024) + 1 units per sequence
+    assert P.pkv_decode_plan_bytes(3, 64) == (8 + 2 * 3 * 2) * 4
+    assert P.pkv_decode_plan_bytes(3, 2049) == (8 + 2 * 3 * 4) * 4
     assert P.pkv_decode_plan_bytes(0, 64) == 0
     # one partition: no partials, just the plan (rounded to 256 bytes)
-    assert P.pkv_attention_workspace_bytes(3, 4, 128, 512) == 256
-    n = P.pkv_attention_workspace_bytes(3, 4, 128, 513)
+    assert P.pkv_attention_workspace_bytes(3, 4, 128, 1024) == 256
+    n = P.pkv_attention_workspace_bytes(3, 4, 128, 1025)
     assert n >= 256 + 3 * 4 * 2 * (2 + 128) * 4
     assert P.pkv_attention_workspace_bytes(0, 4, 128, 64) == 0
 
 
 def test_plan_rejects_bad_arguments(P):
     L = _lib(P)
-    assert L.pkv_decode_plan(None, 0, None, 0, 4, 64, None) == P.PKV_OK
-    assert L.pkv_decode_plan(256, 16, 512, 3, 4, 64, None) == P.PKV_ERR_INVALID_ARG   # buffer too small
-    assert L.pkv_decode_plan(None, 4096, 512, 3, 4, 64, None) == P.PKV_ERR_INVALID_ARG
-    assert L.pkv_decode_plan(264, 4096, 512, 3, 4, 64, None) == P.PKV_ERR_INVALID_ARG  # misaligned
+    #                 plan  bytes ctx_lens S  Hq Hkv MB maxctx dtype
+    assert L.pkv_decode_plan(None, 0, None, 0, 4, 4, 4, 64, 1, None) == P.PKV_OK
+    assert L.pkv_decode_plan(256, 16, 512, 3, 4, 4, 4, 64, 1, None) == P.PKV_ERR_INVALID_ARG   # buffer too small
+    assert L.pkv_decode_plan(None, 4096, 512, 3, 4, 4, 4, 64, 1, None) == P.PKV_ERR_INVALID_ARG
+    assert L.pkv_decode_plan(264, 4096, 512, 3, 4, 4, 4, 64, 1, None) == P.PKV_ERR_INVALID_ARG  # misaligned
+    assert L.pkv_decode_plan(256, 4096, 512, 3, 6, 4, 4, 64, 1, None) == P.PKV_ERR_INVALID_ARG  # Hq % Hkv
+    assert L.pkv_decode_plan(256, 4096, 512, 3, 4, 4, 4, 64, 9, None) == P.PKV_ERR_INVALID_ARG  # dtype
 
 
 def test_allocator_errors_are_status_codes(P):

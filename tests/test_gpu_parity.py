@@ -254,7 +254,7 @@ def test_planned_decode_matches_self_planned_and_reuses_the_plan():
     tables, lens = g.tables(w.decode_seqs)
     td, ld = torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
     mcl = int(lens.max())
-    plan = PK.plan_for(ld, tables.shape[1], mcl)
+    plan = PK.plan_for(ld, 8, 8, tables.shape[1], mcl, PK.PKV_BF16)
     q = rows_to_device(w.q, "cuda")
     pools = [(g.k_pool, g.v_pool), (g.v_pool, g.k_pool)]   # a second "layer": K and V swapped
     for kp, vp in pools:
@@ -273,7 +273,7 @@ def test_plan_built_for_other_sizes_gives_nan_rows():
     tables, lens = g.tables(w.decode_seqs)
     td, ld = torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
     mcl = int(lens.max())
-    plan = PK.plan_for(ld, tables.shape[1], mcl + 1)           # built with another max_context_len
+    plan = PK.plan_for(ld, 2, 2, tables.shape[1], mcl + 1, PK.PKV_F32)   # built with another max_context_len
     o = torch.zeros((4, 2, 64), dtype=torch.float32, device="cuda")
     PK.pkv_attention_decode(o, rows_to_device(w.q, "cuda"), g.k_pool, g.v_pool, td, ld, mcl, float(w.scale),
                             plan=plan)

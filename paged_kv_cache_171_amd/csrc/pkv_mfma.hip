@@ -71,6 +71,27 @@ __device__ __forceinline__ s16x4 lds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
 
+// A wave-uniform 32-bit load through the scalar unit.  Its wait counts only
+// scalar/LDS traffic, so it leaves the direct-to-LDS copies (counted with the
+// vector loads) in flight; a plain load issued after such copies would be a
+// vector load whose wait drains them.
+__device__ __forceinline__ int32_t scalar_load_i32(const int32_t* p) {
+  int32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+
+// Direct global->LDS copy of 16 bytes per lane: lane l's bytes land at LDS
+// address lds + 16 l.  Issued as assembly so that the compiler, which cannot
+// tell LDS stages apart, does not drain every outstanding copy before each LDS
+// read; the caller waits on vmcnt itself (copies complete in issue order) and
+// issues no compiler-visible vector load between a copy and its wait.
+__device__ __forceinline__ void copy16_to_lds(const void* src, const void* lds) {
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const char*)(lds)));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m0) : "memory", "m0");
+}
+
 __device__ __forceinline__ bf16x8 join(const s16x4& lo, const s16x4& hi) {
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -317,29 +338,44 @@ __global__ __launch_bounds__(256, 4) void decode_group_mfma_kernel(pkv_decode_ar
 // the cache); query i sits at position ctx - n + i and attends keys 0..ctx-n+i.
 // The rows of KV head kvh are (query i, head kvh*G + r) for r < G, numbered
 // token-major so that a 16-row MFMA tile spans few positions; a workgroup takes
-// 128 consecutive rows (4 waves x 2 tiles).  The workgroup walks the keys two
-// blocks (32 keys) at a time: all 256 threads stage the pair's K and V tiles
-// into LDS (double-buffered, one barrier per pair), and every wave reads K in
-// the A-operand layout and V^T with transposed reads, shared by its two row
-// tiles.  Pairs past a tile's last causal position are skipped for that tile.
+// 128 consecutive rows (4 waves x 2 tiles), so every K/V element it stages is
+// used by 128 rows.
+//
+// Keys are walked two blocks (32 keys) at a time through a ring of kStages
+// LDS stages.  A stage holds the pair's K and V tiles; the 256 threads fill it
+// with direct global->LDS copies (16 bytes per lane, no registers), kStages-1
+// pairs ahead of the pair being computed, so the copies of later pairs are in
+// flight while this one is on the matrix cores.  One barrier per pair: after
+// it, the stage of the pair computed last is free and is refilled.  K rows keep
+// their 16-byte slots XOR-swizzled by row (slot ^ r mod slots), V rows by
+// vswz, so that the A-operand reads of K and the transposed reads of V spread
+// over the LDS banks.  Keys past the context are copied from key 0 of the pair
+// (finite data) and masked to probability 0; pairs past a tile's last causal
+// position are skipped for that tile.
+//
 // Workgroup b takes group (s, kvh) = b % (S*Hkv) and row tile b / (S*Hkv), so
 // when S*Hkv is a multiple of 8 the tiles of one group share an XCD (dispatch
 // is round-robin over the 8 XCDs) and read the same K/V from that XCD's L2.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void prefill_chunk_mfma_kernel(pkv_prefill_args a) {
+__device__ __forceinline__ int kswz(int r) { return r % (D * 2 / 16); }
+
+constexpr int kPrefillWaves = 8;                     // waves per prefill workgroup
+constexpr int kPrefillThreads = 64 * kPrefillWaves;
+
+template <int D>
+__global__ __launch_bounds__(kPrefillThreads) void prefill_chunk_mfma_kernel(pkv_prefill_args a) {
   constexpr int KC = D / 32;
   constexpr int DC = D / 16;
   constexpr int RB = D * 2;
-  constexpr int KROW = RB + 16;          // padded LDS row of K
-  constexpr int VROW = RB + 32;          // padded LDS row of V
-  constexpr int kTiles = 2;              // 16-row tiles per wave
-  constexpr int64_t kTile = static_cast<int64_t>(kBlock) * RB;
-  constexpr int kChunks = 4 * kBlock * RB / 16;   // 16-byte chunks of a pair's K and V tiles
-  constexpr int kPerThread = kChunks / 256;
-  static_assert(kChunks % 256 == 0, "pair staging");
-  __shared__ __align__(16) char sk[2][2 * kBlock * KROW];
-  __shared__ __align__(16) char sv[2][2 * kBlock * VROW];
+  constexpr int kTiles = kPrefillRowsPerWg / 16 / kPrefillWaves;   // 16-row tiles per wave
+  constexpr int kStages = 4;                       // LDS ring depth (pairs)
+  constexpr int kTileBytes = kBlock * RB;          // one block's K (or V) rows of one head
+  constexpr int kStageBytes = 4 * kTileBytes;      // K0 K1 V0 V1
+  constexpr int kCopies = kStageBytes / (16 * kPrefillThreads);   // 16-byte copies per thread per stage
+  static_assert(kStageBytes % (16 * kPrefillThreads) == 0 && kTiles >= 1, "prefill shape");
+  constexpr int64_t kTile = kTileBytes;
+  __shared__ __align__(16) char ring[kStages][kStageBytes];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -360,7 +396,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_mfma_kernel(pkv_prefill_arg
   const int32_t r_end = min(rows, r0 + kPrefillRowsPerWg);
   const int32_t ctx = a.context_lens[s];
   if (ctx < nq || !len_ok(ctx, a.max_context_len, a.max_blocks_per_seq)) {
-    for (int idx = threadIdx.x; idx < (r_end - r0) * D; idx += 256) {
+    for (int idx = threadIdx.x; idx < (r_end - r0) * D; idx += kPrefillThreads) {
       const int32_t r = r0 + idx / D, d = idx % D;
       a.out[((static_cast<int64_t>(q0) + r / G) * Hq + kvh * G + r % G) * D + d] = __builtin_nanf("");
     }
@@ -372,13 +408,47 @@ __global__ __launch_bounds__(256) void prefill_chunk_mfma_kernel(pkv_prefill_arg
   const char* __restrict__ kc = reinterpret_cast<const char*>(a.k_cache) + kvh * kTile;
   const char* __restrict__ vc = reinterpret_cast<const char*>(a.v_cache) + kvh * kTile;
 
+  const int32_t wg_lim = first_pos + (r_end - 1) / G + 1;      // keys the workgroup needs
+  const int32_t npairs = (wg_lim + 2 * kBlock - 1) / (2 * kBlock);
+  const int32_t nblk = (ctx + kBlock - 1) / kBlock;
+  bool bad = false;
+
+  // Copies of pair pp into stage pp % kStages.  Copy i of wave w fills KiB
+  // kPrefillWaves*i + w of the stage: tile t = that KiB / (tile KiB), rows of
+  // the tile in lane order; each lane fetches the global 16 bytes its (row,
+  // slot) holds.
+  auto issue = [&](int32_t pp) {
+    char* stage = ring[pp % kStages];
+    int32_t id0 = scalar_load_i32(table + 2 * pp);
+    int32_t id1 = 2 * pp + 1 < nblk ? scalar_load_i32(table + 2 * pp + 1) : id0;
+    if (static_cast<uint32_t>(id0) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; id0 = 0; }
+    if (static_cast<uint32_t>(id1) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; id1 = 0; }
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) {
+      const int kib = kPrefillWaves * i + wave;
+      const int t = kib / (kTileBytes / 1024);                 // 0: K0, 1: K1, 2: V0, 3: V1
+      const int off = (kib % (kTileBytes / 1024)) * 1024 + 16 * lane;
+      const int r = off / RB, k = (off % RB) / 16;
+      const int b = t & 1;
+      const int32_t j = 2 * pp + b;
+      // a key past the context, or a missing second block, takes key 0 of the
+      // pair's first block: finite data that gets probability 0
+      const int row = j * kBlock + r < ctx ? r : 0;
+      const int32_t id = (b == 0 || j >= nblk) ? id0 : id1;
+      const int slot = t < 2 ? (k ^ kswz<D>(r)) : (k ^ vswz<D>(r));
+      const char* src = (t < 2 ? kc : vc) + id * block_bytes + row * RB + 16 * slot;
+      copy16_to_lds(src, stage + kib * 1024);
+    }
+  };
+  for (int32_t pp = 0; pp < kStages - 1 && pp < npairs; ++pp) issue(pp);
+
   // this lane's rows (one per tile) and their key limits; invalid rows: limit 0, q = 0
   bf16x8 qb[kTiles][KC];
   int32_t lim[kTiles];
   int32_t tile_lim[kTiles];      // keys any row of the tile needs (uniform)
 #pragma unroll
   for (int tt = 0; tt < kTiles; ++tt) {
-    const int32_t rbase = r0 + wave * 32 + tt * 16;
+    const int32_t rbase = r0 + (wave * kTiles + tt) * 16;
     const int32_t r = rbase + n;
     const bool valid = r < r_end;
     const int32_t i = valid ? r / G : 0;
@@ -394,9 +464,6 @@ __global__ __launch_bounds__(256) void prefill_chunk_mfma_kernel(pkv_prefill_arg
       qb[tt][c] = as_bf16x8(w);
     }
   }
-  const int32_t wg_lim = first_pos + (r_end - 1) / G + 1;      // keys the workgroup needs
-  const int32_t npairs = (wg_lim + 2 * kBlock - 1) / (2 * kBlock);
-  const int32_t nblk = (ctx + kBlock - 1) / kBlock;
 
   f32x4 o[kTiles][DC];
   float m[kTiles], lsum[kTiles];
@@ -407,113 +474,99 @@ __global__ __launch_bounds__(256) void prefill_chunk_mfma_kernel(pkv_prefill_arg
 #pragma unroll
     for (int c = 0; c < DC; ++c) o[tt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  bool bad = false;
+  // per-lane LDS offsets within a stage: K A-operand rows (key n of each block,
+  // slot 4c + g) and the V transposed-read rows (key 4g + n/4)
+  const int k_row = n * RB;
+  const int k_sw = kswz<D>(n);
+  const int tr_row = 4 * g + (n >> 2);
+  const int tr_sw = vswz<D>(tr_row);
+  const int tr_k0 = (n & 3) >> 1;
 
-  // staging: thread chunk q -> tile q / (kBlock*RB/16) in {K0, K1, V0, V1}
-  u32x4 stage[kPerThread];
-  auto load_pair = [&](int32_t pp) {
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int q = threadIdx.x + 256 * i;
-      const int which = q / (kBlock * RB / 16);
-      const int off = (q % (kBlock * RB / 16)) * 16;
-      const int32_t j = 2 * pp + (which & 1);
-      u32x4 w = u32x4{0, 0, 0, 0};
-      if (j < nblk) {
-        int32_t id = table[j];
-        if (static_cast<uint32_t>(id) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; id = 0; }
-        const char* base = (which < 2 ? kc : vc) + id * block_bytes;
-        w = load16_nt(base + off);
-      }
-      stage[i] = w;
-    }
-  };
-  auto store_pair = [&](int32_t pp, int buf) {
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int q = threadIdx.x + 256 * i;
-      const int which = q / (kBlock * RB / 16);
-      const int off = (q % (kBlock * RB / 16)) * 16;
-      const int tok = off / RB, col = off % RB;
-      const int b = which & 1;
-      u32x4 w = stage[i];
-      if (which < 2) {
-        *reinterpret_cast<u32x4*>(&sk[buf][(b * kBlock + tok) * KROW + col]) = w;
-      } else {
-        if ((2 * pp + b) * kBlock + tok >= ctx) w = u32x4{0, 0, 0, 0};
-        *reinterpret_cast<u32x4*>(&sv[buf][(b * kBlock + tok) * VROW + col]) = w;
-      }
-    }
-  };
-
-  load_pair(0);
-  store_pair(0, 0);
-  __syncthreads();
   for (int32_t pp = 0; pp < npairs; ++pp) {
-    const int buf = pp & 1;
-    if (pp + 1 < npairs) load_pair(pp + 1);
+    // this pair's copies have landed once at most the later issued pairs'
+    // copies are outstanding (copies complete in issue order)
+    const int32_t ahead = min(kStages - 2, npairs - 1 - pp);
+    static_assert(kStages == 4 && (kCopies == 1 || kCopies == 2 || kCopies == 4), "wait counts");
+    if (ahead >= 2) {
+      if constexpr (kCopies == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else if constexpr (kCopies == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    } else if (ahead == 1) {
+      if constexpr (kCopies == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else if constexpr (kCopies == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+
+    const char* stage = ring[pp % kStages];
     const int32_t key0 = pp * 2 * kBlock;
     if (key0 < tile_lim[0] || key0 < tile_lim[1]) {
-      // K in the A-operand layout: key 16b + n, dims 32c + 8g
-      bf16x8 ka[2][KC];
+    bf16x8 ka[2][KC];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        ka[b][c] = as_bf16x8(*reinterpret_cast<const u32x4*>(stage + b * kTileBytes + k_row +
+                                                              16 * ((4 * c + g) ^ k_sw)));
+    bf16x8 va[DC];
+    const char* trb = stage + 2 * kTileBytes + tr_row * RB + 8 * (n & 1);
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      const int slot = 16 * ((2 * c + tr_k0) ^ tr_sw);
+      va[c] = join(lds_read_tr(trb + slot), lds_read_tr(trb + kTileBytes + slot));
+    }
+#pragma unroll
+    for (int tt = 0; tt < kTiles; ++tt) {
+      if (key0 >= tile_lim[tt]) continue;
+      float sc[2][4];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < KC; ++c) acc = mfma(ka[b][c], qb[tt][c], acc);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int32_t t = key0 + b * kBlock + 4 * g + jj;
+          sc[b][jj] = t < lim[tt] ? acc[jj] * a.scale_log2 : -INFINITY;
+        }
+      }
+      float mx = sc[0][0];
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int c = 0; c < KC; ++c)
-          ka[b][c] = as_bf16x8(*reinterpret_cast<const u32x4*>(&sk[buf][(b * kBlock + n) * KROW + 64 * c + 16 * g]));
-      bf16x8 va[DC];
-      const char* tr0 = &sv[buf][(4 * g + (n >> 2)) * VROW + 8 * (n & 3)];
+        for (int jj = 0; jj < 4; ++jj) mx = fmaxf(mx, sc[b][jj]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m[tt], mx);
+      const float alpha = fast_exp2(m[tt] - mnew);
+      m[tt] = mnew;
+      bf16x8 ph, pl;
+      float ps = 0.f;
 #pragma unroll
-      for (int c = 0; c < DC; ++c)
-        va[c] = join(lds_read_tr(tr0 + 32 * c), lds_read_tr(tr0 + kBlock * VROW + 32 * c));
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int tt = 0; tt < kTiles; ++tt) {
-        if (key0 >= tile_lim[tt]) continue;
-        float sc[2][4];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int c = 0; c < KC; ++c) acc = mfma(ka[b][c], qb[tt][c], acc);
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int32_t t = key0 + b * kBlock + 4 * g + jj;
-            sc[b][jj] = t < lim[tt] ? acc[jj] * a.scale_log2 : -INFINITY;
-          }
+        for (int jj = 0; jj < 4; ++jj) {
+          const float pr = fast_exp2(sc[b][jj] - mnew);
+          ps += pr;
+          const __bf16 hi = static_cast<__bf16>(pr);
+          ph[4 * b + jj] = hi;
+          pl[4 * b + jj] = static_cast<__bf16>(pr - static_cast<float>(hi));
         }
-        float mx = sc[0][0];
+      lsum[tt] = lsum[tt] * alpha + ps;
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) mx = fmaxf(mx, sc[b][jj]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(m[tt], mx);
-        const float alpha = fast_exp2(m[tt] - mnew);
-        m[tt] = mnew;
-        bf16x8 ph, pl;
-        float ps = 0.f;
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const float pr = fast_exp2(sc[b][jj] - mnew);
-            ps += pr;
-            const __bf16 hi = static_cast<__bf16>(pr);
-            ph[4 * b + jj] = hi;
-            pl[4 * b + jj] = static_cast<__bf16>(pr - static_cast<float>(hi));
-          }
-        lsum[tt] = lsum[tt] * alpha + ps;
-#pragma unroll
-        for (int c = 0; c < DC; ++c) {
-          f32x4 acc = o[tt][c] * alpha;
-          acc = mfma(va[c], ph, acc);
-          o[tt][c] = mfma(va[c], pl, acc);
-        }
+      for (int c = 0; c < DC; ++c) {
+        f32x4 acc = o[tt][c] * alpha;
+        acc = mfma(va[c], ph, acc);
+        o[tt][c] = mfma(va[c], pl, acc);
       }
     }
-    if (pp + 1 < npairs) store_pair(pp + 1, buf ^ 1);
-    __syncthreads();
+    }
+    // every wave passed the barrier after it finished the pair before this
+    // one, so that pair's stage takes pair pp + kStages - 1
+    if (pp + kStages - 1 < npairs) issue(pp + kStages - 1);
   }
 
   // a bad block id anywhere in the workgroup's range poisons its rows
@@ -523,7 +576,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_mfma_kernel(pkv_prefill_arg
     float L = lsum[tt];
     L += __shfl_xor(L, 16);
     L += __shfl_xor(L, 32);
-    const int32_t r = r0 + wave * 32 + tt * 16 + n;
+    const int32_t r = r0 + (wave * kTiles + tt) * 16 + n;
     if (r >= r_end) continue;
     const float inv = any_bad ? __builtin_nanf("") : 1.f / L;
     float* orow = a.out + ((static_cast<int64_t>(q0) + r / G) * Hq + kvh * G + r % G) * D;
@@ -556,9 +609,11 @@ int pkv_launch_prefill(const pkv_prefill_args& a, void* stream) {
   if (grid == 0) return hipSuccess;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (a.head_dim == 128) {
-    hipLaunchKernelGGL((prefill_chunk_mfma_kernel<128>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_chunk_mfma_kernel<128>), dim3(static_cast<uint32_t>(grid)), dim3(kPrefillThreads), 0,
+                       st, a);
   } else {
-    hipLaunchKernelGGL((prefill_chunk_mfma_kernel<64>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((prefill_chunk_mfma_kernel<64>), dim3(static_cast<uint32_t>(grid)), dim3(kPrefillThreads), 0,
+                       st, a);
   }
   return hipGetLastError();
 }

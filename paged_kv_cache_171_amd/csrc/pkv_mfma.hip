@@ -100,7 +100,7 @@ __device__ __forceinline__ bf16x8 join(const s16x4& lo, const s16x4& hi) {
 
 // ---------------------------------------------------------------------------
 // Decode for a query-head group.  One workgroup per (unit, KV head), where a
-// unit is a (sequence, 512-token partition) of the plan (longest first).  The
+// unit is a (sequence, 4096-token partition) of the plan (longest first).  The
 // G query heads of the group are the 16 MFMA rows (rows >= G hold q = 0 and are
 // never written).  The unit's blocks are dealt to the 4 waves in turn; per
 // block a wave

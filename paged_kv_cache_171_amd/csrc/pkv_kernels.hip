@@ -367,10 +367,15 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(pkv_decode_args a) {
         tb[bi] = j * kBlock;
         const u32x4* kp = reinterpret_cast<const u32x4*>(kc + b * block_bytes + head_off);
         const u32x4* vp = reinterpret_cast<const u32x4*>(vc + b * block_bytes + head_off);
+        // rows past the context (the tail of a sequence's last block) are not
+        // loaded: those lanes read nothing and hold 0
+        const int32_t valid = ctx - j * kBlock;
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) kt[bi][i] = __builtin_nontemporal_load(kp + i * 64 + lane);
+        for (int i = 0; i < NLD; ++i)
+          kt[bi][i] = i * TPL + row < valid ? __builtin_nontemporal_load(kp + i * 64 + lane) : u32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int i = 0; i < NLD; ++i) vt[bi][i] = __builtin_nontemporal_load(vp + i * 64 + lane);
+        for (int i = 0; i < NLD; ++i)
+          vt[bi][i] = i * TPL + row < valid ? __builtin_nontemporal_load(vp + i * 64 + lane) : u32x4{0, 0, 0, 0};
       }
     }
 #pragma unroll

@@ -234,9 +234,11 @@ __global__ __launch_bounds__(256, 4) void decode_group_mfma_kernel(pkv_decode_ar
     if (static_cast<uint32_t>(id) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; id = 0; }
     const char* kp = kc + id * block_bytes;
     const char* vp = vc + id * block_bytes;
-#pragma unroll
-    for (int c = 0; c < KC; ++c) kt[c] = load16_nt(kp + n * RB + 64 * c + 16 * g);
     const int32_t valid_rows = min(kBlock, ctx - j * kBlock);
+    // keys past the context are not loaded (their scores are masked)
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+      kt[c] = n < valid_rows ? load16_nt(kp + n * RB + 64 * c + 16 * g) : u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int src = (1024 * i + 16 * lane) / RB < valid_rows ? dma_off[i] : dma_off[i] % RB;
@@ -338,11 +340,11 @@ __global__ __launch_bounds__(256, 4) void decode_group_mfma_kernel(pkv_decode_ar
 // the cache); query i sits at position ctx - n + i and attends keys 0..ctx-n+i.
 // The rows of KV head kvh are (query i, head kvh*G + r) for r < G, numbered
 // token-major so that a 16-row MFMA tile spans few positions; a workgroup takes
-// 128 consecutive rows (4 waves x 2 tiles), so every K/V element it stages is
-// used by 128 rows.
+// 128 consecutive rows (8 waves x one 16-row tile), so every K/V element it
+// stages is used by 128 rows.
 //
 // Keys are walked two blocks (32 keys) at a time through a ring of kStages
-// LDS stages.  A stage holds the pair's K and V tiles; the 256 threads fill it
+// LDS stages.  A stage holds the pair's K and V tiles; the 512 threads fill it
 // with direct global->LDS copies (16 bytes per lane, no registers), kStages-1
 // pairs ahead of the pair being computed, so the copies of later pairs are in
 // flight while this one is on the matrix cores.  One barrier per pair: after

@@ -232,6 +232,7 @@ pkv_status pkv_allocator_create(int32_t num_blocks, int32_t block_size,
                                 pkv_allocator** out);
 void pkv_allocator_destroy(pkv_allocator* a);
 int32_t pkv_allocator_num_free(const pkv_allocator* a);
+int32_t pkv_allocator_num_blocks(const pkv_allocator* a);   /* pool size (-1 for NULL) */
 
 pkv_status pkv_seq_create(pkv_allocator* a, int64_t* seq_id);
 
@@ -271,6 +272,94 @@ pkv_status pkv_block_refcount(const pkv_allocator* a, int32_t block, int32_t* rc
 /* Free blocks that appending n_tokens to seq would take (admission check). */
 pkv_status pkv_seq_blocks_needed(const pkv_allocator* a, int64_t seq, int32_t n_tokens,
                                  int32_t* needed);
+
+/* ------------------------------------------------------------------------
+ * Continuous-batching scheduler (host).  [UL] "Cómo funciona la planificación a
+ * nivel de iteración": after every step finished sequences leave and free
+ * their memory and queued requests are admitted if they fit in the KV cache; a
+ * new request is prefilled in the same step as the others decode.  "Límites y
+ * técnicas complementarias": steps are capped in sequences (max_num_seqs) and
+ * tokens (max_num_batched_tokens).  [CB] "Juntándolo todo: Arquitectura de
+ * vLLM": admission needs enough free blocks; under memory pressure a request's
+ * blocks are copied to CPU memory and freed, and copied back later.
+ *
+ * A request of output length L holds its sequence slot for L steps: the step
+ * that admits it prefills its prompt (one token out), each of the next L-1
+ * steps decodes one token; it leaves at the start of the following step.
+ * Each pkv_scheduler_step, in order: (1) finished requests leave and their
+ * blocks are freed; (2) running requests, in admission order, take one decode
+ * slot each -- while the pool is short, the most recently admitted running
+ * request is swapped out (its blocks, in table order, to host blocks taken
+ * first in first out; if the host pool is full, that request and the later
+ * ones wait this step); (3) if nothing was swapped out, swapped requests return
+ * first in first out (a fresh table, then their decode slot); (4) queued
+ * requests are admitted first in first out -- never ahead of a swapped one --
+ * while a sequence slot, the token budget and free blocks for the whole prompt
+ * allow (PKV_SCHED_STATIC: only when nothing is running or swapped), their
+ * prompts taking slots.  The step's slot_mapping lists the prefill tokens
+ * (admission order) then one decode token per decoding request.
+ *
+ * The caller runs, on one stream and in this order: the swap-out copies
+ * (device block -> host block), the swap-in copies (host block -> device
+ * block), pkv_append of the step's K/V at slot_mapping, then prefill and
+ * decode attention.  The scheduler owns the allocator sequences it creates
+ * (pkv_scheduler_request gives a request's sequence id for block tables); the
+ * caller must not free or fork them.  Not thread-safe.
+ * ------------------------------------------------------------------------ */
+typedef struct pkv_scheduler pkv_scheduler;
+typedef enum { PKV_SCHED_CONTINUOUS = 0, PKV_SCHED_STATIC = 1 } pkv_sched_policy;
+typedef enum { PKV_REQ_WAITING = 0, PKV_REQ_RUNNING = 1, PKV_REQ_SWAPPED = 2, PKV_REQ_FINISHED = 3 } pkv_req_state;
+
+typedef struct {
+  int32_t num_finished;        /* requests that left at the start of this step   */
+  int32_t num_swapped_out;     /* requests moved to host memory                  */
+  int32_t num_swap_out_pairs;  /* (device block, host block) copies              */
+  int32_t num_swapped_in;      /* requests back from host memory (they decode)   */
+  int32_t num_swap_in_pairs;   /* (host block, device block) copies              */
+  int32_t num_prefill;         /* requests admitted and prefilled                */
+  int32_t num_prefill_tokens;  /* their prompt tokens                            */
+  int32_t num_decode;          /* requests decoding one token                    */
+} pkv_step_info;
+
+/* alloc: the allocator whose blocks the scheduler manages (not owned).
+ * num_host_blocks: host swap space in blocks (0 = no swapping). */
+pkv_status pkv_scheduler_create(pkv_allocator* alloc, int32_t max_num_seqs, int32_t max_num_batched_tokens,
+                                pkv_sched_policy policy, int32_t num_host_blocks, pkv_scheduler** out);
+void pkv_scheduler_destroy(pkv_scheduler* s);
+
+/* Queue a request; ids are 0, 1, 2, ... in call order.  Rejected (nothing
+ * queued) if prompt_len is outside [1, max_num_batched_tokens], output_len < 1
+ * (PKV_ERR_INVALID_ARG), or prompt+output tokens exceed the whole pool
+ * (PKV_ERR_OUT_OF_BLOCKS). */
+pkv_status pkv_scheduler_add_request(pkv_scheduler* s, int32_t prompt_len, int32_t output_len,
+                                     int64_t* request_id);
+
+/* One step (see above); *info gets the sizes of its output.  A step with no
+ * request left to run schedules nothing (all counts but num_finished 0).
+ * PKV_ERR_OUT_OF_BLOCKS: requests remain but none can run (host swap space
+ * exhausted); finished requests have still left. */
+pkv_status pkv_scheduler_step(pkv_scheduler* s, pkv_step_info* info);
+
+/* Copy out the last step's lists (each pointer may be NULL to skip it), sized by
+ * its pkv_step_info: finished[num_finished], swapped_out[num_swapped_out],
+ * swap_out_pairs[num_swap_out_pairs][2], swapped_in[num_swapped_in],
+ * swap_in_pairs[num_swap_in_pairs][2], prefill[num_prefill],
+ * prefill_query_start_loc[num_prefill + 1], decode[num_decode],
+ * slot_mapping[num_prefill_tokens + num_decode]. */
+pkv_status pkv_scheduler_step_output(const pkv_scheduler* s, int64_t* finished, int64_t* swapped_out,
+                                     int32_t* swap_out_pairs, int64_t* swapped_in, int32_t* swap_in_pairs,
+                                     int64_t* prefill, int32_t* prefill_query_start_loc, int64_t* decode,
+                                     int64_t* slot_mapping);
+
+/* A request's state (pkv_req_state), allocator sequence id (-1 unless running),
+ * tokens generated so far and cached context length.  Pointers may be NULL. */
+pkv_status pkv_scheduler_request(const pkv_scheduler* s, int64_t request_id, int32_t* state, int64_t* seq_id,
+                                 int32_t* generated, int32_t* context_len);
+
+/* Steps that ran, request-steps (busy sequence slots summed over steps), and
+ * the current queue sizes.  Pointers may be NULL. */
+pkv_status pkv_scheduler_stats(const pkv_scheduler* s, int64_t* steps, int64_t* busy_slot_steps,
+                               int32_t* num_waiting, int32_t* num_running, int32_t* num_swapped);
 
 #ifdef __cplusplus
 }

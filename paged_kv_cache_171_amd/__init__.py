@@ -5,10 +5,11 @@ declared in ``include/pkv.h``); this package is its ctypes binding.  Build the
 library with ``python -m paged_kv_cache_171_amd.build``.
 """
 from .binding import (  # noqa: F401
-    BlockAllocator, PkvError, LIB_PATH, EXPORTED,
+    BlockAllocator, Scheduler, PkvError, LIB_PATH, EXPORTED,
     pkv_version, pkv_append, pkv_copy_blocks, pkv_attention_workspace_bytes,
     pkv_attention_decode, pkv_attention_prefill_chunk, pkv_decode_plan_bytes, pkv_decode_plan, plan_for,
     workspace_for,
     PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_OUT_OF_BLOCKS, PKV_ERR_UNSUPPORTED, PKV_ERR_HIP,
-    PKV_ERR_UNKNOWN_SEQ, PKV_F32, PKV_BF16,
+    PKV_ERR_UNKNOWN_SEQ, PKV_F32, PKV_BF16, PKV_SCHED_CONTINUOUS, PKV_SCHED_STATIC,
+    PKV_REQ_WAITING, PKV_REQ_RUNNING, PKV_REQ_SWAPPED, PKV_REQ_FINISHED,
 )

@@ -22,6 +22,8 @@ _lib = ctypes.CDLL(_LIB_PATH)
 
 PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_OUT_OF_BLOCKS, PKV_ERR_UNSUPPORTED, PKV_ERR_HIP, PKV_ERR_UNKNOWN_SEQ = range(6)
 PKV_F32, PKV_BF16 = 0, 1
+PKV_SCHED_CONTINUOUS, PKV_SCHED_STATIC = 0, 1
+PKV_REQ_WAITING, PKV_REQ_RUNNING, PKV_REQ_SWAPPED, PKV_REQ_FINISHED = range(4)
 STATUS_NAMES = {0: "PKV_OK", 1: "PKV_ERR_INVALID_ARG", 2: "PKV_ERR_OUT_OF_BLOCKS",
                 3: "PKV_ERR_UNSUPPORTED", 4: "PKV_ERR_HIP", 5: "PKV_ERR_UNKNOWN_SEQ"}
 
@@ -48,6 +50,14 @@ _SIGS = {
     "pkv_allocator_create": (_c_i32, [_c_i32, _c_i32, _c_p, ctypes.POINTER(_c_p)]),
     "pkv_allocator_destroy": (None, [_c_p]),
     "pkv_allocator_num_free": (_c_i32, [_c_p]),
+    "pkv_allocator_num_blocks": (_c_i32, [_c_p]),
+    "pkv_scheduler_create": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(_c_p)]),
+    "pkv_scheduler_destroy": (None, [_c_p]),
+    "pkv_scheduler_add_request": (_c_i32, [_c_p, _c_i32, _c_i32, _P_I64]),
+    "pkv_scheduler_step": (_c_i32, [_c_p, _c_p]),
+    "pkv_scheduler_step_output": (_c_i32, [_c_p] + [_c_p] * 9),
+    "pkv_scheduler_request": (_c_i32, [_c_p, _c_i64, _P_I32, _P_I64, _P_I32, _P_I32]),
+    "pkv_scheduler_stats": (_c_i32, [_c_p, _P_I64, _P_I64, _P_I32, _P_I32, _P_I32]),
     "pkv_seq_create": (_c_i32, [_c_p, _P_I64]),
     "pkv_seq_append_slots": (_c_i32, [_c_p, _c_i64, _c_i32, _c_p, _c_p, _P_I32]),
     "pkv_seq_append_slots_batch": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_p, _c_p, _P_I32]),
@@ -275,3 +285,77 @@ class BlockAllocator:
         r = _c_i32()
         _check(_lib.pkv_seq_blocks_needed(self._h, seq, n, ctypes.byref(r)))
         return r.value
+
+
+class _StepInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_finished", "num_swapped_out", "num_swap_out_pairs", "num_swapped_in", "num_swap_in_pairs",
+        "num_prefill", "num_prefill_tokens", "num_decode")]
+
+
+class Step:
+    """One scheduler step's output (host numpy arrays)."""
+
+    def __init__(self, info: _StepInfo, h):
+        def arr(n, dt, shape=None):
+            return np.empty(shape if shape is not None else max(n, 0), dtype=dt)
+        self.finished = arr(info.num_finished, np.int64)
+        self.swapped_out = arr(info.num_swapped_out, np.int64)
+        self.swap_out_pairs = arr(0, np.int32, (info.num_swap_out_pairs, 2))
+        self.swapped_in = arr(info.num_swapped_in, np.int64)
+        self.swap_in_pairs = arr(0, np.int32, (info.num_swap_in_pairs, 2))
+        self.prefill = arr(info.num_prefill, np.int64)
+        self.prefill_query_start_loc = arr(info.num_prefill + 1, np.int32)
+        self.decode = arr(info.num_decode, np.int64)
+        self.slot_mapping = arr(info.num_prefill_tokens + info.num_decode, np.int64)
+        _check(_lib.pkv_scheduler_step_output(
+            h, self.finished.ctypes.data, self.swapped_out.ctypes.data, self.swap_out_pairs.ctypes.data,
+            self.swapped_in.ctypes.data, self.swap_in_pairs.ctypes.data, self.prefill.ctypes.data,
+            self.prefill_query_start_loc.ctypes.data, self.decode.ctypes.data, self.slot_mapping.ctypes.data))
+
+    @property
+    def empty(self) -> bool:
+        return len(self.prefill) == 0 and len(self.decode) == 0
+
+
+class Scheduler:
+    """Host continuous-batching scheduler (pkv_scheduler_*) over a BlockAllocator."""
+
+    def __init__(self, alloc: "BlockAllocator", max_num_seqs: int, max_num_batched_tokens: int,
+                 policy: int = PKV_SCHED_CONTINUOUS, num_host_blocks: int = 0):
+        h = _c_p()
+        _check(_lib.pkv_scheduler_create(alloc._h, max_num_seqs, max_num_batched_tokens, policy, num_host_blocks,
+                                         ctypes.byref(h)))
+        self._h = h
+        self.alloc = alloc            # keeps the allocator alive
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            _lib.pkv_scheduler_destroy(h)
+            self._h = None
+
+    def add_request(self, prompt_len: int, output_len: int) -> int:
+        rid = _c_i64()
+        _check(_lib.pkv_scheduler_add_request(self._h, prompt_len, output_len, ctypes.byref(rid)))
+        return rid.value
+
+    def step(self) -> Step:
+        info = _StepInfo()
+        _check(_lib.pkv_scheduler_step(self._h, ctypes.byref(info)))
+        return Step(info, self._h)
+
+    def request(self, rid: int):
+        """(state, seq_id, generated, context_len)"""
+        st, seq, gen, ctx = _c_i32(), _c_i64(), _c_i32(), _c_i32()
+        _check(_lib.pkv_scheduler_request(self._h, rid, ctypes.byref(st), ctypes.byref(seq), ctypes.byref(gen),
+                                          ctypes.byref(ctx)))
+        return st.value, seq.value, gen.value, ctx.value
+
+    def stats(self):
+        """(steps, busy_slot_steps, num_waiting, num_running, num_swapped)"""
+        a, b = _c_i64(), _c_i64()
+        w, r, sw = _c_i32(), _c_i32(), _c_i32()
+        _check(_lib.pkv_scheduler_stats(self._h, ctypes.byref(a), ctypes.byref(b), ctypes.byref(w), ctypes.byref(r),
+                                        ctypes.byref(sw)))
+        return a.value, b.value, w.value, r.value, sw.value

@@ -111,6 +111,8 @@ int32_t pkv_allocator_num_free(const pkv_allocator* a) {
   return a ? static_cast<int32_t>(a->free_list.size()) : -1;
 }
 
+int32_t pkv_allocator_num_blocks(const pkv_allocator* a) { return a ? a->num_blocks : -1; }
+
 pkv_status pkv_seq_create(pkv_allocator* a, int64_t* seq_id) {
   if (!a || !seq_id) return pkv_fail(PKV_ERR_INVALID_ARG, "pkv_seq_create: NULL argument");
   const int64_t id = a->next_id++;

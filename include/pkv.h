@@ -104,6 +104,30 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst,
                            void* stream);
 
 /* ------------------------------------------------------------------------
+ * Swap copies between pools.  [CB] "Juntándolo todo: Arquitectura de vLLM":
+ * under memory pressure a request's KV blocks are copied to CPU memory and its
+ * GPU blocks freed; when memory allows they are copied back and the request
+ * resumes.
+ *
+ *   for i in [0, num_pairs): dst_k[dst_i] = src_k[src_i]; dst_v[dst_i] = src_v[src_i]
+ *
+ * with (src_i, dst_i) = (src_dst[2i], src_dst[2i+1]) (int32, device or pinned
+ * host memory), whole blocks.  Each pool is [num_blocks][num_kv_heads][16]
+ * [head_dim] in `dtype`, in device memory or in pinned host memory (e.g.
+ * hipHostMalloc, torch pin_memory) that the device sees at the same address,
+ * which the kernel reads or writes over the host link; pageable host memory
+ * is rejected (PKV_ERR_INVALID_ARG, nothing launched).  The pools' 16-byte
+ * alignment and the pair array's placement are checked the same way.  Pairs with an id outside their pool are skipped.
+ * Destinations must be distinct and, when both pools are the same memory, not
+ * among the sources.  Host-side data is read or written asynchronously: the
+ * caller synchronises the stream before touching it.
+ * ------------------------------------------------------------------------ */
+pkv_status pkv_swap_blocks(void* dst_k_cache, void* dst_v_cache, int32_t dst_num_blocks, const void* src_k_cache,
+                           const void* src_v_cache, int32_t src_num_blocks, const int32_t* src_dst,
+                           int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           pkv_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------------------
  * Decode attention.  [OS] "Cómo funciona por dentro": the kernel follows the
  * block table to each block, scores the query against the block's keys and
  * forms one softmax-weighted sum of the values; [IPX] "Separar orden lógico y

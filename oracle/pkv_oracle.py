@@ -210,6 +210,23 @@ def copy_blocks(k_pool: np.ndarray, v_pool: np.ndarray, pairs: Sequence[Tuple[in
             pool[d] = before[s]
 
 
+def swap_blocks(dst_k: np.ndarray, dst_v: np.ndarray, src_k: np.ndarray, src_v: np.ndarray,
+                pairs: Sequence[Tuple[int, int]]) -> None:
+    """dst[d] = src[s] between two pools (a swap to or from CPU memory).
+
+    [CB] "Juntándolo todo: Arquitectura de vLLM": a preempted request's KV
+    blocks are copied out to CPU memory and their GPU blocks freed; when memory
+    is available they are copied back and the request resumes.  Whole blocks,
+    bit for bit; destinations distinct."""
+    pairs = [(int(s), int(d)) for s, d in pairs]
+    dsts = [d for _, d in pairs]
+    if len(set(dsts)) != len(dsts):
+        raise ValueError("swap destinations must be distinct")
+    for dst, src in ((_bits(dst_k), _bits(src_k)), (_bits(dst_v), _bits(src_v))):
+        for s, d in pairs:
+            dst[d] = src[s]
+
+
 # ---------------------------------------------------------------------------
 # Attention.
 # [OS] "Cómo funciona por dentro": attention walks the sequence's blocks in

@@ -36,6 +36,8 @@ _SIGS = {
     "pkv_version": (ctypes.c_char_p, []),
     "pkv_append": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_p]),
     "pkv_copy_blocks": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_p]),
+    "pkv_swap_blocks": (_c_i32, [_c_p, _c_p, _c_i32, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32, _c_i32,
+                                 _c_i32, _c_p]),
     "pkv_attention_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32]),
     "pkv_attention_decode": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32,
                                       _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_p, _c_sz, _c_p]),
@@ -132,6 +134,25 @@ def pkv_copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src_dst: torch
     _check(_lib.pkv_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), src_dst.data_ptr(),
                                 src_dst.shape[0] if src_dst.dim() == 2 else src_dst.numel() // 2,
                                 nb, hkv, d, bs, _dtype_code(k_cache), _stream(stream)))
+
+
+def pkv_swap_blocks(dst_k_cache: torch.Tensor, dst_v_cache: torch.Tensor, src_k_cache: torch.Tensor,
+                    src_v_cache: torch.Tensor, src_dst: torch.Tensor, stream=None) -> None:
+    """dst[d] = src[s] for (s, d) in src_dst (int32 [n, 2]); each pool [NB, Hkv, 16, d]
+    on the GPU or in pinned host memory.  Host pools are touched asynchronously:
+    synchronise the stream before reading or reusing them."""
+    for t in (dst_k_cache, dst_v_cache, src_k_cache, src_v_cache, src_dst):
+        if not t.is_contiguous() or not (t.is_cuda or t.is_pinned()):
+            raise ValueError("expected contiguous GPU or pinned host tensors")
+    assert src_dst.dtype == torch.int32
+    assert dst_k_cache.dtype == dst_v_cache.dtype == src_k_cache.dtype == src_v_cache.dtype
+    assert dst_k_cache.shape[1:] == src_k_cache.shape[1:]
+    assert dst_v_cache.shape == dst_k_cache.shape and src_v_cache.shape == src_k_cache.shape
+    nb_dst, hkv, bs, d = dst_k_cache.shape
+    _check(_lib.pkv_swap_blocks(dst_k_cache.data_ptr(), dst_v_cache.data_ptr(), nb_dst, src_k_cache.data_ptr(),
+                                src_v_cache.data_ptr(), src_k_cache.shape[0], src_dst.data_ptr(),
+                                src_dst.shape[0] if src_dst.dim() == 2 else src_dst.numel() // 2,
+                                hkv, d, bs, _dtype_code(dst_k_cache), _stream(stream)))
 
 
 def pkv_attention_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int) -> int:

@@ -117,6 +117,45 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst,
                                                block_bytes, stream));
 }
 
+// Whether a kernel may dereference `p` as is: device (or managed) memory, or
+// pinned host memory that the runtime maps at the same virtual address on the
+// device.  Pageable host memory and pinned memory mapped elsewhere are refused.
+static bool device_accessible(const void* p) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged) return true;
+  if (attr.type == hipMemoryTypeHost) return attr.devicePointer && attr.devicePointer == attr.hostPointer;
+  return false;
+}
+
+pkv_status pkv_swap_blocks(void* dst_k_cache, void* dst_v_cache, int32_t dst_num_blocks, const void* src_k_cache,
+                           const void* src_v_cache, int32_t src_num_blocks, const int32_t* src_dst,
+                           int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           pkv_dtype dtype, void* stream) {
+  const char* fn = "pkv_swap_blocks";
+  pkv_status st = check_common(fn, num_kv_heads, head_dim, block_size, dtype);
+  if (st != PKV_OK) return st;
+  if (num_pairs < 0) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: num_pairs < 0", fn);
+  if (dst_num_blocks <= 0 || src_num_blocks <= 0)
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: block counts must be > 0", fn);
+  if (num_pairs == 0) return PKV_OK;
+  if (!dst_k_cache || !dst_v_cache || !src_k_cache || !src_v_cache || !src_dst)
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(dst_k_cache) || !aligned16(dst_v_cache) || !aligned16(src_k_cache) || !aligned16(src_v_cache))
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: pool pointers must be 16-byte aligned", fn);
+  if (!device_accessible(dst_k_cache) || !device_accessible(dst_v_cache) || !device_accessible(src_k_cache) ||
+      !device_accessible(src_v_cache))
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: pools must be device memory or pinned host memory", fn);
+  if (!device_accessible(src_dst))
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: src_dst must be device memory or pinned host memory", fn);
+  const int64_t block_bytes = static_cast<int64_t>(num_kv_heads) * kBlock * head_dim * elem_bytes(dtype);
+  return hip_status(fn, pkv_launch_swap_blocks(dst_k_cache, dst_v_cache, dst_num_blocks, src_k_cache, src_v_cache,
+                                               src_num_blocks, src_dst, num_pairs, block_bytes, stream));
+}
+
 size_t pkv_decode_plan_bytes(int32_t num_seqs, int32_t max_context_len) {
   if (num_seqs <= 0 || max_context_len < 0) return 0;
   return plan_bytes(num_seqs, max_context_len);

@@ -17,6 +17,10 @@ int pkv_launch_append(void* k_cache, void* v_cache, const void* k, const void* v
                       int32_t num_kv_heads, int32_t row_bytes, void* stream);
 int pkv_launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst, int32_t num_pairs,
                            int32_t num_blocks, int64_t block_bytes, void* stream);
+// Block copies between two pools (device pointers; a host pool by its mapped address).
+int pkv_launch_swap_blocks(void* k_dst, void* v_dst, int32_t dst_blocks, const void* k_src, const void* v_src,
+                           int32_t src_blocks, const int32_t* src_dst, int32_t num_pairs, int64_t block_bytes,
+                           void* stream);
 
 // Context partitions of the decode work split (multiples of 16 tokens): 1024
 // tokens for the VALU kernel, 4096 for the MFMA group kernel (which reads

@@ -59,26 +59,31 @@ __global__ __launch_bounds__(256) void append_kernel(char* __restrict__ k_cache,
 // ---------------------------------------------------------------------------
 // Copy-on-write block copy ([IPX] "Dos respuestas a una entrada").  A block is
 // num_kv_heads * 16 * row_bytes contiguous bytes in each pool; workgroup
-// (pair, chunk) streams 4 KiB chunks of it with 16-byte loads and stores.
+// (pair, chunk) streams 4 KiB chunks of it with 16-byte loads and stores.  The
+// same kernel swaps blocks between pools ([CB] "Juntándolo todo: Arquitectura
+// de vLLM": a preempted request's blocks go to CPU memory and come back):
+// source and destination may be different pools, one of them pinned host
+// memory mapped for the device.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ k_cache,
-                                                          char* __restrict__ v_cache,
+__global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ k_dst, char* __restrict__ v_dst,
+                                                          const char* __restrict__ k_src,
+                                                          const char* __restrict__ v_src,
                                                           const int32_t* __restrict__ src_dst,
-                                                          int32_t num_blocks, int64_t block_bytes,
-                                                          int32_t chunks_per_block) {
+                                                          int32_t src_blocks, int32_t dst_blocks,
+                                                          int64_t block_bytes, int32_t chunks_per_block) {
   const int32_t pair = blockIdx.x / chunks_per_block;
   const int32_t chunk = blockIdx.x - pair * chunks_per_block;
   const int32_t src = src_dst[2 * pair], dst = src_dst[2 * pair + 1];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
   const int64_t units = block_bytes >> 4;
   const int64_t u = static_cast<int64_t>(chunk) * 256 + threadIdx.x;
   if (u >= units) return;
   const int64_t so = static_cast<int64_t>(src) * block_bytes + (u << 4);
   const int64_t dof = static_cast<int64_t>(dst) * block_bytes + (u << 4);
-  const u32x4 a = *reinterpret_cast<const u32x4*>(k_cache + so);
-  const u32x4 b = *reinterpret_cast<const u32x4*>(v_cache + so);
-  *reinterpret_cast<u32x4*>(k_cache + dof) = a;
-  *reinterpret_cast<u32x4*>(v_cache + dof) = b;
+  const u32x4 a = *reinterpret_cast<const u32x4*>(k_src + so);
+  const u32x4 b = *reinterpret_cast<const u32x4*>(v_src + so);
+  *reinterpret_cast<u32x4*>(k_dst + dof) = a;
+  *reinterpret_cast<u32x4*>(v_dst + dof) = b;
 }
 
 // ---------------------------------------------------------------------------
@@ -541,7 +546,21 @@ int pkv_launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst,
   const int64_t grid = static_cast<int64_t>(num_pairs) * chunks;
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<char*>(k_cache),
-                     static_cast<char*>(v_cache), src_dst, num_blocks, block_bytes, chunks);
+                     static_cast<char*>(v_cache), static_cast<const char*>(k_cache),
+                     static_cast<const char*>(v_cache), src_dst, num_blocks, num_blocks, block_bytes, chunks);
+  return hipGetLastError();
+}
+
+int pkv_launch_swap_blocks(void* k_dst, void* v_dst, int32_t dst_blocks, const void* k_src, const void* v_src,
+                           int32_t src_blocks, const int32_t* src_dst, int32_t num_pairs, int64_t block_bytes,
+                           void* stream) {
+  if (num_pairs == 0) return hipSuccess;
+  const int32_t chunks = static_cast<int32_t>(((block_bytes >> 4) + 255) / 256);
+  const int64_t grid = static_cast<int64_t>(num_pairs) * chunks;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<char*>(k_dst), static_cast<char*>(v_dst),
+                     static_cast<const char*>(k_src), static_cast<const char*>(v_src), src_dst, src_blocks,
+                     dst_blocks, block_bytes, chunks);
   return hipGetLastError();
 }
 

@@ -264,4 +264,67 @@ def random_prefill(seed: int, ctxs, n_queries, hq: int, hkv: int, d: int, pool_f
     return w
 
 
+@dataclasses.dataclass
+class ServingWorkload:
+    """Requests for a continuous-batching run.  Request r has prompts[r] prompt
+    tokens and produces outputs[r] tokens; the cache ever holds positions
+    0 .. prompts[r] + outputs[r] - 2 of it.  The K/V rows and the query of
+    position p of request r are row ``row_start[r] + p`` of k_rows / v_rows /
+    q_rows (a lookup table of inputs, nothing the method computes)."""
+    name: str
+    dtype: str
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    num_blocks: int
+    initial_free_order: np.ndarray
+    num_host_blocks: int
+    max_num_seqs: int
+    max_num_batched_tokens: int
+    prompts: np.ndarray           # int32 [R]
+    outputs: np.ndarray           # int32 [R]
+    row_start: np.ndarray         # int64 [R + 1]
+    k_rows: np.ndarray            # [T, Hkv, d]
+    v_rows: np.ndarray
+    q_rows: np.ndarray            # [T, Hq, d]
+    scale: np.float32
+    block_size: int = BLOCK_SIZE
+
+
+def serving(seed: int = 6, num_requests: int = 24, hq: int = 8, hkv: int = 2, d: int = 64,
+            prompt_median: float = 40.0, output_median: float = 30.0, sigma: float = 0.8,
+            max_prompt: int = 160, max_output: int = 96, num_blocks: int = 40,
+            max_num_seqs: int = 8, max_num_batched_tokens: int = 256, num_host_blocks: int = 160,
+            dtype: str = "bf16", with_rows: bool = True) -> ServingWorkload:
+    """A request stream for the continuous-batching loop: prompt and output
+    lengths lognormal (the right-skewed mix of "Batching Continuo y
+    PagedAttention", section on static batching), clipped to
+    [1, max_prompt] / [1, max_output], each request's total clipped to what the
+    device pool can hold; a device pool small enough that requests compete
+    for blocks, so requests get swapped out to the host pool and back."""
+    rng = np.random.default_rng(seed)
+    prompts = lognormal_lengths(rng, num_requests, prompt_median, sigma, 1,
+                                min(max_prompt, max_num_batched_tokens))
+    outputs = lognormal_lengths(rng, num_requests, output_median, sigma, 1, max_output)
+    cap = num_blocks * BLOCK_SIZE
+    outputs = np.minimum(outputs, cap - prompts).astype(np.int32)
+    if np.any(outputs < 1):
+        raise ValueError("device pool too small for the prompts drawn")
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    per = (prompts + outputs - 1).astype(np.int64)
+    row_start = np.concatenate([[0], np.cumsum(per)]).astype(np.int64)
+    total = int(row_start[-1])
+    if with_rows:
+        k_rows = _rows(rng, total, hkv, d, dtype)
+        v_rows = _rows(rng, total, hkv, d, dtype)
+        q_rows = _rows(rng, total, hq, d, dtype)
+    else:
+        empty = np.empty((0, hkv, d), dtype=np.float32 if dtype == "f32" else np.uint16)
+        k_rows = v_rows = empty
+        q_rows = np.empty((0, hq, d), dtype=empty.dtype)
+    return ServingWorkload(f"serving{seed}", dtype, hq, hkv, d, num_blocks, perm, num_host_blocks,
+                           max_num_seqs, max_num_batched_tokens, prompts, outputs, row_start,
+                           k_rows, v_rows, q_rows, np.float32(1.0 / math.sqrt(d)))
+
+
 WORKLOADS = {1: tiny, 2: shaped_13b, 3: gqa, 4: parallel_sampling, 5: long_mix}

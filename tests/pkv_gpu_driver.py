@@ -105,3 +105,79 @@ class GpuReplay:
                                        mcl, float(w.scale))
         torch.cuda.synchronize()
         return out.cpu().numpy(), tables, lens
+
+
+class GpuServing:
+    """The continuous-batching loop through the HIP library: the native
+    scheduler picks each step's work; swap copies move blocks between the device
+    pool and a pinned host pool; the step's K/V rows go into their slots; then
+    prefill attention for the admitted prompts and decode attention for the
+    decoding requests.  Rows and queries come from the workload by
+    (request, position)."""
+
+    def __init__(self, w, policy, dev="cuda"):
+        self.w = w
+        self.dev = dev
+        self.alloc = PK.BlockAllocator(w.num_blocks, P, w.initial_free_order)
+        self.sched = PK.Scheduler(self.alloc, w.max_num_seqs, w.max_num_batched_tokens, policy,
+                                  w.num_host_blocks)
+        for p, o in zip(w.prompts, w.outputs):
+            self.sched.add_request(int(p), int(o))
+        tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        shape = (w.num_blocks, w.num_kv_heads, P, w.head_dim)
+        hshape = (w.num_host_blocks, w.num_kv_heads, P, w.head_dim)
+        self.k_pool = torch.zeros(shape, dtype=tdt, device=dev)
+        self.v_pool = torch.zeros(shape, dtype=tdt, device=dev)
+        self.k_host = torch.zeros(hshape, dtype=tdt).pin_memory()
+        self.v_host = torch.zeros(hshape, dtype=tdt).pin_memory()
+        self.k_rows = rows_to_device(w.k_rows, dev)
+        self.v_rows = rows_to_device(w.v_rows, dev)
+        self.q_rows = rows_to_device(w.q_rows, dev)
+
+    def _rows(self, labels):
+        idx = [int(self.w.row_start[r]) + p for r, p in labels]
+        return torch.tensor(idx, dtype=torch.int64, device=self.dev)
+
+    def step(self, sync=True):
+        """Runs one step; None once every request has finished."""
+        w, dev = self.w, self.dev
+        s = self.sched.step()
+        if s.empty:
+            return None
+        if len(s.swap_out_pairs):
+            PK.pkv_swap_blocks(self.k_host, self.v_host, self.k_pool, self.v_pool,
+                               torch.from_numpy(s.swap_out_pairs).to(dev))
+        if len(s.swap_in_pairs):
+            PK.pkv_swap_blocks(self.k_pool, self.v_pool, self.k_host, self.v_host,
+                               torch.from_numpy(s.swap_in_pairs).to(dev))
+        plens = np.diff(s.prefill_query_start_loc)
+        pre_labels = [(int(r), p) for r, n in zip(s.prefill, plens) for p in range(int(n))]
+        dec = [self.sched.request(int(r)) for r in s.decode]
+        positions = [ctx - 1 for _, _, _, ctx in dec]
+        dec_labels = [(int(r), p) for r, p in zip(s.decode, positions)]
+        idx = self._rows(pre_labels + dec_labels)
+        PK.pkv_append(self.k_pool, self.v_pool, self.k_rows.index_select(0, idx).contiguous(),
+                      self.v_rows.index_select(0, idx).contiguous(),
+                      torch.from_numpy(s.slot_mapping).to(dev))
+        Hq, d = w.num_heads, w.head_dim
+        pre_out = dec_out = None
+        if len(s.prefill):
+            seqs = [self.sched.request(int(r))[1] for r in s.prefill]
+            mcl = int(plens.max())
+            tables, lens = self.alloc.block_tables(seqs, -(-mcl // P))
+            pre_out = torch.empty((len(pre_labels), Hq, d), dtype=torch.float32, device=dev)
+            PK.pkv_attention_prefill_chunk(pre_out, self.q_rows.index_select(0, idx[:len(pre_labels)]).contiguous(),
+                                           torch.from_numpy(s.prefill_query_start_loc).to(dev), mcl,
+                                           self.k_pool, self.v_pool, torch.from_numpy(tables).to(dev),
+                                           torch.from_numpy(lens).to(dev), mcl, float(w.scale))
+        if len(s.decode):
+            seqs = [seq for _, seq, _, _ in dec]
+            mcl = max(positions) + 1
+            tables, lens = self.alloc.block_tables(seqs, -(-mcl // P))
+            dec_out = torch.empty((len(dec_labels), Hq, d), dtype=torch.float32, device=dev)
+            PK.pkv_attention_decode(dec_out, self.q_rows.index_select(0, idx[len(pre_labels):]).contiguous(),
+                                    self.k_pool, self.v_pool, torch.from_numpy(tables).to(dev),
+                                    torch.from_numpy(lens).to(dev), mcl, float(w.scale))
+        if sync:
+            torch.cuda.synchronize()
+        return s, pre_out, dec_out, positions

@@ -72,6 +72,19 @@ def test_copy_blocks_rejects_bad_arguments(P):
     assert L.pkv_copy_blocks(None, None, None, 0, 8, 2, 64, 16, 1, None) == P.PKV_OK
 
 
+def test_swap_blocks_rejects_bad_arguments_before_touching_memory(P):
+    L = _lib(P)
+    # dst_k, dst_v, dst_nb, src_k, src_v, src_nb, pairs, n, Hkv, d, bs, dtype, stream
+    assert L.pkv_swap_blocks(16, 32, 8, 48, 64, 8, 80, -1, 2, 64, 16, 1, None) == P.PKV_ERR_INVALID_ARG
+    assert L.pkv_swap_blocks(16, 32, 0, 48, 64, 8, 80, 1, 2, 64, 16, 1, None) == P.PKV_ERR_INVALID_ARG
+    assert L.pkv_swap_blocks(16, 32, 8, 48, 64, 8, None, 1, 2, 64, 16, 1, None) == P.PKV_ERR_INVALID_ARG
+    assert L.pkv_swap_blocks(17, 32, 8, 48, 64, 8, 80, 1, 2, 64, 16, 1, None) == P.PKV_ERR_INVALID_ARG
+    assert "aligned" in L.pkv_last_error().decode()
+    assert L.pkv_swap_blocks(16, 32, 8, 48, 64, 8, 80, 1, 2, 96, 16, 1, None) == P.PKV_ERR_UNSUPPORTED
+    assert L.pkv_swap_blocks(16, 32, 8, 48, 64, 8, 80, 1, 2, 64, 8, 1, None) == P.PKV_ERR_UNSUPPORTED
+    assert L.pkv_swap_blocks(None, None, 8, None, None, 8, None, 0, 2, 64, 16, 1, None) == P.PKV_OK
+
+
 def _decode(P, **kw):
     a = dict(out=256, q=512, k=768, v=1024, tables=1280, mb=4, lens=1536, S=2, Hq=4, Hkv=2, d=64, bs=16,
              nb=8, maxctx=64, scale=0.125, dtype=1, ws=None, wsb=0)

@@ -68,9 +68,11 @@ def parse():
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time for the oracle sample")
-    ap.add_argument("--workload", default="13b", choices=["13b", "gqa", "fork", "long"],
+    ap.add_argument("--workload", default="13b", choices=["13b", "gqa", "fork", "long", "swap", "serve"],
                     help="13b: the headline decode step (default).  gqa / fork / long: kernel measurements on the "
-                         "grouped-query, parallel-sampling and long-context + chunked-prefill batches")
+                         "grouped-query, parallel-sampling and long-context + chunked-prefill batches.  swap: "
+                         "block copies between HBM and pinned host memory.  serve: the continuous-batching loop "
+                         "(continuous vs static policy) over a request stream")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run pkv_copy_blocks over 4096 whole blocks (a plain copy of known size, "
                          "used to scale the FETCH_SIZE / WRITE_SIZE counters)")
@@ -244,6 +246,163 @@ def secondary(args):
     print(json.dumps(res), flush=True)
 
 
+PCIE5_X16_GBPS = 64.0     # host link peak per direction (PCIe 5.0 x16)
+
+
+def swap_bench(args):
+    """Swap copies of whole 13B-shaped blocks (40 heads x 16 x 128 bf16, K and V:
+    320 KiB per block) between a device pool of 8192 blocks and a pinned host
+    pool of 2048 blocks: 1024 random blocks out, then 1024 back in.  Beside it,
+    one contiguous copy of the same byte count each way by the runtime (the
+    host link's practical ceiling)."""
+    import torch
+    import paged_kv_cache_171_amd as PK
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    H, D, P, NBD, NBH, n = 40, 128, 16, 8192, 2048, 1024
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    kd = torch.randn(NBD, H, P, D, generator=gen, device=dev).to(torch.bfloat16)
+    vd = torch.randn(NBD, H, P, D, generator=gen, device=dev).to(torch.bfloat16)
+    kh = torch.empty(NBH, H, P, D, dtype=torch.bfloat16).pin_memory()
+    vh = torch.empty(NBH, H, P, D, dtype=torch.bfloat16).pin_memory()
+    rng = np.random.default_rng(args.seed)
+    out_pairs = np.stack([rng.permutation(NBD)[:n], rng.permutation(NBH)[:n]], 1).astype(np.int32)
+    in_pairs = np.stack([rng.permutation(NBH)[:n], rng.permutation(NBD)[:n]], 1).astype(np.int32)
+    po, pi = torch.from_numpy(out_pairs).to(dev), torch.from_numpy(in_pairs).to(dev)
+    reps = max(args.steps, 3)
+
+    def out():
+        PK.pkv_swap_blocks(kh, vh, kd, vd, po)
+
+    def back():
+        PK.pkv_swap_blocks(kd, vd, kh, vh, pi)
+    for _ in range(max(args.warmup, 1)):
+        out()
+        back()
+    torch.cuda.synchronize()
+    out_us = _timed(out, reps, stream)
+    in_us = _timed(back, reps, stream)
+    nbytes = 2 * n * H * P * D * 2
+    flat_h = kh.view(-1)[: nbytes // 2]
+    flat_d = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    d2h_us = _timed(lambda: flat_h.copy_(flat_d, non_blocking=True), reps, stream)
+    h2d_us = _timed(lambda: flat_d.copy_(flat_h, non_blocking=True), reps, stream)
+    gb = lambda us: round(nbytes / us / 1e3, 2)
+    print(json.dumps({
+        "workload": "swap", "kernel": "copy_blocks_kernel (pkv_swap_blocks)", "pairs": n,
+        "block_bytes_k_plus_v": 2 * H * P * D * 2, "bytes_per_launch": nbytes,
+        "swap_out_us": round(out_us, 1), "swap_out_gbps": gb(out_us),
+        "swap_in_us": round(in_us, 1), "swap_in_gbps": gb(in_us),
+        "runtime_contiguous_d2h_gbps": gb(d2h_us), "runtime_contiguous_h2d_gbps": gb(h2d_us),
+        "roofline": {"bound": "host link", "peak": PCIE5_X16_GBPS, "unit": "GB/s",
+                     "swap_out_frac": round(nbytes / out_us / 1e3 / PCIE5_X16_GBPS, 4),
+                     "swap_in_frac": round(nbytes / in_us / 1e3 / PCIE5_X16_GBPS, 4)}}), flush=True)
+
+
+def serve_bench(args):
+    """The continuous-batching loop, end to end on one GPU: 256 requests, prompt
+    lengths lognormal (median 200, sigma 1) clipped to [1, 1024], output
+    lengths lognormal (median 128, sigma 0.8) clipped to [1, 512]; 40 MHA heads
+    x 128, bf16, 4 layer pools; at most 64 running requests and 4096 tokens a
+    step; a device pool of 1600 blocks (64 requests at their mean final length
+    need ~1850), so requests are swapped out to a 512-block pinned host pool
+    and back.  Per step: the native scheduler, then the swap copies, the cache
+    writes, causal prefill of admitted prompts and decode of the running
+    requests in every layer.  Rows and queries are random and reused.  Run once
+    under the continuous policy and once under the static one."""
+    import torch
+    import paged_kv_cache_171_amd as PK
+    import pkv_workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L, H, D, P = 4, 40, 128, 16
+    w = W.serving(seed=args.seed, num_requests=256, hq=H, hkv=H, d=D, prompt_median=200, output_median=128,
+                  sigma=1.0, max_prompt=1024, max_output=512, num_blocks=1600, max_num_seqs=64,
+                  max_num_batched_tokens=4096, num_host_blocks=512, with_rows=False)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    pools = [(randn(w.num_blocks, H, P, D), randn(w.num_blocks, H, P, D)) for _ in range(L)]
+    hosts = [(torch.empty(w.num_host_blocks, H, P, D, dtype=torch.bfloat16).pin_memory(),
+              torch.empty(w.num_host_blocks, H, P, D, dtype=torch.bfloat16).pin_memory()) for _ in range(L)]
+    T = w.max_num_batched_tokens
+    qr, kr, vr = randn(T, H, D), randn(T, H, D), randn(T, H, D)
+    out = torch.empty(T, H, D, dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    results = {}
+    for name, policy in (("continuous", PK.PKV_SCHED_CONTINUOUS), ("static", PK.PKV_SCHED_STATIC)):
+        alloc = PK.BlockAllocator(w.num_blocks, P, w.initial_free_order)
+        sched = PK.Scheduler(alloc, w.max_num_seqs, T, policy, w.num_host_blocks)
+        for p, o in zip(w.prompts, w.outputs):
+            sched.add_request(int(p), int(o))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        steps = tokens = swapped = 0
+        while True:
+            s = sched.step()
+            if s.empty:
+                break
+            steps += 1
+            for a, b in ((s.swap_out_pairs, 0), (s.swap_in_pairs, 1)):
+                if len(a):
+                    sd = torch.from_numpy(a).to(dev, non_blocking=False)
+                    for (kp, vp), (kh, vh) in zip(pools, hosts):
+                        if b == 0:
+                            PK.pkv_swap_blocks(kh, vh, kp, vp, sd)
+                        else:
+                            PK.pkv_swap_blocks(kp, vp, kh, vh, sd)
+            swapped += len(s.swapped_out)
+            n = len(s.slot_mapping)
+            slots = torch.from_numpy(s.slot_mapping).to(dev)
+            npre = int(s.prefill_query_start_loc[-1])
+            plens = np.diff(s.prefill_query_start_loc)
+            pre_t = dec_t = None
+            if len(s.prefill):
+                seqs = [sched.request(int(r))[1] for r in s.prefill]
+                mql = int(plens.max())
+                t, ln = alloc.block_tables(seqs, -(-mql // P))
+                pre_t = (torch.from_numpy(s.prefill_query_start_loc).to(dev), mql, torch.from_numpy(t).to(dev),
+                         torch.from_numpy(ln).to(dev))
+            if len(s.decode):
+                req = [sched.request(int(r)) for r in s.decode]
+                seqs = [x[1] for x in req]
+                mcl = max(x[3] for x in req)
+                t, ln = alloc.block_tables(seqs, -(-mcl // P))
+                lens_d = torch.from_numpy(ln).to(dev)
+                dec_t = (torch.from_numpy(t).to(dev), lens_d, mcl,
+                         PK.workspace_for(len(seqs), H, D, mcl, device=dev),
+                         PK.plan_for(lens_d, H, H, t.shape[1], mcl, PK.PKV_BF16))
+            for kp, vp in pools:
+                PK.pkv_append(kp, vp, kr[:n], vr[:n], slots)
+                if pre_t is not None:
+                    PK.pkv_attention_prefill_chunk(out[:npre], qr[:npre], pre_t[0], pre_t[1], kp, vp, pre_t[2],
+                                                   pre_t[3], pre_t[1], scale)
+                if dec_t is not None:
+                    nd = len(s.decode)
+                    PK.pkv_attention_decode(out[npre:npre + nd], qr[npre:npre + nd], kp, vp, dec_t[0], dec_t[1],
+                                            dec_t[2], scale, workspace=dec_t[3], plan=dec_t[4])
+            tokens += len(s.prefill) + len(s.decode)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        st = sched.stats()
+        results[name] = {"steps": steps, "generated_tokens": tokens, "seconds": round(el, 3),
+                         "tokens_per_s": round(tokens / el, 1), "ms_per_step": round(el / steps * 1e3, 3),
+                         "slot_utilisation": round(st[1] / (steps * w.max_num_seqs), 4),
+                         "swapped_out_requests": swapped}
+    print(json.dumps({"workload": "serve", "layers": L, "requests": len(w.prompts), "heads": H, "head_dim": D,
+                      "max_num_seqs": w.max_num_seqs, "max_num_batched_tokens": T,
+                      "device_blocks": w.num_blocks, "host_blocks": w.num_host_blocks,
+                      "mean_prompt": round(float(w.prompts.mean()), 1), "mean_output": round(float(w.outputs.mean()), 1),
+                      **results,
+                      "continuous_over_static": round(results["continuous"]["tokens_per_s"] /
+                                                      results["static"]["tokens_per_s"], 3)}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -252,6 +411,12 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.workload == "swap":
+        swap_bench(args)
+        return
+    if args.workload == "serve":
+        serve_bench(args)
         return
     if args.workload != "13b":
         secondary(args)

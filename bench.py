@@ -218,6 +218,24 @@ def secondary(args):
         cow_bytes = 2 * 2 * len(pairs) * Hkv * P * D * 2
         res.update({"cow_pairs": len(pairs), "cow_us": round(cow_us, 2),
                     "cow_gbps_read_plus_write": round(cow_bytes / cow_us / 1e3, 1)})
+        # the same decode with the fork groups named: each group's shared prompt
+        # blocks are read once for its 8 samples (pkv_attention_decode_shared)
+        gsd = torch.from_numpy(w.group_start).to(dev)
+        sws = torch.empty(max(PK.pkv_attention_decode_shared_workspace_bytes(len(seqs), Hq, D, mcl), 256),
+                          dtype=torch.uint8, device=dev)
+
+        def shared_all():
+            for kp, vp in pools:
+                PK.pkv_attention_decode_shared(out, q, kp, vp, td, ld, gsd, mcl, scale, workspace=sws)
+        shared_all()
+        torch.cuda.synchronize()
+        sh_us = _timed(shared_all, reps, stream) / L
+        res.update({"shared_decode_us_per_layer": round(sh_us, 2),
+                    "shared_decode_unique_gbps": round(res["kv_unique_bytes"] / sh_us / 1e3, 1),
+                    "shared_decode_hbm_peak_frac": round(res["kv_unique_bytes"] / sh_us / 1e3 / HBM_PEAK_GBPS, 4),
+                    "shared_over_plain_speedup": round(dec_us / sh_us, 3),
+                    "shared_kernels": "shared_plan_kernel + plan_kernel + decode_group_mfma_kernel<128,true> "
+                                      "(shared prompt blocks) + decode_valu_kernel (tails) + merge"})
     if name == "long":
         cs = w.chunk_seqs
         clens = np.array([alloc.seq_block_table(s)[1] for s in cs], dtype=np.int32)

@@ -200,6 +200,38 @@ pkv_status pkv_attention_decode_planned(float* out, const void* q, const void* k
                                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Decode with shared prefixes.  [OS] "El regalo extra: compartir memoria" and
+ * [IPX] "Dos respuestas a una entrada": the parallel samples of one prompt
+ * share the prompt's physical blocks.  The result is that of
+ * pkv_attention_decode (same arguments, same definition, same error rules);
+ * the groups only change how the blocks are read:
+ *
+ *   group_start: device int32 [num_groups + 1], non-decreasing from 0 to
+ *   num_seqs; group g is sequences group_start[g] .. group_start[g+1]-1.
+ *
+ * For each group the library finds on the device the longest run of leading
+ * block-table entries equal in every member and wholly below every member's
+ * context, reads those K/V tiles once for all members (bf16, Hq/Hkv <= 16:
+ * the members' query rows share one matrix-core tile, up to 16 rows), decodes
+ * each member's remaining tokens on its own, and merges the two parts by
+ * their softmax statistics.  A malformed group_start, groups of one sequence,
+ * members with invalid contexts or tables with no common first block simply
+ * give no shared part, so no hint changes a result beyond rounding.  fp32
+ * pools, more than 16 query heads per KV head or num_groups = 0 run plain
+ * decode.  workspace: at least pkv_attention_decode_shared_workspace_bytes(...)
+ * bytes, 256-byte aligned, caller-owned device memory.
+ * ------------------------------------------------------------------------ */
+size_t pkv_attention_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                                   int32_t max_context_len);
+pkv_status pkv_attention_decode_shared(float* out, const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, int32_t num_seqs, const int32_t* group_start,
+                                       int32_t num_groups, int32_t num_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                       int32_t max_context_len, float scale, pkv_dtype dtype, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Causal chunked-prefill attention.  [UL] "Cómo funciona la planificación a
  * nivel de iteración" and "Límites y técnicas complementarias": a long prompt
  * is prefilled in chunks that run in the same step as other sequences' decode.

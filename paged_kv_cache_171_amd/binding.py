@@ -46,6 +46,10 @@ _SIGS = {
     "pkv_attention_decode_planned": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32,
                                               _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_p, _c_sz, _c_p,
                                               _c_sz, _c_p]),
+    "pkv_attention_decode_shared_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32]),
+    "pkv_attention_decode_shared": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_p, _c_i32,
+                                             _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_p,
+                                             _c_sz, _c_p]),
     "pkv_attention_prefill_chunk": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_i32, _c_p,
                                              _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
                                              _c_i32, _c_p]),
@@ -209,6 +213,32 @@ def pkv_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tens
         _dev(plan)
         _check(_lib.pkv_attention_decode_planned(*args, plan.data_ptr(), plan.numel(), workspace.data_ptr(),
                                                  workspace.numel(), _stream(stream)))
+
+
+def pkv_attention_decode_shared_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int,
+                                                max_context_len: int) -> int:
+    return int(_lib.pkv_attention_decode_shared_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len))
+
+
+def pkv_attention_decode_shared(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                block_tables: torch.Tensor, context_lens: torch.Tensor, group_start: torch.Tensor,
+                                max_context_len: int, scale: float, workspace: Optional[torch.Tensor] = None,
+                                stream=None) -> None:
+    """As pkv_attention_decode; group_start int32 [G+1] on the GPU names groups of
+    sequences whose shared leading blocks are read once per group."""
+    _dev(out, q, k_cache, v_cache, block_tables, context_lens, group_start)
+    assert out.dtype == torch.float32 and block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+    assert group_start.dtype == torch.int32
+    S, hq, d = q.shape
+    nb, hkv, bs, _ = k_cache.shape
+    if workspace is None:
+        n = max(pkv_attention_decode_shared_workspace_bytes(S, hq, d, int(max_context_len)), 256)
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    _check(_lib.pkv_attention_decode_shared(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                            block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
+                                            S, group_start.data_ptr(), group_start.numel() - 1, hq, hkv, d, bs, nb,
+                                            int(max_context_len), float(scale), _dtype_code(k_cache),
+                                            workspace.data_ptr(), workspace.numel(), _stream(stream)))
 
 
 def pkv_attention_prefill_chunk(out: torch.Tensor, q: torch.Tensor, query_start_loc: torch.Tensor,

@@ -57,6 +57,29 @@ size_t partial_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int3
   const size_t units = static_cast<size_t>(num_seqs) * num_heads * np;
   return align256(units * 2 * sizeof(float)) + units * head_dim * sizeof(float);
 }
+
+// Shared-prefix decode workspace: the shared plan, seq_start, the plan of the
+// sequences' own units, then partials with prefix slots ahead of the
+// sequence's own ones.
+struct SharedLayout {
+  int32_t prefix_slots, slots;
+  size_t shared_plan, seq_start, plan, part_ml, part_acc, total;
+};
+SharedLayout shared_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len) {
+  SharedLayout l{};
+  l.prefix_slots = (max_context_len + kPrefixPartTokens - 1) / kPrefixPartTokens;
+  if (l.prefix_slots < 1) l.prefix_slots = 1;
+  l.slots = l.prefix_slots + num_partitions(max_context_len);
+  const size_t S = static_cast<size_t>(num_seqs);
+  l.shared_plan = 0;
+  l.seq_start = align256((kPlanHdrWords + 4 * S * l.prefix_slots) * sizeof(int32_t));
+  l.plan = l.seq_start + align256(S * sizeof(int32_t));
+  l.part_ml = l.plan + align256(plan_bytes(num_seqs, max_context_len));
+  const size_t units = S * num_heads * l.slots;
+  l.part_acc = l.part_ml + align256(units * 2 * sizeof(float));
+  l.total = l.part_acc + units * head_dim * sizeof(float);
+  return l;
+}
 }  // namespace
 
 pkv_status pkv_fail(pkv_status st, const char* msg) {
@@ -286,6 +309,89 @@ pkv_status pkv_attention_decode_planned(float* out, const void* q, const void* k
                      context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_context_len, scale, dtype, plan, plan_bytes_given, workspace, workspace_bytes, false,
                      stream);
+}
+
+size_t pkv_attention_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                                   int32_t max_context_len) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
+  const size_t plain = pkv_attention_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len);
+  const size_t shared = shared_layout(num_seqs, num_heads, head_dim, max_context_len).total;
+  return shared > plain ? shared : plain;
+}
+
+pkv_status pkv_attention_decode_shared(float* out, const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, int32_t num_seqs, const int32_t* group_start,
+                                       int32_t num_groups, int32_t num_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                       int32_t max_context_len, float scale, pkv_dtype dtype, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  const char* fn = "pkv_attention_decode_shared";
+  if (num_groups < 0) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: num_groups < 0", fn);
+  if (num_groups > 0 && num_seqs > 0 && !group_start) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: group_start is NULL", fn);
+  const int32_t group = num_kv_heads > 0 ? num_heads / num_kv_heads : 0;
+  // only the bf16 MFMA kernel reads a prefix for several sequences; otherwise
+  // (or with no groups) this is plain decode
+  if (dtype != PKV_BF16 || group < 1 || group > kMaxMfmaGroup || num_groups == 0 || num_seqs <= 0)
+    return decode_impl(fn, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                       num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_context_len, scale, dtype,
+                       nullptr, 0, workspace, workspace_bytes, true, stream);
+  pkv_status st = check_common(fn, num_kv_heads, head_dim, block_size, dtype);
+  if (st != PKV_OK) return st;
+  if (num_heads <= 0 || num_heads % num_kv_heads != 0)
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: num_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                     fn, num_heads, num_kv_heads);
+  if (num_blocks <= 0) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: num_blocks must be > 0", fn);
+  if (max_blocks_per_seq <= 0) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: max_blocks_per_seq must be > 0", fn);
+  if (max_context_len < 0) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: max_context_len < 0", fn);
+  if (num_groups > num_seqs) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: more groups than sequences", fn);
+  if (!std::isfinite(scale)) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: out, q and cache pointers must be 16-byte aligned", fn);
+  const SharedLayout l = shared_layout(num_seqs, num_heads, head_dim, max_context_len);
+  const int64_t grid = static_cast<int64_t>(num_seqs) * num_heads * (l.prefix_slots + num_partitions(max_context_len));
+  if (grid > 0x7FFFFFFF || static_cast<int64_t>(num_seqs) * l.slots > 0x3FFFFFFF)
+    return pkv_failf(PKV_ERR_UNSUPPORTED, "%s: launch grid too large", fn);
+  if (workspace_bytes < l.total)
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: workspace of %zu bytes is smaller than the %zu needed", fn,
+                     workspace_bytes, l.total);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: workspace must be a 256-byte aligned device buffer", fn);
+  char* ws = static_cast<char*>(workspace);
+  pkv_decode_args a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.plan = reinterpret_cast<const int32_t*>(ws + l.plan);
+  a.part_ml = reinterpret_cast<float*>(ws + l.part_ml);
+  a.part_acc = reinterpret_cast<float*>(ws + l.part_acc);
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.max_context_len = max_context_len;
+  a.num_partitions = l.slots;
+  a.part_tokens = pkv_part_tokens(dtype, num_heads, num_kv_heads);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.dtype = dtype;
+  a.seq_start = reinterpret_cast<const int32_t*>(ws + l.seq_start);
+  a.shared_plan = reinterpret_cast<const int32_t*>(ws + l.shared_plan);
+  a.prefix_part_tokens = kPrefixPartTokens;
+  int err = pkv_launch_shared_plan(a, group_start, num_groups, reinterpret_cast<int32_t*>(ws + l.seq_start),
+                                   reinterpret_cast<int32_t*>(ws + l.shared_plan), stream);
+  if (!err)
+    err = pkv_launch_plan(reinterpret_cast<int32_t*>(ws + l.plan), context_lens, num_seqs, max_blocks_per_seq,
+                          max_context_len, a.part_tokens, stream, a.seq_start);
+  if (!err) err = pkv_launch_shared_prefix(a, stream);
+  if (!err) err = pkv_launch_decode(a, stream);
+  return hip_status(fn, err);
 }
 
 pkv_status pkv_attention_prefill_chunk(float* out, const void* q, const int32_t* query_start_loc,

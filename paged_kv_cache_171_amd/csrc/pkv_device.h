@@ -35,6 +35,15 @@ __device__ __forceinline__ bool plan_matches(const int32_t* plan, const pkv_deco
 
 __device__ __forceinline__ const int32_t* plan_units(const int32_t* plan) { return plan + kPlanHdr; }
 
+// First token of sequence s covered by its own plan units (0 unless a shared
+// prefix covers the ones before it) and the partial slot its first unit writes.
+__device__ __forceinline__ int32_t seq_start_of(const pkv_decode_args& a, int32_t s) {
+  return a.seq_start ? a.seq_start[s] : 0;
+}
+__device__ __forceinline__ int32_t slot_base_of(const pkv_decode_args& a, int32_t start) {
+  return start > 0 ? (start + a.prefix_part_tokens - 1) / a.prefix_part_tokens : 0;
+}
+
 // Log-sum-exp merge of the n partials (m in log2 units, l, acc) of one output
 // element: sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M), M = max_p m_p.
 __device__ __forceinline__ float merge_partials(const float* ml, const float* acc, int32_t n, int32_t stride) {

@@ -54,13 +54,30 @@ struct pkv_decode_args {
   int32_t part_tokens;     // tokens per partition for this launch
   float scale_log2;        // scale * log2(e)
   int dtype;               // pkv_dtype
+  // Shared-prefix decode (null / 0 otherwise).  seq_start[s] (a multiple of 16)
+  // is the first token of sequence s that its own plan units cover; tokens
+  // before it belong to its group's shared-prefix units, which write partial
+  // slots 0 .. ceil(seq_start[s] / prefix_part_tokens) - 1 of each row, so the
+  // sequence's own units write the slots after those.
+  const int32_t* seq_start;
+  const int32_t* shared_plan;  // header + (first sequence, members, partition, prefix tokens) per unit
+  int32_t prefix_part_tokens;
 };
 // Decode: the main kernel (VALU, or MFMA for bf16 query-head groups of 2..16
 // heads, pkv_mfma.hip), then the partition merge when a context can be split.
 int pkv_launch_decode(const pkv_decode_args& a, void* stream);
 int pkv_launch_decode_group(const pkv_decode_args& a, void* stream);
 int pkv_launch_plan(int32_t* plan, const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
-                    int32_t max_context_len, int32_t part_tokens, void* stream);
+                    int32_t max_context_len, int32_t part_tokens, void* stream,
+                    const int32_t* seq_start = nullptr);
+
+// Shared-prefix decode (pkv_mfma.hip): the plan of the groups' common leading
+// blocks (fills seq_start and the shared plan), then the MFMA kernel over those
+// blocks.  Tokens per shared-prefix partition:
+constexpr int32_t kPrefixPartTokens = 512;
+int pkv_launch_shared_plan(const pkv_decode_args& a, const int32_t* group_start, int32_t num_groups,
+                           int32_t* seq_start, int32_t* shared_plan, void* stream);
+int pkv_launch_shared_prefix(const pkv_decode_args& a, void* stream);
 
 // Causal chunked-prefill attention (pkv_mfma.hip).
 struct pkv_prefill_args {

@@ -196,12 +196,14 @@ struct DecodeShape {
 // order inside one size is whatever the LDS atomics give, which changes no
 // result: every unit computes the same partial whenever it runs), then one
 // (s, -1) unit per sequence with an empty or invalid context, whose rows the
-// decode kernel writes as 0 or NaN.
+// decode kernel writes as 0 or NaN.  With seq_start (shared-prefix decode) a
+// sequence's units cover tokens seq_start[s] .. ctx - 1 only.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void plan_kernel(int32_t* __restrict__ plan,
                                                     const int32_t* __restrict__ context_lens,
                                                     int32_t num_seqs, int32_t max_blocks_per_seq,
-                                                    int32_t max_context_len, int32_t part) {
+                                                    int32_t max_context_len, int32_t part,
+                                                    const int32_t* __restrict__ seq_start) {
   __shared__ int32_t bucket[kMaxPartTokens];   // remainder size -> count, then -> next slot
   __shared__ int32_t scan[1024];
   __shared__ int32_t sm_full, sm_special;
@@ -214,8 +216,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(int32_t* __restrict__ plan,
   for (int32_t s = tid; s < num_seqs; s += 1024) {
     const int32_t ctx = context_lens[s];
     if (!len_ok(ctx, max_context_len, max_blocks_per_seq)) continue;
-    full += ctx / part;
-    if (ctx % part) atomicAdd(&bucket[ctx % part], 1);
+    const int32_t len = ctx - (seq_start ? seq_start[s] : 0);
+    full += len / part;
+    if (len % part) atomicAdd(&bucket[len % part], 1);
   }
   atomicAdd(&sm_full, full);
   __syncthreads();
@@ -247,7 +250,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(int32_t* __restrict__ plan,
     const int32_t s = base + tid;
     const int32_t ctx = s < num_seqs ? context_lens[s] : 0;
     const bool ok = s < num_seqs && len_ok(ctx, max_context_len, max_blocks_per_seq);
-    const int32_t nf = ok ? ctx / part : 0;
+    const int32_t len = ok ? ctx - (seq_start ? seq_start[s] : 0) : 0;
+    const int32_t nf = len / part;
     scan[tid] = nf;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
@@ -261,8 +265,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(int32_t* __restrict__ plan,
       units[2 * (first + q)] = s;
       units[2 * (first + q) + 1] = q;
     }
-    if (ok && ctx % part) {
-      const int32_t slot = atomicAdd(&bucket[ctx % part], 1);
+    if (ok && len % part) {
+      const int32_t slot = atomicAdd(&bucket[len % part], 1);
       units[2 * slot] = s;
       units[2 * slot + 1] = nf;
     }
@@ -324,9 +328,11 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(pkv_decode_args a) {
     return;
   }
   const int32_t part = a.part_tokens;
-  const int32_t np_s = (ctx + part - 1) / part;
+  const int32_t start = pkvd::seq_start_of(a, s);
+  const int32_t base = pkvd::slot_base_of(a, start);
+  const int32_t np_s = (ctx - start + part - 1) / part;
   const int32_t nblk = (ctx + kBlock - 1) / kBlock;
-  const int32_t blk_begin = p * (part / kBlock);
+  const int32_t blk_begin = start / kBlock + p * (part / kBlock);
   const int32_t blk_end = min(nblk, blk_begin + part / kBlock);
 
   constexpr int64_t kTileBytes = static_cast<int64_t>(kBlock) * D * sizeof(T);
@@ -472,12 +478,12 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(pkv_decode_args a) {
     }
     if (sm_bad[0] | sm_bad[1] | sm_bad[2] | sm_bad[3]) { o = __builtin_nanf(""); L = __builtin_nanf(""); }
   }
-  if (np_s == 1) {
+  if (np_s == 1 && base == 0) {
     if (t < D) a.out[orow + t] = o / L;
     return;
   }
   // a split context: this partition's (max, sum, accumulator) for the merge kernel
-  const int64_t pidx = (static_cast<int64_t>(s) * Hq + h) * a.num_partitions + p;
+  const int64_t pidx = (static_cast<int64_t>(s) * Hq + h) * a.num_partitions + base + p;
   if (t < D) {
     a.part_acc[pidx * D + t] = o;
     if (t == 0) { a.part_ml[2 * pidx] = M; a.part_ml[2 * pidx + 1] = L; }
@@ -501,10 +507,15 @@ __global__ __launch_bounds__(D) void merge_partitions_kernel(pkv_decode_args a) 
   if (!plan_matches(a.plan, a)) return;                // the decode kernel wrote NaN rows
   const int32_t ctx = a.context_lens[s];
   if (!len_ok(ctx, a.max_context_len, a.max_blocks_per_seq)) return;
-  const int32_t np_s = (ctx + a.part_tokens - 1) / a.part_tokens;
-  if (np_s <= 1) return;
+  // slots 0 .. base-1 hold the shared-prefix partials (if any), then the
+  // sequence's own partitions
+  const int32_t start = pkvd::seq_start_of(a, s);
+  const int32_t base = pkvd::slot_base_of(a, start);
+  const int32_t np_s = (ctx - start + a.part_tokens - 1) / a.part_tokens;
+  if (base == 0 && np_s <= 1) return;
   const int64_t prow = sh * a.num_partitions;
-  a.out[sh * D + threadIdx.x] = pkvd::merge_partials(a.part_ml + 2 * prow, a.part_acc + prow * D + threadIdx.x, np_s, D);
+  a.out[sh * D + threadIdx.x] =
+      pkvd::merge_partials(a.part_ml + 2 * prow, a.part_acc + prow * D + threadIdx.x, base + np_s, D);
 }
 
 template <typename T, int D>
@@ -518,9 +529,9 @@ int launch_decode_valu(const pkv_decode_args& a, hipStream_t st) {
 }  // namespace
 
 int pkv_launch_plan(int32_t* plan, const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
-                    int32_t max_context_len, int32_t part_tokens, void* stream) {
+                    int32_t max_context_len, int32_t part_tokens, void* stream, const int32_t* seq_start) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, static_cast<hipStream_t>(stream), plan, context_lens,
-                     num_seqs, max_blocks_per_seq, max_context_len, part_tokens);
+                     num_seqs, max_blocks_per_seq, max_context_len, part_tokens, seq_start);
   return hipGetLastError();
 }
 
@@ -575,7 +586,8 @@ int pkv_launch_decode(const pkv_decode_args& a, void* stream) {
   } else {
     err = a.head_dim == 128 ? launch_decode_valu<float, 128>(a, st) : launch_decode_valu<float, 64>(a, st);
   }
-  if (err != hipSuccess || a.max_context_len <= a.part_tokens) return err;   // no context can be split
+  // no context can be split (and no shared prefix adds partials): no merge
+  if (err != hipSuccess || (a.seq_start == nullptr && a.max_context_len <= a.part_tokens)) return err;
   const uint32_t rows = static_cast<uint32_t>(a.num_seqs) * a.num_heads;
   if (a.head_dim == 128) {
     hipLaunchKernelGGL((merge_partitions_kernel<128>), dim3(rows), dim3(128), 0, st, a);

@@ -132,7 +132,7 @@ __device__ __forceinline__ int vswz(int r) {
   return 2 * ((r / kRowsPerLine) % (kSlots / 2));
 }
 
-template <int D>
+template <int D, bool kShared>
 __global__ __launch_bounds__(256, 4) void decode_group_mfma_kernel(pkv_decode_args a) {
   constexpr int KC = D / 32;            // 32-dim chunks of q.k
   constexpr int DC = D / 16;            // 16-dim chunks of the output
@@ -156,48 +156,73 @@ __global__ __launch_bounds__(256, 4) void decode_group_mfma_kernel(pkv_decode_ar
   const int32_t Hq = a.num_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
   const int32_t u = static_cast<int32_t>(blockIdx.x / static_cast<uint32_t>(Hkv));
   const int32_t kvh = static_cast<int32_t>(blockIdx.x - static_cast<uint32_t>(u) * Hkv);
-  const int32_t* plan = a.plan;
-  if (!plan_matches(plan, a)) {
-    // a plan built for other sizes: every row is NaN
-    if (u < a.num_seqs)
+  // The unit: rows r < nrows are (sequence s0 + r / G, query head kvh*G + r % G);
+  // it walks blocks blk_begin .. blk_end-1 of s0's table, keys below ctx valid,
+  // and writes the output rows (direct) or partial slot `slot` of each row.
+  int32_t s0, nrows, ctx, blk_begin, blk_end, slot;
+  bool direct;
+  if constexpr (kShared) {
+    // a group's shared leading blocks: the rows are the group's sequences
+    const int32_t* sp = a.shared_plan;
+    if (u >= sp[0]) return;
+    const int32_t* su = sp + kPlanHdr + 4 * u;
+    s0 = su[0];
+    nrows = su[1] * G;
+    ctx = su[3];
+    blk_begin = su[2] * (a.prefix_part_tokens / kBlock);
+    blk_end = min(ctx / kBlock, blk_begin + a.prefix_part_tokens / kBlock);
+    slot = su[2];
+    direct = false;
+  } else {
+    const int32_t* plan = a.plan;
+    if (!plan_matches(plan, a)) {
+      // a plan built for other sizes: every row is NaN
+      if (u < a.num_seqs)
+        for (int idx = threadIdx.x; idx < G * D; idx += 256)
+          a.out[(static_cast<int64_t>(u) * Hq + kvh * G) * D + idx] = __builtin_nanf("");
+      return;
+    }
+    if (u >= plan[0]) return;
+    const int32_t* units = pkvd::plan_units(plan);
+    const int32_t s = units[2 * u];
+    const int32_t p = units[2 * u + 1];
+    ctx = a.context_lens[s];
+    if (p < 0) {
+      // no attention work: an empty context gives 0, an invalid one NaN
       for (int idx = threadIdx.x; idx < G * D; idx += 256)
-        a.out[(static_cast<int64_t>(u) * Hq + kvh * G) * D + idx] = __builtin_nanf("");
-    return;
+        a.out[(static_cast<int64_t>(s) * Hq + kvh * G) * D + idx] = ctx == 0 ? 0.f : __builtin_nanf("");
+      return;
+    }
+    const int32_t part = a.part_tokens;
+    const int32_t start = pkvd::seq_start_of(a, s);
+    const int32_t base = pkvd::slot_base_of(a, start);
+    const int32_t np_s = (ctx - start + part - 1) / part;
+    const int32_t nblk = (ctx + kBlock - 1) / kBlock;
+    s0 = s;
+    nrows = G;
+    blk_begin = start / kBlock + p * (part / kBlock);
+    blk_end = min(nblk, blk_begin + part / kBlock);
+    slot = base + p;
+    direct = np_s == 1 && base == 0;
   }
-  if (u >= plan[0]) return;
-  const int32_t* units = pkvd::plan_units(plan);
-  const int32_t s = units[2 * u];
-  const int32_t p = units[2 * u + 1];
-  const int32_t ctx = a.context_lens[s];
-  if (p < 0) {
-    // no attention work: an empty context gives 0, an invalid one NaN
-    for (int idx = threadIdx.x; idx < G * D; idx += 256)
-      a.out[(static_cast<int64_t>(s) * Hq + kvh * G) * D + idx] = ctx == 0 ? 0.f : __builtin_nanf("");
-    return;
-  }
-  const int32_t part = a.part_tokens;
-  const int32_t np_s = (ctx + part - 1) / part;
-  const int32_t nblk = (ctx + kBlock - 1) / kBlock;
-  const int32_t blk_begin = p * (part / kBlock);
-  const int32_t blk_end = min(nblk, blk_begin + part / kBlock);
 
   const int64_t block_bytes = static_cast<int64_t>(Hkv) * kTile;
   const char* __restrict__ kc = reinterpret_cast<const char*>(a.k_cache) + kvh * kTile;
   const char* __restrict__ vc = reinterpret_cast<const char*>(a.v_cache) + kvh * kTile;
-  const int32_t* __restrict__ table = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq;
+  const int32_t* __restrict__ table = a.block_tables + static_cast<int64_t>(s0) * a.max_blocks_per_seq;
 
   char* vs = smem + wave * (2 * kBlock * RB);      // this wave's two V tiles
 
-  // Q^T as the B operand: lane (n, g) holds dims 32c + 8g .. +8 of head kvh*G + n.
+  // Q^T as the B operand: lane (n, g) holds dims 32c + 8g .. +8 of row n.
   bf16x8 qb[KC];
   {
-    const int hr = n < G ? n : 0;
+    const int hr = n < nrows ? n : 0;
     const char* qrow = reinterpret_cast<const char*>(a.q) +
-                       ((static_cast<int64_t>(s) * Hq + kvh * G + hr) * D) * 2;
+                       ((static_cast<int64_t>(s0 + hr / G) * Hq + kvh * G + hr % G) * D) * 2;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 64 * c + 16 * g);
-      if (n >= G) w = u32x4{0, 0, 0, 0};
+      if (n >= nrows) w = u32x4{0, 0, 0, 0};
       qb[c] = as_bf16x8(w);
     }
   }
@@ -309,7 +334,7 @@ __global__ __launch_bounds__(256, 4) void decode_group_mfma_kernel(pkv_decode_ar
   if (lane == 0) sm_bad[wave] = bad ? 1 : 0;
   __syncthreads();
   const bool any_bad = (sm_bad[0] | sm_bad[1] | sm_bad[2] | sm_bad[3]) != 0;
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+  for (int idx = threadIdx.x; idx < nrows * D; idx += 256) {
     const int r = idx / D, d = idx - (idx / D) * D;
     float M = sm_ml[0][r][0];
 #pragma unroll
@@ -322,16 +347,122 @@ __global__ __launch_bounds__(256, 4) void decode_group_mfma_kernel(pkv_decode_ar
       acc += so[(w * 16 + r) * OROW + d] * f;
     }
     if (any_bad) { acc = __builtin_nanf(""); L = __builtin_nanf(""); }
-    const int32_t h = kvh * G + r;
-    if (np_s == 1) {
-      a.out[(static_cast<int64_t>(s) * Hq + h) * D + d] = acc / L;
+    const int64_t row = static_cast<int64_t>(s0 + r / G) * Hq + kvh * G + r % G;
+    if (direct) {
+      a.out[row * D + d] = acc / L;
     } else {
-      const int64_t pidx = (static_cast<int64_t>(s) * Hq + h) * a.num_partitions + p;
+      const int64_t pidx = row * a.num_partitions + slot;
       a.part_acc[pidx * D + d] = acc;
       if (d == 0) { a.part_ml[2 * pidx] = M; a.part_ml[2 * pidx + 1] = L; }
     }
   }
   (void)kSlots;
+}
+
+// ---------------------------------------------------------------------------
+// Shared-prefix plan.  [OS] "El regalo extra: compartir memoria" and [IPX] "Dos
+// respuestas a una entrada": the parallel samples of one prompt hold the same
+// physical blocks for that prompt, so one read of each shared K/V tile can
+// serve every sample -- the samples become the rows of the MFMA tile, as the
+// query heads of a group do in grouped-query decode.
+//
+// Sequences group_start[g] .. group_start[g+1]-1 form group g (the caller's
+// hint).  One wave per group finds its shared prefix: the longest run of
+// leading table entries that are equal in every member and lie wholly below
+// every member's context.  Every member's seq_start becomes that many tokens;
+// the group is cut into sub-groups of at most 16 / G sequences (16 MFMA rows),
+// and each sub-group gets one unit per prefix partition.  A malformed
+// group_start (not 0 .. num_seqs, decreasing), a group of one, a member with an
+// invalid context or no common first block give no prefix: such sequences are
+// decoded whole by their own units, so the hint can never change a result.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int32_t wave_min(int32_t x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = min(x, __shfl_xor(x, off));
+  return x;
+}
+
+__global__ __launch_bounds__(1024) void shared_plan_kernel(pkv_decode_args a, const int32_t* __restrict__ group_start,
+                                                           int32_t num_groups, int32_t* __restrict__ seq_start,
+                                                           int32_t* __restrict__ shared_plan) {
+  __shared__ int32_t sm_units, sm_bad;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int32_t S = a.num_seqs, MB = a.max_blocks_per_seq;
+  if (tid == 0) { sm_units = 0; sm_bad = 0; }
+  __syncthreads();
+  for (int32_t i = tid; i <= num_groups; i += 1024) {
+    const int32_t v = group_start[i];
+    bool ok = v >= 0 && v <= S;
+    if (i == 0) ok = ok && v == 0;
+    if (i == num_groups) ok = ok && v == S;
+    else ok = ok && v <= group_start[i + 1];
+    if (!ok) atomicOr(&sm_bad, 1);
+  }
+  __syncthreads();
+  if (sm_bad) {
+    for (int32_t s = tid; s < S; s += 1024) seq_start[s] = 0;
+  } else {
+    const int32_t per_sub = kMaxMfmaGroup / (a.num_heads / a.num_kv_heads);
+    for (int32_t grp = wave; grp < num_groups; grp += 1024 / 64) {
+      const int32_t b = group_start[grp], e = group_start[grp + 1];
+      const int32_t n = e - b;
+      // whole blocks below every member's context (-1: an invalid context)
+      int32_t lim = 0x7FFFFFFF;
+      for (int32_t m = b + lane; m < e; m += 64) {
+        const int32_t ctx = a.context_lens[m];
+        lim = min(lim, len_ok(ctx, a.max_context_len, MB) ? ctx / kBlock : -1);
+      }
+      lim = wave_min(lim);
+      int32_t cp = 0;
+      if (n >= 2 && lim > 0) {
+        const int32_t* t0 = a.block_tables + static_cast<int64_t>(b) * MB;
+        cp = lim;
+        for (int32_t j0 = 0; j0 < lim; j0 += 64) {
+          const int32_t j = j0 + lane;
+          bool eq = true;
+          if (j < lim) {
+            const int32_t ref = t0[j];
+            for (int32_t m = b + 1; m < e && eq; ++m) eq = a.block_tables[static_cast<int64_t>(m) * MB + j] == ref;
+          }
+          const uint64_t differ = __ballot(!eq);
+          if (differ) {
+            cp = j0 + __ffsll(static_cast<unsigned long long>(differ)) - 1;
+            break;
+          }
+        }
+      }
+      const int32_t pref = cp * kBlock;
+      for (int32_t m = b + lane; m < e; m += 64) seq_start[m] = pref;
+      if (pref > 0) {
+        const int32_t nsub = (n + per_sub - 1) / per_sub;
+        const int32_t npp = (pref + a.prefix_part_tokens - 1) / a.prefix_part_tokens;
+        int32_t first = 0;
+        if (lane == 0) first = atomicAdd(&sm_units, nsub * npp);
+        first = __shfl(first, 0);
+        for (int32_t k = lane; k < nsub * npp; k += 64) {
+          const int32_t sub = k / npp, pp = k - sub * npp;
+          int32_t* unit = shared_plan + kPlanHdr + 4 * (first + k);
+          unit[0] = b + sub * per_sub;
+          unit[1] = min(per_sub, n - sub * per_sub);
+          unit[2] = pp;
+          unit[3] = pref;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    shared_plan[0] = sm_units;
+    shared_plan[1] = S;
+    shared_plan[2] = a.max_context_len;
+    shared_plan[3] = MB;
+    shared_plan[4] = a.prefix_part_tokens;
+    shared_plan[5] = 0;
+    shared_plan[6] = 0;
+    shared_plan[7] = 0;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -597,9 +728,29 @@ int pkv_launch_decode_group(const pkv_decode_args& a, void* stream) {
   const int64_t grid = static_cast<int64_t>(a.num_seqs) * (np < 1 ? 1 : np) * a.num_kv_heads;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (a.head_dim == 128) {
-    hipLaunchKernelGGL((decode_group_mfma_kernel<128>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_group_mfma_kernel<128, false>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st, a);
   } else {
-    hipLaunchKernelGGL((decode_group_mfma_kernel<64>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_group_mfma_kernel<64, false>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+int pkv_launch_shared_plan(const pkv_decode_args& a, const int32_t* group_start, int32_t num_groups,
+                           int32_t* seq_start, int32_t* shared_plan, void* stream) {
+  hipLaunchKernelGGL(shared_plan_kernel, dim3(1), dim3(1024), 0, static_cast<hipStream_t>(stream), a, group_start,
+                     num_groups, seq_start, shared_plan);
+  return hipGetLastError();
+}
+
+int pkv_launch_shared_prefix(const pkv_decode_args& a, void* stream) {
+  // at most num_seqs sub-groups, each with ceil(max_context_len / partition) units
+  const int64_t npp = (a.max_context_len + a.prefix_part_tokens - 1) / a.prefix_part_tokens;
+  const int64_t grid = static_cast<int64_t>(a.num_seqs) * (npp < 1 ? 1 : npp) * a.num_kv_heads;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (a.head_dim == 128) {
+    hipLaunchKernelGGL((decode_group_mfma_kernel<128, true>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((decode_group_mfma_kernel<64, true>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }

@@ -162,20 +162,26 @@ def gqa(seed: int = 3, num_seqs: int = 256, lo: int = 128, hi: int = 4096,
     return _plain_decode("gqa", seed + 1000, ctx, 64, 8, 128, "bf16", with_rows=with_rows)
 
 
-def parallel_sampling(seed: int = 4, groups: int = 32, samples: int = 8, prompt: int = 1000,
+def parallel_sampling(seed: int = 4, groups: int = 32, samples=8, prompt=1000,
                       tail_lo: int = 1, tail_hi: int = 512, hq: int = 40, d: int = 128,
-                      with_rows: bool = True) -> Workload:
+                      with_rows: bool = True, hkv: Optional[int] = None) -> Workload:
     """Workload 4: groups x samples forks of one prompt each; tails U[1, 512].
 
     Script per group: create the prompt sequence (it is sample 0), append the
     prompt, flush, fork it samples-1 times, then append each sample's tail in
-    sample order, flush.  Every sample carries one decode query.
+    sample order (a tail of 0 appends nothing), flush.  Every sample carries
+    one decode query; the samples of a group are consecutive in decode_seqs.
+    For parity cases ``samples`` and ``prompt`` may also be per-group lists and
+    ``hkv`` < hq gives grouped-query heads.
     """
     rng = np.random.default_rng(seed)
-    tails = rng.integers(tail_lo, tail_hi + 1, size=(groups, samples)).astype(np.int32)
+    hkv = hq if hkv is None else hkv
+    n_samples = [int(x) for x in (samples if np.ndim(samples) else [samples] * groups)]
+    prompts = [int(x) for x in (prompt if np.ndim(prompt) else [prompt] * groups)]
+    tails = [rng.integers(tail_lo, tail_hi + 1, size=n).astype(np.int32) for n in n_samples]
     # pool sizing (an upper bound on the blocks in use, times 1.2): the prompt's
     # pages once per group, plus per sample one page of headroom and the tail's pages
-    need = groups * _blocks_for(prompt) + sum(_blocks_for(int(t)) + 1 for t in tails.ravel())
+    need = sum(_blocks_for(p) for p in prompts) + sum(_blocks_for(int(t)) + 1 for ts in tails for t in ts)
     nb = int(math.ceil(1.2 * need))
     perm = rng.permutation(nb).astype(np.int32)
     ops: List[Op] = []
@@ -184,26 +190,28 @@ def parallel_sampling(seed: int = 4, groups: int = 32, samples: int = 8, prompt:
     for g in range(groups):
         root = next_id
         ops.append(("create",)); next_id += 1
-        ops.append(("append", root, prompt))
+        ops.append(("append", root, prompts[g]))
         ops.append(("flush",))
         members = [root]
-        for _ in range(samples - 1):
+        for _ in range(n_samples[g] - 1):
             ops.append(("fork", root)); members.append(next_id); next_id += 1
         for i, s in enumerate(members):
-            ops.append(("append", s, int(tails[g, i])))
+            if tails[g][i] > 0:
+                ops.append(("append", s, int(tails[g][i])))
         ops.append(("flush",))
         decode_seqs.extend(members)
-    total = groups * prompt + int(tails.sum())
+    total = sum(prompts) + int(sum(int(ts.sum()) for ts in tails))
     q = _normal(rng, (len(decode_seqs), hq, d), "bf16")
     if with_rows:
-        k_rows = _rows(rng, total, hq, d, "bf16")
-        v_rows = _rows(rng, total, hq, d, "bf16")
+        k_rows = _rows(rng, total, hkv, d, "bf16")
+        v_rows = _rows(rng, total, hkv, d, "bf16")
     else:
-        k_rows = v_rows = np.empty((0, hq, d), dtype=np.uint16)
-    w = Workload("fork", "bf16", hq, hq, d, nb, perm, ops, k_rows, v_rows, decode_seqs, q,
+        k_rows = v_rows = np.empty((0, hkv, d), dtype=np.uint16)
+    w = Workload("fork", "bf16", hq, hkv, d, nb, perm, ops, k_rows, v_rows, decode_seqs, q,
                  np.float32(1.0 / math.sqrt(d)))
-    w.tails = tails  # type: ignore[attr-defined]
+    w.tails = np.array(tails) if len(set(n_samples)) == 1 else tails  # type: ignore[attr-defined]
     w.prompt = prompt  # type: ignore[attr-defined]
+    w.group_start = np.concatenate([[0], np.cumsum(n_samples)]).astype(np.int32)  # type: ignore[attr-defined]
     return w
 
 

@@ -85,6 +85,32 @@ def test_swap_blocks_rejects_bad_arguments_before_touching_memory(P):
     assert L.pkv_swap_blocks(None, None, 8, None, None, 8, None, 0, 2, 64, 16, 1, None) == P.PKV_OK
 
 
+def test_shared_decode_rejects_bad_arguments_before_any_launch(P):
+    L = _lib(P)
+    # out q k v tables MB lens S group_start n_groups Hq Hkv d bs NB mcl scale dtype ws ws_bytes stream
+    base = [256, 512, 768, 1024, 1280, 4, 1536, 2, 1792, 1, 4, 4, 64, 16, 8, 64, 0.125, 1, 2048, 256, None]
+
+    def call(**kw):
+        a = list(base)
+        names = ["out", "q", "k", "v", "tables", "mb", "lens", "S", "gs", "ng", "Hq", "Hkv", "d", "bs", "nb",
+                 "mcl", "scale", "dtype", "ws", "wsb", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return L.pkv_attention_decode_shared(*a)
+    assert call(ng=-1) == P.PKV_ERR_INVALID_ARG
+    assert call(gs=None) == P.PKV_ERR_INVALID_ARG
+    assert call(ng=3) == P.PKV_ERR_INVALID_ARG                 # more groups than sequences
+    assert call() == P.PKV_ERR_INVALID_ARG                     # workspace too small
+    assert "workspace" in L.pkv_last_error().decode()
+    need = L.pkv_attention_decode_shared_workspace_bytes(2, 4, 64, 64)
+    assert need >= L.pkv_attention_workspace_bytes(2, 4, 64, 64)
+    assert call(wsb=need, ws=2049) == P.PKV_ERR_INVALID_ARG    # misaligned workspace
+    assert call(d=96) == P.PKV_ERR_UNSUPPORTED
+    assert call(Hq=6) == P.PKV_ERR_INVALID_ARG
+    assert call(S=0) == P.PKV_OK
+    assert L.pkv_attention_decode_shared_workspace_bytes(0, 4, 64, 64) == 0
+
+
 def _decode(P, **kw):
     a = dict(out=256, q=512, k=768, v=1024, tables=1280, mb=4, lens=1536, S=2, Hq=4, Hkv=2, d=64, bs=16,
              nb=8, maxctx=64, scale=0.125, dtype=1, ws=None, wsb=0)

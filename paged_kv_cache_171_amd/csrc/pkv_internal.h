@@ -74,7 +74,7 @@ int pkv_launch_plan(int32_t* plan, const int32_t* context_lens, int32_t num_seqs
 // Shared-prefix decode (pkv_mfma.hip): the plan of the groups' common leading
 // blocks (fills seq_start and the shared plan), then the MFMA kernel over those
 // blocks.  Tokens per shared-prefix partition:
-constexpr int32_t kPrefixPartTokens = 512;
+constexpr int32_t kPrefixPartTokens = 1024;
 int pkv_launch_shared_plan(const pkv_decode_args& a, const int32_t* group_start, int32_t num_groups,
                            int32_t* seq_start, int32_t* shared_plan, void* stream);
 int pkv_launch_shared_prefix(const pkv_decode_args& a, void* stream);

@@ -513,7 +513,7 @@ def main():
         lens_d.copy_(lens_h, non_blocking=True)
         max_ctx = int(ln.max())
         # the decode plan depends only on this step's lengths: built once, used by every layer
-        B._check(lib.pkv_decode_plan(plan.data_ptr(), plan.numel(), lens_d.data_ptr(), S, H, H, MB, max_ctx, BF16,
+        B._check(lib.pkv_decode_plan(plan.data_ptr(), plan.numel(), lens_d.data_ptr(), S, H, H, MB, P, max_ctx, BF16,
                                      sp))
         n_pairs = len(pairs)
         if n_pairs:

@@ -31,8 +31,14 @@
  *    visible to the host.  Kernels never touch memory outside the buffers
  *    described by the size arguments: out-of-range slots and block ids are
  *    skipped, and attention rows they affect are written as NaN (see each call).
- *  - Supported: block_size 16; head_dim 64 or 128; dtype PKV_F32 or PKV_BF16
+ *  - Supported: block_size 8, 16 or 32 ([CB] "PagedAttention: Memoria virtual
+ *    para la KV cache" names 16 as typical; the others exist to measure the
+ *    trade-off it describes); head_dim 64 or 128; dtype PKV_F32 or PKV_BF16
  *    (the same dtype for q, K and V); num_heads a multiple of num_kv_heads.
+ *    The matrix-core kernels -- grouped-query bf16 decode, shared-prefix
+ *    decode, chunked prefill -- are built for block_size 16: with another size
+ *    grouped-query decode runs on the vector-ALU kernel, shared-prefix decode
+ *    runs plain decode, and prefill returns PKV_ERR_UNSUPPORTED.
  *  - Calls that enqueue work on one stream are ordered by that stream.  For one
  *    decode step the caller enqueues pkv_copy_blocks, then pkv_append, then the
  *    attention calls: copies must read shared blocks before this step writes.
@@ -174,22 +180,23 @@ pkv_status pkv_attention_decode(float* out, const void* q, const void* k_cache,
  * pkv_attention_decode builds it in its workspace on every call.
  *
  * plan: device buffer of at least pkv_decode_plan_bytes(num_seqs,
- * max_context_len) bytes, 16-byte aligned.  num_heads, num_kv_heads and dtype
- * choose the partition size (they must be those of the decode calls).  A
- * sequence with a context length of 0 or an invalid one (see
+ * max_context_len) bytes, 16-byte aligned.  num_heads, num_kv_heads,
+ * block_size and dtype choose the partition size (they must be those of the
+ * decode calls).  A sequence with a context length of 0 or an invalid one (see
  * pkv_attention_decode) gets a unit that writes its 0 or NaN rows.  A plan
- * records num_seqs, max_context_len, max_blocks_per_seq and the partition
- * size; a decode call with other values writes NaN rows instead of using it.
+ * records num_seqs, max_context_len, max_blocks_per_seq, block_size and the
+ * partition size; a decode call with other values writes NaN rows instead of
+ * using it.
  * ------------------------------------------------------------------------ */
 size_t pkv_decode_plan_bytes(int32_t num_seqs, int32_t max_context_len);
 
 pkv_status pkv_decode_plan(void* plan, size_t plan_bytes, const int32_t* context_lens, int32_t num_seqs,
                            int32_t num_heads, int32_t num_kv_heads, int32_t max_blocks_per_seq,
-                           int32_t max_context_len, pkv_dtype dtype, void* stream);
+                           int32_t block_size, int32_t max_context_len, pkv_dtype dtype, void* stream);
 
 /* pkv_attention_decode with a plan built by pkv_decode_plan from the same
- * context_lens, num_seqs, heads, dtype, max_blocks_per_seq and max_context_len
- * (and not changed since).  Same arguments and results otherwise; the
+ * context_lens, num_seqs, heads, dtype, max_blocks_per_seq, block_size and
+ * max_context_len (and not changed since).  Same arguments and results otherwise; the
  * workspace of pkv_attention_workspace_bytes(...) is enough. */
 pkv_status pkv_attention_decode_planned(float* out, const void* q, const void* k_cache, const void* v_cache,
                                         const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -289,6 +296,7 @@ pkv_status pkv_allocator_create(int32_t num_blocks, int32_t block_size,
 void pkv_allocator_destroy(pkv_allocator* a);
 int32_t pkv_allocator_num_free(const pkv_allocator* a);
 int32_t pkv_allocator_num_blocks(const pkv_allocator* a);   /* pool size (-1 for NULL) */
+int32_t pkv_allocator_block_size(const pkv_allocator* a);   /* tokens per block (0 for NULL) */
 
 pkv_status pkv_seq_create(pkv_allocator* a, int64_t* seq_id);
 

@@ -42,7 +42,7 @@ _SIGS = {
     "pkv_attention_decode": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32,
                                       _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_p, _c_sz, _c_p]),
     "pkv_decode_plan_bytes": (_c_sz, [_c_i32, _c_i32]),
-    "pkv_decode_plan": (_c_i32, [_c_p, _c_sz, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_p]),
+    "pkv_decode_plan": (_c_i32, [_c_p, _c_sz, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_p]),
     "pkv_attention_decode_planned": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32,
                                               _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_p, _c_sz, _c_p,
                                               _c_sz, _c_p]),
@@ -57,6 +57,7 @@ _SIGS = {
     "pkv_allocator_destroy": (None, [_c_p]),
     "pkv_allocator_num_free": (_c_i32, [_c_p]),
     "pkv_allocator_num_blocks": (_c_i32, [_c_p]),
+    "pkv_allocator_block_size": (_c_i32, [_c_p]),
     "pkv_scheduler_create": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.POINTER(_c_p)]),
     "pkv_scheduler_destroy": (None, [_c_p]),
     "pkv_scheduler_add_request": (_c_i32, [_c_p, _c_i32, _c_i32, _P_I64]),
@@ -168,20 +169,22 @@ def pkv_decode_plan_bytes(num_seqs: int, max_context_len: int) -> int:
 
 
 def pkv_decode_plan(plan: torch.Tensor, context_lens: torch.Tensor, num_heads: int, num_kv_heads: int,
-                    max_blocks_per_seq: int, max_context_len: int, dtype: int, stream=None) -> None:
+                    max_blocks_per_seq: int, max_context_len: int, dtype: int, stream=None,
+                    block_size: int = 16) -> None:
     """plan: device uint8 buffer; context_lens: int32 [S] on the GPU; dtype PKV_F32 / PKV_BF16."""
     _dev(plan, context_lens)
     _check(_lib.pkv_decode_plan(plan.data_ptr(), plan.numel() * plan.element_size(), context_lens.data_ptr(),
-                                context_lens.numel(), num_heads, num_kv_heads, max_blocks_per_seq,
+                                context_lens.numel(), num_heads, num_kv_heads, max_blocks_per_seq, block_size,
                                 int(max_context_len), int(dtype), _stream(stream)))
 
 
 def plan_for(context_lens: torch.Tensor, num_heads: int, num_kv_heads: int, max_blocks_per_seq: int,
-             max_context_len: int, dtype: int) -> torch.Tensor:
+             max_context_len: int, dtype: int, block_size: int = 16) -> torch.Tensor:
     """A device plan for these lengths (pkv_decode_plan into a fresh buffer)."""
     n = pkv_decode_plan_bytes(context_lens.numel(), max_context_len)
     plan = torch.empty(max(n, 16), dtype=torch.uint8, device=context_lens.device)
-    pkv_decode_plan(plan, context_lens, num_heads, num_kv_heads, max_blocks_per_seq, max_context_len, dtype)
+    pkv_decode_plan(plan, context_lens, num_heads, num_kv_heads, max_blocks_per_seq, max_context_len, dtype,
+                    block_size=block_size)
     return plan
 
 

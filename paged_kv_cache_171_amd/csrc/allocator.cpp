@@ -80,7 +80,8 @@ pkv_status pkv_allocator_create(int32_t num_blocks, int32_t block_size,
                                 const int32_t* initial_free_order, pkv_allocator** out) {
   if (!out) return pkv_fail(PKV_ERR_INVALID_ARG, "pkv_allocator_create: out is NULL");
   if (num_blocks <= 0) return pkv_fail(PKV_ERR_INVALID_ARG, "pkv_allocator_create: num_blocks must be > 0");
-  if (block_size != 16) return pkv_fail(PKV_ERR_UNSUPPORTED, "pkv_allocator_create: block_size must be 16");
+  if (block_size != 8 && block_size != 16 && block_size != 32)
+    return pkv_fail(PKV_ERR_UNSUPPORTED, "pkv_allocator_create: block_size must be 8, 16 or 32");
   std::vector<int32_t> order(num_blocks);
   if (initial_free_order) {
     std::vector<char> seen(num_blocks, 0);
@@ -106,6 +107,8 @@ pkv_status pkv_allocator_create(int32_t num_blocks, int32_t block_size,
 }
 
 void pkv_allocator_destroy(pkv_allocator* a) { delete a; }
+
+int32_t pkv_allocator_block_size(const pkv_allocator* a) { return a ? a->block_size : 0; }
 
 int32_t pkv_allocator_num_free(const pkv_allocator* a) {
   return a ? static_cast<int32_t>(a->free_list.size()) : -1;

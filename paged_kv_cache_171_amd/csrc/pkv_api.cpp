@@ -13,7 +13,6 @@
 namespace {
 thread_local std::string g_last_error;
 
-constexpr int kBlock = 16;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -22,7 +21,8 @@ int elem_bytes(pkv_dtype dt) { return dt == PKV_F32 ? 4 : 2; }
 pkv_status check_common(const char* fn, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                         pkv_dtype dtype) {
   if (dtype != PKV_F32 && dtype != PKV_BF16) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
-  if (block_size != kBlock) return pkv_failf(PKV_ERR_UNSUPPORTED, "%s: block_size must be 16 (got %d)", fn, block_size);
+  if (block_size != 8 && block_size != 16 && block_size != 32)
+    return pkv_failf(PKV_ERR_UNSUPPORTED, "%s: block_size must be 8, 16 or 32 (got %d)", fn, block_size);
   if (head_dim != 64 && head_dim != 128)
     return pkv_failf(PKV_ERR_UNSUPPORTED, "%s: head_dim must be 64 or 128 (got %d)", fn, head_dim);
   if (num_kv_heads <= 0) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: num_kv_heads must be > 0", fn);
@@ -119,7 +119,7 @@ pkv_status pkv_append(void* k_cache, void* v_cache, const void* k, const void* v
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: cache and row pointers must be 16-byte aligned", fn);
   const int32_t row_bytes = head_dim * elem_bytes(dtype);
   return hip_status(fn, pkv_launch_append(k_cache, v_cache, k, v, slot_mapping, num_tokens,
-                                          num_blocks, num_kv_heads, row_bytes, stream));
+                                          num_blocks, num_kv_heads, row_bytes, block_size, stream));
 }
 
 pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst,
@@ -135,7 +135,7 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst,
   if (!k_cache || !v_cache || !src_dst) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: NULL pointer", fn);
   if (!aligned16(k_cache) || !aligned16(v_cache))
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: cache pointers must be 16-byte aligned", fn);
-  const int64_t block_bytes = static_cast<int64_t>(num_kv_heads) * kBlock * head_dim * elem_bytes(dtype);
+  const int64_t block_bytes = static_cast<int64_t>(num_kv_heads) * block_size * head_dim * elem_bytes(dtype);
   return hip_status(fn, pkv_launch_copy_blocks(k_cache, v_cache, src_dst, num_pairs, num_blocks,
                                                block_bytes, stream));
 }
@@ -174,7 +174,7 @@ pkv_status pkv_swap_blocks(void* dst_k_cache, void* dst_v_cache, int32_t dst_num
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: pools must be device memory or pinned host memory", fn);
   if (!device_accessible(src_dst))
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: src_dst must be device memory or pinned host memory", fn);
-  const int64_t block_bytes = static_cast<int64_t>(num_kv_heads) * kBlock * head_dim * elem_bytes(dtype);
+  const int64_t block_bytes = static_cast<int64_t>(num_kv_heads) * block_size * head_dim * elem_bytes(dtype);
   return hip_status(fn, pkv_launch_swap_blocks(dst_k_cache, dst_v_cache, dst_num_blocks, src_k_cache, src_v_cache,
                                                src_num_blocks, src_dst, num_pairs, block_bytes, stream));
 }
@@ -186,10 +186,12 @@ size_t pkv_decode_plan_bytes(int32_t num_seqs, int32_t max_context_len) {
 
 pkv_status pkv_decode_plan(void* plan, size_t plan_bytes_given, const int32_t* context_lens, int32_t num_seqs,
                            int32_t num_heads, int32_t num_kv_heads, int32_t max_blocks_per_seq,
-                           int32_t max_context_len, pkv_dtype dtype, void* stream) {
+                           int32_t block_size, int32_t max_context_len, pkv_dtype dtype, void* stream) {
   const char* fn = "pkv_decode_plan";
   if (num_seqs < 0 || max_blocks_per_seq <= 0 || max_context_len < 0)
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  if (block_size != 8 && block_size != 16 && block_size != 32)
+    return pkv_failf(PKV_ERR_UNSUPPORTED, "%s: block_size must be 8, 16 or 32 (got %d)", fn, block_size);
   if (dtype != PKV_F32 && dtype != PKV_BF16) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
   if (num_kv_heads <= 0 || num_heads <= 0 || num_heads % num_kv_heads != 0)
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: num_heads (%d) must be a positive multiple of num_kv_heads (%d)", fn,
@@ -204,7 +206,8 @@ pkv_status pkv_decode_plan(void* plan, size_t plan_bytes_given, const int32_t* c
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: plan buffer of %zu bytes is smaller than the %zu needed", fn,
                      plan_bytes_given, need);
   return hip_status(fn, pkv_launch_plan(static_cast<int32_t*>(plan), context_lens, num_seqs, max_blocks_per_seq,
-                                        max_context_len, pkv_part_tokens(dtype, num_heads, num_kv_heads), stream));
+                                        block_size, max_context_len,
+                                        pkv_part_tokens(dtype, num_heads, num_kv_heads, block_size), stream));
 }
 
 size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
@@ -240,7 +243,7 @@ static pkv_status decode_impl(const char* fn, float* out, const void* q, const v
   const int64_t grid = static_cast<int64_t>(num_seqs) * num_heads * np;
   if (grid > 0x7FFFFFFF || static_cast<int64_t>(num_seqs) * (np + 1) > 0x3FFFFFFF)
     return pkv_failf(PKV_ERR_UNSUPPORTED, "%s: launch grid too large", fn);
-  const int32_t part_tokens = pkv_part_tokens(dtype, num_heads, num_kv_heads);
+  const int32_t part_tokens = pkv_part_tokens(dtype, num_heads, num_kv_heads, block_size);
   const size_t pb = plan_bytes(num_seqs, max_context_len);
   const size_t part = partial_bytes(num_seqs, num_heads, head_dim, max_context_len);
   const size_t need = (build_plan ? align256(pb) : 0) + part;
@@ -254,7 +257,7 @@ static pkv_status decode_impl(const char* fn, float* out, const void* q, const v
     plan = ws;
     ws += align256(pb);
     const int err = pkv_launch_plan(static_cast<int32_t*>(const_cast<void*>(plan)), context_lens, num_seqs,
-                                    max_blocks_per_seq, max_context_len, part_tokens, stream);
+                                    max_blocks_per_seq, block_size, max_context_len, part_tokens, stream);
     if (err) return hip_status(fn, err);
   } else {
     if (!plan) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: plan is NULL", fn);
@@ -279,6 +282,7 @@ static pkv_status decode_impl(const char* fn, float* out, const void* q, const v
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;
   a.num_blocks = num_blocks;
+  a.block_size = block_size;
   a.max_context_len = max_context_len;
   a.num_partitions = np;
   a.part_tokens = part_tokens;
@@ -332,7 +336,8 @@ pkv_status pkv_attention_decode_shared(float* out, const void* q, const void* k_
   const int32_t group = num_kv_heads > 0 ? num_heads / num_kv_heads : 0;
   // only the bf16 MFMA kernel reads a prefix for several sequences; otherwise
   // (or with no groups) this is plain decode
-  if (dtype != PKV_BF16 || group < 1 || group > kMaxMfmaGroup || num_groups == 0 || num_seqs <= 0)
+  if (dtype != PKV_BF16 || group < 1 || group > kMaxMfmaGroup || block_size != kMfmaBlockSize || num_groups == 0 ||
+      num_seqs <= 0)
     return decode_impl(fn, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                        num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_context_len, scale, dtype,
                        nullptr, 0, workspace, workspace_bytes, true, stream);
@@ -376,9 +381,10 @@ pkv_status pkv_attention_decode_shared(float* out, const void* q, const void* k_
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;
   a.num_blocks = num_blocks;
+  a.block_size = block_size;
   a.max_context_len = max_context_len;
   a.num_partitions = l.slots;
-  a.part_tokens = pkv_part_tokens(dtype, num_heads, num_kv_heads);
+  a.part_tokens = pkv_part_tokens(dtype, num_heads, num_kv_heads, block_size);
   a.scale_log2 = scale * 1.4426950408889634f;
   a.dtype = dtype;
   a.seq_start = reinterpret_cast<const int32_t*>(ws + l.seq_start);
@@ -388,7 +394,7 @@ pkv_status pkv_attention_decode_shared(float* out, const void* q, const void* k_
                                    reinterpret_cast<int32_t*>(ws + l.shared_plan), stream);
   if (!err)
     err = pkv_launch_plan(reinterpret_cast<int32_t*>(ws + l.plan), context_lens, num_seqs, max_blocks_per_seq,
-                          max_context_len, a.part_tokens, stream, a.seq_start);
+                          block_size, max_context_len, a.part_tokens, stream, a.seq_start);
   if (!err) err = pkv_launch_shared_prefix(a, stream);
   if (!err) err = pkv_launch_decode(a, stream);
   return hip_status(fn, err);
@@ -405,6 +411,8 @@ pkv_status pkv_attention_prefill_chunk(float* out, const void* q, const int32_t*
   pkv_status st = check_common(fn, num_kv_heads, head_dim, block_size, dtype);
   if (st != PKV_OK) return st;
   if (dtype != PKV_BF16) return pkv_failf(PKV_ERR_UNSUPPORTED, "%s: only bf16 is built", fn);
+  if (block_size != kMfmaBlockSize)
+    return pkv_failf(PKV_ERR_UNSUPPORTED, "%s: only block_size %d is built", fn, kMfmaBlockSize);
   if (num_seqs < 0 || num_query_tokens < 0 || max_query_len < 0 || max_context_len < 0)
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: negative size", fn);
   if (num_heads <= 0 || num_heads % num_kv_heads != 0)

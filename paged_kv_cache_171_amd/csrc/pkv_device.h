@@ -12,10 +12,10 @@ namespace pkvd {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBlock = 16;            // tokens per block (the pages' P = 16)
+constexpr int kBlock = 16;            // tokens per block of the MFMA kernels (the pages' P = 16)
 constexpr float kNegBig = -FLT_MAX;   // finite "minus infinity" for running maxima
 // Plan layout (int32): a header of kPlanHdr words -- n_units, num_seqs,
-// max_context_len, max_blocks_per_seq, part_tokens, 0, 0, 0 -- then (s, p) per
+// max_context_len, max_blocks_per_seq, part_tokens, block_size, 0, 0 -- then (s, p) per
 // unit; p = -1 marks a sequence with no attention work (empty or invalid
 // context).
 constexpr int kPlanHdr = 8;
@@ -23,14 +23,15 @@ constexpr int kPlanHdr = 8;
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // A context length that takes part in attention (others give a 0 row or a NaN row).
-__device__ __forceinline__ bool len_ok(int32_t ctx, int32_t max_context_len, int32_t max_blocks_per_seq) {
-  return ctx > 0 && ctx <= max_context_len && ctx <= max_blocks_per_seq * kBlock;
+__device__ __forceinline__ bool len_ok(int32_t ctx, int32_t max_context_len, int32_t max_blocks_per_seq,
+                                       int32_t block_size) {
+  return ctx > 0 && ctx <= max_context_len && static_cast<int64_t>(ctx) <= static_cast<int64_t>(max_blocks_per_seq) * block_size;
 }
 
 // The plan was built for these sizes.
 __device__ __forceinline__ bool plan_matches(const int32_t* plan, const pkv_decode_args& a) {
   return plan[1] == a.num_seqs && plan[2] == a.max_context_len && plan[3] == a.max_blocks_per_seq &&
-         plan[4] == a.part_tokens;
+         plan[4] == a.part_tokens && plan[5] == a.block_size;
 }
 
 __device__ __forceinline__ const int32_t* plan_units(const int32_t* plan) { return plan + kPlanHdr; }

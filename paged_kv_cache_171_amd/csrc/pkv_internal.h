@@ -14,7 +14,7 @@ pkv_status pkv_failf(pkv_status st, const char* fmt, ...);
 // returns hipSuccess or the launch error as an int.
 int pkv_launch_append(void* k_cache, void* v_cache, const void* k, const void* v,
                       const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
-                      int32_t num_kv_heads, int32_t row_bytes, void* stream);
+                      int32_t num_kv_heads, int32_t row_bytes, int32_t block_size, void* stream);
 int pkv_launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst, int32_t num_pairs,
                            int32_t num_blocks, int64_t block_bytes, void* stream);
 // Block copies between two pools (device pointers; a host pool by its mapped address).
@@ -28,9 +28,14 @@ int pkv_launch_swap_blocks(void* k_dst, void* v_dst, int32_t dst_blocks, const v
 constexpr int32_t kMinPartTokens = 1024;
 constexpr int32_t kMaxPartTokens = 4096;
 constexpr int32_t kMaxMfmaGroup = 16;
-inline int32_t pkv_part_tokens(int dtype, int32_t num_heads, int32_t num_kv_heads) {
+constexpr int32_t kMfmaBlockSize = 16;   // the matrix-core kernels' block size
+// Whether decode of these heads runs on the MFMA group kernel.
+inline bool pkv_uses_mfma(int dtype, int32_t num_heads, int32_t num_kv_heads, int32_t block_size) {
   const int32_t group = num_heads / num_kv_heads;
-  return (dtype == PKV_BF16 && group >= 2 && group <= kMaxMfmaGroup) ? kMaxPartTokens : kMinPartTokens;
+  return dtype == PKV_BF16 && group >= 2 && group <= kMaxMfmaGroup && block_size == kMfmaBlockSize;
+}
+inline int32_t pkv_part_tokens(int dtype, int32_t num_heads, int32_t num_kv_heads, int32_t block_size) {
+  return pkv_uses_mfma(dtype, num_heads, num_kv_heads, block_size) ? kMaxPartTokens : kMinPartTokens;
 }
 
 struct pkv_decode_args {
@@ -49,6 +54,7 @@ struct pkv_decode_args {
   int32_t num_kv_heads;
   int32_t head_dim;
   int32_t num_blocks;
+  int32_t block_size;      // tokens per block: 8, 16 or 32 (16 for the MFMA kernels)
   int32_t max_context_len;
   int32_t num_partitions;  // NP = ceil(max_context_len / kMinPartTokens): partial slots per row
   int32_t part_tokens;     // tokens per partition for this launch
@@ -68,7 +74,7 @@ struct pkv_decode_args {
 int pkv_launch_decode(const pkv_decode_args& a, void* stream);
 int pkv_launch_decode_group(const pkv_decode_args& a, void* stream);
 int pkv_launch_plan(int32_t* plan, const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
-                    int32_t max_context_len, int32_t part_tokens, void* stream,
+                    int32_t block_size, int32_t max_context_len, int32_t part_tokens, void* stream,
                     const int32_t* seq_start = nullptr);
 
 // Shared-prefix decode (pkv_mfma.hip): the plan of the groups' common leading

@@ -14,7 +14,6 @@
 namespace {
 
 using pkvd::u32x4;
-using pkvd::kBlock;
 using pkvd::kNegBig;
 using pkvd::kPlanHdr;
 using pkvd::fast_exp2;
@@ -36,7 +35,7 @@ __global__ __launch_bounds__(256) void append_kernel(char* __restrict__ k_cache,
                                                      const char* __restrict__ v,
                                                      const int64_t* __restrict__ slot_mapping,
                                                      int64_t total_units, int64_t num_slots,
-                                                     int32_t num_kv_heads, int32_t row_bytes) {
+                                                     int32_t num_kv_heads, int32_t row_bytes, int32_t bs_log2) {
   const int64_t u = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (u >= total_units) return;
   const int32_t chunks = row_bytes >> 4;                  // 16-byte units per row
@@ -45,10 +44,10 @@ __global__ __launch_bounds__(256) void append_kernel(char* __restrict__ k_cache,
   const int64_t rem = u - t * per_token;                  // h * chunks + c
   const int64_t slot = slot_mapping[t];
   if (slot < 0 || slot >= num_slots) return;
-  const int64_t blk = slot >> 4, off = slot & 15;
+  const int64_t blk = slot >> bs_log2, off = slot & ((1 << bs_log2) - 1);
   const int32_t h = static_cast<int32_t>(rem / chunks);
   const int32_t c = static_cast<int32_t>(rem - static_cast<int64_t>(h) * chunks);
-  const int64_t dst = ((blk * num_kv_heads + h) * kBlock + off) * row_bytes + (static_cast<int64_t>(c) << 4);
+  const int64_t dst = (((blk * num_kv_heads + h) << bs_log2) + off) * row_bytes + (static_cast<int64_t>(c) << 4);
   const int64_t src = u << 4;
   const u32x4 kv = *reinterpret_cast<const u32x4*>(k + src);
   const u32x4 vv = *reinterpret_cast<const u32x4*>(v + src);
@@ -179,14 +178,15 @@ template <> struct Elem<uint16_t> {  // bf16 bits
 // sequence with one partition writes the output row; otherwise it writes a
 // partial (max, sum, unnormalised accumulator) for merge_partitions_kernel.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, int BS>
 struct DecodeShape {
   static constexpr int kEpl = Elem<T>::kEpl;            // elements per lane per load
   static constexpr int kLpr = D / kEpl;                 // lanes per token row
   static constexpr int kTpl = 64 / kLpr;                // tokens per 1 KiB load
-  static constexpr int kNld = kBlock / kTpl;            // KiB per tile
+  static constexpr int kNld = BS / kTpl;                // KiB per tile
   static constexpr int kBpi = kNld <= 4 ? 2 : 1;        // tiles in flight per wave
   static_assert(kLpr == 8 || kLpr == 16 || kLpr == 32, "unsupported shape");
+  static_assert(kNld >= 1, "a tile must fill at least one 1 KiB load");
 };
 
 // ---------------------------------------------------------------------------
@@ -202,7 +202,7 @@ struct DecodeShape {
 __global__ __launch_bounds__(1024) void plan_kernel(int32_t* __restrict__ plan,
                                                     const int32_t* __restrict__ context_lens,
                                                     int32_t num_seqs, int32_t max_blocks_per_seq,
-                                                    int32_t max_context_len, int32_t part,
+                                                    int32_t block_size, int32_t max_context_len, int32_t part,
                                                     const int32_t* __restrict__ seq_start) {
   __shared__ int32_t bucket[kMaxPartTokens];   // remainder size -> count, then -> next slot
   __shared__ int32_t scan[1024];
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(int32_t* __restrict__ plan,
   int32_t full = 0;
   for (int32_t s = tid; s < num_seqs; s += 1024) {
     const int32_t ctx = context_lens[s];
-    if (!len_ok(ctx, max_context_len, max_blocks_per_seq)) continue;
+    if (!len_ok(ctx, max_context_len, max_blocks_per_seq, block_size)) continue;
     const int32_t len = ctx - (seq_start ? seq_start[s] : 0);
     full += len / part;
     if (len % part) atomicAdd(&bucket[len % part], 1);
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(int32_t* __restrict__ plan,
   for (int32_t base = 0; base < num_seqs; base += 1024) {
     const int32_t s = base + tid;
     const int32_t ctx = s < num_seqs ? context_lens[s] : 0;
-    const bool ok = s < num_seqs && len_ok(ctx, max_context_len, max_blocks_per_seq);
+    const bool ok = s < num_seqs && len_ok(ctx, max_context_len, max_blocks_per_seq, block_size);
     const int32_t len = ok ? ctx - (seq_start ? seq_start[s] : 0) : 0;
     const int32_t nf = len / part;
     scan[tid] = nf;
@@ -286,15 +286,16 @@ __global__ __launch_bounds__(1024) void plan_kernel(int32_t* __restrict__ plan,
     plan[2] = max_context_len;
     plan[3] = max_blocks_per_seq;
     plan[4] = part;
-    plan[5] = 0;
+    plan[5] = block_size;
     plan[6] = 0;
     plan[7] = 0;
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, int BS>
 __global__ __launch_bounds__(256) void decode_valu_kernel(pkv_decode_args a) {
-  using S = DecodeShape<T, D>;
+  using S = DecodeShape<T, D, BS>;
+  constexpr int kBlock = BS;          // tokens per block of this instance
   constexpr int EPL = S::kEpl, LPR = S::kLpr, TPL = S::kTpl, NLD = S::kNld, BPI = S::kBpi;
 
   __shared__ float sm_acc[kWaves][D];
@@ -506,7 +507,7 @@ __global__ __launch_bounds__(D) void merge_partitions_kernel(pkv_decode_args a) 
   const int32_t s = static_cast<int32_t>(sh / a.num_heads);
   if (!plan_matches(a.plan, a)) return;                // the decode kernel wrote NaN rows
   const int32_t ctx = a.context_lens[s];
-  if (!len_ok(ctx, a.max_context_len, a.max_blocks_per_seq)) return;
+  if (!len_ok(ctx, a.max_context_len, a.max_blocks_per_seq, a.block_size)) return;
   // slots 0 .. base-1 hold the shared-prefix partials (if any), then the
   // sequence's own partitions
   const int32_t start = pkvd::seq_start_of(a, s);
@@ -521,24 +522,31 @@ __global__ __launch_bounds__(D) void merge_partitions_kernel(pkv_decode_args a) 
 template <typename T, int D>
 int launch_decode_valu(const pkv_decode_args& a, hipStream_t st) {
   const int64_t np = (a.max_context_len + a.part_tokens - 1) / a.part_tokens;
-  const int64_t grid = static_cast<int64_t>(a.num_seqs) * (np < 1 ? 1 : np) * a.num_heads;
-  hipLaunchKernelGGL((decode_valu_kernel<T, D>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st, a);
+  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.num_seqs) * (np < 1 ? 1 : np) * a.num_heads));
+  if (a.block_size == 8) {
+    hipLaunchKernelGGL((decode_valu_kernel<T, D, 8>), grid, dim3(256), 0, st, a);
+  } else if (a.block_size == 32) {
+    hipLaunchKernelGGL((decode_valu_kernel<T, D, 32>), grid, dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((decode_valu_kernel<T, D, 16>), grid, dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
 int pkv_launch_plan(int32_t* plan, const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
-                    int32_t max_context_len, int32_t part_tokens, void* stream, const int32_t* seq_start) {
+                    int32_t block_size, int32_t max_context_len, int32_t part_tokens, void* stream,
+                    const int32_t* seq_start) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, static_cast<hipStream_t>(stream), plan, context_lens,
-                     num_seqs, max_blocks_per_seq, max_context_len, part_tokens, seq_start);
+                     num_seqs, max_blocks_per_seq, block_size, max_context_len, part_tokens, seq_start);
   return hipGetLastError();
 }
 
 
 int pkv_launch_append(void* k_cache, void* v_cache, const void* k, const void* v,
                       const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
-                      int32_t num_kv_heads, int32_t row_bytes, void* stream) {
+                      int32_t num_kv_heads, int32_t row_bytes, int32_t block_size, void* stream) {
   const int64_t units = static_cast<int64_t>(num_tokens) * num_kv_heads * (row_bytes >> 4);
   if (units == 0) return hipSuccess;
   const int64_t grid = (units + 255) / 256;
@@ -546,7 +554,8 @@ int pkv_launch_append(void* k_cache, void* v_cache, const void* k, const void* v
                      static_cast<hipStream_t>(stream), static_cast<char*>(k_cache),
                      static_cast<char*>(v_cache), static_cast<const char*>(k),
                      static_cast<const char*>(v), slot_mapping, units,
-                     static_cast<int64_t>(num_blocks) * kBlock, num_kv_heads, row_bytes);
+                     static_cast<int64_t>(num_blocks) * block_size, num_kv_heads, row_bytes,
+                     block_size == 8 ? 3 : block_size == 16 ? 4 : 5);
   return hipGetLastError();
 }
 
@@ -577,9 +586,8 @@ int pkv_launch_swap_blocks(void* k_dst, void* v_dst, int32_t dst_blocks, const v
 
 int pkv_launch_decode(const pkv_decode_args& a, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int32_t group = a.num_heads / a.num_kv_heads;
   int err;
-  if (a.dtype == PKV_BF16 && group >= 2 && group <= kMaxMfmaGroup) {
+  if (pkv_uses_mfma(a.dtype, a.num_heads, a.num_kv_heads, a.block_size)) {
     err = pkv_launch_decode_group(a, stream);
   } else if (a.dtype == PKV_BF16) {
     err = a.head_dim == 128 ? launch_decode_valu<uint16_t, 128>(a, st) : launch_decode_valu<uint16_t, 64>(a, st);

@@ -412,7 +412,7 @@ __global__ __launch_bounds__(1024) void shared_plan_kernel(pkv_decode_args a, co
       int32_t lim = 0x7FFFFFFF;
       for (int32_t m = b + lane; m < e; m += 64) {
         const int32_t ctx = a.context_lens[m];
-        lim = min(lim, len_ok(ctx, a.max_context_len, MB) ? ctx / kBlock : -1);
+        lim = min(lim, len_ok(ctx, a.max_context_len, MB, kBlock) ? ctx / kBlock : -1);
       }
       lim = wave_min(lim);
       int32_t cp = 0;
@@ -528,7 +528,7 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_chunk_mfma_kernel(pkv
   if (r0 >= rows) return;
   const int32_t r_end = min(rows, r0 + kPrefillRowsPerWg);
   const int32_t ctx = a.context_lens[s];
-  if (ctx < nq || !len_ok(ctx, a.max_context_len, a.max_blocks_per_seq)) {
+  if (ctx < nq || !len_ok(ctx, a.max_context_len, a.max_blocks_per_seq, kBlock)) {
     for (int idx = threadIdx.x; idx < (r_end - r0) * D; idx += kPrefillThreads) {
       const int32_t r = r0 + idx / D, d = idx % D;
       a.out[((static_cast<int64_t>(q0) + r / G) * Hq + kvh * G + r % G) * D + d] = __builtin_nanf("");

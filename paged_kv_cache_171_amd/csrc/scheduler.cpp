@@ -37,8 +37,6 @@
 
 namespace {
 
-constexpr int32_t kBlockTokens = 16;
-
 enum : int32_t { kWaiting = 0, kRunning = 1, kSwapped = 2, kFinished = 3 };
 
 struct Request {
@@ -50,8 +48,6 @@ struct Request {
   int64_t length = 0;                  // cached tokens (kept while swapped)
   std::vector<int32_t> host_table;     // host blocks while swapped
 };
-
-int64_t blocks_for(int64_t tokens) { return (tokens + kBlockTokens - 1) / kBlockTokens; }
 
 }  // namespace
 
@@ -72,6 +68,9 @@ struct pkv_scheduler {
   std::vector<int32_t> swap_out_pairs, swap_in_pairs, prefill_qsl;
 
   bool done() const { return queue.empty() && running.empty() && swapped.empty(); }
+
+  int64_t block_size() const { return pkv_allocator_block_size(alloc); }
+  int64_t blocks_for(int64_t tokens) const { return (tokens + block_size() - 1) / block_size(); }
 
   int32_t free_blocks() const { return pkv_allocator_num_free(alloc); }
 
@@ -163,7 +162,7 @@ struct pkv_scheduler {
         while (!swapped.empty() && static_cast<int32_t>(running.size()) < max_num_seqs && budget >= 1) {
           const int64_t id = swapped.front();
           Request& r = req[id];
-          const int64_t need = blocks_for(r.length) + (r.length % kBlockTokens == 0 ? 1 : 0);
+          const int64_t need = blocks_for(r.length) + (r.length % block_size() == 0 ? 1 : 0);
           if (need > free_blocks()) break;
           swapped.pop_front();
           pkv_seq_create(alloc, &r.seq);
@@ -260,7 +259,7 @@ pkv_status pkv_scheduler_add_request(pkv_scheduler* s, int32_t prompt_len, int32
   if (!s || !request_id) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: NULL argument", fn);
   if (prompt_len < 1 || output_len < 1 || prompt_len > s->max_tokens)
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: prompt must be in [1, %d] and output >= 1", fn, s->max_tokens);
-  if (blocks_for(static_cast<int64_t>(prompt_len) + output_len) > pkv_allocator_num_blocks(s->alloc))
+  if (s->blocks_for(static_cast<int64_t>(prompt_len) + output_len) > pkv_allocator_num_blocks(s->alloc))
     return pkv_failf(PKV_ERR_OUT_OF_BLOCKS, "%s: the request would not fit the pool even alone", fn);
   Request r;
   r.prompt = prompt_len;

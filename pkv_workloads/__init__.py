@@ -109,16 +109,16 @@ def lognormal_lengths(rng, n: int, median: float = 200.0, sigma: float = 1.0,
     return np.clip(np.rint(x), lo, hi).astype(np.int32)
 
 
-def _blocks_for(n_tokens: int) -> int:
-    # pool sizing only: number of 16-token pages that n tokens occupy
-    return -(-int(n_tokens) // BLOCK_SIZE)
+def _blocks_for(n_tokens: int, block_size: int = BLOCK_SIZE) -> int:
+    # pool sizing only: number of pages that n tokens occupy
+    return -(-int(n_tokens) // block_size)
 
 
 def _plain_decode(name, seed, ctx, hq, hkv, d, dtype, num_blocks=None, pool_factor=1.2,
-                  with_rows=True) -> Workload:
+                  with_rows=True, block_size=BLOCK_SIZE) -> Workload:
     rng = np.random.default_rng(seed)
     ctx = np.asarray(ctx, dtype=np.int32)
-    need = sum(_blocks_for(c) for c in ctx)
+    need = sum(_blocks_for(c, block_size) for c in ctx)
     nb = int(num_blocks) if num_blocks is not None else int(math.ceil(pool_factor * need))
     perm = rng.permutation(nb).astype(np.int32)
     q = _normal(rng, (len(ctx), hq, d), dtype)
@@ -135,7 +135,7 @@ def _plain_decode(name, seed, ctx, hq, hkv, d, dtype, num_blocks=None, pool_fact
     ops.append(("flush",))
     scale = np.float32(1.0 / math.sqrt(d))
     return Workload(name, dtype, hq, hkv, d, nb, perm, ops, k_rows, v_rows,
-                    list(range(len(ctx))), q, scale)
+                    list(range(len(ctx))), q, scale, block_size=block_size)
 
 
 def tiny(seed: int = 1) -> Workload:
@@ -147,11 +147,12 @@ def shaped_13b_lengths(seed: int = 2, num_seqs: int = 64) -> np.ndarray:
     return lognormal_lengths(np.random.default_rng(seed), num_seqs)
 
 
-def shaped_13b(seed: int = 2, num_seqs: int = 64, with_rows: bool = True) -> Workload:
-    """Workload 2: 64 seqs, 40 MHA heads, d 128, bf16, lognormal lengths, pool 1.2x."""
+def shaped_13b(seed: int = 2, num_seqs: int = 64, with_rows: bool = True, block_size: int = BLOCK_SIZE) -> Workload:
+    """Workload 2: 64 seqs, 40 MHA heads, d 128, bf16, lognormal lengths, pool 1.2x
+    (of the pages needed at ``block_size``)."""
     rng = np.random.default_rng(seed)
     ctx = lognormal_lengths(rng, num_seqs)
-    return _plain_decode("13b", seed + 1000, ctx, 40, 40, 128, "bf16", with_rows=with_rows)
+    return _plain_decode("13b", seed + 1000, ctx, 40, 40, 128, "bf16", with_rows=with_rows, block_size=block_size)
 
 
 def gqa(seed: int = 3, num_seqs: int = 256, lo: int = 128, hi: int = 4096,
@@ -164,7 +165,8 @@ def gqa(seed: int = 3, num_seqs: int = 256, lo: int = 128, hi: int = 4096,
 
 def parallel_sampling(seed: int = 4, groups: int = 32, samples=8, prompt=1000,
                       tail_lo: int = 1, tail_hi: int = 512, hq: int = 40, d: int = 128,
-                      with_rows: bool = True, hkv: Optional[int] = None) -> Workload:
+                      with_rows: bool = True, hkv: Optional[int] = None,
+                      block_size: int = BLOCK_SIZE) -> Workload:
     """Workload 4: groups x samples forks of one prompt each; tails U[1, 512].
 
     Script per group: create the prompt sequence (it is sample 0), append the
@@ -181,7 +183,8 @@ def parallel_sampling(seed: int = 4, groups: int = 32, samples=8, prompt=1000,
     tails = [rng.integers(tail_lo, tail_hi + 1, size=n).astype(np.int32) for n in n_samples]
     # pool sizing (an upper bound on the blocks in use, times 1.2): the prompt's
     # pages once per group, plus per sample one page of headroom and the tail's pages
-    need = sum(_blocks_for(p) for p in prompts) + sum(_blocks_for(int(t)) + 1 for ts in tails for t in ts)
+    need = sum(_blocks_for(p, block_size) for p in prompts) + \
+        sum(_blocks_for(int(t), block_size) + 1 for ts in tails for t in ts)
     nb = int(math.ceil(1.2 * need))
     perm = rng.permutation(nb).astype(np.int32)
     ops: List[Op] = []
@@ -208,7 +211,7 @@ def parallel_sampling(seed: int = 4, groups: int = 32, samples=8, prompt=1000,
     else:
         k_rows = v_rows = np.empty((0, hkv, d), dtype=np.uint16)
     w = Workload("fork", "bf16", hq, hkv, d, nb, perm, ops, k_rows, v_rows, decode_seqs, q,
-                 np.float32(1.0 / math.sqrt(d)))
+                 np.float32(1.0 / math.sqrt(d)), block_size=block_size)
     w.tails = np.array(tails) if len(set(n_samples)) == 1 else tails  # type: ignore[attr-defined]
     w.prompt = prompt  # type: ignore[attr-defined]
     w.group_start = np.concatenate([[0], np.cumsum(n_samples)]).astype(np.int32)  # type: ignore[attr-defined]
@@ -251,12 +254,12 @@ def long_mix(seed: int = 5, n_decode: int = 16, decode_ctx: int = 32768, n_chunk
 
 
 def random_small(seed: int, num_seqs: int, max_ctx: int, hq: int, hkv: int, d: int,
-                 dtype: str, pool_factor: float = 1.5, min_ctx: int = 1) -> Workload:
+                 dtype: str, pool_factor: float = 1.5, min_ctx: int = 1, block_size: int = BLOCK_SIZE) -> Workload:
     """A small ragged decode batch for parity tests (lengths uniform in [min_ctx, max_ctx])."""
     rng = np.random.default_rng(seed)
     ctx = rng.integers(min_ctx, max_ctx + 1, size=num_seqs).astype(np.int32)
     return _plain_decode(f"small{seed}", seed + 7919, ctx, hq, hkv, d, dtype,
-                         pool_factor=pool_factor)
+                         pool_factor=pool_factor, block_size=block_size)
 
 
 def random_prefill(seed: int, ctxs, n_queries, hq: int, hkv: int, d: int, pool_factor: float = 1.3) -> Workload:

@@ -26,9 +26,10 @@ class GpuReplay:
     def __init__(self, w, dev="cuda", pool_fill=None):
         self.w = w
         self.dev = dev
-        self.alloc = PK.BlockAllocator(w.num_blocks, P, w.initial_free_order)
+        self.bs = w.block_size
+        self.alloc = PK.BlockAllocator(w.num_blocks, self.bs, w.initial_free_order)
         tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-        shape = (w.num_blocks, w.num_kv_heads, P, w.head_dim)
+        shape = (w.num_blocks, w.num_kv_heads, self.bs, w.head_dim)
         if pool_fill is None:
             self.k_pool = torch.zeros(shape, dtype=tdt, device=dev)
         else:
@@ -66,7 +67,7 @@ class GpuReplay:
 
     def tables(self, seqs, max_blocks=None):
         lens = [self.alloc.seq_block_table(s)[1] for s in seqs]
-        mb = max_blocks or max(1, max(-(-n // P) for n in lens))
+        mb = max_blocks or max(1, max(-(-n // self.bs) for n in lens))
         t, l = self.alloc.block_tables(seqs, mb)
         return t, l
 

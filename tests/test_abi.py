@@ -41,7 +41,7 @@ def _lib(P):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(head_dim=96), 3), (dict(block_size=32), 3), (dict(num_kv_heads=0), 1),
+    (dict(head_dim=96), 3), (dict(block_size=24), 3), (dict(block_size=64), 3), (dict(num_kv_heads=0), 1),
     (dict(dtype=7), 1), (dict(num_tokens=-1), 1), (dict(num_blocks=0), 1),
     (dict(k=None), 1),
 ])
@@ -81,7 +81,7 @@ def test_swap_blocks_rejects_bad_arguments_before_touching_memory(P):
     assert L.pkv_swap_blocks(17, 32, 8, 48, 64, 8, 80, 1, 2, 64, 16, 1, None) == P.PKV_ERR_INVALID_ARG
     assert "aligned" in L.pkv_last_error().decode()
     assert L.pkv_swap_blocks(16, 32, 8, 48, 64, 8, 80, 1, 2, 96, 16, 1, None) == P.PKV_ERR_UNSUPPORTED
-    assert L.pkv_swap_blocks(16, 32, 8, 48, 64, 8, 80, 1, 2, 64, 8, 1, None) == P.PKV_ERR_UNSUPPORTED
+    assert L.pkv_swap_blocks(16, 32, 8, 48, 64, 8, 80, 1, 2, 64, 24, 1, None) == P.PKV_ERR_UNSUPPORTED
     assert L.pkv_swap_blocks(None, None, 8, None, None, 8, None, 0, 2, 64, 16, 1, None) == P.PKV_OK
 
 
@@ -148,13 +148,14 @@ def test_workspace_and_plan_sizes(P):
 
 def test_plan_rejects_bad_arguments(P):
     L = _lib(P)
-    #                 plan  bytes ctx_lens S  Hq Hkv MB maxctx dtype
-    assert L.pkv_decode_plan(None, 0, None, 0, 4, 4, 4, 64, 1, None) == P.PKV_OK
-    assert L.pkv_decode_plan(256, 16, 512, 3, 4, 4, 4, 64, 1, None) == P.PKV_ERR_INVALID_ARG   # buffer too small
-    assert L.pkv_decode_plan(None, 4096, 512, 3, 4, 4, 4, 64, 1, None) == P.PKV_ERR_INVALID_ARG
-    assert L.pkv_decode_plan(264, 4096, 512, 3, 4, 4, 4, 64, 1, None) == P.PKV_ERR_INVALID_ARG  # misaligned
-    assert L.pkv_decode_plan(256, 4096, 512, 3, 6, 4, 4, 64, 1, None) == P.PKV_ERR_INVALID_ARG  # Hq % Hkv
-    assert L.pkv_decode_plan(256, 4096, 512, 3, 4, 4, 4, 64, 9, None) == P.PKV_ERR_INVALID_ARG  # dtype
+    #                 plan  bytes ctx_lens S  Hq Hkv MB bs maxctx dtype
+    assert L.pkv_decode_plan(None, 0, None, 0, 4, 4, 4, 16, 64, 1, None) == P.PKV_OK
+    assert L.pkv_decode_plan(256, 16, 512, 3, 4, 4, 4, 16, 64, 1, None) == P.PKV_ERR_INVALID_ARG   # buffer too small
+    assert L.pkv_decode_plan(None, 4096, 512, 3, 4, 4, 4, 16, 64, 1, None) == P.PKV_ERR_INVALID_ARG
+    assert L.pkv_decode_plan(264, 4096, 512, 3, 4, 4, 4, 16, 64, 1, None) == P.PKV_ERR_INVALID_ARG  # misaligned
+    assert L.pkv_decode_plan(256, 4096, 512, 3, 6, 4, 4, 16, 64, 1, None) == P.PKV_ERR_INVALID_ARG  # Hq % Hkv
+    assert L.pkv_decode_plan(256, 4096, 512, 3, 4, 4, 4, 16, 64, 9, None) == P.PKV_ERR_INVALID_ARG  # dtype
+    assert L.pkv_decode_plan(256, 4096, 512, 3, 4, 4, 4, 24, 64, 1, None) == P.PKV_ERR_UNSUPPORTED  # block size
 
 
 def test_allocator_errors_are_status_codes(P):

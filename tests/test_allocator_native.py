@@ -26,13 +26,13 @@ def _same_state(a, m, live):
         assert a.block_refcount(b) == m.refcount(b)
 
 
-@settings(max_examples=200, deadline=None)
+@settings(max_examples=300, deadline=None)
 @given(st.integers(1, 40), st.lists(st.tuples(st.integers(0, 4), st.integers(0, 50), st.integers(0, 70)),
-                                    min_size=1, max_size=80))
-def test_random_operations_match_the_model(PK, nb, ops):
+                                    min_size=1, max_size=80), st.sampled_from([8, 16, 32]))
+def test_random_operations_match_the_model(PK, nb, ops, bs):
     order = list(np.random.default_rng(nb).permutation(nb))
-    a = PK.BlockAllocator(nb, P, order)
-    m = O.BlockAllocatorModel(nb, P, order)
+    a = PK.BlockAllocator(nb, bs, order)
+    m = O.BlockAllocatorModel(nb, bs, order)
     live = []
     for kind, pick, n in ops:
         if kind == 0 or not live:

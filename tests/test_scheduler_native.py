@@ -17,10 +17,10 @@ def PK():
     return PK
 
 
-def lockstep(PK, nb, order, max_seqs, tokens, policy, host, requests):
-    na = PK.BlockAllocator(nb, 16, order)
+def lockstep(PK, nb, order, max_seqs, tokens, policy, host, requests, bs=16):
+    na = PK.BlockAllocator(nb, bs, order)
     ns = PK.Scheduler(na, max_seqs, tokens, policy, host)
-    oa = O.BlockAllocatorModel(nb, 16, order)
+    oa = O.BlockAllocatorModel(nb, bs, order)
     os_ = SC.SchedulerModel(oa, max_seqs, tokens, policy, host)
     for p, o in requests:
         assert ns.add_request(p, o) == os_.add_request(p, o)
@@ -62,17 +62,18 @@ def test_slot_simulation_of_the_page(PK):
 def test_random_workloads_under_memory_pressure_match_the_model(PK, seed):
     rnd = random.Random(seed)
     nb = rnd.randint(6, 48)
+    bs = rnd.choice([8, 16, 16, 32])
     order = rnd.sample(range(nb), nb)
     tokens = rnd.randint(24, 160)
     reqs = []
     for _ in range(rnd.randint(1, 16)):
         while True:
             p, o = rnd.randint(1, min(tokens, 70)), rnd.randint(1, 90)
-            if -(-(p + o) // 16) <= nb:
+            if -(-(p + o) // bs) <= nb:
                 break
         reqs.append((p, o))
     lockstep(PK, nb, order, rnd.randint(1, 9), tokens, rnd.choice([PK.PKV_SCHED_CONTINUOUS, PK.PKV_SCHED_STATIC]),
-             rnd.choice([4 * nb, 8 * nb]), reqs)
+             rnd.choice([4 * nb, 8 * nb]), reqs, bs)
 
 
 def test_rejections_and_exhausted_host_space(PK):

@@ -68,11 +68,12 @@ def parse():
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time for the oracle sample")
-    ap.add_argument("--workload", default="13b", choices=["13b", "gqa", "fork", "long", "swap", "serve"],
+    ap.add_argument("--workload", default="13b", choices=["13b", "gqa", "fork", "long", "swap", "serve", "blocksize"],
                     help="13b: the headline decode step (default).  gqa / fork / long: kernel measurements on the "
                          "grouped-query, parallel-sampling and long-context + chunked-prefill batches.  swap: "
                          "block copies between HBM and pinned host memory.  serve: the continuous-batching loop "
-                         "(continuous vs static policy) over a request stream")
+                         "(continuous vs static policy) over a request stream.  blocksize: the 13B-shaped decode "
+                         "with 8-, 16- and 32-token blocks")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run pkv_copy_blocks over 4096 whole blocks (a plain copy of known size, "
                          "used to scale the FETCH_SIZE / WRITE_SIZE counters)")
@@ -421,6 +422,64 @@ def serve_bench(args):
                                                       results["static"]["tokens_per_s"], 3)}), flush=True)
 
 
+def blocksize_bench(args):
+    """The 13B-shaped decode batch (64 seqs, 40 MHA heads x 128, bf16, lognormal
+    contexts) with 8-, 16- and 32-token blocks: per block size the block-table
+    entries, the slots reserved but unused in each sequence's last block (the
+    tail waste of [CB] "PagedAttention: Memoria virtual para la KV cache"), and
+    the decode kernel's time and K/V bandwidth over 8 layer pools (each 1.2x the
+    blocks needed at that size, shuffled)."""
+    import torch
+    import paged_kv_cache_171_amd as PK
+    import pkv_workloads as W
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    L, H, D = 8, 40, 128
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    reps = max(args.steps, 3)
+    rows = []
+    for bs in (8, 16, 32):
+        w = W.shaped_13b(seed=args.seed, with_rows=False, block_size=bs)
+        alloc = PK.BlockAllocator(w.num_blocks, bs, w.initial_free_order)
+        for op in w.ops:
+            if op[0] == "create":
+                alloc.seq_create()
+            elif op[0] == "append":
+                alloc.seq_append_slots(op[1], op[2])
+        seqs = w.decode_seqs
+        lens = np.array([alloc.seq_block_table(s)[1] for s in seqs], dtype=np.int32)
+        MB = int(-(-lens.max() // bs))
+        tables, _ = alloc.block_tables(seqs, MB)
+        pools = [(torch.randn(w.num_blocks, H, bs, D, generator=gen, device=dev).to(torch.bfloat16),
+                  torch.randn(w.num_blocks, H, bs, D, generator=gen, device=dev).to(torch.bfloat16)) for _ in range(L)]
+        q = torch.randn(len(seqs), H, D, generator=gen, device=dev).to(torch.bfloat16)
+        out = torch.empty(len(seqs), H, D, dtype=torch.float32, device=dev)
+        td, ld = torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev)
+        mcl = int(lens.max())
+        ws = PK.workspace_for(len(seqs), H, D, mcl, device=dev)
+        plan = PK.plan_for(ld, H, H, MB, mcl, PK.PKV_BF16, block_size=bs)
+
+        def decode_all():
+            for kp, vp in pools:
+                PK.pkv_attention_decode(out, q, kp, vp, td, ld, mcl, 1.0 / math.sqrt(D), workspace=ws, plan=plan)
+        decode_all()
+        torch.cuda.synchronize()
+        dec_us = _timed(decode_all, reps, stream) / L
+        blocks = int(sum(-(-int(c) // bs) for c in lens))
+        kv = int(lens.sum()) * 2 * H * D * 2
+        rows.append({"block_size": bs, "pool_blocks": w.num_blocks, "table_entries": blocks,
+                     "table_bytes_padded": len(seqs) * MB * 4,
+                     "tail_waste_frac": round(1 - int(lens.sum()) / (blocks * bs), 4),
+                     "decode_us_per_layer": round(dec_us, 2), "decode_kv_gbps": round(kv / dec_us / 1e3, 1),
+                     "decode_hbm_peak_frac": round(kv / dec_us / 1e3 / HBM_PEAK_GBPS, 4)})
+        del pools
+        torch.cuda.empty_cache()
+    print(json.dumps({"workload": "blocksize", "layers": L, "num_seqs": 64, "heads": H, "head_dim": D,
+                      "kernel": "decode_valu_kernel<bf16,128,BS> + merge", "sweep": rows}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -435,6 +494,9 @@ def main():
         return
     if args.workload == "serve":
         serve_bench(args)
+        return
+    if args.workload == "blocksize":
+        blocksize_bench(args)
         return
     if args.workload != "13b":
         secondary(args)

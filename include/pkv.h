@@ -258,7 +258,9 @@ pkv_status pkv_attention_decode_shared(float* out, const void* q, const void* k_
  * [0, num_query_tokens] or is longer than max_query_len is skipped (its rows
  * are not written); one whose context is shorter than n_s, longer than
  * max_context_len or max_blocks_per_seq*block_size, or whose table names a
- * block outside [0, num_blocks), gets NaN rows.  No workspace.
+ * block outside [0, num_blocks), gets NaN rows.  scale must be positive
+ * (PKV_ERR_INVALID_ARG otherwise: the kernel takes row maxima of unscaled
+ * scores).  No workspace.
  * ------------------------------------------------------------------------ */
 pkv_status pkv_attention_prefill_chunk(float* out, const void* q, const int32_t* query_start_loc,
                                        int32_t num_query_tokens, int32_t max_query_len, const void* k_cache,

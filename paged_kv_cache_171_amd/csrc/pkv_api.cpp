@@ -420,7 +420,8 @@ pkv_status pkv_attention_prefill_chunk(float* out, const void* q, const int32_t*
                      fn, num_heads, num_kv_heads);
   if (num_blocks <= 0) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: num_blocks must be > 0", fn);
   if (max_blocks_per_seq <= 0) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: max_blocks_per_seq must be > 0", fn);
-  if (!std::isfinite(scale)) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: scale must be positive and finite", fn);
   if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0) return PKV_OK;
   if (!out || !q || !query_start_loc || !k_cache || !v_cache || !block_tables || !context_lens)
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: NULL pointer", fn);

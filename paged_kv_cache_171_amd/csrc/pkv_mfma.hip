@@ -496,14 +496,39 @@ __device__ __forceinline__ int kswz(int r) { return r % (D * 2 / 16); }
 constexpr int kPrefillWaves = 8;                     // waves per prefill workgroup
 constexpr int kPrefillThreads = 64 * kPrefillWaves;
 
+// Max over the four 16-lane rows of a wave (lanes n, n+16, n+32, n+48 hold the
+// same MFMA column): swap odd rows with even ones, then halves, taking the max.
+__device__ __forceinline__ float max_over_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Direct global->LDS copy of 16 bytes per lane from a wave-uniform base plus a
+// per-lane 32-bit offset (the scalar-base form of the instruction); lane l's
+// bytes land at LDS address lds + 16 l.
+__device__ __forceinline__ void copy16_to_lds_at(const char* base, uint32_t voff, const void* lds) {
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const char*)(lds)));
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(m0)
+               : "memory", "m0");
+}
+
+// A row's running maximum is raised only when a score exceeds it by more than
+// this (log2 units): until then probabilities stay below 2^8, exact enough in
+// fp32 and in the bf16 pair, and the accumulator rescale is skipped.
+constexpr float kRescaleLog2 = 8.f;
+
 template <int D>
-__global__ __launch_bounds__(kPrefillThreads) void prefill_chunk_mfma_kernel(pkv_prefill_args a) {
+__global__ __launch_bounds__(kPrefillThreads, 4) void prefill_chunk_mfma_kernel(pkv_prefill_args a) {
   constexpr int KC = D / 32;
   constexpr int DC = D / 16;
   constexpr int RB = D * 2;
   constexpr int kTiles = kPrefillRowsPerWg / 16 / kPrefillWaves;   // 16-row tiles per wave
   constexpr int kStages = 4;                       // LDS ring depth (pairs)
   constexpr int kTileBytes = kBlock * RB;          // one block's K (or V) rows of one head
+  constexpr int kTileKiB = kTileBytes / 1024;
   constexpr int kStageBytes = 4 * kTileBytes;      // K0 K1 V0 V1
   constexpr int kCopies = kStageBytes / (16 * kPrefillThreads);   // 16-byte copies per thread per stage
   static_assert(kStageBytes % (16 * kPrefillThreads) == 0 && kTiles >= 1, "prefill shape");
@@ -546,39 +571,55 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_chunk_mfma_kernel(pkv
   const int32_t nblk = (ctx + kBlock - 1) / kBlock;
   bool bad = false;
 
-  // Copies of pair pp into stage pp % kStages.  Copy i of wave w fills KiB
-  // kPrefillWaves*i + w of the stage: tile t = that KiB / (tile KiB), rows of
-  // the tile in lane order; each lane fetches the global 16 bytes its (row,
-  // slot) holds.
-  auto issue = [&](int32_t pp) {
-    char* stage = ring[pp % kStages];
+  // Copy i of wave w fills KiB kPrefillWaves*i + w of a stage: tile t = that KiB
+  // / (tile KiB) (0: K0, 1: K1, 2: V0, 3: V1), rows of the tile in lane order;
+  // LDS row r holds slot k of the tile row at the swizzled source slot.  The
+  // per-lane source offsets are fixed: row r's, and row 0's for keys past the
+  // context (finite data that gets probability 0).
+  uint32_t cp_off[kCopies], cp_off0[kCopies];
+  int32_t cp_row[kCopies];
+#pragma unroll
+  for (int i = 0; i < kCopies; ++i) {
+    const int kib = kPrefillWaves * i + wave;
+    const int t = kib / kTileKiB;
+    const int off = (kib % kTileKiB) * 1024 + 16 * lane;
+    const int r = off / RB, k = (off % RB) / 16;
+    const int slot = t < 2 ? (k ^ kswz<D>(r)) : (k ^ vswz<D>(r));
+    cp_row[i] = r;
+    cp_off[i] = static_cast<uint32_t>(r * RB + 16 * slot);
+    cp_off0[i] = static_cast<uint32_t>(16 * slot);
+  }
+  auto issue = [&](int32_t pp, char* stage) {
     int32_t id0 = scalar_load_i32(table + 2 * pp);
     int32_t id1 = 2 * pp + 1 < nblk ? scalar_load_i32(table + 2 * pp + 1) : id0;
     if (static_cast<uint32_t>(id0) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; id0 = 0; }
     if (static_cast<uint32_t>(id1) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; id1 = 0; }
+    const bool tail = (2 * pp + 2) * kBlock > ctx;     // some keys of the pair lie past the context
 #pragma unroll
     for (int i = 0; i < kCopies; ++i) {
       const int kib = kPrefillWaves * i + wave;
-      const int t = kib / (kTileBytes / 1024);                 // 0: K0, 1: K1, 2: V0, 3: V1
-      const int off = (kib % (kTileBytes / 1024)) * 1024 + 16 * lane;
-      const int r = off / RB, k = (off % RB) / 16;
+      const int t = kib / kTileKiB;
       const int b = t & 1;
       const int32_t j = 2 * pp + b;
-      // a key past the context, or a missing second block, takes key 0 of the
-      // pair's first block: finite data that gets probability 0
-      const int row = j * kBlock + r < ctx ? r : 0;
       const int32_t id = (b == 0 || j >= nblk) ? id0 : id1;
-      const int slot = t < 2 ? (k ^ kswz<D>(r)) : (k ^ vswz<D>(r));
-      const char* src = (t < 2 ? kc : vc) + id * block_bytes + row * RB + 16 * slot;
-      copy16_to_lds(src, stage + kib * 1024);
+      const char* base = (t < 2 ? kc : vc) + id * block_bytes;
+      uint32_t voff = cp_off[i];
+      if (tail && j * kBlock + cp_row[i] >= ctx) voff = cp_off0[i];
+      copy16_to_lds_at(base, voff, stage + kib * 1024);
     }
   };
-  for (int32_t pp = 0; pp < kStages - 1 && pp < npairs; ++pp) issue(pp);
+#pragma unroll
+  for (int pp = 0; pp < kStages - 1; ++pp)
+    if (pp < npairs) issue(pp, ring[pp]);
 
-  // this lane's rows (one per tile) and their key limits; invalid rows: limit 0, q = 0
+  // this lane's rows (one per tile) and their key limits; invalid rows: limit 0,
+  // q = 0 (their results are never written).  Keys below nomask_lim are visible
+  // to every valid row of the tile.
   bf16x8 qb[kTiles][KC];
   int32_t lim[kTiles];
   int32_t tile_lim[kTiles];      // keys any row of the tile needs (uniform)
+  int32_t nomask_lim[kTiles];
+  int32_t wave_lim = 0;
 #pragma unroll
   for (int tt = 0; tt < kTiles; ++tt) {
     const int32_t rbase = r0 + (wave * kTiles + tt) * 16;
@@ -588,6 +629,8 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_chunk_mfma_kernel(pkv
     lim[tt] = valid ? first_pos + i + 1 : 0;
     const int32_t rlast = min(r_end, rbase + 16) - 1;
     tile_lim[tt] = rlast >= rbase ? first_pos + rlast / G + 1 : 0;
+    nomask_lim[tt] = first_pos + rbase / G + 1;
+    wave_lim = max(wave_lim, tile_lim[tt]);
     const char* qrow = reinterpret_cast<const char*>(a.q) +
                        ((static_cast<int64_t>(q0) + i) * Hq + kvh * G + (valid ? r % G : 0)) * D * 2;
 #pragma unroll
@@ -614,92 +657,107 @@ __global__ __launch_bounds__(kPrefillThreads) void prefill_chunk_mfma_kernel(pkv
   const int tr_row = 4 * g + (n >> 2);
   const int tr_sw = vswz<D>(tr_row);
   const int tr_k0 = (n & 3) >> 1;
+  const float c2 = a.scale_log2;                 // > 0
 
-  for (int32_t pp = 0; pp < npairs; ++pp) {
-    // this pair's copies have landed once at most the later issued pairs'
-    // copies are outstanding (copies complete in issue order)
-    const int32_t ahead = min(kStages - 2, npairs - 1 - pp);
-    static_assert(kStages == 4 && (kCopies == 1 || kCopies == 2 || kCopies == 4), "wait counts");
-    if (ahead >= 2) {
-      if constexpr (kCopies == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      else if constexpr (kCopies == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-    } else if (ahead == 1) {
-      if constexpr (kCopies == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      else if constexpr (kCopies == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-
-    const char* stage = ring[pp % kStages];
+  // One pair of blocks (32 keys) from its stage.
+  auto pair = [&](int32_t pp, const char* stage) {
     const int32_t key0 = pp * 2 * kBlock;
-    if (key0 < tile_lim[0] || key0 < tile_lim[1]) {
-    bf16x8 ka[2][KC];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int c = 0; c < KC; ++c)
-        ka[b][c] = as_bf16x8(*reinterpret_cast<const u32x4*>(stage + b * kTileBytes + k_row +
-                                                              16 * ((4 * c + g) ^ k_sw)));
-    bf16x8 va[DC];
-    const char* trb = stage + 2 * kTileBytes + tr_row * RB + 8 * (n & 1);
-#pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      const int slot = 16 * ((2 * c + tr_k0) ^ tr_sw);
-      va[c] = join(lds_read_tr(trb + slot), lds_read_tr(trb + kTileBytes + slot));
-    }
+    if (key0 >= wave_lim) return;
 #pragma unroll
     for (int tt = 0; tt < kTiles; ++tt) {
       if (key0 >= tile_lim[tt]) continue;
-      float sc[2][4];
+      // S^T = K Q^T for the two blocks, K straight from LDS in the A layout
+      f32x4 acc[2];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        bf16x8 ka[KC];
 #pragma unroll
-        for (int c = 0; c < KC; ++c) acc = mfma(ka[b][c], qb[tt][c], acc);
+        for (int c = 0; c < KC; ++c)
+          ka[c] = as_bf16x8(*reinterpret_cast<const u32x4*>(stage + b * kTileBytes + k_row +
+                                                             16 * ((4 * c + g) ^ k_sw)));
+        acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int32_t t = key0 + b * kBlock + 4 * g + jj;
-          sc[b][jj] = t < lim[tt] ? acc[jj] * a.scale_log2 : -INFINITY;
-        }
+        for (int c = 0; c < KC; ++c) acc[b] = mfma(ka[c], qb[tt][c], acc[b]);
       }
-      float mx = sc[0][0];
+      float sc[8];
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) mx = fmaxf(mx, sc[b][jj]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[tt], mx);
-      const float alpha = fast_exp2(m[tt] - mnew);
-      m[tt] = mnew;
+        for (int jj = 0; jj < 4; ++jj) sc[4 * b + jj] = acc[b][jj];
+      if (key0 + 2 * kBlock > nomask_lim[tt]) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            if (key0 + b * kBlock + 4 * g + jj >= lim[tt]) sc[4 * b + jj] = -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+      mx = max_over_rows(mx) * c2;
+      // raise the row maximum (and rescale) only when a score passes it by
+      // more than kRescaleLog2; the branch is uniform over the wave
+      const bool up = mx > m[tt] + kRescaleLog2;
+      if (__builtin_amdgcn_ballot_w64(up)) {
+        const float mnew = up ? mx : m[tt];
+        const float alpha = fast_exp2(m[tt] - mnew);
+        m[tt] = mnew;
+        lsum[tt] *= alpha;
+#pragma unroll
+        for (int c = 0; c < DC; ++c) o[tt][c] *= alpha;
+      }
+      // V^T for the 32 keys by transposed reads, issued before the exponentials
+      bf16x8 va[DC];
+      const char* trb = stage + 2 * kTileBytes + tr_row * RB + 8 * (n & 1);
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        const int slot = 16 * ((2 * c + tr_k0) ^ tr_sw);
+        va[c] = join(lds_read_tr(trb + slot), lds_read_tr(trb + kTileBytes + slot));
+      }
       bf16x8 ph, pl;
       float ps = 0.f;
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const float pr = fast_exp2(sc[b][jj] - mnew);
-          ps += pr;
-          const __bf16 hi = static_cast<__bf16>(pr);
-          ph[4 * b + jj] = hi;
-          pl[4 * b + jj] = static_cast<__bf16>(pr - static_cast<float>(hi));
-        }
-      lsum[tt] = lsum[tt] * alpha + ps;
+      for (int k = 0; k < 8; ++k) {
+        const float pr = fast_exp2(fmaf(sc[k], c2, -m[tt]));
+        ps += pr;
+        const __bf16 hi = static_cast<__bf16>(pr);
+        ph[k] = hi;
+        pl[k] = static_cast<__bf16>(pr - static_cast<float>(hi));
+      }
+      lsum[tt] += ps;
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
-        f32x4 acc = o[tt][c] * alpha;
-        acc = mfma(va[c], ph, acc);
-        o[tt][c] = mfma(va[c], pl, acc);
+        f32x4 t = mfma(va[c], ph, o[tt][c]);
+        o[tt][c] = mfma(va[c], pl, t);
       }
     }
+  };
+
+  static_assert(kStages == 4 && (kCopies == 1 || kCopies == 2 || kCopies == 4), "wait counts");
+  for (int32_t p0 = 0; p0 < npairs; p0 += kStages) {
+#pragma unroll
+    for (int st = 0; st < kStages; ++st) {
+      const int32_t pp = p0 + st;
+      if (pp >= npairs) break;
+      // this pair's copies have landed once at most the later issued pairs'
+      // copies are outstanding (copies complete in issue order)
+      const int32_t ahead = min(kStages - 2, npairs - 1 - pp);
+      if (ahead >= 2) {
+        if constexpr (kCopies == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else if constexpr (kCopies == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+      } else if (ahead == 1) {
+        if constexpr (kCopies == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else if constexpr (kCopies == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      pair(pp, ring[st]);
+      // every wave passed the barrier after it finished the pair before this
+      // one, so that pair's stage takes pair pp + kStages - 1
+      if (pp + kStages - 1 < npairs) issue(pp + kStages - 1, ring[(st + kStages - 1) % kStages]);
     }
-    // every wave passed the barrier after it finished the pair before this
-    // one, so that pair's stage takes pair pp + kStages - 1
-    if (pp + kStages - 1 < npairs) issue(pp + kStages - 1);
   }
 
   // a bad block id anywhere in the workgroup's range poisons its rows

@@ -176,7 +176,7 @@ def test_allocator_errors_are_status_codes(P):
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=0), 3), (dict(head_dim=96), 3), (dict(block_size=8), 3), (dict(num_heads=6, num_kv_heads=4), 1),
     (dict(q=None), 1), (dict(max_query_len=-1), 1), (dict(out=17), 1), (dict(num_blocks=0), 1),
-    (dict(scale=float("inf")), 1),
+    (dict(scale=float("inf")), 1), (dict(scale=-0.125), 1), (dict(scale=0.0), 1),
 ])
 def test_prefill_rejects_bad_arguments(P, kw, code):
     args = dict(out=16, q=32, qsl=48, tq=8, mql=4, k_cache=64, v_cache=80, tables=96, mb=4, lens=112, num_seqs=2,

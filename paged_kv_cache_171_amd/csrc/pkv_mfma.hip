@@ -52,6 +52,8 @@ using pkvd::plan_matches;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kWaves = 4;
@@ -712,17 +714,19 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void prefill_chunk_mfma_kernel(
         const int slot = 16 * ((2 * c + tr_k0) ^ tr_sw);
         va[c] = join(lds_read_tr(trb + slot), lds_read_tr(trb + kTileBytes + slot));
       }
-      bf16x8 ph, pl;
+      u32x4 phw, plw;
       float ps = 0.f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float pr = fast_exp2(fmaf(sc[k], c2, -m[tt]));
-        ps += pr;
-        const __bf16 hi = static_cast<__bf16>(pr);
-        ph[k] = hi;
-        pl[k] = static_cast<__bf16>(pr - static_cast<float>(hi));
+      for (int k = 0; k < 4; ++k) {
+        const f32x2 pr = {fast_exp2(fmaf(sc[2 * k], c2, -m[tt])), fast_exp2(fmaf(sc[2 * k + 1], c2, -m[tt]))};
+        ps += pr[0] + pr[1];
+        const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+        const f32x2 lo = {pr[0] - __uint_as_float(h << 16), pr[1] - __uint_as_float(h & 0xFFFF0000u)};
+        phw[k] = h;
+        plw[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
       }
       lsum[tt] += ps;
+      const bf16x8 ph = as_bf16x8(phw), pl = as_bf16x8(plw);
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
         f32x4 t = mfma(va[c], ph, o[tt][c]);

@@ -427,6 +427,59 @@ pkv_status pkv_scheduler_request(const pkv_scheduler* s, int64_t request_id, int
 pkv_status pkv_scheduler_stats(const pkv_scheduler* s, int64_t* steps, int64_t* busy_slot_steps,
                                int32_t* num_waiting, int32_t* num_running, int32_t* num_swapped);
 
+/* The scheduler's allocator and its limits (for callers that size buffers). */
+pkv_allocator* pkv_scheduler_allocator(const pkv_scheduler* s);
+int32_t pkv_scheduler_max_num_seqs(const pkv_scheduler* s);
+int32_t pkv_scheduler_max_num_batched_tokens(const pkv_scheduler* s);
+
+/* ------------------------------------------------------------------------
+ * Step executor: the continuous-batching loop of [UL] "Cómo funciona la
+ * planificación a nivel de iteración" run natively, one call per step and one
+ * per layer, so that the host builds a step's indices once and the GPU does
+ * everything else.
+ *
+ * pkv_batch_schedule runs pkv_scheduler_step, gathers the step's indices --
+ * slot_mapping, the prefill query ranges, block tables and lengths, the decode
+ * block tables and lengths, the swap-out and swap-in pairs -- into the
+ * caller's pinned host staging buffer (two halves used in turn: a half is
+ * rewritten only after the copy that read it two steps ago has finished, which
+ * the call waits for on the host), copies them to the caller's device buffer
+ * with one asynchronous copy on `stream`, and builds the decode plan there.
+ * Then, for each layer, pkv_batch_layer enqueues on `stream`: the swap-out
+ * copies (that layer's device pools -> its host pools), the swap-in copies,
+ * pkv_append of the step's K/V rows, causal prefill of the admitted prompts
+ * and decode of the running requests.  Per layer the caller passes
+ *   q: [T][num_heads][head_dim], k and v: [T][num_kv_heads][head_dim] (pool
+ *   dtype), out: float32 [T][num_heads][head_dim], with T =
+ *   num_prefill_tokens + num_decode tokens in slot_mapping order (the prefill
+ *   tokens of the admitted requests in admission order, then one decode token
+ *   per decoding request); out gets prefill rows then decode rows.
+ * k_host / v_host may be NULL when no swap copies are due.
+ *
+ * Limits: bf16 pools with 16-token blocks (the prefill kernel's), head_dim 64
+ * or 128, query heads a multiple of KV heads; max_blocks_per_seq bounds every
+ * request's table (PKV_ERR_INVALID_ARG from pkv_batch_schedule otherwise,
+ * after the scheduler step).  Buffers: host_staging of
+ * pkv_batch_host_bytes(...) bytes of pinned host memory and device_buffer of
+ * pkv_batch_device_bytes(...) bytes, both caller-owned and kept until
+ * pkv_batch_destroy; num_blocks is the device pool size (it bounds the swap
+ * pairs of a step).  Not thread-safe; one stream per batch.
+ * ------------------------------------------------------------------------ */
+typedef struct pkv_batch pkv_batch;
+
+size_t pkv_batch_host_bytes(int32_t max_num_seqs, int32_t max_num_batched_tokens, int32_t max_blocks_per_seq,
+                            int32_t num_blocks);
+size_t pkv_batch_device_bytes(int32_t max_num_seqs, int32_t max_num_batched_tokens, int32_t max_blocks_per_seq,
+                              int32_t num_blocks, int32_t num_heads, int32_t head_dim);
+pkv_status pkv_batch_create(pkv_scheduler* sched, int32_t max_blocks_per_seq, int32_t num_blocks,
+                            int32_t num_host_blocks, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                            pkv_dtype dtype, void* host_staging, size_t host_bytes, void* device_buffer,
+                            size_t device_bytes, pkv_batch** out);
+void pkv_batch_destroy(pkv_batch* b);
+pkv_status pkv_batch_schedule(pkv_batch* b, void* stream, pkv_step_info* info);
+pkv_status pkv_batch_layer(pkv_batch* b, void* k_cache, void* v_cache, void* k_host, void* v_host, const void* q,
+                           const void* k, const void* v, float* out, float scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -65,6 +65,16 @@ _SIGS = {
     "pkv_scheduler_step_output": (_c_i32, [_c_p] + [_c_p] * 9),
     "pkv_scheduler_request": (_c_i32, [_c_p, _c_i64, _P_I32, _P_I64, _P_I32, _P_I32]),
     "pkv_scheduler_stats": (_c_i32, [_c_p, _P_I64, _P_I64, _P_I32, _P_I32, _P_I32]),
+    "pkv_scheduler_allocator": (_c_p, [_c_p]),
+    "pkv_scheduler_max_num_seqs": (_c_i32, [_c_p]),
+    "pkv_scheduler_max_num_batched_tokens": (_c_i32, [_c_p]),
+    "pkv_batch_host_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32]),
+    "pkv_batch_device_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "pkv_batch_create": (_c_i32, [_c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_p, _c_sz, _c_p,
+                                  _c_sz, ctypes.POINTER(_c_p)]),
+    "pkv_batch_destroy": (None, [_c_p]),
+    "pkv_batch_schedule": (_c_i32, [_c_p, _c_p, _c_p]),
+    "pkv_batch_layer": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_f32, _c_p]),
     "pkv_seq_create": (_c_i32, [_c_p, _P_I64]),
     "pkv_seq_append_slots": (_c_i32, [_c_p, _c_i64, _c_i32, _c_p, _c_p, _P_I32]),
     "pkv_seq_append_slots_batch": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_p, _c_p, _P_I32]),
@@ -413,3 +423,54 @@ class Scheduler:
         _check(_lib.pkv_scheduler_stats(self._h, ctypes.byref(a), ctypes.byref(b), ctypes.byref(w), ctypes.byref(r),
                                         ctypes.byref(sw)))
         return a.value, b.value, w.value, r.value, sw.value
+
+
+class Batch:
+    """Native step executor (pkv_batch_*) over a Scheduler: schedule() runs one
+    scheduler step and moves its indices to the GPU; layer() enqueues one
+    layer's swaps, cache write, prefill and decode.  The staging (pinned) and
+    device buffers are allocated here with torch and kept alive with the
+    object."""
+
+    def __init__(self, sched: "Scheduler", max_blocks_per_seq: int, num_blocks: int, num_host_blocks: int,
+                 num_heads: int, num_kv_heads: int, head_dim: int, dtype: int = PKV_BF16, device="cuda"):
+        S = _lib.pkv_scheduler_max_num_seqs(sched._h)
+        T = _lib.pkv_scheduler_max_num_batched_tokens(sched._h)
+        hb = _lib.pkv_batch_host_bytes(S, T, max_blocks_per_seq, num_blocks)
+        db = _lib.pkv_batch_device_bytes(S, T, max_blocks_per_seq, num_blocks, num_heads, head_dim)
+        self.staging = torch.empty(hb + 256, dtype=torch.uint8).pin_memory()
+        self.device_buffer = torch.empty(db + 256, dtype=torch.uint8, device=device)
+        hp = (self.staging.data_ptr() + 255) & ~255
+        dp = (self.device_buffer.data_ptr() + 255) & ~255
+        h = _c_p()
+        _check(_lib.pkv_batch_create(sched._h, max_blocks_per_seq, num_blocks, num_host_blocks, num_heads,
+                                     num_kv_heads, head_dim, dtype, hp, hb, dp, db, ctypes.byref(h)))
+        self._h = h
+        self.sched = sched
+        self.info = None
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            _lib.pkv_batch_destroy(h)
+            self._h = None
+
+    def schedule(self, stream=None) -> _StepInfo:
+        info = _StepInfo()
+        _check(_lib.pkv_batch_schedule(self._h, _stream(stream), ctypes.byref(info)))
+        self.info = info
+        return info
+
+    def step_output(self) -> "Step":
+        """The last step's lists, as Scheduler.step() returns them."""
+        return Step(self.info, self.sched._h)
+
+    def layer(self, k_cache: torch.Tensor, v_cache: torch.Tensor, k_host: Optional[torch.Tensor],
+              v_host: Optional[torch.Tensor], q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+              scale: float, stream=None) -> None:
+        _check(_lib.pkv_batch_layer(self._h, k_cache.data_ptr(), v_cache.data_ptr(),
+                                    k_host.data_ptr() if k_host is not None else None,
+                                    v_host.data_ptr() if v_host is not None else None,
+                                    q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), float(scale),
+                                    _stream(stream)))
+

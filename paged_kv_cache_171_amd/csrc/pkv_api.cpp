@@ -35,28 +35,11 @@ pkv_status hip_status(const char* fn, int err) {
                    hipGetErrorString(static_cast<hipError_t>(err)));
 }
 
-size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
-
-// Partial-result slots per (sequence, head): enough for the smallest partition.
-int32_t num_partitions(int32_t max_context_len) {
-  const int32_t np = (max_context_len + kMinPartTokens - 1) / kMinPartTokens;
-  return np < 1 ? 1 : np;
-}
-
-// Header and (s, p) per unit: at most num_partitions per sequence, or one
-// rowless unit.
-constexpr size_t kPlanHdrWords = 8;
-size_t plan_bytes(int32_t num_seqs, int32_t max_context_len) {
-  return (kPlanHdrWords + 2 * static_cast<size_t>(num_seqs) * (num_partitions(max_context_len) + 1)) *
-         sizeof(int32_t);
-}
-
-size_t partial_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len) {
-  const int32_t np = num_partitions(max_context_len);
-  if (np <= 1) return 0;
-  const size_t units = static_cast<size_t>(num_seqs) * num_heads * np;
-  return align256(units * 2 * sizeof(float)) + units * head_dim * sizeof(float);
-}
+using pkv_ws::align256;
+using pkv_ws::num_partitions;
+using pkv_ws::kPlanHdrWords;
+using pkv_ws::plan_bytes;
+using pkv_ws::partial_bytes;
 
 // Shared-prefix decode workspace: the shared plan, seq_start, the plan of the
 // sequences' own units, then partials with prefix slots ahead of the

@@ -38,6 +38,29 @@ inline int32_t pkv_part_tokens(int dtype, int32_t num_heads, int32_t num_kv_head
   return pkv_uses_mfma(dtype, num_heads, num_kv_heads, block_size) ? kMaxPartTokens : kMinPartTokens;
 }
 
+// Sizes of the decode plan and of the split-context partials.
+namespace pkv_ws {
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+// Partial-result slots per (sequence, head): enough for the smallest partition.
+inline int32_t num_partitions(int32_t max_context_len) {
+  const int32_t np = (max_context_len + kMinPartTokens - 1) / kMinPartTokens;
+  return np < 1 ? 1 : np;
+}
+// Header and (s, p) per unit: at most num_partitions per sequence, or one
+// rowless unit.
+constexpr size_t kPlanHdrWords = 8;
+inline size_t plan_bytes(int32_t num_seqs, int32_t max_context_len) {
+  return (kPlanHdrWords + 2 * static_cast<size_t>(num_seqs) * (num_partitions(max_context_len) + 1)) *
+         sizeof(int32_t);
+}
+inline size_t partial_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len) {
+  const int32_t np = num_partitions(max_context_len);
+  if (np <= 1) return 0;
+  const size_t units = static_cast<size_t>(num_seqs) * num_heads * np;
+  return align256(units * 2 * sizeof(float)) + units * head_dim * sizeof(float);
+}
+}  // namespace pkv_ws
+
 struct pkv_decode_args {
   float* out;
   const void* q;

@@ -307,6 +307,10 @@ pkv_status pkv_scheduler_request(const pkv_scheduler* s, int64_t request_id, int
   return PKV_OK;
 }
 
+pkv_allocator* pkv_scheduler_allocator(const pkv_scheduler* s) { return s ? s->alloc : nullptr; }
+int32_t pkv_scheduler_max_num_seqs(const pkv_scheduler* s) { return s ? s->max_num_seqs : 0; }
+int32_t pkv_scheduler_max_num_batched_tokens(const pkv_scheduler* s) { return s ? s->max_tokens : 0; }
+
 pkv_status pkv_scheduler_stats(const pkv_scheduler* s, int64_t* steps, int64_t* busy_slot_steps,
                                int32_t* num_waiting, int32_t* num_running, int32_t* num_swapped) {
   if (!s) return pkv_fail(PKV_ERR_INVALID_ARG, "pkv_scheduler_stats: NULL scheduler");

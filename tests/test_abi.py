@@ -111,6 +111,31 @@ def test_shared_decode_rejects_bad_arguments_before_any_launch(P):
     assert L.pkv_attention_decode_shared_workspace_bytes(0, 4, 64, 64) == 0
 
 
+def test_batch_rejects_bad_arguments_before_any_device_call(P):
+    L = _lib(P)
+    a16 = P.BlockAllocator(20)
+    s16 = P.Scheduler(a16, 4, 64)
+    hb = L.pkv_batch_host_bytes(4, 64, 8, 20)
+    db = L.pkv_batch_device_bytes(4, 64, 8, 20, 8, 64)
+    assert hb > 0 and db > hb // 2
+    out = ctypes.c_void_p()
+    # (sched, MB, NB, NH, Hq, Hkv, d, dtype, host, hb, dev, db, out)
+    assert L.pkv_batch_create(None, 8, 20, 0, 8, 8, 64, 1, 256, hb, 512, db, ctypes.byref(out)) == P.PKV_ERR_INVALID_ARG
+    assert L.pkv_batch_create(s16._h, 8, 20, 0, 8, 8, 64, 0, 256, hb, 512, db, ctypes.byref(out)) == P.PKV_ERR_UNSUPPORTED
+    assert L.pkv_batch_create(s16._h, 8, 20, 0, 8, 8, 96, 1, 256, hb, 512, db, ctypes.byref(out)) == P.PKV_ERR_UNSUPPORTED
+    assert L.pkv_batch_create(s16._h, 8, 20, 0, 8, 3, 64, 1, 256, hb, 512, db, ctypes.byref(out)) == P.PKV_ERR_INVALID_ARG
+    assert L.pkv_batch_create(s16._h, 8, 21, 0, 8, 8, 64, 1, 256, hb, 512, db, ctypes.byref(out)) == P.PKV_ERR_INVALID_ARG
+    assert L.pkv_batch_create(s16._h, 8, 20, 0, 8, 8, 64, 1, 256, hb - 1, 512, db, ctypes.byref(out)) == P.PKV_ERR_INVALID_ARG
+    assert L.pkv_batch_create(s16._h, 8, 20, 0, 8, 8, 64, 1, 256, hb, 512, db - 1, ctypes.byref(out)) == P.PKV_ERR_INVALID_ARG
+    assert L.pkv_batch_create(s16._h, 8, 20, 0, 8, 8, 64, 1, 256, hb, 520, db, ctypes.byref(out)) == P.PKV_ERR_INVALID_ARG
+    a8 = P.BlockAllocator(20, 8)
+    s8 = P.Scheduler(a8, 4, 64)
+    assert L.pkv_batch_create(s8._h, 8, 20, 0, 8, 8, 64, 1, 256, hb, 512, db, ctypes.byref(out)) == P.PKV_ERR_UNSUPPORTED
+    assert L.pkv_batch_schedule(None, None, None) == P.PKV_ERR_INVALID_ARG
+    assert L.pkv_batch_layer(None, None, None, None, None, None, None, None, None, 1.0, None) == P.PKV_ERR_INVALID_ARG
+    assert L.pkv_scheduler_max_num_seqs(s16._h) == 4 and L.pkv_scheduler_max_num_batched_tokens(s16._h) == 64
+
+
 def _decode(P, **kw):
     a = dict(out=256, q=512, k=768, v=1024, tables=1280, mb=4, lens=1536, S=2, Hq=4, Hkv=2, d=64, bs=16,
              nb=8, maxctx=64, scale=0.125, dtype=1, ws=None, wsb=0)

@@ -128,3 +128,78 @@ def test_serving_loop_with_grouped_heads_and_long_prompts():
     steps, swaps, err = _serve(w, SC.CONTINUOUS)
     print(f"steps={steps} swaps={swaps} err={err:.2e}", flush=True)
     assert err <= TOL
+
+
+def _serve_native(w, policy):
+    """The same loop through the native step executor (pkv_batch_schedule once
+    per step, pkv_batch_layer for the one layer)."""
+    dev = "cuda"
+    alloc = PK.BlockAllocator(w.num_blocks, 16, w.initial_free_order)
+    sched = PK.Scheduler(alloc, w.max_num_seqs, w.max_num_batched_tokens, policy, w.num_host_blocks)
+    for p, o in zip(w.prompts, w.outputs):
+        sched.add_request(int(p), int(o))
+    mb = int(-(-int((w.prompts + w.outputs).max()) // 16))
+    batch = PK.Batch(sched, mb, w.num_blocks, w.num_host_blocks, w.num_heads, w.num_kv_heads, w.head_dim)
+    tdt = torch.bfloat16
+    shape = (w.num_blocks, w.num_kv_heads, 16, w.head_dim)
+    k_pool, v_pool = torch.zeros(shape, dtype=tdt, device=dev), torch.zeros(shape, dtype=tdt, device=dev)
+    hshape = (w.num_host_blocks,) + shape[1:]
+    k_host, v_host = torch.zeros(hshape, dtype=tdt).pin_memory(), torch.zeros(hshape, dtype=tdt).pin_memory()
+    k_rows, v_rows, q_rows = (rows_to_device(x, dev) for x in (w.k_rows, w.v_rows, w.q_rows))
+    m = SV.ServingModel(w, policy)
+    steps = swaps = 0
+    err = 0.0
+    while True:
+        x = m.step()
+        info = batch.schedule()
+        s = batch.step_output()
+        if s.empty:
+            assert not x.step.prefill and not x.step.decode
+            break
+        assert list(s.prefill) == x.step.prefill and list(s.decode) == x.step.decode
+        assert [tuple(p) for p in s.swap_out_pairs] == x.step.swap_out_pairs
+        assert [tuple(p) for p in s.swap_in_pairs] == x.step.swap_in_pairs
+        assert list(s.slot_mapping) == x.step.slots
+        plens = np.diff(s.prefill_query_start_loc)
+        labels = [(int(r), p) for r, n in zip(s.prefill, plens) for p in range(int(n))]
+        labels += [(int(r), sched.request(int(r))[3] - 1) for r in s.decode]
+        assert [p for _, p in labels[len(labels) - len(s.decode):]] == x.decode_positions
+        idx = torch.tensor([int(w.row_start[r]) + p for r, p in labels], dtype=torch.int64, device=dev)
+        q, k, v = (t.index_select(0, idx).contiguous() for t in (q_rows, k_rows, v_rows))
+        out = torch.full((len(labels), w.num_heads, w.head_dim), -5.0, dtype=torch.float32, device=dev)
+        batch.layer(k_pool, v_pool, k_host, v_host, q, k, v, out, float(w.scale))
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()
+        npre = int(info.num_prefill_tokens)
+        if npre:
+            err = max(err, float(np.abs(o[:npre] - x.prefill_out).max()))
+        if len(s.decode):
+            err = max(err, float(np.abs(o[npre:] - x.decode_out).max()))
+        if len(s.swap_out_pairs) or len(s.swap_in_pairs) or steps % 16 == 0:
+            assert np.array_equal(pool_to_host(k_pool), m.k_pool) and np.array_equal(pool_to_host(v_pool), m.v_pool)
+            assert np.array_equal(pool_to_host(k_host), m.k_host) and np.array_equal(pool_to_host(v_host), m.v_host)
+        steps += 1
+        swaps += len(s.swapped_out)
+    assert np.array_equal(pool_to_host(k_pool), m.k_pool) and np.array_equal(pool_to_host(v_pool), m.v_pool)
+    return steps, swaps, err
+
+
+@pytest.mark.parametrize("policy", [SC.CONTINUOUS, SC.STATIC])
+def test_native_step_executor_matches_the_oracle_loop(policy):
+    print(f"case: native serving policy={policy}", flush=True)
+    w = W.serving()
+    steps, swaps, err = _serve_native(w, policy)
+    print(f"steps={steps} swaps={swaps} err={err:.2e}", flush=True)
+    assert err <= TOL
+    if policy == SC.CONTINUOUS:
+        assert swaps > 0
+
+
+def test_native_step_executor_with_grouped_heads():
+    print("case: native serving gqa", flush=True)
+    w = W.serving(seed=9, num_requests=16, hq=16, hkv=2, d=128, prompt_median=150, output_median=40,
+                  max_prompt=400, max_output=120, num_blocks=60, max_num_seqs=6, max_num_batched_tokens=512,
+                  num_host_blocks=200)
+    steps, swaps, err = _serve_native(w, SC.CONTINUOUS)
+    assert err <= TOL
+

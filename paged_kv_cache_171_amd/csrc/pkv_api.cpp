@@ -378,8 +378,7 @@ pkv_status pkv_attention_decode_shared(float* out, const void* q, const void* k_
   if (!err)
     err = pkv_launch_plan(reinterpret_cast<int32_t*>(ws + l.plan), context_lens, num_seqs, max_blocks_per_seq,
                           block_size, max_context_len, a.part_tokens, stream, a.seq_start);
-  if (!err) err = pkv_launch_shared_prefix(a, stream);
-  if (!err) err = pkv_launch_decode(a, stream);
+  if (!err) err = pkv_launch_shared_fused(a, stream);
   return hip_status(fn, err);
 }
 

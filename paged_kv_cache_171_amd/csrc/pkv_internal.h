@@ -106,7 +106,10 @@ int pkv_launch_plan(int32_t* plan, const int32_t* context_lens, int32_t num_seqs
 constexpr int32_t kPrefixPartTokens = 1024;
 int pkv_launch_shared_plan(const pkv_decode_args& a, const int32_t* group_start, int32_t num_groups,
                            int32_t* seq_start, int32_t* shared_plan, void* stream);
-int pkv_launch_shared_prefix(const pkv_decode_args& a, void* stream);
+// The shared-prefix units and the sequences' own units in one launch, then the merge.
+int pkv_launch_shared_fused(const pkv_decode_args& a, void* stream);
+// The partition merge alone (pkv_kernels.hip).
+int pkv_launch_merge(const pkv_decode_args& a, void* stream);
 
 // Causal chunked-prefill attention (pkv_mfma.hip).
 struct pkv_prefill_args {

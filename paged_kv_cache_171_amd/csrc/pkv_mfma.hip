@@ -37,7 +37,7 @@
 // error of up to 2^-9 |v| on short contexts.  Masked keys are removed by select
 // (score -inf, V row 0), never by multiplying, so NaN in unused slots cannot
 // reach the output.
-#include "pkv_device.h"
+#include "pkv_decode_valu.h"
 
 namespace {
 
@@ -134,8 +134,8 @@ __device__ __forceinline__ int vswz(int r) {
   return 2 * ((r / kRowsPerLine) % (kSlots / 2));
 }
 
-template <int D, bool kShared>
-__global__ __launch_bounds__(256, 4) void decode_group_mfma_kernel(pkv_decode_args a) {
+template <int D>
+__device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a, uint32_t bid, bool shared_unit) {
   constexpr int KC = D / 32;            // 32-dim chunks of q.k
   constexpr int DC = D / 16;            // 16-dim chunks of the output
   constexpr int RB = D * 2;             // bytes per key row
@@ -156,14 +156,14 @@ __global__ __launch_bounds__(256, 4) void decode_group_mfma_kernel(pkv_decode_ar
   const int g = lane >> 4;
 
   const int32_t Hq = a.num_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
-  const int32_t u = static_cast<int32_t>(blockIdx.x / static_cast<uint32_t>(Hkv));
-  const int32_t kvh = static_cast<int32_t>(blockIdx.x - static_cast<uint32_t>(u) * Hkv);
+  const int32_t u = static_cast<int32_t>(bid / static_cast<uint32_t>(Hkv));
+  const int32_t kvh = static_cast<int32_t>(bid - static_cast<uint32_t>(u) * Hkv);
   // The unit: rows r < nrows are (sequence s0 + r / G, query head kvh*G + r % G);
   // it walks blocks blk_begin .. blk_end-1 of s0's table, keys below ctx valid,
   // and writes the output rows (direct) or partial slot `slot` of each row.
   int32_t s0, nrows, ctx, blk_begin, blk_end, slot;
   bool direct;
-  if constexpr (kShared) {
+  if (shared_unit) {
     // a group's shared leading blocks: the rows are the group's sequences
     const int32_t* sp = a.shared_plan;
     if (u >= sp[0]) return;
@@ -361,6 +361,28 @@ __global__ __launch_bounds__(256, 4) void decode_group_mfma_kernel(pkv_decode_ar
   (void)kSlots;
 }
 
+template <int D, bool kShared>
+__global__ __launch_bounds__(256, 4) void decode_group_mfma_kernel(pkv_decode_args a) {
+  decode_group_mfma_body<D>(a, blockIdx.x, kShared);
+}
+
+// Shared-prefix decode in one launch: the first shared_wgs workgroups take
+// the groups' shared-prefix units (matrix cores), the rest the sequences' own
+// units -- on the MFMA group kernel for grouped-query heads, else the VALU
+// kernel -- so the short per-sequence units fill the CUs the long shared units
+// leave free instead of waiting for them.
+template <int D, bool kGroupTail>
+__global__ __launch_bounds__(256, 4) void decode_shared_fused_kernel(pkv_decode_args a, uint32_t shared_wgs) {
+  if constexpr (kGroupTail) {
+    const bool shared_unit = blockIdx.x < shared_wgs;
+    decode_group_mfma_body<D>(a, shared_unit ? blockIdx.x : blockIdx.x - shared_wgs, shared_unit);
+  } else if (blockIdx.x < shared_wgs) {
+    decode_group_mfma_body<D>(a, blockIdx.x, true);
+  } else {
+    decode_valu_body<uint16_t, D, kBlock>(a, blockIdx.x - shared_wgs);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Shared-prefix plan.  [OS] "El regalo extra: compartir memoria" and [IPX] "Dos
 // respuestas a una entrada": the parallel samples of one prompt hold the same
@@ -425,8 +447,17 @@ __global__ __launch_bounds__(1024) void shared_plan_kernel(pkv_decode_args a, co
           const int32_t j = j0 + lane;
           bool eq = true;
           if (j < lim) {
+            // every member's entry is loaded before any is compared, four at a
+            // time, so the loads overlap instead of waiting on each other
             const int32_t ref = t0[j];
-            for (int32_t m = b + 1; m < e && eq; ++m) eq = a.block_tables[static_cast<int64_t>(m) * MB + j] == ref;
+            const int32_t* col = a.block_tables + j;
+            int32_t m = b + 1;
+            for (; m + 3 < e; m += 4) {
+              const int32_t x0 = col[static_cast<int64_t>(m) * MB], x1 = col[static_cast<int64_t>(m + 1) * MB];
+              const int32_t x2 = col[static_cast<int64_t>(m + 2) * MB], x3 = col[static_cast<int64_t>(m + 3) * MB];
+              eq = eq & (x0 == ref) & (x1 == ref) & (x2 == ref) & (x3 == ref);
+            }
+            for (; m < e; ++m) eq = eq & (col[static_cast<int64_t>(m) * MB] == ref);
           }
           const uint64_t differ = __ballot(!eq);
           if (differ) {
@@ -804,17 +835,25 @@ int pkv_launch_shared_plan(const pkv_decode_args& a, const int32_t* group_start,
   return hipGetLastError();
 }
 
-int pkv_launch_shared_prefix(const pkv_decode_args& a, void* stream) {
+int pkv_launch_shared_fused(const pkv_decode_args& a, void* stream) {
   // at most num_seqs sub-groups, each with ceil(max_context_len / partition) units
   const int64_t npp = (a.max_context_len + a.prefix_part_tokens - 1) / a.prefix_part_tokens;
-  const int64_t grid = static_cast<int64_t>(a.num_seqs) * (npp < 1 ? 1 : npp) * a.num_kv_heads;
+  const int64_t shared = static_cast<int64_t>(a.num_seqs) * (npp < 1 ? 1 : npp) * a.num_kv_heads;
+  const bool group_tail = pkv_uses_mfma(a.dtype, a.num_heads, a.num_kv_heads, a.block_size);
+  const int64_t np = (a.max_context_len + a.part_tokens - 1) / a.part_tokens;
+  const int64_t own = static_cast<int64_t>(a.num_seqs) * (np < 1 ? 1 : np) * (group_tail ? a.num_kv_heads : a.num_heads);
+  const dim3 grid(static_cast<uint32_t>(shared + own));
+  const uint32_t sw = static_cast<uint32_t>(shared);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (a.head_dim == 128) {
-    hipLaunchKernelGGL((decode_group_mfma_kernel<128, true>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st, a);
+    if (group_tail) hipLaunchKernelGGL((decode_shared_fused_kernel<128, true>), grid, dim3(256), 0, st, a, sw);
+    else hipLaunchKernelGGL((decode_shared_fused_kernel<128, false>), grid, dim3(256), 0, st, a, sw);
   } else {
-    hipLaunchKernelGGL((decode_group_mfma_kernel<64, true>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st, a);
+    if (group_tail) hipLaunchKernelGGL((decode_shared_fused_kernel<64, true>), grid, dim3(256), 0, st, a, sw);
+    else hipLaunchKernelGGL((decode_shared_fused_kernel<64, false>), grid, dim3(256), 0, st, a, sw);
   }
-  return hipGetLastError();
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  return pkv_launch_merge(a, stream);
 }
 
 int pkv_launch_prefill(const pkv_prefill_args& a, void* stream) {

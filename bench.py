@@ -37,11 +37,16 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 METRIC = "paged decode attention: KV GB/s and % of HBM peak; decode tokens/s per step"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_13b_counters.md")
-KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_171_amd", "csrc", "pkv_kernels.hip")
+# the sources the headline decode kernel is built from
+KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_cache_171_amd", "csrc", f)
+               for f in ("pkv_kernels.hip", "pkv_decode_valu.h", "pkv_device.h", "pkv_internal.h")]
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def stored_traffic(alg_bytes_per_launch: float):

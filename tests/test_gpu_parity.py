@@ -90,6 +90,48 @@ def test_13b_shaped_batch_full():
     assert err <= TOL["bf16"], err
 
 
+def test_13b_step_in_the_bench_launch_configuration():
+    """The full 13B-shaped batch driven the way bench.py times it: one new token
+    per sequence (batched slot reservation, pkv_append), one pkv_decode_plan for
+    the step, then pkv_attention_decode_planned on two layer pools that share
+    the tables (the second with K and V exchanged); every output row against the
+    oracle, and the pools bit-exact after the writes."""
+    w = W.shaped_13b()
+    print("case: 13b bench step", flush=True)
+    g, r = GpuReplay(w), _oracle(w)
+    seqs = list(w.decode_seqs)
+    slots, cow = g.alloc.seq_append_slots_batch(seqs, [1] * len(seqs))
+    oslots = []
+    for s_ in seqs:
+        sl, pairs = r.alloc.append_slots(s_, 1)
+        oslots += sl
+        assert not pairs
+    assert list(slots) == oslots and len(cow) == 0
+    rng = np.random.default_rng(2024)
+    kn = W.f32_to_bf16_bits(rng.standard_normal((len(seqs), 40, 128), dtype=np.float32))
+    vn = W.f32_to_bf16_bits(rng.standard_normal((len(seqs), 40, 128), dtype=np.float32))
+    PK.pkv_append(g.k_pool, g.v_pool, rows_to_device(kn, "cuda"), rows_to_device(vn, "cuda"),
+                  torch.from_numpy(np.asarray(slots, dtype=np.int64)).cuda())
+    O.write_cache(r.k_pool, r.v_pool, kn, vn, oslots)
+    tables, lens = g.tables(seqs)
+    td, ld = torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
+    mcl = int(lens.max())
+    plan = PK.plan_for(ld, 40, 40, tables.shape[1], mcl, PK.PKV_BF16)
+    ws = PK.workspace_for(len(seqs), 40, 128, mcl)
+    q = rows_to_device(w.q, "cuda")
+    otables = [r.alloc.block_table(s_) for s_ in seqs]
+    olens = [r.alloc.num_tokens(s_) for s_ in seqs]
+    assert list(lens) == olens
+    for kp, vp, okp, ovp in ((g.k_pool, g.v_pool, r.k_pool, r.v_pool), (g.v_pool, g.k_pool, r.v_pool, r.k_pool)):
+        out = torch.full((len(seqs), 40, 128), -4.0, dtype=torch.float32, device="cuda")
+        PK.pkv_attention_decode(out, q, kp, vp, td, ld, mcl, float(w.scale), workspace=ws, plan=plan)
+        torch.cuda.synchronize()
+        ref = O.decode_attention(w.q, okp, ovp, otables, olens, w.scale)
+        err = float(np.abs(out.cpu().numpy() - ref).max())
+        assert err <= TOL["bf16"], err
+    assert np.array_equal(pool_to_host(g.k_pool), r.k_pool) and np.array_equal(pool_to_host(g.v_pool), r.v_pool)
+
+
 def test_gqa_batch_full_sampled():
     w = W.gqa()
     print("case: gqa S=256 H=64/8", flush=True)

@@ -207,6 +207,33 @@ pkv_status pkv_attention_decode_planned(float* out, const void* q, const void* k
                                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Decode with the step's cache write.  [OS] "Cómo funciona por dentro": each
+ * decode step writes the new token's key and value into the sequence's last
+ * block, then attends over the whole context.  This call does both in the
+ * decode launch: the result and the pools afterwards are those of
+ *
+ *   pkv_append(k_cache, v_cache, k, v, slot_mapping, num_seqs, ...);
+ *   pkv_attention_decode(_planned)(out, q, k_cache, v_cache, ...);
+ *
+ * where k, v: device [num_seqs][num_kv_heads][head_dim] (pool dtype) hold each
+ * sequence's new token and slot_mapping: device int64 [num_seqs] its slot,
+ * which must be the slot of token context_lens[s]-1 (context_lens count the
+ * new token).  The decode kernels store the row there and take that token from
+ * k / v directly, saving the separate cache-write launch.  slot -1: the
+ * sequence has no new token this step (nothing written; attention as usual);
+ * any other slot than token context_lens[s]-1's: NaN rows, nothing written.
+ * plan: from pkv_decode_plan, or NULL to build it in the workspace (then the
+ * workspace must hold pkv_attention_workspace_bytes(...)).
+ * ------------------------------------------------------------------------ */
+pkv_status pkv_attention_decode_append(float* out, const void* q, const void* k, const void* v,
+                                       const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                       int32_t max_context_len, float scale, pkv_dtype dtype, const void* plan,
+                                       size_t plan_bytes, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Decode with shared prefixes.  [OS] "El regalo extra: compartir memoria" and
  * [IPX] "Dos respuestas a una entrada": the parallel samples of one prompt
  * share the prompt's physical blocks.  The result is that of

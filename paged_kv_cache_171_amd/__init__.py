@@ -7,7 +7,7 @@ library with ``python -m paged_kv_cache_171_amd.build``.
 from .binding import (  # noqa: F401
     BlockAllocator, Scheduler, Batch, PkvError, LIB_PATH, EXPORTED,
     pkv_version, pkv_append, pkv_copy_blocks, pkv_swap_blocks, pkv_attention_workspace_bytes,
-    pkv_attention_decode_shared, pkv_attention_decode_shared_workspace_bytes,
+    pkv_attention_decode_shared, pkv_attention_decode_shared_workspace_bytes, pkv_attention_decode_append,
     pkv_attention_decode, pkv_attention_prefill_chunk, pkv_decode_plan_bytes, pkv_decode_plan, plan_for,
     workspace_for,
     PKV_OK, PKV_ERR_INVALID_ARG, PKV_ERR_OUT_OF_BLOCKS, PKV_ERR_UNSUPPORTED, PKV_ERR_HIP,

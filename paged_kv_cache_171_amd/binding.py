@@ -46,6 +46,9 @@ _SIGS = {
     "pkv_attention_decode_planned": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32,
                                               _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_p, _c_sz, _c_p,
                                               _c_sz, _c_p]),
+    "pkv_attention_decode_append": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_i32,
+                                             _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_p,
+                                             _c_sz, _c_p, _c_sz, _c_p]),
     "pkv_attention_decode_shared_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32]),
     "pkv_attention_decode_shared": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_p, _c_i32,
                                              _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_p,
@@ -226,6 +229,30 @@ def pkv_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tens
         _dev(plan)
         _check(_lib.pkv_attention_decode_planned(*args, plan.data_ptr(), plan.numel(), workspace.data_ptr(),
                                                  workspace.numel(), _stream(stream)))
+
+
+def pkv_attention_decode_append(out: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                slot_mapping: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                                scale: float, workspace: Optional[torch.Tensor] = None, stream=None,
+                                plan: Optional[torch.Tensor] = None) -> None:
+    """pkv_append of each sequence's new token (k, v [S, Hkv, d]; slot_mapping int64 [S], the slot of
+    token context_lens[s]-1, or -1) fused into decode attention."""
+    _dev(out, q, k, v, slot_mapping, k_cache, v_cache, block_tables, context_lens)
+    assert slot_mapping.dtype == torch.int64 and out.dtype == torch.float32
+    S, hq, d = q.shape
+    nb, hkv, bs, _ = k_cache.shape
+    assert k.shape == v.shape == (S, hkv, d) and slot_mapping.numel() == S
+    assert k.dtype == v.dtype == k_cache.dtype == v_cache.dtype == q.dtype
+    if workspace is None:
+        workspace = workspace_for(S, hq, d, max_context_len, device=q.device)
+    _check(_lib.pkv_attention_decode_append(out.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                            slot_mapping.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                            block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
+                                            S, hq, hkv, d, bs, nb, int(max_context_len), float(scale),
+                                            _dtype_code(k_cache), plan.data_ptr() if plan is not None else None,
+                                            plan.numel() if plan is not None else 0, workspace.data_ptr(),
+                                            workspace.numel(), _stream(stream)))
 
 
 def pkv_attention_decode_shared_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int,

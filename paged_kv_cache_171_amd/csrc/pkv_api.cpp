@@ -206,7 +206,8 @@ static pkv_status decode_impl(const char* fn, float* out, const void* q, const v
                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                               int32_t max_context_len, float scale, pkv_dtype dtype, const void* plan,
                               size_t plan_bytes_given, void* workspace, size_t workspace_bytes,
-                              bool build_plan, void* stream) {
+                              bool build_plan, void* stream, const void* new_k = nullptr,
+                              const void* new_v = nullptr, const int64_t* new_slots = nullptr) {
   pkv_status st = check_common(fn, num_kv_heads, head_dim, block_size, dtype);
   if (st != PKV_OK) return st;
   if (num_seqs < 0) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: num_seqs < 0", fn);
@@ -222,6 +223,8 @@ static pkv_status decode_impl(const char* fn, float* out, const void* q, const v
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: NULL pointer", fn);
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: out, q and cache pointers must be 16-byte aligned", fn);
+  if (new_slots && (!new_k || !new_v || !aligned16(new_k) || !aligned16(new_v)))
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: k and v must be 16-byte aligned device pointers", fn);
   const int32_t np = num_partitions(max_context_len);
   const int64_t grid = static_cast<int64_t>(num_seqs) * num_heads * np;
   if (grid > 0x7FFFFFFF || static_cast<int64_t>(num_seqs) * (np + 1) > 0x3FFFFFFF)
@@ -271,7 +274,25 @@ static pkv_status decode_impl(const char* fn, float* out, const void* q, const v
   a.part_tokens = part_tokens;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.dtype = dtype;
+  a.new_k = new_k;
+  a.new_v = new_v;
+  a.new_slots = new_slots;
   return hip_status(fn, pkv_launch_decode(a, stream));
+}
+
+pkv_status pkv_attention_decode_append(float* out, const void* q, const void* k, const void* v,
+                                       const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                       int32_t max_context_len, float scale, pkv_dtype dtype, const void* plan,
+                                       size_t plan_bytes_given, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  const char* fn = "pkv_attention_decode_append";
+  if (num_seqs > 0 && !slot_mapping) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: slot_mapping is NULL", fn);
+  return decode_impl(fn, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                     num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_context_len, scale, dtype, plan,
+                     plan_bytes_given, workspace, workspace_bytes, plan == nullptr, stream, k, v, slot_mapping);
 }
 
 pkv_status pkv_attention_decode(float* out, const void* q, const void* k_cache, const void* v_cache,

@@ -147,11 +147,46 @@ __device__ __forceinline__ void decode_valu_body(const pkv_decode_args& a, uint3
   const int32_t blk_end = min(nblk, blk_begin + part / kBlock);
 
   constexpr int64_t kTileBytes = static_cast<int64_t>(kBlock) * D * sizeof(T);
+  constexpr int kRowBytes = D * sizeof(T);
+  const int32_t G = Hq / a.num_kv_heads;
+  const int32_t kvh = h / G;
   const int64_t block_bytes = static_cast<int64_t>(a.num_kv_heads) * kTileBytes;
-  const int64_t head_off = static_cast<int64_t>(h / (Hq / a.num_kv_heads)) * kTileBytes;
+  const int64_t head_off = static_cast<int64_t>(kvh) * kTileBytes;
   const char* __restrict__ kc = reinterpret_cast<const char*>(a.k_cache);
   const char* __restrict__ vc = reinterpret_cast<const char*>(a.v_cache);
   const int32_t* __restrict__ table = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq;
+  bool bad = false;
+
+  // The step's new token (decode with the cache write): the unit holding the
+  // last block checks that the new slot is token ctx-1's, stores the row there
+  // (one workgroup per KV head) and takes token ctx-1 from the new row.
+  int32_t new_blk = -1, new_row = -1;
+  const char* nk = nullptr;
+  const char* nv = nullptr;
+  if (a.new_slots && blk_end == nblk) {
+    const int64_t slot = a.new_slots[s];
+    if (slot >= 0) {
+      const int32_t lb = table[nblk - 1];
+      const int32_t lr = (ctx - 1) % kBlock;
+      if (static_cast<uint32_t>(lb) >= static_cast<uint32_t>(a.num_blocks) ||
+          slot != static_cast<int64_t>(lb) * kBlock + lr) {
+        bad = true;
+      } else {
+        new_blk = nblk - 1;
+        new_row = lr;
+        const int64_t src = (static_cast<int64_t>(s) * a.num_kv_heads + kvh) * kRowBytes;
+        nk = reinterpret_cast<const char*>(a.new_k) + src;
+        nv = reinterpret_cast<const char*>(a.new_v) + src;
+        if (h % G == 0 && threadIdx.x < 2 * (kRowBytes / 16)) {
+          const int c = threadIdx.x % (kRowBytes / 16);
+          const bool is_v = threadIdx.x >= kRowBytes / 16;
+          const int64_t dst = lb * block_bytes + head_off + static_cast<int64_t>(lr) * kRowBytes + 16 * c;
+          *reinterpret_cast<u32x4*>(const_cast<char*>(is_v ? vc : kc) + dst) =
+              *reinterpret_cast<const u32x4*>((is_v ? nv : nk) + 16 * c);
+        }
+      }
+    }
+  }
 
   // q slice of this lane, pre-scaled into base-2 units
   float qv[EPL];
@@ -166,7 +201,6 @@ __device__ __forceinline__ void decode_valu_body(const pkv_decode_args& a, uint3
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  bool bad = false;
 
   // The block ids of the next iteration are fetched (scalar loads) while the
   // current iteration's tiles are in flight.
@@ -192,12 +226,28 @@ __device__ __forceinline__ void decode_valu_body(const pkv_decode_args& a, uint3
         // rows past the context (the tail of a sequence's last block) are not
         // loaded: those lanes read nothing and hold 0
         const int32_t valid = ctx - j * kBlock;
+        if (j != new_blk) {
 #pragma unroll
-        for (int i = 0; i < NLD; ++i)
-          kt[bi][i] = i * TPL + row < valid ? __builtin_nontemporal_load(kp + i * 64 + lane) : u32x4{0, 0, 0, 0};
+          for (int i = 0; i < NLD; ++i)
+            kt[bi][i] = i * TPL + row < valid ? __builtin_nontemporal_load(kp + i * 64 + lane) : u32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int i = 0; i < NLD; ++i)
-          vt[bi][i] = i * TPL + row < valid ? __builtin_nontemporal_load(vp + i * 64 + lane) : u32x4{0, 0, 0, 0};
+          for (int i = 0; i < NLD; ++i)
+            vt[bi][i] = i * TPL + row < valid ? __builtin_nontemporal_load(vp + i * 64 + lane) : u32x4{0, 0, 0, 0};
+        } else {
+          // the block of the new token: its row comes from the new K/V
+#pragma unroll
+          for (int i = 0; i < NLD; ++i) {
+            const int r = i * TPL + row;
+            kt[bi][i] = r < new_row ? __builtin_nontemporal_load(kp + i * 64 + lane)
+                        : r == new_row ? *reinterpret_cast<const u32x4*>(nk + 16 * col) : u32x4{0, 0, 0, 0};
+          }
+#pragma unroll
+          for (int i = 0; i < NLD; ++i) {
+            const int r = i * TPL + row;
+            vt[bi][i] = r < new_row ? __builtin_nontemporal_load(vp + i * 64 + lane)
+                        : r == new_row ? *reinterpret_cast<const u32x4*>(nv + 16 * col) : u32x4{0, 0, 0, 0};
+          }
+        }
       }
     }
 #pragma unroll

@@ -91,6 +91,12 @@ struct pkv_decode_args {
   const int32_t* seq_start;
   const int32_t* shared_plan;  // header + (first sequence, members, partition, prefix tokens) per unit
   int32_t prefix_part_tokens;
+  // Decode with the step's cache write (null otherwise): sequence s's token
+  // ctx-1 is new_k/new_v row s ([S][Hkv][d]); the decode kernels store it at
+  // new_slots[s] and use it from there on the fly (-1: no new token).
+  const void* new_k;
+  const void* new_v;
+  const int64_t* new_slots;
 };
 // Decode: the main kernel (VALU, or MFMA for bf16 query-head groups of 2..16
 // heads, pkv_mfma.hip), then the partition merge when a context can be split.

@@ -247,6 +247,38 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
   float m = kNegBig, lsum = 0.f;
   bool bad = false;
 
+  // The step's new token (decode with the cache write): the unit holding the
+  // sequence's last block checks that the new slot is token ctx-1's, stores
+  // the row there and takes token ctx-1 (and the unused rows after it) from
+  // the new row.
+  int32_t new_blk = -1, new_row = kBlock;
+  const char* nk = nullptr;
+  const char* nv = nullptr;
+  if (a.new_slots && !shared_unit && blk_end * kBlock >= ctx) {
+    const int64_t slot = a.new_slots[s0];
+    if (slot >= 0) {
+      const int32_t lb = table[blk_end - 1];
+      const int32_t lr = (ctx - 1) % kBlock;
+      if (static_cast<uint32_t>(lb) >= static_cast<uint32_t>(a.num_blocks) ||
+          slot != static_cast<int64_t>(lb) * kBlock + lr) {
+        bad = true;
+      } else {
+        new_blk = blk_end - 1;
+        new_row = lr;
+        const int64_t src = (static_cast<int64_t>(s0) * Hkv + kvh) * RB;
+        nk = reinterpret_cast<const char*>(a.new_k) + src;
+        nv = reinterpret_cast<const char*>(a.new_v) + src;
+        if (threadIdx.x < 2 * (RB / 16)) {
+          const int c = threadIdx.x % (RB / 16);
+          const bool is_v = threadIdx.x >= RB / 16;
+          const int64_t dst = lb * block_bytes + static_cast<int64_t>(lr) * RB + 16 * c;
+          *reinterpret_cast<u32x4*>(const_cast<char*>(is_v ? vc : kc) + dst) =
+              *reinterpret_cast<const u32x4*>((is_v ? nv : nk) + 16 * c);
+        }
+      }
+    }
+  }
+
   // The wave's block ids (at most kMaxPartTokens/16/4 = 64 of them), one per lane,
   // fetched once before the loop; each block takes its id with a lane read.
   const int32_t nit = (blk_end - blk_begin - wave + kWaves - 1) / kWaves;
@@ -262,15 +294,30 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
     const char* kp = kc + id * block_bytes;
     const char* vp = vc + id * block_bytes;
     const int32_t valid_rows = min(kBlock, ctx - j * kBlock);
-    // keys past the context are not loaded (their scores are masked)
+    if (j != new_blk) {
+      // keys past the context are not loaded (their scores are masked)
 #pragma unroll
-    for (int c = 0; c < KC; ++c)
-      kt[c] = n < valid_rows ? load16_nt(kp + n * RB + 64 * c + 16 * g) : u32x4{0, 0, 0, 0};
+      for (int c = 0; c < KC; ++c)
+        kt[c] = n < valid_rows ? load16_nt(kp + n * RB + 64 * c + 16 * g) : u32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int src = (1024 * i + 16 * lane) / RB < valid_rows ? dma_off[i] : dma_off[i] % RB;
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vp + src),
-                                       (__attribute__((address_space(3))) void*)(tile + 1024 * i), 16, 0, 0);
+      for (int i = 0; i < NLD; ++i) {
+        const int src = (1024 * i + 16 * lane) / RB < valid_rows ? dma_off[i] : dma_off[i] % RB;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vp + src),
+                                         (__attribute__((address_space(3))) void*)(tile + 1024 * i), 16, 0, 0);
+      }
+    } else {
+      // the block of the new token: its row, and the unused rows after it,
+      // come from the new K/V (finite data; the unused rows are masked)
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        kt[c] = n < new_row ? load16_nt(kp + n * RB + 64 * c + 16 * g)
+                : n == new_row ? *reinterpret_cast<const u32x4*>(nk + 64 * c + 16 * g) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const char* src = (1024 * i + 16 * lane) / RB < new_row ? vp + dma_off[i] : nv + dma_off[i] % RB;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                         (__attribute__((address_space(3))) void*)(tile + 1024 * i), 16, 0, 0);
+      }
     }
   };
   // Online-softmax update of block `it` from its K registers and V tile.

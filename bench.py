@@ -2,9 +2,11 @@
 
 A step is one pass of the hot path over the batch: the host allocator reserves
 one new slot per sequence (and names any copy-on-write pairs), the slot map,
-block tables and context lengths go to the device, and then for each of the 40
-layers the new token's K/V is written into that layer's paged pool
-(pkv_append) and paged decode attention runs over it (pkv_attention_decode).
+block tables and context lengths go to the device, the decode plan is built
+once, and then for each of the 40 layers one call writes the new token's K/V
+into that layer's paged pool and runs paged decode attention over it
+(pkv_attention_decode_append: the cache write happens inside the decode
+launch).
 
 Workload: 64 sequences, 40 MHA heads, head_dim 128, bf16, context lengths
 lognormal (median 200, sigma 1.0) clipped to [1, 2048], 16-token blocks shuffled
@@ -567,16 +569,14 @@ def main():
         for l in range(L):
             if n_pairs:   # (a2) copy-on-write (none arise in this workload)
                 B._check(lib.pkv_copy_blocks(kp[l][0], kp[l][1], pairs_d.data_ptr(), n_pairs, NB, H, D, P, BF16, sp))
-            # (a3) write this step's K/V
-            B._check(lib.pkv_append(kp[l][0], kp[l][1], kvn[l][0], kvn[l][1], slots_d.data_ptr(), S, NB, H, D, P,
-                                    BF16, sp))
-            # (a4, a5) paged decode attention and the partition merge
+            # (a3, a4, a5) this step's K/V written at their slots inside the paged
+            # decode attention launch, then the partition merge
             if events is not None:
                 events[l][0].record(stream)
-            B._check(lib.pkv_attention_decode_planned(op[l], qp[l], kp[l][0], kp[l][1], tables_d.data_ptr(), MB,
-                                                      lens_d.data_ptr(), S, H, H, D, P, NB, max_ctx, scale, BF16,
-                                                      plan.data_ptr(), plan.numel(), ws.data_ptr(), ws.numel(),
-                                                      sp))
+            B._check(lib.pkv_attention_decode_append(op[l], qp[l], kvn[l][0], kvn[l][1], slots_d.data_ptr(),
+                                                     kp[l][0], kp[l][1], tables_d.data_ptr(), MB, lens_d.data_ptr(),
+                                                     S, H, H, D, P, NB, max_ctx, scale, BF16, plan.data_ptr(),
+                                                     plan.numel(), ws.data_ptr(), ws.numel(), sp))
             if events is not None:
                 events[l][1].record(stream)
         return ln
@@ -596,10 +596,13 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
-    # algorithmic bytes of one decode launch: K and V of every live token once,
-    # plus q, the fp32 output, the table entries in use and the lengths
+    # algorithmic bytes of one decode launch: K and V of every live token once
+    # (the new token's from the step's rows), the new K/V rows written to the
+    # pool, plus q, the fp32 output, the table entries in use, the lengths and
+    # the slots
     kv_bytes = [int(ln.sum()) * 2 * H * D * 2 for ln in step_lens]
-    other = [S * H * D * 2 + S * H * D * 4 + int(sum(-(-int(c) // P) for c in ln)) * 4 + S * 4 for ln in step_lens]
+    other = [S * 2 * H * D * 2 + S * H * D * 2 + S * H * D * 4 + int(sum(-(-int(c) // P) for c in ln)) * 4 + S * 4 +
+             S * 8 for ln in step_lens]
     dec_ms = [sum(ev[k][l][0].elapsed_time(ev[k][l][1]) for l in range(L)) for k in range(args.steps)]
     launches = args.steps * L
     alg_bytes_total = sum((kv + o) * L for kv, o in zip(kv_bytes, other))
@@ -634,7 +637,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": "decode_valu_kernel<bf16,128> + merge_partitions_kernel<128>",
+                     "kernel": "decode_valu_kernel<bf16,128,16> (with the cache write) + merge_partitions_kernel<128>",
                      "avg_launch_us": round(avg_launch_us, 2),
                      "alg_bytes_per_launch": round(alg_bytes_total / launches)},
     }

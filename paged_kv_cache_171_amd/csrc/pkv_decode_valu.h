@@ -157,36 +157,15 @@ __device__ __forceinline__ void decode_valu_body(const pkv_decode_args& a, uint3
   const int32_t* __restrict__ table = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq;
   bool bad = false;
 
-  // The step's new token (decode with the cache write): the unit holding the
-  // last block checks that the new slot is token ctx-1's, stores the row there
-  // (one workgroup per KV head) and takes token ctx-1 from the new row.
-  int32_t new_blk = -1, new_row = -1;
-  const char* nk = nullptr;
-  const char* nv = nullptr;
-  if (a.new_slots && blk_end == nblk) {
-    const int64_t slot = a.new_slots[s];
-    if (slot >= 0) {
-      const int32_t lb = table[nblk - 1];
-      const int32_t lr = (ctx - 1) % kBlock;
-      if (static_cast<uint32_t>(lb) >= static_cast<uint32_t>(a.num_blocks) ||
-          slot != static_cast<int64_t>(lb) * kBlock + lr) {
-        bad = true;
-      } else {
-        new_blk = nblk - 1;
-        new_row = lr;
-        const int64_t src = (static_cast<int64_t>(s) * a.num_kv_heads + kvh) * kRowBytes;
-        nk = reinterpret_cast<const char*>(a.new_k) + src;
-        nv = reinterpret_cast<const char*>(a.new_v) + src;
-        if (h % G == 0 && threadIdx.x < 2 * (kRowBytes / 16)) {
-          const int c = threadIdx.x % (kRowBytes / 16);
-          const bool is_v = threadIdx.x >= kRowBytes / 16;
-          const int64_t dst = lb * block_bytes + head_off + static_cast<int64_t>(lr) * kRowBytes + 16 * c;
-          *reinterpret_cast<u32x4*>(const_cast<char*>(is_v ? vc : kc) + dst) =
-              *reinterpret_cast<const u32x4*>((is_v ? nv : nk) + 16 * c);
-        }
-      }
-    }
-  }
+  // The step's new token (decode with the cache write).  Only the wave that
+  // walks the sequence's last block uses it: there it checks that the new slot
+  // is token ctx-1's, takes that row from the new K/V and stores it into the
+  // pool (one workgroup per KV head stores).  The slot is loaded here and
+  // waited for only there.
+  const int64_t new_slot = a.new_slots ? a.new_slots[s] : -1;
+  const int32_t last_row = (ctx - 1) % kBlock;
+  const int64_t new_src = (static_cast<int64_t>(s) * a.num_kv_heads + kvh) * kRowBytes + 16 * col;
+  const bool writer = h % G == 0;
 
   // q slice of this lane, pre-scaled into base-2 units
   float qv[EPL];
@@ -219,33 +198,51 @@ __device__ __forceinline__ void decode_valu_body(const pkv_decode_args& a, uint3
       int32_t b = nxt[bi];
       tb[bi] = -1;
       if (j < blk_end) {
-        if (static_cast<uint32_t>(b) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; b = 0; }
+        const bool id_bad = static_cast<uint32_t>(b) >= static_cast<uint32_t>(a.num_blocks);
+        if (id_bad) { bad = true; b = 0; }
         tb[bi] = j * kBlock;
         const u32x4* kp = reinterpret_cast<const u32x4*>(kc + b * block_bytes + head_off);
         const u32x4* vp = reinterpret_cast<const u32x4*>(vc + b * block_bytes + head_off);
         // rows past the context (the tail of a sequence's last block) are not
         // loaded: those lanes read nothing and hold 0
         const int32_t valid = ctx - j * kBlock;
-        if (j != new_blk) {
+        int mode = 0;       // 0: all rows from the pool; 1: the new token's block; 2: a wrong slot
+        if (j == nblk - 1) {
+          if (new_slot >= 0) mode = (!id_bad && new_slot == static_cast<int64_t>(b) * kBlock + last_row) ? 1 : 2;
+        }
+        if (mode == 0) {
 #pragma unroll
           for (int i = 0; i < NLD; ++i)
             kt[bi][i] = i * TPL + row < valid ? __builtin_nontemporal_load(kp + i * 64 + lane) : u32x4{0, 0, 0, 0};
 #pragma unroll
           for (int i = 0; i < NLD; ++i)
             vt[bi][i] = i * TPL + row < valid ? __builtin_nontemporal_load(vp + i * 64 + lane) : u32x4{0, 0, 0, 0};
+        } else if (mode == 2) {
+          bad = true;       // not token ctx-1's slot: NaN rows, nothing stored
+#pragma unroll
+          for (int i = 0; i < NLD; ++i) { kt[bi][i] = u32x4{0, 0, 0, 0}; vt[bi][i] = u32x4{0, 0, 0, 0}; }
         } else {
-          // the block of the new token: its row comes from the new K/V
+          // the block of the new token: its row comes from the new K/V and is
+          // stored into the pool by the lanes that hold it
+          const char* nk = reinterpret_cast<const char*>(a.new_k) + new_src;
+          const char* nv = reinterpret_cast<const char*>(a.new_v) + new_src;
 #pragma unroll
           for (int i = 0; i < NLD; ++i) {
             const int r = i * TPL + row;
-            kt[bi][i] = r < new_row ? __builtin_nontemporal_load(kp + i * 64 + lane)
-                        : r == new_row ? *reinterpret_cast<const u32x4*>(nk + 16 * col) : u32x4{0, 0, 0, 0};
-          }
-#pragma unroll
-          for (int i = 0; i < NLD; ++i) {
-            const int r = i * TPL + row;
-            vt[bi][i] = r < new_row ? __builtin_nontemporal_load(vp + i * 64 + lane)
-                        : r == new_row ? *reinterpret_cast<const u32x4*>(nv + 16 * col) : u32x4{0, 0, 0, 0};
+            if (r < last_row) {
+              kt[bi][i] = __builtin_nontemporal_load(kp + i * 64 + lane);
+              vt[bi][i] = __builtin_nontemporal_load(vp + i * 64 + lane);
+            } else if (r == last_row) {
+              kt[bi][i] = *reinterpret_cast<const u32x4*>(nk);
+              vt[bi][i] = *reinterpret_cast<const u32x4*>(nv);
+              if (writer) {
+                *const_cast<u32x4*>(kp + i * 64 + lane) = kt[bi][i];
+                *const_cast<u32x4*>(vp + i * 64 + lane) = vt[bi][i];
+              }
+            } else {
+              kt[bi][i] = u32x4{0, 0, 0, 0};
+              vt[bi][i] = u32x4{0, 0, 0, 0};
+            }
           }
         }
       }

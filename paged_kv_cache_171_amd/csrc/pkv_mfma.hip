@@ -247,37 +247,15 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
   float m = kNegBig, lsum = 0.f;
   bool bad = false;
 
-  // The step's new token (decode with the cache write): the unit holding the
-  // sequence's last block checks that the new slot is token ctx-1's, stores
-  // the row there and takes token ctx-1 (and the unused rows after it) from
-  // the new row.
-  int32_t new_blk = -1, new_row = kBlock;
-  const char* nk = nullptr;
-  const char* nv = nullptr;
-  if (a.new_slots && !shared_unit && blk_end * kBlock >= ctx) {
-    const int64_t slot = a.new_slots[s0];
-    if (slot >= 0) {
-      const int32_t lb = table[blk_end - 1];
-      const int32_t lr = (ctx - 1) % kBlock;
-      if (static_cast<uint32_t>(lb) >= static_cast<uint32_t>(a.num_blocks) ||
-          slot != static_cast<int64_t>(lb) * kBlock + lr) {
-        bad = true;
-      } else {
-        new_blk = blk_end - 1;
-        new_row = lr;
-        const int64_t src = (static_cast<int64_t>(s0) * Hkv + kvh) * RB;
-        nk = reinterpret_cast<const char*>(a.new_k) + src;
-        nv = reinterpret_cast<const char*>(a.new_v) + src;
-        if (threadIdx.x < 2 * (RB / 16)) {
-          const int c = threadIdx.x % (RB / 16);
-          const bool is_v = threadIdx.x >= RB / 16;
-          const int64_t dst = lb * block_bytes + static_cast<int64_t>(lr) * RB + 16 * c;
-          *reinterpret_cast<u32x4*>(const_cast<char*>(is_v ? vc : kc) + dst) =
-              *reinterpret_cast<const u32x4*>((is_v ? nv : nk) + 16 * c);
-        }
-      }
-    }
-  }
+  // The step's new token (decode with the cache write).  Only the wave that
+  // loads the sequence's last block uses it: there it checks that the new slot
+  // is token ctx-1's, takes that row (and the unused rows after it) from the
+  // new K/V and stores the row into the pool.  The slot is loaded here and
+  // waited for only there.
+  const int64_t new_slot = (a.new_slots && !shared_unit) ? a.new_slots[s0] : -1;
+  const int32_t last_blk = (ctx + kBlock - 1) / kBlock - 1;
+  const int32_t last_row = (ctx - 1) % kBlock;
+  const int64_t new_src = (static_cast<int64_t>(s0) * Hkv + kvh) * RB;
 
   // The wave's block ids (at most kMaxPartTokens/16/4 = 64 of them), one per lane,
   // fetched once before the loop; each block takes its id with a lane read.
@@ -289,12 +267,20 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
   // their probabilities are 0), so the copies need no branches.
   auto issue = [&](int32_t it, u32x4 (&kt)[KC], char* tile) {
     const int32_t j = blk_begin + wave + kWaves * it;
-    int32_t id = __builtin_amdgcn_readlane(my_ids, it);
+    const int32_t raw_id = __builtin_amdgcn_readlane(my_ids, it);
+    int32_t id = raw_id;
     if (static_cast<uint32_t>(id) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; id = 0; }
     const char* kp = kc + id * block_bytes;
     const char* vp = vc + id * block_bytes;
     const int32_t valid_rows = min(kBlock, ctx - j * kBlock);
-    if (j != new_blk) {
+    int mode = 0;       // 0: all rows from the pool; 1: the new token's block; 2: a wrong slot
+    if (j == last_blk) {
+      if (new_slot >= 0)
+        mode = (static_cast<uint32_t>(raw_id) < static_cast<uint32_t>(a.num_blocks) &&
+                new_slot == static_cast<int64_t>(raw_id) * kBlock + last_row) ? 1 : 2;
+    }
+    if (mode != 1) {
+      if (mode == 2) bad = true;    // not token ctx-1's slot: NaN rows, nothing stored
       // keys past the context are not loaded (their scores are masked)
 #pragma unroll
       for (int c = 0; c < KC; ++c)
@@ -307,16 +293,27 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
       }
     } else {
       // the block of the new token: its row, and the unused rows after it,
-      // come from the new K/V (finite data; the unused rows are masked)
+      // come from the new K/V (finite data; the unused rows are masked); the
+      // lanes of the new row store it into the pool
+      const char* nk = reinterpret_cast<const char*>(a.new_k) + new_src;
+      const char* nv = reinterpret_cast<const char*>(a.new_v) + new_src;
 #pragma unroll
       for (int c = 0; c < KC; ++c)
-        kt[c] = n < new_row ? load16_nt(kp + n * RB + 64 * c + 16 * g)
-                : n == new_row ? *reinterpret_cast<const u32x4*>(nk + 64 * c + 16 * g) : u32x4{0, 0, 0, 0};
+        kt[c] = n < last_row ? load16_nt(kp + n * RB + 64 * c + 16 * g)
+                : n == last_row ? *reinterpret_cast<const u32x4*>(nk + 64 * c + 16 * g) : u32x4{0, 0, 0, 0};
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
-        const char* src = (1024 * i + 16 * lane) / RB < new_row ? vp + dma_off[i] : nv + dma_off[i] % RB;
+        const char* src = (1024 * i + 16 * lane) / RB < last_row ? vp + dma_off[i] : nv + dma_off[i] % RB;
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
                                          (__attribute__((address_space(3))) void*)(tile + 1024 * i), 16, 0, 0);
+      }
+      if (n == last_row) {
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          *reinterpret_cast<u32x4*>(const_cast<char*>(kp) + last_row * RB + 64 * c + 16 * g) = kt[c];
+          *reinterpret_cast<u32x4*>(const_cast<char*>(vp) + last_row * RB + 64 * c + 16 * g) =
+              *reinterpret_cast<const u32x4*>(nv + 64 * c + 16 * g);
+        }
       }
     }
   };

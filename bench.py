@@ -527,14 +527,17 @@ def main():
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     plan_bytes = PK.pkv_decode_plan_bytes(S, max_ctx_cap)
     plan = torch.zeros(max(plan_bytes, 256), dtype=torch.uint8, device=dev)
-    tables_h = torch.zeros(S, MB, dtype=torch.int32).pin_memory()
-    lens_h = torch.zeros(S, dtype=torch.int32).pin_memory()
-    slots_h = torch.zeros(S, dtype=torch.int64).pin_memory()
+    # pinned staging for the step's indices: one set per step of a phase (the
+    # host runs steps ahead of the GPU, so a set must not be refilled while an
+    # earlier step's copy may still read it; the warm-up and the timed phase are
+    # separated by a synchronize, so the timed steps reuse the warm-up's sets)
+    staging = [(torch.zeros(S, MB, dtype=torch.int32).pin_memory(), torch.zeros(S, dtype=torch.int32).pin_memory(),
+                torch.zeros(S, dtype=torch.int64).pin_memory(), torch.zeros(S, 2, dtype=torch.int32).pin_memory())
+               for _ in range(max(args.warmup, args.steps))]
     tables_d = torch.zeros(S, MB, dtype=torch.int32, device=dev)
     lens_d = torch.zeros(S, dtype=torch.int32, device=dev)
     slots_d = torch.zeros(S, dtype=torch.int64, device=dev)
     pairs_d = torch.zeros(S, 2, dtype=torch.int32, device=dev)
-    pairs_h = torch.zeros(S, 2, dtype=torch.int32).pin_memory()
     scale = 1.0 / math.sqrt(D)
     torch.cuda.synchronize()
 
@@ -548,10 +551,13 @@ def main():
     op = [out[l].data_ptr() for l in range(L)]
     BF16 = PK.PKV_BF16
 
-    def step(events=None):
+    def step(k, events=None):
+        """Step k of its phase; events: a (start, end) pair recorded around the
+        step's L decode launches."""
         # (a1) host: reserve one slot per sequence, refresh the tables
         slots, pairs = alloc.seq_append_slots_batch(seqs, ones)
         t, ln = alloc.block_tables(seqs, MB)
+        tables_h, lens_h, slots_h, pairs_h = staging[k]
         slots_h.numpy()[:] = slots
         tables_h.numpy()[:] = t
         lens_h.numpy()[:] = ln
@@ -571,30 +577,37 @@ def main():
                 B._check(lib.pkv_copy_blocks(kp[l][0], kp[l][1], pairs_d.data_ptr(), n_pairs, NB, H, D, P, BF16, sp))
             # (a3, a4, a5) this step's K/V written at their slots inside the paged
             # decode attention launch, then the partition merge
-            if events is not None:
-                events[l][0].record(stream)
+            if events is not None and l == 0:
+                events[0].record(stream)
             B._check(lib.pkv_attention_decode_append(op[l], qp[l], kvn[l][0], kvn[l][1], slots_d.data_ptr(),
                                                      kp[l][0], kp[l][1], tables_d.data_ptr(), MB, lens_d.data_ptr(),
                                                      S, H, H, D, P, NB, max_ctx, scale, BF16, plan.data_ptr(),
                                                      plan.numel(), ws.data_ptr(), ws.numel(), sp))
-            if events is not None:
-                events[l][1].record(stream)
+            if events is not None and l == L - 1:
+                events[1].record(stream)
         return ln
 
-    for _ in range(args.warmup):
-        step()
+    for k in range(args.warmup):
+        step(k)
     torch.cuda.synchronize()
 
-    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(L)]
-          for _ in range(args.steps)]
+    # the L decode launches of each step are bracketed by one pair of events
+    # (events around every launch add two markers per layer to the step and
+    # read a few microseconds high each)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     step_lens = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step_lens.append(step(ev[k]))
+        step_lens.append(step(k, ev[k]))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # every output row of the last step is finite: each sequence's slot matched
+    # its last token and every table entry was in the pool
+    for l in range(L):
+        if not bool(torch.isfinite(out[l]).all()):
+            raise SystemExit(f"bench: non-finite attention output in layer {l}")
 
     # algorithmic bytes of one decode launch: K and V of every live token once
     # (the new token's from the step's rows), the new K/V rows written to the
@@ -603,7 +616,7 @@ def main():
     kv_bytes = [int(ln.sum()) * 2 * H * D * 2 for ln in step_lens]
     other = [S * 2 * H * D * 2 + S * H * D * 2 + S * H * D * 4 + int(sum(-(-int(c) // P) for c in ln)) * 4 + S * 4 +
              S * 8 for ln in step_lens]
-    dec_ms = [sum(ev[k][l][0].elapsed_time(ev[k][l][1]) for l in range(L)) for k in range(args.steps)]
+    dec_ms = [ev[k][0].elapsed_time(ev[k][1]) for k in range(args.steps)]
     launches = args.steps * L
     alg_bytes_total = sum((kv + o) * L for kv, o in zip(kv_bytes, other))
     dec_s_total = sum(dec_ms) / 1e3

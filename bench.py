@@ -650,7 +650,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": "decode_valu_kernel<bf16,128,16> (with the cache write) + merge_partitions_kernel<128>",
+                     "kernel": "decode_valu_kernel<bf16,128,16> (with the cache write and the merge of split contexts)",
                      "avg_launch_us": round(avg_launch_us, 2),
                      "alg_bytes_per_launch": round(alg_bytes_total / launches)},
     }

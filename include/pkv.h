@@ -155,11 +155,15 @@ pkv_status pkv_swap_blocks(void* dst_k_cache, void* dst_v_cache, int32_t dst_num
  * max_blocks_per_seq*block_size, or whose table names a block outside
  * [0, num_blocks), is written as NaN.
  * workspace: device scratch of at least pkv_attention_workspace_bytes(...) bytes
- * for the decode plan and the partial results of split contexts (the context
- * is cut into partitions of 1024 tokens, 4096 for the matrix-core group
- * kernel; a second kernel merges split contexts).  No initialisation is needed; its contents are meaningless
- * between calls.  Calls that share one workspace must not overlap in time
- * (e.g. run them on one stream).
+ * for the decode plan, the partial results of split contexts (the context is
+ * cut into partitions of 1024 tokens, 4096 for the matrix-core group kernel)
+ * and one 8-byte merge ticket per (sequence, head): the last partition of a
+ * row to finish merges the row's partials in the same launch.  No
+ * initialisation is needed (a ticket counts only under the launch's own
+ * 48-bit tag, and the merging unit sets it back to 0, so a launch captured in
+ * a HIP graph can be replayed); the contents are meaningless between calls.
+ * Calls that share one workspace must not overlap in time (e.g. run them on
+ * one stream).
  * ------------------------------------------------------------------------ */
 size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                      int32_t max_context_len);

@@ -2,10 +2,13 @@
 // kernel launchers.  Nothing here allocates device memory or synchronises.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <random>
 #include <string>
 
 #include "pkv_internal.h"
@@ -64,6 +67,21 @@ SharedLayout shared_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim
   return l;
 }
 }  // namespace
+
+// Merge-ticket epochs: 48-bit, nonzero, a new one for every decode launch.  The
+// sequence starts at a random point so that a workspace holding another
+// process's tickets cannot match.
+static uint64_t next_merge_epoch() {
+  static std::atomic<uint64_t> next{[] {
+    std::random_device rd;
+    const uint64_t t = static_cast<uint64_t>(std::chrono::steady_clock::now().time_since_epoch().count());
+    return (static_cast<uint64_t>(rd()) << 32) ^ rd() ^ (t * 0x9E3779B97F4A7C15ull);
+  }()};
+  for (;;) {
+    const uint64_t e = next.fetch_add(1, std::memory_order_relaxed) & 0xFFFFFFFFFFFFull;
+    if (e != 0) return e;
+  }
+}
 
 pkv_status pkv_fail(pkv_status st, const char* msg) {
   g_last_error = msg;
@@ -259,9 +277,15 @@ static pkv_status decode_impl(const char* fn, float* out, const void* q, const v
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.plan = static_cast<const int32_t*>(plan);
-  const size_t units = static_cast<size_t>(num_seqs) * num_heads * np;
   a.part_ml = part ? reinterpret_cast<float*>(ws) : nullptr;
-  a.part_acc = part ? reinterpret_cast<float*>(ws + align256(units * 2 * sizeof(float))) : nullptr;
+  a.part_acc = part ? reinterpret_cast<float*>(ws + pkv_ws::partial_acc_offset(num_seqs, num_heads, max_context_len))
+                    : nullptr;
+  if (part && a.part_tokens < max_context_len) {
+    // split contexts are merged inside the decode launch
+    a.merge_tickets = reinterpret_cast<uint64_t*>(ws + pkv_ws::ticket_offset(num_seqs, num_heads, head_dim,
+                                                                             max_context_len));
+    a.merge_epoch = next_merge_epoch();
+  }
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;

@@ -111,6 +111,7 @@ __device__ __forceinline__ void decode_valu_body(const pkv_decode_args& a, uint3
   __shared__ float sm_acc[kValuWaves][D];
   __shared__ float sm_ml[kValuWaves][2];
   __shared__ int sm_bad[kValuWaves];
+  __shared__ int sm_last;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
@@ -340,12 +341,26 @@ __device__ __forceinline__ void decode_valu_body(const pkv_decode_args& a, uint3
     if (t < D) a.out[orow + t] = o / L;
     return;
   }
-  // a split context: this partition's (max, sum, accumulator) for the merge kernel
-  const int64_t pidx = (static_cast<int64_t>(s) * Hq + h) * a.num_partitions + base + p;
-  if (t < D) {
-    a.part_acc[pidx * D + t] = o;
-    if (t == 0) { a.part_ml[2 * pidx] = M; a.part_ml[2 * pidx + 1] = L; }
+  // a split context: this partition's (max, sum, accumulator) ...
+  const int64_t prow = (static_cast<int64_t>(s) * Hq + h) * a.num_partitions;
+  const int64_t pidx = prow + base + p;
+  if (a.merge_tickets == nullptr) {
+    // ... merged by merge_partitions_kernel
+    if (t < D) {
+      a.part_acc[pidx * D + t] = o;
+      if (t == 0) { a.part_ml[2 * pidx] = M; a.part_ml[2 * pidx + 1] = L; }
+    }
+    return;
   }
+  // ... merged here by the row's last unit to finish
+  if (t < D) {
+    pkvd::store_coherent(a.part_acc + pidx * D + t, o);
+    if (t == 0) { pkvd::store_coherent(a.part_ml + 2 * pidx, M); pkvd::store_coherent(a.part_ml + 2 * pidx + 1, L); }
+  }
+  if (!pkvd::arrive_last(a.merge_tickets + static_cast<int64_t>(s) * Hq + h, a.merge_epoch, base + np_s, &sm_last))
+    return;
+  if (t < D)
+    a.out[orow + t] = pkvd::merge_partials_coherent(a.part_ml + 2 * prow, a.part_acc + prow * D + t, base + np_s, D);
 }
 
 }  // namespace

@@ -47,16 +47,97 @@ __device__ __forceinline__ int32_t slot_base_of(const pkv_decode_args& a, int32_
 
 // Log-sum-exp merge of the n partials (m in log2 units, l, acc) of one output
 // element: sum_p acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M), M = max_p m_p.
-__device__ __forceinline__ float merge_partials(const float* ml, const float* acc, int32_t n, int32_t stride) {
-  float M = ml[0];
-  for (int32_t q = 1; q < n; ++q) M = fmaxf(M, ml[2 * q]);
-  float L = 0.f, o = 0.f;
-  for (int32_t q = 0; q < n; ++q) {
-    const float f = fast_exp2(ml[2 * q] - M);
-    L += ml[2 * q + 1] * f;
-    o += acc[static_cast<int64_t>(q) * stride] * f;
+// The partials are loaded 8 at a time (all loads of a chunk in flight
+// together) and the chunks combined by the same rule; with n <= 8 this is the
+// plain one-pass sum.  Load(p) reads one float.
+template <typename Load>
+__device__ __forceinline__ float merge_partials_with(const float* ml, const float* acc, int32_t n, int32_t stride,
+                                                     Load load) {
+  constexpr int kChunk = 8;
+  float M = -INFINITY, L = 0.f, o = 0.f;
+  for (int32_t q0 = 0; q0 < n; q0 += kChunk) {
+    float mv[kChunk], lv[kChunk], av[kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      const bool in = q0 + i < n;
+      mv[i] = in ? load(ml + 2 * (q0 + i)) : -INFINITY;
+      lv[i] = in ? load(ml + 2 * (q0 + i) + 1) : 0.f;
+      av[i] = in ? load(acc + static_cast<int64_t>(q0 + i) * stride) : 0.f;
+    }
+    float Mc = mv[0];
+#pragma unroll
+    for (int i = 1; i < kChunk; ++i) Mc = fmaxf(Mc, mv[i]);
+    const float Mn = fmaxf(M, Mc);
+    const float r = fast_exp2(M - Mn);     // 0 for the first chunk
+    float Lc = 0.f, oc = 0.f;
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      if (q0 + i < n) {
+        const float f = fast_exp2(mv[i] - Mn);
+        Lc += lv[i] * f;
+        oc += av[i] * f;
+      }
+    }
+    L = L * r + Lc;
+    o = o * r + oc;
+    M = Mn;
   }
   return o / L;
+}
+
+__device__ __forceinline__ float merge_partials(const float* ml, const float* acc, int32_t n, int32_t stride) {
+  return merge_partials_with(ml, acc, n, stride, [](const float* p) { return *p; });
+}
+
+// The partition merge inside the decode launch.  The partials of a row whose
+// merge happens in the launch are written and read with agent-scope atomic
+// accesses, which go through to the level shared by all XCDs (each XCD's L2 is
+// private), so no cache-wide write-back or invalidation is needed: ordering
+// alone (every vector memory access of the thread complete) makes them
+// visible.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_vmem() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0x0F70);    // vmcnt(0): every vector memory access done
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Every thread of a workgroup calls this after its store_coherent partial
+// stores; the result (uniform) says whether the workgroup's unit is the last of
+// the row's `units` units to arrive, in which case the other units' partials
+// can be read with load_coherent and the ticket is already back at 0.  Each
+// unit takes one ticket step, so the compare-and-swap loop ends after at most
+// `units` rounds.
+__device__ __forceinline__ bool arrive_last(uint64_t* ticket, uint64_t epoch, int32_t units, int* sm_flag) {
+  wait_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint64_t tag = epoch << 16;
+    uint64_t old = __hip_atomic_load(ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint64_t arrived;
+    for (;;) {
+      arrived = ((old & ~0xFFFFull) == tag ? (old & 0xFFFFull) : 0) + 1;
+      if (__hip_atomic_compare_exchange_strong(ticket, &old, tag | arrived, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT))
+        break;
+    }
+    const bool last = arrived == static_cast<uint64_t>(units);
+    if (last) __hip_atomic_store(ticket, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *sm_flag = last ? 1 : 0;
+  }
+  __syncthreads();
+  return *sm_flag != 0;
+}
+
+// merge_partials over partials written with store_coherent.
+__device__ __forceinline__ float merge_partials_coherent(const float* ml, const float* acc, int32_t n,
+                                                         int32_t stride) {
+  return merge_partials_with(ml, acc, n, stride, [](const float* p) { return load_coherent(p); });
 }
 
 }  // namespace pkvd

@@ -53,11 +53,20 @@ inline size_t plan_bytes(int32_t num_seqs, int32_t max_context_len) {
   return (kPlanHdrWords + 2 * static_cast<size_t>(num_seqs) * (num_partitions(max_context_len) + 1)) *
          sizeof(int32_t);
 }
+// Partials of the split contexts: (max, sum) pairs, accumulators, then one
+// merge ticket (8 bytes) per (sequence, head).
+inline size_t partial_acc_offset(int32_t num_seqs, int32_t num_heads, int32_t max_context_len) {
+  const size_t units = static_cast<size_t>(num_seqs) * num_heads * num_partitions(max_context_len);
+  return align256(units * 2 * sizeof(float));
+}
+inline size_t ticket_offset(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len) {
+  const size_t units = static_cast<size_t>(num_seqs) * num_heads * num_partitions(max_context_len);
+  return partial_acc_offset(num_seqs, num_heads, max_context_len) + align256(units * head_dim * sizeof(float));
+}
 inline size_t partial_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len) {
-  const int32_t np = num_partitions(max_context_len);
-  if (np <= 1) return 0;
-  const size_t units = static_cast<size_t>(num_seqs) * num_heads * np;
-  return align256(units * 2 * sizeof(float)) + units * head_dim * sizeof(float);
+  if (num_partitions(max_context_len) <= 1) return 0;
+  return ticket_offset(num_seqs, num_heads, head_dim, max_context_len) +
+         static_cast<size_t>(num_seqs) * num_heads * sizeof(uint64_t);
 }
 }  // namespace pkv_ws
 
@@ -97,6 +106,15 @@ struct pkv_decode_args {
   const void* new_k;
   const void* new_v;
   const int64_t* new_slots;
+  // Partition merge inside the decode launch (null: merge_partitions_kernel
+  // runs after it).  One ticket per (sequence, head) row -- for the MFMA group
+  // kernel per (sequence, KV head), at its first query head's row.  A ticket
+  // holds (merge_epoch << 16 | units arrived); a word with another epoch counts
+  // as 0, so the buffer needs no initial clearing; the unit that arrives last
+  // merges the row and sets the word back to 0.  merge_epoch is nonzero, below
+  // 2^48 and new for every launch.
+  uint64_t* merge_tickets;
+  uint64_t merge_epoch;
 };
 // Decode: the main kernel (VALU, or MFMA for bf16 query-head groups of 2..16
 // heads, pkv_mfma.hip), then the partition merge when a context can be split.

@@ -294,8 +294,10 @@ int pkv_launch_decode(const pkv_decode_args& a, void* stream) {
   } else {
     err = a.head_dim == 128 ? launch_decode_valu<float, 128>(a, st) : launch_decode_valu<float, 64>(a, st);
   }
-  // no context can be split (and no shared prefix adds partials): no merge
-  if (err != hipSuccess || (a.seq_start == nullptr && a.max_context_len <= a.part_tokens)) return err;
+  // no context can be split (and no shared prefix adds partials), or the
+  // decode kernel merges the split rows itself: no merge launch
+  if (err != hipSuccess || a.merge_tickets != nullptr || (a.seq_start == nullptr && a.max_context_len <= a.part_tokens))
+    return err;
   return pkv_launch_merge(a, stream);
 }
 

@@ -149,6 +149,7 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
   __shared__ __align__(16) char smem[kSmem];
   __shared__ float sm_ml[kWaves][16][2];
   __shared__ int sm_bad[kWaves];
+  __shared__ int sm_last;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -162,6 +163,7 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
   // it walks blocks blk_begin .. blk_end-1 of s0's table, keys below ctx valid,
   // and writes the output rows (direct) or partial slot `slot` of each row.
   int32_t s0, nrows, ctx, blk_begin, blk_end, slot;
+  int32_t nslots = 0;     // partial slots of each row (merged in this launch when tickets are given)
   bool direct;
   if (shared_unit) {
     // a group's shared leading blocks: the rows are the group's sequences
@@ -205,6 +207,7 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
     blk_begin = start / kBlock + p * (part / kBlock);
     blk_end = min(nblk, blk_begin + part / kBlock);
     slot = base + p;
+    nslots = base + np_s;
     direct = np_s == 1 && base == 0;
   }
 
@@ -380,6 +383,7 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
   if (lane == 0) sm_bad[wave] = bad ? 1 : 0;
   __syncthreads();
   const bool any_bad = (sm_bad[0] | sm_bad[1] | sm_bad[2] | sm_bad[3]) != 0;
+  const bool in_launch_merge = !direct && !shared_unit && a.merge_tickets != nullptr;
   for (int idx = threadIdx.x; idx < nrows * D; idx += 256) {
     const int r = idx / D, d = idx - (idx / D) * D;
     float M = sm_ml[0][r][0];
@@ -396,13 +400,28 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
     const int64_t row = static_cast<int64_t>(s0 + r / G) * Hq + kvh * G + r % G;
     if (direct) {
       a.out[row * D + d] = acc / L;
-    } else {
+    } else if (!in_launch_merge) {
       const int64_t pidx = row * a.num_partitions + slot;
       a.part_acc[pidx * D + d] = acc;
       if (d == 0) { a.part_ml[2 * pidx] = M; a.part_ml[2 * pidx + 1] = L; }
+    } else {
+      const int64_t pidx = row * a.num_partitions + slot;
+      pkvd::store_coherent(a.part_acc + pidx * D + d, acc);
+      if (d == 0) { pkvd::store_coherent(a.part_ml + 2 * pidx, M); pkvd::store_coherent(a.part_ml + 2 * pidx + 1, L); }
     }
   }
   (void)kSlots;
+  // a split context: the last of the sequence's units (for this KV head) to
+  // finish merges the G rows, else merge_partitions_kernel does
+  if (!in_launch_merge) return;
+  const int64_t row0 = static_cast<int64_t>(s0) * Hq + kvh * G;
+  if (!pkvd::arrive_last(a.merge_tickets + row0, a.merge_epoch, nslots, &sm_last)) return;
+  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    const int64_t prow = (row0 + idx / D) * a.num_partitions;
+    const int d = idx - (idx / D) * D;
+    a.out[(row0 + idx / D) * D + d] =
+        pkvd::merge_partials_coherent(a.part_ml + 2 * prow, a.part_acc + prow * D + d, nslots, D);
+  }
 }
 
 template <int D, bool kShared>

@@ -90,46 +90,79 @@ def test_13b_shaped_batch_full():
     assert err <= TOL["bf16"], err
 
 
-def test_13b_step_in_the_bench_launch_configuration():
-    """The full 13B-shaped batch driven the way bench.py times it: one new token
-    per sequence (batched slot reservation, pkv_append), one pkv_decode_plan for
-    the step, then pkv_attention_decode_planned on two layer pools that share
-    the tables (the second with K and V exchanged); every output row against the
-    oracle, and the pools bit-exact after the writes."""
+def test_13b_steps_in_the_bench_launch_configuration():
+    """Three decode steps of the full 13B-shaped batch enqueued back to back the
+    way bench.py times them: per step the batched slot reservation, the step's
+    indices staged through a pinned buffer of its own with asynchronous copies
+    (no host wait between steps), one pkv_decode_plan, then
+    pkv_attention_decode_append (cache write, decode and the in-launch merge of
+    split contexts) on two layers with pools of their own.  Every step's outputs
+    of both layers against the oracle, and all four pools bit-exact at the end."""
     w = W.shaped_13b()
-    print("case: 13b bench step", flush=True)
+    print("case: 13b bench steps", flush=True)
     g, r = GpuReplay(w), _oracle(w)
     seqs = list(w.decode_seqs)
-    slots, cow = g.alloc.seq_append_slots_batch(seqs, [1] * len(seqs))
-    oslots = []
-    for s_ in seqs:
-        sl, pairs = r.alloc.append_slots(s_, 1)
-        oslots += sl
-        assert not pairs
-    assert list(slots) == oslots and len(cow) == 0
+    S, H, D, steps = len(seqs), 40, 128, 3
+    lens0 = np.array([r.alloc.num_tokens(s_) for s_ in seqs])
+    assert lens0.max() > 1024              # some contexts split: the merge runs
+    cap = int(lens0.max()) + steps
+    MB = -(-cap // 16)
+    # layer 1 has pools of its own (copies of layer 0's)
+    gpools = [(g.k_pool, g.v_pool), (g.k_pool.clone(), g.v_pool.clone())]
+    opools = [(r.k_pool, r.v_pool), (r.k_pool.copy(), r.v_pool.copy())]
     rng = np.random.default_rng(2024)
-    kn = W.f32_to_bf16_bits(rng.standard_normal((len(seqs), 40, 128), dtype=np.float32))
-    vn = W.f32_to_bf16_bits(rng.standard_normal((len(seqs), 40, 128), dtype=np.float32))
-    PK.pkv_append(g.k_pool, g.v_pool, rows_to_device(kn, "cuda"), rows_to_device(vn, "cuda"),
-                  torch.from_numpy(np.asarray(slots, dtype=np.int64)).cuda())
-    O.write_cache(r.k_pool, r.v_pool, kn, vn, oslots)
-    tables, lens = g.tables(seqs)
-    td, ld = torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
-    mcl = int(lens.max())
-    plan = PK.plan_for(ld, 40, 40, tables.shape[1], mcl, PK.PKV_BF16)
-    ws = PK.workspace_for(len(seqs), 40, 128, mcl)
-    q = rows_to_device(w.q, "cuda")
-    otables = [r.alloc.block_table(s_) for s_ in seqs]
-    olens = [r.alloc.num_tokens(s_) for s_ in seqs]
-    assert list(lens) == olens
-    for kp, vp, okp, ovp in ((g.k_pool, g.v_pool, r.k_pool, r.v_pool), (g.v_pool, g.k_pool, r.v_pool, r.k_pool)):
-        out = torch.full((len(seqs), 40, 128), -4.0, dtype=torch.float32, device="cuda")
-        PK.pkv_attention_decode(out, q, kp, vp, td, ld, mcl, float(w.scale), workspace=ws, plan=plan)
-        torch.cuda.synchronize()
-        ref = O.decode_attention(w.q, okp, ovp, otables, olens, w.scale)
-        err = float(np.abs(out.cpu().numpy() - ref).max())
-        assert err <= TOL["bf16"], err
-    assert np.array_equal(pool_to_host(g.k_pool), r.k_pool) and np.array_equal(pool_to_host(g.v_pool), r.v_pool)
+
+    def bf16(shape):
+        return W.f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+
+    new = [[(bf16((S, H, D)), bf16((S, H, D)), bf16((S, H, D))) for _ in range(2)] for _ in range(steps)]
+    dnew = [[tuple(rows_to_device(x, "cuda") for x in lay) for lay in st] for st in new]
+    staging = [(torch.zeros(S, MB, dtype=torch.int32).pin_memory(), torch.zeros(S, dtype=torch.int32).pin_memory(),
+                torch.zeros(S, dtype=torch.int64).pin_memory()) for _ in range(steps)]
+    tables_d = torch.zeros(S, MB, dtype=torch.int32, device="cuda")
+    lens_d = torch.zeros(S, dtype=torch.int32, device="cuda")
+    slots_d = torch.zeros(S, dtype=torch.int64, device="cuda")
+    plan = torch.zeros(max(PK.pkv_decode_plan_bytes(S, cap), 256), dtype=torch.uint8, device="cuda")
+    ws = PK.workspace_for(S, H, D, cap)
+    outs = [[torch.full((S, H, D), -4.0, dtype=torch.float32, device="cuda") for _ in range(2)] for _ in range(steps)]
+    host = []
+    for k in range(steps):
+        slots, cow = g.alloc.seq_append_slots_batch(seqs, [1] * S)
+        assert len(cow) == 0
+        t, ln = g.alloc.block_tables(seqs, MB)
+        th, lh, sh = staging[k]
+        sh.numpy()[:] = slots
+        th.numpy()[:] = t
+        lh.numpy()[:] = ln
+        slots_d.copy_(sh, non_blocking=True)
+        tables_d.copy_(th, non_blocking=True)
+        lens_d.copy_(lh, non_blocking=True)
+        mcl = int(ln.max())
+        PK.pkv_decode_plan(plan, lens_d, H, H, MB, mcl, PK.PKV_BF16)
+        for lay in range(2):
+            q, kn, vn = dnew[k][lay]
+            PK.pkv_attention_decode_append(outs[k][lay], q, kn, vn, slots_d, gpools[lay][0], gpools[lay][1],
+                                           tables_d, lens_d, mcl, float(w.scale), workspace=ws, plan=plan)
+        host.append((list(slots), ln.copy()))
+    torch.cuda.synchronize()
+    for k in range(steps):
+        oslots = []
+        for s_ in seqs:
+            sl, pairs = r.alloc.append_slots(s_, 1)
+            oslots += sl
+            assert not pairs
+        assert host[k][0] == oslots
+        otables = [r.alloc.block_table(s_) for s_ in seqs]
+        olens = [r.alloc.num_tokens(s_) for s_ in seqs]
+        assert list(host[k][1]) == olens
+        for lay in range(2):
+            q, kn, vn = new[k][lay]
+            O.write_cache(opools[lay][0], opools[lay][1], kn, vn, oslots)
+            ref = O.decode_attention(q, opools[lay][0], opools[lay][1], otables, olens, w.scale)
+            err = float(np.abs(outs[k][lay].cpu().numpy() - ref).max())
+            assert err <= TOL["bf16"], (k, lay, err)
+    for (gk, gv), (ok, ov) in zip(gpools, opools):
+        assert np.array_equal(pool_to_host(gk), ok) and np.array_equal(pool_to_host(gv), ov)
 
 
 def test_gqa_batch_full_sampled():

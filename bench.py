@@ -2,11 +2,11 @@
 
 A step is one pass of the hot path over the batch: the host allocator reserves
 one new slot per sequence (and names any copy-on-write pairs), the slot map,
-block tables and context lengths go to the device, the decode plan is built
-once, and then for each of the 40 layers one call writes the new token's K/V
-into that layer's paged pool and runs paged decode attention over it
-(pkv_attention_decode_append: the cache write happens inside the decode
-launch).
+block tables and context lengths go to the device in one packed copy and the
+decode plan is built from them, and then for each of the 40 layers one call writes the new
+token's K/V into that layer's paged pool and runs paged decode attention over
+it (pkv_attention_decode_append: the cache write and the merge of split
+contexts happen inside the decode launch).
 
 Workload: 64 sequences, 40 MHA heads, head_dim 128, bf16, context lengths
 lognormal (median 200, sigma 1.0) clipped to [1, 2048], 16-token blocks shuffled
@@ -526,18 +526,30 @@ def main():
     ws_bytes = PK.pkv_attention_workspace_bytes(S, H, D, max_ctx_cap)
     ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     plan_bytes = PK.pkv_decode_plan_bytes(S, max_ctx_cap)
+
+    # The step's indices (slots, tables, lengths, copy pairs) travel in one
+    # packed buffer: pinned staging on the host, one set per step of a phase
+    # (the host runs steps ahead of the GPU, so a set must not be refilled
+    # while an earlier step's copy may still read it; the warm-up and the timed
+    # phase are separated by a synchronize, so the timed steps reuse the
+    # warm-up's sets), one copy per step into the device set on the launch
+    # stream.  (A side stream that copies and plans step k while step k-1's
+    # layers run made the step 10-20 % slower on this GPU.)
+    def a256(n):
+        return (n + 255) // 256 * 256
+    off_tables = a256(S * 8)
+    off_lens = off_tables + a256(S * MB * 4)
+    off_pairs = off_lens + a256(S * 4)
+    packed = off_pairs + a256(S * 8)
+
+    def views(buf):
+        return (buf[off_tables:off_tables + S * MB * 4].view(torch.int32).view(S, MB),
+                buf[off_lens:off_lens + S * 4].view(torch.int32), buf[:S * 8].view(torch.int64),
+                buf[off_pairs:off_pairs + S * 8].view(torch.int32).view(S, 2))
+    staging = [torch.zeros(packed, dtype=torch.uint8).pin_memory() for _ in range(max(args.warmup, args.steps))]
+    buf_d = torch.zeros(packed, dtype=torch.uint8, device=dev)
     plan = torch.zeros(max(plan_bytes, 256), dtype=torch.uint8, device=dev)
-    # pinned staging for the step's indices: one set per step of a phase (the
-    # host runs steps ahead of the GPU, so a set must not be refilled while an
-    # earlier step's copy may still read it; the warm-up and the timed phase are
-    # separated by a synchronize, so the timed steps reuse the warm-up's sets)
-    staging = [(torch.zeros(S, MB, dtype=torch.int32).pin_memory(), torch.zeros(S, dtype=torch.int32).pin_memory(),
-                torch.zeros(S, dtype=torch.int64).pin_memory(), torch.zeros(S, 2, dtype=torch.int32).pin_memory())
-               for _ in range(max(args.warmup, args.steps))]
-    tables_d = torch.zeros(S, MB, dtype=torch.int32, device=dev)
-    lens_d = torch.zeros(S, dtype=torch.int32, device=dev)
-    slots_d = torch.zeros(S, dtype=torch.int64, device=dev)
-    pairs_d = torch.zeros(S, 2, dtype=torch.int32, device=dev)
+    tables_d, lens_d, slots_d, pairs_d = views(buf_d)
     scale = 1.0 / math.sqrt(D)
     torch.cuda.synchronize()
 
@@ -557,21 +569,18 @@ def main():
         # (a1) host: reserve one slot per sequence, refresh the tables
         slots, pairs = alloc.seq_append_slots_batch(seqs, ones)
         t, ln = alloc.block_tables(seqs, MB)
-        tables_h, lens_h, slots_h, pairs_h = staging[k]
+        tables_h, lens_h, slots_h, pairs_h = views(staging[k])
         slots_h.numpy()[:] = slots
         tables_h.numpy()[:] = t
         lens_h.numpy()[:] = ln
-        slots_d.copy_(slots_h, non_blocking=True)
-        tables_d.copy_(tables_h, non_blocking=True)
-        lens_d.copy_(lens_h, non_blocking=True)
-        max_ctx = int(ln.max())
-        # the decode plan depends only on this step's lengths: built once, used by every layer
-        B._check(lib.pkv_decode_plan(plan.data_ptr(), plan.numel(), lens_d.data_ptr(), S, H, H, MB, P, max_ctx, BF16,
-                                     sp))
         n_pairs = len(pairs)
         if n_pairs:
             pairs_h.numpy()[:n_pairs] = pairs
-            pairs_d.copy_(pairs_h, non_blocking=True)
+        max_ctx = int(ln.max())
+        buf_d.copy_(staging[k], non_blocking=True)
+        # the decode plan depends only on this step's lengths: built once, used by every layer
+        B._check(lib.pkv_decode_plan(plan.data_ptr(), plan.numel(), lens_d.data_ptr(), S, H, H, MB, P, max_ctx, BF16,
+                                     sp))
         for l in range(L):
             if n_pairs:   # (a2) copy-on-write (none arise in this workload)
                 B._check(lib.pkv_copy_blocks(kp[l][0], kp[l][1], pairs_d.data_ptr(), n_pairs, NB, H, D, P, BF16, sp))

@@ -93,8 +93,9 @@ def test_13b_shaped_batch_full():
 def test_13b_steps_in_the_bench_launch_configuration():
     """Three decode steps of the full 13B-shaped batch enqueued back to back the
     way bench.py times them: per step the batched slot reservation, the step's
-    indices staged through a pinned buffer of its own with asynchronous copies
-    (no host wait between steps), one pkv_decode_plan, then
+    indices staged through a pinned buffer of its own and copied to the device
+    in one packed copy on the launch stream (no host wait between steps), one
+    pkv_decode_plan, then
     pkv_attention_decode_append (cache write, decode and the in-launch merge of
     split contexts) on two layers with pools of their own.  Every step's outputs
     of both layers against the oracle, and all four pools bit-exact at the end."""
@@ -117,11 +118,17 @@ def test_13b_steps_in_the_bench_launch_configuration():
 
     new = [[(bf16((S, H, D)), bf16((S, H, D)), bf16((S, H, D))) for _ in range(2)] for _ in range(steps)]
     dnew = [[tuple(rows_to_device(x, "cuda") for x in lay) for lay in st] for st in new]
-    staging = [(torch.zeros(S, MB, dtype=torch.int32).pin_memory(), torch.zeros(S, dtype=torch.int32).pin_memory(),
-                torch.zeros(S, dtype=torch.int64).pin_memory()) for _ in range(steps)]
-    tables_d = torch.zeros(S, MB, dtype=torch.int32, device="cuda")
-    lens_d = torch.zeros(S, dtype=torch.int32, device="cuda")
-    slots_d = torch.zeros(S, dtype=torch.int64, device="cuda")
+    # packed staging: slots (int64), tables, lengths at 256-byte aligned offsets
+    o_t = -(-S * 8 // 256) * 256
+    o_l = o_t + -(-S * MB * 4 // 256) * 256
+    nbytes = o_l + -(-S * 4 // 256) * 256
+
+    def views(buf):
+        return (buf[o_t:o_t + S * MB * 4].view(torch.int32).view(S, MB), buf[o_l:o_l + S * 4].view(torch.int32),
+                buf[:S * 8].view(torch.int64))
+    staging = [torch.zeros(nbytes, dtype=torch.uint8).pin_memory() for _ in range(steps)]
+    buf_d = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    tables_d, lens_d, slots_d = views(buf_d)
     plan = torch.zeros(max(PK.pkv_decode_plan_bytes(S, cap), 256), dtype=torch.uint8, device="cuda")
     ws = PK.workspace_for(S, H, D, cap)
     outs = [[torch.full((S, H, D), -4.0, dtype=torch.float32, device="cuda") for _ in range(2)] for _ in range(steps)]
@@ -130,14 +137,12 @@ def test_13b_steps_in_the_bench_launch_configuration():
         slots, cow = g.alloc.seq_append_slots_batch(seqs, [1] * S)
         assert len(cow) == 0
         t, ln = g.alloc.block_tables(seqs, MB)
-        th, lh, sh = staging[k]
+        th, lh, sh = views(staging[k])
         sh.numpy()[:] = slots
         th.numpy()[:] = t
         lh.numpy()[:] = ln
-        slots_d.copy_(sh, non_blocking=True)
-        tables_d.copy_(th, non_blocking=True)
-        lens_d.copy_(lh, non_blocking=True)
         mcl = int(ln.max())
+        buf_d.copy_(staging[k], non_blocking=True)
         PK.pkv_decode_plan(plan, lens_d, H, H, MB, mcl, PK.PKV_BF16)
         for lay in range(2):
             q, kn, vn = dnew[k][lay]

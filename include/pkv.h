@@ -478,8 +478,9 @@ int32_t pkv_scheduler_max_num_batched_tokens(const pkv_scheduler* s);
  * with one asynchronous copy on `stream`, and builds the decode plan there.
  * Then, for each layer, pkv_batch_layer enqueues on `stream`: the swap-out
  * copies (that layer's device pools -> its host pools), the swap-in copies,
- * pkv_append of the step's K/V rows, causal prefill of the admitted prompts
- * and decode of the running requests.  Per layer the caller passes
+ * pkv_append of the prompts' K/V rows, causal prefill of the admitted prompts
+ * and decode of the running requests (pkv_attention_decode_append: the decode
+ * tokens' K/V rows are written by the decode launch).  Per layer the caller passes
  *   q: [T][num_heads][head_dim], k and v: [T][num_kv_heads][head_dim] (pool
  *   dtype), out: float32 [T][num_heads][head_dim], with T =
  *   num_prefill_tokens + num_decode tokens in slot_mapping order (the prefill

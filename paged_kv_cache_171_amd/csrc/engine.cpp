@@ -258,9 +258,12 @@ pkv_status pkv_batch_layer(pkv_batch* b, void* k_cache, void* v_cache, void* k_h
     if (st != PKV_OK) return st;
   }
   if (b->n_tokens == 0) return PKV_OK;
-  st = pkv_append(k_cache, v_cache, k, v, b->slots, b->n_tokens, b->NB, b->Hkv, b->d, kBatchBlock, b->dtype, stream);
-  if (st != PKV_OK) return st;
   const int32_t npt = in.num_prefill_tokens;
+  if (npt > 0) {
+    // the prompts' K/V rows; each decode token's row is written by the decode launch
+    st = pkv_append(k_cache, v_cache, k, v, b->slots, npt, b->NB, b->Hkv, b->d, kBatchBlock, b->dtype, stream);
+    if (st != PKV_OK) return st;
+  }
   if (in.num_prefill > 0) {
     st = pkv_attention_prefill_chunk(out, q, b->pf_qsl, npt, b->mql, k_cache, v_cache, b->pf_tables, b->mbp,
                                      b->pf_lens, in.num_prefill, b->Hq, b->Hkv, b->d, kBatchBlock, b->NB, b->mql,
@@ -268,12 +271,15 @@ pkv_status pkv_batch_layer(pkv_batch* b, void* k_cache, void* v_cache, void* k_h
     if (st != PKV_OK) return st;
   }
   if (in.num_decode > 0) {
-    const size_t row = static_cast<size_t>(b->Hq) * b->d;
+    const size_t row = static_cast<size_t>(b->Hq) * b->d;        // q / out elements per token
+    const size_t kv_row = static_cast<size_t>(b->Hkv) * b->d * 2;  // bytes of a bf16 K or V row
     char* ws = b->dev + b->meta + pkv_ws::align256(b->plan_cap);
-    st = pkv_attention_decode_planned(out + npt * row, static_cast<const char*>(q) + npt * row * 2, k_cache, v_cache,
-                                      b->dc_tables, b->mbd, b->dc_lens, in.num_decode, b->Hq, b->Hkv, b->d,
-                                      kBatchBlock, b->NB, b->mcl_d, scale, b->dtype, b->dev + b->meta, b->plan_cap,
-                                      ws, b->ws_cap, stream);
+    st = pkv_attention_decode_append(out + npt * row, static_cast<const char*>(q) + npt * row * 2,
+                                     static_cast<const char*>(k) + npt * kv_row,
+                                     static_cast<const char*>(v) + npt * kv_row, b->slots + npt, k_cache, v_cache,
+                                     b->dc_tables, b->mbd, b->dc_lens, in.num_decode, b->Hq, b->Hkv, b->d,
+                                     kBatchBlock, b->NB, b->mcl_d, scale, b->dtype, b->dev + b->meta, b->plan_cap,
+                                     ws, b->ws_cap, stream);
   }
   return st;
 }

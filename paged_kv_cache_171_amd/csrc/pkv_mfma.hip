@@ -82,6 +82,18 @@ __device__ __forceinline__ int32_t scalar_load_i32(const int32_t* p) {
   asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
   return v;
 }
+// The same load issued without waiting for it: the value may be used only
+// after scalar_load_wait on it.  An outstanding scalar load only makes the
+// compiler's own LDS waits (lgkmcnt) wait longer, never shorter, because LDS
+// operations complete in order.
+__device__ __forceinline__ int32_t scalar_load_i32_nowait(const int32_t* p) {
+  int32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ void scalar_load_wait(int32_t& v0, int32_t& v1) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(v0), "+s"(v1) : : "memory");
+}
 
 // Direct global->LDS copy of 16 bytes per lane: lane l's bytes land at LDS
 // address lds + 16 l.  Issued as assembly so that the compiler, which cannot
@@ -596,9 +608,9 @@ constexpr int kPrefillThreads = 64 * kPrefillWaves;
 // same MFMA column): swap odd rows with even ones, then halves, taking the max.
 __device__ __forceinline__ float max_over_rows(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // Direct global->LDS copy of 16 bytes per lane from a wave-uniform base plus a
@@ -685,9 +697,8 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void prefill_chunk_mfma_kernel(
     cp_off[i] = static_cast<uint32_t>(r * RB + 16 * slot);
     cp_off0[i] = static_cast<uint32_t>(16 * slot);
   }
-  auto issue = [&](int32_t pp, char* stage) {
-    int32_t id0 = scalar_load_i32(table + 2 * pp);
-    int32_t id1 = 2 * pp + 1 < nblk ? scalar_load_i32(table + 2 * pp + 1) : id0;
+  // the pair's block ids; the second is the first again past the last block
+  auto issue = [&](int32_t pp, int32_t id0, int32_t id1, char* stage) {
     if (static_cast<uint32_t>(id0) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; id0 = 0; }
     if (static_cast<uint32_t>(id1) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; id1 = 0; }
     const bool tail = (2 * pp + 2) * kBlock > ctx;     // some keys of the pair lie past the context
@@ -706,7 +717,9 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void prefill_chunk_mfma_kernel(
   };
 #pragma unroll
   for (int pp = 0; pp < kStages - 1; ++pp)
-    if (pp < npairs) issue(pp, ring[pp]);
+    if (pp < npairs)
+      issue(pp, scalar_load_i32(table + 2 * pp),
+            scalar_load_i32(table + __builtin_amdgcn_readfirstlane(min(2 * pp + 1, nblk - 1))), ring[pp]);
 
   // this lane's rows (one per tile) and their key limits; invalid rows: limit 0,
   // q = 0 (their results are never written).  Keys below nomask_lim are visible
@@ -787,7 +800,12 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void prefill_chunk_mfma_kernel(
           for (int jj = 0; jj < 4; ++jj)
             if (key0 + b * kBlock + 4 * g + jj >= lim[tt]) sc[4 * b + jj] = -INFINITY;
       }
-      float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+      // NaN-propagating maximum: three-input instructions, no operand quieting
+      float mx = __builtin_elementwise_maximum(
+          __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[0], sc[1]),
+                                        __builtin_elementwise_maximum(sc[2], sc[3])),
+          __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[4], sc[5]),
+                                        __builtin_elementwise_maximum(sc[6], sc[7])));
       mx = max_over_rows(mx) * c2;
       // raise the row maximum (and rescale) only when a score passes it by
       // more than kRescaleLog2; the branch is uniform over the wave
@@ -851,10 +869,21 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void prefill_chunk_mfma_kernel(
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
+      // the block ids of the pair issued after this one are loaded now and
+      // waited for only when its copies are issued
+      const int32_t pn = pp + kStages - 1;
+      int32_t nid0 = 0, nid1 = 0;
+      if (pn < npairs) {
+        nid0 = scalar_load_i32_nowait(table + 2 * pn);
+        nid1 = scalar_load_i32_nowait(table + __builtin_amdgcn_readfirstlane(min(2 * pn + 1, nblk - 1)));
+      }
       pair(pp, ring[st]);
       // every wave passed the barrier after it finished the pair before this
       // one, so that pair's stage takes pair pp + kStages - 1
-      if (pp + kStages - 1 < npairs) issue(pp + kStages - 1, ring[(st + kStages - 1) % kStages]);
+      if (pn < npairs) {
+        scalar_load_wait(nid0, nid1);
+        issue(pn, nid0, nid1, ring[(st + kStages - 1) % kStages]);
+      }
     }
   }
 

@@ -262,6 +262,13 @@ def random_small(seed: int, num_seqs: int, max_ctx: int, hq: int, hkv: int, d: i
                          pool_factor=pool_factor, block_size=block_size)
 
 
+def from_lengths(seed: int, ctx, hq: int, hkv: int, d: int, dtype: str, pool_factor: float = 1.2,
+                 block_size: int = BLOCK_SIZE) -> Workload:
+    """A decode batch with the given context lengths (0 allowed)."""
+    return _plain_decode(f"lengths{seed}", seed, ctx, hq, hkv, d, dtype, pool_factor=pool_factor,
+                         block_size=block_size)
+
+
 def random_prefill(seed: int, ctxs, n_queries, hq: int, hkv: int, d: int, pool_factor: float = 1.3) -> Workload:
     """Chunked-prefill parity cases: sequence s has ctxs[s] cached tokens, the last
     n_queries[s] of which are its chunk's queries (bf16).  Every sequence also

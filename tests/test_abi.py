@@ -152,6 +152,9 @@ def test_decode_rejects_bad_arguments(P):
     assert _decode(P, mb=0) == P.PKV_ERR_INVALID_ARG
     assert _decode(P, q=None) == P.PKV_ERR_INVALID_ARG
     assert _decode(P, S=0, q=None) == P.PKV_OK                  # nothing to do
+    # more (sequence, head, partition) units than one launch grid holds
+    assert _decode(P, S=1 << 20, Hq=1 << 12, Hkv=1 << 12) == P.PKV_ERR_UNSUPPORTED
+    assert "grid" in _lib(P).pkv_last_error().decode()
     # the plan and the split-context partials need a workspace
     need = P.pkv_attention_workspace_bytes(2, 4, 64, 5000)      # 5 partitions of 1024
     assert need > 0

@@ -672,9 +672,39 @@ def main():
                      "avg_launch_us": round(avg_launch_us, 2),
                      "alg_bytes_per_launch": round(alg_bytes_total / launches)},
     }
+    # a second denominator: what a library streaming read reaches on this GPU
+    del k_pools, v_pools
+    torch.cuda.empty_cache()
+    probe = read_probe(stream)
+    res["roofline"]["read_probe_gbps"] = round(probe, 1)
+    res["roofline"]["frac_of_read_probe"] = round(achieved / probe, 4)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def read_probe(stream, reps: int = 10) -> float:
+    """GB/s of a library streaming read on this GPU: torch.mv (the BLAS gemv)
+    of a 65536 x 32768 bf16 matrix (4 GiB, read once; the 64 KiB vector and the
+    128 KiB result are noise), median of `reps` runs timed with HIP events on
+    `stream`.  (torch's sum over the same bytes reaches about half of it.)"""
+    import torch
+    m = torch.ones(65536, 32768, dtype=torch.bfloat16, device="cuda")
+    v = torch.ones(32768, dtype=torch.bfloat16, device="cuda")
+    torch.mv(m, v)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        torch.mv(m, v)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    nbytes = m.numel() * 2
+    del m, v
+    torch.cuda.empty_cache()
+    return nbytes / float(np.median(ts)) / 1e9
 
 
 if __name__ == "__main__":

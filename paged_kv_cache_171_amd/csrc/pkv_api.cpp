@@ -280,8 +280,9 @@ static pkv_status decode_impl(const char* fn, float* out, const void* q, const v
   a.part_ml = part ? reinterpret_cast<float*>(ws) : nullptr;
   a.part_acc = part ? reinterpret_cast<float*>(ws + pkv_ws::partial_acc_offset(num_seqs, num_heads, max_context_len))
                     : nullptr;
-  if (part && a.part_tokens < max_context_len) {
-    // split contexts are merged inside the decode launch
+  if (part && a.part_tokens < max_context_len && np <= 0xFFFF) {
+    // split contexts are merged inside the decode launch (a ticket counts at
+    // most 0xFFFF partitions of a row; longer rows go to the merge kernel)
     a.merge_tickets = reinterpret_cast<uint64_t*>(ws + pkv_ws::ticket_offset(num_seqs, num_heads, head_dim,
                                                                              max_context_len));
     a.merge_epoch = next_merge_epoch();

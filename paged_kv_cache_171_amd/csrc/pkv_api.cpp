@@ -49,7 +49,7 @@ using pkv_ws::partial_bytes;
 // sequence's own ones.
 struct SharedLayout {
   int32_t prefix_slots, slots;
-  size_t shared_plan, seq_start, plan, part_ml, part_acc, total;
+  size_t shared_plan, seq_start, plan, part_ml, part_acc, tickets, total;
 };
 SharedLayout shared_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len) {
   SharedLayout l{};
@@ -63,7 +63,8 @@ SharedLayout shared_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim
   l.part_ml = l.plan + align256(plan_bytes(num_seqs, max_context_len));
   const size_t units = S * num_heads * l.slots;
   l.part_acc = l.part_ml + align256(units * 2 * sizeof(float));
-  l.total = l.part_acc + units * head_dim * sizeof(float);
+  l.tickets = l.part_acc + align256(units * head_dim * sizeof(float));
+  l.total = l.tickets + S * num_heads * sizeof(uint64_t);
   return l;
 }
 }  // namespace
@@ -419,11 +420,14 @@ pkv_status pkv_attention_decode_shared(float* out, const void* q, const void* k_
   a.seq_start = reinterpret_cast<const int32_t*>(ws + l.seq_start);
   a.shared_plan = reinterpret_cast<const int32_t*>(ws + l.shared_plan);
   a.prefix_part_tokens = kPrefixPartTokens;
-  int err = pkv_launch_shared_plan(a, group_start, num_groups, reinterpret_cast<int32_t*>(ws + l.seq_start),
-                                   reinterpret_cast<int32_t*>(ws + l.shared_plan), stream);
-  if (!err)
-    err = pkv_launch_plan(reinterpret_cast<int32_t*>(ws + l.plan), context_lens, num_seqs, max_blocks_per_seq,
-                          block_size, max_context_len, a.part_tokens, stream, a.seq_start);
+  if (l.slots <= 0xFFFF) {
+    // split rows are merged inside the decode launch (see decode_impl)
+    a.merge_tickets = reinterpret_cast<uint64_t*>(ws + l.tickets);
+    a.merge_epoch = next_merge_epoch();
+  }
+  int err = pkv_launch_shared_plans(a, group_start, num_groups, reinterpret_cast<int32_t*>(ws + l.seq_start),
+                                    reinterpret_cast<int32_t*>(ws + l.shared_plan), reinterpret_cast<int32_t*>(ws + l.plan),
+                                    stream);
   if (!err) err = pkv_launch_shared_fused(a, stream);
   return hip_status(fn, err);
 }

@@ -113,23 +113,27 @@ __device__ __forceinline__ void wait_vmem() {
 // can be read with load_coherent and the ticket is already back at 0.  Each
 // unit takes one ticket step, so the compare-and-swap loop ends after at most
 // `units` rounds.
+// One arrival on a ticket (one thread): whether it was the last of `units`,
+// in which case the ticket is set back to 0.
+__device__ __forceinline__ bool ticket_arrive(uint64_t* ticket, uint64_t epoch, int32_t units) {
+  const uint64_t tag = epoch << 16;
+  uint64_t old = __hip_atomic_load(ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint64_t arrived;
+  for (;;) {
+    arrived = ((old & ~0xFFFFull) == tag ? (old & 0xFFFFull) : 0) + 1;
+    if (__hip_atomic_compare_exchange_strong(ticket, &old, tag | arrived, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      break;
+  }
+  const bool last = arrived == static_cast<uint64_t>(units);
+  if (last) __hip_atomic_store(ticket, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return last;
+}
+
 __device__ __forceinline__ bool arrive_last(uint64_t* ticket, uint64_t epoch, int32_t units, int* sm_flag) {
   wait_vmem();
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint64_t tag = epoch << 16;
-    uint64_t old = __hip_atomic_load(ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    uint64_t arrived;
-    for (;;) {
-      arrived = ((old & ~0xFFFFull) == tag ? (old & 0xFFFFull) : 0) + 1;
-      if (__hip_atomic_compare_exchange_strong(ticket, &old, tag | arrived, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT))
-        break;
-    }
-    const bool last = arrived == static_cast<uint64_t>(units);
-    if (last) __hip_atomic_store(ticket, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *sm_flag = last ? 1 : 0;
-  }
+  if (threadIdx.x == 0) *sm_flag = ticket_arrive(ticket, epoch, units) ? 1 : 0;
   __syncthreads();
   return *sm_flag != 0;
 }

@@ -124,13 +124,15 @@ int pkv_launch_plan(int32_t* plan, const int32_t* context_lens, int32_t num_seqs
                     int32_t block_size, int32_t max_context_len, int32_t part_tokens, void* stream,
                     const int32_t* seq_start = nullptr);
 
-// Shared-prefix decode (pkv_mfma.hip): the plan of the groups' common leading
-// blocks (fills seq_start and the shared plan), then the MFMA kernel over those
-// blocks.  Tokens per shared-prefix partition:
+// Shared-prefix decode (pkv_mfma.hip): one kernel plans the groups' common
+// leading blocks (fills seq_start and the shared plan) and then the sequences'
+// own units from those starts; then one launch decodes both.  Tokens per
+// shared-prefix partition:
 constexpr int32_t kPrefixPartTokens = 1024;
-int pkv_launch_shared_plan(const pkv_decode_args& a, const int32_t* group_start, int32_t num_groups,
-                           int32_t* seq_start, int32_t* shared_plan, void* stream);
-// The shared-prefix units and the sequences' own units in one launch, then the merge.
+int pkv_launch_shared_plans(const pkv_decode_args& a, const int32_t* group_start, int32_t num_groups,
+                            int32_t* seq_start, int32_t* shared_plan, int32_t* plan, void* stream);
+// The shared-prefix units and the sequences' own units in one launch (with the
+// merge of split rows inside it when tickets are given, else a merge launch).
 int pkv_launch_shared_fused(const pkv_decode_args& a, void* stream);
 // The partition merge alone (pkv_kernels.hip).
 int pkv_launch_merge(const pkv_decode_args& a, void* stream);

@@ -38,6 +38,7 @@
 // (score -inf, V row 0), never by multiplying, so NaN in unused slots cannot
 // reach the output.
 #include "pkv_decode_valu.h"
+#include "pkv_plan.h"
 
 namespace {
 
@@ -162,6 +163,7 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
   __shared__ float sm_ml[kWaves][16][2];
   __shared__ int sm_bad[kWaves];
   __shared__ int sm_last;
+  __shared__ int sm_member_last[kMaxMfmaGroup], sm_member_slots[kMaxMfmaGroup];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -395,7 +397,7 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
   if (lane == 0) sm_bad[wave] = bad ? 1 : 0;
   __syncthreads();
   const bool any_bad = (sm_bad[0] | sm_bad[1] | sm_bad[2] | sm_bad[3]) != 0;
-  const bool in_launch_merge = !direct && !shared_unit && a.merge_tickets != nullptr;
+  const bool in_launch_merge = !direct && a.merge_tickets != nullptr;
   for (int idx = threadIdx.x; idx < nrows * D; idx += 256) {
     const int r = idx / D, d = idx - (idx / D) * D;
     float M = sm_ml[0][r][0];
@@ -424,15 +426,44 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
   }
   (void)kSlots;
   // a split context: the last of the sequence's units (for this KV head) to
-  // finish merges the G rows, else merge_partitions_kernel does
+  // finish merges its G rows, else merge_partitions_kernel does
   if (!in_launch_merge) return;
-  const int64_t row0 = static_cast<int64_t>(s0) * Hq + kvh * G;
-  if (!pkvd::arrive_last(a.merge_tickets + row0, a.merge_epoch, nslots, &sm_last)) return;
-  for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-    const int64_t prow = (row0 + idx / D) * a.num_partitions;
-    const int d = idx - (idx / D) * D;
-    a.out[(row0 + idx / D) * D + d] =
-        pkvd::merge_partials_coherent(a.part_ml + 2 * prow, a.part_acc + prow * D + d, nslots, D);
+  if (!shared_unit) {
+    const int64_t row0 = static_cast<int64_t>(s0) * Hq + kvh * G;
+    if (!pkvd::arrive_last(a.merge_tickets + row0, a.merge_epoch, nslots, &sm_last)) return;
+    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+      const int64_t prow = (row0 + idx / D) * a.num_partitions;
+      const int d = idx - (idx / D) * D;
+      a.out[(row0 + idx / D) * D + d] =
+          pkvd::merge_partials_coherent(a.part_ml + 2 * prow, a.part_acc + prow * D + d, nslots, D);
+    }
+    return;
+  }
+  // a shared-prefix unit arrives once for each member sequence (on the ticket
+  // of its G rows, counting its prefix and its own partitions) and merges the
+  // members it was the last unit of
+  const int32_t members = nrows / G;
+  pkvd::wait_vmem();
+  __syncthreads();
+  if (threadIdx.x < members) {
+    const int32_t s = s0 + threadIdx.x;
+    const int32_t start = pkvd::seq_start_of(a, s);
+    const int32_t slots = pkvd::slot_base_of(a, start) + (a.context_lens[s] - start + a.part_tokens - 1) / a.part_tokens;
+    sm_member_slots[threadIdx.x] = slots;
+    sm_member_last[threadIdx.x] =
+        pkvd::ticket_arrive(a.merge_tickets + static_cast<int64_t>(s) * Hq + kvh * G, a.merge_epoch, slots) ? 1 : 0;
+  }
+  __syncthreads();
+  for (int32_t mi = 0; mi < members; ++mi) {
+    if (!sm_member_last[mi]) continue;
+    const int32_t slots = sm_member_slots[mi];
+    const int64_t row0 = static_cast<int64_t>(s0 + mi) * Hq + kvh * G;
+    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+      const int64_t prow = (row0 + idx / D) * a.num_partitions;
+      const int d = idx - (idx / D) * D;
+      a.out[(row0 + idx / D) * D + d] =
+          pkvd::merge_partials_coherent(a.part_ml + 2 * prow, a.part_acc + prow * D + d, slots, D);
+    }
   }
 }
 
@@ -481,9 +512,9 @@ __device__ __forceinline__ int32_t wave_min(int32_t x) {
   return x;
 }
 
-__global__ __launch_bounds__(1024) void shared_plan_kernel(pkv_decode_args a, const int32_t* __restrict__ group_start,
-                                                           int32_t num_groups, int32_t* __restrict__ seq_start,
-                                                           int32_t* __restrict__ shared_plan) {
+__device__ __forceinline__ void shared_plan_body(const pkv_decode_args& a, const int32_t* __restrict__ group_start,
+                                                 int32_t num_groups, int32_t* __restrict__ seq_start,
+                                                 int32_t* __restrict__ shared_plan) {
   __shared__ int32_t sm_units, sm_bad;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -571,6 +602,19 @@ __global__ __launch_bounds__(1024) void shared_plan_kernel(pkv_decode_args a, co
     shared_plan[6] = 0;
     shared_plan[7] = 0;
   }
+}
+
+// Both plans of a shared-prefix launch in one workgroup: the groups' shared
+// prefixes (seq_start, the shared plan), then the plan of every sequence's own
+// tokens from those starts (the barrier makes the starts visible to every
+// thread of the workgroup).
+__global__ __launch_bounds__(1024) void shared_plans_kernel(pkv_decode_args a, const int32_t* __restrict__ group_start,
+                                                            int32_t num_groups, int32_t* __restrict__ seq_start,
+                                                            int32_t* __restrict__ shared_plan, int32_t* __restrict__ plan) {
+  shared_plan_body(a, group_start, num_groups, seq_start, shared_plan);
+  __syncthreads();
+  plan_body(plan, a.context_lens, a.num_seqs, a.max_blocks_per_seq, a.block_size, a.max_context_len, a.part_tokens,
+            seq_start);
 }
 
 // ---------------------------------------------------------------------------
@@ -920,10 +964,10 @@ int pkv_launch_decode_group(const pkv_decode_args& a, void* stream) {
   return hipGetLastError();
 }
 
-int pkv_launch_shared_plan(const pkv_decode_args& a, const int32_t* group_start, int32_t num_groups,
-                           int32_t* seq_start, int32_t* shared_plan, void* stream) {
-  hipLaunchKernelGGL(shared_plan_kernel, dim3(1), dim3(1024), 0, static_cast<hipStream_t>(stream), a, group_start,
-                     num_groups, seq_start, shared_plan);
+int pkv_launch_shared_plans(const pkv_decode_args& a, const int32_t* group_start, int32_t num_groups,
+                            int32_t* seq_start, int32_t* shared_plan, int32_t* plan, void* stream) {
+  hipLaunchKernelGGL(shared_plans_kernel, dim3(1), dim3(1024), 0, static_cast<hipStream_t>(stream), a, group_start,
+                     num_groups, seq_start, shared_plan, plan);
   return hipGetLastError();
 }
 
@@ -945,7 +989,8 @@ int pkv_launch_shared_fused(const pkv_decode_args& a, void* stream) {
     else hipLaunchKernelGGL((decode_shared_fused_kernel<64, false>), grid, dim3(256), 0, st, a, sw);
   }
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  return pkv_launch_merge(a, stream);
+  // the split rows are merged inside the launch when tickets are given
+  return a.merge_tickets ? hipSuccess : pkv_launch_merge(a, stream);
 }
 
 int pkv_launch_prefill(const pkv_prefill_args& a, void* stream) {

@@ -102,3 +102,61 @@ def test_graph_replays_match_the_eager_call(seed, S, max_ctx, hq, hkv, d, dtype)
                                 workspace=ws)
         torch.cuda.synchronize()
         assert np.array_equal(other.cpu().numpy(), e)
+
+
+SHARED = [
+    # seed, hq, hkv, d, samples, prompt, tail_lo, tail_hi: every row has 2 or 3
+    # prefix partials (prompts past 1024 tokens) plus its own
+    (91, 8, 8, 128, [4, 3], [1500, 2100], 0, 40),       # MHA: vector-ALU own units
+    (92, 32, 8, 128, [6, 2], [1100, 3000], 1, 1200),    # G=4: matrix-core own units, some split
+]
+
+
+@pytest.mark.parametrize("seed,hq,hkv,d,samples,prompt,tail_lo,tail_hi", SHARED)
+def test_shared_prefix_merge_with_random_workspace_and_graph_replays(seed, hq, hkv, d, samples, prompt,
+                                                                      tail_lo, tail_hi):
+    print(f"case: merge in launch, shared prefix seed={seed} {hq}/{hkv}", flush=True)
+    w = W.parallel_sampling(seed=seed, groups=len(samples), samples=samples, prompt=prompt, tail_lo=tail_lo,
+                            tail_hi=tail_hi, hq=hq, hkv=hkv, d=d)
+    g = GpuReplay(w)
+    r = O.replay(w.ops, w.k_rows, w.v_rows, w.num_blocks, w.num_kv_heads, w.head_dim, w.initial_free_order)
+    tables, lens = g.tables(w.decode_seqs)
+    S, mcl = len(w.decode_seqs), int(lens.max())
+    ref = O.decode_attention(w.q, r.k_pool, r.v_pool, [r.alloc.block_table(s) for s in w.decode_seqs],
+                             [r.alloc.num_tokens(s) for s in w.decode_seqs], w.scale)
+    q = rows_to_device(w.q, "cuda")
+    td, ld = torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
+    gs = torch.from_numpy(np.ascontiguousarray(w.group_start, dtype=np.int32)).cuda()
+    n = PK.pkv_attention_decode_shared_workspace_bytes(S, hq, d, mcl)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    ws = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda", generator=gen)
+
+    def call(out):
+        PK.pkv_attention_decode_shared(out, q, g.k_pool, g.v_pool, td, ld, gs, mcl, float(w.scale), workspace=ws)
+
+    eager = torch.full((S, hq, d), -3.0, dtype=torch.float32, device="cuda")
+    call(eager)
+    torch.cuda.synchronize()
+    e = eager.cpu().numpy()
+    err = float(np.abs(e - ref).max())
+    assert err <= TOL["bf16"], err
+    out = torch.full_like(eager, -3.0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(out)
+    for _ in range(3):
+        out.fill_(-3.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), e)
+        other = torch.full_like(eager, -3.0)
+        call(other)
+        torch.cuda.synchronize()
+        assert np.array_equal(other.cpu().numpy(), e)

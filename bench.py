@@ -477,7 +477,7 @@ def blocksize_bench(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the library has no multi-GPU path (one process, one device)",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_probe:

@@ -158,15 +158,25 @@ __device__ __forceinline__ void decode_valu_body(const pkv_decode_args& a, uint3
   const int32_t* __restrict__ table = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq;
   bool bad = false;
 
-  // The step's new token (decode with the cache write).  Only the wave that
-  // walks the sequence's last block uses it: there it checks that the new slot
-  // is token ctx-1's, takes that row from the new K/V and stores it into the
-  // pool (one workgroup per KV head stores).  The slot is loaded here and
-  // waited for only there.
-  const int64_t new_slot = a.new_slots ? a.new_slots[s] : -1;
-  const int32_t last_row = (ctx - 1) % kBlock;
-  const int64_t new_src = (static_cast<int64_t>(s) * a.num_kv_heads + kvh) * kRowBytes + 16 * col;
-  const bool writer = h % G == 0;
+  // The step's new token (decode with the cache write): in the unit that holds
+  // the sequence's last token, the block loop covers tokens 0 .. ctx-2 only,
+  // and wave 0 adds token ctx-1 afterwards -- from the new K/V, loaded here
+  // into registers, when the slot is token ctx-1's (one workgroup per KV head
+  // then stores the row into the pool), else from the pool (no new token this
+  // step).  So the loop neither stores nor waits on anything extra.
+  const bool with_new = a.new_slots != nullptr && blk_end == nblk;
+  const int32_t ctx_loop = with_new ? ctx - 1 : ctx;
+  const int32_t loop_end = with_new ? min(blk_end, (ctx_loop + kBlock - 1) / kBlock) : blk_end;
+  int64_t new_slot = -1;
+  int32_t last_id = 0;
+  u32x4 nk_row{0, 0, 0, 0}, nv_row{0, 0, 0, 0};
+  if (with_new && wave == 0) {
+    new_slot = a.new_slots[s];
+    last_id = table[nblk - 1];
+    const int64_t src = (static_cast<int64_t>(s) * a.num_kv_heads + kvh) * kRowBytes + 16 * col;
+    nk_row = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.new_k) + src);
+    nv_row = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.new_v) + src);
+  }
 
   // q slice of this lane, pre-scaled into base-2 units
   float qv[EPL];
@@ -182,15 +192,62 @@ __device__ __forceinline__ void decode_valu_body(const pkv_decode_args& a, uint3
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
 
+  // Online-softmax update with the tile of tokens t0 .. t0+kBlock-1 (rows past
+  // the context are masked).
+  auto update = [&](const u32x4 (&kt)[NLD], const u32x4 (&vt)[NLD], int32_t t0) {
+    const bool full = t0 + kBlock <= ctx_loop;
+    float sc[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      float kf[EPL];
+      Elem<T>::unpack(kt[i], kf);
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) part = fmaf(qv[e], kf[e], part);
+      sc[i] = group_sum<LPR>(part);
+    }
+    float mt = m;
+    if (full) {
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) mt = fmaxf(mt, sc[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const bool valid = t0 + i * TPL + row < ctx_loop;
+        sc[i] = valid ? sc[i] : -INFINITY;
+        mt = fmaxf(mt, sc[i]);
+      }
+    }
+    const float alpha = fast_exp2(m - mt);
+    m = mt;
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const float pr = fast_exp2(sc[i] - m);
+      l += pr;
+      float vf[EPL];
+      Elem<T>::unpack(vt[i], vf);
+      if (!full) {
+        const bool valid = t0 + i * TPL + row < ctx_loop;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vf[e] = valid ? vf[e] : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(pr, vf[e], acc[e]);
+    }
+  };
+
   // The block ids of the next iteration are fetched (scalar loads) while the
   // current iteration's tiles are in flight.
   int32_t nxt[BPI];
 #pragma unroll
   for (int bi = 0; bi < BPI; ++bi) {
     const int32_t j = blk_begin + wave + bi * kValuWaves;
-    nxt[bi] = j < blk_end ? table[j] : 0;
+    nxt[bi] = j < loop_end ? table[j] : 0;
   }
-  for (int32_t j0 = blk_begin + wave; j0 < blk_end; j0 += kValuWaves * BPI) {
+  for (int32_t j0 = blk_begin + wave; j0 < loop_end; j0 += kValuWaves * BPI) {
     u32x4 kt[BPI][NLD], vt[BPI][NLD];
     int32_t tb[BPI];
 #pragma unroll
@@ -198,107 +255,68 @@ __device__ __forceinline__ void decode_valu_body(const pkv_decode_args& a, uint3
       const int32_t j = j0 + bi * kValuWaves;
       int32_t b = nxt[bi];
       tb[bi] = -1;
-      if (j < blk_end) {
-        const bool id_bad = static_cast<uint32_t>(b) >= static_cast<uint32_t>(a.num_blocks);
-        if (id_bad) { bad = true; b = 0; }
+      if (j < loop_end) {
+        if (static_cast<uint32_t>(b) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; b = 0; }
         tb[bi] = j * kBlock;
         const u32x4* kp = reinterpret_cast<const u32x4*>(kc + b * block_bytes + head_off);
         const u32x4* vp = reinterpret_cast<const u32x4*>(vc + b * block_bytes + head_off);
         // rows past the context (the tail of a sequence's last block) are not
         // loaded: those lanes read nothing and hold 0
-        const int32_t valid = ctx - j * kBlock;
-        int mode = 0;       // 0: all rows from the pool; 1: the new token's block; 2: a wrong slot
-        if (j == nblk - 1) {
-          if (new_slot >= 0) mode = (!id_bad && new_slot == static_cast<int64_t>(b) * kBlock + last_row) ? 1 : 2;
-        }
-        if (mode == 0) {
+        const int32_t valid = ctx_loop - j * kBlock;
 #pragma unroll
-          for (int i = 0; i < NLD; ++i)
-            kt[bi][i] = i * TPL + row < valid ? __builtin_nontemporal_load(kp + i * 64 + lane) : u32x4{0, 0, 0, 0};
+        for (int i = 0; i < NLD; ++i)
+          kt[bi][i] = i * TPL + row < valid ? __builtin_nontemporal_load(kp + i * 64 + lane) : u32x4{0, 0, 0, 0};
 #pragma unroll
-          for (int i = 0; i < NLD; ++i)
-            vt[bi][i] = i * TPL + row < valid ? __builtin_nontemporal_load(vp + i * 64 + lane) : u32x4{0, 0, 0, 0};
-        } else if (mode == 2) {
-          bad = true;       // not token ctx-1's slot: NaN rows, nothing stored
-#pragma unroll
-          for (int i = 0; i < NLD; ++i) { kt[bi][i] = u32x4{0, 0, 0, 0}; vt[bi][i] = u32x4{0, 0, 0, 0}; }
-        } else {
-          // the block of the new token: its row comes from the new K/V and is
-          // stored into the pool by the lanes that hold it
-          const char* nk = reinterpret_cast<const char*>(a.new_k) + new_src;
-          const char* nv = reinterpret_cast<const char*>(a.new_v) + new_src;
-#pragma unroll
-          for (int i = 0; i < NLD; ++i) {
-            const int r = i * TPL + row;
-            if (r < last_row) {
-              kt[bi][i] = __builtin_nontemporal_load(kp + i * 64 + lane);
-              vt[bi][i] = __builtin_nontemporal_load(vp + i * 64 + lane);
-            } else if (r == last_row) {
-              kt[bi][i] = *reinterpret_cast<const u32x4*>(nk);
-              vt[bi][i] = *reinterpret_cast<const u32x4*>(nv);
-              if (writer) {
-                *const_cast<u32x4*>(kp + i * 64 + lane) = kt[bi][i];
-                *const_cast<u32x4*>(vp + i * 64 + lane) = vt[bi][i];
-              }
-            } else {
-              kt[bi][i] = u32x4{0, 0, 0, 0};
-              vt[bi][i] = u32x4{0, 0, 0, 0};
-            }
-          }
-        }
+        for (int i = 0; i < NLD; ++i)
+          vt[bi][i] = i * TPL + row < valid ? __builtin_nontemporal_load(vp + i * 64 + lane) : u32x4{0, 0, 0, 0};
       }
     }
 #pragma unroll
     for (int bi = 0; bi < BPI; ++bi) {
       const int32_t j = j0 + kValuWaves * BPI + bi * kValuWaves;
-      nxt[bi] = j < blk_end ? table[j] : 0;
+      nxt[bi] = j < loop_end ? table[j] : 0;
     }
 #pragma unroll
     for (int bi = 0; bi < BPI; ++bi) {
       if (tb[bi] < 0) break;
-      const bool full = tb[bi] + kBlock <= ctx;
-      float sc[NLD];
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        float kf[EPL];
-        Elem<T>::unpack(kt[bi][i], kf);
-        float part = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) part = fmaf(qv[e], kf[e], part);
-        sc[i] = group_sum<LPR>(part);
-      }
-      float mt = m;
-      if (full) {
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) mt = fmaxf(mt, sc[i]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < NLD; ++i) {
-          const bool valid = tb[bi] + i * TPL + row < ctx;
-          sc[i] = valid ? sc[i] : -INFINITY;
-          mt = fmaxf(mt, sc[i]);
-        }
-      }
-      const float alpha = fast_exp2(m - mt);
-      m = mt;
-      l *= alpha;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) {
-        const float pr = fast_exp2(sc[i] - m);
-        l += pr;
-        float vf[EPL];
-        Elem<T>::unpack(vt[bi][i], vf);
-        if (!full) {
-          const bool valid = tb[bi] + i * TPL + row < ctx;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) vf[e] = valid ? vf[e] : 0.f;
-        }
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(pr, vf[e], acc[e]);
-      }
+      update(kt[bi], vt[bi], tb[bi]);
     }
+  }
+
+  if (with_new && wave == 0) {
+    // token ctx-1: one more key for the lanes of row 0 (the other rows mask it)
+    const int32_t last_row = (ctx - 1) % kBlock;
+    int32_t b = last_id;
+    const bool id_bad = static_cast<uint32_t>(b) >= static_cast<uint32_t>(a.num_blocks);
+    if (id_bad) { bad = true; b = 0; }
+    char* krow = const_cast<char*>(kc) + b * block_bytes + head_off + last_row * kRowBytes + 16 * col;
+    char* vrow = const_cast<char*>(vc) + b * block_bytes + head_off + last_row * kRowBytes + 16 * col;
+    u32x4 kn = nk_row, vn = nv_row;
+    if (new_slot < 0) {
+      // no new token this step: the token is in the pool
+      kn = *reinterpret_cast<const u32x4*>(krow);
+      vn = *reinterpret_cast<const u32x4*>(vrow);
+    } else if (id_bad || new_slot != static_cast<int64_t>(b) * kBlock + last_row) {
+      bad = true;       // not token ctx-1's slot: NaN rows, nothing stored
+    } else if (h % G == 0 && row == 0) {
+      *reinterpret_cast<u32x4*>(krow) = kn;
+      *reinterpret_cast<u32x4*>(vrow) = vn;
+    }
+    float kf[EPL], vf[EPL];
+    Elem<T>::unpack(kn, kf);
+    Elem<T>::unpack(vn, vf);
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) part = fmaf(qv[e], kf[e], part);
+    const float dot = group_sum<LPR>(part);      // every lane takes part in the row sums
+    const float sc = row == 0 ? dot : -INFINITY;
+    const float mt = fmaxf(m, sc);
+    const float alpha = fast_exp2(m - mt);
+    m = mt;
+    const float pr = fast_exp2(sc - m);
+    l = l * alpha + pr;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(pr, vf[e], acc[e] * alpha);
   }
 
   // merge the rows of the wave (lanes that hold the same dims) ...

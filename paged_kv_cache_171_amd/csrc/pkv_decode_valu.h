@@ -89,7 +89,8 @@ template <> struct Elem<uint16_t> {  // bf16 bits
 // traffic.  Masked tokens (past the context) are removed by select, never by
 // multiplying with 0, so NaN in unused slots cannot leak.  A unit of a
 // sequence with one partition writes the output row; otherwise it writes a
-// partial (max, sum, unnormalised accumulator) for merge_partitions_kernel.
+// partial (max, sum, unnormalised accumulator), and the row's last unit to
+// finish merges the row (else merge_partitions_kernel does).
 // ---------------------------------------------------------------------------
 template <typename T, int D, int BS>
 struct DecodeShape {

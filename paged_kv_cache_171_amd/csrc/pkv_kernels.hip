@@ -93,14 +93,14 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(pkv_decode_args a) {
 }
 
 // ---------------------------------------------------------------------------
-// Partition merge, one workgroup per (s, h), for contexts cut into more than
-// one partition:  M = max_p m_p,  out = sum_p acc_p 2^(m_p - M) / sum_p l_p
-// 2^(m_p - M) -- the log-sum-exp identity that makes the split softmax equal
-// the unsplit one.  A separate launch keeps the decode kernel free of
-// cross-workgroup synchronisation: a device-scope release/acquire per split
-// unit writes back and invalidates an XCD L2 and costs far more (measured 2x on
-// the 13B-shaped batch) than this launch, whose kernel boundary publishes all
-// partials at once.  It is launched only when some context can be split.
+// Partition merge as a launch of its own, one workgroup per (s, h), for
+// contexts cut into more than one partition:  M = max_p m_p,  out = sum_p
+// acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M) -- the log-sum-exp identity that
+// makes the split softmax equal the unsplit one.  The decode kernels normally
+// merge a split row themselves (its last unit to finish, counted on a ticket;
+// pkvd::arrive_last); this launch serves the rows a ticket cannot count (more
+// than 65535 partitions) and is launched only when no tickets are given and
+// some context can be split.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(D) void merge_partitions_kernel(pkv_decode_args a) {

@@ -130,8 +130,8 @@ __device__ __forceinline__ bf16x8 join(const s16x4& lo, const s16x4& hi) {
 //     O^T += V^T P^T with 16x16x16 MFMAs (P^T is exactly the S^T of the block).
 // Each wave keeps an online softmax per row; the waves are merged through LDS
 // with the log-sum-exp rule, and the unit writes the output rows (one-partition
-// sequences) or (max, sum, accumulator) partials for the merge kernel -- the
-// same partial format as the VALU decode kernel.
+// sequences) or (max, sum, accumulator) partials -- the same partial format as
+// the VALU decode kernel -- which the row's last unit to finish merges.
 // ---------------------------------------------------------------------------
 typedef short s16x4v __attribute__((ext_vector_type(4)));
 

@@ -61,6 +61,22 @@ def test_zero_query_gives_mean_of_values():
     np.testing.assert_allclose(o[0, 0], rows.mean(axis=0), rtol=0, atol=1e-14)
 
 
+def test_identical_keys_give_mean_of_values():
+    # every key the same: every score the same, so the softmax is uniform
+    # whatever the query
+    rng = np.random.default_rng(11)
+    k, v, tables = _pool_with_context(rng, [29], 2, 64, "f32")
+    key = rng.standard_normal((2, 64)).astype(np.float32)
+    for t in range(29):
+        k[tables[0][t // P], :, t % P] = key
+    q = _q(rng, 1, 4, 64, "f32")
+    o = O.decode_attention(q, k, v, tables, [29], 0.125)
+    for h in range(4):
+        g = h // 2
+        rows = np.stack([v[tables[0][t // P], g, t % P] for t in range(29)]).astype(np.float64)
+        np.testing.assert_allclose(o[0, h], rows.mean(axis=0), rtol=0, atol=1e-14)
+
+
 def test_constant_value_rows_give_that_row():
     rng = np.random.default_rng(2)
     k, v, tables = _pool_with_context(rng, [45], 1, 32, "f32")

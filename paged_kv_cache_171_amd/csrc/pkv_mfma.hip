@@ -74,6 +74,18 @@ __device__ __forceinline__ s16x4 lds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
 
+// The same reads from a 32-bit LDS byte address, and a 16-byte LDS read.
+__device__ __forceinline__ s16x4 lds_read_tr_at(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(static_cast<uintptr_t>(addr)));
+}
+__device__ __forceinline__ u32x4 lds_read16_at(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(static_cast<uintptr_t>(addr));
+}
+// The LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
+}
+
 // A wave-uniform 32-bit load through the scalar unit.  Its wait counts only
 // scalar/LDS traffic, so it leaves the direct-to-LDS copies (counted with the
 // vector loads) in flight; a plain load issued after such copies would be a
@@ -794,23 +806,44 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void prefill_chunk_mfma_kernel(
     }
   }
 
+  const float c2 = a.scale_log2;                 // > 0
+  const float rescale_raw = kRescaleLog2 / c2;   // kRescaleLog2 in raw score units
+
+  // m: the row's running maximum in log2 units (scores times c2); thr: the raw
+  // score above which it is raised (the maximum it was last set from, plus
+  // rescale_raw)
   f32x4 o[kTiles][DC];
-  float m[kTiles], lsum[kTiles];
+  float m[kTiles], thr[kTiles], lsum[kTiles];
 #pragma unroll
   for (int tt = 0; tt < kTiles; ++tt) {
     m[tt] = kNegBig;
+    thr[tt] = kNegBig;
     lsum[tt] = 0.f;
 #pragma unroll
     for (int c = 0; c < DC; ++c) o[tt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   // per-lane LDS offsets within a stage: K A-operand rows (key n of each block,
-  // slot 4c + g) and the V transposed-read rows (key 4g + n/4)
+  // slot 4c + g) and the V transposed-read rows (key 4g + n/4); the V addresses
+  // are those of stage 0, the other stages sit at fixed offsets from them
   const int k_row = n * RB;
   const int k_sw = kswz<D>(n);
   const int tr_row = 4 * g + (n >> 2);
   const int tr_sw = vswz<D>(tr_row);
   const int tr_k0 = (n & 3) >> 1;
-  const float c2 = a.scale_log2;                 // > 0
+  // (held opaque, so that each stays one register and a stage's reads take
+  // the stage offset as an immediate instead of re-adding its parts per pair)
+  const uint32_t ring0 = lds_addr(ring[0]);
+  uint32_t k_addr[KC], tr_addr[DC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) {
+    k_addr[c] = ring0 + k_row + 16 * ((4 * c + g) ^ k_sw);
+    asm volatile("" : "+v"(k_addr[c]));
+  }
+#pragma unroll
+  for (int c = 0; c < DC; ++c) {
+    tr_addr[c] = ring0 + 2 * kTileBytes + tr_row * RB + 8 * (n & 1) + 16 * ((2 * c + tr_k0) ^ tr_sw);
+    asm volatile("" : "+v"(tr_addr[c]));
+  }
 
   // One pair of blocks (32 keys) from its stage.
   auto pair = [&](int32_t pp, const char* stage) {
@@ -820,14 +853,17 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void prefill_chunk_mfma_kernel(
     for (int tt = 0; tt < kTiles; ++tt) {
       if (key0 >= tile_lim[tt]) continue;
       // S^T = K Q^T for the two blocks, K straight from LDS in the A layout
+      const uint32_t stage_off = static_cast<uint32_t>(stage - ring[0]);
+      // the matrix-core phases (K Q^T here, P V below) run at a raised issue
+      // priority, so that a SIMD whose other waves are in their softmax keeps
+      // its matrix core fed and their vector instructions fill the gaps
+      __builtin_amdgcn_s_setprio(1);
       f32x4 acc[2];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         bf16x8 ka[KC];
 #pragma unroll
-        for (int c = 0; c < KC; ++c)
-          ka[c] = as_bf16x8(*reinterpret_cast<const u32x4*>(stage + b * kTileBytes + k_row +
-                                                             16 * ((4 * c + g) ^ k_sw)));
+        for (int c = 0; c < KC; ++c) ka[c] = as_bf16x8(lds_read16_at(k_addr[c] + stage_off + b * kTileBytes));
         acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < KC; ++c) acc[b] = mfma(ka[c], qb[tt][c], acc[b]);
@@ -844,50 +880,52 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void prefill_chunk_mfma_kernel(
           for (int jj = 0; jj < 4; ++jj)
             if (key0 + b * kBlock + 4 * g + jj >= lim[tt]) sc[4 * b + jj] = -INFINITY;
       }
-      // NaN-propagating maximum: three-input instructions, no operand quieting
-      float mx = __builtin_elementwise_maximum(
+      __builtin_amdgcn_s_setprio(0);
+      // the lane's maximum (NaN-propagating three-input instructions, no
+      // operand quieting) against the row's threshold: only when some score
+      // passes it are the row maxima formed and the row maximum raised (with
+      // the rescale); the branch is uniform over the wave
+      const float lane_mx = __builtin_elementwise_maximum(
           __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[0], sc[1]),
                                         __builtin_elementwise_maximum(sc[2], sc[3])),
           __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[4], sc[5]),
                                         __builtin_elementwise_maximum(sc[6], sc[7])));
-      mx = max_over_rows(mx) * c2;
-      // raise the row maximum (and rescale) only when a score passes it by
-      // more than kRescaleLog2; the branch is uniform over the wave
-      const bool up = mx > m[tt] + kRescaleLog2;
-      if (__builtin_amdgcn_ballot_w64(up)) {
-        const float mnew = up ? mx : m[tt];
+      if (__builtin_amdgcn_ballot_w64(lane_mx > thr[tt])) {
+        const float mx = max_over_rows(lane_mx);
+        const bool up = mx > thr[tt];            // the same in the four lanes of a row
+        const float mnew = up ? mx * c2 : m[tt];
         const float alpha = fast_exp2(m[tt] - mnew);
         m[tt] = mnew;
+        thr[tt] = up ? mx + rescale_raw : thr[tt];
         lsum[tt] *= alpha;
 #pragma unroll
         for (int c = 0; c < DC; ++c) o[tt][c] *= alpha;
       }
       // V^T for the 32 keys by transposed reads, issued before the exponentials
       bf16x8 va[DC];
-      const char* trb = stage + 2 * kTileBytes + tr_row * RB + 8 * (n & 1);
 #pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        const int slot = 16 * ((2 * c + tr_k0) ^ tr_sw);
-        va[c] = join(lds_read_tr(trb + slot), lds_read_tr(trb + kTileBytes + slot));
-      }
+      for (int c = 0; c < DC; ++c)
+        va[c] = join(lds_read_tr_at(tr_addr[c] + stage_off), lds_read_tr_at(tr_addr[c] + stage_off + kTileBytes));
       u32x4 phw, plw;
-      float ps = 0.f;
+      float ps[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const f32x2 pr = {fast_exp2(fmaf(sc[2 * k], c2, -m[tt])), fast_exp2(fmaf(sc[2 * k + 1], c2, -m[tt]))};
-        ps += pr[0] + pr[1];
+        ps[k] = pr[0] + pr[1];
         const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
         const f32x2 lo = {pr[0] - __uint_as_float(h << 16), pr[1] - __uint_as_float(h & 0xFFFF0000u)};
         phw[k] = h;
         plw[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
       }
-      lsum[tt] += ps;
+      lsum[tt] += (ps[0] + ps[1]) + (ps[2] + ps[3]);
       const bf16x8 ph = as_bf16x8(phw), pl = as_bf16x8(plw);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int c = 0; c < DC; ++c) {
         f32x4 t = mfma(va[c], ph, o[tt][c]);
         o[tt][c] = mfma(va[c], pl, t);
       }
+      __builtin_amdgcn_s_setprio(0);
     }
   };
 

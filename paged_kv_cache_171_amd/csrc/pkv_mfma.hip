@@ -113,10 +113,10 @@ __device__ __forceinline__ void scalar_load_wait(int32_t& v0, int32_t& v1) {
 // tell LDS stages apart, does not drain every outstanding copy before each LDS
 // read; the caller waits on vmcnt itself (copies complete in issue order) and
 // issues no compiler-visible vector load between a copy and its wait.
+// The LDS destination goes in m0, which the compiler loads for the statement
+// (a register operand, so it knows m0 is taken).
 __device__ __forceinline__ void copy16_to_lds(const void* src, const void* lds) {
-  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) const char*)(lds)));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m0) : "memory", "m0");
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds_addr(lds)) : "memory");
 }
 
 __device__ __forceinline__ bf16x8 join(const s16x4& lo, const s16x4& hi) {
@@ -673,10 +673,7 @@ __device__ __forceinline__ float max_over_rows(float x) {
 // per-lane 32-bit offset (the scalar-base form of the instruction); lane l's
 // bytes land at LDS address lds + 16 l.
 __device__ __forceinline__ void copy16_to_lds_at(const char* base, uint32_t voff, const void* lds) {
-  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) const char*)(lds)));
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "s"(m0)
-               : "memory", "m0");
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "{m0}"(lds_addr(lds)) : "memory");
 }
 
 // A row's running maximum is raised only when a score exceeds it by more than

@@ -252,8 +252,9 @@ def secondary(args):
                     "shared_decode_unique_gbps": round(res["kv_unique_bytes"] / sh_us / 1e3, 1),
                     "shared_decode_hbm_peak_frac": round(res["kv_unique_bytes"] / sh_us / 1e3 / HBM_PEAK_GBPS, 4),
                     "shared_over_plain_speedup": round(dec_us / sh_us, 3),
-                    "shared_kernels": "shared_plan_kernel + plan_kernel + decode_group_mfma_kernel<128,true> "
-                                      "(shared prompt blocks) + decode_valu_kernel (tails) + merge"})
+                    "shared_kernels": "shared_plans_kernel (shared prefixes, then the tails' plan) + "
+                                      "decode_shared_fused_kernel (shared prompt blocks on the matrix cores, "
+                                      "each sample's tail on the vector ALUs, merge of split rows inside)"})
     if name == "long":
         cs = w.chunk_seqs
         clens = np.array([alloc.seq_block_table(s)[1] for s in cs], dtype=np.int32)

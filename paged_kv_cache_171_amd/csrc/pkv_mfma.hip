@@ -565,17 +565,18 @@ __device__ __forceinline__ void shared_plan_body(const pkv_decode_args& a, const
           const int32_t j = j0 + lane;
           bool eq = true;
           if (j < lim) {
-            // every member's entry is loaded before any is compared, four at a
-            // time, so the loads overlap instead of waiting on each other
+            // the members' entries are loaded eight at a time, all before any
+            // is compared, so the loads overlap instead of waiting on each other
+            // (past the last member the last one is read again)
             const int32_t ref = t0[j];
             const int32_t* col = a.block_tables + j;
-            int32_t m = b + 1;
-            for (; m + 3 < e; m += 4) {
-              const int32_t x0 = col[static_cast<int64_t>(m) * MB], x1 = col[static_cast<int64_t>(m + 1) * MB];
-              const int32_t x2 = col[static_cast<int64_t>(m + 2) * MB], x3 = col[static_cast<int64_t>(m + 3) * MB];
-              eq = eq & (x0 == ref) & (x1 == ref) & (x2 == ref) & (x3 == ref);
+            for (int32_t m0 = b + 1; m0 < e; m0 += 8) {
+              int32_t x[8];
+#pragma unroll
+              for (int i = 0; i < 8; ++i) x[i] = col[static_cast<int64_t>(min(m0 + i, e - 1)) * MB];
+#pragma unroll
+              for (int i = 0; i < 8; ++i) eq = eq & (x[i] == ref);
             }
-            for (; m < e; ++m) eq = eq & (col[static_cast<int64_t>(m) * MB] == ref);
           }
           const uint64_t differ = __ballot(!eq);
           if (differ) {

@@ -417,6 +417,57 @@ def test_prefill_chunks(seed, ctxs, nqs, hq, hkv, d):
     assert err <= TOL["bf16"], err
 
 
+def _bf16_to_f32(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _raises(scores_log2, threshold=8.0, step=32):
+    """How often a running maximum kept within `threshold` of the scores seen
+    so far is raised, keys taken `step` at a time (scores in log2 units)."""
+    top, n = -np.inf, 0
+    for j in range(0, len(scores_log2), step):
+        m = float(np.max(scores_log2[j:j + step]))
+        if m > top + threshold:
+            top, n = m, n + 1
+    return n
+
+
+def test_prefill_rows_whose_maximum_rises_through_the_keys():
+    """Keys that rise along the context (each row's running maximum is raised
+    and its accumulators rescaled again and again) and scores spread over
+    hundreds of log2 units, so early keys' probabilities underflow."""
+    ctxs, nqs = [900, 333], [300, 77]
+    w = W.random_prefill(67, ctxs, nqs, 8, 2, 128)
+    rng = np.random.default_rng(67)
+    q = np.abs(rng.standard_normal((int(sum(nqs)), 8, 128), dtype=np.float32))
+    w.chunk_q = W.f32_to_bf16_bits(q)
+    pos = np.concatenate([np.arange(c) for c in ctxs]).astype(np.float32)
+    w.k_rows = W.f32_to_bf16_bits(0.5 * _bf16_to_f32(w.k_rows) + (0.02 * pos)[:, None, None])
+    print("case: prefill rising maxima", flush=True)
+    g, r = GpuReplay(w), _oracle(w)
+    # the last query of sequence 0, head 0 (KV head 0): its running maximum is
+    # raised many times
+    k0 = _bf16_to_f32(w.k_rows[:ctxs[0], 0]).astype(np.float64)
+    s_log2 = k0 @ _bf16_to_f32(w.chunk_q[nqs[0] - 1, 0]).astype(np.float64) * float(w.scale) / np.log(2)
+    assert _raises(s_log2) >= 20
+    out, _, _ = g.prefill()
+    assert np.isfinite(out).all()
+    err = float(np.abs(out - _prefill_ref(r, w)).max())
+    assert err <= TOL["bf16"], err
+
+
+def test_prefill_with_a_wide_score_range():
+    """Scale 1 on random rows: scores of standard deviation ~11 (16 log2 units)."""
+    w = W.random_prefill(68, [700, 150, 40], [120, 150, 7], 16, 4, 128)
+    w.scale = np.float32(1.0)
+    print("case: prefill wide scores", flush=True)
+    g, r = GpuReplay(w), _oracle(w)
+    out, _, _ = g.prefill()
+    assert np.isfinite(out).all()
+    err = float(np.abs(out - _prefill_ref(r, w)).max())
+    assert err <= TOL["bf16"], err
+
+
 def test_prefill_nan_in_unused_slots_never_reaches_the_output():
     w = W.random_prefill(65, [70, 33], [20, 33], 8, 2, 128)
     print("case: prefill nan poison", flush=True)

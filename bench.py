@@ -573,10 +573,13 @@ def main():
     op = [out[l].data_ptr() for l in range(L)]
     BF16 = PK.PKV_BF16
 
+    host_us = []
+
     def step(k, events=None):
         """Step k of its phase; events: a (start, end) pair recorded around the
         step's L decode launches."""
         # (a1) host: reserve one slot per sequence, refresh the tables
+        h0 = time.perf_counter()
         slots, pairs = alloc.seq_append_slots_batch(seqs, ones)
         t, ln = alloc.block_tables(seqs, MB)
         tables_h, lens_h, slots_h, pairs_h = views(staging[k])
@@ -587,6 +590,8 @@ def main():
         if n_pairs:
             pairs_h.numpy()[:n_pairs] = pairs
         max_ctx = int(ln.max())
+        if events is not None:
+            host_us.append((time.perf_counter() - h0) * 1e6)
         buf_d.copy_(staging[k], non_blocking=True)
         # the decode plan depends only on this step's lengths: built once, used by every layer
         B._check(lib.pkv_decode_plan(plan.data_ptr(), plan.numel(), lens_d.data_ptr(), S, H, H, MB, P, max_ctx, BF16,
@@ -672,6 +677,10 @@ def main():
                      "kernel": "decode_valu_kernel<bf16,128,16> (with the cache write and the merge of split contexts)",
                      "avg_launch_us": round(avg_launch_us, 2),
                      "alg_bytes_per_launch": round(alg_bytes_total / launches)},
+        # (a1) on the host, while the GPU runs earlier steps: slot reservation
+        # for the 64 sequences and the table refresh in the native allocator
+        # (one binding call each), and the staging fill
+        "host_slots_tables_us_per_step": round(float(np.median(host_us)), 1),
     }
     # a second denominator: what a library streaming read reaches on this GPU
     del k_pools, v_pools

@@ -37,7 +37,11 @@ def test_kernel_source_hash_covers_the_decode_sources():
     assert re.fullmatch(r"[0-9a-f]{16}", bench.kernel_source_hash())
 
 
-def test_cpu_baseline_record():
+def test_cpu_baseline_record(monkeypatch):
+    import pkv_workloads as W
+    full = W.shaped_13b
+    # the record's fields, on 4 of the batch's sequences (the bench times all 64)
+    monkeypatch.setattr(W, "shaped_13b", lambda seed: full(seed=seed, num_seqs=4))
     rec = bench.cpu_baseline(2, 0.2)
     assert rec["kind"] == "oracle" and rec["unit"] == "tokens/s" and rec["cores"] == 1
     assert rec["value"] > 0 and "layers" in rec["sample"]

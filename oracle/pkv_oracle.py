@@ -309,14 +309,21 @@ def prefill_chunk_attention(q: np.ndarray, query_start_loc: Sequence[int], k_poo
         n = b - a
         if n > ctx:
             raise ValueError("chunk longer than its context")
+        if n == 0:
+            continue
         K = storage_to_f64(gather_context(k_pool, block_tables[s], ctx, block_size))
         V = storage_to_f64(gather_context(v_pool, block_tables[s], ctx, block_size))
-        for i in range(n):
-            p = ctx - n + i
-            qi = storage_to_f64(q[a + i])
-            for h in range(Hq):
-                g = kv_head_of(h, Hq, Hkv)
-                out[a + i, h] = softmax_attention(qi[h], K[:p + 1, g, :], V[:p + 1, g, :], scale64)
+        Q = storage_to_f64(q[a:b])                                  # [n, Hq, d]
+        pos = ctx - n + np.arange(n)                                # absolute position of each query
+        visible = np.arange(ctx)[None, :] <= pos[:, None]           # [n, ctx]: key t seen by query i
+        for h in range(Hq):
+            g = kv_head_of(h, Hq, Hkv)
+            # every query's scores against every key of the context, then the
+            # keys after the query's own position taken out of its softmax
+            z = scale64 * (Q[:, h, :] @ K[:, g, :].T)
+            z = np.where(visible, z, -np.inf)
+            w = np.exp(z - z.max(axis=1, keepdims=True))
+            out[a:b, h] = (w @ V[:, g, :]) / w.sum(axis=1, keepdims=True)
     return out
 
 

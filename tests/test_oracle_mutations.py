@@ -185,3 +185,33 @@ def test_write_with_block_and_offset_swapped_is_caught(monkeypatch):
     monkeypatch.setattr(O, "write_cache", bad_write)
     assert _fails(lambda: TC.test_write_then_gather_returns_the_rows_and_touches_nothing_else("f32"),
                   TC.test_forked_samples_equal_unshared_copies)
+
+
+def _widen_as_fp16(a):
+    if a.dtype == np.uint16:
+        return a.view(np.float16).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def _widen_byte_swapped(a):
+    if a.dtype == np.uint16:
+        return (a.byteswap().astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def _widen_truncated_to_f32_low_half(a):
+    if a.dtype == np.uint16:
+        return a.astype(np.uint32).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+@pytest.mark.parametrize("name,mutant", [
+    ("bf16 bits read as fp16", _widen_as_fp16),
+    ("bf16 bytes swapped", _widen_byte_swapped),
+    ("bf16 bits in the low half of a float32", _widen_truncated_to_f32_low_half),
+])
+def test_storage_widening_mutants_are_caught(monkeypatch, name, mutant):
+    import test_oracle_storage as TS
+    monkeypatch.setattr(O, "storage_to_f64", mutant)
+    assert _fails(TS.test_bf16_widening_matches_torch_bfloat16_on_every_bit_pattern,
+                  TS.test_bf16_widening_of_fixed_patterns), name

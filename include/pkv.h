@@ -158,11 +158,11 @@ pkv_status pkv_swap_blocks(void* dst_k_cache, void* dst_v_cache, int32_t dst_num
  * for the decode plan, the partial results of split contexts (the context is
  * cut into partitions of 1024 tokens, 4096 for the matrix-core group kernel)
  * and one 8-byte merge ticket per (sequence, head): the last partition of a
- * row to finish merges the row's partials in the same launch (a second kernel
- * merges them when a row can have more than 65535 partitions).  No
+ * row to finish merges the row's partials in the same launch.  No
  * initialisation is needed (a ticket counts only under the launch's own
- * 48-bit tag, and the merging unit sets it back to 0, so a launch captured in
- * a HIP graph can be replayed); the contents are meaningless between calls.
+ * 40-bit tag, its 24-bit count covers every partition a row can have, and the
+ * merging unit sets it back to 0, so a launch captured in a HIP graph can be
+ * replayed); the contents are meaningless between calls.
  * Calls that share one workspace must not overlap in time (e.g. run them on
  * one stream).
  * ------------------------------------------------------------------------ */

@@ -129,6 +129,27 @@ def _dev(*ts: torch.Tensor) -> None:
             raise ValueError("expected contiguous GPU tensors")
 
 
+def _check_decode_shapes(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         block_tables: torch.Tensor, context_lens: torch.Tensor) -> None:
+    """The library reads q in the pool dtype and writes out as fp32 [S, Hq, d]:
+    refuse mismatched tensors before any call."""
+    if out.dtype != torch.float32:
+        raise TypeError("out must be float32")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError(f"q, k_cache and v_cache must share one dtype (got {q.dtype}, {k_cache.dtype}, "
+                        f"{v_cache.dtype})")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [S, Hq, d] and both pools [NB, Hkv, block_size, d] of one shape")
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError(f"out {tuple(out.shape)} must have q's shape {tuple(q.shape)}")
+    if q.shape[2] != k_cache.shape[3]:
+        raise ValueError("q and the pools must have the same head_dim")
+    if block_tables.dim() != 2 or block_tables.shape[0] != q.shape[0] or context_lens.numel() != q.shape[0]:
+        raise ValueError("block_tables must be [S, MB] and context_lens [S] for the S rows of q")
+
+
 def pkv_version() -> str:
     return _lib.pkv_version().decode()
 
@@ -215,7 +236,7 @@ def pkv_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tens
     """out fp32 [S, Hq, d]; q [S, Hq, d]; block_tables int32 [S, MB]; context_lens int32 [S].
     With ``plan`` (from pkv_decode_plan / plan_for) this calls pkv_attention_decode_planned."""
     _dev(out, q, k_cache, v_cache, block_tables, context_lens)
-    assert out.dtype == torch.float32 and block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+    _check_decode_shapes(out, q, k_cache, v_cache, block_tables, context_lens)
     S, hq, d = q.shape
     nb, hkv, bs, _ = k_cache.shape
     if workspace is None:
@@ -239,7 +260,8 @@ def pkv_attention_decode_append(out: torch.Tensor, q: torch.Tensor, k: torch.Ten
     """pkv_append of each sequence's new token (k, v [S, Hkv, d]; slot_mapping int64 [S], the slot of
     token context_lens[s]-1, or -1) fused into decode attention."""
     _dev(out, q, k, v, slot_mapping, k_cache, v_cache, block_tables, context_lens)
-    assert slot_mapping.dtype == torch.int64 and out.dtype == torch.float32
+    _check_decode_shapes(out, q, k_cache, v_cache, block_tables, context_lens)
+    assert slot_mapping.dtype == torch.int64
     S, hq, d = q.shape
     nb, hkv, bs, _ = k_cache.shape
     assert k.shape == v.shape == (S, hkv, d) and slot_mapping.numel() == S
@@ -267,7 +289,7 @@ def pkv_attention_decode_shared(out: torch.Tensor, q: torch.Tensor, k_cache: tor
     """As pkv_attention_decode; group_start int32 [G+1] on the GPU names groups of
     sequences whose shared leading blocks are read once per group."""
     _dev(out, q, k_cache, v_cache, block_tables, context_lens, group_start)
-    assert out.dtype == torch.float32 and block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+    _check_decode_shapes(out, q, k_cache, v_cache, block_tables, context_lens)
     assert group_start.dtype == torch.int32
     S, hq, d = q.shape
     nb, hkv, bs, _ = k_cache.shape
@@ -288,8 +310,14 @@ def pkv_attention_prefill_chunk(out: torch.Tensor, q: torch.Tensor, query_start_
     """out fp32 [Tq, Hq, d]; q bf16 [Tq, Hq, d]; query_start_loc int32 [S+1]; block_tables int32 [S, MB];
     context_lens int32 [S] (each sequence's chunk is the last tokens of its context)."""
     _dev(out, q, query_start_loc, k_cache, v_cache, block_tables, context_lens)
-    assert out.dtype == torch.float32 and query_start_loc.dtype == torch.int32
+    if out.dtype != torch.float32 or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must be float32 with q's shape [Tq, Hq, d]")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("q, k_cache and v_cache must share one dtype")
+    assert query_start_loc.dtype == torch.int32
     assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+    if query_start_loc.numel() != context_lens.numel() + 1 or block_tables.shape[0] != context_lens.numel():
+        raise ValueError("query_start_loc must be [S+1], block_tables [S, MB] and context_lens [S]")
     tq, hq, d = q.shape
     nb, hkv, bs, _ = k_cache.shape
     _check(_lib.pkv_attention_prefill_chunk(out.data_ptr(), q.data_ptr(), query_start_loc.data_ptr(), tq,

@@ -69,7 +69,7 @@ SharedLayout shared_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim
 }
 }  // namespace
 
-// Merge-ticket epochs: 48-bit, nonzero, a new one for every decode launch.  The
+// Merge-ticket epochs: 40-bit, nonzero, a new one for every decode launch.  The
 // sequence starts at a random point so that a workspace holding another
 // process's tickets cannot match.
 static uint64_t next_merge_epoch() {
@@ -79,7 +79,7 @@ static uint64_t next_merge_epoch() {
     return (static_cast<uint64_t>(rd()) << 32) ^ rd() ^ (t * 0x9E3779B97F4A7C15ull);
   }()};
   for (;;) {
-    const uint64_t e = next.fetch_add(1, std::memory_order_relaxed) & 0xFFFFFFFFFFFFull;
+    const uint64_t e = next.fetch_add(1, std::memory_order_relaxed) & 0xFFFFFFFFFFull;
     if (e != 0) return e;
   }
 }
@@ -281,9 +281,8 @@ static pkv_status decode_impl(const char* fn, float* out, const void* q, const v
   a.part_ml = part ? reinterpret_cast<float*>(ws) : nullptr;
   a.part_acc = part ? reinterpret_cast<float*>(ws + pkv_ws::partial_acc_offset(num_seqs, num_heads, max_context_len))
                     : nullptr;
-  if (part && a.part_tokens < max_context_len && np <= 0xFFFF) {
-    // split contexts are merged inside the decode launch (a ticket counts at
-    // most 0xFFFF partitions of a row; longer rows go to the merge kernel)
+  if (part && part_tokens < max_context_len) {
+    // a context can be split: its rows are merged inside the decode launch
     a.merge_tickets = reinterpret_cast<uint64_t*>(ws + pkv_ws::ticket_offset(num_seqs, num_heads, head_dim,
                                                                              max_context_len));
     a.merge_epoch = next_merge_epoch();
@@ -420,11 +419,9 @@ pkv_status pkv_attention_decode_shared(float* out, const void* q, const void* k_
   a.seq_start = reinterpret_cast<const int32_t*>(ws + l.seq_start);
   a.shared_plan = reinterpret_cast<const int32_t*>(ws + l.shared_plan);
   a.prefix_part_tokens = kPrefixPartTokens;
-  if (l.slots <= 0xFFFF) {
-    // split rows are merged inside the decode launch (see decode_impl)
-    a.merge_tickets = reinterpret_cast<uint64_t*>(ws + l.tickets);
-    a.merge_epoch = next_merge_epoch();
-  }
+  // split rows are merged inside the decode launch
+  a.merge_tickets = reinterpret_cast<uint64_t*>(ws + l.tickets);
+  a.merge_epoch = next_merge_epoch();
   int err = pkv_launch_shared_plans(a, group_start, num_groups, reinterpret_cast<int32_t*>(ws + l.seq_start),
                                     reinterpret_cast<int32_t*>(ws + l.shared_plan), reinterpret_cast<int32_t*>(ws + l.plan),
                                     stream);

@@ -90,7 +90,7 @@ template <> struct Elem<uint16_t> {  // bf16 bits
 // multiplying with 0, so NaN in unused slots cannot leak.  A unit of a
 // sequence with one partition writes the output row; otherwise it writes a
 // partial (max, sum, unnormalised accumulator), and the row's last unit to
-// finish merges the row (else merge_partitions_kernel does).
+// finish merges the row.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int BS>
 struct DecodeShape {
@@ -360,18 +360,10 @@ __device__ __forceinline__ void decode_valu_body(const pkv_decode_args& a, uint3
     if (t < D) a.out[orow + t] = o / L;
     return;
   }
-  // a split context: this partition's (max, sum, accumulator) ...
+  // a split context: this partition's (max, sum, accumulator), merged by the
+  // row's last unit to finish
   const int64_t prow = (static_cast<int64_t>(s) * Hq + h) * a.num_partitions;
   const int64_t pidx = prow + base + p;
-  if (a.merge_tickets == nullptr) {
-    // ... merged by merge_partitions_kernel
-    if (t < D) {
-      a.part_acc[pidx * D + t] = o;
-      if (t == 0) { a.part_ml[2 * pidx] = M; a.part_ml[2 * pidx + 1] = L; }
-    }
-    return;
-  }
-  // ... merged here by the row's last unit to finish
   if (t < D) {
     pkvd::store_coherent(a.part_acc + pidx * D + t, o);
     if (t == 0) { pkvd::store_coherent(a.part_ml + 2 * pidx, M); pkvd::store_coherent(a.part_ml + 2 * pidx + 1, L); }

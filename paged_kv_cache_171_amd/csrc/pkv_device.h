@@ -85,10 +85,6 @@ __device__ __forceinline__ float merge_partials_with(const float* ml, const floa
   return o / L;
 }
 
-__device__ __forceinline__ float merge_partials(const float* ml, const float* acc, int32_t n, int32_t stride) {
-  return merge_partials_with(ml, acc, n, stride, [](const float* p) { return *p; });
-}
-
 // The partition merge inside the decode launch.  The partials of a row whose
 // merge happens in the launch are written and read with agent-scope atomic
 // accesses, which go through to the level shared by all XCDs (each XCD's L2 is
@@ -107,20 +103,24 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-// Every thread of a workgroup calls this after its store_coherent partial
-// stores; the result (uniform) says whether the workgroup's unit is the last of
-// the row's `units` units to arrive, in which case the other units' partials
-// can be read with load_coherent and the ticket is already back at 0.  Each
-// unit takes one ticket step, so the compare-and-swap loop ends after at most
-// `units` rounds.
+// Merge tickets.  A ticket is one 64-bit word per row: (epoch << 24) | units
+// arrived.  The epoch (40 bits, nonzero) is new for every launch, so a word
+// left by another launch counts as 0 arrivals and the buffer never needs
+// clearing.  24 bits count every partition a row can have: a context of at
+// most 2^31 - 1 tokens in 1024-token partitions is at most 2^21 of them, plus
+// as many shared-prefix partitions.
+constexpr int kTicketCountBits = 24;
+constexpr uint64_t kTicketCountMask = (uint64_t{1} << kTicketCountBits) - 1;
+
 // One arrival on a ticket (one thread): whether it was the last of `units`,
-// in which case the ticket is set back to 0.
+// in which case the ticket is set back to 0.  Each unit takes one ticket step,
+// so the compare-and-swap loop ends after at most `units` rounds.
 __device__ __forceinline__ bool ticket_arrive(uint64_t* ticket, uint64_t epoch, int32_t units) {
-  const uint64_t tag = epoch << 16;
+  const uint64_t tag = epoch << kTicketCountBits;
   uint64_t old = __hip_atomic_load(ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   uint64_t arrived;
   for (;;) {
-    arrived = ((old & ~0xFFFFull) == tag ? (old & 0xFFFFull) : 0) + 1;
+    arrived = ((old & ~kTicketCountMask) == tag ? (old & kTicketCountMask) : 0) + 1;
     if (__hip_atomic_compare_exchange_strong(ticket, &old, tag | arrived, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT))
       break;
@@ -130,6 +130,10 @@ __device__ __forceinline__ bool ticket_arrive(uint64_t* ticket, uint64_t epoch, 
   return last;
 }
 
+// Every thread of a workgroup calls this after its store_coherent partial
+// stores; the result (uniform) says whether the workgroup's unit is the last of
+// the row's `units` units to arrive, in which case the other units' partials
+// can be read with load_coherent and the ticket is already back at 0.
 __device__ __forceinline__ bool arrive_last(uint64_t* ticket, uint64_t epoch, int32_t units, int* sm_flag) {
   wait_vmem();
   __syncthreads();

@@ -106,18 +106,17 @@ struct pkv_decode_args {
   const void* new_k;
   const void* new_v;
   const int64_t* new_slots;
-  // Partition merge inside the decode launch (null: merge_partitions_kernel
-  // runs after it).  One ticket per (sequence, head) row -- for the MFMA group
-  // kernel per (sequence, KV head), at its first query head's row.  A ticket
-  // holds (merge_epoch << 16 | units arrived); a word with another epoch counts
-  // as 0, so the buffer needs no initial clearing; the unit that arrives last
-  // merges the row and sets the word back to 0.  merge_epoch is nonzero, below
-  // 2^48 and new for every launch.
+  // Partition merge inside the decode launch, set whenever a row can have
+  // more than one partial.  One ticket per (sequence, head) row -- for the
+  // MFMA group kernel per (sequence, KV head), at its first query head's row
+  // (pkvd::ticket_arrive: (merge_epoch << 24) | units arrived); the unit that
+  // arrives last merges the row and sets the word back to 0.  merge_epoch is
+  // nonzero, below 2^40 and new for every launch.
   uint64_t* merge_tickets;
   uint64_t merge_epoch;
 };
-// Decode: the main kernel (VALU, or MFMA for bf16 query-head groups of 2..16
-// heads, pkv_mfma.hip), then the partition merge when a context can be split.
+// Decode: the VALU kernel, or the MFMA kernel for bf16 query-head groups of
+// 2..16 heads (pkv_mfma.hip); split contexts are merged inside the launch.
 int pkv_launch_decode(const pkv_decode_args& a, void* stream);
 int pkv_launch_decode_group(const pkv_decode_args& a, void* stream);
 int pkv_launch_plan(int32_t* plan, const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
@@ -131,11 +130,9 @@ int pkv_launch_plan(int32_t* plan, const int32_t* context_lens, int32_t num_seqs
 constexpr int32_t kPrefixPartTokens = 1024;
 int pkv_launch_shared_plans(const pkv_decode_args& a, const int32_t* group_start, int32_t num_groups,
                             int32_t* seq_start, int32_t* shared_plan, int32_t* plan, void* stream);
-// The shared-prefix units and the sequences' own units in one launch (with the
-// merge of split rows inside it when tickets are given, else a merge launch).
+// The shared-prefix units and the sequences' own units in one launch (split
+// rows merged inside it).
 int pkv_launch_shared_fused(const pkv_decode_args& a, void* stream);
-// The partition merge alone (pkv_kernels.hip).
-int pkv_launch_merge(const pkv_decode_args& a, void* stream);
 
 // Causal chunked-prefill attention (pkv_mfma.hip).
 struct pkv_prefill_args {

@@ -1,5 +1,6 @@
 // HIP kernels for gfx950 (MI355X, CDNA4, wave64): cache write, block copy,
-// paged decode attention with a context split, and the partition merge.
+// the decode plan and paged decode attention with a context split (the
+// partition merge runs inside the decode launch).
 //
 // Pages cited:
 //   [CB]  "Batching Continuo y PagedAttention" (cruxr.ai)
@@ -92,34 +93,6 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(pkv_decode_args a) {
   decode_valu_body<T, D, BS>(a, blockIdx.x);
 }
 
-// ---------------------------------------------------------------------------
-// Partition merge as a launch of its own, one workgroup per (s, h), for
-// contexts cut into more than one partition:  M = max_p m_p,  out = sum_p
-// acc_p 2^(m_p - M) / sum_p l_p 2^(m_p - M) -- the log-sum-exp identity that
-// makes the split softmax equal the unsplit one.  The decode kernels normally
-// merge a split row themselves (its last unit to finish, counted on a ticket;
-// pkvd::arrive_last); this launch serves the rows a ticket cannot count (more
-// than 65535 partitions) and is launched only when no tickets are given and
-// some context can be split.
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(D) void merge_partitions_kernel(pkv_decode_args a) {
-  const int64_t sh = blockIdx.x;                       // s * Hq + h
-  const int32_t s = static_cast<int32_t>(sh / a.num_heads);
-  if (!plan_matches(a.plan, a)) return;                // the decode kernel wrote NaN rows
-  const int32_t ctx = a.context_lens[s];
-  if (!len_ok(ctx, a.max_context_len, a.max_blocks_per_seq, a.block_size)) return;
-  // slots 0 .. base-1 hold the shared-prefix partials (if any), then the
-  // sequence's own partitions
-  const int32_t start = pkvd::seq_start_of(a, s);
-  const int32_t base = pkvd::slot_base_of(a, start);
-  const int32_t np_s = (ctx - start + a.part_tokens - 1) / a.part_tokens;
-  if (base == 0 && np_s <= 1) return;
-  const int64_t prow = sh * a.num_partitions;
-  a.out[sh * D + threadIdx.x] =
-      pkvd::merge_partials(a.part_ml + 2 * prow, a.part_acc + prow * D + threadIdx.x, base + np_s, D);
-}
-
 template <typename T, int D>
 int launch_decode_valu(const pkv_decode_args& a, hipStream_t st) {
   const int64_t np = (a.max_context_len + a.part_tokens - 1) / a.part_tokens;
@@ -187,28 +160,8 @@ int pkv_launch_swap_blocks(void* k_dst, void* v_dst, int32_t dst_blocks, const v
 
 int pkv_launch_decode(const pkv_decode_args& a, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  int err;
-  if (pkv_uses_mfma(a.dtype, a.num_heads, a.num_kv_heads, a.block_size)) {
-    err = pkv_launch_decode_group(a, stream);
-  } else if (a.dtype == PKV_BF16) {
-    err = a.head_dim == 128 ? launch_decode_valu<uint16_t, 128>(a, st) : launch_decode_valu<uint16_t, 64>(a, st);
-  } else {
-    err = a.head_dim == 128 ? launch_decode_valu<float, 128>(a, st) : launch_decode_valu<float, 64>(a, st);
-  }
-  // no context can be split (and no shared prefix adds partials), or the
-  // decode kernel merges the split rows itself: no merge launch
-  if (err != hipSuccess || a.merge_tickets != nullptr || (a.seq_start == nullptr && a.max_context_len <= a.part_tokens))
-    return err;
-  return pkv_launch_merge(a, stream);
-}
-
-int pkv_launch_merge(const pkv_decode_args& a, void* stream) {
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const uint32_t rows = static_cast<uint32_t>(a.num_seqs) * a.num_heads;
-  if (a.head_dim == 128) {
-    hipLaunchKernelGGL((merge_partitions_kernel<128>), dim3(rows), dim3(128), 0, st, a);
-  } else {
-    hipLaunchKernelGGL((merge_partitions_kernel<64>), dim3(rows), dim3(64), 0, st, a);
-  }
-  return hipGetLastError();
+  if (pkv_uses_mfma(a.dtype, a.num_heads, a.num_kv_heads, a.block_size)) return pkv_launch_decode_group(a, stream);
+  if (a.dtype == PKV_BF16)
+    return a.head_dim == 128 ? launch_decode_valu<uint16_t, 128>(a, st) : launch_decode_valu<uint16_t, 64>(a, st);
+  return a.head_dim == 128 ? launch_decode_valu<float, 128>(a, st) : launch_decode_valu<float, 64>(a, st);
 }

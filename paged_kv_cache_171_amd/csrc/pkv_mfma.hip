@@ -409,7 +409,6 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
   if (lane == 0) sm_bad[wave] = bad ? 1 : 0;
   __syncthreads();
   const bool any_bad = (sm_bad[0] | sm_bad[1] | sm_bad[2] | sm_bad[3]) != 0;
-  const bool in_launch_merge = !direct && a.merge_tickets != nullptr;
   for (int idx = threadIdx.x; idx < nrows * D; idx += 256) {
     const int r = idx / D, d = idx - (idx / D) * D;
     float M = sm_ml[0][r][0];
@@ -426,10 +425,6 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
     const int64_t row = static_cast<int64_t>(s0 + r / G) * Hq + kvh * G + r % G;
     if (direct) {
       a.out[row * D + d] = acc / L;
-    } else if (!in_launch_merge) {
-      const int64_t pidx = row * a.num_partitions + slot;
-      a.part_acc[pidx * D + d] = acc;
-      if (d == 0) { a.part_ml[2 * pidx] = M; a.part_ml[2 * pidx + 1] = L; }
     } else {
       const int64_t pidx = row * a.num_partitions + slot;
       pkvd::store_coherent(a.part_acc + pidx * D + d, acc);
@@ -438,8 +433,8 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
   }
   (void)kSlots;
   // a split context: the last of the sequence's units (for this KV head) to
-  // finish merges its G rows, else merge_partitions_kernel does
-  if (!in_launch_merge) return;
+  // finish merges its G rows
+  if (direct) return;
   if (!shared_unit) {
     const int64_t row0 = static_cast<int64_t>(s0) * Hq + kvh * G;
     if (!pkvd::arrive_last(a.merge_tickets + row0, a.merge_epoch, nslots, &sm_last)) return;
@@ -1024,9 +1019,7 @@ int pkv_launch_shared_fused(const pkv_decode_args& a, void* stream) {
     if (group_tail) hipLaunchKernelGGL((decode_shared_fused_kernel<64, true>), grid, dim3(256), 0, st, a, sw);
     else hipLaunchKernelGGL((decode_shared_fused_kernel<64, false>), grid, dim3(256), 0, st, a, sw);
   }
-  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  // the split rows are merged inside the launch when tickets are given
-  return a.merge_tickets ? hipSuccess : pkv_launch_merge(a, stream);
+  return hipGetLastError();
 }
 
 int pkv_launch_prefill(const pkv_prefill_args& a, void* stream) {

@@ -3,7 +3,8 @@
 Bit-exact: allocator tables, slots and copy pairs; pool contents after copy and
 append (every byte, untouched ones included).  Attention: max abs error <= 1e-5
 for fp32 K/V and <= 2e-3 for bf16 K/V against the float64 oracle, on every
-workload (full sizes; large ones on sampled sequences), plus edge cases.
+workload at full size and on every output row (all decode rows of all five
+workloads, every query of the long workload's prefill chunks), plus edge cases.
 """
 import math
 
@@ -40,14 +41,27 @@ def _check_state(g, r, w):
     assert np.array_equal(pool_to_host(g.v_pool), r.v_pool)
 
 
-def _attn_err(g, r, w, sample=None):
+def _attn_err(g, r, w):
+    """Max abs error of every decode row of the workload against the oracle."""
     out, tables, lens = g.decode()
-    seqs = range(len(w.decode_seqs)) if sample is None else sample
-    idx = list(seqs)
-    ref = O.decode_attention(w.q[idx], r.k_pool, r.v_pool, [r.alloc.block_table(w.decode_seqs[i]) for i in idx],
-                             [r.alloc.num_tokens(w.decode_seqs[i]) for i in idx], w.scale)
+    ref = O.decode_attention(w.q, r.k_pool, r.v_pool, [r.alloc.block_table(s) for s in w.decode_seqs],
+                             [r.alloc.num_tokens(s) for s in w.decode_seqs], w.scale)
+    assert out.shape == ref.shape
     assert np.isfinite(out).all()
-    return float(np.abs(out[idx] - ref).max())
+    return float(np.abs(out - ref).max())
+
+
+_BIG = {}
+
+
+def _big(name):
+    """The full-size workload, its GPU replay and its oracle replay, built once
+    per module (the long workload serves both its decode and its prefill test)."""
+    if name not in _BIG:
+        _BIG.clear()
+        w = {"gqa": W.gqa, "fork": W.parallel_sampling, "long": W.long_mix}[name]()
+        _BIG[name] = (w, GpuReplay(w), _oracle(w))
+    return _BIG[name]
 
 
 def test_tiny_workload_bit_exact_state_and_attention():
@@ -60,11 +74,14 @@ def test_tiny_workload_bit_exact_state_and_attention():
 
 
 SMALL = [
-    # seed, S, max_ctx, Hq, Hkv, d, dtype  (512-token partitions: > 512 exercises the merge)
+    # seed, S, max_ctx, Hq, Hkv, d, dtype.  Contexts are cut into 1024-token
+    # partitions on the VALU kernel (MHA, fp32, groups above 16) and 4096-token
+    # ones on the MFMA group kernel (bf16, 2..16 heads per KV head); a longer
+    # context exercises the merge.
     (11, 7, 70, 4, 4, 64, "f32"),
     (12, 9, 1300, 2, 2, 128, "f32"),
-    (13, 5, 1100, 8, 2, 128, "bf16"),
-    (14, 12, 520, 4, 4, 128, "bf16"),
+    (13, 5, 4700, 8, 2, 128, "bf16"),
+    (14, 12, 1100, 4, 4, 128, "bf16"),
     (15, 6, 1700, 4, 1, 64, "bf16"),
     (16, 10, 2100, 2, 2, 64, "f32"),
     (17, 3, 33, 16, 16, 128, "bf16"),
@@ -170,33 +187,28 @@ def test_13b_steps_in_the_bench_launch_configuration():
         assert np.array_equal(pool_to_host(gk), ok) and np.array_equal(pool_to_host(gv), ov)
 
 
-def test_gqa_batch_full_sampled():
-    w = W.gqa()
-    print("case: gqa S=256 H=64/8", flush=True)
-    g, r = GpuReplay(w), _oracle(w)
+def test_gqa_batch_all_rows():
+    print("case: gqa S=256 H=64/8, every row", flush=True)
+    w, g, r = _big("gqa")
     _check_state(g, r, w)
-    lens = [r.alloc.num_tokens(s) for s in w.decode_seqs]
-    sample = sorted(set([int(np.argmax(lens)), int(np.argmin(lens))] + list(range(0, 256, 37))))
-    err = _attn_err(g, r, w, sample)
+    err = _attn_err(g, r, w)
     assert err <= TOL["bf16"], err
 
 
-def test_parallel_sampling_full():
-    w = W.parallel_sampling()
-    print("case: fork 32x8", flush=True)
-    g, r = GpuReplay(w), _oracle(w)
+def test_parallel_sampling_all_rows():
+    print("case: fork 32x8, every row", flush=True)
+    w, g, r = _big("fork")
     _check_state(g, r, w)
     assert len(g.cow_pairs) == 32 * 7
-    err = _attn_err(g, r, w, sample=list(range(0, 256, 9)) + [255])
+    err = _attn_err(g, r, w)
     assert err <= TOL["bf16"], err
 
 
-def test_long_context_decode_sampled():
-    w = W.long_mix()
-    print("case: long 16x32768 (+chunks)", flush=True)
-    g, r = GpuReplay(w), _oracle(w)
+def test_long_context_decode_all_rows():
+    print("case: long 16x32768 (+chunks), every decode row", flush=True)
+    w, g, r = _big("long")
     _check_state(g, r, w)
-    err = _attn_err(g, r, w, sample=[0, 7, 15])
+    err = _attn_err(g, r, w)
     assert err <= TOL["bf16"], err
 
 
@@ -361,12 +373,16 @@ def test_plan_built_for_other_sizes_gives_nan_rows():
     assert torch.isnan(o).all()
 
 
-@pytest.mark.parametrize("ctxs", [[512, 513, 1024, 1, 16, 17, 1536], [4096, 3, 700]])
-def test_partition_boundaries(ctxs):
-    """Context lengths on and next to the 512-token partition edges."""
-    print(f"case: partition edges {ctxs}", flush=True)
-    rng = np.random.default_rng(sum(ctxs))
-    w = W._plain_decode("edges", 77, ctxs, 4, 4, 128, "bf16")
+@pytest.mark.parametrize("ctxs,hq,hkv", [
+    # the VALU kernel's 1024-token partitions (MHA)
+    ([1023, 1024, 1025, 1, 16, 17, 2047, 2048, 2049, 3073], 4, 4),
+    # the MFMA group kernel's 4096-token partitions (bf16, 4 query heads per KV head)
+    ([4095, 4096, 4097, 3, 8191, 8192, 8193, 700], 8, 2),
+])
+def test_partition_boundaries(ctxs, hq, hkv):
+    """Context lengths on and next to the partition edges of both decode kernels."""
+    print(f"case: partition edges {ctxs} H={hq}/{hkv}", flush=True)
+    w = W._plain_decode("edges", 77, ctxs, hq, hkv, 128, "bf16")
     g, r = GpuReplay(w), _oracle(w)
     err = _attn_err(g, r, w)
     assert err <= TOL["bf16"], err
@@ -498,20 +514,13 @@ def test_prefill_bad_rows():
     assert np.array_equal(out3[:qsl[2]], out[:qsl[2]])
 
 
-def test_long_context_prefill_chunks_sampled():
-    w = W.long_mix()
-    print("case: long mix prefill 4x512 on 8192", flush=True)
-    g, r = GpuReplay(w), _oracle(w)
+def test_long_context_prefill_all_queries():
+    print("case: long mix prefill 4x512 on 8192, every query row", flush=True)
+    w, g, r = _big("long")
     out, _, _ = g.prefill()
     assert np.isfinite(out).all()
-    qsl = w.chunk_query_start_loc
-    err = 0.0
-    for c, s in enumerate(w.chunk_seqs):
-        table, ctx = r.alloc.block_table(s), r.alloc.num_tokens(s)
-        n = qsl[c + 1] - qsl[c]
-        for i in (0, 1, 255, n - 2, n - 1):
-            # a chunk query equals a decode query over the prefix ending at its position
-            ref = O.decode_attention(w.chunk_q[qsl[c] + i][None], r.k_pool, r.v_pool, [table], [ctx - n + i + 1],
-                                     w.scale)
-            err = max(err, float(np.abs(out[qsl[c] + i] - ref[0]).max()))
+    ref = _prefill_ref(r, w)
+    assert out.shape == ref.shape == (4 * 512, 32, 128)
+    err = float(np.abs(out - ref).max())
     assert err <= TOL["bf16"], err
+    _BIG.clear()

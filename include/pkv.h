@@ -239,6 +239,33 @@ pkv_status pkv_attention_decode_append(float* out, const void* q, const void* k,
                                        size_t plan_bytes, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Decode for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments (minus the workspace), kernels, results and error rules as
+ * pkv_attention_decode; the plan, split-context partials and merge tickets go
+ * to a scratch array inside the library, PKV_NOALLOC_SCRATCH_BYTES on every
+ * GPU the library runs on, held until the process ends (located once per
+ * device, on that device's first call).  The call allocates nothing: sizes
+ * whose pkv_attention_workspace_bytes(num_seqs, num_heads, head_dim,
+ * max_context_len) exceeds PKV_NOALLOC_SCRATCH_BYTES give PKV_ERR_INVALID_ARG
+ * with nothing enqueued (e.g. 256 sequences x 64 heads x 128 dims up to
+ * 4096-token contexts fit, and 16 sequences x 32 heads at 32768 tokens).  The scratch needs no clearing between calls
+ * (merge tickets count only under each launch's own tag and end at 0).  All
+ * calls on one GPU share its array: calls that may overlap in time on one GPU
+ * (other streams, other threads) race and give wrong results -- keep them on
+ * one stream.  The scratch belongs to the device of `stream` (of the current
+ * device for NULL).
+ * ------------------------------------------------------------------------ */
+#define PKV_NOALLOC_SCRATCH_BYTES (48u * 1024u * 1024u)
+
+pkv_status pkv_attention_decode_noalloc(float* out, const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                        int32_t num_blocks, int32_t max_context_len, float scale,
+                                        pkv_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------------------
  * Decode with shared prefixes.  [OS] "El regalo extra: compartir memoria" and
  * [IPX] "Dos respuestas a una entrada": the parallel samples of one prompt
  * share the prompt's physical blocks.  The result is that of

@@ -41,6 +41,8 @@ _SIGS = {
     "pkv_attention_workspace_bytes": (_c_sz, [_c_i32, _c_i32, _c_i32, _c_i32]),
     "pkv_attention_decode": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32,
                                       _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_p, _c_sz, _c_p]),
+    "pkv_attention_decode_noalloc": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32,
+                                              _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_p]),
     "pkv_decode_plan_bytes": (_c_sz, [_c_i32, _c_i32]),
     "pkv_decode_plan": (_c_i32, [_c_p, _c_sz, _c_p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_p]),
     "pkv_attention_decode_planned": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32,
@@ -250,6 +252,24 @@ def pkv_attention_decode(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tens
         _dev(plan)
         _check(_lib.pkv_attention_decode_planned(*args, plan.data_ptr(), plan.numel(), workspace.data_ptr(),
                                                  workspace.numel(), _stream(stream)))
+
+
+PKV_NOALLOC_SCRATCH_BYTES = 48 * 1024 * 1024     # include/pkv.h
+
+
+def pkv_attention_decode_noalloc(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                 block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
+                                 scale: float, stream=None) -> None:
+    """pkv_attention_decode without a workspace: the library's own scratch array
+    holds the plan and partials (no allocation anywhere in the call)."""
+    _dev(out, q, k_cache, v_cache, block_tables, context_lens)
+    _check_decode_shapes(out, q, k_cache, v_cache, block_tables, context_lens)
+    S, hq, d = q.shape
+    nb, hkv, bs, _ = k_cache.shape
+    _check(_lib.pkv_attention_decode_noalloc(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                             block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
+                                             S, hq, hkv, d, bs, nb, int(max_context_len), float(scale),
+                                             _dtype_code(k_cache), _stream(stream)))
 
 
 def pkv_attention_decode_append(out: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

@@ -219,14 +219,15 @@ size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_
          partial_bytes(num_seqs, num_heads, head_dim, max_context_len);
 }
 
-static pkv_status decode_impl(const char* fn, float* out, const void* q, const void* k_cache,
-                              const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                              const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
-                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                              int32_t max_context_len, float scale, pkv_dtype dtype, const void* plan,
-                              size_t plan_bytes_given, void* workspace, size_t workspace_bytes,
-                              bool build_plan, void* stream, const void* new_k = nullptr,
-                              const void* new_v = nullptr, const int64_t* new_slots = nullptr) {
+}  // extern "C"
+
+pkv_status pkv_decode_impl(const char* fn, float* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks, int32_t max_context_len, float scale,
+                           pkv_dtype dtype, const void* plan, size_t plan_bytes_given, void* workspace,
+                           size_t workspace_bytes, bool build_plan, void* stream, const void* new_k,
+                           const void* new_v, const int64_t* new_slots) {
   pkv_status st = check_common(fn, num_kv_heads, head_dim, block_size, dtype);
   if (st != PKV_OK) return st;
   if (num_seqs < 0) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: num_seqs < 0", fn);
@@ -305,6 +306,8 @@ static pkv_status decode_impl(const char* fn, float* out, const void* q, const v
   return hip_status(fn, pkv_launch_decode(a, stream));
 }
 
+extern "C" {
+
 pkv_status pkv_attention_decode_append(float* out, const void* q, const void* k, const void* v,
                                        const int64_t* slot_mapping, void* k_cache, void* v_cache,
                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -315,7 +318,7 @@ pkv_status pkv_attention_decode_append(float* out, const void* q, const void* k,
                                        void* stream) {
   const char* fn = "pkv_attention_decode_append";
   if (num_seqs > 0 && !slot_mapping) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: slot_mapping is NULL", fn);
-  return decode_impl(fn, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+  return pkv_decode_impl(fn, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                      num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_context_len, scale, dtype, plan,
                      plan_bytes_given, workspace, workspace_bytes, plan == nullptr, stream, k, v, slot_mapping);
 }
@@ -326,7 +329,7 @@ pkv_status pkv_attention_decode(float* out, const void* q, const void* k_cache, 
                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                 int32_t max_context_len, float scale, pkv_dtype dtype, void* workspace,
                                 size_t workspace_bytes, void* stream) {
-  return decode_impl("pkv_attention_decode", out, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+  return pkv_decode_impl("pkv_attention_decode", out, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
                      context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_context_len, scale, dtype, nullptr, 0, workspace, workspace_bytes, true, stream);
 }
@@ -338,7 +341,7 @@ pkv_status pkv_attention_decode_planned(float* out, const void* q, const void* k
                                         int32_t num_blocks, int32_t max_context_len, float scale,
                                         pkv_dtype dtype, const void* plan, size_t plan_bytes_given,
                                         void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_impl("pkv_attention_decode_planned", out, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+  return pkv_decode_impl("pkv_attention_decode_planned", out, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
                      context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                      max_context_len, scale, dtype, plan, plan_bytes_given, workspace, workspace_bytes, false,
                      stream);
@@ -367,7 +370,7 @@ pkv_status pkv_attention_decode_shared(float* out, const void* q, const void* k_
   // (or with no groups) this is plain decode
   if (dtype != PKV_BF16 || group < 1 || group > kMaxMfmaGroup || block_size != kMfmaBlockSize || num_groups == 0 ||
       num_seqs <= 0)
-    return decode_impl(fn, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+    return pkv_decode_impl(fn, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                        num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_context_len, scale, dtype,
                        nullptr, 0, workspace, workspace_bytes, true, stream);
   pkv_status st = check_common(fn, num_kv_heads, head_dim, block_size, dtype);

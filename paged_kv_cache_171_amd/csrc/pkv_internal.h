@@ -10,6 +10,18 @@
 pkv_status pkv_fail(pkv_status st, const char* msg);
 pkv_status pkv_failf(pkv_status st, const char* fmt, ...);
 
+// Decode with every argument validated here (pkv_api.cpp): the body of
+// pkv_attention_decode, _planned and _append (and of the allocation-free
+// variant, pkv_noalloc.hip); `fn` names the entry point in error messages.
+// With build_plan the plan is built at the start of the workspace.
+pkv_status pkv_decode_impl(const char* fn, float* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks, int32_t max_context_len, float scale,
+                           pkv_dtype dtype, const void* plan, size_t plan_bytes_given, void* workspace,
+                           size_t workspace_bytes, bool build_plan, void* stream, const void* new_k = nullptr,
+                           const void* new_v = nullptr, const int64_t* new_slots = nullptr);
+
 // Kernel launchers (pkv_kernels.hip).  Arguments are already validated; each
 // returns hipSuccess or the launch error as an int.
 int pkv_launch_append(void* k_cache, void* v_cache, const void* k, const void* v,

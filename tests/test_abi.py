@@ -162,6 +162,23 @@ def test_decode_rejects_bad_arguments(P):
     assert "workspace" in _lib(P).pkv_last_error().decode()
 
 
+def test_noalloc_decode_refuses_sizes_beyond_its_scratch_before_any_device_call(P):
+    lib = _lib(P)
+    S, Hq, d, maxctx = 400, 16, 128, 32768
+    assert P.pkv_attention_workspace_bytes(S, Hq, d, maxctx) > P.PKV_NOALLOC_SCRATCH_BYTES
+    st = lib.pkv_attention_decode_noalloc(256, 512, 768, 1024, 1280, 1024, 1536, S, Hq, 2, d, 16, 8, maxctx,
+                                          0.125, 1, None)
+    assert st == P.PKV_ERR_INVALID_ARG
+    assert "scratch" in lib.pkv_last_error().decode()
+    # no rows: nothing to do
+    assert lib.pkv_attention_decode_noalloc(None, None, None, None, None, 4, None, 0, 4, 2, 64, 16, 8, 64, 0.125, 1,
+                                            None) == P.PKV_OK
+    # the stated cap is the header's
+    text = open(HEADER).read()
+    assert re.search(r"#define PKV_NOALLOC_SCRATCH_BYTES \(48u \* 1024u \* 1024u\)", text)
+    assert P.PKV_NOALLOC_SCRATCH_BYTES == 48 * 1024 * 1024
+
+
 def test_workspace_and_plan_sizes(P):
     # plan: 8 header ints + (s, p) for up to ceil(max_ctx / 1024) + 1 units per sequence
     assert P.pkv_decode_plan_bytes(3, 64) == (8 + 2 * 3 * 2) * 4

@@ -1,0 +1,92 @@
+"""pkv_attention_decode_noalloc (through the C ABI) against pkv_attention_decode.
+
+The allocation-free entry point runs the same kernels with the library's own
+scratch array as workspace, so its outputs must equal pkv_attention_decode's
+bit for bit, and the oracle's within the usual tolerance.  Two calls in a row,
+the second with a smaller batch (the scratch keeps the first call's plan,
+partials and tickets), both with contexts split over several partitions;
+then a batch too large for the scratch is refused with nothing launched, and
+the first batch again gives the same bits.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import paged_kv_cache_171_amd as PK  # noqa: E402
+import pkv_workloads as W  # noqa: E402
+from oracle import pkv_oracle as O  # noqa: E402
+from pkv_gpu_driver import GpuReplay, rows_to_device  # noqa: E402
+
+TOL = {"f32": 1e-5, "bf16": 2e-3}
+
+
+def _case(w):
+    g = GpuReplay(w)
+    tables, lens = g.tables(w.decode_seqs)
+    args = (rows_to_device(w.q, "cuda"), g.k_pool, g.v_pool, torch.from_numpy(tables).cuda(),
+            torch.from_numpy(lens).cuda(), int(lens.max()), float(w.scale))
+    r = O.replay(w.ops, w.k_rows, w.v_rows, w.num_blocks, w.num_kv_heads, w.head_dim, w.initial_free_order)
+    ref = O.decode_attention(w.q, r.k_pool, r.v_pool, [r.alloc.block_table(s) for s in w.decode_seqs],
+                             [r.alloc.num_tokens(s) for s in w.decode_seqs], w.scale)
+    return args, ref
+
+
+def _noalloc(args, shape):
+    q, kp, vp, td, ld, mcl, scale = args
+    out = torch.full(shape, -5.0, dtype=torch.float32, device="cuda")
+    PK.pkv_attention_decode_noalloc(out, q, kp, vp, td, ld, mcl, scale)
+    return out
+
+
+def _with_workspace(args, shape):
+    q, kp, vp, td, ld, mcl, scale = args
+    out = torch.full(shape, -6.0, dtype=torch.float32, device="cuda")
+    PK.pkv_attention_decode(out, q, kp, vp, td, ld, mcl, scale)
+    return out
+
+
+def test_noalloc_matches_the_workspace_entry_point_on_consecutive_calls():
+    # first: grouped-query bf16 (matrix-core kernel, 4096-token partitions), contexts up to 9000
+    wa = W.random_small(81, 14, 9000, 8, 2, 128, "bf16", min_ctx=3000)
+    # second, smaller: fp32 MHA (vector-ALU kernel, 1024-token partitions)
+    wb = W.random_small(82, 5, 2600, 4, 4, 64, "f32", min_ctx=900)
+    print("case: noalloc A (14 x <=9000, 8/2 heads, bf16) then B (5 x <=2600, 4/4, f32)", flush=True)
+    a_args, a_ref = _case(wa)
+    b_args, b_ref = _case(wb)
+    assert int(a_args[4].max()) > 4096 and int(b_args[4].max()) > 1024      # both split
+    shape_a, shape_b = tuple(a_args[0].shape), tuple(b_args[0].shape)
+
+    na = _noalloc(a_args, shape_a)
+    nb = _noalloc(b_args, shape_b)
+    wa_out = _with_workspace(a_args, shape_a)
+    wb_out = _with_workspace(b_args, shape_b)
+    torch.cuda.synchronize()
+    assert torch.equal(na, wa_out)
+    assert torch.equal(nb, wb_out)
+    assert float(np.abs(na.cpu().numpy() - a_ref).max()) <= TOL["bf16"]
+    assert float(np.abs(nb.cpu().numpy() - b_ref).max()) <= TOL["f32"]
+
+    # a batch whose workspace would exceed the scratch array is refused before any launch
+    q, kp, vp, td, ld, mcl, scale = a_args
+    S, H = 400, 16
+    need = PK.pkv_attention_workspace_bytes(S, H, 128, 32768)
+    assert need > PK.PKV_NOALLOC_SCRATCH_BYTES
+    big_q = torch.zeros((S, H, 128), dtype=torch.bfloat16, device="cuda")
+    big_out = torch.full((S, H, 128), -7.0, dtype=torch.float32, device="cuda")
+    big_t = torch.zeros((S, td.shape[1]), dtype=torch.int32, device="cuda")
+    big_l = torch.ones(S, dtype=torch.int32, device="cuda")
+    with pytest.raises(PK.PkvError) as e:
+        PK.pkv_attention_decode_noalloc(big_out, big_q, kp, vp, big_t, big_l, 32768, scale)
+    assert e.value.status == PK.PKV_ERR_INVALID_ARG and "scratch" in str(e.value)
+    torch.cuda.synchronize()
+    assert bool((big_out == -7.0).all())
+
+    # the first batch again, after the smaller one: the same bits
+    na2 = _noalloc(a_args, shape_a)
+    torch.cuda.synchronize()
+    assert torch.equal(na2, wa_out)

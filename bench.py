@@ -76,12 +76,14 @@ def parse():
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time for the oracle sample")
-    ap.add_argument("--workload", default="13b", choices=["13b", "gqa", "fork", "long", "swap", "serve", "blocksize"],
+    ap.add_argument("--workload", default="13b",
+                    choices=["13b", "gqa", "fork", "long", "swap", "serve", "blocksize", "probes"],
                     help="13b: the headline decode step (default).  gqa / fork / long: kernel measurements on the "
                          "grouped-query, parallel-sampling and long-context + chunked-prefill batches.  swap: "
                          "block copies between HBM and pinned host memory.  serve: the continuous-batching loop "
                          "(continuous vs static policy) over a request stream.  blocksize: the 13B-shaped decode "
-                         "with 8-, 16- and 32-token blocks")
+                         "with 8-, 16- and 32-token blocks.  probes: streaming-read and decode-access-pattern "
+                         "read ceilings")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run pkv_copy_blocks over 4096 whole blocks (a plain copy of known size, "
                          "used to scale the FETCH_SIZE / WRITE_SIZE counters)")
@@ -106,40 +108,92 @@ def copy_probe():
                       "write_bytes": 2 * n * block_bytes, "launches": 3}), flush=True)
 
 
-def cpu_baseline(seed: int, target_s: float):
-    """The oracle (float64 numpy, one BLAS thread) on a bounded sample: the same
-    64-sequence batch, one layer at a time, repeated until ~target_s seconds;
-    then the same with the BLAS threads at their default (all host cores) for
-    half that time."""
+def _host_bits(t):
+    """A device tensor's storage as numpy (bf16 as its uint16 bits)."""
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def cpu_baseline(layers, tables, lens, scale, target_s: float, tol: float):
+    """The oracle (float64 numpy) on the inputs of the last timed step, as the
+    GPU saw them: for layers taken in turn (first, last, second, ...), that
+    layer's pools, queries and outputs are copied to the host, the oracle
+    decodes all 64 sequences three times on one BLAS thread (best of 3), and
+    its outputs are compared with the GPU's; until ~target_s seconds of oracle
+    time.  Then one layer again with the BLAS threads at their default (all
+    host cores).  layers(l) -> (q, k_pool, v_pool, out) device tensors."""
     from threadpoolctl import threadpool_limits
-    import pkv_workloads as W
     from oracle import pkv_oracle as O
 
-    w = W.shaped_13b(seed=seed)
-    r = O.replay(w.ops, w.k_rows, w.v_rows, w.num_blocks, w.num_kv_heads, w.head_dim, w.initial_free_order)
-    tables = [r.alloc.block_table(s) for s in w.decode_seqs]
-    lens = [r.alloc.num_tokens(s) for s in w.decode_seqs]
-
-    def timed(threads, budget):
-        layers = 0
-        with threadpool_limits(limits=threads):
-            t0 = time.perf_counter()
-            while True:
-                O.decode_attention(w.q, r.k_pool, r.v_pool, tables, lens, w.scale)
-                layers += 1
-                el = time.perf_counter() - t0
-                if el >= budget or layers >= 40:
-                    break
-        return layers, el, len(lens) / (el / layers * 40)
-    layers, el, tok_s = timed(1, target_s)
-    # the same with the BLAS thread pool at its default size (all host cores)
+    n_layers = layers(None)
+    order = []
+    lo, hi = 0, n_layers - 1
+    while lo <= hi:
+        order.append(lo)
+        if hi != lo:
+            order.append(hi)
+        lo, hi = lo + 1, hi - 1
+    best, spent, err, rows, done = [], 0.0, 0.0, 0, 0
+    first = None
+    for l in order:
+        q, kp, vp, out = (_host_bits(x) if i < 3 else x.cpu().numpy() for i, x in enumerate(layers(l)))
+        if first is None:
+            first = (q, kp, vp)
+        ts = []
+        with threadpool_limits(limits=1):
+            for _ in range(3):
+                t0 = time.perf_counter()
+                ref = O.decode_attention(q, kp, vp, tables, lens, scale)
+                ts.append(time.perf_counter() - t0)
+        spent += sum(ts)
+        best.append(min(ts))
+        err = max(err, float(np.abs(out - ref).max()))
+        rows += out.shape[0] * out.shape[1]
+        done += 1
+        if spent >= target_s:
+            break
+    per_layer = float(np.median(best))
+    tok_s = len(lens) / (per_layer * n_layers)
     cores = os.cpu_count() or 1
-    layers_all, el_all, tok_s_all = timed(None, target_s / 2)
-    return {"value": tok_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{layers} of the 40 layers of one decode step (64 seqs, {sum(lens)} cached tokens, "
-                      f"40 heads x 128, bf16 inputs, float64 math), {el:.1f} s; scaled to a 40-layer step",
-            "all_cores": {"value": tok_s_all, "cores": cores,
-                          "sample": f"{layers_all} layers, {el_all:.1f} s, BLAS threads at their default"}}
+    q, kp, vp = first
+    ts = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        O.decode_attention(q, kp, vp, tables, lens, scale)
+        ts.append(time.perf_counter() - t0)
+    tok_s_all = len(lens) / (min(ts) * n_layers)
+    return {"value": round(tok_s, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of the {n_layers} layers of the last timed step (64 seqs, {int(np.sum(lens))} "
+                      f"cached tokens, the GPU's own pools and queries, 40 heads x 128, bf16 inputs, float64 "
+                      f"math), each best of 3 on one thread ({spent:.1f} s in all); median layer time scaled "
+                      f"to a {n_layers}-layer step",
+            "max_abs_err": err, "tol": tol, "rows_checked": rows,
+            "all_cores": {"value": round(tok_s_all, 3), "cores": cores,
+                          "sample": "the first sampled layer, best of 3, BLAS threads at their default"}}
+
+
+def secondary_cpu_check(name, cases, target_s: float):
+    """The oracle on a few rows of a secondary workload's last call (its own
+    inputs, copied from the device): max abs error and the oracle's rate.
+    cases: list of (label, fn) where fn() -> (oracle output, GPU output, rows)."""
+    from threadpoolctl import threadpool_limits
+    res = {"kind": "oracle", "cores": 1}
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        for label, fn in cases:
+            t1 = time.perf_counter()
+            ref, got, rows = fn()
+            dt = time.perf_counter() - t1
+            res[f"{label}_max_abs_err"] = float(np.abs(got - ref).max())
+            res[f"{label}_rows_checked"] = rows
+            res[f"{label}_oracle_rows_per_s"] = round(rows / dt, 2)
+            if time.perf_counter() - t0 > target_s:
+                break
+    res["tol"] = 2e-3
+    res["seconds"] = round(time.perf_counter() - t0, 1)
+    return res
 
 
 def _timed(fn, reps, stream):
@@ -241,20 +295,31 @@ def secondary(args):
         gsd = torch.from_numpy(w.group_start).to(dev)
         sws = torch.empty(max(PK.pkv_attention_decode_shared_workspace_bytes(len(seqs), Hq, D, mcl), 256),
                           dtype=torch.uint8, device=dev)
+        splan = torch.empty(max(PK.pkv_decode_shared_plan_bytes(len(seqs), mcl), 256), dtype=torch.uint8,
+                            device=dev)
 
         def shared_all():
+            # one shared-prefix plan per step, used by every layer
+            PK.pkv_decode_shared_plan(splan, td, ld, gsd, Hq, Hkv, mcl, PK.PKV_BF16)
+            for kp, vp in pools:
+                PK.pkv_attention_decode_shared_planned(out, q, kp, vp, td, ld, mcl, scale, splan, workspace=sws)
+
+        def shared_self_planned():
             for kp, vp in pools:
                 PK.pkv_attention_decode_shared(out, q, kp, vp, td, ld, gsd, mcl, scale, workspace=sws)
         shared_all()
+        shared_self_planned()
         torch.cuda.synchronize()
         sh_us = _timed(shared_all, reps, stream) / L
+        sh_self_us = _timed(shared_self_planned, reps, stream) / L
         res.update({"shared_decode_us_per_layer": round(sh_us, 2),
                     "shared_decode_unique_gbps": round(res["kv_unique_bytes"] / sh_us / 1e3, 1),
                     "shared_decode_hbm_peak_frac": round(res["kv_unique_bytes"] / sh_us / 1e3 / HBM_PEAK_GBPS, 4),
                     "shared_over_plain_speedup": round(dec_us / sh_us, 3),
-                    "shared_kernels": "shared_plans_kernel (shared prefixes, then the tails' plan) + "
-                                      "decode_shared_fused_kernel (shared prompt blocks on the matrix cores, "
-                                      "each sample's tail on the vector ALUs, merge of split rows inside)"})
+                    "shared_self_planned_us_per_layer": round(sh_self_us, 2),
+                    "shared_kernels": "shared_plans_kernel once per step (shared prefixes, then the tails' plan) "
+                                      "+ decode_shared_fused_kernel per layer (shared prompt blocks on the matrix "
+                                      "cores, each sample's tail on the vector ALUs, merge of split rows inside)"})
     if name == "long":
         cs = w.chunk_seqs
         clens = np.array([alloc.seq_block_table(s)[1] for s in cs], dtype=np.int32)
@@ -280,7 +345,57 @@ def secondary(args):
                     "prefill_mfma_peak_frac": round(flops / pf_us / 1e6 / 2500.0, 4),
                     "prefill_tokens_per_s_per_layer": round(int(nq.sum()) / pf_us * 1e6, 1),
                     "prefill_kernel": "prefill_chunk_mfma_kernel"})
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = secondary_oracle_check(args, w, pools[-1], q, td, ld, tables_h, lens_h, scale,
+                                                     locals())
     print(json.dumps(res), flush=True)
+
+
+def secondary_oracle_check(args, w, pool, q, td, ld, tables_h, lens_h, scale, env):
+    """Outside the timed region: the last layer's outputs of a secondary
+    workload recomputed on a few rows (its own device inputs, copied to the
+    host) by the oracle, reported as max abs error; the oracle's rate beside."""
+    import torch
+    import paged_kv_cache_171_amd as PK
+    from oracle import pkv_oracle as O
+    P = 16
+    kp, vp = pool
+    S, Hq, D = q.shape
+    mcl = int(lens_h.max())
+    kh, vh, qh = _host_bits(kp), _host_bits(vp), _host_bits(q)
+    tl = [list(tables_h[i, :-(-int(c) // P)]) for i, c in enumerate(lens_h)]
+    order = np.argsort(-lens_h, kind="stable")
+    rows = sorted(set([int(order[0]), int(order[-1])] + [int(x) for x in
+                      np.random.default_rng(args.seed).choice(S, size=min(S, 14), replace=False)]))
+    cases = []
+
+    def decode_case(outt):
+        def fn():
+            ref = O.decode_attention(qh[rows], kh, vh, [tl[i] for i in rows], [int(lens_h[i]) for i in rows], scale)
+            return ref, outt.cpu().numpy()[rows], len(rows) * Hq
+        return fn
+    plain = torch.empty(S, Hq, D, dtype=torch.float32, device=q.device)
+    PK.pkv_attention_decode(plain, q, kp, vp, td, ld, mcl, scale)
+    cases.append(("decode", decode_case(plain)))
+    if w.name == "fork":
+        shared = torch.empty_like(plain)
+        PK.pkv_attention_decode_shared_planned(shared, q, kp, vp, td, ld, mcl, scale, env["splan"],
+                                               workspace=env["sws"])
+        cases.append(("shared_decode", decode_case(shared)))
+    if w.name == "long":
+        cout, cq, ct, clens, qsl = env["cout"], env["cq"], env["ct"], env["clens"], w.chunk_query_start_loc
+        cqh = _host_bits(cq)
+        ctl = [list(ct[i, :-(-int(c) // P)]) for i, c in enumerate(clens)]
+
+        def prefill_fn():
+            # the first chunk, all of its queries
+            a, b = int(qsl[0]), int(qsl[1])
+            ref = O.prefill_chunk_attention(cqh[a:b], np.array([0, b - a], dtype=np.int32), kh, vh, ctl[:1],
+                                            [int(clens[0])], scale)
+            return ref, cout.cpu().numpy()[a:b], (b - a) * Hq
+        cases.append(("prefill", prefill_fn))
+    torch.cuda.synchronize()
+    return secondary_cpu_check(w.name, cases, args.cpu_seconds)
 
 
 PCIE5_X16_GBPS = 64.0     # host link peak per direction (PCIe 5.0 x16)
@@ -493,6 +608,9 @@ def main():
     if args.workload == "blocksize":
         blocksize_bench(args)
         return
+    if args.workload == "probes":
+        probes_bench(args)
+        return
     if args.workload != "13b":
         secondary(args)
         return
@@ -682,39 +800,140 @@ def main():
         # (one binding call each), and the staging fill
         "host_slots_tables_us_per_step": round(float(np.median(host_us)), 1),
     }
-    # a second denominator: what a library streaming read reaches on this GPU
+    if not args.no_cpu_baseline:
+        # the oracle on the last timed step's inputs, compared with its outputs
+        tables_last, _ = alloc.block_tables(seqs, MB)
+        lens_last = step_lens[-1]
+        tl = [list(tables_last[i, :-(-int(c) // P)]) for i, c in enumerate(lens_last)]
+
+        def layer_tensors(l):
+            return L if l is None else (q[l], k_pools[l], v_pools[l], out[l])
+        res["cpu_baseline"] = cpu_baseline(layer_tensors, tl, lens_last, np.float32(scale), args.cpu_seconds, 2e-3)
+    # a second denominator: the best streaming read measured on this GPU
     del k_pools, v_pools
     torch.cuda.empty_cache()
-    probe = read_probe(stream)
-    res["roofline"]["read_probe_gbps"] = round(probe, 1)
-    res["roofline"]["frac_of_read_probe"] = round(achieved / probe, 4)
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(args.seed, args.cpu_seconds)
+    probe = read_probes(stream)
+    res["roofline"]["read_probe_gbps"] = round(probe["best_gbps"], 1)
+    res["roofline"]["read_probe"] = probe
+    res["roofline"]["frac_of_read_probe"] = round(achieved / probe["best_gbps"], 4)
     print(json.dumps(res), flush=True)
 
 
-def read_probe(stream, reps: int = 10) -> float:
-    """GB/s of a library streaming read on this GPU: torch.mv (the BLAS gemv)
-    of a 65536 x 32768 bf16 matrix (4 GiB, read once; the 64 KiB vector and the
-    128 KiB result are noise), median of `reps` runs timed with HIP events on
-    `stream`.  (torch's sum over the same bytes reaches about half of it.)"""
+def _median_us(fn, stream, reps):
     import torch
-    m = torch.ones(65536, 32768, dtype=torch.bfloat16, device="cuda")
-    v = torch.ones(32768, dtype=torch.bfloat16, device="cuda")
-    torch.mv(m, v)
+    fn()
     torch.cuda.synchronize()
     ts = []
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        torch.mv(m, v)
+        fn()
         e1.record(stream)
         torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1) * 1e-3)
-    nbytes = m.numel() * 2
-    del m, v
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    return float(np.median(ts))
+
+
+STREAM_MODES = {0: "nt x4", 1: "nt x8", 2: "nt x16", 3: "plain x4", 4: "plain x8", 5: "plain x16"}
+
+
+def read_probes(stream, reps: int = 10, gib: int = 4, sweep: bool = False) -> dict:
+    """GB/s of streaming reads of one 4 GiB buffer on this GPU (median of `reps`
+    runs each, HIP events on `stream`): the hand-written stream_read_kernel
+    (libpkv_probes.so) over launch shapes (16-byte loads, 4/8/16 in flight per
+    thread, non-temporal or ordinary, 1024..8192 workgroups of 256 threads),
+    and torch.mv, the BLAS gemv, over the same bytes as a 65536 x 32768 bf16
+    matrix.  The best of all is the measured read ceiling."""
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_171_amd", "libpkv_probes.so"))
+    lib.pkvprobe_stream_read.restype = ctypes.c_int
+    lib.pkvprobe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+    nbytes = gib << 30
+    m = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    grids = (1024, 2048, 4096, 8192) if sweep else (2048, 4096)
+    modes = tuple(STREAM_MODES) if sweep else (1, 4)
+    sink = torch.zeros(max(grids) * 256, dtype=torch.int32, device="cuda")
+    sp = stream.cuda_stream
+    res = {"bytes": nbytes, "stream_read": {}}
+    best = (0.0, None)
+    for mode in modes:
+        for grid in grids:
+            def run(mode=mode, grid=grid):
+                rc = lib.pkvprobe_stream_read(m.data_ptr(), nbytes, grid, mode, sink.data_ptr(), sp)
+                if rc != 0:
+                    raise RuntimeError(f"stream_read launch failed: {rc}")
+            gbps = nbytes / _median_us(run, stream, reps) / 1e3
+            res["stream_read"][f"{STREAM_MODES[mode]} grid {grid}"] = round(gbps, 1)
+            if gbps > best[0]:
+                best = (gbps, f"stream_read_kernel {STREAM_MODES[mode]}, grid {grid}")
+    mat = m.view(65536, nbytes // 2 // 65536)
+    v = torch.ones(mat.shape[1], dtype=torch.bfloat16, device="cuda")
+    mv = nbytes / _median_us(lambda: torch.mv(mat, v), stream, reps) / 1e3
+    res["torch_mv_gbps"] = round(mv, 1)
+    if mv > best[0]:
+        best = (mv, "torch.mv")
+    res["best_gbps"] = best[0]
+    res["best"] = best[1]
+    del m, mat, v, sink
     torch.cuda.empty_cache()
-    return nbytes / float(np.median(ts)) / 1e9
+    return res
+
+
+def probes_bench(args):
+    """The read ceilings behind the decode figures: the streaming-read sweep
+    (read_probes), and a read-only probe of the 13B-shaped decode's own access
+    pattern -- the same 64 lognormal contexts, tables and 40 layer pools of
+    whole 4 KiB K and V tiles, one workgroup per (16-block chunk, head), chunks
+    longest first, nothing computed -- timed over the 40 layers."""
+    import torch
+    import paged_kv_cache_171_amd as PK
+    import pkv_workloads as W
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    res = {"workload": "probes", "read": read_probes(stream, sweep=True)}
+    L, H, D, P = args.layers, 40, 128, 16
+    w = W.shaped_13b(seed=args.seed, with_rows=False)
+    alloc = PK.BlockAllocator(w.num_blocks, P, w.initial_free_order)
+    for op in w.ops:
+        if op[0] == "create":
+            alloc.seq_create()
+        elif op[0] == "append":
+            alloc.seq_append_slots(op[1], op[2])
+    seqs = w.decode_seqs
+    lens = np.array([alloc.seq_block_table(s_)[1] for s_ in seqs], dtype=np.int32)
+    MB = int(-(-lens.max() // P))
+    tables, _ = alloc.block_tables(seqs, MB)
+    nblk = -(-lens // P)
+    work = [(s_, c) for s_ in range(len(seqs)) for c in range(-(-int(nblk[s_]) // 16))]
+    work.sort(key=lambda sc: -min(16, int(nblk[sc[0]]) - 16 * sc[1]))       # full chunks first
+    work_d = torch.tensor(work, dtype=torch.int32, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    pools = [(torch.randn(w.num_blocks, H, P, D, generator=gen, device=dev).to(torch.bfloat16),
+              torch.randn(w.num_blocks, H, P, D, generator=gen, device=dev).to(torch.bfloat16)) for _ in range(L)]
+    td, ld = torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev)
+    sink = torch.zeros(len(work) * H * 4, dtype=torch.int32, device=dev)
+    lib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_171_amd", "libpkv_probes.so"))
+    lib.pkvprobe_tile_read.restype = ctypes.c_int
+    sp = stream.cuda_stream
+
+    def all_layers():
+        for kp, vp in pools:
+            rc = lib.pkvprobe_tile_read(ctypes.c_void_p(kp.data_ptr()), ctypes.c_void_p(vp.data_ptr()),
+                                        ctypes.c_void_p(td.data_ptr()), MB, ctypes.c_void_p(ld.data_ptr()), P,
+                                        ctypes.c_void_p(work_d.data_ptr()), len(work), H, 4096,
+                                        ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(sp))
+            if rc != 0:
+                raise RuntimeError(f"tile_read launch failed: {rc}")
+    us = _median_us(all_layers, stream, max(args.steps, 5)) / L
+    kv = int(lens.sum()) * 2 * H * D * 2
+    res["tile_read"] = {"kernel": "tile_read_kernel (one workgroup per 16-block chunk and head, 4 waves)",
+                        "layers": L, "num_seqs": len(seqs), "cached_tokens": int(lens.sum()),
+                        "kv_bytes_per_layer": kv, "us_per_layer": round(us, 2),
+                        "gbps": round(kv / us / 1e3, 1), "hbm_peak_frac": round(kv / us / 1e3 / HBM_PEAK_GBPS, 4)}
+    print(json.dumps(res), flush=True)
 
 
 if __name__ == "__main__":

@@ -298,6 +298,45 @@ pkv_status pkv_attention_decode_shared(float* out, const void* q, const void* k_
                                        size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * The shared-prefix plan once per step.  Like the decode plan, what
+ * pkv_attention_decode_shared works out before reading K/V -- each group's
+ * shared leading blocks, the shared units, every sequence's own units --
+ * depends only on the tables, lengths and groups, not on the layer, so a
+ * caller may build it once per step and use it for every layer's pools:
+ *
+ *   pkv_decode_shared_plan(plan, ...)                  once per step
+ *   pkv_attention_decode_shared_planned(..., plan, ...) once per layer
+ *
+ * gives the same bits as pkv_attention_decode_shared on every layer.
+ * plan: device buffer of at least pkv_decode_shared_plan_bytes(num_seqs,
+ * max_context_len) bytes, 256-byte aligned; the other arguments as for
+ * pkv_attention_decode_shared (num_heads, num_kv_heads, block_size and dtype
+ * must be those of the decode calls; group_start may be NULL when num_groups
+ * is 0).  Where the shared path does not apply (fp32, more than 16 query
+ * heads per KV head, block_size other than 16) the plan is a plain decode
+ * plan and the planned call runs plain decode.  A plan built for other sizes
+ * or another head grouping makes the planned call write NaN rows.
+ * The planned call's workspace: at least
+ * pkv_attention_decode_shared_workspace_bytes(...) bytes (partials and merge
+ * tickets; no initialisation needed), 256-byte aligned.
+ * ------------------------------------------------------------------------ */
+size_t pkv_decode_shared_plan_bytes(int32_t num_seqs, int32_t max_context_len);
+
+pkv_status pkv_decode_shared_plan(void* plan, size_t plan_bytes, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                                  const int32_t* group_start, int32_t num_groups, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t block_size, int32_t max_context_len, pkv_dtype dtype,
+                                  void* stream);
+
+pkv_status pkv_attention_decode_shared_planned(float* out, const void* q, const void* k_cache, const void* v_cache,
+                                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                               const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                               int32_t num_blocks, int32_t max_context_len, float scale,
+                                               pkv_dtype dtype, const void* plan, size_t plan_bytes,
+                                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Causal chunked-prefill attention.  [UL] "Cómo funciona la planificación a
  * nivel de iteración" and "Límites y técnicas complementarias": a long prompt
  * is prefilled in chunks that run in the same step as other sequences' decode.

@@ -55,6 +55,12 @@ _SIGS = {
     "pkv_attention_decode_shared": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_p, _c_i32,
                                              _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_p,
                                              _c_sz, _c_p]),
+    "pkv_decode_shared_plan_bytes": (_c_sz, [_c_i32, _c_i32]),
+    "pkv_decode_shared_plan": (_c_i32, [_c_p, _c_sz, _c_p, _c_i32, _c_p, _c_i32, _c_p, _c_i32, _c_i32, _c_i32,
+                                        _c_i32, _c_i32, _c_i32, _c_p]),
+    "pkv_attention_decode_shared_planned": (_c_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_p, _c_i32, _c_i32,
+                                                     _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _c_i32, _c_p,
+                                                     _c_sz, _c_p, _c_sz, _c_p]),
     "pkv_attention_prefill_chunk": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_i32, _c_p,
                                              _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
                                              _c_i32, _c_p]),
@@ -321,6 +327,60 @@ def pkv_attention_decode_shared(out: torch.Tensor, q: torch.Tensor, k_cache: tor
                                             S, group_start.data_ptr(), group_start.numel() - 1, hq, hkv, d, bs, nb,
                                             int(max_context_len), float(scale), _dtype_code(k_cache),
                                             workspace.data_ptr(), workspace.numel(), _stream(stream)))
+
+
+def pkv_decode_shared_plan_bytes(num_seqs: int, max_context_len: int) -> int:
+    return int(_lib.pkv_decode_shared_plan_bytes(num_seqs, max_context_len))
+
+
+def pkv_decode_shared_plan(plan: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                           group_start: Optional[torch.Tensor], num_heads: int, num_kv_heads: int,
+                           max_context_len: int, dtype: int, block_size: int = 16, stream=None) -> None:
+    """plan: device uint8 buffer (256-byte aligned) of pkv_decode_shared_plan_bytes(S, max_context_len)."""
+    _dev(plan, block_tables, context_lens)
+    if group_start is not None:
+        _dev(group_start)
+        assert group_start.dtype == torch.int32
+    assert block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32
+    S = context_lens.numel()
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be [S, MB] for the S lengths")
+    ng = group_start.numel() - 1 if group_start is not None else 0
+    _check(_lib.pkv_decode_shared_plan(plan.data_ptr(), plan.numel(), block_tables.data_ptr(), block_tables.shape[1],
+                                       context_lens.data_ptr(), S,
+                                       group_start.data_ptr() if group_start is not None else None, ng, num_heads,
+                                       num_kv_heads, block_size, int(max_context_len), int(dtype), _stream(stream)))
+
+
+def shared_plan_for(block_tables: torch.Tensor, context_lens: torch.Tensor, group_start: Optional[torch.Tensor],
+                    num_heads: int, num_kv_heads: int, max_context_len: int, dtype: int,
+                    block_size: int = 16) -> torch.Tensor:
+    """A shared-prefix plan for these tables and groups (pkv_decode_shared_plan into a fresh buffer)."""
+    n = max(pkv_decode_shared_plan_bytes(context_lens.numel(), max_context_len), 256)
+    plan = torch.empty(n, dtype=torch.uint8, device=context_lens.device)
+    pkv_decode_shared_plan(plan, block_tables, context_lens, group_start, num_heads, num_kv_heads, max_context_len,
+                           dtype, block_size=block_size)
+    return plan
+
+
+def pkv_attention_decode_shared_planned(out: torch.Tensor, q: torch.Tensor, k_cache: torch.Tensor,
+                                        v_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                        max_context_len: int, scale: float, plan: torch.Tensor,
+                                        workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """pkv_attention_decode_shared with a plan from pkv_decode_shared_plan (same tables, lengths, groups)."""
+    _dev(out, q, k_cache, v_cache, block_tables, context_lens, plan)
+    _check_decode_shapes(out, q, k_cache, v_cache, block_tables, context_lens)
+    S, hq, d = q.shape
+    nb, hkv, bs, _ = k_cache.shape
+    if workspace is None:
+        n = max(pkv_attention_decode_shared_workspace_bytes(S, hq, d, int(max_context_len)), 256)
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    _check(_lib.pkv_attention_decode_shared_planned(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(),
+                                                    v_cache.data_ptr(), block_tables.data_ptr(),
+                                                    block_tables.shape[1], context_lens.data_ptr(), S, hq, hkv, d, bs,
+                                                    nb, int(max_context_len), float(scale), _dtype_code(k_cache),
+                                                    plan.data_ptr(), plan.numel(), workspace.data_ptr(),
+                                                    workspace.numel(), _stream(stream)))
 
 
 def pkv_attention_prefill_chunk(out: torch.Tensor, q: torch.Tensor, query_start_loc: torch.Tensor,

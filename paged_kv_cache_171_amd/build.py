@@ -3,6 +3,8 @@
     python -m paged_kv_cache_171_amd.build          # or: python paged_kv_cache_171_amd/build.py
 
 Kernels (.hip) are compiled for gfx950 only; host sources (.cpp) as C++17.
+The bench's read probes (probes/pkv_probes.hip) go into libpkv_probes.so, a
+library of their own that the product never loads.
 Every HIP compile disables packed-fp32 instruction selection.  The shared
 library gets an rpath to torch's bundled HIP runtime first (the process that
 imports torch already has it loaded under the same soname) and to /opt/rocm.
@@ -20,6 +22,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libpkv.so")
+PROBE_SRC = os.path.join(PKG, "probes", "pkv_probes.hip")
+PROBE_OUT = os.path.join(PKG, "libpkv_probes.so")
 ARCH = "gfx950"
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -77,6 +81,12 @@ def build(verbose: bool = False) -> str:
         link += [f"-Wl,-rpath,{p}" for p in rpaths] + ["-Wl,--no-undefined", "-lamdhip64"]
         _run(link)
         os.replace(OUT + ".tmp", OUT)
+        # the bench's read probes: a library of their own, outside the ABI
+        pobj = os.path.join(tmp, "pkv_probes.o")
+        _run([hipcc, "-x", "hip", "-c", PROBE_SRC, "-o", pobj] + HIP_FLAGS)
+        _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", PROBE_OUT + ".tmp", pobj]
+             + [f"-Wl,-rpath,{p}" for p in rpaths] + ["-Wl,--no-undefined", "-lamdhip64"])
+        os.replace(PROBE_OUT + ".tmp", PROBE_OUT)
     return OUT
 
 

@@ -44,12 +44,17 @@ using pkv_ws::kPlanHdrWords;
 using pkv_ws::plan_bytes;
 using pkv_ws::partial_bytes;
 
-// Shared-prefix decode workspace: the shared plan, seq_start, the plan of the
-// sequences' own units, then partials with prefix slots ahead of the
-// sequence's own ones.
+// Shared-prefix decode buffers.  The plan buffer holds the shared plan (a
+// header, then 4 ints per shared unit), seq_start and the plan of the
+// sequences' own units, in that order; the partial buffer holds the partials
+// (prefix slots ahead of each sequence's own) and one merge ticket per
+// (sequence, head).  The self-planning call puts the plan at the start of its
+// workspace and the partials after it.
 struct SharedLayout {
   int32_t prefix_slots, slots;
-  size_t shared_plan, seq_start, plan, part_ml, part_acc, tickets, total;
+  size_t shared_plan, seq_start, plan, plan_total;   // within the plan buffer
+  size_t part_ml, part_acc, tickets, part_total;     // within the partial buffer
+  size_t total() const { return align256(plan_total) + part_total; }
 };
 SharedLayout shared_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len) {
   SharedLayout l{};
@@ -60,12 +65,76 @@ SharedLayout shared_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim
   l.shared_plan = 0;
   l.seq_start = align256((kPlanHdrWords + 4 * S * l.prefix_slots) * sizeof(int32_t));
   l.plan = l.seq_start + align256(S * sizeof(int32_t));
-  l.part_ml = l.plan + align256(plan_bytes(num_seqs, max_context_len));
+  l.plan_total = l.plan + plan_bytes(num_seqs, max_context_len);
   const size_t units = S * num_heads * l.slots;
-  l.part_acc = l.part_ml + align256(units * 2 * sizeof(float));
+  l.part_ml = 0;
+  l.part_acc = align256(units * 2 * sizeof(float));
   l.tickets = l.part_acc + align256(units * head_dim * sizeof(float));
-  l.total = l.tickets + S * num_heads * sizeof(uint64_t);
+  l.part_total = l.tickets + S * num_heads * sizeof(uint64_t);
   return l;
+}
+
+// Whether shared-prefix decode reads shared blocks on the matrix cores for
+// these heads (bf16, 1..16 query heads per KV head, 16-token blocks); other
+// shapes run plain decode.
+bool shared_applies(pkv_dtype dtype, int32_t num_heads, int32_t num_kv_heads, int32_t block_size) {
+  const int32_t group = num_kv_heads > 0 ? num_heads / num_kv_heads : 0;
+  return dtype == PKV_BF16 && group >= 1 && group <= kMaxMfmaGroup && block_size == kMfmaBlockSize;
+}
+
+// The checks every shared-prefix call makes on its sizes.
+pkv_status check_shared(const char* fn, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                        int32_t max_context_len, pkv_dtype dtype) {
+  pkv_status st = check_common(fn, num_kv_heads, head_dim, block_size, dtype);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: num_seqs < 0", fn);
+  if (num_heads <= 0 || num_heads % num_kv_heads != 0)
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: num_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                     fn, num_heads, num_kv_heads);
+  if (num_blocks <= 0) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: num_blocks must be > 0", fn);
+  if (max_blocks_per_seq <= 0) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: max_blocks_per_seq must be > 0", fn);
+  if (max_context_len < 0) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: max_context_len < 0", fn);
+  const SharedLayout l = shared_layout(num_seqs, num_heads, head_dim, max_context_len);
+  const int64_t grid = static_cast<int64_t>(num_seqs) * num_heads * (l.prefix_slots + num_partitions(max_context_len));
+  if (grid > 0x7FFFFFFF || static_cast<int64_t>(num_seqs) * l.slots > 0x3FFFFFFF)
+    return pkv_failf(PKV_ERR_UNSUPPORTED, "%s: launch grid too large", fn);
+  return PKV_OK;
+}
+
+// The kernel arguments of a shared-prefix decode over a plan buffer and a
+// partial buffer laid out by shared_layout.
+pkv_decode_args shared_args(const SharedLayout& l, float* out, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t num_blocks, int32_t max_context_len,
+                            float scale, pkv_dtype dtype, const char* plan, char* part) {
+  pkv_decode_args a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.plan = reinterpret_cast<const int32_t*>(plan + l.plan);
+  a.part_ml = part ? reinterpret_cast<float*>(part + l.part_ml) : nullptr;
+  a.part_acc = part ? reinterpret_cast<float*>(part + l.part_acc) : nullptr;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.max_context_len = max_context_len;
+  a.num_partitions = l.slots;
+  a.part_tokens = pkv_part_tokens(dtype, num_heads, num_kv_heads, block_size);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.dtype = dtype;
+  a.seq_start = reinterpret_cast<const int32_t*>(plan + l.seq_start);
+  a.shared_plan = reinterpret_cast<const int32_t*>(plan + l.shared_plan);
+  a.prefix_part_tokens = kPrefixPartTokens;
+  return a;
 }
 }  // namespace
 
@@ -351,9 +420,94 @@ size_t pkv_attention_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num
                                                    int32_t max_context_len) {
   if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len < 0) return 0;
   const size_t plain = pkv_attention_workspace_bytes(num_seqs, num_heads, head_dim, max_context_len);
-  const size_t shared = shared_layout(num_seqs, num_heads, head_dim, max_context_len).total;
+  const size_t shared = shared_layout(num_seqs, num_heads, head_dim, max_context_len).total();
   return shared > plain ? shared : plain;
 }
+
+size_t pkv_decode_shared_plan_bytes(int32_t num_seqs, int32_t max_context_len) {
+  if (num_seqs <= 0 || max_context_len < 0) return 0;
+  return shared_layout(num_seqs, 1, 1, max_context_len).plan_total;
+}
+
+pkv_status pkv_decode_shared_plan(void* plan, size_t plan_bytes_given, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                                  const int32_t* group_start, int32_t num_groups, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t block_size, int32_t max_context_len, pkv_dtype dtype,
+                                  void* stream) {
+  const char* fn = "pkv_decode_shared_plan";
+  if (num_groups < 0) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: num_groups < 0", fn);
+  if (num_groups > num_seqs && num_seqs >= 0)
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: more groups than sequences", fn);
+  // head_dim does not enter the plan: any supported value passes the checks
+  pkv_status st = check_shared(fn, num_seqs, num_heads, num_kv_heads, 128, block_size, 1, max_blocks_per_seq,
+                               max_context_len, dtype);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0) return PKV_OK;
+  if (!plan || !block_tables || !context_lens || (num_groups > 0 && !group_start))
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (reinterpret_cast<uintptr_t>(plan) & 255u)
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: plan must be 256-byte aligned", fn);
+  const SharedLayout l = shared_layout(num_seqs, num_heads, 128, max_context_len);
+  if (plan_bytes_given < l.plan_total)
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: plan buffer of %zu bytes is smaller than the %zu needed", fn,
+                     plan_bytes_given, l.plan_total);
+  char* pb = static_cast<char*>(plan);
+  if (!shared_applies(dtype, num_heads, num_kv_heads, block_size)) {
+    // plain decode: only the own plan region is used
+    return hip_status(fn, pkv_launch_plan(reinterpret_cast<int32_t*>(pb + l.plan), context_lens, num_seqs,
+                                          max_blocks_per_seq, block_size, max_context_len,
+                                          pkv_part_tokens(dtype, num_heads, num_kv_heads, block_size), stream));
+  }
+  const pkv_decode_args a = shared_args(l, nullptr, nullptr, nullptr, nullptr, block_tables, max_blocks_per_seq,
+                                        context_lens, num_seqs, num_heads, num_kv_heads, 128, block_size, 1,
+                                        max_context_len, 1.f, dtype, pb, nullptr);
+  // (no groups: every sequence is decoded by its own units)
+  return hip_status(fn, pkv_launch_shared_plans(a, num_groups > 0 ? group_start : nullptr, num_groups,
+                                                reinterpret_cast<int32_t*>(pb + l.seq_start),
+                                                reinterpret_cast<int32_t*>(pb + l.shared_plan),
+                                                reinterpret_cast<int32_t*>(pb + l.plan), stream));
+}
+
+}  // extern "C"
+
+// Shared-prefix decode from a plan buffer (built by pkv_decode_shared_plan, or
+// just now into the workspace) and a partial buffer.  With num_groups == 0 or
+// a shape the shared path does not cover the plan is a plain decode plan.
+static pkv_status shared_decode(const char* fn, float* out, const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                int32_t max_context_len, float scale, pkv_dtype dtype, const char* plan,
+                                char* part, size_t part_bytes, bool plain, void* stream) {
+  const SharedLayout l = shared_layout(num_seqs, num_heads, head_dim, max_context_len);
+  if (plain)
+    return pkv_decode_impl(fn, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                           num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_context_len, scale, dtype,
+                           plan + l.plan, plan_bytes(num_seqs, max_context_len), part, part_bytes, false, stream);
+  if (part_bytes < l.part_total)
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: workspace of %zu bytes is smaller than the %zu needed", fn,
+                     part_bytes, l.part_total);
+  pkv_decode_args a = shared_args(l, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                                  num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_context_len,
+                                  scale, dtype, plan, part);
+  // split rows are merged inside the decode launch
+  a.merge_tickets = reinterpret_cast<uint64_t*>(part + l.tickets);
+  a.merge_epoch = next_merge_epoch();
+  return hip_status(fn, pkv_launch_shared_fused(a, stream));
+}
+
+static pkv_status check_decode_pointers(const char* fn, float* out, const void* q, const void* k_cache,
+                                        const void* v_cache, const int32_t* block_tables,
+                                        const int32_t* context_lens, float scale) {
+  if (!std::isfinite(scale)) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: out, q and cache pointers must be 16-byte aligned", fn);
+  return PKV_OK;
+}
+
+extern "C" {
 
 pkv_status pkv_attention_decode_shared(float* out, const void* q, const void* k_cache, const void* v_cache,
                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
@@ -365,71 +519,64 @@ pkv_status pkv_attention_decode_shared(float* out, const void* q, const void* k_
   const char* fn = "pkv_attention_decode_shared";
   if (num_groups < 0) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: num_groups < 0", fn);
   if (num_groups > 0 && num_seqs > 0 && !group_start) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: group_start is NULL", fn);
-  const int32_t group = num_kv_heads > 0 ? num_heads / num_kv_heads : 0;
   // only the bf16 MFMA kernel reads a prefix for several sequences; otherwise
   // (or with no groups) this is plain decode
-  if (dtype != PKV_BF16 || group < 1 || group > kMaxMfmaGroup || block_size != kMfmaBlockSize || num_groups == 0 ||
-      num_seqs <= 0)
+  if (!shared_applies(dtype, num_heads, num_kv_heads, block_size) || num_groups == 0 || num_seqs <= 0)
     return pkv_decode_impl(fn, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
-                       num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_context_len, scale, dtype,
-                       nullptr, 0, workspace, workspace_bytes, true, stream);
-  pkv_status st = check_common(fn, num_kv_heads, head_dim, block_size, dtype);
+                           num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_context_len, scale, dtype,
+                           nullptr, 0, workspace, workspace_bytes, true, stream);
+  pkv_status st = check_shared(fn, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                               max_blocks_per_seq, max_context_len, dtype);
   if (st != PKV_OK) return st;
-  if (num_heads <= 0 || num_heads % num_kv_heads != 0)
-    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: num_heads (%d) must be a positive multiple of num_kv_heads (%d)",
-                     fn, num_heads, num_kv_heads);
-  if (num_blocks <= 0) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: num_blocks must be > 0", fn);
-  if (max_blocks_per_seq <= 0) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: max_blocks_per_seq must be > 0", fn);
-  if (max_context_len < 0) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: max_context_len < 0", fn);
   if (num_groups > num_seqs) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: more groups than sequences", fn);
-  if (!std::isfinite(scale)) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: scale is not finite", fn);
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
-    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: NULL pointer", fn);
-  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
-    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: out, q and cache pointers must be 16-byte aligned", fn);
+  st = check_decode_pointers(fn, out, q, k_cache, v_cache, block_tables, context_lens, scale);
+  if (st != PKV_OK) return st;
   const SharedLayout l = shared_layout(num_seqs, num_heads, head_dim, max_context_len);
-  const int64_t grid = static_cast<int64_t>(num_seqs) * num_heads * (l.prefix_slots + num_partitions(max_context_len));
-  if (grid > 0x7FFFFFFF || static_cast<int64_t>(num_seqs) * l.slots > 0x3FFFFFFF)
-    return pkv_failf(PKV_ERR_UNSUPPORTED, "%s: launch grid too large", fn);
-  if (workspace_bytes < l.total)
+  if (workspace_bytes < l.total())
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: workspace of %zu bytes is smaller than the %zu needed", fn,
-                     workspace_bytes, l.total);
+                     workspace_bytes, l.total());
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: workspace must be a 256-byte aligned device buffer", fn);
   char* ws = static_cast<char*>(workspace);
-  pkv_decode_args a{};
-  a.out = out;
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.plan = reinterpret_cast<const int32_t*>(ws + l.plan);
-  a.part_ml = reinterpret_cast<float*>(ws + l.part_ml);
-  a.part_acc = reinterpret_cast<float*>(ws + l.part_acc);
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.num_seqs = num_seqs;
-  a.num_heads = num_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.head_dim = head_dim;
-  a.num_blocks = num_blocks;
-  a.block_size = block_size;
-  a.max_context_len = max_context_len;
-  a.num_partitions = l.slots;
-  a.part_tokens = pkv_part_tokens(dtype, num_heads, num_kv_heads, block_size);
-  a.scale_log2 = scale * 1.4426950408889634f;
-  a.dtype = dtype;
-  a.seq_start = reinterpret_cast<const int32_t*>(ws + l.seq_start);
-  a.shared_plan = reinterpret_cast<const int32_t*>(ws + l.shared_plan);
-  a.prefix_part_tokens = kPrefixPartTokens;
-  // split rows are merged inside the decode launch
-  a.merge_tickets = reinterpret_cast<uint64_t*>(ws + l.tickets);
-  a.merge_epoch = next_merge_epoch();
-  int err = pkv_launch_shared_plans(a, group_start, num_groups, reinterpret_cast<int32_t*>(ws + l.seq_start),
-                                    reinterpret_cast<int32_t*>(ws + l.shared_plan), reinterpret_cast<int32_t*>(ws + l.plan),
-                                    stream);
-  if (!err) err = pkv_launch_shared_fused(a, stream);
-  return hip_status(fn, err);
+  const pkv_decode_args a = shared_args(l, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                                        num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                                        max_context_len, scale, dtype, ws, nullptr);
+  const int err = pkv_launch_shared_plans(a, group_start, num_groups, reinterpret_cast<int32_t*>(ws + l.seq_start),
+                                          reinterpret_cast<int32_t*>(ws + l.shared_plan),
+                                          reinterpret_cast<int32_t*>(ws + l.plan), stream);
+  if (err) return hip_status(fn, err);
+  const size_t off = align256(l.plan_total);
+  return shared_decode(fn, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                       num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_context_len, scale, dtype, ws,
+                       ws + off, workspace_bytes - off, false, stream);
+}
+
+pkv_status pkv_attention_decode_shared_planned(float* out, const void* q, const void* k_cache, const void* v_cache,
+                                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                               const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                               int32_t num_blocks, int32_t max_context_len, float scale,
+                                               pkv_dtype dtype, const void* plan, size_t plan_bytes_given,
+                                               void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "pkv_attention_decode_shared_planned";
+  pkv_status st = check_shared(fn, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                               max_blocks_per_seq, max_context_len, dtype);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0) return PKV_OK;
+  st = check_decode_pointers(fn, out, q, k_cache, v_cache, block_tables, context_lens, scale);
+  if (st != PKV_OK) return st;
+  const SharedLayout l = shared_layout(num_seqs, num_heads, head_dim, max_context_len);
+  if (!plan || (reinterpret_cast<uintptr_t>(plan) & 255u))
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: plan must be a 256-byte aligned device buffer", fn);
+  if (plan_bytes_given < l.plan_total)
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: plan of %zu bytes is smaller than the %zu these sizes need", fn,
+                     plan_bytes_given, l.plan_total);
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: workspace must be a 256-byte aligned device buffer", fn);
+  return shared_decode(fn, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                       num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_context_len, scale, dtype,
+                       static_cast<const char*>(plan), static_cast<char*>(workspace), workspace ? workspace_bytes : 0,
+                       !shared_applies(dtype, num_heads, num_kv_heads, block_size), stream);
 }
 
 pkv_status pkv_attention_prefill_chunk(float* out, const void* q, const int32_t* query_start_loc,

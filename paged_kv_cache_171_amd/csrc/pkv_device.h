@@ -28,10 +28,20 @@ __device__ __forceinline__ bool len_ok(int32_t ctx, int32_t max_context_len, int
   return ctx > 0 && ctx <= max_context_len && static_cast<int64_t>(ctx) <= static_cast<int64_t>(max_blocks_per_seq) * block_size;
 }
 
-// The plan was built for these sizes.
+// A shared-prefix plan (header: units, num_seqs, max_context_len,
+// max_blocks_per_seq, prefix partition tokens, query heads per KV head) was
+// built for these sizes.
+__device__ __forceinline__ bool shared_plan_matches(const int32_t* sp, const pkv_decode_args& a) {
+  return sp[1] == a.num_seqs && sp[2] == a.max_context_len && sp[3] == a.max_blocks_per_seq &&
+         sp[4] == a.prefix_part_tokens && sp[5] == a.num_heads / a.num_kv_heads;
+}
+
+// The plan (and with shared-prefix decode the shared plan too) was built for
+// these sizes.
 __device__ __forceinline__ bool plan_matches(const int32_t* plan, const pkv_decode_args& a) {
   return plan[1] == a.num_seqs && plan[2] == a.max_context_len && plan[3] == a.max_blocks_per_seq &&
-         plan[4] == a.part_tokens && plan[5] == a.block_size;
+         plan[4] == a.part_tokens && plan[5] == a.block_size &&
+         (a.shared_plan == nullptr || shared_plan_matches(a.shared_plan, a));
 }
 
 __device__ __forceinline__ const int32_t* plan_units(const int32_t* plan) { return plan + kPlanHdr; }

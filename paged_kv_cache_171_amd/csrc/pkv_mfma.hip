@@ -192,12 +192,14 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
   int32_t nslots = 0;     // partial slots of each row (merged in this launch when tickets are given)
   bool direct;
   if (shared_unit) {
-    // a group's shared leading blocks: the rows are the group's sequences
+    // a group's shared leading blocks: the rows are the group's sequences (a
+    // plan built for other sizes runs no shared unit; the sequences' own units
+    // then write NaN rows)
     const int32_t* sp = a.shared_plan;
-    if (u >= sp[0]) return;
+    if (!pkvd::shared_plan_matches(sp, a) || u >= sp[0]) return;
     const int32_t* su = sp + kPlanHdr + 4 * u;
     s0 = su[0];
-    nrows = su[1] * G;
+    nrows = min(su[1], kMaxMfmaGroup / G) * G;
     ctx = su[3];
     blk_begin = su[2] * (a.prefix_part_tokens / kBlock);
     blk_end = min(ctx / kBlock, blk_begin + a.prefix_part_tokens / kBlock);
@@ -529,7 +531,8 @@ __device__ __forceinline__ void shared_plan_body(const pkv_decode_args& a, const
   const int32_t S = a.num_seqs, MB = a.max_blocks_per_seq;
   if (tid == 0) { sm_units = 0; sm_bad = 0; }
   __syncthreads();
-  for (int32_t i = tid; i <= num_groups; i += 1024) {
+  if (num_groups <= 0 && tid == 0) sm_bad = 1;      // no groups: no shared prefix
+  for (int32_t i = tid; num_groups > 0 && i <= num_groups; i += 1024) {
     const int32_t v = group_start[i];
     bool ok = v >= 0 && v <= S;
     if (i == 0) ok = ok && v == 0;
@@ -606,7 +609,7 @@ __device__ __forceinline__ void shared_plan_body(const pkv_decode_args& a, const
     shared_plan[2] = a.max_context_len;
     shared_plan[3] = MB;
     shared_plan[4] = a.prefix_part_tokens;
-    shared_plan[5] = 0;
+    shared_plan[5] = a.num_heads / a.num_kv_heads;     // query heads per KV head (rows per member)
     shared_plan[6] = 0;
     shared_plan[7] = 0;
   }

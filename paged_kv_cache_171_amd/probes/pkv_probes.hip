@@ -1,0 +1,127 @@
+// Read-bandwidth probes for the bench (libpkv_probes.so, not part of the
+// library's ABI): how fast this GPU reads HBM when nothing but reading is
+// done, as a measured ceiling beside the 8 TB/s specification.
+//
+//   stream_read_kernel  -- one contiguous buffer streamed once with 16-byte
+//                          loads (non-temporal or ordinary), UNROLL loads in
+//                          flight per thread, a grid-stride loop over
+//                          workgroup-sized chunks
+//   tile_read_kernel    -- the paged decode access pattern and nothing else:
+//                          whole (block, head) K and V tiles reached through
+//                          block tables, one workgroup per (16-block chunk of a
+//                          sequence, head), its four waves taking blocks in turn
+//
+// Every load feeds an XOR that is written only if it equals a constant, so
+// the loads cannot be removed and nothing is stored in practice.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr uint32_t kMagic = 0x9E3779B9u;
+
+template <int UNROLL, bool NT>
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ buf, int64_t n16,
+                                                          uint32_t* __restrict__ sink) {
+  constexpr int64_t kChunk = 256 * UNROLL;      // 16-byte units per workgroup per iteration
+  uint32_t acc = 0;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * kChunk; base < n16;
+       base += static_cast<int64_t>(gridDim.x) * kChunk) {
+    u32x4 v[UNROLL];
+#pragma unroll
+    for (int i = 0; i < UNROLL; ++i) {
+      const int64_t idx = base + i * 256 + threadIdx.x;
+      if (idx < n16) v[i] = NT ? __builtin_nontemporal_load(buf + idx) : buf[idx];
+      else v[i] = u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < UNROLL; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+  }
+  if (acc == kMagic) sink[static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x] = acc;
+}
+
+// One (block, head) tile of TILE16 16-byte units read by one wave.
+template <int TILE16>
+__device__ __forceinline__ uint32_t tile_xor(const u32x4* p, int lane) {
+  uint32_t a = 0;
+#pragma unroll
+  for (int i = 0; i < TILE16 / 64; ++i) {
+    const u32x4 v = __builtin_nontemporal_load(p + i * 64 + lane);
+    a ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  return a;
+}
+
+// work: (sequence, chunk) pairs; chunk c covers blocks 16c .. 16c+15 of the
+// sequence's table (clipped to its context).  Tiles of tile_bytes bytes, a
+// block holding num_heads of them.
+template <int TILE16>
+__global__ __launch_bounds__(256) void tile_read_kernel(const char* __restrict__ kc, const char* __restrict__ vc,
+                                                        const int32_t* __restrict__ tables, int32_t max_blocks,
+                                                        const int32_t* __restrict__ lens, int32_t block_size,
+                                                        const int32_t* __restrict__ work, int32_t num_heads,
+                                                        uint32_t* __restrict__ sink) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int32_t wi = blockIdx.x / num_heads, h = blockIdx.x - (blockIdx.x / num_heads) * num_heads;
+  const int32_t s = work[2 * wi], c = work[2 * wi + 1];
+  const int32_t nblk = (lens[s] + block_size - 1) / block_size;
+  const int32_t j0 = 16 * c, j1 = min(nblk, j0 + 16);
+  const int32_t* t = tables + static_cast<int64_t>(s) * max_blocks;
+  constexpr int64_t kTile = static_cast<int64_t>(TILE16) * 16;
+  uint32_t acc = 0;
+  for (int32_t j = j0 + wave; j < j1; j += 8) {
+    const int64_t o1 = (static_cast<int64_t>(t[j]) * num_heads + h) * kTile;
+    uint32_t a = tile_xor<TILE16>(reinterpret_cast<const u32x4*>(kc + o1), lane) ^
+                 tile_xor<TILE16>(reinterpret_cast<const u32x4*>(vc + o1), lane);
+    if (j + 4 < j1) {
+      const int64_t o2 = (static_cast<int64_t>(t[j + 4]) * num_heads + h) * kTile;
+      a ^= tile_xor<TILE16>(reinterpret_cast<const u32x4*>(kc + o2), lane) ^
+           tile_xor<TILE16>(reinterpret_cast<const u32x4*>(vc + o2), lane);
+    }
+    acc ^= a;
+  }
+  if (acc == kMagic) sink[static_cast<int64_t>(blockIdx.x) * 4 + wave] = acc;
+}
+
+}  // namespace
+
+// bytes: a multiple of 16.  sink: at least grid * 256 uint32 words.  mode:
+// UNROLL 4 / 8 / 16 with non-temporal loads (0 / 1 / 2) or ordinary loads (3 /
+// 4 / 5).  Returns the launch status.
+extern "C" int pkvprobe_stream_read(const void* buf, int64_t bytes, int32_t grid, int32_t mode, uint32_t* sink,
+                                    void* stream) {
+  const int64_t n16 = bytes / 16;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const u32x4* p = static_cast<const u32x4*>(buf);
+  switch (mode) {
+    case 0: hipLaunchKernelGGL((stream_read_kernel<4, true>), dim3(grid), dim3(256), 0, st, p, n16, sink); break;
+    case 1: hipLaunchKernelGGL((stream_read_kernel<8, true>), dim3(grid), dim3(256), 0, st, p, n16, sink); break;
+    case 2: hipLaunchKernelGGL((stream_read_kernel<16, true>), dim3(grid), dim3(256), 0, st, p, n16, sink); break;
+    case 3: hipLaunchKernelGGL((stream_read_kernel<4, false>), dim3(grid), dim3(256), 0, st, p, n16, sink); break;
+    case 4: hipLaunchKernelGGL((stream_read_kernel<8, false>), dim3(grid), dim3(256), 0, st, p, n16, sink); break;
+    default: hipLaunchKernelGGL((stream_read_kernel<16, false>), dim3(grid), dim3(256), 0, st, p, n16, sink); break;
+  }
+  return hipGetLastError();
+}
+
+// tile_bytes: 4096 (16 tokens x 128 dims bf16) or 2048.  Every table entry of
+// tokens below lens[s] must lie in the pools.  sink: num_work * num_heads * 4
+// words.
+extern "C" int pkvprobe_tile_read(const void* k_cache, const void* v_cache, const int32_t* tables,
+                                  int32_t max_blocks, const int32_t* lens, int32_t block_size, const int32_t* work,
+                                  int32_t num_work, int32_t num_heads, int32_t tile_bytes, uint32_t* sink,
+                                  void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(num_work) * num_heads));
+  const char* kc = static_cast<const char*>(k_cache);
+  const char* vc = static_cast<const char*>(v_cache);
+  if (tile_bytes == 2048)
+    hipLaunchKernelGGL((tile_read_kernel<128>), grid, dim3(256), 0, st, kc, vc, tables, max_blocks, lens, block_size,
+                       work, num_heads, sink);
+  else
+    hipLaunchKernelGGL((tile_read_kernel<256>), grid, dim3(256), 0, st, kc, vc, tables, max_blocks, lens, block_size,
+                       work, num_heads, sink);
+  return hipGetLastError();
+}

@@ -111,6 +111,47 @@ def test_shared_decode_rejects_bad_arguments_before_any_launch(P):
     assert L.pkv_attention_decode_shared_workspace_bytes(0, 4, 64, 64) == 0
 
 
+def test_shared_plan_and_planned_decode_reject_bad_arguments_before_any_launch(P):
+    L = _lib(P)
+    pb = L.pkv_decode_shared_plan_bytes(2, 64)
+    assert pb > 0 and L.pkv_decode_shared_plan_bytes(0, 64) == 0
+    # plan tables MB lens S group_start n_groups Hq Hkv bs mcl dtype stream
+    plan_args = [4096, pb, 1280, 4, 1536, 2, 1792, 1, 4, 4, 16, 64, 1, None]
+    names = ["plan", "pb", "tables", "mb", "lens", "S", "gs", "ng", "Hq", "Hkv", "bs", "mcl", "dtype", "stream"]
+
+    def plan(**kw):
+        a = list(plan_args)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return L.pkv_decode_shared_plan(*a)
+    assert plan(ng=3) == P.PKV_ERR_INVALID_ARG                 # more groups than sequences
+    assert plan(ng=-1) == P.PKV_ERR_INVALID_ARG
+    assert plan(pb=pb - 1) == P.PKV_ERR_INVALID_ARG            # plan buffer too small
+    assert plan(plan=4096 + 16) == P.PKV_ERR_INVALID_ARG       # misaligned plan
+    assert plan(gs=None) == P.PKV_ERR_INVALID_ARG              # groups named but no group_start
+    assert plan(bs=12) == P.PKV_ERR_UNSUPPORTED
+    assert plan(Hq=6) == P.PKV_ERR_INVALID_ARG
+    assert plan(S=0, ng=0) == P.PKV_OK
+    # out q k v tables MB lens S Hq Hkv d bs NB mcl scale dtype plan plan_bytes ws ws_bytes stream
+    dec_args = [256, 512, 768, 1024, 1280, 4, 1536, 2, 4, 4, 64, 16, 8, 64, 0.125, 1, 4096, pb, 8192, 1 << 20, None]
+    dnames = ["out", "q", "k", "v", "tables", "mb", "lens", "S", "Hq", "Hkv", "d", "bs", "nb", "mcl", "scale",
+              "dtype", "plan", "pb", "ws", "wsb", "stream"]
+
+    def dec(**kw):
+        a = list(dec_args)
+        for k, v in kw.items():
+            a[dnames.index(k)] = v
+        return L.pkv_attention_decode_shared_planned(*a)
+    assert dec(plan=None) == P.PKV_ERR_INVALID_ARG
+    assert dec(pb=pb - 1) == P.PKV_ERR_INVALID_ARG
+    assert dec(ws=8192 + 8) == P.PKV_ERR_INVALID_ARG           # misaligned workspace
+    assert dec(wsb=16) == P.PKV_ERR_INVALID_ARG                # workspace too small
+    assert "workspace" in L.pkv_last_error().decode()
+    assert dec(scale=float("inf")) == P.PKV_ERR_INVALID_ARG
+    assert dec(q=None) == P.PKV_ERR_INVALID_ARG
+    assert dec(S=0) == P.PKV_OK
+
+
 def test_batch_rejects_bad_arguments_before_any_device_call(P):
     L = _lib(P)
     a16 = P.BlockAllocator(20)

@@ -37,12 +37,29 @@ def test_kernel_source_hash_covers_the_decode_sources():
     assert re.fullmatch(r"[0-9a-f]{16}", bench.kernel_source_hash())
 
 
-def test_cpu_baseline_record(monkeypatch):
+def test_cpu_baseline_record():
+    """The record's fields, on a 4-sequence batch held in host tensors (the
+    bench passes the last timed step's device tensors), and the max abs error
+    between the given outputs and the oracle's: a planted error of 0.25 in one
+    output element is what it reports."""
+    import numpy as np
+    import torch
     import pkv_workloads as W
-    full = W.shaped_13b
-    # the record's fields, on 4 of the batch's sequences (the bench times all 64)
-    monkeypatch.setattr(W, "shaped_13b", lambda seed: full(seed=seed, num_seqs=4))
-    rec = bench.cpu_baseline(2, 0.2)
+    from oracle import pkv_oracle as O
+    w = W.shaped_13b(seed=2, num_seqs=4)
+    r = O.replay(w.ops, w.k_rows, w.v_rows, w.num_blocks, w.num_kv_heads, w.head_dim, w.initial_free_order)
+    tables = [r.alloc.block_table(s) for s in w.decode_seqs]
+    lens = np.array([r.alloc.num_tokens(s) for s in w.decode_seqs])
+    ref = O.decode_attention(w.q, r.k_pool, r.v_pool, tables, lens, w.scale)
+
+    def bf16(bits):
+        return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16)
+    out = torch.from_numpy(ref.astype(np.float32))
+    out[1, 3, 7] += 0.25
+    tensors = (bf16(w.q), bf16(r.k_pool), bf16(r.v_pool), out)
+    rec = bench.cpu_baseline(lambda l: 2 if l is None else tensors, tables, lens, w.scale, 0.2, 2e-3)
     assert rec["kind"] == "oracle" and rec["unit"] == "tokens/s" and rec["cores"] == 1
-    assert rec["value"] > 0 and "layers" in rec["sample"]
+    assert rec["value"] > 0 and "layers" in rec["sample"] and "best of 3" in rec["sample"]
+    assert abs(rec["max_abs_err"] - 0.25) < 1e-6 and rec["tol"] == 2e-3
+    assert rec["rows_checked"] in (4 * 40, 2 * 4 * 40)
     assert rec["all_cores"]["value"] > 0 and rec["all_cores"]["cores"] >= 1

@@ -114,3 +114,75 @@ def test_empty_and_invalid_contexts_inside_a_group():
     ok = [i for i in range(len(lens)) if i not in (1, 5)]
     err = float(np.abs(out[ok] - _ref(w, ok, tables, lens)).max())
     assert err <= TOL
+
+
+# ---------------------------------------------------------------------------
+# The shared-prefix plan built once per step and used by every layer.
+# ---------------------------------------------------------------------------
+def _device_inputs(g, w, group_start):
+    tables, lens = g.tables(w.decode_seqs)
+    td = torch.from_numpy(np.ascontiguousarray(tables)).cuda()
+    ld = torch.from_numpy(np.ascontiguousarray(lens, dtype=np.int32)).cuda()
+    gs = None if group_start is None else torch.from_numpy(np.ascontiguousarray(group_start, dtype=np.int32)).cuda()
+    return rows_to_device(w.q, "cuda"), td, ld, gs, int(lens.max()), tables, lens
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(40, 40, 128), (16, 2, 128), (8, 8, 64)])
+def test_planned_shared_decode_equals_self_planned_on_every_layer(hq, hkv, d):
+    """One pkv_decode_shared_plan serves two "layers" (the second with K and V
+    swapped): each planned call gives the self-planning call's bits."""
+    print(f"case: shared planned H={hq}/{hkv} d={d}", flush=True)
+    w = W.parallel_sampling(seed=21, groups=5, samples=[8, 3, 1, 6, 4], prompt=[1000, 300, 80, 1500, 17],
+                            tail_lo=0, tail_hi=200, hq=hq, hkv=hkv, d=d)
+    g = GpuReplay(w)
+    q, td, ld, gs, mcl, tables, lens = _device_inputs(g, w, w.group_start)
+    plan = PK.shared_plan_for(td, ld, gs, hq, hkv, mcl, PK.PKV_BF16)
+    ws = torch.empty(max(PK.pkv_attention_decode_shared_workspace_bytes(len(lens), hq, d, mcl), 256),
+                     dtype=torch.uint8, device="cuda")
+    ref = _ref(w, list(range(len(lens))), tables, lens)
+    for kp, vp in ((g.k_pool, g.v_pool), (g.v_pool, g.k_pool)):
+        o1 = torch.full((len(lens), hq, d), -3.0, dtype=torch.float32, device="cuda")
+        o2 = torch.full_like(o1, -4.0)
+        PK.pkv_attention_decode_shared(o1, q, kp, vp, td, ld, gs, mcl, float(w.scale))
+        PK.pkv_attention_decode_shared_planned(o2, q, kp, vp, td, ld, mcl, float(w.scale), plan, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2)
+    # the first layer's outputs against the oracle
+    PK.pkv_attention_decode_shared_planned(o2, q, g.k_pool, g.v_pool, td, ld, mcl, float(w.scale), plan, workspace=ws)
+    torch.cuda.synchronize()
+    assert float(np.abs(o2.cpu().numpy() - ref).max()) <= TOL
+
+
+def test_planned_shared_decode_plain_shapes_and_mismatched_plans():
+    print("case: shared planned fallbacks", flush=True)
+    # fp32 pools: the plan is a plain decode plan and the planned call is plain decode
+    w = W.random_small(31, 7, 1500, 4, 4, 64, "f32")
+    g = GpuReplay(w)
+    q, td, ld, _, mcl, tables, lens = _device_inputs(g, w, None)
+    gs = torch.tensor([0, 3, 7], dtype=torch.int32, device="cuda")
+    plan = PK.shared_plan_for(td, ld, gs, 4, 4, mcl, PK.PKV_F32)
+    o1 = torch.empty((7, 4, 64), dtype=torch.float32, device="cuda")
+    o2 = torch.empty_like(o1)
+    PK.pkv_attention_decode(o1, q, g.k_pool, g.v_pool, td, ld, mcl, float(w.scale))
+    PK.pkv_attention_decode_shared_planned(o2, q, g.k_pool, g.v_pool, td, ld, mcl, float(w.scale), plan)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+    # bf16 with no groups: every sequence decoded by its own units
+    wb = W.parallel_sampling(seed=22, groups=2, samples=[4, 3], prompt=[200, 64], tail_lo=0, tail_hi=30, hq=8, d=128)
+    gb = GpuReplay(wb)
+    q, td, ld, _, mcl, tables, lens = _device_inputs(gb, wb, None)
+    plan0 = PK.shared_plan_for(td, ld, None, 8, 8, mcl, PK.PKV_BF16)
+    o3 = torch.empty((7, 8, 128), dtype=torch.float32, device="cuda")
+    PK.pkv_attention_decode_shared_planned(o3, q, gb.k_pool, gb.v_pool, td, ld, mcl, float(wb.scale), plan0)
+    torch.cuda.synchronize()
+    assert float(np.abs(o3.cpu().numpy() - _ref(wb, list(range(7)), tables, lens)).max()) <= TOL
+
+    # a plan built for another max_context_len, or another head grouping: NaN rows
+    gs = torch.from_numpy(wb.group_start).cuda()
+    for bad in (PK.shared_plan_for(td, ld, gs, 8, 8, mcl + 16, PK.PKV_BF16),
+                PK.shared_plan_for(td, ld, gs, 8, 4, mcl, PK.PKV_BF16)):
+        o4 = torch.zeros((7, 8, 128), dtype=torch.float32, device="cuda")
+        PK.pkv_attention_decode_shared_planned(o4, q, gb.k_pool, gb.v_pool, td, ld, mcl, float(wb.scale), bad)
+        torch.cuda.synchronize()
+        assert torch.isnan(o4).all()

@@ -86,26 +86,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
 }
 
-// A wave-uniform 32-bit load through the scalar unit.  Its wait counts only
-// scalar/LDS traffic, so it leaves the direct-to-LDS copies (counted with the
-// vector loads) in flight; a plain load issued after such copies would be a
-// vector load whose wait drains them.
-__device__ __forceinline__ int32_t scalar_load_i32(const int32_t* p) {
-  int32_t v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
-  return v;
-}
-// The same load issued without waiting for it: the value may be used only
-// after scalar_load_wait on it.  An outstanding scalar load only makes the
-// compiler's own LDS waits (lgkmcnt) wait longer, never shorter, because LDS
-// operations complete in order.
-__device__ __forceinline__ int32_t scalar_load_i32_nowait(const int32_t* p) {
-  int32_t v;
-  asm volatile("s_load_dword %0, %1, 0x0" : "=s"(v) : "s"(p) : "memory");
-  return v;
-}
-__device__ __forceinline__ void scalar_load_wait(int32_t& v0, int32_t& v1) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(v0), "+s"(v1) : : "memory");
+// A wave-uniform 32-bit load of a block id through the constant address
+// space: the compiler issues it as a scalar load and tracks its wait itself.
+// Scalar loads share their wait counter with LDS operations, not with the
+// direct-to-LDS copies (counted with the vector loads), so waiting for one
+// never drains the copies in flight.
+__device__ __forceinline__ int32_t load_block_id(const int32_t* table, int32_t j) {
+  return ((const __attribute__((address_space(4))) int32_t*)table)[j];
 }
 
 // Direct global->LDS copy of 16 bytes per lane: lane l's bytes land at LDS
@@ -767,11 +754,22 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void prefill_chunk_mfma_kernel(
       copy16_to_lds_at(base, voff, stage + kib * 1024);
     }
   };
+  // the block ids of pair pp; past the last block the pair's second block is
+  // its first one again
+  auto pair_ids = [&](int32_t pp, int32_t& id0, int32_t& id1) {
+    id0 = load_block_id(table, 2 * pp);
+    id1 = load_block_id(table, __builtin_amdgcn_readfirstlane(min(2 * pp + 1, nblk - 1)));
+  };
 #pragma unroll
   for (int pp = 0; pp < kStages - 1; ++pp)
-    if (pp < npairs)
-      issue(pp, scalar_load_i32(table + 2 * pp),
-            scalar_load_i32(table + __builtin_amdgcn_readfirstlane(min(2 * pp + 1, nblk - 1))), ring[pp]);
+    if (pp < npairs) {
+      int32_t id0, id1;
+      pair_ids(pp, id0, id1);
+      issue(pp, id0, id1, ring[pp]);
+    }
+  // the ids of the next pair to issue, loaded a pair ahead of its copies
+  int32_t nid0 = 0, nid1 = 0;
+  if (kStages - 1 < npairs) pair_ids(kStages - 1, nid0, nid1);
 
   // this lane's rows (one per tile) and their key limits; invalid rows: limit 0,
   // q = 0 (their results are never written).  Keys below nomask_lim are visible
@@ -946,22 +944,17 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void prefill_chunk_mfma_kernel(
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      // the block ids of the pair issued after this one are loaded now and
-      // waited for only when its copies are issued
+      // the pair issued after this one takes the ids loaded a pair ago; the
+      // ids of the pair after it are loaded now, with no LDS read pending,
+      // and arrive during the barrier
       const int32_t pn = pp + kStages - 1;
-      int32_t nid0 = 0, nid1 = 0;
-      if (pn < npairs) {
-        nid0 = scalar_load_i32_nowait(table + 2 * pn);
-        nid1 = scalar_load_i32_nowait(table + __builtin_amdgcn_readfirstlane(min(2 * pn + 1, nblk - 1)));
-      }
+      const int32_t id0 = nid0, id1 = nid1;
+      if (pn + 1 < npairs) pair_ids(pn + 1, nid0, nid1);
+      __builtin_amdgcn_s_barrier();
       pair(pp, ring[st]);
       // every wave passed the barrier after it finished the pair before this
       // one, so that pair's stage takes pair pp + kStages - 1
-      if (pn < npairs) {
-        scalar_load_wait(nid0, nid1);
-        issue(pn, nid0, nid1, ring[(st + kStages - 1) % kStages]);
-      }
+      if (pn < npairs) issue(pn, id0, id1, ring[(st + kStages - 1) % kStages]);
     }
   }
 

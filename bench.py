@@ -880,9 +880,36 @@ def read_probes(stream, reps: int = 10, gib: int = 4, sweep: bool = False) -> di
     return res
 
 
+def mfma_probe(stream, reps: int = 10) -> dict:
+    """TFLOP/s of the bf16 matrix cores with no memory traffic (mfma_rate_kernel:
+    chains of v_mfma_f32_16x16x32_bf16, 256-thread workgroups, 1024 or 2048 of
+    them, i.e. 4 or 8 waves per SIMD), medians of `reps` runs."""
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_171_amd", "libpkv_probes.so"))
+    lib.pkvprobe_mfma_rate.restype = ctypes.c_int
+    lib.pkvprobe_mfma_rate.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_void_p]
+    out = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+    res = {}
+    for grid in (1024, 2048):
+        for chains in (1, 2):
+            iters = 4096 // chains
+
+            def run(grid=grid, chains=chains, iters=iters):
+                rc = lib.pkvprobe_mfma_rate(out.data_ptr(), grid, iters, chains, stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"mfma_rate launch failed: {rc}")
+            flops = grid * 4 * iters * chains * 16384
+            res[f"{chains} chain(s), {grid // 256} waves/SIMD"] = round(flops / _median_us(run, stream, reps) / 1e6, 1)
+    res["unit"] = "TFLOP/s"
+    res["dense_bf16_peak"] = 2500.0
+    return res
+
+
 def probes_bench(args):
-    """The read ceilings behind the decode figures: the streaming-read sweep
-    (read_probes), and a read-only probe of the 13B-shaped decode's own access
+    """The ceilings behind the figures: the streaming-read sweep (read_probes),
+    the bf16 matrix-core rate with no memory traffic (mfma_probe), and a
+    read-only probe of the 13B-shaped decode's own access
     pattern -- the same 64 lognormal contexts, tables and 40 layer pools of
     whole 4 KiB K and V tiles, one workgroup per (16-block chunk, head), chunks
     longest first, nothing computed -- timed over the 40 layers."""
@@ -892,7 +919,7 @@ def probes_bench(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
-    res = {"workload": "probes", "read": read_probes(stream, sweep=True)}
+    res = {"workload": "probes", "read": read_probes(stream, sweep=True), "mfma": mfma_probe(stream)}
     L, H, D, P = args.layers, 40, 128, 16
     w = W.shaped_13b(seed=args.seed, with_rows=False)
     alloc = PK.BlockAllocator(w.num_blocks, P, w.initial_free_order)

@@ -10,6 +10,9 @@
 //                          whole (block, head) K and V tiles reached through
 //                          block tables, one workgroup per (16-block chunk of a
 //                          sequence, head), its four waves taking blocks in turn
+//   mfma_rate_kernel    -- the bf16 matrix-core rate with no memory traffic:
+//                          chains of v_mfma_f32_16x16x32_bf16 per wave (the
+//                          instruction the prefill kernel is built on)
 //
 // Every load feeds an XOR that is written only if it equals a constant, so
 // the loads cannot be removed and nothing is stored in practice.
@@ -85,7 +88,43 @@ __global__ __launch_bounds__(256) void tile_read_kernel(const char* __restrict__
   if (acc == kMagic) sink[static_cast<int64_t>(blockIdx.x) * 4 + wave] = acc;
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// CH independent accumulator chains per wave, iters MFMAs on each.
+template <int CH>
+__global__ __launch_bounds__(256) void mfma_rate_kernel(float* __restrict__ out, int32_t iters) {
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = static_cast<__bf16>(threadIdx.x * 0.001f + i);
+    b[i] = static_cast<__bf16>(i * 0.5f);
+  }
+  f32x4 acc[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int32_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) sum += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  out[static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x] = sum;
+}
+
 }  // namespace
+
+// out: grid * 256 floats.  chains: 1 or 2 accumulator chains per wave (each
+// MFMA 16 x 16 x 32 x 2 = 16384 flops).  Returns the launch status.
+extern "C" int pkvprobe_mfma_rate(float* out, int32_t grid, int32_t iters, int32_t chains, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (chains == 1)
+    hipLaunchKernelGGL((mfma_rate_kernel<1>), dim3(grid), dim3(256), 0, st, out, iters);
+  else
+    hipLaunchKernelGGL((mfma_rate_kernel<2>), dim3(grid), dim3(256), 0, st, out, iters);
+  return hipGetLastError();
+}
 
 // bytes: a multiple of 16.  sink: at least grid * 256 uint32 words.  mode:
 // UNROLL 4 / 8 / 16 with non-temporal loads (0 / 1 / 2) or ordinary loads (3 /

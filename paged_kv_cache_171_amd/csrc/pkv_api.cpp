@@ -79,7 +79,8 @@ SharedLayout shared_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim
 // shapes run plain decode.
 bool shared_applies(pkv_dtype dtype, int32_t num_heads, int32_t num_kv_heads, int32_t block_size) {
   const int32_t group = num_kv_heads > 0 ? num_heads / num_kv_heads : 0;
-  return dtype == PKV_BF16 && group >= 1 && group <= kMaxMfmaGroup && block_size == kMfmaBlockSize;
+  (void)block_size;
+  return dtype == PKV_BF16 && group >= 1 && group <= kMaxMfmaGroup;
 }
 
 // The checks every shared-prefix call makes on its sizes.
@@ -590,8 +591,6 @@ pkv_status pkv_attention_prefill_chunk(float* out, const void* q, const int32_t*
   pkv_status st = check_common(fn, num_kv_heads, head_dim, block_size, dtype);
   if (st != PKV_OK) return st;
   if (dtype != PKV_BF16) return pkv_failf(PKV_ERR_UNSUPPORTED, "%s: only bf16 is built", fn);
-  if (block_size != kMfmaBlockSize)
-    return pkv_failf(PKV_ERR_UNSUPPORTED, "%s: only block_size %d is built", fn, kMfmaBlockSize);
   if (num_seqs < 0 || num_query_tokens < 0 || max_query_len < 0 || max_context_len < 0)
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: negative size", fn);
   if (num_heads <= 0 || num_heads % num_kv_heads != 0)
@@ -599,8 +598,7 @@ pkv_status pkv_attention_prefill_chunk(float* out, const void* q, const int32_t*
                      fn, num_heads, num_kv_heads);
   if (num_blocks <= 0) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: num_blocks must be > 0", fn);
   if (max_blocks_per_seq <= 0) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: max_blocks_per_seq must be > 0", fn);
-  if (!std::isfinite(scale) || !(scale > 0.f))
-    return pkv_failf(PKV_ERR_INVALID_ARG, "%s: scale must be positive and finite", fn);
+  if (!std::isfinite(scale)) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: scale is not finite", fn);
   if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0) return PKV_OK;
   if (!out || !q || !query_start_loc || !k_cache || !v_cache || !block_tables || !context_lens)
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: NULL pointer", fn);
@@ -626,8 +624,10 @@ pkv_status pkv_attention_prefill_chunk(float* out, const void* q, const int32_t*
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;
   a.num_blocks = num_blocks;
+  a.block_size = block_size;
   a.max_context_len = max_context_len;
-  a.scale_log2 = scale * 1.4426950408889634f;
+  a.scale_log2 = scale != 0.f ? std::fabs(scale) * 1.4426950408889634f : 1.f;
+  a.q_mode = scale > 0.f ? 0 : scale < 0.f ? 1 : 2;
   return hip_status(fn, pkv_launch_prefill(a, stream));
 }
 

@@ -40,11 +40,12 @@ int pkv_launch_swap_blocks(void* k_dst, void* v_dst, int32_t dst_blocks, const v
 constexpr int32_t kMinPartTokens = 1024;
 constexpr int32_t kMaxPartTokens = 4096;
 constexpr int32_t kMaxMfmaGroup = 16;
-constexpr int32_t kMfmaBlockSize = 16;   // the matrix-core kernels' block size
-// Whether decode of these heads runs on the MFMA group kernel.
+// Whether decode of these heads runs on the MFMA group kernel (any block size:
+// the matrix-core kernels walk contexts in 16-key tiles).
 inline bool pkv_uses_mfma(int dtype, int32_t num_heads, int32_t num_kv_heads, int32_t block_size) {
   const int32_t group = num_heads / num_kv_heads;
-  return dtype == PKV_BF16 && group >= 2 && group <= kMaxMfmaGroup && block_size == kMfmaBlockSize;
+  (void)block_size;
+  return dtype == PKV_BF16 && group >= 2 && group <= kMaxMfmaGroup;
 }
 inline int32_t pkv_part_tokens(int dtype, int32_t num_heads, int32_t num_kv_heads, int32_t block_size) {
   return pkv_uses_mfma(dtype, num_heads, num_kv_heads, block_size) ? kMaxPartTokens : kMinPartTokens;
@@ -163,8 +164,14 @@ struct pkv_prefill_args {
   int32_t num_kv_heads;
   int32_t head_dim;
   int32_t num_blocks;
+  int32_t block_size;             // 8, 16 or 32
   int32_t max_context_len;
+  // The kernel exponentiates scores times scale_log2 > 0; the scale's sign
+  // goes into the query: q_mode 0 uses q, 1 uses -q (scale < 0: the scores
+  // scale * q.k = |scale| * (-q).k, exactly), 2 uses q = 0 (scale 0: every
+  // visible key weighs the same).
   float scale_log2;
+  int32_t q_mode;
 };
 // Query rows (token, head of a KV group) per prefill workgroup.
 constexpr int32_t kPrefillRowsPerWg = 128;

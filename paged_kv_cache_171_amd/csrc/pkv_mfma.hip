@@ -146,18 +146,20 @@ __device__ __forceinline__ int vswz(int r) {
   return 2 * ((r / kRowsPerLine) % (kSlots / 2));
 }
 
-template <int D>
+template <int D, int BS>
 __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a, uint32_t bid, bool shared_unit) {
   constexpr int KC = D / 32;            // 32-dim chunks of q.k
   constexpr int DC = D / 16;            // 16-dim chunks of the output
   constexpr int RB = D * 2;             // bytes per key row
-  constexpr int kSlots = RB / 16;
-  constexpr int NLD = kBlock * RB / 1024;   // 1 KiB direct-to-LDS loads per V tile
+  constexpr int kT = 16;                // keys per MFMA tile (the unit of the walk)
+  constexpr int NLD = kT * RB / 1024;   // 1 KiB direct-to-LDS loads per V tile
   constexpr int OROW = D + 4;           // padded LDS row (floats) of the wave merge
-  constexpr int kVBytes = kWaves * 2 * kBlock * RB;     // two V tiles per wave
+  constexpr int kVBytes = kWaves * 2 * kT * RB;     // two V tiles per wave
   constexpr int kOBytes = kWaves * 16 * OROW * 4;
   constexpr int kSmem = kVBytes > kOBytes ? kVBytes : kOBytes;
-  constexpr int64_t kTile = static_cast<int64_t>(kBlock) * RB;
+  constexpr int64_t kHeadTile = static_cast<int64_t>(BS) * RB;   // one (block, head) tile of the pool
+  static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
+  static_assert(RB * 8 % 1024 == 0 || RB * 4 % 1024 == 0, "a 1 KiB load covers rows of one 8-row half");
   __shared__ __align__(16) char smem[kSmem];
   __shared__ float sm_ml[kWaves][16][2];
   __shared__ int sm_bad[kWaves];
@@ -173,10 +175,11 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
   const int32_t u = static_cast<int32_t>(bid / static_cast<uint32_t>(Hkv));
   const int32_t kvh = static_cast<int32_t>(bid - static_cast<uint32_t>(u) * Hkv);
   // The unit: rows r < nrows are (sequence s0 + r / G, query head kvh*G + r % G);
-  // it walks blocks blk_begin .. blk_end-1 of s0's table, keys below ctx valid,
+  // it walks the 16-key tiles t_begin .. t_end-1 of s0's context (tile t is
+  // tokens 16t .. 16t+15, whatever blocks hold them), keys below ctx valid,
   // and writes the output rows (direct) or partial slot `slot` of each row.
-  int32_t s0, nrows, ctx, blk_begin, blk_end, slot;
-  int32_t nslots = 0;     // partial slots of each row (merged in this launch when tickets are given)
+  int32_t s0, nrows, ctx, t_begin, t_end, slot;
+  int32_t nslots = 0;     // partial slots of each row (merged in this launch)
   bool direct;
   if (shared_unit) {
     // a group's shared leading blocks: the rows are the group's sequences (a
@@ -188,8 +191,8 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
     s0 = su[0];
     nrows = min(su[1], kMaxMfmaGroup / G) * G;
     ctx = su[3];
-    blk_begin = su[2] * (a.prefix_part_tokens / kBlock);
-    blk_end = min(ctx / kBlock, blk_begin + a.prefix_part_tokens / kBlock);
+    t_begin = su[2] * (a.prefix_part_tokens / kT);
+    t_end = min(ctx / kT, t_begin + a.prefix_part_tokens / kT);
     slot = su[2];
     direct = false;
   } else {
@@ -213,25 +216,26 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
       return;
     }
     const int32_t part = a.part_tokens;
-    const int32_t start = pkvd::seq_start_of(a, s);
+    const int32_t start = pkvd::seq_start_of(a, s);     // a multiple of 16
     const int32_t base = pkvd::slot_base_of(a, start);
     const int32_t np_s = (ctx - start + part - 1) / part;
-    const int32_t nblk = (ctx + kBlock - 1) / kBlock;
+    const int32_t ntiles = (ctx + kT - 1) / kT;
     s0 = s;
     nrows = G;
-    blk_begin = start / kBlock + p * (part / kBlock);
-    blk_end = min(nblk, blk_begin + part / kBlock);
+    t_begin = start / kT + p * (part / kT);
+    t_end = min(ntiles, t_begin + part / kT);
     slot = base + p;
     nslots = base + np_s;
     direct = np_s == 1 && base == 0;
   }
 
-  const int64_t block_bytes = static_cast<int64_t>(Hkv) * kTile;
-  const char* __restrict__ kc = reinterpret_cast<const char*>(a.k_cache) + kvh * kTile;
-  const char* __restrict__ vc = reinterpret_cast<const char*>(a.v_cache) + kvh * kTile;
+  const int64_t block_bytes = static_cast<int64_t>(Hkv) * kHeadTile;
+  const char* __restrict__ kc = reinterpret_cast<const char*>(a.k_cache) + kvh * kHeadTile;
+  const char* __restrict__ vc = reinterpret_cast<const char*>(a.v_cache) + kvh * kHeadTile;
   const int32_t* __restrict__ table = a.block_tables + static_cast<int64_t>(s0) * a.max_blocks_per_seq;
+  const int32_t nblk = (ctx + BS - 1) / BS;
 
-  char* vs = smem + wave * (2 * kBlock * RB);      // this wave's two V tiles
+  char* vs = smem + wave * (2 * kT * RB);      // this wave's two V tiles
 
   // Q^T as the B operand: lane (n, g) holds dims 32c + 8g .. +8 of row n.
   bf16x8 qb[KC];
@@ -247,8 +251,10 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
     }
   }
 
-  // per-lane pieces of the V tile traffic: DMA source offset (swizzled) and
-  // transposed-read address (key row 4g + n/4, dims 4(n%4) of each 16-dim chunk)
+  // per-lane pieces of the V tile traffic: for each 1 KiB copy, the tile row
+  // r this lane reads times RB plus the byte offset within the row (swizzled
+  // slot), and the transposed-read address (key row 4g + n/4, dims 4(n%4) of
+  // each 16-dim chunk)
   int dma_off[NLD];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
@@ -266,79 +272,157 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
   bool bad = false;
 
   // The step's new token (decode with the cache write).  Only the wave that
-  // loads the sequence's last block uses it: there it checks that the new slot
+  // loads the tile of token ctx-1 uses it: there it checks that the new slot
   // is token ctx-1's, takes that row (and the unused rows after it) from the
   // new K/V and stores the row into the pool.  The slot is loaded here and
   // waited for only there.
   const int64_t new_slot = (a.new_slots && !shared_unit) ? a.new_slots[s0] : -1;
-  const int32_t last_blk = (ctx + kBlock - 1) / kBlock - 1;
-  const int32_t last_row = (ctx - 1) % kBlock;
+  const int32_t last_tile = (ctx + kT - 1) / kT - 1;
+  const int32_t last_row = (ctx - 1) % kT;                   // row of token ctx-1 in its tile
   const int64_t new_src = (static_cast<int64_t>(s0) * Hkv + kvh) * RB;
 
-  // The wave's block ids (at most kMaxPartTokens/16/4 = 64 of them), one per lane,
-  // fetched once before the loop; each block takes its id with a lane read.
-  const int32_t nit = (blk_end - blk_begin - wave + kWaves - 1) / kWaves;
-  const int32_t my_ids = lane < nit ? table[blk_begin + wave + kWaves * lane] : 0;
+  // The wave's tiles' block ids (at most kMaxPartTokens/16/4 = 64 tiles), one
+  // tile per lane, fetched once before the loop: the block of rows 0-7 (lo)
+  // and of rows 8-15 (hi) of the tile -- the same block unless blocks hold 8
+  // tokens; a block past the context is never read (its rows get row 0's).
+  const int32_t nit = (t_end - t_begin - wave + kWaves - 1) / kWaves;
+  int32_t ids_lo = 0, ids_hi = 0;
+  if (lane < nit) {
+    const int32_t t = t_begin + wave + kWaves * lane;
+    ids_lo = table[(kT * t) / BS];
+    if constexpr (BS == 8) ids_hi = kT * t + 8 < ctx ? table[(kT * t + 8) / BS] : ids_lo;
+  }
+  // Byte offset of row r of tile t in its block's (block, head) tile: the
+  // tile's offset in the block (0 unless a block holds two tiles) plus the
+  // row's (within its 8-token block, when blocks hold 8 tokens).
+  auto tile_off = [&](int32_t t) -> int64_t { return BS == 32 ? static_cast<int64_t>(t & 1) * kT * RB : 0; };
+  auto row_in = [&](int r) -> int { return BS == 8 ? (r & 7) * RB : r * RB; };
 
-  // Loads of block `it`: K into registers, V into an LDS tile.  V rows of keys
-  // past the context are copied from key 0 of the block instead (finite data;
-  // their probabilities are 0), so the copies need no branches.
+  // Loads of the wave's tile `it`: K into registers, V into an LDS tile.  V
+  // rows of keys past the context are copied from row 0 of the tile instead
+  // (finite data; their probabilities are 0), so the copies need no branches.
   auto issue = [&](int32_t it, u32x4 (&kt)[KC], char* tile) {
-    const int32_t j = blk_begin + wave + kWaves * it;
-    const int32_t raw_id = __builtin_amdgcn_readlane(my_ids, it);
-    int32_t id = raw_id;
-    if (static_cast<uint32_t>(id) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; id = 0; }
-    const char* kp = kc + id * block_bytes;
-    const char* vp = vc + id * block_bytes;
-    const int32_t valid_rows = min(kBlock, ctx - j * kBlock);
-    int mode = 0;       // 0: all rows from the pool; 1: the new token's block; 2: a wrong slot
-    if (j == last_blk) {
-      if (new_slot >= 0)
+    const int32_t t = t_begin + wave + kWaves * it;
+    if constexpr (BS != 8) {
+      // one block holds the whole tile (a tile is a block, or half of one)
+      const int32_t raw_id = __builtin_amdgcn_readlane(ids_lo, it);
+      int32_t id = raw_id;
+      if (static_cast<uint32_t>(id) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; id = 0; }
+      const char* kp = kc + id * block_bytes + tile_off(t);
+      const char* vp = vc + id * block_bytes + tile_off(t);
+      const int32_t valid_rows = min(kT, ctx - t * kT);
+      int mode = 0;       // 0: all rows from the pool; 1: the new token's block; 2: a wrong slot
+      if (t == last_tile && new_slot >= 0)
         mode = (static_cast<uint32_t>(raw_id) < static_cast<uint32_t>(a.num_blocks) &&
-                new_slot == static_cast<int64_t>(raw_id) * kBlock + last_row) ? 1 : 2;
+                new_slot == static_cast<int64_t>(raw_id) * BS + (ctx - 1) % BS) ? 1 : 2;
+      if (mode != 1) {
+        if (mode == 2) bad = true;    // not token ctx-1's slot: NaN rows, nothing stored
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+          kt[c] = n < valid_rows ? load16_nt(kp + n * RB + 64 * c + 16 * g) : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+          const int src = (1024 * i + 16 * lane) / RB < valid_rows ? dma_off[i] : dma_off[i] % RB;
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vp + src),
+                                           (__attribute__((address_space(3))) void*)(tile + 1024 * i), 16, 0, 0);
+        }
+      } else {
+        const char* nk = reinterpret_cast<const char*>(a.new_k) + new_src;
+        const char* nv = reinterpret_cast<const char*>(a.new_v) + new_src;
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+          kt[c] = n < last_row ? load16_nt(kp + n * RB + 64 * c + 16 * g)
+                  : n == last_row ? *reinterpret_cast<const u32x4*>(nk + 64 * c + 16 * g) : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+          const char* src = (1024 * i + 16 * lane) / RB < last_row ? vp + dma_off[i] : nv + dma_off[i] % RB;
+          __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                           (__attribute__((address_space(3))) void*)(tile + 1024 * i), 16, 0, 0);
+        }
+        if (n == last_row) {
+#pragma unroll
+          for (int c = 0; c < KC; ++c) {
+            *reinterpret_cast<u32x4*>(const_cast<char*>(kp) + last_row * RB + 64 * c + 16 * g) = kt[c];
+            *reinterpret_cast<u32x4*>(const_cast<char*>(vp) + last_row * RB + 64 * c + 16 * g) =
+                *reinterpret_cast<const u32x4*>(nv + 64 * c + 16 * g);
+          }
+        }
+      }
+      return;
+    }
+    const int32_t raw_lo = __builtin_amdgcn_readlane(ids_lo, it);
+    const int32_t raw_hi = BS == 8 ? __builtin_amdgcn_readlane(ids_hi, it) : raw_lo;
+    int32_t id_lo = raw_lo, id_hi = raw_hi;
+    if (static_cast<uint32_t>(id_lo) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; id_lo = 0; }
+    if (BS == 8) {
+      if (static_cast<uint32_t>(id_hi) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; id_hi = 0; }
+    } else {
+      id_hi = id_lo;
+    }
+    const int64_t toff = tile_off(t);
+    const char* kbase = kc + toff;
+    const char* vbase = vc + toff;
+    // block of tile row r (the same for every row unless blocks hold 8 tokens)
+    auto blk = [&](int r) -> int64_t { return static_cast<int64_t>(BS == 8 && r >= 8 ? id_hi : id_lo) * block_bytes; };
+    const int32_t valid_rows = min(kT, ctx - t * kT);
+    int mode = 0;       // 0: all rows from the pool; 1: the new token's tile; 2: a wrong slot
+    if (t == last_tile && new_slot >= 0) {
+      const int32_t raw_last = BS == 8 && last_row >= 8 ? raw_hi : raw_lo;
+      mode = (static_cast<uint32_t>(raw_last) < static_cast<uint32_t>(a.num_blocks) &&
+              new_slot == static_cast<int64_t>(raw_last) * BS + (ctx - 1) % BS) ? 1 : 2;
     }
     if (mode != 1) {
       if (mode == 2) bad = true;    // not token ctx-1's slot: NaN rows, nothing stored
       // keys past the context are not loaded (their scores are masked)
+      const char* kp = kbase + blk(n) + n * RB - (BS == 8 && n >= 8 ? 8 * RB : 0);
 #pragma unroll
-      for (int c = 0; c < KC; ++c)
-        kt[c] = n < valid_rows ? load16_nt(kp + n * RB + 64 * c + 16 * g) : u32x4{0, 0, 0, 0};
+      for (int c = 0; c < KC; ++c) kt[c] = n < valid_rows ? load16_nt(kp + 64 * c + 16 * g) : u32x4{0, 0, 0, 0};
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
-        const int src = (1024 * i + 16 * lane) / RB < valid_rows ? dma_off[i] : dma_off[i] % RB;
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(vp + src),
+        const char* src;
+        if constexpr (BS == 8) {
+          const int row = dma_off[i] / RB, col = dma_off[i] % RB;
+          const int r = row < valid_rows ? row : 0;
+          src = vbase + blk(r) + row_in(r) + col;
+        } else {
+          // one block holds the whole tile: the rows at their offsets, row 0's past the context
+          src = vbase + blk(0) + ((1024 * i + 16 * lane) / RB < valid_rows ? dma_off[i] : dma_off[i] % RB);
+        }
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
                                          (__attribute__((address_space(3))) void*)(tile + 1024 * i), 16, 0, 0);
       }
     } else {
-      // the block of the new token: its row, and the unused rows after it,
+      // the tile of the new token: its row, and the unused rows after it,
       // come from the new K/V (finite data; the unused rows are masked); the
       // lanes of the new row store it into the pool
       const char* nk = reinterpret_cast<const char*>(a.new_k) + new_src;
       const char* nv = reinterpret_cast<const char*>(a.new_v) + new_src;
+      const char* kp = kbase + blk(n) + row_in(n);
 #pragma unroll
       for (int c = 0; c < KC; ++c)
-        kt[c] = n < last_row ? load16_nt(kp + n * RB + 64 * c + 16 * g)
+        kt[c] = n < last_row ? load16_nt(kp + 64 * c + 16 * g)
                 : n == last_row ? *reinterpret_cast<const u32x4*>(nk + 64 * c + 16 * g) : u32x4{0, 0, 0, 0};
 #pragma unroll
       for (int i = 0; i < NLD; ++i) {
-        const char* src = (1024 * i + 16 * lane) / RB < last_row ? vp + dma_off[i] : nv + dma_off[i] % RB;
+        const int row = dma_off[i] / RB, col = dma_off[i] % RB;
+        const char* src = row < last_row ? vbase + blk(row) + row_in(row) + col : nv + col;
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
                                          (__attribute__((address_space(3))) void*)(tile + 1024 * i), 16, 0, 0);
       }
       if (n == last_row) {
+        char* vp = const_cast<char*>(vbase) + blk(n) + row_in(n);
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
-          *reinterpret_cast<u32x4*>(const_cast<char*>(kp) + last_row * RB + 64 * c + 16 * g) = kt[c];
-          *reinterpret_cast<u32x4*>(const_cast<char*>(vp) + last_row * RB + 64 * c + 16 * g) =
-              *reinterpret_cast<const u32x4*>(nv + 64 * c + 16 * g);
+          *reinterpret_cast<u32x4*>(const_cast<char*>(kp) + 64 * c + 16 * g) = kt[c];
+          *reinterpret_cast<u32x4*>(vp + 64 * c + 16 * g) = *reinterpret_cast<const u32x4*>(nv + 64 * c + 16 * g);
         }
       }
     }
   };
-  // Online-softmax update of block `it` from its K registers and V tile.
+  // Online-softmax update of tile `it` from its K registers and V tile.
   auto compute = [&](int32_t it, const u32x4 (&kt)[KC], const char* tile) {
-    const int32_t j = blk_begin + wave + kWaves * it;
-    const int32_t valid_rows = min(kBlock, ctx - j * kBlock);
+    const int32_t t = t_begin + wave + kWaves * it;
+    const int32_t valid_rows = min(kT, ctx - t * kT);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < KC; ++c) acc = mfma(as_bf16x8(kt[c]), qb[c], acc);
@@ -367,16 +451,17 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
       const s16x4 vt = lds_read_tr(trb + 16 * ((2 * c + tr_k0) ^ tr_sw));
-      f32x4 t = o[c] * alpha;
-      t = mfma16(vt, ph, t);
-      o[c] = mfma16(vt, pl, t);
+      f32x4 tacc = o[c] * alpha;
+      tacc = mfma16(vt, ph, tacc);
+      o[c] = mfma16(vt, pl, tacc);
     }
   };
-  // Two blocks per step: both blocks' K and V loads are issued, then both are
+  (void)nblk;
+  // Two tiles per step: both tiles' K and V loads are issued, then both are
   // computed, so a wave keeps 2 x (K + V) tiles in flight.
   u32x4 ktA[KC], ktB[KC];
   char* tileA = vs;
-  char* tileB = vs + kBlock * RB;
+  char* tileB = vs + kT * RB;
   for (int32_t it = 0; it < nit; it += 2) {
     issue(it, ktA, tileA);
     if (it + 1 < nit) issue(it + 1, ktB, tileB);
@@ -420,7 +505,6 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
       if (d == 0) { pkvd::store_coherent(a.part_ml + 2 * pidx, M); pkvd::store_coherent(a.part_ml + 2 * pidx + 1, L); }
     }
   }
-  (void)kSlots;
   // a split context: the last of the sequence's units (for this KV head) to
   // finish merges its G rows
   if (direct) return;
@@ -463,9 +547,11 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
   }
 }
 
-template <int D, bool kShared>
-__global__ __launch_bounds__(256, 4) void decode_group_mfma_kernel(pkv_decode_args a) {
-  decode_group_mfma_body<D>(a, blockIdx.x, kShared);
+// 8-token blocks take two block ids per tile: three workgroups per CU, so the
+// body keeps its registers
+template <int D, int BS>
+__global__ __launch_bounds__(256, BS == 8 ? 3 : 4) void decode_group_mfma_kernel(pkv_decode_args a) {
+  decode_group_mfma_body<D, BS>(a, blockIdx.x, false);
 }
 
 // Shared-prefix decode in one launch: the first shared_wgs workgroups take
@@ -473,15 +559,16 @@ __global__ __launch_bounds__(256, 4) void decode_group_mfma_kernel(pkv_decode_ar
 // units -- on the MFMA group kernel for grouped-query heads, else the VALU
 // kernel -- so the short per-sequence units fill the CUs the long shared units
 // leave free instead of waiting for them.
-template <int D, bool kGroupTail>
-__global__ __launch_bounds__(256, 4) void decode_shared_fused_kernel(pkv_decode_args a, uint32_t shared_wgs) {
+template <int D, int BS, bool kGroupTail>
+__global__ __launch_bounds__(256, BS == 8 ? 3 : 4) void decode_shared_fused_kernel(pkv_decode_args a,
+                                                                                  uint32_t shared_wgs) {
   if constexpr (kGroupTail) {
     const bool shared_unit = blockIdx.x < shared_wgs;
-    decode_group_mfma_body<D>(a, shared_unit ? blockIdx.x : blockIdx.x - shared_wgs, shared_unit);
+    decode_group_mfma_body<D, BS>(a, shared_unit ? blockIdx.x : blockIdx.x - shared_wgs, shared_unit);
   } else if (blockIdx.x < shared_wgs) {
-    decode_group_mfma_body<D>(a, blockIdx.x, true);
+    decode_group_mfma_body<D, BS>(a, blockIdx.x, true);
   } else {
-    decode_valu_body<uint16_t, D, kBlock>(a, blockIdx.x - shared_wgs);
+    decode_valu_body<uint16_t, D, BS>(a, blockIdx.x - shared_wgs);
   }
 }
 
@@ -515,7 +602,7 @@ __device__ __forceinline__ void shared_plan_body(const pkv_decode_args& a, const
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int32_t S = a.num_seqs, MB = a.max_blocks_per_seq;
+  const int32_t S = a.num_seqs, MB = a.max_blocks_per_seq, BSZ = a.block_size;
   if (tid == 0) { sm_units = 0; sm_bad = 0; }
   __syncthreads();
   if (num_groups <= 0 && tid == 0) sm_bad = 1;      // no groups: no shared prefix
@@ -539,7 +626,7 @@ __device__ __forceinline__ void shared_plan_body(const pkv_decode_args& a, const
       int32_t lim = 0x7FFFFFFF;
       for (int32_t m = b + lane; m < e; m += 64) {
         const int32_t ctx = a.context_lens[m];
-        lim = min(lim, len_ok(ctx, a.max_context_len, MB, kBlock) ? ctx / kBlock : -1);
+        lim = min(lim, len_ok(ctx, a.max_context_len, MB, BSZ) ? ctx / BSZ : -1);
       }
       lim = wave_min(lim);
       int32_t cp = 0;
@@ -570,7 +657,9 @@ __device__ __forceinline__ void shared_plan_body(const pkv_decode_args& a, const
           }
         }
       }
-      const int32_t pref = cp * kBlock;
+      // the prefix is walked in 16-key tiles: with 8-token blocks an odd last
+      // common block is left to the members' own units
+      const int32_t pref = (cp * BSZ) & ~15;
       for (int32_t m = b + lane; m < e; m += 64) seq_start[m] = pref;
       if (pref > 0) {
         const int32_t nsub = (n + per_sub - 1) / per_sub;
@@ -667,19 +756,22 @@ __device__ __forceinline__ void copy16_to_lds_at(const char* base, uint32_t voff
 // fp32 and in the bf16 pair, and the accumulator rescale is skipped.
 constexpr float kRescaleLog2 = 8.f;
 
-template <int D>
+template <int D, int BS>
 __global__ __launch_bounds__(kPrefillThreads, 4) void prefill_chunk_mfma_kernel(pkv_prefill_args a) {
   constexpr int KC = D / 32;
   constexpr int DC = D / 16;
   constexpr int RB = D * 2;
   constexpr int kTiles = kPrefillRowsPerWg / 16 / kPrefillWaves;   // 16-row tiles per wave
   constexpr int kStages = 4;                       // LDS ring depth (pairs)
-  constexpr int kTileBytes = kBlock * RB;          // one block's K (or V) rows of one head
+  constexpr int kTileBytes = kBlock * RB;          // 16 keys' K (or V) rows of one head: an LDS tile
   constexpr int kTileKiB = kTileBytes / 1024;
   constexpr int kStageBytes = 4 * kTileBytes;      // K0 K1 V0 V1
   constexpr int kCopies = kStageBytes / (16 * kPrefillThreads);   // 16-byte copies per thread per stage
   static_assert(kStageBytes % (16 * kPrefillThreads) == 0 && kTiles >= 1, "prefill shape");
-  constexpr int64_t kTile = kTileBytes;
+  constexpr int64_t kHeadTile = static_cast<int64_t>(BS) * RB;   // one (block, head) tile of the pool
+  constexpr int kBPP = 2 * kBlock / BS;            // blocks per 32-key pair
+  static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
+  static_assert(RB * 8 >= 1024, "a 1 KiB copy covers rows of one 8-token block");
   __shared__ __align__(16) char ring[kStages][kStageBytes];
 
   const int lane = threadIdx.x & 63;
@@ -700,7 +792,7 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void prefill_chunk_mfma_kernel(
   if (r0 >= rows) return;
   const int32_t r_end = min(rows, r0 + kPrefillRowsPerWg);
   const int32_t ctx = a.context_lens[s];
-  if (ctx < nq || !len_ok(ctx, a.max_context_len, a.max_blocks_per_seq, kBlock)) {
+  if (ctx < nq || !len_ok(ctx, a.max_context_len, a.max_blocks_per_seq, BS)) {
     for (int idx = threadIdx.x; idx < (r_end - r0) * D; idx += kPrefillThreads) {
       const int32_t r = r0 + idx / D, d = idx % D;
       a.out[((static_cast<int64_t>(q0) + r / G) * Hq + kvh * G + r % G) * D + d] = __builtin_nanf("");
@@ -709,22 +801,24 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void prefill_chunk_mfma_kernel(
   }
   const int32_t first_pos = ctx - nq;            // position of query 0
   const int32_t* __restrict__ table = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq;
-  const int64_t block_bytes = static_cast<int64_t>(Hkv) * kTile;
-  const char* __restrict__ kc = reinterpret_cast<const char*>(a.k_cache) + kvh * kTile;
-  const char* __restrict__ vc = reinterpret_cast<const char*>(a.v_cache) + kvh * kTile;
+  const int64_t block_bytes = static_cast<int64_t>(Hkv) * kHeadTile;
+  const char* __restrict__ kc = reinterpret_cast<const char*>(a.k_cache) + kvh * kHeadTile;
+  const char* __restrict__ vc = reinterpret_cast<const char*>(a.v_cache) + kvh * kHeadTile;
 
   const int32_t wg_lim = first_pos + (r_end - 1) / G + 1;      // keys the workgroup needs
   const int32_t npairs = (wg_lim + 2 * kBlock - 1) / (2 * kBlock);
-  const int32_t nblk = (ctx + kBlock - 1) / kBlock;
+  const int32_t nblk = (ctx + BS - 1) / BS;
   bool bad = false;
 
   // Copy i of wave w fills KiB kPrefillWaves*i + w of a stage: tile t = that KiB
   // / (tile KiB) (0: K0, 1: K1, 2: V0, 3: V1), rows of the tile in lane order;
   // LDS row r holds slot k of the tile row at the swizzled source slot.  The
-  // per-lane source offsets are fixed: row r's, and row 0's for keys past the
-  // context (finite data that gets probability 0).
+  // copy reads rows of one pool block (block cp_blk[i] of the pair: a 1 KiB
+  // copy never spans two blocks); the per-lane source offsets within it are
+  // fixed: the row's, and the block's row 0 for keys past the context (finite
+  // data that gets probability 0).
   uint32_t cp_off[kCopies], cp_off0[kCopies];
-  int32_t cp_row[kCopies];
+  int32_t cp_key[kCopies], cp_blk[kCopies];
 #pragma unroll
   for (int i = 0; i < kCopies; ++i) {
     const int kib = kPrefillWaves * i + wave;
@@ -732,44 +826,49 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void prefill_chunk_mfma_kernel(
     const int off = (kib % kTileKiB) * 1024 + 16 * lane;
     const int r = off / RB, k = (off % RB) / 16;
     const int slot = t < 2 ? (k ^ kswz<D>(r)) : (k ^ vswz<D>(r));
-    cp_row[i] = r;
-    cp_off[i] = static_cast<uint32_t>(r * RB + 16 * slot);
+    const int key = kBlock * (t & 1) + r;                 // key of the row within the pair
+    cp_key[i] = key;
+    cp_blk[i] = ((kib % kTileKiB) * 1024 / RB + kBlock * (t & 1)) / BS;   // the copy's first row's block
+    cp_off[i] = static_cast<uint32_t>((key % BS) * RB + 16 * slot);
     cp_off0[i] = static_cast<uint32_t>(16 * slot);
   }
-  // the pair's block ids; the second is the first again past the last block
-  auto issue = [&](int32_t pp, int32_t id0, int32_t id1, char* stage) {
-    if (static_cast<uint32_t>(id0) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; id0 = 0; }
-    if (static_cast<uint32_t>(id1) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; id1 = 0; }
-    const bool tail = (2 * pp + 2) * kBlock > ctx;     // some keys of the pair lie past the context
+  // the pair's block ids: ids[q] holds keys 32 pp + BS q ..; past the last
+  // block a copy takes the pair's first block (all its rows past the context)
+  auto issue = [&](int32_t pp, int32_t (&ids)[kBPP], char* stage) {
+#pragma unroll
+    for (int q = 0; q < kBPP; ++q)
+      if (static_cast<uint32_t>(ids[q]) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; ids[q] = 0; }
+    const bool tail = (pp + 1) * 2 * kBlock > ctx;     // some keys of the pair lie past the context
 #pragma unroll
     for (int i = 0; i < kCopies; ++i) {
       const int kib = kPrefillWaves * i + wave;
       const int t = kib / kTileKiB;
-      const int b = t & 1;
-      const int32_t j = 2 * pp + b;
-      const int32_t id = (b == 0 || j >= nblk) ? id0 : id1;
+      const int32_t j = kBPP * pp + cp_blk[i];
+      const int32_t id = j < nblk ? ids[cp_blk[i]] : ids[0];
       const char* base = (t < 2 ? kc : vc) + id * block_bytes;
       uint32_t voff = cp_off[i];
-      if (tail && j * kBlock + cp_row[i] >= ctx) voff = cp_off0[i];
+      if (tail && pp * 2 * kBlock + cp_key[i] >= ctx) voff = cp_off0[i];
       copy16_to_lds_at(base, voff, stage + kib * 1024);
     }
   };
-  // the block ids of pair pp; past the last block the pair's second block is
-  // its first one again
-  auto pair_ids = [&](int32_t pp, int32_t& id0, int32_t& id1) {
-    id0 = load_block_id(table, 2 * pp);
-    id1 = load_block_id(table, __builtin_amdgcn_readfirstlane(min(2 * pp + 1, nblk - 1)));
+  // the block ids of pair pp (entries past the context's last block are not
+  // read: the last one is read again instead)
+  auto pair_ids = [&](int32_t pp, int32_t (&ids)[kBPP]) {
+#pragma unroll
+    for (int q = 0; q < kBPP; ++q) ids[q] = load_block_id(table, __builtin_amdgcn_readfirstlane(min(kBPP * pp + q, nblk - 1)));
   };
 #pragma unroll
   for (int pp = 0; pp < kStages - 1; ++pp)
     if (pp < npairs) {
-      int32_t id0, id1;
-      pair_ids(pp, id0, id1);
-      issue(pp, id0, id1, ring[pp]);
+      int32_t ids[kBPP];
+      pair_ids(pp, ids);
+      issue(pp, ids, ring[pp]);
     }
   // the ids of the next pair to issue, loaded a pair ahead of its copies
-  int32_t nid0 = 0, nid1 = 0;
-  if (kStages - 1 < npairs) pair_ids(kStages - 1, nid0, nid1);
+  int32_t nids[kBPP];
+#pragma unroll
+  for (int q = 0; q < kBPP; ++q) nids[q] = 0;
+  if (kStages - 1 < npairs) pair_ids(kStages - 1, nids);
 
   // this lane's rows (one per tile) and their key limits; invalid rows: limit 0,
   // q = 0 (their results are never written).  Keys below nomask_lim are visible
@@ -795,12 +894,13 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void prefill_chunk_mfma_kernel(
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 64 * c + 16 * g);
-      if (!valid) w = u32x4{0, 0, 0, 0};
+      if (!valid || a.q_mode == 2) w = u32x4{0, 0, 0, 0};
+      if (a.q_mode == 1) w ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};   // -q, exactly
       qb[tt][c] = as_bf16x8(w);
     }
   }
 
-  const float c2 = a.scale_log2;                 // > 0
+  const float c2 = a.scale_log2;                 // > 0 (the scale's sign is in q)
   const float rescale_raw = kRescaleLog2 / c2;   // kRescaleLog2 in raw score units
 
   // m: the row's running maximum in log2 units (scores times c2); thr: the raw
@@ -948,13 +1048,15 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void prefill_chunk_mfma_kernel(
       // ids of the pair after it are loaded now, with no LDS read pending,
       // and arrive during the barrier
       const int32_t pn = pp + kStages - 1;
-      const int32_t id0 = nid0, id1 = nid1;
-      if (pn + 1 < npairs) pair_ids(pn + 1, nid0, nid1);
+      int32_t ids[kBPP];
+#pragma unroll
+      for (int q = 0; q < kBPP; ++q) ids[q] = nids[q];
+      if (pn + 1 < npairs) pair_ids(pn + 1, nids);
       __builtin_amdgcn_s_barrier();
       pair(pp, ring[st]);
       // every wave passed the barrier after it finished the pair before this
       // one, so that pair's stage takes pair pp + kStages - 1
-      if (pn < npairs) issue(pn, id0, id1, ring[(st + kStages - 1) % kStages]);
+      if (pn < npairs) issue(pn, ids, ring[(st + kStages - 1) % kStages]);
     }
   }
 
@@ -979,15 +1081,45 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void prefill_chunk_mfma_kernel(
 
 }  // namespace
 
+namespace {
+// A kernel instance for the launch's head_dim and block size.
+template <template <int, int> class K, typename... Args>
+void launch_d_bs(int head_dim, int block_size, dim3 grid, hipStream_t st, Args... args) {
+  if (head_dim == 128) {
+    if (block_size == 8) K<128, 8>::launch(grid, st, args...);
+    else if (block_size == 32) K<128, 32>::launch(grid, st, args...);
+    else K<128, 16>::launch(grid, st, args...);
+  } else {
+    if (block_size == 8) K<64, 8>::launch(grid, st, args...);
+    else if (block_size == 32) K<64, 32>::launch(grid, st, args...);
+    else K<64, 16>::launch(grid, st, args...);
+  }
+}
+template <int D, int BS>
+struct GroupDecode {
+  static void launch(dim3 grid, hipStream_t st, const pkv_decode_args& a) {
+    hipLaunchKernelGGL((decode_group_mfma_kernel<D, BS>), grid, dim3(256), 0, st, a);
+  }
+};
+template <int D, int BS>
+struct SharedFusedGroupTail {
+  static void launch(dim3 grid, hipStream_t st, const pkv_decode_args& a, uint32_t sw) {
+    hipLaunchKernelGGL((decode_shared_fused_kernel<D, BS, true>), grid, dim3(256), 0, st, a, sw);
+  }
+};
+template <int D, int BS>
+struct SharedFusedValuTail {
+  static void launch(dim3 grid, hipStream_t st, const pkv_decode_args& a, uint32_t sw) {
+    hipLaunchKernelGGL((decode_shared_fused_kernel<D, BS, false>), grid, dim3(256), 0, st, a, sw);
+  }
+};
+}  // namespace
+
 int pkv_launch_decode_group(const pkv_decode_args& a, void* stream) {
   const int64_t np = (a.max_context_len + a.part_tokens - 1) / a.part_tokens;
   const int64_t grid = static_cast<int64_t>(a.num_seqs) * (np < 1 ? 1 : np) * a.num_kv_heads;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (a.head_dim == 128) {
-    hipLaunchKernelGGL((decode_group_mfma_kernel<128, false>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st, a);
-  } else {
-    hipLaunchKernelGGL((decode_group_mfma_kernel<64, false>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st, a);
-  }
+  launch_d_bs<GroupDecode>(a.head_dim, a.block_size, dim3(static_cast<uint32_t>(grid)),
+                           static_cast<hipStream_t>(stream), a);
   return hipGetLastError();
 }
 
@@ -1008,28 +1140,26 @@ int pkv_launch_shared_fused(const pkv_decode_args& a, void* stream) {
   const dim3 grid(static_cast<uint32_t>(shared + own));
   const uint32_t sw = static_cast<uint32_t>(shared);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (a.head_dim == 128) {
-    if (group_tail) hipLaunchKernelGGL((decode_shared_fused_kernel<128, true>), grid, dim3(256), 0, st, a, sw);
-    else hipLaunchKernelGGL((decode_shared_fused_kernel<128, false>), grid, dim3(256), 0, st, a, sw);
-  } else {
-    if (group_tail) hipLaunchKernelGGL((decode_shared_fused_kernel<64, true>), grid, dim3(256), 0, st, a, sw);
-    else hipLaunchKernelGGL((decode_shared_fused_kernel<64, false>), grid, dim3(256), 0, st, a, sw);
-  }
+  if (group_tail) launch_d_bs<SharedFusedGroupTail>(a.head_dim, a.block_size, grid, st, a, sw);
+  else launch_d_bs<SharedFusedValuTail>(a.head_dim, a.block_size, grid, st, a, sw);
   return hipGetLastError();
 }
+
+namespace {
+template <int D, int BS>
+struct Prefill {
+  static void launch(dim3 grid, hipStream_t st, const pkv_prefill_args& a) {
+    hipLaunchKernelGGL((prefill_chunk_mfma_kernel<D, BS>), grid, dim3(kPrefillThreads), 0, st, a);
+  }
+};
+}  // namespace
 
 int pkv_launch_prefill(const pkv_prefill_args& a, void* stream) {
   const int32_t group = a.num_heads / a.num_kv_heads;
   const int64_t tiles = (static_cast<int64_t>(a.max_query_len) * group + kPrefillRowsPerWg - 1) / kPrefillRowsPerWg;
   const int64_t grid = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * tiles;
   if (grid == 0) return hipSuccess;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (a.head_dim == 128) {
-    hipLaunchKernelGGL((prefill_chunk_mfma_kernel<128>), dim3(static_cast<uint32_t>(grid)), dim3(kPrefillThreads), 0,
-                       st, a);
-  } else {
-    hipLaunchKernelGGL((prefill_chunk_mfma_kernel<64>), dim3(static_cast<uint32_t>(grid)), dim3(kPrefillThreads), 0,
-                       st, a);
-  }
+  launch_d_bs<Prefill>(a.head_dim, a.block_size, dim3(static_cast<uint32_t>(grid)), static_cast<hipStream_t>(stream),
+                       a);
   return hipGetLastError();
 }

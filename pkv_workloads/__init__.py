@@ -269,11 +269,13 @@ def from_lengths(seed: int, ctx, hq: int, hkv: int, d: int, dtype: str, pool_fac
                          block_size=block_size)
 
 
-def random_prefill(seed: int, ctxs, n_queries, hq: int, hkv: int, d: int, pool_factor: float = 1.3) -> Workload:
+def random_prefill(seed: int, ctxs, n_queries, hq: int, hkv: int, d: int, pool_factor: float = 1.3,
+                   block_size: int = BLOCK_SIZE) -> Workload:
     """Chunked-prefill parity cases: sequence s has ctxs[s] cached tokens, the last
     n_queries[s] of which are its chunk's queries (bf16).  Every sequence also
     carries one decode query."""
-    w = _plain_decode(f"prefill{seed}", seed + 104729, ctxs, hq, hkv, d, "bf16", pool_factor=pool_factor)
+    w = _plain_decode(f"prefill{seed}", seed + 104729, ctxs, hq, hkv, d, "bf16", pool_factor=pool_factor,
+                      block_size=block_size)
     rng = np.random.default_rng(seed + 31337)
     nq = np.asarray(n_queries, dtype=np.int32)
     w.chunk_seqs = list(range(len(ctxs)))
@@ -313,7 +315,7 @@ def serving(seed: int = 6, num_requests: int = 24, hq: int = 8, hkv: int = 2, d:
             prompt_median: float = 40.0, output_median: float = 30.0, sigma: float = 0.8,
             max_prompt: int = 160, max_output: int = 96, num_blocks: int = 40,
             max_num_seqs: int = 8, max_num_batched_tokens: int = 256, num_host_blocks: int = 160,
-            dtype: str = "bf16", with_rows: bool = True) -> ServingWorkload:
+            dtype: str = "bf16", with_rows: bool = True, block_size: int = BLOCK_SIZE) -> ServingWorkload:
     """A request stream for the continuous-batching loop: prompt and output
     lengths lognormal (the right-skewed mix of "Batching Continuo y
     PagedAttention", section on static batching), clipped to
@@ -324,7 +326,7 @@ def serving(seed: int = 6, num_requests: int = 24, hq: int = 8, hkv: int = 2, d:
     prompts = lognormal_lengths(rng, num_requests, prompt_median, sigma, 1,
                                 min(max_prompt, max_num_batched_tokens))
     outputs = lognormal_lengths(rng, num_requests, output_median, sigma, 1, max_output)
-    cap = num_blocks * BLOCK_SIZE
+    cap = num_blocks * block_size
     outputs = np.minimum(outputs, cap - prompts).astype(np.int32)
     if np.any(outputs < 1):
         raise ValueError("device pool too small for the prompts drawn")
@@ -342,7 +344,7 @@ def serving(seed: int = 6, num_requests: int = 24, hq: int = 8, hkv: int = 2, d:
         q_rows = np.empty((0, hq, d), dtype=empty.dtype)
     return ServingWorkload(f"serving{seed}", dtype, hq, hkv, d, num_blocks, perm, num_host_blocks,
                            max_num_seqs, max_num_batched_tokens, prompts, outputs, row_start,
-                           k_rows, v_rows, q_rows, np.float32(1.0 / math.sqrt(d)))
+                           k_rows, v_rows, q_rows, np.float32(1.0 / math.sqrt(d)), block_size=block_size)
 
 
 WORKLOADS = {1: tiny, 2: shaped_13b, 3: gqa, 4: parallel_sampling, 5: long_mix}

@@ -158,7 +158,7 @@ def test_batch_rejects_bad_arguments_before_any_device_call(P):
     s16 = P.Scheduler(a16, 4, 64)
     hb = L.pkv_batch_host_bytes(4, 64, 8, 20)
     db = L.pkv_batch_device_bytes(4, 64, 8, 20, 8, 64)
-    assert hb > 0 and db > hb // 2
+    assert hb > 0 and db >= hb // 2          # device: the index region (plan included) and the partials
     out = ctypes.c_void_p()
     # (sched, MB, NB, NH, Hq, Hkv, d, dtype, host, hb, dev, db, out)
     assert L.pkv_batch_create(None, 8, 20, 0, 8, 8, 64, 1, 256, hb, 512, db, ctypes.byref(out)) == P.PKV_ERR_INVALID_ARG
@@ -169,9 +169,10 @@ def test_batch_rejects_bad_arguments_before_any_device_call(P):
     assert L.pkv_batch_create(s16._h, 8, 20, 0, 8, 8, 64, 1, 256, hb - 1, 512, db, ctypes.byref(out)) == P.PKV_ERR_INVALID_ARG
     assert L.pkv_batch_create(s16._h, 8, 20, 0, 8, 8, 64, 1, 256, hb, 512, db - 1, ctypes.byref(out)) == P.PKV_ERR_INVALID_ARG
     assert L.pkv_batch_create(s16._h, 8, 20, 0, 8, 8, 64, 1, 256, hb, 520, db, ctypes.byref(out)) == P.PKV_ERR_INVALID_ARG
+    # 8-token blocks are taken; their sizes are checked the same way
     a8 = P.BlockAllocator(20, 8)
     s8 = P.Scheduler(a8, 4, 64)
-    assert L.pkv_batch_create(s8._h, 8, 20, 0, 8, 8, 64, 1, 256, hb, 512, db, ctypes.byref(out)) == P.PKV_ERR_UNSUPPORTED
+    assert L.pkv_batch_create(s8._h, 8, 20, 0, 8, 8, 64, 1, 256, hb - 1, 512, db, ctypes.byref(out)) == P.PKV_ERR_INVALID_ARG
     assert L.pkv_batch_schedule(None, None, None) == P.PKV_ERR_INVALID_ARG
     assert L.pkv_batch_layer(None, None, None, None, None, None, None, None, None, 1.0, None) == P.PKV_ERR_INVALID_ARG
     assert L.pkv_scheduler_max_num_seqs(s16._h) == 4 and L.pkv_scheduler_max_num_batched_tokens(s16._h) == 64
@@ -260,9 +261,9 @@ def test_allocator_errors_are_status_codes(P):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dtype=0), 3), (dict(head_dim=96), 3), (dict(block_size=8), 3), (dict(num_heads=6, num_kv_heads=4), 1),
+    (dict(dtype=0), 3), (dict(head_dim=96), 3), (dict(block_size=12), 3), (dict(num_heads=6, num_kv_heads=4), 1),
     (dict(q=None), 1), (dict(max_query_len=-1), 1), (dict(out=17), 1), (dict(num_blocks=0), 1),
-    (dict(scale=float("inf")), 1), (dict(scale=-0.125), 1), (dict(scale=0.0), 1),
+    (dict(scale=float("inf")), 1), (dict(scale=float("nan")), 1),
 ])
 def test_prefill_rejects_bad_arguments(P, kw, code):
     args = dict(out=16, q=32, qsl=48, tq=8, mql=4, k_cache=64, v_cache=80, tables=96, mb=4, lens=112, num_seqs=2,

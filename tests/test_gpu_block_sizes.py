@@ -1,9 +1,11 @@
 """Block sizes 8 and 32 (the 16 of the pages is covered everywhere else) through
 the C ABI against the oracle: allocator tables, slots, copy-on-write pairs and
 whole pools bit-exact after copy + append; decode attention (fp32 within 1e-5,
-bf16 within 2e-3) for MHA and grouped-query heads (which run on the vector-ALU
-kernel at these sizes), planned decode, a plan built for another block size,
-swap copies, and the calls built for 16-token blocks only."""
+bf16 within 2e-3) for MHA (vector-ALU kernel) and grouped-query heads (the
+matrix-core kernel, which walks contexts in 16-key tiles: two 8-token blocks
+or half a 32-token block per tile), planned decode, a plan built for another
+block size, swap copies, shared-prefix decode (plain and planned) and causal
+chunked prefill at these sizes."""
 import numpy as np
 import pytest
 
@@ -53,7 +55,8 @@ def _check(w, planned=False):
 @pytest.mark.parametrize("bs", [8, 32])
 @pytest.mark.parametrize("dtype,hq,hkv,d,max_ctx", [("f32", 4, 4, 64, 700), ("f32", 8, 2, 128, 2100),
                                                     ("bf16", 8, 8, 128, 2500), ("bf16", 16, 2, 64, 1500),
-                                                    ("bf16", 32, 8, 128, 900)])
+                                                    ("bf16", 32, 8, 128, 900), ("bf16", 16, 2, 128, 9000),
+                                                    ("bf16", 8, 4, 128, 77)])
 def test_decode_and_cache_ops(bs, dtype, hq, hkv, d, max_ctx):
     print(f"case: bs={bs} {dtype} {hq}/{hkv} d={d} ctx<={max_ctx}", flush=True)
     w = W.random_small(100 + bs, 9, max_ctx, hq, hkv, d, dtype, block_size=bs)
@@ -97,22 +100,48 @@ def test_swap_copies(bs):
     assert np.array_equal(pool_to_host(ghk), hk) and np.array_equal(pool_to_host(ghv), hv)
 
 
-def test_sixteen_token_only_calls():
-    print("case: bs 16-only calls", flush=True)
-    w = W.parallel_sampling(seed=41, groups=2, samples=[3, 2], prompt=[70, 50], tail_lo=0, tail_hi=20, hq=8, d=128,
-                            block_size=8)
+@pytest.mark.parametrize("bs", [8, 32])
+@pytest.mark.parametrize("hq,hkv,d", [(8, 8, 128), (16, 2, 128), (4, 4, 64)])
+def test_shared_prefix_decode(bs, hq, hkv, d):
+    """The groups' common leading blocks read once on the matrix cores (with
+    8-token blocks an odd last common block is left to the members' own
+    units): the oracle's result, and planned calls give the same bits."""
+    print(f"case: bs={bs} shared {hq}/{hkv} d={d}", flush=True)
+    w = W.parallel_sampling(seed=41 + bs, groups=3, samples=[5, 2, 8], prompt=[70, 1100, 200], tail_lo=0,
+                            tail_hi=50, hq=hq, hkv=hkv, d=d, block_size=bs)
     g, qd, td, ld, mcl = _check(w)
-    # shared-prefix decode at block size 8 runs plain decode: same result
-    out = torch.zeros((5, 8, 128), dtype=torch.float32, device="cuda")
-    plain = torch.zeros_like(out)
-    PK.pkv_attention_decode(plain, qd, g.k_pool, g.v_pool, td, ld, mcl, float(w.scale))
+    r = _oracle(w)
+    S = len(w.decode_seqs)
     gs = torch.tensor(w.group_start, dtype=torch.int32, device="cuda")
+    out = torch.full((S, hq, d), -1.0, dtype=torch.float32, device="cuda")
     PK.pkv_attention_decode_shared(out, qd, g.k_pool, g.v_pool, td, ld, gs, mcl, float(w.scale))
+    plan = PK.shared_plan_for(td, ld, gs, hq, hkv, mcl, PK.PKV_BF16, block_size=bs)
+    out2 = torch.full_like(out, -2.0)
+    PK.pkv_attention_decode_shared_planned(out2, qd, g.k_pool, g.v_pool, td, ld, mcl, float(w.scale), plan)
     torch.cuda.synchronize()
-    assert torch.equal(out, plain)
-    # chunked prefill is built for 16-token blocks only
-    with pytest.raises(PK.PkvError) as e:
-        PK.pkv_attention_prefill_chunk(torch.empty((2, 8, 128), device="cuda"), qd[:2].contiguous(),
-                                       torch.tensor([0, 2], dtype=torch.int32, device="cuda"), 2, g.k_pool, g.v_pool,
-                                       td[:1].contiguous(), ld[:1].contiguous(), mcl, float(w.scale))
-    assert e.value.status == PK.PKV_ERR_UNSUPPORTED
+    ref = O.decode_attention(w.q, r.k_pool, r.v_pool, [r.alloc.block_table(s) for s in w.decode_seqs],
+                             [r.alloc.num_tokens(s) for s in w.decode_seqs], w.scale, block_size=bs)
+    assert float(np.abs(out.cpu().numpy() - ref).max()) <= TOL["bf16"]
+    assert torch.equal(out, out2)
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+@pytest.mark.parametrize("ctxs,nqs,hq,hkv,d", [
+    ([60, 300, 700], [37, 64, 100], 8, 2, 128),
+    ([16, 33, 129, 1], [16, 1, 129, 1], 4, 4, 64),
+    ([1000, 45], [200, 5], 32, 1, 128),
+])
+def test_chunked_prefill(bs, ctxs, nqs, hq, hkv, d):
+    """Causal chunked prefill with 8- or 32-token blocks (a 32-key pair of the
+    kernel is four 8-token blocks or one 32-token block), every query row
+    against the oracle."""
+    print(f"case: bs={bs} prefill ctx={ctxs} n={nqs} H={hq}/{hkv} d={d}", flush=True)
+    w = W.random_prefill(90 + bs, ctxs, nqs, hq, hkv, d, block_size=bs)
+    g, r = GpuReplay(w), _oracle(w)
+    out, _, _ = g.prefill()
+    tables = [r.alloc.block_table(s) for s in w.chunk_seqs]
+    lens = [r.alloc.num_tokens(s) for s in w.chunk_seqs]
+    ref = O.prefill_chunk_attention(w.chunk_q, w.chunk_query_start_loc, r.k_pool, r.v_pool, tables, lens, w.scale,
+                                    block_size=bs)
+    assert np.isfinite(out).all()
+    assert float(np.abs(out - ref).max()) <= TOL["bf16"]

@@ -1,8 +1,8 @@
 """Decode with the step's cache write (pkv_attention_decode_append) against the
 oracle's two steps -- write each sequence's new token at its slot, then decode
 over the whole context: pools bit-exact afterwards, outputs within 1e-5 (fp32)
-/ 2e-3 (bf16), on the VALU kernel (MHA, fp32, block sizes 8 and 32) and the
-MFMA group kernel (GQA), across partition splits, with sequences that have no
+/ 2e-3 (bf16), on the VALU kernel (MHA, fp32) and the MFMA group kernel
+(GQA), at block sizes 8, 16 and 32, across partition splits, with sequences that have no
 new token (slot -1), a slot that is not the last token's (NaN rows, nothing
 written) and a planned call."""
 import numpy as np
@@ -83,6 +83,9 @@ def _run(w, seed, no_new=(), wrong=(), planned=False):
     (4, 5, 900, 8, 2, 64, "f32", 16),        # grouped heads on the VALU kernel
     (5, 7, 700, 4, 4, 128, "bf16", 8),
     (6, 7, 1300, 8, 8, 64, "f32", 32),
+    (7, 6, 5000, 16, 2, 128, "bf16", 8),     # MFMA group kernel: two 8-token blocks per 16-key tile
+    (8, 6, 5000, 16, 2, 128, "bf16", 32),    # MFMA group kernel: two 16-key tiles per block
+    (9, 9, 300, 8, 4, 64, "bf16", 8),        # the new token in either half of a tile
 ])
 def test_decode_append_matches_write_then_decode(seed, S, max_ctx, hq, hkv, d, dtype, bs):
     print(f"case: decode_append seed={seed} {dtype} {hq}/{hkv} d={d} bs={bs}", flush=True)
@@ -91,10 +94,11 @@ def test_decode_append_matches_write_then_decode(seed, S, max_ctx, hq, hkv, d, d
     _run(w, seed + 1, planned=True)
 
 
-def test_no_new_token_and_a_wrong_slot():
-    print("case: decode_append -1 and wrong slots", flush=True)
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_no_new_token_and_a_wrong_slot(bs):
+    print(f"case: decode_append -1 and wrong slots bs={bs}", flush=True)
     for hq, hkv in ((8, 8), (16, 2)):
-        w = W.random_small(77, 8, 700, hq, hkv, 128, "bf16")
+        w = W.random_small(77, 8, 700, hq, hkv, 128, "bf16", block_size=bs)
         _run(w, 9, no_new=(1, 4), wrong=(2, 6))
 
 

@@ -484,6 +484,20 @@ def test_prefill_with_a_wide_score_range():
     assert err <= TOL["bf16"], err
 
 
+@pytest.mark.parametrize("scale", [-0.3, 0.0, -1.0])
+def test_prefill_with_negative_and_zero_scales(scale):
+    """Any finite scale, as decode takes: a negative one reverses the scores'
+    order, zero weighs every visible key the same."""
+    w = W.random_prefill(69, [500, 90, 33], [70, 90, 3], 8, 2, 128)
+    w.scale = np.float32(scale)
+    print(f"case: prefill scale {scale}", flush=True)
+    g, r = GpuReplay(w), _oracle(w)
+    out, _, _ = g.prefill()
+    assert np.isfinite(out).all()
+    err = float(np.abs(out - _prefill_ref(r, w)).max())
+    assert err <= TOL["bf16"], err
+
+
 def test_prefill_nan_in_unused_slots_never_reaches_the_output():
     w = W.random_prefill(65, [70, 33], [20, 33], 8, 2, 128)
     print("case: prefill nan poison", flush=True)

@@ -132,16 +132,18 @@ def test_serving_loop_with_grouped_heads_and_long_prompts():
 
 def _serve_native(w, policy):
     """The same loop through the native step executor (pkv_batch_schedule once
-    per step, pkv_batch_layer for the one layer)."""
+    per step, which also builds the decode plan on the host; pkv_batch_layer
+    for the one layer), at the workload's block size."""
     dev = "cuda"
-    alloc = PK.BlockAllocator(w.num_blocks, 16, w.initial_free_order)
+    bs = w.block_size
+    alloc = PK.BlockAllocator(w.num_blocks, bs, w.initial_free_order)
     sched = PK.Scheduler(alloc, w.max_num_seqs, w.max_num_batched_tokens, policy, w.num_host_blocks)
     for p, o in zip(w.prompts, w.outputs):
         sched.add_request(int(p), int(o))
-    mb = int(-(-int((w.prompts + w.outputs).max()) // 16))
+    mb = int(-(-int((w.prompts + w.outputs).max()) // bs))
     batch = PK.Batch(sched, mb, w.num_blocks, w.num_host_blocks, w.num_heads, w.num_kv_heads, w.head_dim)
     tdt = torch.bfloat16
-    shape = (w.num_blocks, w.num_kv_heads, 16, w.head_dim)
+    shape = (w.num_blocks, w.num_kv_heads, bs, w.head_dim)
     k_pool, v_pool = torch.zeros(shape, dtype=tdt, device=dev), torch.zeros(shape, dtype=tdt, device=dev)
     hshape = (w.num_host_blocks,) + shape[1:]
     k_host, v_host = torch.zeros(hshape, dtype=tdt).pin_memory(), torch.zeros(hshape, dtype=tdt).pin_memory()
@@ -203,3 +205,18 @@ def test_native_step_executor_with_grouped_heads():
     steps, swaps, err = _serve_native(w, SC.CONTINUOUS)
     assert err <= TOL
 
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+def test_native_step_executor_at_other_block_sizes(bs):
+    """Block sizes 8 and 32 through the executor: the matrix-core prefill and
+    grouped-query decode at that size, the host-built plan, swaps of whole
+    blocks; step by step against the oracle loop."""
+    print(f"case: native serving bs={bs}", flush=True)
+    w = W.serving(seed=10 + bs, num_requests=16, hq=8, hkv=2, d=128, prompt_median=120, output_median=40,
+                  max_prompt=300, max_output=100, num_blocks=60 * 16 // bs, max_num_seqs=6,
+                  max_num_batched_tokens=512, num_host_blocks=200 * 16 // bs, block_size=bs)
+    steps, swaps, err = _serve_native(w, SC.CONTINUOUS)
+    print(f"steps={steps} swaps={swaps} err={err:.2e}", flush=True)
+    assert err <= TOL
+    assert swaps > 0

@@ -533,61 +533,76 @@ def serve_bench(args):
 
 
 def blocksize_bench(args):
-    """The 13B-shaped decode batch (64 seqs, 40 MHA heads x 128, bf16, lognormal
-    contexts) with 8-, 16- and 32-token blocks: per block size the block-table
-    entries, the slots reserved but unused in each sequence's last block (the
-    tail waste of [CB] "PagedAttention: Memoria virtual para la KV cache"), and
-    the decode kernel's time and K/V bandwidth over 8 layer pools (each 1.2x the
-    blocks needed at that size, shuffled)."""
+    """Block sizes 8, 16 and 32 on two batches: the 13B-shaped decode (64 seqs,
+    40 MHA heads x 128, bf16, lognormal contexts; the vector-ALU kernel, 8
+    layer pools) and the grouped-query batch (256 seqs, 64 query / 8 KV heads,
+    contexts U[128, 4096]; the matrix-core kernel, which walks 16-key tiles --
+    two 8-token blocks or half a 32-token block each; 4 layer pools).  Per
+    block size the block-table entries, the slots reserved but unused in each
+    sequence's last block (the tail waste of [CB] "PagedAttention: Memoria
+    virtual para la KV cache"), and the decode kernel's time and K/V bandwidth
+    (each pool 1.2x the blocks needed at that size, shuffled)."""
     import torch
     import paged_kv_cache_171_amd as PK
     import pkv_workloads as W
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
-    L, H, D = 8, 40, 128
     gen = torch.Generator(device=dev)
     gen.manual_seed(args.seed)
     reps = max(args.steps, 3)
-    rows = []
-    for bs in (8, 16, 32):
-        w = W.shaped_13b(seed=args.seed, with_rows=False, block_size=bs)
-        alloc = PK.BlockAllocator(w.num_blocks, bs, w.initial_free_order)
-        for op in w.ops:
-            if op[0] == "create":
-                alloc.seq_create()
-            elif op[0] == "append":
-                alloc.seq_append_slots(op[1], op[2])
-        seqs = w.decode_seqs
-        lens = np.array([alloc.seq_block_table(s)[1] for s in seqs], dtype=np.int32)
-        MB = int(-(-lens.max() // bs))
-        tables, _ = alloc.block_tables(seqs, MB)
-        pools = [(torch.randn(w.num_blocks, H, bs, D, generator=gen, device=dev).to(torch.bfloat16),
-                  torch.randn(w.num_blocks, H, bs, D, generator=gen, device=dev).to(torch.bfloat16)) for _ in range(L)]
-        q = torch.randn(len(seqs), H, D, generator=gen, device=dev).to(torch.bfloat16)
-        out = torch.empty(len(seqs), H, D, dtype=torch.float32, device=dev)
-        td, ld = torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev)
-        mcl = int(lens.max())
-        ws = PK.workspace_for(len(seqs), H, D, mcl, device=dev)
-        plan = PK.plan_for(ld, H, H, MB, mcl, PK.PKV_BF16, block_size=bs)
 
-        def decode_all():
-            for kp, vp in pools:
-                PK.pkv_attention_decode(out, q, kp, vp, td, ld, mcl, 1.0 / math.sqrt(D), workspace=ws, plan=plan)
-        decode_all()
-        torch.cuda.synchronize()
-        dec_us = _timed(decode_all, reps, stream) / L
-        blocks = int(sum(-(-int(c) // bs) for c in lens))
-        kv = int(lens.sum()) * 2 * H * D * 2
-        rows.append({"block_size": bs, "pool_blocks": w.num_blocks, "table_entries": blocks,
-                     "table_bytes_padded": len(seqs) * MB * 4,
-                     "tail_waste_frac": round(1 - int(lens.sum()) / (blocks * bs), 4),
-                     "decode_us_per_layer": round(dec_us, 2), "decode_kv_gbps": round(kv / dec_us / 1e3, 1),
-                     "decode_hbm_peak_frac": round(kv / dec_us / 1e3 / HBM_PEAK_GBPS, 4)})
-        del pools
-        torch.cuda.empty_cache()
-    print(json.dumps({"workload": "blocksize", "layers": L, "num_seqs": 64, "heads": H, "head_dim": D,
-                      "kernel": "decode_valu_kernel<bf16,128,BS> + merge", "sweep": rows}), flush=True)
+    def sweep(make, L, kernel):
+        rows = []
+        for bs in (8, 16, 32):
+            w = make(bs)
+            H, Hkv, D = w.num_heads, w.num_kv_heads, w.head_dim
+            alloc = PK.BlockAllocator(w.num_blocks, bs, w.initial_free_order)
+            for op in w.ops:
+                if op[0] == "create":
+                    alloc.seq_create()
+                elif op[0] == "append":
+                    alloc.seq_append_slots(op[1], op[2])
+            seqs = w.decode_seqs
+            lens = np.array([alloc.seq_block_table(s)[1] for s in seqs], dtype=np.int32)
+            MB = int(-(-lens.max() // bs))
+            tables, _ = alloc.block_tables(seqs, MB)
+            pools = [(torch.randn(w.num_blocks, Hkv, bs, D, generator=gen, device=dev).to(torch.bfloat16),
+                      torch.randn(w.num_blocks, Hkv, bs, D, generator=gen, device=dev).to(torch.bfloat16))
+                     for _ in range(L)]
+            q = torch.randn(len(seqs), H, D, generator=gen, device=dev).to(torch.bfloat16)
+            out = torch.empty(len(seqs), H, D, dtype=torch.float32, device=dev)
+            td, ld = torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev)
+            mcl = int(lens.max())
+            ws = PK.workspace_for(len(seqs), H, D, mcl, device=dev)
+            plan = PK.plan_for(ld, H, Hkv, MB, mcl, PK.PKV_BF16, block_size=bs)
+
+            def decode_all():
+                for kp, vp in pools:
+                    PK.pkv_attention_decode(out, q, kp, vp, td, ld, mcl, 1.0 / math.sqrt(D), workspace=ws,
+                                            plan=plan)
+            decode_all()
+            torch.cuda.synchronize()
+            dec_us = _timed(decode_all, reps, stream) / L
+            blocks = int(sum(-(-int(c) // bs) for c in lens))
+            kv = int(lens.sum()) * 2 * Hkv * D * 2
+            rows.append({"block_size": bs, "pool_blocks": w.num_blocks, "table_entries": blocks,
+                         "table_bytes_padded": len(seqs) * MB * 4,
+                         "tail_waste_frac": round(1 - int(lens.sum()) / (blocks * bs), 4),
+                         "decode_us_per_layer": round(dec_us, 2), "decode_kv_gbps": round(kv / dec_us / 1e3, 1),
+                         "decode_hbm_peak_frac": round(kv / dec_us / 1e3 / HBM_PEAK_GBPS, 4)})
+            del pools
+            torch.cuda.empty_cache()
+        return {"kernel": kernel, "layers": L, "sweep": rows}
+
+    res = {"workload": "blocksize",
+           "13b": dict(num_seqs=64, heads="40/40", head_dim=128,
+                       **sweep(lambda bs: W.shaped_13b(seed=args.seed, with_rows=False, block_size=bs), 8,
+                               "decode_valu_kernel<bf16,128,BS> (merge inside)")),
+           "gqa": dict(num_seqs=256, heads="64/8", head_dim=128,
+                       **sweep(lambda bs: W.gqa(with_rows=False, block_size=bs), 4,
+                               "decode_group_mfma_kernel<128,BS> (merge inside)"))}
+    print(json.dumps(res), flush=True)
 
 
 def main():

@@ -36,9 +36,9 @@
  *    trade-off it describes); head_dim 64 or 128; dtype PKV_F32 or PKV_BF16
  *    (the same dtype for q, K and V); num_heads a multiple of num_kv_heads.
  *    The matrix-core kernels -- grouped-query bf16 decode, shared-prefix
- *    decode, chunked prefill -- are built for block_size 16: with another size
- *    grouped-query decode runs on the vector-ALU kernel, shared-prefix decode
- *    runs plain decode, and prefill returns PKV_ERR_UNSUPPORTED.
+ *    decode, chunked prefill -- walk contexts in 16-key tiles and take every
+ *    supported block size: a tile is two 8-token blocks, one 16-token block
+ *    or half of a 32-token block.
  *  - Calls that enqueue work on one stream are ordered by that stream.  For one
  *    decode step the caller enqueues pkv_copy_blocks, then pkv_append, then the
  *    attention calls: copies must read shared blocks before this step writes.
@@ -356,9 +356,10 @@ pkv_status pkv_attention_decode_shared_planned(float* out, const void* q, const 
  * [0, num_query_tokens] or is longer than max_query_len is skipped (its rows
  * are not written); one whose context is shorter than n_s, longer than
  * max_context_len or max_blocks_per_seq*block_size, or whose table names a
- * block outside [0, num_blocks), gets NaN rows.  scale must be positive
- * (PKV_ERR_INVALID_ARG otherwise: the kernel takes row maxima of unscaled
- * scores).  No workspace.
+ * block outside [0, num_blocks), gets NaN rows.  scale may be any finite
+ * value (PKV_ERR_INVALID_ARG for NaN or infinity): the kernel takes row
+ * maxima of scores scaled by |scale|, with the sign moved into the query
+ * (a zero scale gives the plain mean of the visible V rows).  No workspace.
  * ------------------------------------------------------------------------ */
 pkv_status pkv_attention_prefill_chunk(float* out, const void* q, const int32_t* query_start_loc,
                                        int32_t num_query_tokens, int32_t max_query_len, const void* k_cache,

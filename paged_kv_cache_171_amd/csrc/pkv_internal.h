@@ -99,7 +99,7 @@ struct pkv_decode_args {
   int32_t num_kv_heads;
   int32_t head_dim;
   int32_t num_blocks;
-  int32_t block_size;      // tokens per block: 8, 16 or 32 (16 for the MFMA kernels)
+  int32_t block_size;      // tokens per block: 8, 16 or 32
   int32_t max_context_len;
   int32_t num_partitions;  // NP = ceil(max_context_len / kMinPartTokens): partial slots per row
   int32_t part_tokens;     // tokens per partition for this launch

@@ -156,11 +156,12 @@ def shaped_13b(seed: int = 2, num_seqs: int = 64, with_rows: bool = True, block_
 
 
 def gqa(seed: int = 3, num_seqs: int = 256, lo: int = 128, hi: int = 4096,
-        with_rows: bool = True) -> Workload:
-    """Workload 3: 256 seqs, 64 q / 8 KV heads, d 128, bf16, ctx U[128, 4096], pool 1.2x."""
+        with_rows: bool = True, block_size: int = BLOCK_SIZE) -> Workload:
+    """Workload 3: 256 seqs, 64 q / 8 KV heads, d 128, bf16, ctx U[128, 4096], pool 1.2x
+    (of the pages needed at ``block_size``)."""
     rng = np.random.default_rng(seed)
     ctx = rng.integers(lo, hi + 1, size=num_seqs).astype(np.int32)
-    return _plain_decode("gqa", seed + 1000, ctx, 64, 8, 128, "bf16", with_rows=with_rows)
+    return _plain_decode("gqa", seed + 1000, ctx, 64, 8, 128, "bf16", with_rows=with_rows, block_size=block_size)
 
 
 def parallel_sampling(seed: int = 4, groups: int = 32, samples=8, prompt=1000,

@@ -37,6 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+FP32_MFMA_PEAK_TFLOPS = 157.3   # dense fp32 matrix-core peak of the MI355X
 METRIC = "paged decode attention: KV GB/s and % of HBM peak; decode tokens/s per step"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_13b_counters.md")
 # the sources the headline decode kernel is built from
@@ -192,6 +193,8 @@ def secondary_cpu_check(name, cases, target_s: float):
             if time.perf_counter() - t0 > target_s:
                 break
     res["tol"] = 2e-3
+    if any(label.endswith("_f32") for label, _ in cases):
+        res["f32_tol"] = 1e-5
     res["seconds"] = round(time.perf_counter() - t0, 1)
     return res
 
@@ -345,6 +348,24 @@ def secondary(args):
                     "prefill_mfma_peak_frac": round(flops / pf_us / 1e6 / 2500.0, 4),
                     "prefill_tokens_per_s_per_layer": round(int(nq.sum()) / pf_us * 1e6, 1),
                     "prefill_kernel": "prefill_chunk_mfma_kernel"})
+        # the same chunks over float32 pools (2 layers of the same tables): the
+        # fp32 matrix-core kernel, against the fp32 MFMA peak
+        fpools = [(torch.randn(NB, Hkv, P, D, generator=gen, device=dev),
+                   torch.randn(NB, Hkv, P, D, generator=gen, device=dev)) for _ in range(2)]
+        cq32 = torch.randn(int(nq.sum()), Hq, D, generator=gen, device=dev)
+        cout32 = torch.empty_like(cout)
+
+        def prefill_f32_all():
+            for kp, vp in fpools:
+                PK.pkv_attention_prefill_chunk(cout32, cq32, qsl, int(nq.max()), kp, vp, ctd, cld, int(clens.max()),
+                                               scale)
+        prefill_f32_all()
+        torch.cuda.synchronize()
+        pf32_us = _timed(prefill_f32_all, reps, stream) / len(fpools)
+        res.update({"prefill_f32_us_per_layer": round(pf32_us, 2),
+                    "prefill_f32_tflops": round(flops / pf32_us / 1e6, 1),
+                    "prefill_f32_mfma_peak_frac": round(flops / pf32_us / 1e6 / FP32_MFMA_PEAK_TFLOPS, 4),
+                    "prefill_f32_kernel": "prefill_chunk_f32_kernel"})
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = secondary_oracle_check(args, w, pools[-1], q, td, ld, tables_h, lens_h, scale,
                                                      locals())
@@ -393,6 +414,17 @@ def secondary_oracle_check(args, w, pool, q, td, ld, tables_h, lens_h, scale, en
             ref = O.prefill_chunk_attention(cqh[a:b], np.array([0, b - a], dtype=np.int32), kh, vh, ctl[:1],
                                             [int(clens[0])], scale)
             return ref, cout.cpu().numpy()[a:b], (b - a) * Hq
+        kp32, vp32 = env["fpools"][-1]
+        kh32, vh32, cqh32, cout32 = _host_bits(kp32), _host_bits(vp32), _host_bits(env["cq32"]), env["cout32"]
+
+        def prefill_f32_fn():
+            # the float32 chunk 0's last 64 queries (the longest contexts)
+            b = int(qsl[1])
+            a = b - 64
+            ref = O.prefill_chunk_attention(cqh32[a:b], np.array([0, 64], dtype=np.int32), kh32, vh32, ctl[:1],
+                                            [int(clens[0])], scale)
+            return ref, cout32.cpu().numpy()[a:b], 64 * Hq
+        cases.append(("prefill_f32", prefill_f32_fn))
         cases.append(("prefill", prefill_fn))
     torch.cuda.synchronize()
     return secondary_cpu_check(w.name, cases, args.cpu_seconds)

@@ -348,10 +348,12 @@ pkv_status pkv_attention_decode_shared_planned(float* out, const void* q, const 
  *   for s, i < n_s, h:  g = h / (num_heads/num_kv_heads)
  *     out[qsl[s]+i][h][:] = sum_{j<=p_i} softmax_j(scale * <q[qsl[s]+i][h], K_j>) V_j
  *
- * q: device [num_query_tokens][num_heads][head_dim] bf16; out: device float32
- * of the same shape; query_start_loc: device int32 [num_seqs+1].  bf16 only
- * (PKV_ERR_UNSUPPORTED otherwise); matrix-core (MFMA) kernel with float32
- * scores, softmax and accumulation.  max_query_len must be >= every n_s (it
+ * q: device [num_query_tokens][num_heads][head_dim] in the pools' dtype; out:
+ * device float32 of the same shape; query_start_loc: device int32
+ * [num_seqs+1].  Both dtypes run on the matrix cores with float32 scores,
+ * softmax and accumulation: bf16 pools on the bf16 MFMA (probabilities as a
+ * bf16 pair, ~16 significant bits), float32 pools on the fp32 MFMA (exact
+ * fp32 products).  max_query_len must be >= every n_s (it
  * sizes the grid).  A sequence whose query range is not inside
  * [0, num_query_tokens] or is longer than max_query_len is skipped (its rows
  * are not written); one whose context is shorter than n_s, longer than
@@ -556,8 +558,9 @@ int32_t pkv_scheduler_max_num_batched_tokens(const pkv_scheduler* s);
  *   per decoding request); out gets prefill rows then decode rows.
  * k_host / v_host may be NULL when no swap copies are due.
  *
- * Limits: bf16 pools with 16-token blocks (the prefill kernel's), head_dim 64
- * or 128, query heads a multiple of KV heads; max_blocks_per_seq bounds every
+ * Limits: bf16 or float32 pools (PKV_ERR_INVALID_ARG for another dtype), the
+ * allocator's block size 8, 16 or 32, head_dim 64 or 128, query heads a
+ * multiple of KV heads; max_blocks_per_seq bounds every
  * request's table (PKV_ERR_INVALID_ARG from pkv_batch_schedule otherwise,
  * after the scheduler step).  Buffers: host_staging of
  * pkv_batch_host_bytes(...) bytes of pinned host memory and device_buffer of

@@ -387,8 +387,9 @@ def pkv_attention_prefill_chunk(out: torch.Tensor, q: torch.Tensor, query_start_
                                 max_query_len: int, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                 block_tables: torch.Tensor, context_lens: torch.Tensor, max_context_len: int,
                                 scale: float, stream=None) -> None:
-    """out fp32 [Tq, Hq, d]; q bf16 [Tq, Hq, d]; query_start_loc int32 [S+1]; block_tables int32 [S, MB];
-    context_lens int32 [S] (each sequence's chunk is the last tokens of its context)."""
+    """out fp32 [Tq, Hq, d]; q [Tq, Hq, d] in the pools' dtype (bf16 or float32); query_start_loc int32 [S+1];
+    block_tables int32 [S, MB]; context_lens int32 [S] (each sequence's chunk is the last tokens of its
+    context)."""
     _dev(out, q, query_start_loc, k_cache, v_cache, block_tables, context_lens)
     if out.dtype != torch.float32 or tuple(out.shape) != tuple(q.shape):
         raise ValueError("out must be float32 with q's shape [Tq, Hq, d]")

@@ -139,7 +139,7 @@ pkv_status pkv_batch_create(pkv_scheduler* sched, int32_t max_blocks_per_seq, in
   const int32_t bs = pkv_allocator_block_size(alloc);
   if (bs != 8 && bs != 16 && bs != 32)
     return pkv_failf(PKV_ERR_UNSUPPORTED, "%s: the allocator's block size must be 8, 16 or 32", fn);
-  if (dtype != PKV_BF16) return pkv_failf(PKV_ERR_UNSUPPORTED, "%s: only bf16 pools are built", fn);
+  if (dtype != PKV_BF16 && dtype != PKV_F32) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: unknown dtype", fn);
   if (head_dim != 64 && head_dim != 128)
     return pkv_failf(PKV_ERR_UNSUPPORTED, "%s: head_dim must be 64 or 128", fn);
   if (num_kv_heads <= 0 || num_heads <= 0 || num_heads % num_kv_heads != 0)
@@ -333,10 +333,11 @@ pkv_status pkv_batch_layer(pkv_batch* b, void* k_cache, void* v_cache, void* k_h
     if (st != PKV_OK) return st;
   }
   if (in.num_decode > 0) {
-    const size_t row = static_cast<size_t>(b->Hq) * b->d;        // q / out elements per token
-    const size_t kv_row = static_cast<size_t>(b->Hkv) * b->d * 2;  // bytes of a bf16 K or V row
+    const size_t elem = b->dtype == PKV_BF16 ? 2 : 4;                // bytes of a pool element
+    const size_t row = static_cast<size_t>(b->Hq) * b->d;            // q / out elements per token
+    const size_t kv_row = static_cast<size_t>(b->Hkv) * b->d * elem;  // bytes of a K or V row
     char* ws = b->dev + b->meta;
-    st = pkv_attention_decode_append(out + npt * row, static_cast<const char*>(q) + npt * row * 2,
+    st = pkv_attention_decode_append(out + npt * row, static_cast<const char*>(q) + npt * row * elem,
                                      static_cast<const char*>(k) + npt * kv_row,
                                      static_cast<const char*>(v) + npt * kv_row, b->slots + npt, k_cache, v_cache,
                                      b->dc_tables, b->mbd, b->dc_lens, in.num_decode, b->Hq, b->Hkv, b->d, b->BS,

@@ -590,7 +590,6 @@ pkv_status pkv_attention_prefill_chunk(float* out, const void* q, const int32_t*
   const char* fn = "pkv_attention_prefill_chunk";
   pkv_status st = check_common(fn, num_kv_heads, head_dim, block_size, dtype);
   if (st != PKV_OK) return st;
-  if (dtype != PKV_BF16) return pkv_failf(PKV_ERR_UNSUPPORTED, "%s: only bf16 is built", fn);
   if (num_seqs < 0 || num_query_tokens < 0 || max_query_len < 0 || max_context_len < 0)
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: negative size", fn);
   if (num_heads <= 0 || num_heads % num_kv_heads != 0)
@@ -605,7 +604,8 @@ pkv_status pkv_attention_prefill_chunk(float* out, const void* q, const int32_t*
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: out, q and cache pointers must be 16-byte aligned", fn);
   const int64_t group = num_heads / num_kv_heads;
-  const int64_t tiles = (static_cast<int64_t>(max_query_len) * group + kPrefillRowsPerWg - 1) / kPrefillRowsPerWg;
+  const int64_t rows_per_wg = dtype == PKV_BF16 ? kPrefillRowsPerWg : kPrefillF32RowsPerWg;
+  const int64_t tiles = (static_cast<int64_t>(max_query_len) * group + rows_per_wg - 1) / rows_per_wg;
   if (static_cast<int64_t>(num_seqs) * num_kv_heads * tiles > 0x7FFFFFFF)
     return pkv_failf(PKV_ERR_UNSUPPORTED, "%s: launch grid too large", fn);
   pkv_prefill_args a{};
@@ -628,7 +628,7 @@ pkv_status pkv_attention_prefill_chunk(float* out, const void* q, const int32_t*
   a.max_context_len = max_context_len;
   a.scale_log2 = scale != 0.f ? std::fabs(scale) * 1.4426950408889634f : 1.f;
   a.q_mode = scale > 0.f ? 0 : scale < 0.f ? 1 : 2;
-  return hip_status(fn, pkv_launch_prefill(a, stream));
+  return hip_status(fn, dtype == PKV_BF16 ? pkv_launch_prefill(a, stream) : pkv_launch_prefill_f32(a, stream));
 }
 
 }  // extern "C"

@@ -22,6 +22,25 @@ constexpr int kPlanHdr = 8;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max over the four 16-lane rows of a wave (lanes n, n+16, n+32, n+48 hold the
+// same MFMA column): swap odd rows with even ones, then halves, taking the
+// NaN-propagating maximum.
+__device__ __forceinline__ float max_over_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// A wave-uniform 32-bit load of a block id through the constant address
+// space: the compiler issues it as a scalar load and tracks its wait itself.
+// Scalar loads share their wait counter with LDS operations, not with the
+// direct-to-LDS copies (counted with the vector loads), so waiting for one
+// never drains the copies in flight.  j must be wave-uniform.
+__device__ __forceinline__ int32_t load_block_id(const int32_t* table, int32_t j) {
+  return ((const __attribute__((address_space(4))) int32_t*)table)[j];
+}
+
 // A context length that takes part in attention (others give a 0 row or a NaN row).
 __device__ __forceinline__ bool len_ok(int32_t ctx, int32_t max_context_len, int32_t max_blocks_per_seq,
                                        int32_t block_size) {

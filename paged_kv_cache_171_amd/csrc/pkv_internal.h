@@ -173,6 +173,9 @@ struct pkv_prefill_args {
   float scale_log2;
   int32_t q_mode;
 };
-// Query rows (token, head of a KV group) per prefill workgroup.
+// Query rows (token, head of a KV group) per prefill workgroup: the bf16
+// kernel, and the float32 one.
 constexpr int32_t kPrefillRowsPerWg = 128;
+constexpr int32_t kPrefillF32RowsPerWg = 64;
 int pkv_launch_prefill(const pkv_prefill_args& a, void* stream);
+int pkv_launch_prefill_f32(const pkv_prefill_args& a, void* stream);

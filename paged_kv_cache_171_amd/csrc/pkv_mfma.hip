@@ -49,6 +49,8 @@ using pkvd::kPlanHdr;
 using pkvd::fast_exp2;
 using pkvd::len_ok;
 using pkvd::plan_matches;
+using pkvd::max_over_rows;
+using pkvd::load_block_id;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -84,15 +86,6 @@ __device__ __forceinline__ u32x4 lds_read16_at(uint32_t addr) {
 // The LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
-}
-
-// A wave-uniform 32-bit load of a block id through the constant address
-// space: the compiler issues it as a scalar load and tracks its wait itself.
-// Scalar loads share their wait counter with LDS operations, not with the
-// direct-to-LDS copies (counted with the vector loads), so waiting for one
-// never drains the copies in flight.
-__device__ __forceinline__ int32_t load_block_id(const int32_t* table, int32_t j) {
-  return ((const __attribute__((address_space(4))) int32_t*)table)[j];
 }
 
 // Direct global->LDS copy of 16 bytes per lane: lane l's bytes land at LDS
@@ -734,15 +727,6 @@ __device__ __forceinline__ int kswz(int r) { return r % (D * 2 / 16); }
 
 constexpr int kPrefillWaves = 8;                     // waves per prefill workgroup
 constexpr int kPrefillThreads = 64 * kPrefillWaves;
-
-// Max over the four 16-lane rows of a wave (lanes n, n+16, n+32, n+48 hold the
-// same MFMA column): swap odd rows with even ones, then halves, taking the max.
-__device__ __forceinline__ float max_over_rows(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
 
 // Direct global->LDS copy of 16 bytes per lane from a wave-uniform base plus a
 // per-lane 32-bit offset (the scalar-base form of the instruction); lane l's

@@ -271,16 +271,16 @@ def from_lengths(seed: int, ctx, hq: int, hkv: int, d: int, dtype: str, pool_fac
 
 
 def random_prefill(seed: int, ctxs, n_queries, hq: int, hkv: int, d: int, pool_factor: float = 1.3,
-                   block_size: int = BLOCK_SIZE) -> Workload:
+                   block_size: int = BLOCK_SIZE, dtype: str = "bf16") -> Workload:
     """Chunked-prefill parity cases: sequence s has ctxs[s] cached tokens, the last
-    n_queries[s] of which are its chunk's queries (bf16).  Every sequence also
-    carries one decode query."""
-    w = _plain_decode(f"prefill{seed}", seed + 104729, ctxs, hq, hkv, d, "bf16", pool_factor=pool_factor,
+    n_queries[s] of which are its chunk's queries (bf16 or f32, the pool's
+    type).  Every sequence also carries one decode query."""
+    w = _plain_decode(f"prefill{seed}", seed + 104729, ctxs, hq, hkv, d, dtype, pool_factor=pool_factor,
                       block_size=block_size)
     rng = np.random.default_rng(seed + 31337)
     nq = np.asarray(n_queries, dtype=np.int32)
     w.chunk_seqs = list(range(len(ctxs)))
-    w.chunk_q = _normal(rng, (int(nq.sum()), hq, d), "bf16")
+    w.chunk_q = _normal(rng, (int(nq.sum()), hq, d), dtype)
     w.chunk_query_start_loc = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
     return w
 

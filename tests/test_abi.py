@@ -162,7 +162,7 @@ def test_batch_rejects_bad_arguments_before_any_device_call(P):
     out = ctypes.c_void_p()
     # (sched, MB, NB, NH, Hq, Hkv, d, dtype, host, hb, dev, db, out)
     assert L.pkv_batch_create(None, 8, 20, 0, 8, 8, 64, 1, 256, hb, 512, db, ctypes.byref(out)) == P.PKV_ERR_INVALID_ARG
-    assert L.pkv_batch_create(s16._h, 8, 20, 0, 8, 8, 64, 0, 256, hb, 512, db, ctypes.byref(out)) == P.PKV_ERR_UNSUPPORTED
+    assert L.pkv_batch_create(s16._h, 8, 20, 0, 8, 8, 64, 7, 256, hb, 512, db, ctypes.byref(out)) == P.PKV_ERR_INVALID_ARG
     assert L.pkv_batch_create(s16._h, 8, 20, 0, 8, 8, 96, 1, 256, hb, 512, db, ctypes.byref(out)) == P.PKV_ERR_UNSUPPORTED
     assert L.pkv_batch_create(s16._h, 8, 20, 0, 8, 3, 64, 1, 256, hb, 512, db, ctypes.byref(out)) == P.PKV_ERR_INVALID_ARG
     assert L.pkv_batch_create(s16._h, 8, 21, 0, 8, 8, 64, 1, 256, hb, 512, db, ctypes.byref(out)) == P.PKV_ERR_INVALID_ARG
@@ -261,7 +261,7 @@ def test_allocator_errors_are_status_codes(P):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dtype=0), 3), (dict(head_dim=96), 3), (dict(block_size=12), 3), (dict(num_heads=6, num_kv_heads=4), 1),
+    (dict(dtype=9), 1), (dict(head_dim=96), 3), (dict(block_size=12), 3), (dict(num_heads=6, num_kv_heads=4), 1),
     (dict(q=None), 1), (dict(max_query_len=-1), 1), (dict(out=17), 1), (dict(num_blocks=0), 1),
     (dict(scale=float("inf")), 1), (dict(scale=float("nan")), 1),
 ])

@@ -125,18 +125,20 @@ def test_shared_prefix_decode(bs, hq, hkv, d):
     assert torch.equal(out, out2)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("bs", [8, 32])
 @pytest.mark.parametrize("ctxs,nqs,hq,hkv,d", [
     ([60, 300, 700], [37, 64, 100], 8, 2, 128),
     ([16, 33, 129, 1], [16, 1, 129, 1], 4, 4, 64),
     ([1000, 45], [200, 5], 32, 1, 128),
 ])
-def test_chunked_prefill(bs, ctxs, nqs, hq, hkv, d):
+def test_chunked_prefill(bs, ctxs, nqs, hq, hkv, d, dtype):
     """Causal chunked prefill with 8- or 32-token blocks (a 32-key pair of the
-    kernel is four 8-token blocks or one 32-token block), every query row
-    against the oracle."""
-    print(f"case: bs={bs} prefill ctx={ctxs} n={nqs} H={hq}/{hkv} d={d}", flush=True)
-    w = W.random_prefill(90 + bs, ctxs, nqs, hq, hkv, d, block_size=bs)
+    bf16 kernel is four 8-token blocks or one 32-token block, a 16-key tile of
+    the float32 kernel two 8-token blocks or half a 32-token block), every
+    query row against the oracle."""
+    print(f"case: bs={bs} prefill {dtype} ctx={ctxs} n={nqs} H={hq}/{hkv} d={d}", flush=True)
+    w = W.random_prefill(90 + bs, ctxs, nqs, hq, hkv, d, block_size=bs, dtype=dtype)
     g, r = GpuReplay(w), _oracle(w)
     out, _, _ = g.prefill()
     tables = [r.alloc.block_table(s) for s in w.chunk_seqs]
@@ -144,4 +146,4 @@ def test_chunked_prefill(bs, ctxs, nqs, hq, hkv, d):
     ref = O.prefill_chunk_attention(w.chunk_q, w.chunk_query_start_loc, r.k_pool, r.v_pool, tables, lens, w.scale,
                                     block_size=bs)
     assert np.isfinite(out).all()
-    assert float(np.abs(out - ref).max()) <= TOL["bf16"]
+    assert float(np.abs(out - ref).max()) <= TOL[dtype]

@@ -421,16 +421,32 @@ PREFILL = [
 ]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("seed,ctxs,nqs,hq,hkv,d", PREFILL)
-def test_prefill_chunks(seed, ctxs, nqs, hq, hkv, d):
-    print(f"case: prefill seed={seed} ctx={ctxs} n={nqs} H={hq}/{hkv} d={d}", flush=True)
-    w = W.random_prefill(seed, ctxs, nqs, hq, hkv, d)
+def test_prefill_chunks(seed, ctxs, nqs, hq, hkv, d, dtype):
+    """bf16 pools on the bf16 matrix-core kernel, float32 pools on the fp32
+    one; every query row against the oracle."""
+    print(f"case: prefill {dtype} seed={seed} ctx={ctxs} n={nqs} H={hq}/{hkv} d={d}", flush=True)
+    w = W.random_prefill(seed, ctxs, nqs, hq, hkv, d, dtype=dtype)
     g, r = GpuReplay(w), _oracle(w)
     out, _, _ = g.prefill()
     ref = _prefill_ref(r, w)
     assert np.isfinite(out).all()
     err = float(np.abs(out - ref).max())
-    assert err <= TOL["bf16"], err
+    assert err <= TOL[dtype], err
+
+
+def test_prefill_f32_long_chunks():
+    """float32 chunks over a few thousand keys (rounding accumulated over
+    hundreds of 16-key tiles stays within 1e-5), 64 and 128 dims."""
+    for seed, ctxs, nqs, hq, hkv, d in [(71, [4700, 1500], [300, 1500], 8, 2, 128), (72, [3000], [700], 4, 4, 64)]:
+        print(f"case: prefill f32 long seed={seed} ctx={ctxs} n={nqs}", flush=True)
+        w = W.random_prefill(seed, ctxs, nqs, hq, hkv, d, dtype="f32")
+        g, r = GpuReplay(w), _oracle(w)
+        out, _, _ = g.prefill()
+        assert np.isfinite(out).all()
+        err = float(np.abs(out - _prefill_ref(r, w)).max())
+        assert err <= TOL["f32"], err
 
 
 def _bf16_to_f32(bits):
@@ -484,35 +500,58 @@ def test_prefill_with_a_wide_score_range():
     assert err <= TOL["bf16"], err
 
 
-@pytest.mark.parametrize("scale", [-0.3, 0.0, -1.0])
-def test_prefill_with_negative_and_zero_scales(scale):
+@pytest.mark.parametrize("scale,dtype", [(-0.3, "bf16"), (0.0, "bf16"), (-1.0, "bf16"),
+                                         (-0.3, "f32"), (0.0, "f32"), (-0.0884, "f32")])
+def test_prefill_with_negative_and_zero_scales(scale, dtype):
     """Any finite scale, as decode takes: a negative one reverses the scores'
-    order, zero weighs every visible key the same."""
-    w = W.random_prefill(69, [500, 90, 33], [70, 90, 3], 8, 2, 128)
+    order, zero weighs every visible key the same.  float32 takes scales of
+    the size attention uses (up to a few times 1/sqrt(d)): at |scale| = 1 with
+    128 dims the scores reach +-40, and rounding them to float32 alone moves
+    outputs by about 1e-5, the float32 bar itself."""
+    w = W.random_prefill(69, [500, 90, 33], [70, 90, 3], 8, 2, 128, dtype=dtype)
     w.scale = np.float32(scale)
-    print(f"case: prefill scale {scale}", flush=True)
+    print(f"case: prefill {dtype} scale {scale}", flush=True)
     g, r = GpuReplay(w), _oracle(w)
     out, _, _ = g.prefill()
     assert np.isfinite(out).all()
     err = float(np.abs(out - _prefill_ref(r, w)).max())
-    assert err <= TOL["bf16"], err
+    assert err <= TOL[dtype], err
 
 
-def test_prefill_nan_in_unused_slots_never_reaches_the_output():
-    w = W.random_prefill(65, [70, 33], [20, 33], 8, 2, 128)
-    print("case: prefill nan poison", flush=True)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_nan_in_unused_slots_never_reaches_the_output(dtype):
+    w = W.random_prefill(65, [70, 33], [20, 33], 8, 2, 128, dtype=dtype)
+    print(f"case: prefill {dtype} nan poison", flush=True)
     g = GpuReplay(w, pool_fill=float("nan"))
-    r = _oracle(w, pool_fill=np.uint16(0x7FC0))
+    r = _oracle(w, pool_fill=np.uint16(0x7FC0) if dtype == "bf16" else np.float32("nan"))
     out, _, _ = g.prefill()
     err = float(np.abs(out - _prefill_ref(r, w)).max())
-    assert err <= TOL["bf16"], err
+    assert err <= TOL[dtype], err
 
 
-def test_prefill_bad_rows():
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_block_id_outside_the_pool_gives_nan_rows(dtype):
+    """A table entry outside [0, num_blocks) in a sequence's first block: every
+    row of that sequence is NaN (every row's keys start there); the other
+    sequences come out as without it."""
+    w = W.random_prefill(70, [300, 120, 64], [100, 20, 64], 8, 2, 128, dtype=dtype)
+    print(f"case: prefill {dtype} bad block id", flush=True)
+    g = GpuReplay(w)
+    out, tables, lens = g.prefill()
+    t2 = np.array(tables).copy()
+    t2[1, 0] = w.num_blocks + 3
+    out2, _, _ = g.prefill(tables=t2, lens=lens)
+    qsl = w.chunk_query_start_loc
+    assert np.isnan(out2[qsl[1]:qsl[2]]).all()
+    assert np.array_equal(out2[:qsl[1]], out[:qsl[1]]) and np.array_equal(out2[qsl[2]:], out[qsl[2]:])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_bad_rows(dtype):
     """A chunk longer than its context gets NaN rows; a query range outside the
     query buffer is not written; other sequences are computed as before."""
-    w = W.random_prefill(66, [50, 80, 64], [10, 20, 30], 8, 2, 128)
-    print("case: prefill bad rows", flush=True)
+    w = W.random_prefill(66, [50, 80, 64], [10, 20, 30], 8, 2, 128, dtype=dtype)
+    print(f"case: prefill {dtype} bad rows", flush=True)
     g = GpuReplay(w)
     out, tables, lens = g.prefill()
     l2 = np.array(lens).copy()

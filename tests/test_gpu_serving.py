@@ -141,8 +141,9 @@ def _serve_native(w, policy):
     for p, o in zip(w.prompts, w.outputs):
         sched.add_request(int(p), int(o))
     mb = int(-(-int((w.prompts + w.outputs).max()) // bs))
-    batch = PK.Batch(sched, mb, w.num_blocks, w.num_host_blocks, w.num_heads, w.num_kv_heads, w.head_dim)
-    tdt = torch.bfloat16
+    batch = PK.Batch(sched, mb, w.num_blocks, w.num_host_blocks, w.num_heads, w.num_kv_heads, w.head_dim,
+                     PK.PKV_BF16 if w.dtype == "bf16" else PK.PKV_F32)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     shape = (w.num_blocks, w.num_kv_heads, bs, w.head_dim)
     k_pool, v_pool = torch.zeros(shape, dtype=tdt, device=dev), torch.zeros(shape, dtype=tdt, device=dev)
     hshape = (w.num_host_blocks,) + shape[1:]
@@ -205,6 +206,20 @@ def test_native_step_executor_with_grouped_heads():
     steps, swaps, err = _serve_native(w, SC.CONTINUOUS)
     assert err <= TOL
 
+
+
+def test_native_step_executor_with_float32_pools():
+    """float32 pools through the executor: the fp32 matrix-core prefill, the
+    vector-ALU decode with the cache write, swaps; step by step against the
+    oracle loop within the float32 bar."""
+    print("case: native serving f32", flush=True)
+    w = W.serving(seed=12, num_requests=16, hq=8, hkv=2, d=128, prompt_median=120, output_median=40,
+                  max_prompt=300, max_output=100, num_blocks=60, max_num_seqs=6, max_num_batched_tokens=512,
+                  num_host_blocks=200, dtype="f32")
+    steps, swaps, err = _serve_native(w, SC.CONTINUOUS)
+    print(f"steps={steps} swaps={swaps} err={err:.2e}", flush=True)
+    assert err <= 1e-5
+    assert swaps > 0
 
 
 @pytest.mark.parametrize("bs", [8, 32])

@@ -113,6 +113,7 @@ __device__ __forceinline__ void decode_valu_body(const pkv_decode_args& a, uint3
   __shared__ float sm_ml[kValuWaves][2];
   __shared__ int sm_bad[kValuWaves];
   __shared__ int sm_last;
+  __shared__ int sm_peek;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
@@ -320,6 +321,13 @@ __device__ __forceinline__ void decode_valu_body(const pkv_decode_args& a, uint3
     for (int e = 0; e < EPL; ++e) acc[e] = fmaf(pr, vf[e], acc[e] * alpha);
   }
 
+  // A split row: one thread looks at the row's ticket now, so that the load
+  // is in flight while the rows and waves merge.
+  const bool split = np_s != 1 || base != 0;
+  uint64_t* const ticket = split ? a.merge_tickets + static_cast<int64_t>(s) * Hq + h : nullptr;
+  uint64_t seen = 0;
+  if (split && threadIdx.x == 0) seen = pkvd::peek_ticket(ticket);
+
   // merge the rows of the wave (lanes that hold the same dims) ...
 #pragma unroll
   for (int off = LPR; off < 64; off <<= 1) {
@@ -341,6 +349,7 @@ __device__ __forceinline__ void decode_valu_body(const pkv_decode_args& a, uint3
     for (int e = 0; e < EPL; ++e) sm_acc[wave][col * EPL + e] = acc[e];
   }
   if (lane == 0) { sm_ml[wave][0] = m; sm_ml[wave][1] = l; sm_bad[wave] = bad ? 1 : 0; }
+  if (threadIdx.x == 0) sm_peek = split && pkvd::ticket_all_others(seen, a.merge_epoch, base + np_s) ? 1 : 0;
   __syncthreads();
   float M = 0.f, L = 0.f, o = 0.f;
   const int t = threadIdx.x;
@@ -361,15 +370,22 @@ __device__ __forceinline__ void decode_valu_body(const pkv_decode_args& a, uint3
     return;
   }
   // a split context: this partition's (max, sum, accumulator), merged by the
-  // row's last unit to finish
+  // row's last unit to finish -- at once, from registers, when every other
+  // unit of the row had arrived before this one looked
   const int64_t prow = (static_cast<int64_t>(s) * Hq + h) * a.num_partitions;
   const int64_t pidx = prow + base + p;
+  if (sm_peek) {
+    if (t == 0) pkvd::reset_ticket(ticket);
+    if (t < D)
+      a.out[orow + t] = pkvd::merge_partials_coherent_self(a.part_ml + 2 * prow, a.part_acc + prow * D + t,
+                                                           base + np_s, D, base + p, M, L, o);
+    return;
+  }
   if (t < D) {
     pkvd::store_coherent(a.part_acc + pidx * D + t, o);
     if (t == 0) { pkvd::store_coherent(a.part_ml + 2 * pidx, M); pkvd::store_coherent(a.part_ml + 2 * pidx + 1, L); }
   }
-  if (!pkvd::arrive_last(a.merge_tickets + static_cast<int64_t>(s) * Hq + h, a.merge_epoch, base + np_s, &sm_last))
-    return;
+  if (!pkvd::arrive_last(ticket, a.merge_epoch, base + np_s, &sm_last)) return;
   if (t < D)
     a.out[orow + t] = pkvd::merge_partials_coherent(a.part_ml + 2 * prow, a.part_acc + prow * D + t, base + np_s, D);
 }

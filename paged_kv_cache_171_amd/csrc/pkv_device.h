@@ -79,19 +79,21 @@ __device__ __forceinline__ int32_t slot_base_of(const pkv_decode_args& a, int32_
 // The partials are loaded 8 at a time (all loads of a chunk in flight
 // together) and the chunks combined by the same rule; with n <= 8 this is the
 // plain one-pass sum.  Load(p) reads one float.
+// Slot `self` (if >= 0) is not read: its (m, l, acc) are sm, sl, so.
 template <typename Load>
 __device__ __forceinline__ float merge_partials_with(const float* ml, const float* acc, int32_t n, int32_t stride,
-                                                     Load load) {
+                                                     Load load, int32_t self = -1, float sm = 0.f, float sl = 0.f,
+                                                     float so = 0.f) {
   constexpr int kChunk = 8;
   float M = -INFINITY, L = 0.f, o = 0.f;
   for (int32_t q0 = 0; q0 < n; q0 += kChunk) {
     float mv[kChunk], lv[kChunk], av[kChunk];
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
-      const bool in = q0 + i < n;
-      mv[i] = in ? load(ml + 2 * (q0 + i)) : -INFINITY;
-      lv[i] = in ? load(ml + 2 * (q0 + i) + 1) : 0.f;
-      av[i] = in ? load(acc + static_cast<int64_t>(q0 + i) * stride) : 0.f;
+      const bool in = q0 + i < n && q0 + i != self;
+      mv[i] = in ? load(ml + 2 * (q0 + i)) : q0 + i == self ? sm : -INFINITY;
+      lv[i] = in ? load(ml + 2 * (q0 + i) + 1) : q0 + i == self ? sl : 0.f;
+      av[i] = in ? load(acc + static_cast<int64_t>(q0 + i) * stride) : q0 + i == self ? so : 0.f;
     }
     float Mc = mv[0];
 #pragma unroll
@@ -175,6 +177,30 @@ __device__ __forceinline__ bool arrive_last(uint64_t* ticket, uint64_t epoch, in
 __device__ __forceinline__ float merge_partials_coherent(const float* ml, const float* acc, int32_t n,
                                                          int32_t stride) {
   return merge_partials_with(ml, acc, n, stride, [](const float* p) { return load_coherent(p); });
+}
+
+// A look at a row's ticket before arriving: whether every other one of its
+// `units` units has arrived already (their partials stored and complete, as
+// they store before they arrive).  Arrivals only add to the count within a
+// launch, so a unit that sees units - 1 is the last one, and no other unit
+// waits for it: it need not store its own partial nor arrive; it merges the
+// others' partials with its own (merge_partials_coherent_self) and sets the
+// ticket back to 0 (reset_ticket).
+__device__ __forceinline__ uint64_t peek_ticket(const uint64_t* ticket) {
+  return __hip_atomic_load(const_cast<uint64_t*>(ticket), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool ticket_all_others(uint64_t seen, uint64_t epoch, int32_t units) {
+  const uint64_t tag = epoch << kTicketCountBits;
+  const uint64_t arrived = (seen & ~kTicketCountMask) == tag ? (seen & kTicketCountMask) : 0;
+  return arrived + 1 == static_cast<uint64_t>(units);
+}
+__device__ __forceinline__ void reset_ticket(uint64_t* ticket) {
+  __hip_atomic_store(ticket, uint64_t{0}, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float merge_partials_coherent_self(const float* ml, const float* acc, int32_t n,
+                                                              int32_t stride, int32_t self, float sm, float sl,
+                                                              float so) {
+  return merge_partials_with(ml, acc, n, stride, [](const float* p) { return load_coherent(p); }, self, sm, sl, so);
 }
 
 }  // namespace pkvd

@@ -277,7 +277,9 @@ pkv_status pkv_attention_decode_noalloc(float* out, const void* q, const void* k
  *
  * For each group the library finds on the device the longest run of leading
  * block-table entries equal in every member and wholly below every member's
- * context, reads those K/V tiles once for all members (bf16, Hq/Hkv <= 16:
+ * context (its tokens rounded down to a multiple of 16: with 8-token blocks
+ * an odd last common block goes to the members' own parts), reads those K/V
+ * tiles once for all members (bf16, Hq/Hkv <= 16:
  * the members' query rows share one matrix-core tile, up to 16 rows), decodes
  * each member's remaining tokens on its own, and merges the two parts by
  * their softmax statistics.  A malformed group_start, groups of one sequence,

@@ -75,11 +75,10 @@ SharedLayout shared_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim
 }
 
 // Whether shared-prefix decode reads shared blocks on the matrix cores for
-// these heads (bf16, 1..16 query heads per KV head, 16-token blocks); other
-// shapes run plain decode.
-bool shared_applies(pkv_dtype dtype, int32_t num_heads, int32_t num_kv_heads, int32_t block_size) {
+// these heads (bf16, 1..16 query heads per KV head, any supported block
+// size); other shapes run plain decode.
+bool shared_applies(pkv_dtype dtype, int32_t num_heads, int32_t num_kv_heads) {
   const int32_t group = num_kv_heads > 0 ? num_heads / num_kv_heads : 0;
-  (void)block_size;
   return dtype == PKV_BF16 && group >= 1 && group <= kMaxMfmaGroup;
 }
 
@@ -453,7 +452,7 @@ pkv_status pkv_decode_shared_plan(void* plan, size_t plan_bytes_given, const int
     return pkv_failf(PKV_ERR_INVALID_ARG, "%s: plan buffer of %zu bytes is smaller than the %zu needed", fn,
                      plan_bytes_given, l.plan_total);
   char* pb = static_cast<char*>(plan);
-  if (!shared_applies(dtype, num_heads, num_kv_heads, block_size)) {
+  if (!shared_applies(dtype, num_heads, num_kv_heads)) {
     // plain decode: only the own plan region is used
     return hip_status(fn, pkv_launch_plan(reinterpret_cast<int32_t*>(pb + l.plan), context_lens, num_seqs,
                                           max_blocks_per_seq, block_size, max_context_len,
@@ -522,7 +521,7 @@ pkv_status pkv_attention_decode_shared(float* out, const void* q, const void* k_
   if (num_groups > 0 && num_seqs > 0 && !group_start) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: group_start is NULL", fn);
   // only the bf16 MFMA kernel reads a prefix for several sequences; otherwise
   // (or with no groups) this is plain decode
-  if (!shared_applies(dtype, num_heads, num_kv_heads, block_size) || num_groups == 0 || num_seqs <= 0)
+  if (!shared_applies(dtype, num_heads, num_kv_heads) || num_groups == 0 || num_seqs <= 0)
     return pkv_decode_impl(fn, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                            num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_context_len, scale, dtype,
                            nullptr, 0, workspace, workspace_bytes, true, stream);
@@ -577,7 +576,7 @@ pkv_status pkv_attention_decode_shared_planned(float* out, const void* q, const 
   return shared_decode(fn, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                        num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_context_len, scale, dtype,
                        static_cast<const char*>(plan), static_cast<char*>(workspace), workspace ? workspace_bytes : 0,
-                       !shared_applies(dtype, num_heads, num_kv_heads, block_size), stream);
+                       !shared_applies(dtype, num_heads, num_kv_heads), stream);
 }
 
 pkv_status pkv_attention_prefill_chunk(float* out, const void* q, const int32_t* query_start_loc,

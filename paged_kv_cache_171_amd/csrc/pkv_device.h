@@ -12,7 +12,7 @@ namespace pkvd {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBlock = 16;            // tokens per block of the MFMA kernels (the pages' P = 16)
+constexpr int kBlock = 16;            // keys per tile of the MFMA kernels (one 16-token block, two 8-token blocks or half a 32-token one)
 constexpr float kNegBig = -FLT_MAX;   // finite "minus infinity" for running maxima
 // Plan layout (int32): a header of kPlanHdr words -- n_units, num_seqs,
 // max_context_len, max_blocks_per_seq, part_tokens, block_size, 0, 0 -- then (s, p) per

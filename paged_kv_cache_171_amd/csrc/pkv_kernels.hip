@@ -8,8 +8,9 @@
 //   [OS]  "PagedAttention: gestionar la KV cache como memoria de un sistema operativo"
 //   [UL]  "Continuous Batching" (Ultralytics glossary)
 //
-// Pool layout: [num_blocks][num_kv_heads][16][head_dim].  One (block, KV head)
-// tile is 16 * head_dim contiguous elements (4 KiB for bf16, head_dim 128).
+// Pool layout: [num_blocks][num_kv_heads][block_size][head_dim], block_size 8,
+// 16 or 32.  One (block, KV head) tile is block_size * head_dim contiguous
+// elements (4 KiB for bf16, head_dim 128, 16-token blocks).
 #include "pkv_decode_valu.h"
 #include "pkv_plan.h"
 
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(256) void append_kernel(char* __restrict__ k_cache,
 
 // ---------------------------------------------------------------------------
 // Copy-on-write block copy ([IPX] "Dos respuestas a una entrada").  A block is
-// num_kv_heads * 16 * row_bytes contiguous bytes in each pool; workgroup
+// num_kv_heads * block_size * row_bytes contiguous bytes in each pool; workgroup
 // (pair, chunk) streams 4 KiB chunks of it with 16-byte loads and stores.  The
 // same kernel swaps blocks between pools ([CB] "Juntándolo todo: Arquitectura
 // de vLLM": a preempted request's blocks go to CPU memory and come back):

@@ -953,6 +953,36 @@ def mfma_probe(stream, reps: int = 10) -> dict:
     return res
 
 
+def overlap_probe(stream, reps: int = 5) -> dict:
+    """How far matrix-core work of some waves and vector work (fma + exp2, the
+    softmax's kind) of other waves on the same SIMD overlap (overlap_kernel:
+    roles by wave slot, so every SIMD holds both): the mixed launch against
+    each role's waves alone, at 4 and 8 waves per SIMD.  overlap = (sum of the
+    two alone - mixed) / the shorter alone: 1 is full overlap, 0 none."""
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_171_amd", "libpkv_probes.so"))
+    lib.pkvprobe_overlap.restype = ctypes.c_int
+    lib.pkvprobe_overlap.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_void_p]
+    out = torch.empty(2048 * 256, dtype=torch.float32, device="cuda")
+    res = {}
+    for grid in (1024, 2048):
+        def run(mode, grid=grid):
+            rc = lib.pkvprobe_overlap(out.data_ptr(), grid, mode, 2048, 1024, stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"overlap probe launch failed: {rc}")
+        t = {m: _median_us(lambda m=m: run(m), stream, reps) for m in range(5)}
+        run(2)
+        torch.cuda.synchronize()
+        share = float((out[:grid * 256].view(-1, 64)[:, 0] > 1e29).float().mean())
+        alone = t[3] + t[4]
+        res[f"{grid // 256} waves/SIMD"] = {
+            "all_matrix_us": round(t[0], 1), "all_vector_us": round(t[1], 1), "mixed_us": round(t[2], 1),
+            "matrix_waves_alone_us": round(t[3], 1), "vector_waves_alone_us": round(t[4], 1),
+            "vector_share": round(share, 3), "overlap": round((alone - t[2]) / min(t[3], t[4]), 3)}
+    return res
+
+
 def probes_bench(args):
     """The ceilings behind the figures: the streaming-read sweep (read_probes),
     the bf16 matrix-core rate with no memory traffic (mfma_probe), and a
@@ -966,7 +996,8 @@ def probes_bench(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
-    res = {"workload": "probes", "read": read_probes(stream, sweep=True), "mfma": mfma_probe(stream)}
+    res = {"workload": "probes", "read": read_probes(stream, sweep=True), "mfma": mfma_probe(stream),
+           "overlap": overlap_probe(stream)}
     L, H, D, P = args.layers, 40, 128, 16
     w = W.shaped_13b(seed=args.seed, with_rows=False)
     alloc = PK.BlockAllocator(w.num_blocks, P, w.initial_free_order)

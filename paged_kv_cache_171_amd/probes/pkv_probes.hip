@@ -13,6 +13,11 @@
 //   mfma_rate_kernel    -- the bf16 matrix-core rate with no memory traffic:
 //                          chains of v_mfma_f32_16x16x32_bf16 per wave (the
 //                          instruction the prefill kernel is built on)
+//   overlap_kernel      -- how far matrix-core work of some waves and vector
+//                          work (fma and exp2, the softmax's kind) of other
+//                          waves on the same SIMD run at the same time: each
+//                          wave takes its role from its slot on its SIMD (the
+//                          HW_ID register), so every SIMD holds both kinds
 //
 // Every load feeds an XOR that is written only if it equals a constant, so
 // the loads cannot be removed and nothing is stored in practice.
@@ -113,7 +118,63 @@ __global__ __launch_bounds__(256) void mfma_rate_kernel(float* __restrict__ out,
   out[static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x] = sum;
 }
 
+__device__ __forceinline__ float overlap_mfma(int32_t iters) {
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = static_cast<__bf16>(threadIdx.x * 0.001f + i);
+    b[i] = static_cast<__bf16>(i * 0.5f);
+  }
+  f32x4 c0 = f32x4{0.f, 0.f, 0.f, 0.f}, c1 = c0;
+  for (int32_t it = 0; it < iters; ++it) {
+    c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c1, 0, 0, 0);
+  }
+  return c0[0] + c1[1];
+}
+// four independent chains, per step 4 fma, 4 exp2 and 4 adds
+__device__ __forceinline__ float overlap_valu(int32_t iters) {
+  float x0 = threadIdx.x * 1e-3f, x1 = x0 + 0.5f, x2 = x0 + 0.25f, x3 = x0 + 0.125f;
+  float s = 0.f;
+  for (int32_t it = 0; it < iters; ++it) {
+    x0 = fmaf(x0, 0.999f, -0.001f);
+    x1 = fmaf(x1, 0.999f, -0.001f);
+    x2 = fmaf(x2, 0.999f, -0.001f);
+    x3 = fmaf(x3, 0.999f, -0.001f);
+    const float e0 = __builtin_amdgcn_exp2f(x0), e1 = __builtin_amdgcn_exp2f(x1);
+    const float e2 = __builtin_amdgcn_exp2f(x2), e3 = __builtin_amdgcn_exp2f(x3);
+    s += (e0 + e1) + (e2 + e3);
+  }
+  return s + x0 + x1 + x2 + x3;
+}
+
+// mode 0: every wave matrix work; 1: every wave vector work; 2: waves in odd
+// slots vector work, the others matrix work; 3: only the matrix-role waves of
+// mode 2 work; 4: only its vector-role ones.  out[i] gets the wave's result,
+// plus 1e30 for a vector-role wave (so the host can count the roles).
+__global__ __launch_bounds__(256) void overlap_kernel(float* __restrict__ out, int32_t mode, int32_t mfma_iters,
+                                                      int32_t valu_iters) {
+  const uint32_t hw_id = __builtin_amdgcn_s_getreg((31 << 11) | (0 << 6) | 4);   // HW_ID, bits 31:0
+  const bool odd = (hw_id & 1u) != 0;                                           // wave slot parity
+  float r = 0.f;
+  if (mode == 0) r = overlap_mfma(mfma_iters);
+  else if (mode == 1) r = overlap_valu(valu_iters);
+  else if (mode == 2) r = odd ? overlap_valu(valu_iters) : overlap_mfma(mfma_iters);
+  else if (mode == 3) r = odd ? 0.f : overlap_mfma(mfma_iters);
+  else r = odd ? overlap_valu(valu_iters) : 0.f;
+  out[static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x] = odd ? r + 1e30f : r;
+}
+
 }  // namespace
+
+// out: grid * 256 floats.  mode as overlap_kernel's (0..4).  Returns the
+// launch status.
+extern "C" int pkvprobe_overlap(float* out, int32_t grid, int32_t mode, int32_t mfma_iters, int32_t valu_iters,
+                                void* stream) {
+  hipLaunchKernelGGL(overlap_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), out, mode,
+                     mfma_iters, valu_iters);
+  return hipGetLastError();
+}
 
 // out: grid * 256 floats.  chains: 1 or 2 accumulator chains per wave (each
 // MFMA 16 x 16 x 32 x 2 = 16384 flops).  Returns the launch status.

@@ -57,7 +57,9 @@ __device__ __forceinline__ float max4(f32x4 v) {
 }
 
 template <int D, int BS>
-__global__ __launch_bounds__(64 * kF32Waves, 4) void prefill_chunk_f32_kernel(pkv_prefill_args a) {
+// Two waves per SIMD: each wave holds the K and V rows of two tiles (the next
+// one loads while this one is on the matrix cores), 256 registers.
+__global__ __launch_bounds__(64 * kF32Waves, 2) void prefill_chunk_f32_kernel(pkv_prefill_args a) {
   constexpr int KQ = D / 16;   // 16-byte pieces of a K or q row per lane
   constexpr int DT = D / 16;   // 16-dim output tiles; a lane holds DT dims of each of its V rows
   constexpr int DV = DT / 4;   // 16-byte pieces of those
@@ -127,39 +129,39 @@ __global__ __launch_bounds__(64 * kF32Waves, 4) void prefill_chunk_f32_kernel(pk
   bool bad = false;
 
   const int32_t ntiles = (tile_lim + 15) / 16;
-  for (int32_t t = 0; t < ntiles; ++t) {
+  // the tile's block ids (wave-uniform): its block, or with 8-token blocks its
+  // two (the second clamped to the context's last block: keys past the context
+  // are never read from it); a key past the context reads the tile's first key
+  // instead (a cached token: finite data, masked to probability 0)
+  auto load_tile = [&](int32_t t, f32x4 (&kv)[KQ], f32x4 (&vv)[4][DV]) {
     const int32_t key0 = 16 * t;
-    // the tile's block ids (wave-uniform): its block, or with 8-token blocks
-    // its two (the second clamped to the context's last block: keys past the
-    // context are never read from it)
     const int32_t j0 = key0 / BS;
     int32_t id_a = load_block_id(table, __builtin_amdgcn_readfirstlane(j0));
     int32_t id_b = id_a;
     if constexpr (BS == 8) id_b = load_block_id(table, __builtin_amdgcn_readfirstlane(min(j0 + 1, nblk - 1)));
     if (static_cast<uint32_t>(id_a) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; id_a = 0; }
     if (static_cast<uint32_t>(id_b) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; id_b = 0; }
-    // a key past the context reads the tile's first key instead (a cached
-    // token: finite data, masked to probability 0)
     auto row_ptr = [&](const float* base, int32_t off) {
       const int32_t o2 = key0 + off < ctx ? off : 0;
       const int32_t id = (BS == 8 && o2 >= 8) ? id_b : id_a;
       return base + id * block_stride + ((key0 + o2) % BS) * D;
     };
-    f32x4 kv[KQ];
     {
       const float* krow = row_ptr(kc, n);
 #pragma unroll
       for (int m = 0; m < KQ; ++m) kv[m] = *reinterpret_cast<const f32x4*>(krow + 16 * m + 4 * g);
     }
-    f32x4 vv[4][DV];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const float* vrow = row_ptr(vc, 4 * g + kk) + DT * n;
 #pragma unroll
       for (int c = 0; c < DV; ++c) vv[kk][c] = *reinterpret_cast<const f32x4*>(vrow + 4 * c);
     }
-
-    // S^T = K Q^T, two accumulator chains
+  };
+  // S^T = K Q^T (two accumulator chains), the online softmax over the tile's
+  // 16 keys (base 2, maximum taken every tile), then O^T += V^T P^T
+  auto compute_tile = [&](int32_t t, const f32x4 (&kv)[KQ], const f32x4 (&vv)[4][DV]) {
+    const int32_t key0 = 16 * t;
     f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
 #pragma unroll
     for (int m = 0; m < KQ; ++m)
@@ -168,14 +170,12 @@ __global__ __launch_bounds__(64 * kF32Waves, 4) void prefill_chunk_f32_kernel(pk
         if (m & 1) acc1 = mfma4(kv[m][tt], qv[m][tt], acc1);
         else acc0 = mfma4(kv[m][tt], qv[m][tt], acc0);
       }
-    f32x4 sc = acc0 + acc1;                      // S[row n][key key0 + 4g + j]
+    f32x4 sc = acc0 + acc1;
     if (key0 + 16 > nomask_lim) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (key0 + 4 * g + j >= lim) sc[j] = -INFINITY;
     }
-    // online softmax (base 2): the row maximum over the tile's 16 keys, then
-    // the rescale of what the row holds so far
     const float mx = max_over_rows(max4(sc));
     const float mnew = __builtin_elementwise_maximum(m_run, mx * c2);
     const float alpha = fast_exp2(m_run - mnew);
@@ -187,11 +187,20 @@ __global__ __launch_bounds__(64 * kF32Waves, 4) void prefill_chunk_f32_kernel(pk
 #pragma unroll
     for (int j = 0; j < 4; ++j) p[j] = fast_exp2(fmaf(sc[j], c2, -m_run));
     lsum += (p[0] + p[1]) + (p[2] + p[3]);
-    // O^T += V^T P^T
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) o[dt] = mfma4(vv[kk][dt / 4][dt % 4], p[kk], o[dt]);
+  };
+  // two register sets, the loop unrolled by two so that each stays in place
+  f32x4 kA[KQ], vA[4][DV], kB[KQ], vB[4][DV];
+  if (ntiles > 0) load_tile(0, kA, vA);
+  for (int32_t t = 0; t < ntiles; t += 2) {
+    if (t + 1 < ntiles) load_tile(t + 1, kB, vB);
+    compute_tile(t, kA, vA);
+    if (t + 1 >= ntiles) break;
+    if (t + 2 < ntiles) load_tile(t + 2, kA, vA);
+    compute_tile(t + 1, kB, vB);
   }
 
   float L = lsum;

@@ -13,6 +13,8 @@
 //   mfma_rate_kernel    -- the bf16 matrix-core rate with no memory traffic:
 //                          chains of v_mfma_f32_16x16x32_bf16 per wave (the
 //                          instruction the prefill kernel is built on)
+//   mfma_f32_rate_kernel -- the same for the fp32 matrix cores
+//                          (v_mfma_f32_16x16x4_f32, the float32 prefill's)
 //   overlap_kernel      -- how far matrix-core work of some waves and vector
 //                          work (fma and exp2, the softmax's kind) of other
 //                          waves on the same SIMD run at the same time: each
@@ -118,6 +120,23 @@ __global__ __launch_bounds__(256) void mfma_rate_kernel(float* __restrict__ out,
   out[static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x] = sum;
 }
 
+// CH independent accumulator chains per wave, iters fp32 MFMAs on each.
+template <int CH>
+__global__ __launch_bounds__(256) void mfma_f32_rate_kernel(float* __restrict__ out, int32_t iters) {
+  const float a = threadIdx.x * 1e-3f, b = 0.5f;
+  f32x4 acc[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int32_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[c], 0, 0, 0);
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) sum += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  out[static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x] = sum;
+}
+
 __device__ __forceinline__ float overlap_mfma(int32_t iters) {
   bf16x8 a, b;
 #pragma unroll
@@ -166,6 +185,17 @@ __global__ __launch_bounds__(256) void overlap_kernel(float* __restrict__ out, i
 }
 
 }  // namespace
+
+// out: grid * 256 floats.  chains: 1 or 2 (each MFMA 16 x 16 x 4 x 2 = 2048
+// flops).  Returns the launch status.
+extern "C" int pkvprobe_mfma_f32_rate(float* out, int32_t grid, int32_t iters, int32_t chains, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (chains == 1)
+    hipLaunchKernelGGL((mfma_f32_rate_kernel<1>), dim3(grid), dim3(256), 0, st, out, iters);
+  else
+    hipLaunchKernelGGL((mfma_f32_rate_kernel<2>), dim3(grid), dim3(256), 0, st, out, iters);
+  return hipGetLastError();
+}
 
 // out: grid * 256 floats.  mode as overlap_kernel's (0..4).  Returns the
 // launch status.

@@ -88,17 +88,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
 }
 
-// Direct global->LDS copy of 16 bytes per lane: lane l's bytes land at LDS
-// address lds + 16 l.  Issued as assembly so that the compiler, which cannot
-// tell LDS stages apart, does not drain every outstanding copy before each LDS
-// read; the caller waits on vmcnt itself (copies complete in issue order) and
-// issues no compiler-visible vector load between a copy and its wait.
-// The LDS destination goes in m0, which the compiler loads for the statement
-// (a register operand, so it knows m0 is taken).
-__device__ __forceinline__ void copy16_to_lds(const void* src, const void* lds) {
-  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds_addr(lds)) : "memory");
-}
-
 __device__ __forceinline__ bf16x8 join(const s16x4& lo, const s16x4& hi) {
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -730,7 +719,13 @@ constexpr int kPrefillThreads = 64 * kPrefillWaves;
 
 // Direct global->LDS copy of 16 bytes per lane from a wave-uniform base plus a
 // per-lane 32-bit offset (the scalar-base form of the instruction); lane l's
-// bytes land at LDS address lds + 16 l.
+// bytes land at LDS address lds + 16 l.  Issued as assembly so that the
+// compiler, which cannot tell LDS stages apart, does not drain every
+// outstanding copy before each LDS read; the caller waits on vmcnt itself
+// (copies complete in issue order) and issues no compiler-visible vector load
+// between a copy and its wait.  The LDS destination goes in m0, which the
+// compiler loads for the statement (a register operand, so it knows m0 is
+// taken).
 __device__ __forceinline__ void copy16_to_lds_at(const char* base, uint32_t voff, const void* lds) {
   asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "{m0}"(lds_addr(lds)) : "memory");
 }

@@ -278,6 +278,25 @@ def secondary(args):
            "decode_hbm_peak_frac": round(kv_logical / dec_us / 1e3 / HBM_PEAK_GBPS, 4),
            "decode_tokens_per_s_per_layer": round(len(seqs) / dec_us * 1e6, 1),
            "kernel": "decode_group_mfma_kernel" if 2 <= Hq // Hkv <= 16 else "decode_valu_kernel"}
+    if name == "gqa":
+        # the same batch over float32 pools (2 layers of the same tables): the
+        # fp32 matrix-core group kernel, against HBM peak like the bf16 line
+        fpools = [(torch.randn(NB, Hkv, P, D, generator=gen, device=dev),
+                   torch.randn(NB, Hkv, P, D, generator=gen, device=dev)) for _ in range(2)]
+        q32 = torch.randn(len(seqs), Hq, D, generator=gen, device=dev)
+        out32 = torch.empty_like(out)
+        plan32 = PK.plan_for(ld, Hq, Hkv, MB, mcl, PK.PKV_F32)
+
+        def decode_f32_all():
+            for kp, vp in fpools:
+                PK.pkv_attention_decode(out32, q32, kp, vp, td, ld, mcl, scale, workspace=ws, plan=plan32)
+        decode_f32_all()
+        torch.cuda.synchronize()
+        d32_us = _timed(decode_f32_all, reps, stream) / len(fpools)
+        kv32 = kv_logical * 2
+        res.update({"decode_f32_us_per_layer": round(d32_us, 2), "decode_f32_kv_gbps": round(kv32 / d32_us / 1e3, 1),
+                    "decode_f32_hbm_peak_frac": round(kv32 / d32_us / 1e3 / HBM_PEAK_GBPS, 4),
+                    "decode_f32_kernel": "decode_group_f32_kernel"})
     if name == "fork":
         unique = len({int(b) for s, c in zip(range(len(seqs)), lens_h) for b in tables_h[s, :-(-int(c) // P)]})
         res["kv_unique_bytes"] = unique * P * 2 * Hkv * D * 2
@@ -398,6 +417,17 @@ def secondary_oracle_check(args, w, pool, q, td, ld, tables_h, lens_h, scale, en
     plain = torch.empty(S, Hq, D, dtype=torch.float32, device=q.device)
     PK.pkv_attention_decode(plain, q, kp, vp, td, ld, mcl, scale)
     cases.append(("decode", decode_case(plain)))
+    if w.name.startswith("gqa"):
+        kp32, vp32 = env["fpools"][-1]
+        kh32, vh32, qh32 = _host_bits(kp32), _host_bits(vp32), _host_bits(env["q32"])
+        plain32 = torch.empty_like(plain)
+        PK.pkv_attention_decode(plain32, env["q32"], kp32, vp32, td, ld, mcl, scale)
+
+        def decode_f32_fn():
+            ref = O.decode_attention(qh32[rows], kh32, vh32, [tl[i] for i in rows], [int(lens_h[i]) for i in rows],
+                                     scale)
+            return ref, plain32.cpu().numpy()[rows], len(rows) * Hq
+        cases.append(("decode_f32", decode_f32_fn))
     if w.name == "fork":
         shared = torch.empty_like(plain)
         PK.pkv_attention_decode_shared_planned(shared, q, kp, vp, td, ld, mcl, scale, env["splan"],

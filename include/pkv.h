@@ -143,14 +143,16 @@ pkv_status pkv_swap_blocks(void* dst_k_cache, void* dst_v_cache, int32_t dst_num
  *
  *   for s, h:  g = h / (num_heads/num_kv_heads);  n = context_lens[s]
  *     K_j, V_j = key/value of token j < n of sequence s, KV head g, found at
- *                block_tables[s][j/16], offset j%16
+ *                block_tables[s][j/block_size], offset j%block_size
  *     out[s][h][:] = sum_j softmax_j(scale * <q[s][h], K_j>) V_j      (0 if n == 0)
  *
  * q: device [num_seqs][num_heads][head_dim] in `dtype`; out: device float32
  * [num_seqs][num_heads][head_dim]; context_lens: device int32 [num_seqs].
- * Scores, softmax and accumulation are float32 (bf16 query-head groups of 2..16
- * heads per KV head run on the matrix cores with the probabilities carried as
- * a bf16 pair, ~16 significant bits).  max_context_len must be >= every
+ * Scores, softmax and accumulation are float32.  Query-head groups of 2..16
+ * heads per KV head run on the matrix cores, every K/V row read once for the
+ * group: bf16 pools with the probabilities carried as a bf16 pair (~16
+ * significant bits), float32 pools with exact fp32 products; other shapes run
+ * on the vector ALUs, one query head per workgroup.  max_context_len must be >= every
  * context length (it sizes the context split); a row whose length exceeds it or
  * max_blocks_per_seq*block_size, or whose table names a block outside
  * [0, num_blocks), is written as NaN.

@@ -1,0 +1,319 @@
+// Paged decode attention for float32 pools with grouped-query heads (2..16
+// query heads per KV head) on the gfx950 fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32: exact fp32 products, fp32 accumulation).
+//
+// Pages cited:
+//   [OS]  "PagedAttention: gestionar la KV cache como memoria de un sistema
+//         operativo", "Cómo funciona por dentro": attention follows the block
+//         table, scores each block, then one softmax-weighted sum;
+//         "Qué significa esto para lo que pagas": decode is memory-bound.
+//   [CB]  "Batching Continuo y PagedAttention", "PagedAttention: Memoria
+//         virtual para la KV cache": the query heads that share a KV head
+//         read the same blocks.
+//
+// The G query heads of a KV group are the rows of one 16-row MFMA tile, so
+// every K/V row is read once for all of them (the vector-ALU kernel reads it
+// once per query head).  Work units are the plan's (sequence, 4096-token
+// partition) pairs, one workgroup per (unit, KV head); its four waves take the
+// unit's 16-key tiles in turn (a tile: two 8-token blocks, one 16-token block
+// or half a 32-token block) and keep an online softmax per row; the waves are
+// merged through LDS, and the unit writes the output rows or the partials
+// that the row's last unit to finish merges (the layout of the vector-ALU
+// kernel's partials).
+//
+// Matrix-core layout of v_mfma_f32_16x16x4_f32: lane l, n = l % 16,
+// g = l / 16, supplies A[n][g] and B[g][n] and receives D[4g + j][n] in
+// register j.  As in the float32 prefill kernel:
+//     S^T = K Q^T   k = 4m + t  <->  dim 16m + 4g + t  (lane (n, g) loads
+//                   K[key n] and q[row n] at dims 16m + 4g .. +3)
+//     O^T += V^T P^T  k = kk  <->  key 4g + kk, output row i of tile dt
+//                   <->  dim DT i + dt (lane n loads dims DT n .. DT n + DT-1
+//                   of the four V rows 4g .. 4g+3)
+// so the S^T result is the P^T operand and every per-row quantity lives in
+// the lanes whose n is the row.
+#include "pkv_device.h"
+
+namespace {
+
+using pkvd::fast_exp2;
+using pkvd::kNegBig;
+using pkvd::kPlanHdr;
+using pkvd::load_block_id;
+using pkvd::max_over_rows;
+using pkvd::plan_matches;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGroupWaves = 4;
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float max4(f32x4 v) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(v[0], v[1]),
+                                       __builtin_elementwise_maximum(v[2], v[3]));
+}
+
+// Two waves per SIMD: each wave holds the K and V rows of two tiles (the next
+// one loads while this one is on the matrix cores).
+template <int D, int BS>
+__global__ __launch_bounds__(64 * kGroupWaves, 2) void decode_group_f32_kernel(pkv_decode_args a) {
+  constexpr int KQ = D / 16;   // 16-byte pieces of a K or q row per lane
+  constexpr int DT = D / 16;   // 16-dim output tiles; a lane holds DT dims of each of its V rows
+  constexpr int DV = DT / 4;   // 16-byte pieces of those
+  constexpr int kT = 16;       // keys per tile
+  constexpr int OROW = D + 4;  // padded LDS row (floats) of the wave merge
+  static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
+  static_assert(D == 64 || D == 128, "head_dim");
+  constexpr int64_t kHeadTile = static_cast<int64_t>(BS) * D;   // floats of one (block, head) tile
+  __shared__ float sm_o[kGroupWaves][16][OROW];
+  __shared__ float sm_ml[kGroupWaves][16][2];
+  __shared__ int sm_bad[kGroupWaves];
+  __shared__ int sm_last;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;
+  const int g = lane >> 4;
+
+  const int32_t Hq = a.num_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
+  const int32_t u = static_cast<int32_t>(blockIdx.x / static_cast<uint32_t>(Hkv));
+  const int32_t kvh = static_cast<int32_t>(blockIdx.x - static_cast<uint32_t>(u) * Hkv);
+  const int32_t* plan = a.plan;
+  if (!plan_matches(plan, a)) {
+    // a plan built for other sizes: every row is NaN
+    if (u < a.num_seqs)
+      for (int idx = threadIdx.x; idx < G * D; idx += 64 * kGroupWaves)
+        a.out[(static_cast<int64_t>(u) * Hq + kvh * G) * D + idx] = __builtin_nanf("");
+    return;
+  }
+  if (u >= plan[0]) return;
+  const int32_t* units = pkvd::plan_units(plan);
+  const int32_t s = units[2 * u];
+  const int32_t p = units[2 * u + 1];
+  const int32_t ctx = a.context_lens[s];
+  const int64_t row0 = static_cast<int64_t>(s) * Hq + kvh * G;     // the group's first output row
+  if (p < 0) {
+    // no attention work: an empty context gives 0, an invalid one NaN
+    for (int idx = threadIdx.x; idx < G * D; idx += 64 * kGroupWaves)
+      a.out[row0 * D + idx] = ctx == 0 ? 0.f : __builtin_nanf("");
+    return;
+  }
+  const int32_t part = a.part_tokens;
+  const int32_t start = pkvd::seq_start_of(a, s);
+  const int32_t base = pkvd::slot_base_of(a, start);
+  const int32_t np_s = (ctx - start + part - 1) / part;
+  const int32_t ntiles = (ctx + kT - 1) / kT;
+  const int32_t t_begin = start / kT + p * (part / kT);
+  const int32_t t_end = min(ntiles, t_begin + part / kT);
+  const int32_t slot = base + p;
+  const int32_t nslots = base + np_s;
+  const bool direct = np_s == 1 && base == 0;
+
+  const int64_t block_stride = static_cast<int64_t>(Hkv) * kHeadTile;
+  float* const kc = const_cast<float*>(static_cast<const float*>(a.k_cache)) + kvh * kHeadTile;
+  float* const vc = const_cast<float*>(static_cast<const float*>(a.v_cache)) + kvh * kHeadTile;
+  const int32_t* __restrict__ table = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq;
+  const int32_t nblk = (ctx + BS - 1) / BS;
+
+  // q of the group's heads as the B operand (rows >= G: q = 0, never written)
+  f32x4 qv[KQ];
+  {
+    const float* qrow = static_cast<const float*>(a.q) + (row0 + (n < G ? n : 0)) * D;
+#pragma unroll
+    for (int m = 0; m < KQ; ++m) {
+      const f32x4 w = *reinterpret_cast<const f32x4*>(qrow + 16 * m + 4 * g);
+      qv[m] = n < G ? w : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  // The step's new token (decode with the cache write): in the tile of token
+  // ctx-1 its K and V rows come from the step's rows when the new slot is
+  // token ctx-1's, and the lanes holding them store them into the pool; a
+  // slot elsewhere gives NaN rows and stores nothing.
+  const int64_t new_slot = a.new_slots ? a.new_slots[s] : -1;
+  const int32_t last_tile = ntiles - 1;
+  const int32_t last_row = (ctx - 1) % kT;
+  const float* nk = a.new_k ? static_cast<const float*>(a.new_k) + (static_cast<int64_t>(s) * Hkv + kvh) * D : nullptr;
+  const float* nv = a.new_v ? static_cast<const float*>(a.new_v) + (static_cast<int64_t>(s) * Hkv + kvh) * D : nullptr;
+
+  const float c2 = a.scale_log2;               // scale * log2(e), any sign
+  f32x4 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegBig, lsum = 0.f;
+  bool bad = false;
+
+  // The tile's block ids (wave-uniform): its block, or with 8-token blocks its
+  // two (the second clamped to the context's last block: keys past the context
+  // are never read from it); a key past the context reads the tile's first key
+  // instead (a cached token: finite data, masked to probability 0).
+  auto load_tile = [&](int32_t it, f32x4 (&kv)[KQ], f32x4 (&vv)[4][DV]) {
+    const int32_t t = t_begin + wave + kGroupWaves * it;
+    const int32_t key0 = kT * t;
+    const int32_t j0 = key0 / BS;
+    const int32_t raw_a = load_block_id(table, __builtin_amdgcn_readfirstlane(j0));
+    int32_t raw_b = raw_a;
+    if constexpr (BS == 8) raw_b = load_block_id(table, __builtin_amdgcn_readfirstlane(min(j0 + 1, nblk - 1)));
+    int32_t id_a = raw_a, id_b = raw_b;
+    if (static_cast<uint32_t>(id_a) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; id_a = 0; }
+    if (static_cast<uint32_t>(id_b) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; id_b = 0; }
+    bool from_new = false;
+    int32_t id_last = 0;
+    if (t == last_tile && new_slot >= 0) {
+      const int32_t raw_last = (BS == 8 && last_row >= 8) ? raw_b : raw_a;
+      from_new = static_cast<uint32_t>(raw_last) < static_cast<uint32_t>(a.num_blocks) &&
+                 new_slot == static_cast<int64_t>(raw_last) * BS + (ctx - 1) % BS;
+      if (!from_new) bad = true;
+      id_last = raw_last;
+    }
+    auto row_ptr = [&](const float* pool, const float* fresh, int32_t off) {
+      if (from_new && key0 + off == ctx - 1) return fresh;
+      const int32_t o2 = key0 + off < ctx ? off : 0;
+      const int32_t id = (BS == 8 && o2 >= 8) ? id_b : id_a;
+      return pool + id * block_stride + ((key0 + o2) % BS) * D;
+    };
+    {
+      const float* krow = row_ptr(kc, nk, n);
+#pragma unroll
+      for (int m = 0; m < KQ; ++m) kv[m] = *reinterpret_cast<const f32x4*>(krow + 16 * m + 4 * g);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const float* vrow = row_ptr(vc, nv, 4 * g + kk) + DT * n;
+#pragma unroll
+      for (int c = 0; c < DV; ++c) vv[kk][c] = *reinterpret_cast<const f32x4*>(vrow + 4 * c);
+    }
+    if (from_new) {
+      // the new token's rows into the pool: K from the lanes of key row
+      // last_row, V from the lanes of group last_row / 4
+      const int64_t dst = id_last * block_stride + static_cast<int64_t>((ctx - 1) % BS) * D;
+      if (n == last_row) {
+#pragma unroll
+        for (int m = 0; m < KQ; ++m) *reinterpret_cast<f32x4*>(kc + dst + 16 * m + 4 * g) = kv[m];
+      }
+      if (g == last_row / 4) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          if (kk == last_row % 4) {
+#pragma unroll
+            for (int c = 0; c < DV; ++c) *reinterpret_cast<f32x4*>(vc + dst + DT * n + 4 * c) = vv[kk][c];
+          }
+      }
+    }
+  };
+  // S^T = K Q^T (two accumulator chains), the online softmax over the tile's
+  // 16 keys (base 2, maximum taken every tile), then O^T += V^T P^T
+  auto compute_tile = [&](int32_t it, const f32x4 (&kv)[KQ], const f32x4 (&vv)[4][DV]) {
+    const int32_t key0 = kT * (t_begin + wave + kGroupWaves * it);
+    f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+#pragma unroll
+    for (int m = 0; m < KQ; ++m)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        if (m & 1) acc1 = mfma4(kv[m][tt], qv[m][tt], acc1);
+        else acc0 = mfma4(kv[m][tt], qv[m][tt], acc0);
+      }
+    f32x4 sc = (acc0 + acc1) * c2;               // S[row n][key key0 + 4g + j], base 2
+    if (key0 + kT > ctx) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (key0 + 4 * g + j >= ctx) sc[j] = -INFINITY;
+    }
+    const float mx = max_over_rows(max4(sc));
+    const float mnew = __builtin_elementwise_maximum(m_run, mx);
+    const float alpha = fast_exp2(m_run - mnew);
+    m_run = mnew;
+    lsum *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    float pr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pr[j] = fast_exp2(sc[j] - m_run);
+    lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) o[dt] = mfma4(vv[kk][dt / 4][dt % 4], pr[kk], o[dt]);
+  };
+  // this wave's tiles t_begin + wave, + 4, ...; two register sets, the loop
+  // unrolled by two so that each stays in place
+  const int32_t nit = (t_end - t_begin - wave + kGroupWaves - 1) / kGroupWaves;
+  f32x4 kA[KQ], vA[4][DV], kB[KQ], vB[4][DV];
+  if (nit > 0) load_tile(0, kA, vA);
+  for (int32_t it = 0; it < nit; it += 2) {
+    if (it + 1 < nit) load_tile(it + 1, kB, vB);
+    compute_tile(it, kA, vA);
+    if (it + 1 >= nit) break;
+    if (it + 2 < nit) load_tile(it + 2, kA, vA);
+    compute_tile(it + 1, kB, vB);
+  }
+
+  // merge the four waves through LDS: lane (n, g) holds dims DT (4g + j) + dt
+  // of row n in o[dt][j]; its row's sum is spread over the four lane groups
+  float L = lsum;
+  L += __shfl_xor(L, 16);
+  L += __shfl_xor(L, 32);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) sm_o[wave][n][DT * (4 * g + j) + dt] = o[dt][j];
+  if (g == 0) { sm_ml[wave][n][0] = m_run; sm_ml[wave][n][1] = L; }
+  if (lane == 0) sm_bad[wave] = bad ? 1 : 0;
+  __syncthreads();
+  const bool any_bad = (sm_bad[0] | sm_bad[1] | sm_bad[2] | sm_bad[3]) != 0;
+  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kGroupWaves) {
+    const int r = idx / D, d = idx - (idx / D) * D;
+    float M = sm_ml[0][r][0];
+#pragma unroll
+    for (int w = 1; w < kGroupWaves; ++w) M = fmaxf(M, sm_ml[w][r][0]);
+    float Ls = 0.f, acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < kGroupWaves; ++w) {
+      const float f = fast_exp2(sm_ml[w][r][0] - M);
+      Ls += sm_ml[w][r][1] * f;
+      acc += sm_o[w][r][d] * f;
+    }
+    if (any_bad) { acc = __builtin_nanf(""); Ls = __builtin_nanf(""); }
+    const int64_t row = row0 + r;
+    if (direct) {
+      a.out[row * D + d] = acc / Ls;
+    } else {
+      const int64_t pidx = row * a.num_partitions + slot;
+      pkvd::store_coherent(a.part_acc + pidx * D + d, acc);
+      if (d == 0) { pkvd::store_coherent(a.part_ml + 2 * pidx, M); pkvd::store_coherent(a.part_ml + 2 * pidx + 1, Ls); }
+    }
+  }
+  if (direct) return;
+  // a split context: the last of the sequence's units (for this KV head) to
+  // finish merges its G rows
+  if (!pkvd::arrive_last(a.merge_tickets + row0, a.merge_epoch, nslots, &sm_last)) return;
+  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kGroupWaves) {
+    const int64_t prow = (row0 + idx / D) * a.num_partitions;
+    const int d = idx - (idx / D) * D;
+    a.out[(row0 + idx / D) * D + d] = pkvd::merge_partials_coherent(a.part_ml + 2 * prow, a.part_acc + prow * D + d,
+                                                                    nslots, D);
+  }
+}
+
+template <int D>
+void launch_bs(int block_size, dim3 grid, hipStream_t st, const pkv_decode_args& a) {
+  if (block_size == 8)
+    hipLaunchKernelGGL((decode_group_f32_kernel<D, 8>), grid, dim3(64 * kGroupWaves), 0, st, a);
+  else if (block_size == 32)
+    hipLaunchKernelGGL((decode_group_f32_kernel<D, 32>), grid, dim3(64 * kGroupWaves), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_group_f32_kernel<D, 16>), grid, dim3(64 * kGroupWaves), 0, st, a);
+}
+
+}  // namespace
+
+int pkv_launch_decode_group_f32(const pkv_decode_args& a, void* stream) {
+  const int64_t np = (a.max_context_len + a.part_tokens - 1) / a.part_tokens;
+  const int64_t grid = static_cast<int64_t>(a.num_seqs) * (np < 1 ? 1 : np) * a.num_kv_heads;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (a.head_dim == 128) launch_bs<128>(a.block_size, dim3(static_cast<uint32_t>(grid)), st, a);
+  else launch_bs<64>(a.block_size, dim3(static_cast<uint32_t>(grid)), st, a);
+  return hipGetLastError();
+}

@@ -40,12 +40,13 @@ int pkv_launch_swap_blocks(void* k_dst, void* v_dst, int32_t dst_blocks, const v
 constexpr int32_t kMinPartTokens = 1024;
 constexpr int32_t kMaxPartTokens = 4096;
 constexpr int32_t kMaxMfmaGroup = 16;
-// Whether decode of these heads runs on the MFMA group kernel (any block size:
-// the matrix-core kernels walk contexts in 16-key tiles).
+// Whether decode of these heads runs on a matrix-core group kernel -- bf16 or
+// float32, 2..16 query heads per KV head, any block size (the matrix-core
+// kernels walk contexts in 16-key tiles).
 inline bool pkv_uses_mfma(int dtype, int32_t num_heads, int32_t num_kv_heads, int32_t block_size) {
   const int32_t group = num_heads / num_kv_heads;
   (void)block_size;
-  return dtype == PKV_BF16 && group >= 2 && group <= kMaxMfmaGroup;
+  return (dtype == PKV_BF16 || dtype == PKV_F32) && group >= 2 && group <= kMaxMfmaGroup;
 }
 inline int32_t pkv_part_tokens(int dtype, int32_t num_heads, int32_t num_kv_heads, int32_t block_size) {
   return pkv_uses_mfma(dtype, num_heads, num_kv_heads, block_size) ? kMaxPartTokens : kMinPartTokens;
@@ -132,6 +133,7 @@ struct pkv_decode_args {
 // 2..16 heads (pkv_mfma.hip); split contexts are merged inside the launch.
 int pkv_launch_decode(const pkv_decode_args& a, void* stream);
 int pkv_launch_decode_group(const pkv_decode_args& a, void* stream);
+int pkv_launch_decode_group_f32(const pkv_decode_args& a, void* stream);
 int pkv_launch_plan(int32_t* plan, const int32_t* context_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
                     int32_t block_size, int32_t max_context_len, int32_t part_tokens, void* stream,
                     const int32_t* seq_start = nullptr);

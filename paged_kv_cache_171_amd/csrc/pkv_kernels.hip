@@ -161,7 +161,8 @@ int pkv_launch_swap_blocks(void* k_dst, void* v_dst, int32_t dst_blocks, const v
 
 int pkv_launch_decode(const pkv_decode_args& a, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (pkv_uses_mfma(a.dtype, a.num_heads, a.num_kv_heads, a.block_size)) return pkv_launch_decode_group(a, stream);
+  if (pkv_uses_mfma(a.dtype, a.num_heads, a.num_kv_heads, a.block_size))
+    return a.dtype == PKV_BF16 ? pkv_launch_decode_group(a, stream) : pkv_launch_decode_group_f32(a, stream);
   if (a.dtype == PKV_BF16)
     return a.head_dim == 128 ? launch_decode_valu<uint16_t, 128>(a, st) : launch_decode_valu<uint16_t, 64>(a, st);
   return a.head_dim == 128 ? launch_decode_valu<float, 128>(a, st) : launch_decode_valu<float, 64>(a, st);

@@ -80,12 +80,14 @@ def _run(w, seed, no_new=(), wrong=(), planned=False):
     (1, 7, 300, 4, 4, 64, "f32", 16),
     (2, 9, 2500, 8, 8, 128, "bf16", 16),     # split contexts on the VALU kernel
     (3, 6, 5000, 16, 2, 128, "bf16", 16),    # MFMA group kernel, split past 4096
-    (4, 5, 900, 8, 2, 64, "f32", 16),        # grouped heads on the VALU kernel
+    (4, 5, 900, 8, 2, 64, "f32", 16),        # fp32 group kernel
     (5, 7, 700, 4, 4, 128, "bf16", 8),
     (6, 7, 1300, 8, 8, 64, "f32", 32),
     (7, 6, 5000, 16, 2, 128, "bf16", 8),     # MFMA group kernel: two 8-token blocks per 16-key tile
     (8, 6, 5000, 16, 2, 128, "bf16", 32),    # MFMA group kernel: two 16-key tiles per block
     (9, 9, 300, 8, 4, 64, "bf16", 8),        # the new token in either half of a tile
+    (10, 6, 5000, 8, 2, 128, "f32", 8),      # fp32 group kernel, split past 4096, 8-token blocks
+    (11, 7, 400, 16, 4, 128, "f32", 32),     # fp32 group kernel, 32-token blocks
 ])
 def test_decode_append_matches_write_then_decode(seed, S, max_ctx, hq, hkv, d, dtype, bs):
     print(f"case: decode_append seed={seed} {dtype} {hq}/{hkv} d={d} bs={bs}", flush=True)
@@ -97,8 +99,8 @@ def test_decode_append_matches_write_then_decode(seed, S, max_ctx, hq, hkv, d, d
 @pytest.mark.parametrize("bs", [8, 16, 32])
 def test_no_new_token_and_a_wrong_slot(bs):
     print(f"case: decode_append -1 and wrong slots bs={bs}", flush=True)
-    for hq, hkv in ((8, 8), (16, 2)):
-        w = W.random_small(77, 8, 700, hq, hkv, 128, "bf16", block_size=bs)
+    for hq, hkv, dtype in ((8, 8, "bf16"), (16, 2, "bf16"), (16, 2, "f32")):
+        w = W.random_small(77, 8, 700, hq, hkv, 128, dtype, block_size=bs)
         _run(w, 9, no_new=(1, 4), wrong=(2, 6))
 
 

@@ -2,7 +2,7 @@
 sequences than the plan kernel's 1024 threads (three chunks of its scans),
 empty contexts among them; a vector-ALU context of 70,000 tokens (69 partitions
 of 1024, merged in nine chunks of eight) and a grouped-query context of 140,000
-tokens on the matrix-core kernel (35 partitions of 4096); a 3000-query prefill
+tokens on the matrix-core kernels, bf16 and float32 (35 partitions of 4096); a 3000-query prefill
 chunk ending a 20,000-token context (hundreds of key tiles per wave, dozens of
 row tiles), bf16 and float32, checked on its first, middle and last queries."""
 import numpy as np
@@ -51,9 +51,10 @@ def test_seventy_thousand_token_context_on_the_vector_kernel():
     _check(w)
 
 
-def test_hundred_forty_thousand_token_context_on_the_matrix_kernel():
-    print("case: max sizes, 140000-token GQA context", flush=True)
-    w = W.from_lengths(83, [140000, 4097, 1], 8, 1, 128, "bf16")
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_hundred_forty_thousand_token_context_on_the_matrix_kernel(dtype):
+    print(f"case: max sizes, 140000-token GQA context {dtype}", flush=True)
+    w = W.from_lengths(83, [140000, 4097, 1], 8, 1, 128, dtype)
     _check(w)
 
 

@@ -75,9 +75,9 @@ def test_tiny_workload_bit_exact_state_and_attention():
 
 SMALL = [
     # seed, S, max_ctx, Hq, Hkv, d, dtype.  Contexts are cut into 1024-token
-    # partitions on the VALU kernel (MHA, fp32, groups above 16) and 4096-token
-    # ones on the MFMA group kernel (bf16, 2..16 heads per KV head); a longer
-    # context exercises the merge.
+    # partitions on the VALU kernel (MHA, groups above 16) and 4096-token ones
+    # on the matrix-core group kernels (bf16 or fp32, 2..16 heads per KV head);
+    # a longer context exercises the merge.
     (11, 7, 70, 4, 4, 64, "f32"),
     (12, 9, 1300, 2, 2, 128, "f32"),
     (13, 5, 4700, 8, 2, 128, "bf16"),
@@ -85,6 +85,8 @@ SMALL = [
     (15, 6, 1700, 4, 1, 64, "bf16"),
     (16, 10, 2100, 2, 2, 64, "f32"),
     (17, 3, 33, 16, 16, 128, "bf16"),
+    (18, 9, 9000, 8, 2, 128, "f32"),       # fp32 group kernel, contexts split at 4096 and merged
+    (19, 11, 700, 12, 4, 64, "f32"),       # G = 3
 ]
 
 
@@ -373,37 +375,39 @@ def test_plan_built_for_other_sizes_gives_nan_rows():
     assert torch.isnan(o).all()
 
 
-@pytest.mark.parametrize("ctxs,hq,hkv", [
+@pytest.mark.parametrize("ctxs,hq,hkv,dtype", [
     # the VALU kernel's 1024-token partitions (MHA)
-    ([1023, 1024, 1025, 1, 16, 17, 2047, 2048, 2049, 3073], 4, 4),
-    # the MFMA group kernel's 4096-token partitions (bf16, 4 query heads per KV head)
-    ([4095, 4096, 4097, 3, 8191, 8192, 8193, 700], 8, 2),
+    ([1023, 1024, 1025, 1, 16, 17, 2047, 2048, 2049, 3073], 4, 4, "bf16"),
+    # the matrix-core group kernels' 4096-token partitions (4 query heads per KV head)
+    ([4095, 4096, 4097, 3, 8191, 8192, 8193, 700], 8, 2, "bf16"),
+    ([4095, 4096, 4097, 3, 8191, 8192, 8193, 700], 8, 2, "f32"),
 ])
-def test_partition_boundaries(ctxs, hq, hkv):
-    """Context lengths on and next to the partition edges of both decode kernels."""
-    print(f"case: partition edges {ctxs} H={hq}/{hkv}", flush=True)
-    w = W._plain_decode("edges", 77, ctxs, hq, hkv, 128, "bf16")
+def test_partition_boundaries(ctxs, hq, hkv, dtype):
+    """Context lengths on and next to the partition edges of the decode kernels."""
+    print(f"case: partition edges {ctxs} H={hq}/{hkv} {dtype}", flush=True)
+    w = W._plain_decode("edges", 77, ctxs, hq, hkv, 128, dtype)
     g, r = GpuReplay(w), _oracle(w)
     err = _attn_err(g, r, w)
-    assert err <= TOL["bf16"], err
+    assert err <= TOL[dtype], err
 
 
 # ---------------------------------------------------------------------------
-# Query-head groups (MFMA decode kernel for bf16 groups of 2..16 heads; the
-# VALU kernel above 16) and causal chunked prefill (MFMA kernel).
+# Query-head groups (matrix-core decode kernels for bf16 and fp32 groups of
+# 2..16 heads; the VALU kernel above 16) and causal chunked prefill.
 # ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("seed,S,max_ctx,hq,hkv,d", [
     (71, 9, 1300, 16, 1, 128),    # G = 16: the whole MFMA row tile
     (72, 7, 600, 6, 2, 64),       # G = 3
     (73, 5, 900, 32, 1, 128),     # G = 32: VALU kernel
     (74, 12, 40, 16, 8, 128),     # G = 2, short contexts (P rounding matters most)
 ])
-def test_query_head_groups(seed, S, max_ctx, hq, hkv, d):
-    print(f"case: groups seed={seed} H={hq}/{hkv} d={d}", flush=True)
-    w = W.random_small(seed, S, max_ctx, hq, hkv, d, "bf16")
+def test_query_head_groups(seed, S, max_ctx, hq, hkv, d, dtype):
+    print(f"case: groups seed={seed} H={hq}/{hkv} d={d} {dtype}", flush=True)
+    w = W.random_small(seed, S, max_ctx, hq, hkv, d, dtype)
     g, r = GpuReplay(w), _oracle(w)
     err = _attn_err(g, r, w)
-    assert err <= TOL["bf16"], err
+    assert err <= TOL[dtype], err
 
 
 def _prefill_ref(r, w, rows=None):

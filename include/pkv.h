@@ -148,17 +148,17 @@ pkv_status pkv_swap_blocks(void* dst_k_cache, void* dst_v_cache, int32_t dst_num
  *
  * q: device [num_seqs][num_heads][head_dim] in `dtype`; out: device float32
  * [num_seqs][num_heads][head_dim]; context_lens: device int32 [num_seqs].
- * Scores, softmax and accumulation are float32.  Query-head groups of 2..16
- * heads per KV head run on the matrix cores, every K/V row read once for the
- * group: bf16 pools with the probabilities carried as a bf16 pair (~16
- * significant bits), float32 pools with exact fp32 products; other shapes run
- * on the vector ALUs, one query head per workgroup.  max_context_len must be >= every
+ * Scores, softmax and accumulation are float32.  Query-head groups of two or
+ * more heads per KV head run on the matrix cores, every K/V row read once per
+ * 16 heads of the group: bf16 pools with the probabilities carried as a bf16
+ * pair (~16 significant bits), float32 pools with exact fp32 products; one
+ * query head per KV head runs on the vector ALUs, one head per workgroup.  max_context_len must be >= every
  * context length (it sizes the context split); a row whose length exceeds it or
  * max_blocks_per_seq*block_size, or whose table names a block outside
  * [0, num_blocks), is written as NaN.
  * workspace: device scratch of at least pkv_attention_workspace_bytes(...) bytes
  * for the decode plan, the partial results of split contexts (the context is
- * cut into partitions of 1024 tokens, 4096 for the matrix-core group kernel)
+ * cut into partitions of 1024 tokens, 4096 for the matrix-core group kernels)
  * and one 8-byte merge ticket per (sequence, head): the last partition of a
  * row to finish merges the row's partials in the same launch.  No
  * initialisation is needed (a ticket counts only under the launch's own
@@ -317,8 +317,8 @@ pkv_status pkv_attention_decode_shared(float* out, const void* q, const void* k_
  * pkv_attention_decode_shared (num_heads, num_kv_heads, block_size and dtype
  * must be those of the decode calls; group_start may be NULL when num_groups
  * is 0).  Where the shared path does not apply (fp32, more than 16 query
- * heads per KV head, block_size other than 16) the plan is a plain decode
- * plan and the planned call runs plain decode.  A plan built for other sizes
+ * heads per KV head) the plan is a plain decode plan and the planned call
+ * runs plain decode.  A plan built for other sizes
  * or another head grouping makes the planned call write NaN rows.
  * The planned call's workspace: at least
  * pkv_attention_decode_shared_workspace_bytes(...) bytes (partials and merge

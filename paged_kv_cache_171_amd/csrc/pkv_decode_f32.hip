@@ -1,4 +1,4 @@
-// Paged decode attention for float32 pools with grouped-query heads (2..16
+// Paged decode attention for float32 pools with grouped-query heads (2 or more
 // query heads per KV head) on the gfx950 fp32 matrix cores
 // (v_mfma_f32_16x16x4_f32: exact fp32 products, fp32 accumulation).
 //
@@ -13,8 +13,9 @@
 //
 // The G query heads of a KV group are the rows of one 16-row MFMA tile, so
 // every K/V row is read once for all of them (the vector-ALU kernel reads it
-// once per query head).  Work units are the plan's (sequence, 4096-token
-// partition) pairs, one workgroup per (unit, KV head); its four waves take the
+// once per query head); a group of more than 16 heads is cut into slices of
+// 16 rows, one workgroup each.  Work units are the plan's (sequence, 4096-token
+// partition) pairs, one workgroup per (unit, KV head, slice); its four waves take the
 // unit's 16-key tiles in turn (a tile: two 8-token blocks, one 16-token block
 // or half a 32-token block) and keep an online softmax per row; the waves are
 // merged through LDS, and the unit writes the output rows or the partials
@@ -78,14 +79,19 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void decode_group_f32_kernel(p
   const int g = lane >> 4;
 
   const int32_t Hq = a.num_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
-  const int32_t u = static_cast<int32_t>(blockIdx.x / static_cast<uint32_t>(Hkv));
-  const int32_t kvh = static_cast<int32_t>(blockIdx.x - static_cast<uint32_t>(u) * Hkv);
+  const int32_t nsl = (G + 15) / 16;                 // 16-row slices of the group
+  const uint32_t per_unit = static_cast<uint32_t>(Hkv * nsl);
+  const int32_t u = static_cast<int32_t>(blockIdx.x / per_unit);
+  const int32_t rem = static_cast<int32_t>(blockIdx.x - static_cast<uint32_t>(u) * per_unit);
+  const int32_t kvh = rem / nsl;
+  const int32_t slice = rem - kvh * nsl;
+  const int32_t R = min(16, G - 16 * slice);          // rows of this slice
   const int32_t* plan = a.plan;
   if (!plan_matches(plan, a)) {
     // a plan built for other sizes: every row is NaN
     if (u < a.num_seqs)
-      for (int idx = threadIdx.x; idx < G * D; idx += 64 * kGroupWaves)
-        a.out[(static_cast<int64_t>(u) * Hq + kvh * G) * D + idx] = __builtin_nanf("");
+      for (int idx = threadIdx.x; idx < R * D; idx += 64 * kGroupWaves)
+        a.out[(static_cast<int64_t>(u) * Hq + kvh * G + 16 * slice) * D + idx] = __builtin_nanf("");
     return;
   }
   if (u >= plan[0]) return;
@@ -93,10 +99,10 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void decode_group_f32_kernel(p
   const int32_t s = units[2 * u];
   const int32_t p = units[2 * u + 1];
   const int32_t ctx = a.context_lens[s];
-  const int64_t row0 = static_cast<int64_t>(s) * Hq + kvh * G;     // the group's first output row
+  const int64_t row0 = static_cast<int64_t>(s) * Hq + kvh * G + 16 * slice;   // the slice's first output row
   if (p < 0) {
     // no attention work: an empty context gives 0, an invalid one NaN
-    for (int idx = threadIdx.x; idx < G * D; idx += 64 * kGroupWaves)
+    for (int idx = threadIdx.x; idx < R * D; idx += 64 * kGroupWaves)
       a.out[row0 * D + idx] = ctx == 0 ? 0.f : __builtin_nanf("");
     return;
   }
@@ -117,14 +123,14 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void decode_group_f32_kernel(p
   const int32_t* __restrict__ table = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq;
   const int32_t nblk = (ctx + BS - 1) / BS;
 
-  // q of the group's heads as the B operand (rows >= G: q = 0, never written)
+  // q of the slice's heads as the B operand (rows >= R: q = 0, never written)
   f32x4 qv[KQ];
   {
-    const float* qrow = static_cast<const float*>(a.q) + (row0 + (n < G ? n : 0)) * D;
+    const float* qrow = static_cast<const float*>(a.q) + (row0 + (n < R ? n : 0)) * D;
 #pragma unroll
     for (int m = 0; m < KQ; ++m) {
       const f32x4 w = *reinterpret_cast<const f32x4*>(qrow + 16 * m + 4 * g);
-      qv[m] = n < G ? w : f32x4{0.f, 0.f, 0.f, 0.f};
+      qv[m] = n < R ? w : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
 
@@ -185,9 +191,10 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void decode_group_f32_kernel(p
 #pragma unroll
       for (int c = 0; c < DV; ++c) vv[kk][c] = *reinterpret_cast<const f32x4*>(vrow + 4 * c);
     }
-    if (from_new) {
-      // the new token's rows into the pool: K from the lanes of key row
-      // last_row, V from the lanes of group last_row / 4
+    if (from_new && slice == 0) {
+      // the new token's rows into the pool (by the first slice's workgroup):
+      // K from the lanes of key row last_row, V from the lanes of group
+      // last_row / 4
       const int64_t dst = id_last * block_stride + static_cast<int64_t>((ctx - 1) % BS) * D;
       if (n == last_row) {
 #pragma unroll
@@ -263,7 +270,7 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void decode_group_f32_kernel(p
   if (lane == 0) sm_bad[wave] = bad ? 1 : 0;
   __syncthreads();
   const bool any_bad = (sm_bad[0] | sm_bad[1] | sm_bad[2] | sm_bad[3]) != 0;
-  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kGroupWaves) {
+  for (int idx = threadIdx.x; idx < R * D; idx += 64 * kGroupWaves) {
     const int r = idx / D, d = idx - (idx / D) * D;
     float M = sm_ml[0][r][0];
 #pragma unroll
@@ -286,10 +293,10 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void decode_group_f32_kernel(p
     }
   }
   if (direct) return;
-  // a split context: the last of the sequence's units (for this KV head) to
-  // finish merges its G rows
+  // a split context: the last of the sequence's units (for this KV head and
+  // slice) to finish merges its rows
   if (!pkvd::arrive_last(a.merge_tickets + row0, a.merge_epoch, nslots, &sm_last)) return;
-  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kGroupWaves) {
+  for (int idx = threadIdx.x; idx < R * D; idx += 64 * kGroupWaves) {
     const int64_t prow = (row0 + idx / D) * a.num_partitions;
     const int d = idx - (idx / D) * D;
     a.out[(row0 + idx / D) * D + d] = pkvd::merge_partials_coherent(a.part_ml + 2 * prow, a.part_acc + prow * D + d,
@@ -311,7 +318,8 @@ void launch_bs(int block_size, dim3 grid, hipStream_t st, const pkv_decode_args&
 
 int pkv_launch_decode_group_f32(const pkv_decode_args& a, void* stream) {
   const int64_t np = (a.max_context_len + a.part_tokens - 1) / a.part_tokens;
-  const int64_t grid = static_cast<int64_t>(a.num_seqs) * (np < 1 ? 1 : np) * a.num_kv_heads;
+  const int32_t slices = (a.num_heads / a.num_kv_heads + 15) / 16;
+  const int64_t grid = static_cast<int64_t>(a.num_seqs) * (np < 1 ? 1 : np) * a.num_kv_heads * slices;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (a.head_dim == 128) launch_bs<128>(a.block_size, dim3(static_cast<uint32_t>(grid)), st, a);
   else launch_bs<64>(a.block_size, dim3(static_cast<uint32_t>(grid)), st, a);

@@ -41,12 +41,13 @@ constexpr int32_t kMinPartTokens = 1024;
 constexpr int32_t kMaxPartTokens = 4096;
 constexpr int32_t kMaxMfmaGroup = 16;
 // Whether decode of these heads runs on a matrix-core group kernel -- bf16 or
-// float32, 2..16 query heads per KV head, any block size (the matrix-core
-// kernels walk contexts in 16-key tiles).
+// float32, two or more query heads per KV head (a group of more than 16 in
+// 16-row slices), any block size (the matrix-core kernels walk contexts in
+// 16-key tiles).
 inline bool pkv_uses_mfma(int dtype, int32_t num_heads, int32_t num_kv_heads, int32_t block_size) {
   const int32_t group = num_heads / num_kv_heads;
   (void)block_size;
-  return (dtype == PKV_BF16 || dtype == PKV_F32) && group >= 2 && group <= kMaxMfmaGroup;
+  return (dtype == PKV_BF16 || dtype == PKV_F32) && group >= 2;
 }
 inline int32_t pkv_part_tokens(int dtype, int32_t num_heads, int32_t num_kv_heads, int32_t block_size) {
   return pkv_uses_mfma(dtype, num_heads, num_kv_heads, block_size) ? kMaxPartTokens : kMinPartTokens;

@@ -95,10 +95,11 @@ __device__ __forceinline__ bf16x8 join(const s16x4& lo, const s16x4& hi) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode for a query-head group.  One workgroup per (unit, KV head), where a
-// unit is a (sequence, 4096-token partition) of the plan (longest first).  The
-// G query heads of the group are the 16 MFMA rows (rows >= G hold q = 0 and are
-// never written).  The unit's blocks are dealt to the 4 waves in turn; per
+// Decode for a query-head group.  One workgroup per (unit, KV head, slice),
+// where a unit is a (sequence, 4096-token partition) of the plan (longest
+// first).  The G query heads of the group are the 16 MFMA rows (rows >= G hold
+// q = 0 and are never written); a group of more than 16 heads is cut into
+// slices of 16, one workgroup each, which read the same K/V (mostly from L2).  The unit's blocks are dealt to the 4 waves in turn; per
 // block a wave
 //   - loads the K tile straight into the A-operand layout (lane (n, g) reads
 //     16 B of key n at dims 32c + 8g) and forms S^T = K Q^T (D/32 MFMAs),
@@ -154,13 +155,22 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
   const int g = lane >> 4;
 
   const int32_t Hq = a.num_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
-  const int32_t u = static_cast<int32_t>(bid / static_cast<uint32_t>(Hkv));
-  const int32_t kvh = static_cast<int32_t>(bid - static_cast<uint32_t>(u) * Hkv);
-  // The unit: rows r < nrows are (sequence s0 + r / G, query head kvh*G + r % G);
+  // A plan unit's group of more than 16 query heads is cut into slices of 16
+  // rows, one workgroup each (shared-prefix units have G <= 16: one slice).
+  const int32_t nsl = shared_unit ? 1 : (G + kMaxMfmaGroup - 1) / kMaxMfmaGroup;
+  const uint32_t per_unit = static_cast<uint32_t>(Hkv * nsl);
+  const int32_t u = static_cast<int32_t>(bid / per_unit);
+  const int32_t rem = static_cast<int32_t>(bid - static_cast<uint32_t>(u) * per_unit);
+  const int32_t kvh = rem / nsl;
+  const int32_t slice = rem - kvh * nsl;
+  const int32_t slice_rows = min(kMaxMfmaGroup, G - kMaxMfmaGroup * slice);
+  // The unit: rows r < nrows are (sequence s0 + r / GR, query head hb + r % GR);
   // it walks the 16-key tiles t_begin .. t_end-1 of s0's context (tile t is
   // tokens 16t .. 16t+15, whatever blocks hold them), keys below ctx valid,
   // and writes the output rows (direct) or partial slot `slot` of each row.
   int32_t s0, nrows, ctx, t_begin, t_end, slot;
+  int32_t GR = G;                                        // rows per sequence
+  const int32_t hb = kvh * G + kMaxMfmaGroup * slice;    // query head of row 0
   int32_t nslots = 0;     // partial slots of each row (merged in this launch)
   bool direct;
   if (shared_unit) {
@@ -182,8 +192,8 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
     if (!plan_matches(plan, a)) {
       // a plan built for other sizes: every row is NaN
       if (u < a.num_seqs)
-        for (int idx = threadIdx.x; idx < G * D; idx += 256)
-          a.out[(static_cast<int64_t>(u) * Hq + kvh * G) * D + idx] = __builtin_nanf("");
+        for (int idx = threadIdx.x; idx < slice_rows * D; idx += 256)
+          a.out[(static_cast<int64_t>(u) * Hq + hb) * D + idx] = __builtin_nanf("");
       return;
     }
     if (u >= plan[0]) return;
@@ -193,8 +203,8 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
     ctx = a.context_lens[s];
     if (p < 0) {
       // no attention work: an empty context gives 0, an invalid one NaN
-      for (int idx = threadIdx.x; idx < G * D; idx += 256)
-        a.out[(static_cast<int64_t>(s) * Hq + kvh * G) * D + idx] = ctx == 0 ? 0.f : __builtin_nanf("");
+      for (int idx = threadIdx.x; idx < slice_rows * D; idx += 256)
+        a.out[(static_cast<int64_t>(s) * Hq + hb) * D + idx] = ctx == 0 ? 0.f : __builtin_nanf("");
       return;
     }
     const int32_t part = a.part_tokens;
@@ -203,7 +213,8 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
     const int32_t np_s = (ctx - start + part - 1) / part;
     const int32_t ntiles = (ctx + kT - 1) / kT;
     s0 = s;
-    nrows = G;
+    nrows = slice_rows;
+    GR = slice_rows;
     t_begin = start / kT + p * (part / kT);
     t_end = min(ntiles, t_begin + part / kT);
     slot = base + p;
@@ -224,7 +235,7 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
   {
     const int hr = n < nrows ? n : 0;
     const char* qrow = reinterpret_cast<const char*>(a.q) +
-                       ((static_cast<int64_t>(s0 + hr / G) * Hq + kvh * G + hr % G) * D) * 2;
+                       ((static_cast<int64_t>(s0 + hr / GR) * Hq + hb + hr % GR) * D) * 2;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 64 * c + 16 * g);
@@ -321,7 +332,7 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
           __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
                                            (__attribute__((address_space(3))) void*)(tile + 1024 * i), 16, 0, 0);
         }
-        if (n == last_row) {
+        if (n == last_row && slice == 0) {   // the first slice stores the row
 #pragma unroll
           for (int c = 0; c < KC; ++c) {
             *reinterpret_cast<u32x4*>(const_cast<char*>(kp) + last_row * RB + 64 * c + 16 * g) = kt[c];
@@ -391,7 +402,7 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
                                          (__attribute__((address_space(3))) void*)(tile + 1024 * i), 16, 0, 0);
       }
-      if (n == last_row) {
+      if (n == last_row && slice == 0) {   // the first slice stores the row
         char* vp = const_cast<char*>(vbase) + blk(n) + row_in(n);
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
@@ -478,7 +489,7 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
       acc += so[(w * 16 + r) * OROW + d] * f;
     }
     if (any_bad) { acc = __builtin_nanf(""); L = __builtin_nanf(""); }
-    const int64_t row = static_cast<int64_t>(s0 + r / G) * Hq + kvh * G + r % G;
+    const int64_t row = static_cast<int64_t>(s0 + r / GR) * Hq + hb + r % GR;
     if (direct) {
       a.out[row * D + d] = acc / L;
     } else {
@@ -487,13 +498,13 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
       if (d == 0) { pkvd::store_coherent(a.part_ml + 2 * pidx, M); pkvd::store_coherent(a.part_ml + 2 * pidx + 1, L); }
     }
   }
-  // a split context: the last of the sequence's units (for this KV head) to
-  // finish merges its G rows
+  // a split context: the last of the sequence's units (for this KV head and
+  // slice) to finish merges its rows
   if (direct) return;
   if (!shared_unit) {
-    const int64_t row0 = static_cast<int64_t>(s0) * Hq + kvh * G;
+    const int64_t row0 = static_cast<int64_t>(s0) * Hq + hb;
     if (!pkvd::arrive_last(a.merge_tickets + row0, a.merge_epoch, nslots, &sm_last)) return;
-    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    for (int idx = threadIdx.x; idx < nrows * D; idx += 256) {
       const int64_t prow = (row0 + idx / D) * a.num_partitions;
       const int d = idx - (idx / D) * D;
       a.out[(row0 + idx / D) * D + d] =
@@ -1096,7 +1107,8 @@ struct SharedFusedValuTail {
 
 int pkv_launch_decode_group(const pkv_decode_args& a, void* stream) {
   const int64_t np = (a.max_context_len + a.part_tokens - 1) / a.part_tokens;
-  const int64_t grid = static_cast<int64_t>(a.num_seqs) * (np < 1 ? 1 : np) * a.num_kv_heads;
+  const int32_t slices = (a.num_heads / a.num_kv_heads + kMaxMfmaGroup - 1) / kMaxMfmaGroup;
+  const int64_t grid = static_cast<int64_t>(a.num_seqs) * (np < 1 ? 1 : np) * a.num_kv_heads * slices;
   launch_d_bs<GroupDecode>(a.head_dim, a.block_size, dim3(static_cast<uint32_t>(grid)),
                            static_cast<hipStream_t>(stream), a);
   return hipGetLastError();

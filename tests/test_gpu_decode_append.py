@@ -88,6 +88,8 @@ def _run(w, seed, no_new=(), wrong=(), planned=False):
     (9, 9, 300, 8, 4, 64, "bf16", 8),        # the new token in either half of a tile
     (10, 6, 5000, 8, 2, 128, "f32", 8),      # fp32 group kernel, split past 4096, 8-token blocks
     (11, 7, 400, 16, 4, 128, "f32", 32),     # fp32 group kernel, 32-token blocks
+    (12, 5, 4500, 32, 1, 128, "bf16", 16),   # two 16-row slices (the first one stores the row)
+    (13, 4, 900, 64, 2, 64, "f32", 8),       # fp32, two slices
 ])
 def test_decode_append_matches_write_then_decode(seed, S, max_ctx, hq, hkv, d, dtype, bs):
     print(f"case: decode_append seed={seed} {dtype} {hq}/{hkv} d={d} bs={bs}", flush=True)

@@ -31,6 +31,7 @@ CASES = [
     (64, 3, 12000, 4, 4, 64, "f32"),      # VALU: 12 partitions, merged in two chunks of 8
     (66, 3, 40000, 8, 2, 64, "bf16"),     # MFMA: 10 partitions
     (67, 4, 13000, 8, 2, 128, "f32"),     # fp32 MFMA: up to 4 partitions of 4096
+    (68, 3, 9000, 32, 1, 128, "bf16"),    # two 16-row slices, each merged on its own ticket
 ]
 
 
@@ -39,7 +40,7 @@ def _setup(seed, S, max_ctx, hq, hkv, d, dtype):
     g = GpuReplay(w)
     r = O.replay(w.ops, w.k_rows, w.v_rows, w.num_blocks, w.num_kv_heads, w.head_dim, w.initial_free_order)
     tables, lens = g.tables(w.decode_seqs)
-    split = 4096 if 2 <= hq // hkv <= 16 else 1024
+    split = 4096 if hq // hkv >= 2 else 1024
     assert int(lens.max()) > split          # at least one row is merged in the launch
     ref = O.decode_attention(w.q, r.k_pool, r.v_pool, [r.alloc.block_table(s) for s in w.decode_seqs],
                              [r.alloc.num_tokens(s) for s in w.decode_seqs], w.scale)

@@ -75,8 +75,8 @@ def test_tiny_workload_bit_exact_state_and_attention():
 
 SMALL = [
     # seed, S, max_ctx, Hq, Hkv, d, dtype.  Contexts are cut into 1024-token
-    # partitions on the VALU kernel (MHA, groups above 16) and 4096-token ones
-    # on the matrix-core group kernels (bf16 or fp32, 2..16 heads per KV head);
+    # partitions on the VALU kernel (MHA) and 4096-token ones on the
+    # matrix-core group kernels (bf16 or fp32, two or more heads per KV head);
     # a longer context exercises the merge.
     (11, 7, 70, 4, 4, 64, "f32"),
     (12, 9, 1300, 2, 2, 128, "f32"),
@@ -393,14 +393,16 @@ def test_partition_boundaries(ctxs, hq, hkv, dtype):
 
 # ---------------------------------------------------------------------------
 # Query-head groups (matrix-core decode kernels for bf16 and fp32 groups of
-# 2..16 heads; the VALU kernel above 16) and causal chunked prefill.
+# two or more heads, in 16-row slices) and causal chunked prefill.
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("seed,S,max_ctx,hq,hkv,d", [
     (71, 9, 1300, 16, 1, 128),    # G = 16: the whole MFMA row tile
     (72, 7, 600, 6, 2, 64),       # G = 3
-    (73, 5, 900, 32, 1, 128),     # G = 32: VALU kernel
+    (73, 5, 900, 32, 1, 128),     # G = 32: two 16-row slices
     (74, 12, 40, 16, 8, 128),     # G = 2, short contexts (P rounding matters most)
+    (75, 6, 2500, 64, 1, 128),    # G = 64: four slices
+    (76, 5, 5000, 48, 2, 64),     # G = 24: slices of 16 and 8, contexts split past 4096
 ])
 def test_query_head_groups(seed, S, max_ctx, hq, hkv, d, dtype):
     print(f"case: groups seed={seed} H={hq}/{hkv} d={d} {dtype}", flush=True)

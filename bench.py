@@ -297,6 +297,20 @@ def secondary(args):
         res.update({"decode_f32_us_per_layer": round(d32_us, 2), "decode_f32_kv_gbps": round(kv32 / d32_us / 1e3, 1),
                     "decode_f32_hbm_peak_frac": round(kv32 / d32_us / 1e3 / HBM_PEAK_GBPS, 4),
                     "decode_f32_kernel": "decode_group_f32_kernel"})
+        # one KV head for all 64 query heads (the same tables, a pool of one
+        # head, 2 layers): the group kernel in four 16-row slices
+        mpools = [(randn(NB, 1, P, D), randn(NB, 1, P, D)) for _ in range(2)]
+        mplan = PK.plan_for(ld, Hq, 1, MB, mcl, PK.PKV_BF16)
+
+        def decode_mqa_all():
+            for kp, vp in mpools:
+                PK.pkv_attention_decode(out, q, kp, vp, td, ld, mcl, scale, workspace=ws, plan=mplan)
+        decode_mqa_all()
+        torch.cuda.synchronize()
+        mq_us = _timed(decode_mqa_all, reps, stream) / len(mpools)
+        res.update({"decode_64x1_us_per_layer": round(mq_us, 2),
+                    "decode_64x1_kv_gbps": round(kv_logical / Hkv / mq_us / 1e3, 1)})
+        del mpools
     if name == "fork":
         unique = len({int(b) for s, c in zip(range(len(seqs)), lens_h) for b in tables_h[s, :-(-int(c) // P)]})
         res["kv_unique_bytes"] = unique * P * 2 * Hkv * D * 2

@@ -80,11 +80,13 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void decode_group_f32_kernel(p
 
   const int32_t Hq = a.num_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
   const int32_t nsl = (G + 15) / 16;                 // 16-row slices of the group
-  const uint32_t per_unit = static_cast<uint32_t>(Hkv * nsl);
-  const int32_t u = static_cast<int32_t>(blockIdx.x / per_unit);
-  const int32_t rem = static_cast<int32_t>(blockIdx.x - static_cast<uint32_t>(u) * per_unit);
-  const int32_t kvh = rem / nsl;
-  const int32_t slice = rem - kvh * nsl;
+  // the slices of one (unit, KV head) get workgroup ids 8 apart, i.e. one XCD
+  // (workgroups go to the 8 XCDs in turn), so they read its K/V through one L2
+  const uint32_t bid = blockIdx.x;
+  const uint32_t x = nsl == 1 ? bid : (bid / (8u * nsl)) * 8u + bid % 8u;
+  const int32_t slice = nsl == 1 ? 0 : static_cast<int32_t>((bid / 8u) % static_cast<uint32_t>(nsl));
+  const int32_t u = static_cast<int32_t>(x / static_cast<uint32_t>(Hkv));
+  const int32_t kvh = static_cast<int32_t>(x - static_cast<uint32_t>(u) * Hkv);
   const int32_t R = min(16, G - 16 * slice);          // rows of this slice
   const int32_t* plan = a.plan;
   if (!plan_matches(plan, a)) {
@@ -319,7 +321,8 @@ void launch_bs(int block_size, dim3 grid, hipStream_t st, const pkv_decode_args&
 int pkv_launch_decode_group_f32(const pkv_decode_args& a, void* stream) {
   const int64_t np = (a.max_context_len + a.part_tokens - 1) / a.part_tokens;
   const int32_t slices = (a.num_heads / a.num_kv_heads + 15) / 16;
-  const int64_t grid = static_cast<int64_t>(a.num_seqs) * (np < 1 ? 1 : np) * a.num_kv_heads * slices;
+  const int64_t units = static_cast<int64_t>(a.num_seqs) * (np < 1 ? 1 : np) * a.num_kv_heads;
+  const int64_t grid = slices == 1 ? units : (units + 7) / 8 * 8 * slices;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (a.head_dim == 128) launch_bs<128>(a.block_size, dim3(static_cast<uint32_t>(grid)), st, a);
   else launch_bs<64>(a.block_size, dim3(static_cast<uint32_t>(grid)), st, a);

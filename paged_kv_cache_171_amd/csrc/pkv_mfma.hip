@@ -158,11 +158,13 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
   // A plan unit's group of more than 16 query heads is cut into slices of 16
   // rows, one workgroup each (shared-prefix units have G <= 16: one slice).
   const int32_t nsl = shared_unit ? 1 : (G + kMaxMfmaGroup - 1) / kMaxMfmaGroup;
-  const uint32_t per_unit = static_cast<uint32_t>(Hkv * nsl);
-  const int32_t u = static_cast<int32_t>(bid / per_unit);
-  const int32_t rem = static_cast<int32_t>(bid - static_cast<uint32_t>(u) * per_unit);
-  const int32_t kvh = rem / nsl;
-  const int32_t slice = rem - kvh * nsl;
+  // the slices of one (unit, KV head) get workgroup ids 8 apart, i.e. one XCD
+  // (workgroups go to the 8 XCDs in turn), so they read its K/V through one L2
+  // (the grid is padded to whole groups of 8; padding units exit at the plan)
+  const uint32_t x = nsl == 1 ? bid : (bid / (8u * nsl)) * 8u + bid % 8u;
+  const int32_t slice = nsl == 1 ? 0 : static_cast<int32_t>((bid / 8u) % static_cast<uint32_t>(nsl));
+  const int32_t u = static_cast<int32_t>(x / static_cast<uint32_t>(Hkv));
+  const int32_t kvh = static_cast<int32_t>(x - static_cast<uint32_t>(u) * Hkv);
   const int32_t slice_rows = min(kMaxMfmaGroup, G - kMaxMfmaGroup * slice);
   // The unit: rows r < nrows are (sequence s0 + r / GR, query head hb + r % GR);
   // it walks the 16-key tiles t_begin .. t_end-1 of s0's context (tile t is
@@ -1108,7 +1110,8 @@ struct SharedFusedValuTail {
 int pkv_launch_decode_group(const pkv_decode_args& a, void* stream) {
   const int64_t np = (a.max_context_len + a.part_tokens - 1) / a.part_tokens;
   const int32_t slices = (a.num_heads / a.num_kv_heads + kMaxMfmaGroup - 1) / kMaxMfmaGroup;
-  const int64_t grid = static_cast<int64_t>(a.num_seqs) * (np < 1 ? 1 : np) * a.num_kv_heads * slices;
+  const int64_t units = static_cast<int64_t>(a.num_seqs) * (np < 1 ? 1 : np) * a.num_kv_heads;
+  const int64_t grid = slices == 1 ? units : (units + 7) / 8 * 8 * slices;
   launch_d_bs<GroupDecode>(a.head_dim, a.block_size, dim3(static_cast<uint32_t>(grid)),
                            static_cast<hipStream_t>(stream), a);
   return hipGetLastError();

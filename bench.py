@@ -215,9 +215,12 @@ def secondary(args):
     """Kernel measurements on the other batches (one JSON line each; not the headline).
 
     gqa:  256 seqs, 64 query / 8 KV heads, d 128, bf16, ctx U[128, 4096], pool 1.2x
-          shuffled, 8 layer pools: decode (MFMA group kernel) per layer.
-    fork: 32 groups x 8 samples of a 1000-token prompt, tails U[1, 512], 40 heads,
-          4 layer pools: the copy-on-write copies, then decode over the shared blocks.
+          shuffled, 8 layer pools: decode (MFMA group kernel) per layer; then 2
+          float32 layers and 2 layers of one KV head for the 64 query heads.
+    fork: 32 groups x 8 samples of a 1000-token prompt, tails U[1, 512], 40 heads x
+          128 (13B-shaped), 40 layer pools like the headline's: the copy-on-write
+          copies, then decode over the shared blocks (the shared-prefix plan built
+          once per step, for all 40 layers).
     long: 16 seqs at ctx 32768 (split over 64 partitions each) + 4 prefill chunks of
           512 causal queries ending 8192-token contexts, 32 / 8 heads, 4 layer pools.
     """
@@ -238,7 +241,7 @@ def secondary(args):
     name = args.workload
     w = {"gqa": lambda: W.gqa(with_rows=False), "fork": lambda: W.parallel_sampling(with_rows=False),
          "long": lambda: W.long_mix(with_rows=False)}[name]()
-    L = {"gqa": 8, "fork": 4, "long": 4}[name]
+    L = {"gqa": 8, "fork": 40, "long": 4}[name]
     Hq, Hkv, NB = w.num_heads, w.num_kv_heads, w.num_blocks
     alloc = PK.BlockAllocator(NB, P, w.initial_free_order)
     pairs = []

@@ -34,7 +34,7 @@
 //
 // P is split into a bf16 high part and a bf16 remainder, two MFMAs each, so
 // that the probabilities keep ~16 significant bits: a plain bf16 P would put an
-// error of up to 2^-9 |v| on short contexts.  Masked keys are removed by select
+// error of up to 2^-9 |v_j - v_k| on a row whose weight sits on two keys j, k.  Masked keys are removed by select
 // (score -inf, V row 0), never by multiplying, so NaN in unused slots cannot
 // reach the output.
 #include "pkv_decode_valu.h"

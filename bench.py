@@ -220,7 +220,8 @@ def secondary(args):
     fork: 32 groups x 8 samples of a 1000-token prompt, tails U[1, 512], 40 heads x
           128 (13B-shaped), 40 layer pools like the headline's: the copy-on-write
           copies, then decode over the shared blocks (the shared-prefix plan built
-          once per step, for all 40 layers).
+          once per step, for all 40 layers); then plain and shared-prefix decode
+          over 2 float32 layers of the same tables.
     long: 16 seqs at ctx 32768 (split over 64 partitions each) + 4 prefill chunks of
           512 causal queries ending 8192-token contexts, 32 / 8 heads, 4 layer pools.
     """
@@ -359,6 +360,38 @@ def secondary(args):
                     "shared_kernels": "shared_plans_kernel once per step (shared prefixes, then the tails' plan) "
                                       "+ decode_shared_fused_kernel per layer (shared prompt blocks on the matrix "
                                       "cores, each sample's tail on the vector ALUs, merge of split rows inside)"})
+        # the same batch over float32 pools (2 layers of the same tables): plain
+        # decode, and shared-prefix decode (the shared blocks on the fp32 matrix
+        # cores, then the samples' tails on the vector-ALU kernel)
+        fpools = [(torch.randn(NB, Hkv, P, D, generator=gen, device=dev),
+                   torch.randn(NB, Hkv, P, D, generator=gen, device=dev)) for _ in range(2)]
+        q32 = torch.randn(len(seqs), Hq, D, generator=gen, device=dev)
+        out32 = torch.empty_like(out)
+        plan32 = PK.plan_for(ld, Hq, Hkv, MB, mcl, PK.PKV_F32)
+        splan32 = torch.empty_like(splan)
+
+        def plain_f32_all():
+            for kp, vp in fpools:
+                PK.pkv_attention_decode(out32, q32, kp, vp, td, ld, mcl, scale, workspace=ws, plan=plan32)
+
+        def shared_f32_all():
+            PK.pkv_decode_shared_plan(splan32, td, ld, gsd, Hq, Hkv, mcl, PK.PKV_F32)
+            for kp, vp in fpools:
+                PK.pkv_attention_decode_shared_planned(out32, q32, kp, vp, td, ld, mcl, scale, splan32,
+                                                       workspace=sws)
+        plain_f32_all()
+        shared_f32_all()
+        torch.cuda.synchronize()
+        p32_us = _timed(plain_f32_all, reps, stream) / len(fpools)
+        s32_us = _timed(shared_f32_all, reps, stream) / len(fpools)
+        u32 = res["kv_unique_bytes"] * 2
+        res.update({"decode_f32_us_per_layer": round(p32_us, 2),
+                    "shared_decode_f32_us_per_layer": round(s32_us, 2),
+                    "shared_decode_f32_unique_gbps": round(u32 / s32_us / 1e3, 1),
+                    "shared_decode_f32_hbm_peak_frac": round(u32 / s32_us / 1e3 / HBM_PEAK_GBPS, 4),
+                    "shared_f32_over_plain_speedup": round(p32_us / s32_us, 3),
+                    "shared_f32_kernels": "shared_plans_kernel once per step + decode_shared_f32_kernel and "
+                                          "decode_valu_kernel<float> per layer"})
     if name == "long":
         cs = w.chunk_seqs
         clens = np.array([alloc.seq_block_table(s)[1] for s in cs], dtype=np.int32)
@@ -450,6 +483,17 @@ def secondary_oracle_check(args, w, pool, q, td, ld, tables_h, lens_h, scale, en
         PK.pkv_attention_decode_shared_planned(shared, q, kp, vp, td, ld, mcl, scale, env["splan"],
                                                workspace=env["sws"])
         cases.append(("shared_decode", decode_case(shared)))
+        kp32, vp32 = env["fpools"][-1]
+        kh32, vh32, qh32 = _host_bits(kp32), _host_bits(vp32), _host_bits(env["q32"])
+        shared32 = torch.empty_like(plain)
+        PK.pkv_attention_decode_shared_planned(shared32, env["q32"], kp32, vp32, td, ld, mcl, scale, env["splan32"],
+                                               workspace=env["sws"])
+
+        def shared_f32_fn():
+            ref = O.decode_attention(qh32[rows], kh32, vh32, [tl[i] for i in rows], [int(lens_h[i]) for i in rows],
+                                     scale)
+            return ref, shared32.cpu().numpy()[rows], len(rows) * Hq
+        cases.append(("shared_decode_f32", shared_f32_fn))
     if w.name == "long":
         cout, cq, ct, clens, qsl = env["cout"], env["cq"], env["ct"], env["clens"], w.chunk_query_start_loc
         cqh = _host_bits(cq)

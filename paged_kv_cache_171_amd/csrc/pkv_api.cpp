@@ -75,11 +75,11 @@ SharedLayout shared_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim
 }
 
 // Whether shared-prefix decode reads shared blocks on the matrix cores for
-// these heads (bf16, 1..16 query heads per KV head, any supported block
-// size); other shapes run plain decode.
+// these heads (bf16 or float32, 1..16 query heads per KV head, any supported
+// block size); other shapes run plain decode.
 bool shared_applies(pkv_dtype dtype, int32_t num_heads, int32_t num_kv_heads) {
   const int32_t group = num_kv_heads > 0 ? num_heads / num_kv_heads : 0;
-  return dtype == PKV_BF16 && group >= 1 && group <= kMaxMfmaGroup;
+  return (dtype == PKV_BF16 || dtype == PKV_F32) && group >= 1 && group <= kMaxMfmaGroup;
 }
 
 // The checks every shared-prefix call makes on its sizes.
@@ -493,7 +493,7 @@ static pkv_status shared_decode(const char* fn, float* out, const void* q, const
   // split rows are merged inside the decode launch
   a.merge_tickets = reinterpret_cast<uint64_t*>(part + l.tickets);
   a.merge_epoch = next_merge_epoch();
-  return hip_status(fn, pkv_launch_shared_fused(a, stream));
+  return hip_status(fn, dtype == PKV_BF16 ? pkv_launch_shared_fused(a, stream) : pkv_launch_shared_f32(a, stream));
 }
 
 static pkv_status check_decode_pointers(const char* fn, float* out, const void* q, const void* k_cache,
@@ -519,8 +519,8 @@ pkv_status pkv_attention_decode_shared(float* out, const void* q, const void* k_
   const char* fn = "pkv_attention_decode_shared";
   if (num_groups < 0) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: num_groups < 0", fn);
   if (num_groups > 0 && num_seqs > 0 && !group_start) return pkv_failf(PKV_ERR_INVALID_ARG, "%s: group_start is NULL", fn);
-  // only the bf16 MFMA kernel reads a prefix for several sequences; otherwise
-  // (or with no groups) this is plain decode
+  // only the matrix-core kernels read a prefix for several sequences;
+  // otherwise (or with no groups) this is plain decode
   if (!shared_applies(dtype, num_heads, num_kv_heads) || num_groups == 0 || num_seqs <= 0)
     return pkv_decode_impl(fn, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                            num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_context_len, scale, dtype,

@@ -22,6 +22,12 @@
 // that the row's last unit to finish merges (the layout of the vector-ALU
 // kernel's partials).
 //
+// Shared-prefix decode ([OS] "El regalo extra: compartir memoria"): the same
+// body takes a fork group's shared leading blocks once for all its members,
+// whose (member, query head) pairs become the tile's rows (16 / G members per
+// unit); each member's own tokens are then decoded by the plain kernels, and
+// a row's last unit to finish merges it.
+//
 // Matrix-core layout of v_mfma_f32_16x16x4_f32: lane l, n = l % 16,
 // g = l / 16, supplies A[n][g] and B[g][n] and receives D[4g + j][n] in
 // register j.  As in the float32 prefill kernel:
@@ -59,7 +65,7 @@ __device__ __forceinline__ float max4(f32x4 v) {
 // Two waves per SIMD: each wave holds the K and V rows of two tiles (the next
 // one loads while this one is on the matrix cores).
 template <int D, int BS>
-__global__ __launch_bounds__(64 * kGroupWaves, 2) void decode_group_f32_kernel(pkv_decode_args a) {
+__device__ __forceinline__ void decode_group_f32_body(const pkv_decode_args& a, uint32_t bid, bool shared_unit) {
   constexpr int KQ = D / 16;   // 16-byte pieces of a K or q row per lane
   constexpr int DT = D / 16;   // 16-dim output tiles; a lane holds DT dims of each of its V rows
   constexpr int DV = DT / 4;   // 16-byte pieces of those
@@ -72,6 +78,7 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void decode_group_f32_kernel(p
   __shared__ float sm_ml[kGroupWaves][16][2];
   __shared__ int sm_bad[kGroupWaves];
   __shared__ int sm_last;
+  __shared__ int sm_member_last[16], sm_member_slots[16];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -79,60 +86,87 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void decode_group_f32_kernel(p
   const int g = lane >> 4;
 
   const int32_t Hq = a.num_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
-  const int32_t nsl = (G + 15) / 16;                 // 16-row slices of the group
+  // 16-row slices of the group (shared-prefix units have G <= 16: one slice)
+  const int32_t nsl = shared_unit ? 1 : (G + 15) / 16;
   // the slices of one (unit, KV head) get workgroup ids 8 apart, i.e. one XCD
   // (workgroups go to the 8 XCDs in turn), so they read its K/V through one L2
-  const uint32_t bid = blockIdx.x;
   const uint32_t x = nsl == 1 ? bid : (bid / (8u * nsl)) * 8u + bid % 8u;
   const int32_t slice = nsl == 1 ? 0 : static_cast<int32_t>((bid / 8u) % static_cast<uint32_t>(nsl));
   const int32_t u = static_cast<int32_t>(x / static_cast<uint32_t>(Hkv));
   const int32_t kvh = static_cast<int32_t>(x - static_cast<uint32_t>(u) * Hkv);
   const int32_t R = min(16, G - 16 * slice);          // rows of this slice
-  const int32_t* plan = a.plan;
-  if (!plan_matches(plan, a)) {
-    // a plan built for other sizes: every row is NaN
-    if (u < a.num_seqs)
+  const int32_t hb = kvh * G + 16 * slice;            // query head of row 0
+  // The unit: rows r < nrows are (sequence s0 + r / GR, query head hb + r % GR);
+  // it walks the 16-key tiles t_begin .. t_end-1 of s0's context, keys below
+  // ctx valid, and writes the output rows (direct) or partial slot `slot` of
+  // each row.
+  int32_t s0, nrows, GR, ctx, t_begin, t_end, slot, nslots = 0;
+  bool direct;
+  if (shared_unit) {
+    // a group's shared leading blocks: the rows are the group's sequences (a
+    // plan built for other sizes runs no shared unit; the sequences' own units
+    // then write NaN rows)
+    const int32_t* sp = a.shared_plan;
+    if (!pkvd::shared_plan_matches(sp, a) || u >= sp[0]) return;
+    const int32_t* su = sp + kPlanHdr + 4 * u;
+    s0 = su[0];
+    nrows = min(su[1], 16 / G) * G;
+    GR = G;
+    ctx = su[3];
+    t_begin = su[2] * (a.prefix_part_tokens / kT);
+    t_end = min(ctx / kT, t_begin + a.prefix_part_tokens / kT);
+    slot = su[2];
+    direct = false;
+  } else {
+    const int32_t* plan = a.plan;
+    if (!plan_matches(plan, a)) {
+      // a plan built for other sizes: every row is NaN
+      if (u < a.num_seqs)
+        for (int idx = threadIdx.x; idx < R * D; idx += 64 * kGroupWaves)
+          a.out[(static_cast<int64_t>(u) * Hq + hb) * D + idx] = __builtin_nanf("");
+      return;
+    }
+    if (u >= plan[0]) return;
+    const int32_t* units = pkvd::plan_units(plan);
+    const int32_t s = units[2 * u];
+    const int32_t p = units[2 * u + 1];
+    ctx = a.context_lens[s];
+    if (p < 0) {
+      // no attention work: an empty context gives 0, an invalid one NaN
       for (int idx = threadIdx.x; idx < R * D; idx += 64 * kGroupWaves)
-        a.out[(static_cast<int64_t>(u) * Hq + kvh * G + 16 * slice) * D + idx] = __builtin_nanf("");
-    return;
+        a.out[(static_cast<int64_t>(s) * Hq + hb) * D + idx] = ctx == 0 ? 0.f : __builtin_nanf("");
+      return;
+    }
+    const int32_t part = a.part_tokens;
+    const int32_t start = pkvd::seq_start_of(a, s);
+    const int32_t base = pkvd::slot_base_of(a, start);
+    const int32_t np_s = (ctx - start + part - 1) / part;
+    s0 = s;
+    nrows = R;
+    GR = R;
+    t_begin = start / kT + p * (part / kT);
+    t_end = min((ctx + kT - 1) / kT, t_begin + part / kT);
+    slot = base + p;
+    nslots = base + np_s;
+    direct = np_s == 1 && base == 0;
   }
-  if (u >= plan[0]) return;
-  const int32_t* units = pkvd::plan_units(plan);
-  const int32_t s = units[2 * u];
-  const int32_t p = units[2 * u + 1];
-  const int32_t ctx = a.context_lens[s];
-  const int64_t row0 = static_cast<int64_t>(s) * Hq + kvh * G + 16 * slice;   // the slice's first output row
-  if (p < 0) {
-    // no attention work: an empty context gives 0, an invalid one NaN
-    for (int idx = threadIdx.x; idx < R * D; idx += 64 * kGroupWaves)
-      a.out[row0 * D + idx] = ctx == 0 ? 0.f : __builtin_nanf("");
-    return;
-  }
-  const int32_t part = a.part_tokens;
-  const int32_t start = pkvd::seq_start_of(a, s);
-  const int32_t base = pkvd::slot_base_of(a, start);
-  const int32_t np_s = (ctx - start + part - 1) / part;
   const int32_t ntiles = (ctx + kT - 1) / kT;
-  const int32_t t_begin = start / kT + p * (part / kT);
-  const int32_t t_end = min(ntiles, t_begin + part / kT);
-  const int32_t slot = base + p;
-  const int32_t nslots = base + np_s;
-  const bool direct = np_s == 1 && base == 0;
 
   const int64_t block_stride = static_cast<int64_t>(Hkv) * kHeadTile;
   float* const kc = const_cast<float*>(static_cast<const float*>(a.k_cache)) + kvh * kHeadTile;
   float* const vc = const_cast<float*>(static_cast<const float*>(a.v_cache)) + kvh * kHeadTile;
-  const int32_t* __restrict__ table = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq;
+  const int32_t* __restrict__ table = a.block_tables + static_cast<int64_t>(s0) * a.max_blocks_per_seq;
   const int32_t nblk = (ctx + BS - 1) / BS;
 
-  // q of the slice's heads as the B operand (rows >= R: q = 0, never written)
+  // q of the unit's rows as the B operand (rows >= nrows: q = 0, never written)
   f32x4 qv[KQ];
   {
-    const float* qrow = static_cast<const float*>(a.q) + (row0 + (n < R ? n : 0)) * D;
+    const int32_t hr = n < nrows ? n : 0;
+    const float* qrow = static_cast<const float*>(a.q) + ((static_cast<int64_t>(s0) + hr / GR) * Hq + hb + hr % GR) * D;
 #pragma unroll
     for (int m = 0; m < KQ; ++m) {
       const f32x4 w = *reinterpret_cast<const f32x4*>(qrow + 16 * m + 4 * g);
-      qv[m] = n < R ? w : f32x4{0.f, 0.f, 0.f, 0.f};
+      qv[m] = n < nrows ? w : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
 
@@ -140,11 +174,11 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void decode_group_f32_kernel(p
   // ctx-1 its K and V rows come from the step's rows when the new slot is
   // token ctx-1's, and the lanes holding them store them into the pool; a
   // slot elsewhere gives NaN rows and stores nothing.
-  const int64_t new_slot = a.new_slots ? a.new_slots[s] : -1;
+  const int64_t new_slot = (a.new_slots && !shared_unit) ? a.new_slots[s0] : -1;
   const int32_t last_tile = ntiles - 1;
   const int32_t last_row = (ctx - 1) % kT;
-  const float* nk = a.new_k ? static_cast<const float*>(a.new_k) + (static_cast<int64_t>(s) * Hkv + kvh) * D : nullptr;
-  const float* nv = a.new_v ? static_cast<const float*>(a.new_v) + (static_cast<int64_t>(s) * Hkv + kvh) * D : nullptr;
+  const float* nk = a.new_k ? static_cast<const float*>(a.new_k) + (static_cast<int64_t>(s0) * Hkv + kvh) * D : nullptr;
+  const float* nv = a.new_v ? static_cast<const float*>(a.new_v) + (static_cast<int64_t>(s0) * Hkv + kvh) * D : nullptr;
 
   const float c2 = a.scale_log2;               // scale * log2(e), any sign
   f32x4 o[DT];
@@ -272,7 +306,7 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void decode_group_f32_kernel(p
   if (lane == 0) sm_bad[wave] = bad ? 1 : 0;
   __syncthreads();
   const bool any_bad = (sm_bad[0] | sm_bad[1] | sm_bad[2] | sm_bad[3]) != 0;
-  for (int idx = threadIdx.x; idx < R * D; idx += 64 * kGroupWaves) {
+  for (int idx = threadIdx.x; idx < nrows * D; idx += 64 * kGroupWaves) {
     const int r = idx / D, d = idx - (idx / D) * D;
     float M = sm_ml[0][r][0];
 #pragma unroll
@@ -285,7 +319,7 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void decode_group_f32_kernel(p
       acc += sm_o[w][r][d] * f;
     }
     if (any_bad) { acc = __builtin_nanf(""); Ls = __builtin_nanf(""); }
-    const int64_t row = row0 + r;
+    const int64_t row = (static_cast<int64_t>(s0) + r / GR) * Hq + hb + r % GR;
     if (direct) {
       a.out[row * D + d] = acc / Ls;
     } else {
@@ -295,19 +329,70 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void decode_group_f32_kernel(p
     }
   }
   if (direct) return;
-  // a split context: the last of the sequence's units (for this KV head and
-  // slice) to finish merges its rows
-  if (!pkvd::arrive_last(a.merge_tickets + row0, a.merge_epoch, nslots, &sm_last)) return;
-  for (int idx = threadIdx.x; idx < R * D; idx += 64 * kGroupWaves) {
-    const int64_t prow = (row0 + idx / D) * a.num_partitions;
-    const int d = idx - (idx / D) * D;
-    a.out[(row0 + idx / D) * D + d] = pkvd::merge_partials_coherent(a.part_ml + 2 * prow, a.part_acc + prow * D + d,
-                                                                    nslots, D);
+  if (!shared_unit) {
+    // a split context: the last of the sequence's units (for this KV head and
+    // slice) to finish merges its rows
+    const int64_t row0 = static_cast<int64_t>(s0) * Hq + hb;
+    if (!pkvd::arrive_last(a.merge_tickets + row0, a.merge_epoch, nslots, &sm_last)) return;
+    for (int idx = threadIdx.x; idx < R * D; idx += 64 * kGroupWaves) {
+      const int64_t prow = (row0 + idx / D) * a.num_partitions;
+      const int d = idx - (idx / D) * D;
+      a.out[(row0 + idx / D) * D + d] = pkvd::merge_partials_coherent(a.part_ml + 2 * prow,
+                                                                      a.part_acc + prow * D + d, nslots, D);
+    }
+    return;
+  }
+  // a shared-prefix unit arrives once for each member sequence (on the ticket
+  // of its G rows, counting its prefix and its own partitions) and merges the
+  // members it was the last unit of
+  const int32_t members = nrows / G;
+  pkvd::wait_vmem();
+  __syncthreads();
+  if (threadIdx.x < members) {
+    const int32_t s = s0 + threadIdx.x;
+    const int32_t start = pkvd::seq_start_of(a, s);
+    const int32_t slots = pkvd::slot_base_of(a, start) + (a.context_lens[s] - start + a.part_tokens - 1) / a.part_tokens;
+    sm_member_slots[threadIdx.x] = slots;
+    sm_member_last[threadIdx.x] =
+        pkvd::ticket_arrive(a.merge_tickets + static_cast<int64_t>(s) * Hq + kvh * G, a.merge_epoch, slots) ? 1 : 0;
+  }
+  __syncthreads();
+  for (int32_t mi = 0; mi < members; ++mi) {
+    if (!sm_member_last[mi]) continue;
+    const int32_t slots = sm_member_slots[mi];
+    const int64_t row0 = static_cast<int64_t>(s0 + mi) * Hq + kvh * G;
+    for (int idx = threadIdx.x; idx < G * D; idx += 64 * kGroupWaves) {
+      const int64_t prow = (row0 + idx / D) * a.num_partitions;
+      const int d = idx - (idx / D) * D;
+      a.out[(row0 + idx / D) * D + d] = pkvd::merge_partials_coherent(a.part_ml + 2 * prow,
+                                                                      a.part_acc + prow * D + d, slots, D);
+    }
   }
 }
 
+template <int D, int BS>
+__global__ __launch_bounds__(64 * kGroupWaves, 2) void decode_group_f32_kernel(pkv_decode_args a) {
+  decode_group_f32_body<D, BS>(a, blockIdx.x, false);
+}
+
+// The shared-prefix units of a shared-prefix decode (one workgroup per
+// possible unit and KV head; those past the shared plan's count exit).
+template <int D, int BS>
+__global__ __launch_bounds__(64 * kGroupWaves, 2) void decode_shared_f32_kernel(pkv_decode_args a) {
+  decode_group_f32_body<D, BS>(a, blockIdx.x, true);
+}
+
 template <int D>
-void launch_bs(int block_size, dim3 grid, hipStream_t st, const pkv_decode_args& a) {
+void launch_bs(int block_size, dim3 grid, hipStream_t st, const pkv_decode_args& a, bool shared) {
+  if (shared) {
+    if (block_size == 8)
+      hipLaunchKernelGGL((decode_shared_f32_kernel<D, 8>), grid, dim3(64 * kGroupWaves), 0, st, a);
+    else if (block_size == 32)
+      hipLaunchKernelGGL((decode_shared_f32_kernel<D, 32>), grid, dim3(64 * kGroupWaves), 0, st, a);
+    else
+      hipLaunchKernelGGL((decode_shared_f32_kernel<D, 16>), grid, dim3(64 * kGroupWaves), 0, st, a);
+    return;
+  }
   if (block_size == 8)
     hipLaunchKernelGGL((decode_group_f32_kernel<D, 8>), grid, dim3(64 * kGroupWaves), 0, st, a);
   else if (block_size == 32)
@@ -324,7 +409,26 @@ int pkv_launch_decode_group_f32(const pkv_decode_args& a, void* stream) {
   const int64_t units = static_cast<int64_t>(a.num_seqs) * (np < 1 ? 1 : np) * a.num_kv_heads;
   const int64_t grid = slices == 1 ? units : (units + 7) / 8 * 8 * slices;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (a.head_dim == 128) launch_bs<128>(a.block_size, dim3(static_cast<uint32_t>(grid)), st, a);
-  else launch_bs<64>(a.block_size, dim3(static_cast<uint32_t>(grid)), st, a);
+  if (a.head_dim == 128) launch_bs<128>(a.block_size, dim3(static_cast<uint32_t>(grid)), st, a, false);
+  else launch_bs<64>(a.block_size, dim3(static_cast<uint32_t>(grid)), st, a, false);
   return hipGetLastError();
+}
+
+// Shared-prefix decode over float32 pools: the shared units, then every
+// sequence's own units on the plain decode kernels (the vector-ALU kernel or
+// the group kernel above), on one stream.  The two launches share the merge
+// epoch, so a row's tickets count the units of both, and its last unit (in
+// the second launch, or a shared unit when a member has no own tokens)
+// merges it.  (Two launches rather than one fused kernel: this body needs
+// twice the registers of the vector-ALU one, which in one kernel would halve
+// the occupancy of the sequences' own units.)
+int pkv_launch_shared_f32(const pkv_decode_args& a, void* stream) {
+  const int64_t npp = (a.max_context_len + a.prefix_part_tokens - 1) / a.prefix_part_tokens;
+  const int64_t shared = static_cast<int64_t>(a.num_seqs) * (npp < 1 ? 1 : npp) * a.num_kv_heads;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (a.head_dim == 128) launch_bs<128>(a.block_size, dim3(static_cast<uint32_t>(shared)), st, a, true);
+  else launch_bs<64>(a.block_size, dim3(static_cast<uint32_t>(shared)), st, a, true);
+  const int err = hipGetLastError();
+  if (err) return err;
+  return pkv_launch_decode(a, stream);
 }

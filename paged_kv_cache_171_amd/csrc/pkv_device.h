@@ -135,9 +135,9 @@ __device__ __forceinline__ void wait_vmem() {
 }
 
 // Merge tickets.  A ticket is one 64-bit word per row: (epoch << 24) | units
-// arrived.  The epoch (40 bits, nonzero) is new for every launch, so a word
-// left by another launch counts as 0 arrivals and the buffer never needs
-// clearing.  24 bits count every partition a row can have: a context of at
+// arrived.  The epoch (40 bits, nonzero) is new for every call, so a word
+// left by another call counts as 0 arrivals and the buffer never needs
+// clearing (a call of two launches counts the arrivals of both).  24 bits count every partition a row can have: a context of at
 // most 2^31 - 1 tokens in 1024-token partitions is at most 2^21 of them, plus
 // as many shared-prefix partitions.
 constexpr int kTicketCountBits = 24;

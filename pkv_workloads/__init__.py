@@ -167,15 +167,16 @@ def gqa(seed: int = 3, num_seqs: int = 256, lo: int = 128, hi: int = 4096,
 def parallel_sampling(seed: int = 4, groups: int = 32, samples=8, prompt=1000,
                       tail_lo: int = 1, tail_hi: int = 512, hq: int = 40, d: int = 128,
                       with_rows: bool = True, hkv: Optional[int] = None,
-                      block_size: int = BLOCK_SIZE) -> Workload:
+                      block_size: int = BLOCK_SIZE, dtype: str = "bf16") -> Workload:
     """Workload 4: groups x samples forks of one prompt each; tails U[1, 512].
 
     Script per group: create the prompt sequence (it is sample 0), append the
     prompt, flush, fork it samples-1 times, then append each sample's tail in
     sample order (a tail of 0 appends nothing), flush.  Every sample carries
     one decode query; the samples of a group are consecutive in decode_seqs.
-    For parity cases ``samples`` and ``prompt`` may also be per-group lists and
-    ``hkv`` < hq gives grouped-query heads.
+    For parity cases ``samples`` and ``prompt`` may also be per-group lists,
+    ``hkv`` < hq gives grouped-query heads and ``dtype`` "f32" float32 pools
+    (the same draws, not rounded to bf16).
     """
     rng = np.random.default_rng(seed)
     hkv = hq if hkv is None else hkv
@@ -205,13 +206,13 @@ def parallel_sampling(seed: int = 4, groups: int = 32, samples=8, prompt=1000,
         ops.append(("flush",))
         decode_seqs.extend(members)
     total = sum(prompts) + int(sum(int(ts.sum()) for ts in tails))
-    q = _normal(rng, (len(decode_seqs), hq, d), "bf16")
+    q = _normal(rng, (len(decode_seqs), hq, d), dtype)
     if with_rows:
-        k_rows = _rows(rng, total, hkv, d, "bf16")
-        v_rows = _rows(rng, total, hkv, d, "bf16")
+        k_rows = _rows(rng, total, hkv, d, dtype)
+        v_rows = _rows(rng, total, hkv, d, dtype)
     else:
-        k_rows = v_rows = np.empty((0, hkv, d), dtype=np.uint16)
-    w = Workload("fork", "bf16", hq, hkv, d, nb, perm, ops, k_rows, v_rows, decode_seqs, q,
+        k_rows = v_rows = np.empty((0, hkv, d), dtype=np.float32 if dtype == "f32" else np.uint16)
+    w = Workload("fork", dtype, hq, hkv, d, nb, perm, ops, k_rows, v_rows, decode_seqs, q,
                  np.float32(1.0 / math.sqrt(d)), block_size=block_size)
     w.tails = np.array(tails) if len(set(n_samples)) == 1 else tails  # type: ignore[attr-defined]
     w.prompt = prompt  # type: ignore[attr-defined]

@@ -101,27 +101,29 @@ def test_swap_copies(bs):
 
 
 @pytest.mark.parametrize("bs", [8, 32])
-@pytest.mark.parametrize("hq,hkv,d", [(8, 8, 128), (16, 2, 128), (4, 4, 64)])
-def test_shared_prefix_decode(bs, hq, hkv, d):
+@pytest.mark.parametrize("hq,hkv,d,dtype", [(8, 8, 128, "bf16"), (16, 2, 128, "bf16"), (4, 4, 64, "bf16"),
+                                            (8, 8, 128, "f32"), (16, 2, 64, "f32")])
+def test_shared_prefix_decode(bs, hq, hkv, d, dtype):
     """The groups' common leading blocks read once on the matrix cores (with
     8-token blocks an odd last common block is left to the members' own
     units): the oracle's result, and planned calls give the same bits."""
-    print(f"case: bs={bs} shared {hq}/{hkv} d={d}", flush=True)
+    print(f"case: bs={bs} shared {hq}/{hkv} d={d} {dtype}", flush=True)
     w = W.parallel_sampling(seed=41 + bs, groups=3, samples=[5, 2, 8], prompt=[70, 1100, 200], tail_lo=0,
-                            tail_hi=50, hq=hq, hkv=hkv, d=d, block_size=bs)
+                            tail_hi=50, hq=hq, hkv=hkv, d=d, block_size=bs, dtype=dtype)
     g, qd, td, ld, mcl = _check(w)
     r = _oracle(w)
     S = len(w.decode_seqs)
     gs = torch.tensor(w.group_start, dtype=torch.int32, device="cuda")
     out = torch.full((S, hq, d), -1.0, dtype=torch.float32, device="cuda")
     PK.pkv_attention_decode_shared(out, qd, g.k_pool, g.v_pool, td, ld, gs, mcl, float(w.scale))
-    plan = PK.shared_plan_for(td, ld, gs, hq, hkv, mcl, PK.PKV_BF16, block_size=bs)
+    plan = PK.shared_plan_for(td, ld, gs, hq, hkv, mcl, PK.PKV_BF16 if dtype == "bf16" else PK.PKV_F32,
+                              block_size=bs)
     out2 = torch.full_like(out, -2.0)
     PK.pkv_attention_decode_shared_planned(out2, qd, g.k_pool, g.v_pool, td, ld, mcl, float(w.scale), plan)
     torch.cuda.synchronize()
     ref = O.decode_attention(w.q, r.k_pool, r.v_pool, [r.alloc.block_table(s) for s in w.decode_seqs],
                              [r.alloc.num_tokens(s) for s in w.decode_seqs], w.scale, block_size=bs)
-    assert float(np.abs(out.cpu().numpy() - ref).max()) <= TOL["bf16"]
+    assert float(np.abs(out.cpu().numpy() - ref).max()) <= TOL[dtype]
     assert torch.equal(out, out2)
 
 

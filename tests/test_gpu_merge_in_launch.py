@@ -107,19 +107,22 @@ def test_graph_replays_match_the_eager_call(seed, S, max_ctx, hq, hkv, d, dtype)
 
 
 SHARED = [
-    # seed, hq, hkv, d, samples, prompt, tail_lo, tail_hi: every row has 2 or 3
-    # prefix partials (prompts past 1024 tokens) plus its own
-    (91, 8, 8, 128, [4, 3], [1500, 2100], 0, 40),       # MHA: vector-ALU own units
-    (92, 32, 8, 128, [6, 2], [1100, 3000], 1, 1200),    # G=4: matrix-core own units, some split
+    # seed, hq, hkv, d, samples, prompt, tail_lo, tail_hi, dtype: every row has
+    # 2 or 3 prefix partials (prompts past 1024 tokens) plus its own
+    (91, 8, 8, 128, [4, 3], [1500, 2100], 0, 40, "bf16"),       # MHA: vector-ALU own units
+    (92, 32, 8, 128, [6, 2], [1100, 3000], 1, 1200, "bf16"),    # G=4: matrix-core own units, some split
+    # float32: the shared units and the own units are two launches on one ticket epoch
+    (93, 8, 8, 128, [4, 3], [1500, 2100], 0, 40, "f32"),
+    (94, 32, 8, 128, [6, 2], [1100, 3000], 1, 1200, "f32"),
 ]
 
 
-@pytest.mark.parametrize("seed,hq,hkv,d,samples,prompt,tail_lo,tail_hi", SHARED)
+@pytest.mark.parametrize("seed,hq,hkv,d,samples,prompt,tail_lo,tail_hi,dtype", SHARED)
 def test_shared_prefix_merge_with_random_workspace_and_graph_replays(seed, hq, hkv, d, samples, prompt,
-                                                                      tail_lo, tail_hi):
-    print(f"case: merge in launch, shared prefix seed={seed} {hq}/{hkv}", flush=True)
+                                                                      tail_lo, tail_hi, dtype):
+    print(f"case: merge in launch, shared prefix seed={seed} {hq}/{hkv} {dtype}", flush=True)
     w = W.parallel_sampling(seed=seed, groups=len(samples), samples=samples, prompt=prompt, tail_lo=tail_lo,
-                            tail_hi=tail_hi, hq=hq, hkv=hkv, d=d)
+                            tail_hi=tail_hi, hq=hq, hkv=hkv, d=d, dtype=dtype)
     g = GpuReplay(w)
     r = O.replay(w.ops, w.k_rows, w.v_rows, w.num_blocks, w.num_kv_heads, w.head_dim, w.initial_free_order)
     tables, lens = g.tables(w.decode_seqs)
@@ -142,7 +145,7 @@ def test_shared_prefix_merge_with_random_workspace_and_graph_replays(seed, hq, h
     torch.cuda.synchronize()
     e = eager.cpu().numpy()
     err = float(np.abs(e - ref).max())
-    assert err <= TOL["bf16"], err
+    assert err <= TOL[dtype], err
     out = torch.full_like(eager, -3.0)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())

@@ -7,8 +7,8 @@ every row), grouped-query heads (2..8 query heads per KV head), groups
 larger than one 16-row tile, members whose context ends exactly at the shared
 prefix, a partial shared last block, an empty context in a group, groups whose
 tables share nothing, and malformed group boundaries (which must give plain
-decode).  Max abs error <= 2e-3 (bf16 K/V), and the result may differ from
-plain decode only by rounding.
+decode); bf16 and float32 pools.  Max abs error <= 2e-3 (bf16 K/V) and 1e-5
+(float32 K/V), and the result may differ from plain decode only by rounding.
 """
 import numpy as np
 import pytest
@@ -24,7 +24,7 @@ import pkv_workloads as W  # noqa: E402
 from oracle import pkv_oracle as O  # noqa: E402
 from pkv_gpu_driver import GpuReplay, rows_to_device  # noqa: E402
 
-TOL = 2e-3
+TOL = {"bf16": 2e-3, "f32": 1e-5}
 
 
 def _run(g, w, group_start, tables=None, lens=None, mcl=None):
@@ -58,10 +58,26 @@ def test_full_parallel_sampling_batch_all_rows():
     idx = list(range(len(w.decode_seqs)))
     err = float(np.abs(out - _ref(w, idx, tables, lens)).max())
     print(f"err={err:.2e} vs plain={float(np.abs(out - plain).max()):.2e}", flush=True)
-    assert err <= TOL
-    assert float(np.abs(out - plain).max()) <= TOL
+    assert err <= TOL["bf16"]
+    assert float(np.abs(out - plain).max()) <= TOL["bf16"]
 
 
+def test_float32_parallel_sampling_all_rows():
+    """A quarter of the fork batch over float32 pools (prompts of 300 to 2100
+    tokens, so one or three prefix partitions), every row."""
+    print("case: shared fork float32, every row", flush=True)
+    w = W.parallel_sampling(seed=44, groups=4, samples=8, prompt=[1000, 2100, 1000, 300], dtype="f32")
+    g = GpuReplay(w)
+    out, plain, tables, lens = _run(g, w, w.group_start)
+    assert np.isfinite(out).all()
+    idx = list(range(len(w.decode_seqs)))
+    err = float(np.abs(out - _ref(w, idx, tables, lens)).max())
+    print(f"err={err:.2e} vs plain={float(np.abs(out - plain).max()):.2e}", flush=True)
+    assert err <= TOL["f32"]
+    assert float(np.abs(out - plain).max()) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("seed,hq,hkv,d,samples,prompt,tail_lo,tail_hi", [
     (1, 8, 8, 128, [3, 1, 5, 2], [70, 33, 160, 16], 0, 40),      # MHA, small groups, a group of one
     (2, 16, 8, 64, [9, 4], [300, 48], 0, 20),                   # G=2: 8 rows per sequence pair
@@ -70,17 +86,17 @@ def test_full_parallel_sampling_batch_all_rows():
     (5, 4, 4, 64, [20, 17], [96, 200], 0, 70),                  # 20 members: two 16-row tiles
     (6, 8, 8, 128, [4], [16], 0, 0),                             # every context is exactly the prefix
 ])
-def test_groups_of_every_shape(seed, hq, hkv, d, samples, prompt, tail_lo, tail_hi):
-    print(f"case: shared seed={seed} hq={hq} hkv={hkv} d={d}", flush=True)
+def test_groups_of_every_shape(seed, hq, hkv, d, samples, prompt, tail_lo, tail_hi, dtype):
+    print(f"case: shared seed={seed} hq={hq} hkv={hkv} d={d} {dtype}", flush=True)
     w = W.parallel_sampling(seed=seed, groups=len(samples), samples=samples, prompt=prompt, tail_lo=tail_lo,
-                            tail_hi=tail_hi, hq=hq, hkv=hkv, d=d)
+                            tail_hi=tail_hi, hq=hq, hkv=hkv, d=d, dtype=dtype)
     g = GpuReplay(w)
     out, plain, tables, lens = _run(g, w, w.group_start)
     idx = list(range(len(w.decode_seqs)))
     err = float(np.abs(out - _ref(w, idx, tables, lens)).max())
     print(f"err={err:.2e}", flush=True)
-    assert err <= TOL
-    assert float(np.abs(out - plain).max()) <= TOL
+    assert err <= TOL[dtype]
+    assert float(np.abs(out - plain).max()) <= TOL[dtype]
 
 
 def test_hints_that_share_nothing_or_are_malformed_give_plain_decode():
@@ -93,17 +109,19 @@ def test_hints_that_share_nothing_or_are_malformed_give_plain_decode():
     for gs in ([0, S], [0, 2, 5, 9], [0, 9, 3, S], [1, 4, S], [0, 3, S + 5], [0] + list(range(1, S + 1))):
         out, plain, tables, lens = _run(g, w, gs)
         err = float(np.abs(out - _ref(w, idx, tables, lens)).max())
-        assert err <= TOL, (gs, err)
+        assert err <= TOL["bf16"], (gs, err)
     # one group over sequences that were not forked from each other: nothing shared
     u = W.random_small(11, 6, 200, 8, 8, 128, "bf16")
     gu = GpuReplay(u)
     out, plain, tables, lens = _run(gu, u, [0, 6])
-    assert float(np.abs(out - _ref(u, list(range(6)), tables, lens)).max()) <= TOL
+    assert float(np.abs(out - _ref(u, list(range(6)), tables, lens)).max()) <= TOL["bf16"]
 
 
-def test_empty_and_invalid_contexts_inside_a_group():
-    print("case: shared empty/invalid", flush=True)
-    w = W.parallel_sampling(seed=8, groups=2, samples=[4, 3], prompt=[64, 120], tail_lo=0, tail_hi=20, hq=8, d=64)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_empty_and_invalid_contexts_inside_a_group(dtype):
+    print(f"case: shared empty/invalid {dtype}", flush=True)
+    w = W.parallel_sampling(seed=8, groups=2, samples=[4, 3], prompt=[64, 120], tail_lo=0, tail_hi=20, hq=8, d=64,
+                            dtype=dtype)
     g = GpuReplay(w)
     tables, lens = g.tables(w.decode_seqs)
     lens = lens.copy()
@@ -113,7 +131,7 @@ def test_empty_and_invalid_contexts_inside_a_group():
     assert (out[1] == 0).all() and np.isnan(out[5]).all()
     ok = [i for i in range(len(lens)) if i not in (1, 5)]
     err = float(np.abs(out[ok] - _ref(w, ok, tables, lens)).max())
-    assert err <= TOL
+    assert err <= TOL[dtype]
 
 
 # ---------------------------------------------------------------------------
@@ -127,16 +145,17 @@ def _device_inputs(g, w, group_start):
     return rows_to_device(w.q, "cuda"), td, ld, gs, int(lens.max()), tables, lens
 
 
-@pytest.mark.parametrize("hq,hkv,d", [(40, 40, 128), (16, 2, 128), (8, 8, 64)])
-def test_planned_shared_decode_equals_self_planned_on_every_layer(hq, hkv, d):
+@pytest.mark.parametrize("hq,hkv,d,dtype", [(40, 40, 128, "bf16"), (16, 2, 128, "bf16"), (8, 8, 64, "bf16"),
+                                            (40, 40, 128, "f32"), (16, 2, 128, "f32")])
+def test_planned_shared_decode_equals_self_planned_on_every_layer(hq, hkv, d, dtype):
     """One pkv_decode_shared_plan serves two "layers" (the second with K and V
     swapped): each planned call gives the self-planning call's bits."""
-    print(f"case: shared planned H={hq}/{hkv} d={d}", flush=True)
+    print(f"case: shared planned H={hq}/{hkv} d={d} {dtype}", flush=True)
     w = W.parallel_sampling(seed=21, groups=5, samples=[8, 3, 1, 6, 4], prompt=[1000, 300, 80, 1500, 17],
-                            tail_lo=0, tail_hi=200, hq=hq, hkv=hkv, d=d)
+                            tail_lo=0, tail_hi=200, hq=hq, hkv=hkv, d=d, dtype=dtype)
     g = GpuReplay(w)
     q, td, ld, gs, mcl, tables, lens = _device_inputs(g, w, w.group_start)
-    plan = PK.shared_plan_for(td, ld, gs, hq, hkv, mcl, PK.PKV_BF16)
+    plan = PK.shared_plan_for(td, ld, gs, hq, hkv, mcl, PK.PKV_BF16 if dtype == "bf16" else PK.PKV_F32)
     ws = torch.empty(max(PK.pkv_attention_decode_shared_workspace_bytes(len(lens), hq, d, mcl), 256),
                      dtype=torch.uint8, device="cuda")
     ref = _ref(w, list(range(len(lens))), tables, lens)
@@ -150,12 +169,13 @@ def test_planned_shared_decode_equals_self_planned_on_every_layer(hq, hkv, d):
     # the first layer's outputs against the oracle
     PK.pkv_attention_decode_shared_planned(o2, q, g.k_pool, g.v_pool, td, ld, mcl, float(w.scale), plan, workspace=ws)
     torch.cuda.synchronize()
-    assert float(np.abs(o2.cpu().numpy() - ref).max()) <= TOL
+    assert float(np.abs(o2.cpu().numpy() - ref).max()) <= TOL[dtype]
 
 
 def test_planned_shared_decode_plain_shapes_and_mismatched_plans():
     print("case: shared planned fallbacks", flush=True)
-    # fp32 pools: the plan is a plain decode plan and the planned call is plain decode
+    # fp32 pools, one group over sequences that share no blocks: no prefix, so
+    # the planned call runs every sequence on its own units, as plain decode does
     w = W.random_small(31, 7, 1500, 4, 4, 64, "f32")
     g = GpuReplay(w)
     q, td, ld, _, mcl, tables, lens = _device_inputs(g, w, None)
@@ -176,7 +196,7 @@ def test_planned_shared_decode_plain_shapes_and_mismatched_plans():
     o3 = torch.empty((7, 8, 128), dtype=torch.float32, device="cuda")
     PK.pkv_attention_decode_shared_planned(o3, q, gb.k_pool, gb.v_pool, td, ld, mcl, float(wb.scale), plan0)
     torch.cuda.synchronize()
-    assert float(np.abs(o3.cpu().numpy() - _ref(wb, list(range(7)), tables, lens)).max()) <= TOL
+    assert float(np.abs(o3.cpu().numpy() - _ref(wb, list(range(7)), tables, lens)).max()) <= TOL["bf16"]
 
     # a plan built for another max_context_len, or another head grouping: NaN rows
     gs = torch.from_numpy(wb.group_start).cuda()

@@ -35,8 +35,8 @@
  *    para la KV cache" names 16 as typical; the others exist to measure the
  *    trade-off it describes); head_dim 64 or 128; dtype PKV_F32 or PKV_BF16
  *    (the same dtype for q, K and V); num_heads a multiple of num_kv_heads.
- *    The matrix-core kernels -- grouped-query bf16 decode, shared-prefix
- *    decode, chunked prefill -- walk contexts in 16-key tiles and take every
+ *    The matrix-core kernels -- grouped-query decode, shared-prefix decode,
+ *    chunked prefill, each for bf16 and fp32 -- walk contexts in 16-key tiles and take every
  *    supported block size: a tile is two 8-token blocks, one 16-token block
  *    or half of a 32-token block.
  *  - Calls that enqueue work on one stream are ordered by that stream.  For one
@@ -281,14 +281,14 @@ pkv_status pkv_attention_decode_noalloc(float* out, const void* q, const void* k
  * block-table entries equal in every member and wholly below every member's
  * context (its tokens rounded down to a multiple of 16: with 8-token blocks
  * an odd last common block goes to the members' own parts), reads those K/V
- * tiles once for all members (bf16, Hq/Hkv <= 16:
- * the members' query rows share one matrix-core tile, up to 16 rows), decodes
- * each member's remaining tokens on its own, and merges the two parts by
- * their softmax statistics.  A malformed group_start, groups of one sequence,
- * members with invalid contexts or tables with no common first block simply
- * give no shared part, so no hint changes a result beyond rounding.  fp32
- * pools, more than 16 query heads per KV head or num_groups = 0 run plain
- * decode.  workspace: at least pkv_attention_decode_shared_workspace_bytes(...)
+ * tiles once for all members (Hq/Hkv <= 16: the members' query rows share
+ * one matrix-core tile, up to 16 rows; bf16 pools on the bf16 matrix cores,
+ * fp32 pools on the fp32 ones), decodes each member's remaining tokens on its
+ * own, and merges the two parts by their softmax statistics.  A malformed
+ * group_start, groups of one sequence, members with invalid contexts or
+ * tables with no common first block simply give no shared part, so no hint
+ * changes a result beyond rounding.  More than 16 query heads per KV head or
+ * num_groups = 0 run plain decode.  workspace: at least pkv_attention_decode_shared_workspace_bytes(...)
  * bytes, 256-byte aligned, caller-owned device memory.
  * ------------------------------------------------------------------------ */
 size_t pkv_attention_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
@@ -316,8 +316,8 @@ pkv_status pkv_attention_decode_shared(float* out, const void* q, const void* k_
  * max_context_len) bytes, 256-byte aligned; the other arguments as for
  * pkv_attention_decode_shared (num_heads, num_kv_heads, block_size and dtype
  * must be those of the decode calls; group_start may be NULL when num_groups
- * is 0).  Where the shared path does not apply (fp32, more than 16 query
- * heads per KV head) the plan is a plain decode plan and the planned call
+ * is 0).  Where the shared path does not apply (more than 16 query heads
+ * per KV head) the plan is a plain decode plan and the planned call
  * runs plain decode.  A plan built for other sizes
  * or another head grouping makes the planned call write NaN rows.
  * The planned call's workspace: at least

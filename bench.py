@@ -358,8 +358,9 @@ def secondary(args):
                     "shared_over_plain_speedup": round(dec_us / sh_us, 3),
                     "shared_self_planned_us_per_layer": round(sh_self_us, 2),
                     "shared_kernels": "shared_plans_kernel once per step (shared prefixes, then the tails' plan) "
-                                      "+ decode_shared_fused_kernel per layer (shared prompt blocks on the matrix "
-                                      "cores, each sample's tail on the vector ALUs, merge of split rows inside)"})
+                                      "+ per layer decode_shared_mfma_kernel (shared prompt blocks on the matrix "
+                                      "cores) and decode_valu_kernel (each sample's tail, merge of split rows "
+                                      "inside)"})
         # the same batch over float32 pools (2 layers of the same tables): plain
         # decode, and shared-prefix decode (the shared blocks on the fp32 matrix
         # cores, then the samples' tails on the vector-ALU kernel)

@@ -288,8 +288,10 @@ pkv_status pkv_attention_decode_noalloc(float* out, const void* q, const void* k
  * group_start, groups of one sequence, members with invalid contexts or
  * tables with no common first block simply give no shared part, so no hint
  * changes a result beyond rounding.  More than 16 query heads per KV head or
- * num_groups = 0 run plain decode.  workspace: at least pkv_attention_decode_shared_workspace_bytes(...)
- * bytes, 256-byte aligned, caller-owned device memory.
+ * num_groups = 0 run plain decode.  The work is two launches on `stream`
+ * (the shared parts, then the members' own parts).  workspace: at least
+ * pkv_attention_decode_shared_workspace_bytes(...) bytes, 256-byte aligned,
+ * caller-owned device memory.
  * ------------------------------------------------------------------------ */
 size_t pkv_attention_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                                    int32_t max_context_len);

@@ -493,7 +493,10 @@ static pkv_status shared_decode(const char* fn, float* out, const void* q, const
   // split rows are merged inside the decode launch
   a.merge_tickets = reinterpret_cast<uint64_t*>(part + l.tickets);
   a.merge_epoch = next_merge_epoch();
-  return hip_status(fn, dtype == PKV_BF16 ? pkv_launch_shared_fused(a, stream) : pkv_launch_shared_f32(a, stream));
+  // the shared units, then every sequence's own units, on one epoch
+  const int err = dtype == PKV_BF16 ? pkv_launch_shared_units(a, stream) : pkv_launch_shared_units_f32(a, stream);
+  if (err) return hip_status(fn, err);
+  return hip_status(fn, pkv_launch_decode(a, stream));
 }
 
 static pkv_status check_decode_pointers(const char* fn, float* out, const void* q, const void* k_cache,

@@ -25,8 +25,8 @@
 // Shared-prefix decode ([OS] "El regalo extra: compartir memoria"): the same
 // body takes a fork group's shared leading blocks once for all its members,
 // whose (member, query head) pairs become the tile's rows (16 / G members per
-// unit); each member's own tokens are then decoded by the plain kernels, and
-// a row's last unit to finish merges it.
+// unit); each member's own tokens are then decoded by the plain kernels in a
+// second launch, and a row's last unit to finish merges it.
 //
 // Matrix-core layout of v_mfma_f32_16x16x4_f32: lane l, n = l % 16,
 // g = l / 16, supplies A[n][g] and B[g][n] and receives D[4g + j][n] in
@@ -414,21 +414,13 @@ int pkv_launch_decode_group_f32(const pkv_decode_args& a, void* stream) {
   return hipGetLastError();
 }
 
-// Shared-prefix decode over float32 pools: the shared units, then every
-// sequence's own units on the plain decode kernels (the vector-ALU kernel or
-// the group kernel above), on one stream.  The two launches share the merge
-// epoch, so a row's tickets count the units of both, and its last unit (in
-// the second launch, or a shared unit when a member has no own tokens)
-// merges it.  (Two launches rather than one fused kernel: this body needs
-// twice the registers of the vector-ALU one, which in one kernel would halve
-// the occupancy of the sequences' own units.)
-int pkv_launch_shared_f32(const pkv_decode_args& a, void* stream) {
+// The shared-prefix units over float32 pools (the sequences' own units follow
+// in a launch of the plain decode kernels).
+int pkv_launch_shared_units_f32(const pkv_decode_args& a, void* stream) {
   const int64_t npp = (a.max_context_len + a.prefix_part_tokens - 1) / a.prefix_part_tokens;
   const int64_t shared = static_cast<int64_t>(a.num_seqs) * (npp < 1 ? 1 : npp) * a.num_kv_heads;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (a.head_dim == 128) launch_bs<128>(a.block_size, dim3(static_cast<uint32_t>(shared)), st, a, true);
   else launch_bs<64>(a.block_size, dim3(static_cast<uint32_t>(shared)), st, a, true);
-  const int err = hipGetLastError();
-  if (err) return err;
-  return pkv_launch_decode(a, stream);
+  return hipGetLastError();
 }

@@ -1,6 +1,6 @@
 // Vector-ALU paged decode (one query per (sequence, head)) as a device
-// function, included by the kernel sources: the decode kernel runs it alone,
-// the fused shared-prefix kernel runs it for the sequences' own tokens.
+// function run by the decode kernel, also for the sequences' own tokens of a
+// shared-prefix decode (units from a per-sequence start).
 #pragma once
 
 #include "pkv_device.h"

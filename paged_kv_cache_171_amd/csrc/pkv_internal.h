@@ -126,7 +126,7 @@ struct pkv_decode_args {
   // MFMA group kernel per (sequence, KV head), at its first query head's row
   // (pkvd::ticket_arrive: (merge_epoch << 24) | units arrived); the unit that
   // arrives last merges the row and sets the word back to 0.  merge_epoch is
-  // nonzero, below 2^40 and new for every call (the two launches of a float32
+  // nonzero, below 2^40 and new for every call (the two launches of a
   // shared-prefix decode share one: a row's units in both count together).
   uint64_t* merge_tickets;
   uint64_t merge_epoch;
@@ -143,19 +143,17 @@ int pkv_launch_plan(int32_t* plan, const int32_t* context_lens, int32_t num_seqs
 
 // Shared-prefix decode (pkv_mfma.hip): one kernel plans the groups' common
 // leading blocks (fills seq_start and the shared plan) and then the sequences'
-// own units from those starts; then one launch decodes both (bf16), or one
-// launch the shared units and one the own units (float32).  Tokens per
+// own units from those starts; then one launch decodes the shared units and
+// one (pkv_launch_decode) the own units, on one merge epoch.  Tokens per
 // shared-prefix partition:
 constexpr int32_t kPrefixPartTokens = 1024;
 int pkv_launch_shared_plans(const pkv_decode_args& a, const int32_t* group_start, int32_t num_groups,
                             int32_t* seq_start, int32_t* shared_plan, int32_t* plan, void* stream);
-// The shared-prefix units and the sequences' own units in one launch (split
-// rows merged inside it), bf16 pools.
-int pkv_launch_shared_fused(const pkv_decode_args& a, void* stream);
-// The same over float32 pools (pkv_decode_f32.hip): the shared units on the
-// fp32 matrix cores, then the own units on the plain decode kernels; rows are
-// merged by their last unit, in either launch.
-int pkv_launch_shared_f32(const pkv_decode_args& a, void* stream);
+// The shared-prefix units on the matrix cores: bf16 pools (pkv_mfma.hip) and
+// float32 pools (pkv_decode_f32.hip).  A row is merged by its last unit, in
+// this launch or in the own units' launch after it.
+int pkv_launch_shared_units(const pkv_decode_args& a, void* stream);
+int pkv_launch_shared_units_f32(const pkv_decode_args& a, void* stream);
 
 // Causal chunked-prefill attention (pkv_mfma.hip).
 struct pkv_prefill_args {

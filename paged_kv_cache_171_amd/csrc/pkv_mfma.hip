@@ -37,7 +37,7 @@
 // error of up to 2^-9 |v_j - v_k| on a row whose weight sits on two keys j, k.  Masked keys are removed by select
 // (score -inf, V row 0), never by multiplying, so NaN in unused slots cannot
 // reach the output.
-#include "pkv_decode_valu.h"
+#include "pkv_device.h"
 #include "pkv_plan.h"
 
 namespace {
@@ -549,22 +549,12 @@ __global__ __launch_bounds__(256, BS == 8 ? 3 : 4) void decode_group_mfma_kernel
   decode_group_mfma_body<D, BS>(a, blockIdx.x, false);
 }
 
-// Shared-prefix decode in one launch: the first shared_wgs workgroups take
-// the groups' shared-prefix units (matrix cores), the rest the sequences' own
-// units -- on the MFMA group kernel for grouped-query heads, else the VALU
-// kernel -- so the short per-sequence units fill the CUs the long shared units
-// leave free instead of waiting for them.
-template <int D, int BS, bool kGroupTail>
-__global__ __launch_bounds__(256, BS == 8 ? 3 : 4) void decode_shared_fused_kernel(pkv_decode_args a,
-                                                                                  uint32_t shared_wgs) {
-  if constexpr (kGroupTail) {
-    const bool shared_unit = blockIdx.x < shared_wgs;
-    decode_group_mfma_body<D, BS>(a, shared_unit ? blockIdx.x : blockIdx.x - shared_wgs, shared_unit);
-  } else if (blockIdx.x < shared_wgs) {
-    decode_group_mfma_body<D, BS>(a, blockIdx.x, true);
-  } else {
-    decode_valu_body<uint16_t, D, BS>(a, blockIdx.x - shared_wgs);
-  }
+// The shared-prefix units of a shared-prefix decode (one workgroup per
+// possible unit and KV head; those past the shared plan's count exit).  The
+// sequences' own units follow in a launch of the plain decode kernels.
+template <int D, int BS>
+__global__ __launch_bounds__(256, BS == 8 ? 3 : 4) void decode_shared_mfma_kernel(pkv_decode_args a) {
+  decode_group_mfma_body<D, BS>(a, blockIdx.x, true);
 }
 
 // ---------------------------------------------------------------------------
@@ -1094,15 +1084,9 @@ struct GroupDecode {
   }
 };
 template <int D, int BS>
-struct SharedFusedGroupTail {
-  static void launch(dim3 grid, hipStream_t st, const pkv_decode_args& a, uint32_t sw) {
-    hipLaunchKernelGGL((decode_shared_fused_kernel<D, BS, true>), grid, dim3(256), 0, st, a, sw);
-  }
-};
-template <int D, int BS>
-struct SharedFusedValuTail {
-  static void launch(dim3 grid, hipStream_t st, const pkv_decode_args& a, uint32_t sw) {
-    hipLaunchKernelGGL((decode_shared_fused_kernel<D, BS, false>), grid, dim3(256), 0, st, a, sw);
+struct SharedUnits {
+  static void launch(dim3 grid, hipStream_t st, const pkv_decode_args& a) {
+    hipLaunchKernelGGL((decode_shared_mfma_kernel<D, BS>), grid, dim3(256), 0, st, a);
   }
 };
 }  // namespace
@@ -1124,18 +1108,12 @@ int pkv_launch_shared_plans(const pkv_decode_args& a, const int32_t* group_start
   return hipGetLastError();
 }
 
-int pkv_launch_shared_fused(const pkv_decode_args& a, void* stream) {
+int pkv_launch_shared_units(const pkv_decode_args& a, void* stream) {
   // at most num_seqs sub-groups, each with ceil(max_context_len / partition) units
   const int64_t npp = (a.max_context_len + a.prefix_part_tokens - 1) / a.prefix_part_tokens;
   const int64_t shared = static_cast<int64_t>(a.num_seqs) * (npp < 1 ? 1 : npp) * a.num_kv_heads;
-  const bool group_tail = pkv_uses_mfma(a.dtype, a.num_heads, a.num_kv_heads, a.block_size);
-  const int64_t np = (a.max_context_len + a.part_tokens - 1) / a.part_tokens;
-  const int64_t own = static_cast<int64_t>(a.num_seqs) * (np < 1 ? 1 : np) * (group_tail ? a.num_kv_heads : a.num_heads);
-  const dim3 grid(static_cast<uint32_t>(shared + own));
-  const uint32_t sw = static_cast<uint32_t>(shared);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (group_tail) launch_d_bs<SharedFusedGroupTail>(a.head_dim, a.block_size, grid, st, a, sw);
-  else launch_d_bs<SharedFusedValuTail>(a.head_dim, a.block_size, grid, st, a, sw);
+  launch_d_bs<SharedUnits>(a.head_dim, a.block_size, dim3(static_cast<uint32_t>(shared)),
+                           static_cast<hipStream_t>(stream), a);
   return hipGetLastError();
 }
 

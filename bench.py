@@ -1040,6 +1040,20 @@ def mfma_probe(stream, reps: int = 10) -> dict:
                     raise RuntimeError(f"mfma_rate launch failed: {rc}")
             flops = grid * 4 * iters * chains * 16384
             res[f"{chains} chain(s), {grid // 256} waves/SIMD"] = round(flops / _median_us(run, stream, reps) / 1e6, 1)
+    # the 32 x 32 x 16 instruction (32768 flops each)
+    lib.pkvprobe_mfma32_rate.restype = ctypes.c_int
+    lib.pkvprobe_mfma32_rate.argtypes = lib.pkvprobe_mfma_rate.argtypes
+    for grid in (1024, 2048):
+        for chains in (1, 2):
+            iters = 2048 // chains
+
+            def run_wide(grid=grid, chains=chains, iters=iters):
+                rc = lib.pkvprobe_mfma32_rate(out.data_ptr(), grid, iters, chains, stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"mfma32_rate launch failed: {rc}")
+            flops = grid * 4 * iters * chains * 32768
+            res[f"32x32x16: {chains} chain(s), {grid // 256} waves/SIMD"] = round(
+                flops / _median_us(run_wide, stream, reps) / 1e6, 1)
     res["unit"] = "TFLOP/s"
     res["dense_bf16_peak"] = 2500.0
     # the fp32 matrix cores (v_mfma_f32_16x16x4_f32, 2048 flops each)

@@ -13,6 +13,9 @@
 //   mfma_rate_kernel    -- the bf16 matrix-core rate with no memory traffic:
 //                          chains of v_mfma_f32_16x16x32_bf16 per wave (the
 //                          instruction the prefill kernel is built on)
+//   mfma32_rate_kernel  -- the same with the 32 x 32 x 16 bf16 instruction
+//                          (v_mfma_f32_32x32x16_bf16: twice the work per
+//                          instruction, half the operand reads per flop)
 //   mfma_f32_rate_kernel -- the same for the fp32 matrix cores
 //                          (v_mfma_f32_16x16x4_f32, the float32 prefill's)
 //   overlap_kernel      -- how far matrix-core work of some waves and vector
@@ -120,6 +123,33 @@ __global__ __launch_bounds__(256) void mfma_rate_kernel(float* __restrict__ out,
   out[static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x] = sum;
 }
 
+// CH independent accumulator chains per wave, iters 32 x 32 x 16 MFMAs on each.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+template <int CH>
+__global__ __launch_bounds__(256) void mfma32_rate_kernel(float* __restrict__ out, int32_t iters) {
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = static_cast<__bf16>(threadIdx.x * 0.001f + i);
+    b[i] = static_cast<__bf16>(i * 0.5f);
+  }
+  f32x16 acc[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[c][j] = 0.f;
+  for (int32_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sum += acc[c][j];
+  out[static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x] = sum;
+}
+
 // CH independent accumulator chains per wave, iters fp32 MFMAs on each.
 template <int CH>
 __global__ __launch_bounds__(256) void mfma_f32_rate_kernel(float* __restrict__ out, int32_t iters) {
@@ -203,6 +233,17 @@ extern "C" int pkvprobe_overlap(float* out, int32_t grid, int32_t mode, int32_t 
                                 void* stream) {
   hipLaunchKernelGGL(overlap_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), out, mode,
                      mfma_iters, valu_iters);
+  return hipGetLastError();
+}
+
+// out: grid * 256 floats.  chains: 1 or 2 accumulator chains per wave (each
+// MFMA 32 x 32 x 16 x 2 = 32768 flops).  Returns the launch status.
+extern "C" int pkvprobe_mfma32_rate(float* out, int32_t grid, int32_t iters, int32_t chains, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (chains == 1)
+    hipLaunchKernelGGL((mfma32_rate_kernel<1>), dim3(grid), dim3(256), 0, st, out, iters);
+  else
+    hipLaunchKernelGGL((mfma32_rate_kernel<2>), dim3(grid), dim3(256), 0, st, out, iters);
   return hipGetLastError();
 }
 

@@ -118,6 +118,20 @@ def test_hints_that_share_nothing_or_are_malformed_give_plain_decode():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_groups_of_more_than_sixteen_query_heads_per_kv_head_run_plain_decode(dtype):
+    """32 query heads over one KV head: no 16-row tile holds a member, so the
+    call is plain decode (the group kernel in two 16-row slices), bit for bit."""
+    print(f"case: shared G=32 {dtype}", flush=True)
+    w = W.parallel_sampling(seed=9, groups=2, samples=[3, 4], prompt=[300, 1100], tail_lo=0, tail_hi=60, hq=32,
+                            hkv=1, d=128, dtype=dtype)
+    g = GpuReplay(w)
+    out, plain, tables, lens = _run(g, w, w.group_start)
+    assert np.array_equal(out, plain)
+    err = float(np.abs(out - _ref(w, list(range(len(lens))), tables, lens)).max())
+    assert err <= TOL[dtype], err
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_empty_and_invalid_contexts_inside_a_group(dtype):
     print(f"case: shared empty/invalid {dtype}", flush=True)
     w = W.parallel_sampling(seed=8, groups=2, samples=[4, 3], prompt=[64, 120], tail_lo=0, tail_hi=20, hq=8, d=64,

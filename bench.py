@@ -314,6 +314,21 @@ def secondary(args):
         mq_us = _timed(decode_mqa_all, reps, stream) / len(mpools)
         res.update({"decode_64x1_us_per_layer": round(mq_us, 2),
                     "decode_64x1_kv_gbps": round(kv_logical / Hkv / mq_us / 1e3, 1)})
+        # 16 query heads over the one KV head: 256 (sequence, KV head) pairs,
+        # so the library cuts contexts into 1024-token partitions to fill the CUs
+        q16 = q[:, :16].contiguous()
+        out16 = torch.empty(len(seqs), 16, D, dtype=torch.float32, device=dev)
+        plan16 = PK.plan_for(ld, 16, 1, MB, mcl, PK.PKV_BF16)
+
+        def decode_16x1_all():
+            for kp, vp in mpools:
+                PK.pkv_attention_decode(out16, q16, kp, vp, td, ld, mcl, scale, workspace=ws, plan=plan16)
+        decode_16x1_all()
+        torch.cuda.synchronize()
+        m16_us = _timed(decode_16x1_all, reps, stream) / len(mpools)
+        res.update({"decode_16x1_us_per_layer": round(m16_us, 2),
+                    "decode_16x1_kv_gbps": round(kv_logical / Hkv / m16_us / 1e3, 1),
+                    "decode_16x1_partition_tokens": int(plan16[16:20].view(torch.int32).item())})
         del mpools
     if name == "fork":
         unique = len({int(b) for s, c in zip(range(len(seqs)), lens_h) for b in tables_h[s, :-(-int(c) // P)]})

@@ -277,7 +277,7 @@ pkv_status pkv_batch_schedule(pkv_batch* b, void* stream, pkv_step_info* info) {
   // the same copy, so the step needs no plan kernel
   if (nd > 0)
     host_plan(reinterpret_cast<int32_t*>(hs + o_plan), reinterpret_cast<const int32_t*>(hs + o_dcl), nd, mbd, BS,
-              mcl_d, pkv_part_tokens(b->dtype, b->Hq, b->Hkv, BS), b->plan_count);
+              mcl_d, pkv_part_tokens(b->dtype, nd, b->Hq, b->Hkv, BS, mcl_d), b->plan_count);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (hipMemcpyAsync(b->dev, hs, off, hipMemcpyHostToDevice, s) != hipSuccess ||
       hipEventRecord(b->ev[h], s) != hipSuccess) {

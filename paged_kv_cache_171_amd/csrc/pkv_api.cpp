@@ -128,7 +128,7 @@ pkv_decode_args shared_args(const SharedLayout& l, float* out, const void* q, co
   a.block_size = block_size;
   a.max_context_len = max_context_len;
   a.num_partitions = l.slots;
-  a.part_tokens = pkv_part_tokens(dtype, num_heads, num_kv_heads, block_size);
+  a.part_tokens = pkv_part_tokens(dtype, num_seqs, num_heads, num_kv_heads, block_size, max_context_len);
   a.scale_log2 = scale * 1.4426950408889634f;
   a.dtype = dtype;
   a.seq_start = reinterpret_cast<const int32_t*>(plan + l.seq_start);
@@ -278,7 +278,7 @@ pkv_status pkv_decode_plan(void* plan, size_t plan_bytes_given, const int32_t* c
                      plan_bytes_given, need);
   return hip_status(fn, pkv_launch_plan(static_cast<int32_t*>(plan), context_lens, num_seqs, max_blocks_per_seq,
                                         block_size, max_context_len,
-                                        pkv_part_tokens(dtype, num_heads, num_kv_heads, block_size), stream));
+                                        pkv_part_tokens(dtype, num_seqs, num_heads, num_kv_heads, block_size, max_context_len), stream));
 }
 
 size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
@@ -318,7 +318,7 @@ pkv_status pkv_decode_impl(const char* fn, float* out, const void* q, const void
   const int64_t grid = static_cast<int64_t>(num_seqs) * num_heads * np;
   if (grid > 0x7FFFFFFF || static_cast<int64_t>(num_seqs) * (np + 1) > 0x3FFFFFFF)
     return pkv_failf(PKV_ERR_UNSUPPORTED, "%s: launch grid too large", fn);
-  const int32_t part_tokens = pkv_part_tokens(dtype, num_heads, num_kv_heads, block_size);
+  const int32_t part_tokens = pkv_part_tokens(dtype, num_seqs, num_heads, num_kv_heads, block_size, max_context_len);
   const size_t pb = plan_bytes(num_seqs, max_context_len);
   const size_t part = partial_bytes(num_seqs, num_heads, head_dim, max_context_len);
   const size_t need = (build_plan ? align256(pb) : 0) + part;
@@ -456,7 +456,7 @@ pkv_status pkv_decode_shared_plan(void* plan, size_t plan_bytes_given, const int
     // plain decode: only the own plan region is used
     return hip_status(fn, pkv_launch_plan(reinterpret_cast<int32_t*>(pb + l.plan), context_lens, num_seqs,
                                           max_blocks_per_seq, block_size, max_context_len,
-                                          pkv_part_tokens(dtype, num_heads, num_kv_heads, block_size), stream));
+                                          pkv_part_tokens(dtype, num_seqs, num_heads, num_kv_heads, block_size, max_context_len), stream));
   }
   const pkv_decode_args a = shared_args(l, nullptr, nullptr, nullptr, nullptr, block_tables, max_blocks_per_seq,
                                         context_lens, num_seqs, num_heads, num_kv_heads, 128, block_size, 1,

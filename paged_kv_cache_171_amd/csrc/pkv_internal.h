@@ -35,10 +35,14 @@ int pkv_launch_swap_blocks(void* k_dst, void* v_dst, int32_t dst_blocks, const v
                            void* stream);
 
 // Context partitions of the decode work split (multiples of 16 tokens): 1024
-// tokens for the VALU kernel, 4096 for the MFMA group kernel (which reads
-// Hq/Hkv heads per tile and gains more from long units than from balance).
+// tokens for the VALU kernel; for the MFMA group kernels (which read Hq/Hkv
+// heads per tile and gain more from long units than from balance) the largest
+// of 4096, 2048 and 1024 tokens that still gives a full round of workgroups --
+// four per CU on 256 CUs -- for the call's sizes, so that a batch of few
+// sequences or KV heads gets shorter units instead of idle CUs.
 constexpr int32_t kMinPartTokens = 1024;
 constexpr int32_t kMaxPartTokens = 4096;
+constexpr int64_t kMfmaRoundWorkgroups = 1024;
 constexpr int32_t kMaxMfmaGroup = 16;
 // Whether decode of these heads runs on a matrix-core group kernel -- bf16 or
 // float32, two or more query heads per KV head (a group of more than 16 in
@@ -49,8 +53,17 @@ inline bool pkv_uses_mfma(int dtype, int32_t num_heads, int32_t num_kv_heads, in
   (void)block_size;
   return (dtype == PKV_BF16 || dtype == PKV_F32) && group >= 2;
 }
-inline int32_t pkv_part_tokens(int dtype, int32_t num_heads, int32_t num_kv_heads, int32_t block_size) {
-  return pkv_uses_mfma(dtype, num_heads, num_kv_heads, block_size) ? kMaxPartTokens : kMinPartTokens;
+inline int32_t pkv_part_tokens(int dtype, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                               int32_t block_size, int32_t max_context_len) {
+  if (!pkv_uses_mfma(dtype, num_heads, num_kv_heads, block_size)) return kMinPartTokens;
+  // workgroups per partition of every context: (sequence, KV head, 16-row slice)
+  const int64_t groups = static_cast<int64_t>(num_seqs > 0 ? num_seqs : 0) * num_kv_heads *
+                         ((num_heads / num_kv_heads + kMaxMfmaGroup - 1) / kMaxMfmaGroup);
+  for (int32_t p = kMaxPartTokens; p > kMinPartTokens; p /= 2) {
+    const int64_t parts = (static_cast<int64_t>(max_context_len) + p - 1) / p;
+    if (groups * (parts < 1 ? 1 : parts) >= kMfmaRoundWorkgroups) return p;
+  }
+  return kMinPartTokens;
 }
 
 // Sizes of the decode plan and of the split-context partials.

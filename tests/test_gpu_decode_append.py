@@ -79,14 +79,14 @@ def _run(w, seed, no_new=(), wrong=(), planned=False):
 @pytest.mark.parametrize("seed,S,max_ctx,hq,hkv,d,dtype,bs", [
     (1, 7, 300, 4, 4, 64, "f32", 16),
     (2, 9, 2500, 8, 8, 128, "bf16", 16),     # split contexts on the VALU kernel
-    (3, 6, 5000, 16, 2, 128, "bf16", 16),    # MFMA group kernel, split past 4096
+    (3, 6, 5000, 16, 2, 128, "bf16", 16),    # MFMA group kernel, split contexts
     (4, 5, 900, 8, 2, 64, "f32", 16),        # fp32 group kernel
     (5, 7, 700, 4, 4, 128, "bf16", 8),
     (6, 7, 1300, 8, 8, 64, "f32", 32),
     (7, 6, 5000, 16, 2, 128, "bf16", 8),     # MFMA group kernel: two 8-token blocks per 16-key tile
     (8, 6, 5000, 16, 2, 128, "bf16", 32),    # MFMA group kernel: two 16-key tiles per block
     (9, 9, 300, 8, 4, 64, "bf16", 8),        # the new token in either half of a tile
-    (10, 6, 5000, 8, 2, 128, "f32", 8),      # fp32 group kernel, split past 4096, 8-token blocks
+    (10, 6, 5000, 8, 2, 128, "f32", 8),      # fp32 group kernel, split contexts, 8-token blocks
     (11, 7, 400, 16, 4, 128, "f32", 32),     # fp32 group kernel, 32-token blocks
     (12, 5, 4500, 32, 1, 128, "bf16", 16),   # two 16-row slices (the first one stores the row)
     (13, 4, 900, 64, 2, 64, "f32", 8),       # fp32, two slices

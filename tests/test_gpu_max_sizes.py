@@ -2,8 +2,8 @@
 sequences than the plan kernel's 1024 threads (three chunks of its scans),
 empty contexts among them; a vector-ALU context of 70,000 tokens (69 partitions
 of 1024, merged in nine chunks of eight) and a grouped-query context of 140,000
-tokens on the matrix-core kernels, bf16 and float32 (35 partitions of 4096); a 3000-query prefill
-chunk ending a 20,000-token context (hundreds of key tiles per wave, dozens of
+tokens on the matrix-core kernels, bf16 and float32 (137 partitions of 1024 for a
+batch of three sequences); a 3000-query prefill chunk ending a 20,000-token context (hundreds of key tiles per wave, dozens of
 row tiles), bf16 and float32, checked on its first, middle and last queries."""
 import numpy as np
 import pytest

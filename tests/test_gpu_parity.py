@@ -75,8 +75,9 @@ def test_tiny_workload_bit_exact_state_and_attention():
 
 SMALL = [
     # seed, S, max_ctx, Hq, Hkv, d, dtype.  Contexts are cut into 1024-token
-    # partitions on the VALU kernel (MHA) and 4096-token ones on the
-    # matrix-core group kernels (bf16 or fp32, two or more heads per KV head);
+    # partitions on the VALU kernel (MHA) and on the matrix-core group
+    # kernels (bf16 or fp32, two or more heads per KV head) for batches as
+    # small as these (4096 tokens once the units fill a round of workgroups);
     # a longer context exercises the merge.
     (11, 7, 70, 4, 4, 64, "f32"),
     (12, 9, 1300, 2, 2, 128, "f32"),
@@ -85,7 +86,7 @@ SMALL = [
     (15, 6, 1700, 4, 1, 64, "bf16"),
     (16, 10, 2100, 2, 2, 64, "f32"),
     (17, 3, 33, 16, 16, 128, "bf16"),
-    (18, 9, 9000, 8, 2, 128, "f32"),       # fp32 group kernel, contexts split at 4096 and merged
+    (18, 9, 9000, 8, 2, 128, "f32"),       # fp32 group kernel, contexts split and merged
     (19, 11, 700, 12, 4, 64, "f32"),       # G = 3
 ]
 
@@ -375,18 +376,30 @@ def test_plan_built_for_other_sizes_gives_nan_rows():
     assert torch.isnan(o).all()
 
 
-@pytest.mark.parametrize("ctxs,hq,hkv,dtype", [
+_EDGES_4096 = [4095, 4096, 4097, 3, 8191, 8192, 8193, 700]
+
+
+@pytest.mark.parametrize("ctxs,hq,hkv,dtype,part", [
     # the VALU kernel's 1024-token partitions (MHA)
-    ([1023, 1024, 1025, 1, 16, 17, 2047, 2048, 2049, 3073], 4, 4, "bf16"),
-    # the matrix-core group kernels' 4096-token partitions (4 query heads per KV head)
-    ([4095, 4096, 4097, 3, 8191, 8192, 8193, 700], 8, 2, "bf16"),
-    ([4095, 4096, 4097, 3, 8191, 8192, 8193, 700], 8, 2, "f32"),
+    ([1023, 1024, 1025, 1, 16, 17, 2047, 2048, 2049, 3073], 4, 4, "bf16", 1024),
+    # the matrix-core group kernels: few (sequence, KV head) pairs take
+    # 1024-token partitions, so that the units fill a round of workgroups ...
+    ([1023, 1024, 1025, 4095, 4096, 4097, 3, 2049], 8, 2, "bf16", 1024),
+    ([1023, 1024, 1025, 4095, 4096, 4097, 3, 2049], 8, 2, "f32", 1024),
+    # ... and 512 pairs over three 4096-token partitions already do
+    (_EDGES_4096 * 8, 16, 8, "bf16", 4096),
+    (_EDGES_4096 * 8, 16, 8, "f32", 4096),
 ])
-def test_partition_boundaries(ctxs, hq, hkv, dtype):
-    """Context lengths on and next to the partition edges of the decode kernels."""
-    print(f"case: partition edges {ctxs} H={hq}/{hkv} {dtype}", flush=True)
+def test_partition_boundaries(ctxs, hq, hkv, dtype, part):
+    """Context lengths on and next to the partition edges of the decode kernels
+    (the partition the library chose is read from the plan's header)."""
+    print(f"case: partition edges {len(ctxs)} seqs H={hq}/{hkv} {dtype} part {part}", flush=True)
     w = W._plain_decode("edges", 77, ctxs, hq, hkv, 128, dtype)
     g, r = GpuReplay(w), _oracle(w)
+    tables, lens = g.tables(w.decode_seqs)
+    plan = PK.plan_for(torch.from_numpy(lens).cuda(), hq, hkv, tables.shape[1], int(lens.max()),
+                       PK.PKV_BF16 if dtype == "bf16" else PK.PKV_F32)
+    assert int(plan[16:20].view(torch.int32).item()) == part      # header word 4: tokens per partition
     err = _attn_err(g, r, w)
     assert err <= TOL[dtype], err
 

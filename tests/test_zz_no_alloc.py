@@ -51,7 +51,7 @@ def _with_workspace(args, shape):
 
 
 def test_noalloc_matches_the_workspace_entry_point_on_consecutive_calls():
-    # first: grouped-query bf16 (matrix-core kernel, 4096-token partitions), contexts up to 9000
+    # first: grouped-query bf16 (matrix-core kernel), contexts up to 9000
     wa = W.random_small(81, 14, 9000, 8, 2, 128, "bf16", min_ctx=3000)
     # second, smaller: fp32 MHA (vector-ALU kernel, 1024-token partitions)
     wb = W.random_small(82, 5, 2600, 4, 4, 64, "f32", min_ctx=900)

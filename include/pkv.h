@@ -149,11 +149,13 @@ pkv_status pkv_swap_blocks(void* dst_k_cache, void* dst_v_cache, int32_t dst_num
  * q: device [num_seqs][num_heads][head_dim] in `dtype`; out: device float32
  * [num_seqs][num_heads][head_dim]; context_lens: device int32 [num_seqs].
  * Scores, softmax and accumulation are float32.  Query-head groups of two or
- * more heads per KV head run on the matrix cores, every K/V row read once per
- * 16 heads of the group: bf16 pools with the probabilities carried as a bf16
- * pair (~16 significant bits), float32 pools with exact fp32 products; one
- * query head per KV head runs on the vector ALUs, one head per workgroup.  max_context_len must be >= every
- * context length (it sizes the context split); a row whose length exceeds it or
+ * more heads per KV head run on the matrix cores: bf16 pools with the
+ * probabilities carried as a bf16 pair (~16 significant bits), every K/V row
+ * read once per group of up to 64 heads (once per 16 heads beyond); float32
+ * pools with exact fp32 products, every K/V row read once per 16 heads.  One
+ * query head per KV head runs on the vector ALUs, one head per workgroup.
+ * max_context_len must be >= every context length (it sizes the context
+ * split); a row whose length exceeds it or
  * max_blocks_per_seq*block_size, or whose table names a block outside
  * [0, num_blocks), is written as NaN.
  * workspace: device scratch of at least pkv_attention_workspace_bytes(...) bytes

@@ -53,15 +53,25 @@ inline bool pkv_uses_mfma(int dtype, int32_t num_heads, int32_t num_kv_heads, in
   (void)block_size;
   return (dtype == PKV_BF16 || dtype == PKV_F32) && group >= 2;
 }
+// Whether a bf16 group of 17..64 query heads per KV head runs on the wide
+// group kernel (one workgroup for all its 16-row slices, K/V staged once in
+// LDS; two workgroups per CU) instead of one workgroup per slice.
+inline bool pkv_wide_group(int dtype, int32_t num_heads, int32_t num_kv_heads) {
+  const int32_t group = num_heads / num_kv_heads;
+  return dtype == PKV_BF16 && group > kMaxMfmaGroup && group <= 4 * kMaxMfmaGroup;
+}
 inline int32_t pkv_part_tokens(int dtype, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                int32_t block_size, int32_t max_context_len) {
   if (!pkv_uses_mfma(dtype, num_heads, num_kv_heads, block_size)) return kMinPartTokens;
-  // workgroups per partition of every context: (sequence, KV head, 16-row slice)
+  // workgroups per partition of every context: (sequence, KV head), and per
+  // 16-row slice unless the wide kernel takes all slices in one
+  const bool wide = pkv_wide_group(dtype, num_heads, num_kv_heads);
   const int64_t groups = static_cast<int64_t>(num_seqs > 0 ? num_seqs : 0) * num_kv_heads *
-                         ((num_heads / num_kv_heads + kMaxMfmaGroup - 1) / kMaxMfmaGroup);
+                         (wide ? 1 : (num_heads / num_kv_heads + kMaxMfmaGroup - 1) / kMaxMfmaGroup);
+  const int64_t round = wide ? kMfmaRoundWorkgroups / 2 : kMfmaRoundWorkgroups;
   for (int32_t p = kMaxPartTokens; p > kMinPartTokens; p /= 2) {
     const int64_t parts = (static_cast<int64_t>(max_context_len) + p - 1) / p;
-    if (groups * (parts < 1 ? 1 : parts) >= kMfmaRoundWorkgroups) return p;
+    if (groups * (parts < 1 ? 1 : parts) >= round) return p;
   }
   return kMinPartTokens;
 }

@@ -1,8 +1,13 @@
 // MFMA kernels for gfx950 (CDNA4, wave64): attention of query-head groups that
 // share one KV head, where the work is a real dense contraction.
 //
-//   decode_group_mfma_kernel   -- decode with grouped-query heads (G = Hq/Hkv in
-//                                 2..16 query heads read the same K/V tiles)
+//   decode_group_mfma_kernel   -- decode with grouped-query heads (G = Hq/Hkv
+//                                 query heads read the same K/V tiles; groups
+//                                 past 64 heads in 16-row slice workgroups)
+//   decode_wide_group_kernel   -- the same for 17..64 heads per KV head: one
+//                                 workgroup for all slices, K/V staged in LDS
+//   decode_shared_mfma_kernel  -- a fork group's shared prefix blocks read once
+//                                 for all its members (the members are rows)
 //   prefill_chunk_mfma_kernel  -- causal attention of a prefill chunk: every
 //                                 (query token, head) row of a KV group against
 //                                 its sequence's paged context
@@ -1061,6 +1066,360 @@ __global__ __launch_bounds__(kPrefillThreads, 4) void prefill_chunk_mfma_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode for wide query-head groups: 17..64 query heads per KV head (down to
+// one KV head for all of them).  The group kernel above gives each 16-row
+// slice of such a group a workgroup of its own, so every K/V tile crosses
+// from L2 into a CU once per slice.  Here one workgroup per (unit, KV head)
+// stages the unit's K/V once in LDS -- the prefill kernel's ring of 32-key
+// stages, filled by direct global->LDS copies kStages-1 stages ahead -- and
+// wave w computes slice w (query heads kvh*G + 16w ..) over every stage with
+// the prefill kernel's softmax (the row maximum raised only past a 2^8
+// margin, the bf16 probability pair).  Keys past the context are copied from
+// key 0 of their pair and masked.  With the cache write, token ctx-1's rows
+// are copied from the step's rows when the new slot is token ctx-1's, and
+// stored into the pool by the workgroup; any other slot gives NaN rows.
+// Each wave writes its rows, or their partials and one step on its slice's
+// ticket (the group kernel's ticket layout), merging the slice if it is last.
+// Partitions start at multiples of 1024 tokens (wide groups take no shared
+// prefix), so every 32-key stage lies in whole blocks.
+// ---------------------------------------------------------------------------
+constexpr int kWideWaves = 4;
+constexpr int kWideThreads = 64 * kWideWaves;
+
+// Direct global->LDS copy of 16 bytes per lane from a per-lane 64-bit address
+// (the vector-address form of the instruction), under the same rules as
+// copy16_to_lds_at.
+__device__ __forceinline__ void copy16_to_lds_va(const char* p, const void* lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(p), "{m0}"(lds_addr(lds)) : "memory");
+}
+
+template <int D, int BS>
+__global__ __launch_bounds__(kWideThreads, 2) void decode_wide_group_kernel(pkv_decode_args a) {
+  constexpr int KC = D / 32;
+  constexpr int DC = D / 16;
+  constexpr int RB = D * 2;
+  constexpr int kStages = 4;                       // LDS ring depth (32-key stages)
+  constexpr int kTileBytes = kBlock * RB;          // 16 keys' K (or V) rows
+  constexpr int kTileKiB = kTileBytes / 1024;
+  constexpr int kStageBytes = 4 * kTileBytes;      // K0 K1 V0 V1
+  constexpr int kCopies = kStageBytes / (16 * kWideThreads);   // 16-byte copies per thread per stage
+  static_assert(kStageBytes % (16 * kWideThreads) == 0 && (kCopies == 2 || kCopies == 4), "wide decode shape");
+  constexpr int64_t kHeadTile = static_cast<int64_t>(BS) * RB;
+  constexpr int kBPP = 2 * kBlock / BS;            // blocks per 32-key stage
+  static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
+  static_assert(RB * 8 >= 1024, "a 1 KiB copy covers rows of one 8-token block");
+  __shared__ __align__(16) char ring[kStages][kStageBytes];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;
+  const int g = lane >> 4;
+
+  const int32_t Hq = a.num_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
+  const int32_t nsl = (G + 15) / 16;               // 2..4 slices
+  const bool active = wave < nsl;                  // this wave has a slice
+  const int32_t R = active ? min(16, G - 16 * wave) : 0;
+  const uint32_t bid = blockIdx.x;
+  const int32_t u = static_cast<int32_t>(bid / static_cast<uint32_t>(Hkv));
+  const int32_t kvh = static_cast<int32_t>(bid - static_cast<uint32_t>(u) * Hkv);
+  const int32_t* plan = a.plan;
+  if (!plan_matches(plan, a)) {
+    // a plan built for other sizes: every row is NaN
+    if (u < a.num_seqs)
+      for (int idx = threadIdx.x; idx < G * D; idx += kWideThreads)
+        a.out[(static_cast<int64_t>(u) * Hq + kvh * G) * D + idx] = __builtin_nanf("");
+    return;
+  }
+  if (u >= plan[0]) return;
+  const int32_t* units = pkvd::plan_units(plan);
+  const int32_t s = units[2 * u];
+  const int32_t p = units[2 * u + 1];
+  const int32_t ctx = a.context_lens[s];
+  const int64_t grow0 = static_cast<int64_t>(s) * Hq + kvh * G;   // the group's first output row
+  if (p < 0) {
+    // no attention work: an empty context gives 0, an invalid one NaN
+    for (int idx = threadIdx.x; idx < G * D; idx += kWideThreads)
+      a.out[grow0 * D + idx] = ctx == 0 ? 0.f : __builtin_nanf("");
+    return;
+  }
+  const int32_t part = a.part_tokens;
+  const int32_t np_s = (ctx + part - 1) / part;
+  const int32_t k_begin = p * part;
+  const int32_t k_end = min(ctx, k_begin + part);
+  const int32_t npairs = (k_end - k_begin + 2 * kBlock - 1) / (2 * kBlock);
+  const int32_t blk0 = k_begin / BS;               // the unit's first block
+  const int32_t nblk = (ctx + BS - 1) / BS;
+  const bool direct = np_s == 1;
+  const int32_t* __restrict__ table = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq;
+  const int64_t block_bytes = static_cast<int64_t>(Hkv) * kHeadTile;
+  const char* __restrict__ kc = reinterpret_cast<const char*>(a.k_cache) + kvh * kHeadTile;
+  const char* __restrict__ vc = reinterpret_cast<const char*>(a.v_cache) + kvh * kHeadTile;
+  bool bad = false;
+
+  // The step's new token: the unit that holds token ctx-1 checks its slot.
+  const int64_t new_slot = (a.new_slots && k_end == ctx) ? a.new_slots[s] : -1;
+  int32_t new_blk = 0;
+  bool use_new = false;
+  if (new_slot >= 0) {
+    new_blk = load_block_id(table, __builtin_amdgcn_readfirstlane((ctx - 1) / BS));
+    use_new = static_cast<uint32_t>(new_blk) < static_cast<uint32_t>(a.num_blocks) &&
+              new_slot == static_cast<int64_t>(new_blk) * BS + (ctx - 1) % BS;
+    if (!use_new) bad = true;      // not token ctx-1's slot: NaN rows, nothing stored
+  }
+  const char* nk = use_new ? reinterpret_cast<const char*>(a.new_k) + (static_cast<int64_t>(s) * Hkv + kvh) * RB
+                           : nullptr;
+  const char* nv = use_new ? reinterpret_cast<const char*>(a.new_v) + (static_cast<int64_t>(s) * Hkv + kvh) * RB
+                           : nullptr;
+
+  // Copy i of wave w fills KiB kWideWaves*i + w of a stage (0: K0, 1: K1, 2:
+  // V0, 3: V1 by tile), rows in lane order, LDS row r's 16-byte slot k from
+  // the swizzled source slot; the copy's rows lie in one pool block (block
+  // cp_blk[i] of the stage).
+  uint32_t cp_off[kCopies], cp_slot[kCopies];
+  int32_t cp_key[kCopies], cp_blk[kCopies];
+#pragma unroll
+  for (int i = 0; i < kCopies; ++i) {
+    const int kib = kWideWaves * i + wave;
+    const int t = kib / kTileKiB;
+    const int off = (kib % kTileKiB) * 1024 + 16 * lane;
+    const int r = off / RB, k = (off % RB) / 16;
+    const int slot = t < 2 ? (k ^ kswz<D>(r)) : (k ^ vswz<D>(r));
+    const int key = kBlock * (t & 1) + r;               // key of the row within the stage
+    cp_key[i] = key;
+    cp_blk[i] = ((kib % kTileKiB) * 1024 / RB + kBlock * (t & 1)) / BS;
+    cp_off[i] = static_cast<uint32_t>((key % BS) * RB + 16 * slot);
+    cp_slot[i] = static_cast<uint32_t>(16 * slot);
+  }
+  auto issue = [&](int32_t pp, int32_t (&ids)[kBPP], char* stage) {
+#pragma unroll
+    for (int q = 0; q < kBPP; ++q)
+      if (static_cast<uint32_t>(ids[q]) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; ids[q] = 0; }
+    const int32_t key0 = k_begin + pp * 2 * kBlock;
+    const bool tail = key0 + 2 * kBlock > ctx;         // some keys of the stage lie past the context
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) {
+      const int kib = kWideWaves * i + wave;
+      const int t = kib / kTileKiB;
+      const int32_t j = blk0 + kBPP * pp + cp_blk[i];
+      const int32_t id = j < nblk ? ids[cp_blk[i]] : ids[0];
+      const int32_t key = key0 + cp_key[i];
+      const char* src = (t < 2 ? kc : vc) + id * block_bytes + cp_off[i];
+      if (tail && key >= ctx) src = (t < 2 ? kc : vc) + id * block_bytes + cp_slot[i];
+      if (use_new && key == ctx - 1) src = (t < 2 ? nk : nv) + cp_slot[i];
+      copy16_to_lds_va(src, stage + kib * 1024);
+    }
+  };
+  // the stage's block ids (entries past the context's last block are not
+  // read: the last one is read again instead)
+  auto pair_ids = [&](int32_t pp, int32_t (&ids)[kBPP]) {
+#pragma unroll
+    for (int q = 0; q < kBPP; ++q)
+      ids[q] = load_block_id(table, __builtin_amdgcn_readfirstlane(min(blk0 + kBPP * pp + q, nblk - 1)));
+  };
+#pragma unroll
+  for (int pp = 0; pp < kStages - 1; ++pp)
+    if (pp < npairs) {
+      int32_t ids[kBPP];
+      pair_ids(pp, ids);
+      issue(pp, ids, ring[pp]);
+    }
+  int32_t nids[kBPP];
+#pragma unroll
+  for (int q = 0; q < kBPP; ++q) nids[q] = 0;
+  if (kStages - 1 < npairs) pair_ids(kStages - 1, nids);
+
+  // the wave's query rows as the B operand (rows >= R: q = 0, never written);
+  // the scale's sign goes into q so that the exponent factor c2 is positive
+  const float sl = a.scale_log2;
+  const int q_mode = sl > 0.f ? 0 : sl < 0.f ? 1 : 2;
+  const float c2 = q_mode == 2 ? 1.f : fabsf(sl);
+  const float rescale_raw = kRescaleLog2 / c2;
+  bf16x8 qb[KC];
+  {
+    // (a wave without a slice reads the group's first row and zeroes it)
+    const char* qrow = reinterpret_cast<const char*>(a.q) + ((grow0 + (n < R ? 16 * wave + n : 0)) * D) * 2;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      u32x4 w = *reinterpret_cast<const u32x4*>(qrow + 64 * c + 16 * g);
+      if (n >= R || q_mode == 2) w = u32x4{0, 0, 0, 0};
+      if (q_mode == 1) w ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};   // -q, exactly
+      qb[c] = as_bf16x8(w);
+    }
+  }
+
+  f32x4 o[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = kNegBig, thr = kNegBig, lsum = 0.f;
+  const int k_row = n * RB;
+  const int k_sw = kswz<D>(n);
+  const int tr_row = 4 * g + (n >> 2);
+  const int tr_sw = vswz<D>(tr_row);
+  const int tr_k0 = (n & 3) >> 1;
+  const uint32_t ring0 = lds_addr(ring[0]);
+  uint32_t k_addr[KC], tr_addr[DC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) {
+    k_addr[c] = ring0 + k_row + 16 * ((4 * c + g) ^ k_sw);
+    asm volatile("" : "+v"(k_addr[c]));
+  }
+#pragma unroll
+  for (int c = 0; c < DC; ++c) {
+    tr_addr[c] = ring0 + 2 * kTileBytes + tr_row * RB + 8 * (n & 1) + 16 * ((2 * c + tr_k0) ^ tr_sw);
+    asm volatile("" : "+v"(tr_addr[c]));
+  }
+
+  // One 32-key stage: S^T = K Q^T, the online softmax, O^T += V^T P^T.
+  auto pair = [&](int32_t pp, const char* stage) {
+    const int32_t key0 = k_begin + pp * 2 * kBlock;
+    const uint32_t stage_off = static_cast<uint32_t>(stage - ring[0]);
+    __builtin_amdgcn_s_setprio(1);
+    f32x4 acc[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      bf16x8 ka[KC];
+#pragma unroll
+      for (int c = 0; c < KC; ++c) ka[c] = as_bf16x8(lds_read16_at(k_addr[c] + stage_off + b * kTileBytes));
+      acc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < KC; ++c) acc[b] = mfma(ka[c], qb[c], acc[b]);
+    }
+    float sc[8];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) sc[4 * b + jj] = acc[b][jj];
+    if (key0 + 2 * kBlock > ctx) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          if (key0 + b * kBlock + 4 * g + jj >= ctx) sc[4 * b + jj] = -INFINITY;
+    }
+    __builtin_amdgcn_s_setprio(0);
+    const float lane_mx = __builtin_elementwise_maximum(
+        __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[0], sc[1]),
+                                      __builtin_elementwise_maximum(sc[2], sc[3])),
+        __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[4], sc[5]),
+                                      __builtin_elementwise_maximum(sc[6], sc[7])));
+    if (__builtin_amdgcn_ballot_w64(lane_mx > thr)) {
+      const float mx = max_over_rows(lane_mx);
+      const bool up = mx > thr;
+      const float mnew = up ? mx * c2 : m;
+      const float alpha = fast_exp2(m - mnew);
+      m = mnew;
+      thr = up ? mx + rescale_raw : thr;
+      lsum *= alpha;
+#pragma unroll
+      for (int c = 0; c < DC; ++c) o[c] *= alpha;
+    }
+    bf16x8 va[DC];
+#pragma unroll
+    for (int c = 0; c < DC; ++c)
+      va[c] = join(lds_read_tr_at(tr_addr[c] + stage_off), lds_read_tr_at(tr_addr[c] + stage_off + kTileBytes));
+    u32x4 phw, plw;
+    float ps[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const f32x2 pr = {fast_exp2(fmaf(sc[2 * k], c2, -m)), fast_exp2(fmaf(sc[2 * k + 1], c2, -m))};
+      ps[k] = pr[0] + pr[1];
+      const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+      const f32x2 lo = {pr[0] - __uint_as_float(h << 16), pr[1] - __uint_as_float(h & 0xFFFF0000u)};
+      phw[k] = h;
+      plw[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2));
+    }
+    lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    const bf16x8 ph = as_bf16x8(phw), pl = as_bf16x8(plw);
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      f32x4 t = mfma(va[c], ph, o[c]);
+      o[c] = mfma(va[c], pl, t);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  for (int32_t p0 = 0; p0 < npairs; p0 += kStages) {
+#pragma unroll
+    for (int st = 0; st < kStages; ++st) {
+      const int32_t pp = p0 + st;
+      if (pp >= npairs) break;
+      // this stage's copies have landed once at most the later issued stages'
+      // copies are outstanding (copies complete in issue order)
+      const int32_t ahead = min(kStages - 2, npairs - 1 - pp);
+      if (ahead >= 2) {
+        if constexpr (kCopies == 4) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      } else if (ahead == 1) {
+        if constexpr (kCopies == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const int32_t pn = pp + kStages - 1;
+      int32_t ids[kBPP];
+#pragma unroll
+      for (int q = 0; q < kBPP; ++q) ids[q] = nids[q];
+      if (pn + 1 < npairs) pair_ids(pn + 1, nids);
+      __builtin_amdgcn_s_barrier();
+      if (active) pair(pp, ring[st]);
+      if (pn < npairs) issue(pn, ids, ring[(st + kStages - 1) % kStages]);
+    }
+  }
+
+  // a bad block id anywhere in the unit's range, or a wrong new slot, poisons its rows
+  const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0;
+  if (use_new && threadIdx.x < 2 * RB / 16) {
+    // the new token's K and V rows into the pool (16 bytes per thread)
+    const int half = threadIdx.x / (RB / 16), piece = threadIdx.x % (RB / 16);
+    const char* src = (half == 0 ? nk : nv) + 16 * piece;
+    char* dst = const_cast<char*>(half == 0 ? kc : vc) + new_blk * block_bytes + ((ctx - 1) % BS) * RB + 16 * piece;
+    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+  }
+  if (!active) return;
+  float L = lsum;
+  L += __shfl_xor(L, 16);
+  L += __shfl_xor(L, 32);
+  const int64_t row0 = grow0 + 16 * wave;          // the wave's first row
+  if (direct) {
+    if (n < R) {
+      const float inv = any_bad ? __builtin_nanf("") : 1.f / L;
+      float* orow = a.out + (row0 + n) * D;
+#pragma unroll
+      for (int c = 0; c < DC; ++c) *reinterpret_cast<f32x4*>(orow + 16 * c + 4 * g) = o[c] * inv;
+    }
+    return;
+  }
+  // a split context: the wave's partial (the running maximum it scaled by,
+  // the sum, the accumulator), then one step on its slice's ticket
+  if (n < R) {
+    const int64_t pidx = (row0 + n) * a.num_partitions + p;
+#pragma unroll
+    for (int c = 0; c < DC; ++c)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        pkvd::store_coherent(a.part_acc + pidx * D + 16 * c + 4 * g + jj,
+                             any_bad ? __builtin_nanf("") : o[c][jj]);
+    if (g == 0) {
+      pkvd::store_coherent(a.part_ml + 2 * pidx, m);
+      pkvd::store_coherent(a.part_ml + 2 * pidx + 1, any_bad ? __builtin_nanf("") : L);
+    }
+  }
+  pkvd::wait_vmem();
+  int last = 0;
+  if (lane == 0) last = pkvd::ticket_arrive(a.merge_tickets + row0, a.merge_epoch, np_s) ? 1 : 0;
+  last = __shfl(last, 0);
+  if (!last) return;
+  for (int idx = lane; idx < R * D; idx += 64) {
+    const int64_t prow = (row0 + idx / D) * a.num_partitions;
+    const int d = idx - (idx / D) * D;
+    a.out[(row0 + idx / D) * D + d] =
+        pkvd::merge_partials_coherent(a.part_ml + 2 * prow, a.part_acc + prow * D + d, np_s, D);
+  }
+}
+
 }  // namespace
 
 namespace {
@@ -1084,6 +1443,12 @@ struct GroupDecode {
   }
 };
 template <int D, int BS>
+struct WideGroupDecode {
+  static void launch(dim3 grid, hipStream_t st, const pkv_decode_args& a) {
+    hipLaunchKernelGGL((decode_wide_group_kernel<D, BS>), grid, dim3(kWideThreads), 0, st, a);
+  }
+};
+template <int D, int BS>
 struct SharedUnits {
   static void launch(dim3 grid, hipStream_t st, const pkv_decode_args& a) {
     hipLaunchKernelGGL((decode_shared_mfma_kernel<D, BS>), grid, dim3(256), 0, st, a);
@@ -1093,6 +1458,13 @@ struct SharedUnits {
 
 int pkv_launch_decode_group(const pkv_decode_args& a, void* stream) {
   const int64_t np = (a.max_context_len + a.part_tokens - 1) / a.part_tokens;
+  if (pkv_wide_group(a.dtype, a.num_heads, a.num_kv_heads)) {
+    // one workgroup per (unit, KV head) for all the group's slices
+    const int64_t units = static_cast<int64_t>(a.num_seqs) * (np < 1 ? 1 : np) * a.num_kv_heads;
+    launch_d_bs<WideGroupDecode>(a.head_dim, a.block_size, dim3(static_cast<uint32_t>(units)),
+                                 static_cast<hipStream_t>(stream), a);
+    return hipGetLastError();
+  }
   const int32_t slices = (a.num_heads / a.num_kv_heads + kMaxMfmaGroup - 1) / kMaxMfmaGroup;
   const int64_t units = static_cast<int64_t>(a.num_seqs) * (np < 1 ? 1 : np) * a.num_kv_heads;
   const int64_t grid = slices == 1 ? units : (units + 7) / 8 * 8 * slices;

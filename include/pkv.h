@@ -189,9 +189,11 @@ pkv_status pkv_attention_decode(float* out, const void* q, const void* k_cache,
  * pkv_attention_decode builds it in its workspace on every call.
  *
  * plan: device buffer of at least pkv_decode_plan_bytes(num_seqs,
- * max_context_len) bytes, 16-byte aligned.  num_heads, num_kv_heads,
- * block_size and dtype choose the partition size (they must be those of the
- * decode calls).  A sequence with a context length of 0 or an invalid one (see
+ * max_context_len) bytes, 16-byte aligned.  num_seqs, num_heads,
+ * num_kv_heads, block_size, max_context_len and dtype choose the partition
+ * size (1024 tokens for one query head per KV head; for groups 4096, 2048 or
+ * 1024, the largest that still gives the GPU a full round of workgroups);
+ * they must be those of the decode calls.  A sequence with a context length of 0 or an invalid one (see
  * pkv_attention_decode) gets a unit that writes its 0 or NaN rows.  A plan
  * records num_seqs, max_context_len, max_blocks_per_seq, block_size and the
  * partition size; a decode call with other values writes NaN rows instead of

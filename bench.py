@@ -216,13 +216,14 @@ def secondary(args):
 
     gqa:  256 seqs, 64 query / 8 KV heads, d 128, bf16, ctx U[128, 4096], pool 1.2x
           shuffled, 8 layer pools: decode (MFMA group kernel) per layer; then 2
-          float32 layers and 2 layers of one KV head for the 64 query heads.
+          float32 layers, and 2 layers of one KV head for the 64 query heads (the
+          wide group kernel) and for 16 of them.
     fork: 32 groups x 8 samples of a 1000-token prompt, tails U[1, 512], 40 heads x
           128 (13B-shaped), 40 layer pools like the headline's: the copy-on-write
           copies, then decode over the shared blocks (the shared-prefix plan built
           once per step, for all 40 layers); then plain and shared-prefix decode
           over 2 float32 layers of the same tables.
-    long: 16 seqs at ctx 32768 (split over 64 partitions each) + 4 prefill chunks of
+    long: 16 seqs at ctx 32768 (8 partitions of 4096 each) + 4 prefill chunks of
           512 causal queries ending 8192-token contexts, 32 / 8 heads, 4 layer pools.
     """
     import torch

@@ -1,0 +1,96 @@
+"""A seeded sweep of decode shapes against the oracle.
+
+Sixty draws of batch size (1..12), context lengths (up to past two 1024-token
+partitions, some of 1 token), head layout (MHA; groups of 2..16 query heads per
+KV head; 17..64, the wide group kernel for bf16; beyond 64, 16-row slice
+workgroups), head_dim 64 or 128, bf16 or float32 pools and block size 8, 16 or
+32.  Each draw goes through pkv_attention_decode (plan built in the call),
+through pkv_decode_plan + pkv_attention_decode_planned (the same bits), and
+through pkv_attention_decode_append after one more token per sequence (pools
+bit-exact, outputs against the oracle's write-then-decode).  Bar: max abs error
+2e-3 (bf16 K/V) and 1e-5 (float32 K/V) on every output row.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import paged_kv_cache_171_amd as PK  # noqa: E402
+import pkv_workloads as W  # noqa: E402
+from oracle import pkv_oracle as O  # noqa: E402
+from pkv_gpu_driver import GpuReplay, pool_to_host, rows_to_device  # noqa: E402
+
+TOL = {"f32": 1e-5, "bf16": 2e-3}
+HEADS = [(4, 4), (8, 8), (8, 2), (16, 2), (12, 4), (16, 1), (24, 1), (32, 2), (48, 1), (64, 1), (80, 1)]
+
+
+def _draw(i):
+    rng = np.random.default_rng(9000 + i)
+    hq, hkv = HEADS[int(rng.integers(len(HEADS)))]
+    S = int(rng.integers(1, 13))
+    max_ctx = int(rng.choice([1, 40, 300, 1100, 2500]))
+    d = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["bf16", "f32"]))
+    bs = int(rng.choice([8, 16, 32]))
+    return dict(seed=9100 + i, S=S, max_ctx=max_ctx, hq=hq, hkv=hkv, d=d, dtype=dtype, bs=bs)
+
+
+def _rows(rng, shape, dtype):
+    x = rng.standard_normal(shape, dtype=np.float32)
+    return x if dtype == "f32" else W.f32_to_bf16_bits(x)
+
+
+@pytest.mark.parametrize("i", range(60))
+def test_decode_shape_sweep(i):
+    c = _draw(i)
+    print(f"case: sweep {i} {c}", flush=True)
+    w = W.random_small(c["seed"], c["S"], c["max_ctx"], c["hq"], c["hkv"], c["d"], c["dtype"], block_size=c["bs"])
+    g = GpuReplay(w)
+    r = O.replay(w.ops, w.k_rows, w.v_rows, w.num_blocks, w.num_kv_heads, w.head_dim, w.initial_free_order,
+                 block_size=w.block_size)
+    seqs = list(w.decode_seqs)
+    dt = PK.PKV_BF16 if w.dtype == "bf16" else PK.PKV_F32
+
+    # plain and planned decode over the cached contexts
+    out, tables, lens = g.decode()
+    ref = O.decode_attention(w.q, r.k_pool, r.v_pool, [r.alloc.block_table(s) for s in seqs],
+                             [r.alloc.num_tokens(s) for s in seqs], w.scale, block_size=w.block_size)
+    err = float(np.abs(out - ref).max())
+    assert err <= TOL[w.dtype], err
+    td, ld = torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
+    mcl = int(lens.max())
+    plan = PK.plan_for(ld, w.num_heads, w.num_kv_heads, tables.shape[1], mcl, dt, block_size=w.block_size)
+    out2 = torch.full((len(seqs), w.num_heads, w.head_dim), -5.0, dtype=torch.float32, device="cuda")
+    PK.pkv_attention_decode(out2, rows_to_device(w.q, "cuda"), g.k_pool, g.v_pool, td, ld, mcl, float(w.scale),
+                            plan=plan)
+    torch.cuda.synchronize()
+    assert np.array_equal(out2.cpu().numpy(), out)
+
+    # one more token per sequence, written by the decode launch
+    slots = np.zeros(len(seqs), dtype=np.int64)
+    for k, s in enumerate(seqs):
+        sl, pairs = g.alloc.seq_append_slots(s, 1)
+        osl, opairs = r.alloc.append_slots(s, 1)
+        assert list(sl) == osl and [tuple(p) for p in pairs] == opairs and not pairs
+        slots[k] = sl[0]
+    rng = np.random.default_rng(c["seed"] + 1)
+    kn = _rows(rng, (len(seqs), w.num_kv_heads, w.head_dim), w.dtype)
+    vn = _rows(rng, (len(seqs), w.num_kv_heads, w.head_dim), w.dtype)
+    O.write_cache(r.k_pool, r.v_pool, kn, vn, slots, w.block_size)
+    tables, lens = g.tables(seqs)
+    td, ld = torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
+    mcl = int(lens.max())
+    out3 = torch.full((len(seqs), w.num_heads, w.head_dim), -5.0, dtype=torch.float32, device="cuda")
+    PK.pkv_attention_decode_append(out3, rows_to_device(w.q, "cuda"), rows_to_device(kn, "cuda"),
+                                   rows_to_device(vn, "cuda"), torch.from_numpy(slots).cuda(), g.k_pool, g.v_pool,
+                                   td, ld, mcl, float(w.scale))
+    torch.cuda.synchronize()
+    assert np.array_equal(pool_to_host(g.k_pool), r.k_pool) and np.array_equal(pool_to_host(g.v_pool), r.v_pool)
+    ref3 = O.decode_attention(w.q, r.k_pool, r.v_pool, [r.alloc.block_table(s) for s in seqs],
+                              [r.alloc.num_tokens(s) for s in seqs], w.scale, block_size=w.block_size)
+    err3 = float(np.abs(out3.cpu().numpy() - ref3).max())
+    assert err3 <= TOL[w.dtype], err3

@@ -7,8 +7,10 @@ workgroups), head_dim 64 or 128, bf16 or float32 pools and block size 8, 16 or
 32.  Each draw goes through pkv_attention_decode (plan built in the call),
 through pkv_decode_plan + pkv_attention_decode_planned (the same bits), and
 through pkv_attention_decode_append after one more token per sequence (pools
-bit-exact, outputs against the oracle's write-then-decode).  Bar: max abs error
-2e-3 (bf16 K/V) and 1e-5 (float32 K/V) on every output row.
+bit-exact, outputs against the oracle's write-then-decode).  Thirty draws of
+causal chunked prefill likewise (1..4 chunks, each of 1 query up to its whole
+context).  Bar: max abs error 2e-3 (bf16 K/V) and 1e-5 (float32 K/V) on every
+output row.
 """
 import numpy as np
 import pytest
@@ -94,3 +96,36 @@ def test_decode_shape_sweep(i):
                               [r.alloc.num_tokens(s) for s in seqs], w.scale, block_size=w.block_size)
     err3 = float(np.abs(out3.cpu().numpy() - ref3).max())
     assert err3 <= TOL[w.dtype], err3
+
+
+def _prefill_draw(i):
+    rng = np.random.default_rng(9500 + i)
+    hq, hkv = HEADS[int(rng.integers(len(HEADS)))]
+    S = int(rng.integers(1, 5))
+    ctxs = [int(x) for x in rng.integers(1, int(rng.choice([40, 400, 1500])) + 1, size=S)]
+    nqs = [int(rng.integers(1, c + 1)) if rng.random() < 0.8 else c for c in ctxs]
+    d = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["bf16", "f32"]))
+    bs = int(rng.choice([8, 16, 32]))
+    return dict(seed=9600 + i, ctxs=ctxs, nqs=nqs, hq=hq, hkv=hkv, d=d, dtype=dtype, bs=bs)
+
+
+@pytest.mark.parametrize("i", range(30))
+def test_prefill_shape_sweep(i):
+    """Causal chunked prefill over seeded random shapes: chunks of 1 query up to
+    the whole context, every head layout above, both dtypes and block sizes;
+    every query row against the oracle."""
+    c = _prefill_draw(i)
+    print(f"case: prefill sweep {i} {c}", flush=True)
+    w = W.random_prefill(c["seed"], c["ctxs"], c["nqs"], c["hq"], c["hkv"], c["d"], block_size=c["bs"],
+                         dtype=c["dtype"])
+    g = GpuReplay(w)
+    r = O.replay(w.ops, w.k_rows, w.v_rows, w.num_blocks, w.num_kv_heads, w.head_dim, w.initial_free_order,
+                 block_size=w.block_size)
+    out, _, _ = g.prefill()
+    tables = [r.alloc.block_table(s) for s in w.chunk_seqs]
+    lens = [r.alloc.num_tokens(s) for s in w.chunk_seqs]
+    ref = O.prefill_chunk_attention(w.chunk_q, w.chunk_query_start_loc, r.k_pool, r.v_pool, tables, lens, w.scale,
+                                    block_size=w.block_size)
+    err = float(np.abs(out - ref).max())
+    assert err <= TOL[w.dtype], err

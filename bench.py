@@ -211,6 +211,39 @@ def _timed(fn, reps, stream):
     return sum(a.elapsed_time(b) for a, b in ev) / reps * 1e3
 
 
+def tile_read_ceiling(pools, tables_h, lens_h, num_kv_heads, stream, reps) -> dict:
+    """The read-only probe of a batch's own access pattern (tile_read_kernel:
+    whole 4 KiB K and V tiles through the tables, one workgroup per (16-block
+    chunk, KV head), full chunks first, nothing computed), timed over the same
+    bf16 layer pools as the decode it bounds."""
+    import torch
+    P = 16
+    dev = pools[0][0].device
+    nblk = -(-lens_h // P)
+    work = [(s_, c) for s_ in range(len(lens_h)) for c in range(-(-int(nblk[s_]) // 16))]
+    work.sort(key=lambda sc: -min(16, int(nblk[sc[0]]) - 16 * sc[1]))
+    work_d = torch.tensor(work, dtype=torch.int32, device=dev)
+    td, ld = torch.from_numpy(np.ascontiguousarray(tables_h)).to(dev), torch.from_numpy(lens_h).to(dev)
+    sink = torch.zeros(len(work) * num_kv_heads * 4, dtype=torch.int32, device=dev)
+    lib = ctypes.CDLL(os.path.join(ROOT, "paged_kv_cache_171_amd", "libpkv_probes.so"))
+    lib.pkvprobe_tile_read.restype = ctypes.c_int
+    sp = stream.cuda_stream
+
+    def all_layers():
+        for kp, vp in pools:
+            rc = lib.pkvprobe_tile_read(ctypes.c_void_p(kp.data_ptr()), ctypes.c_void_p(vp.data_ptr()),
+                                        ctypes.c_void_p(td.data_ptr()), int(tables_h.shape[1]),
+                                        ctypes.c_void_p(ld.data_ptr()), P, ctypes.c_void_p(work_d.data_ptr()),
+                                        len(work), num_kv_heads, 4096, ctypes.c_void_p(sink.data_ptr()),
+                                        ctypes.c_void_p(sp))
+            if rc != 0:
+                raise RuntimeError(f"tile_read launch failed: {rc}")
+    us = _median_us(all_layers, stream, reps) / len(pools)
+    kv = int(lens_h.sum()) * 2 * num_kv_heads * 128 * 2
+    return {"us_per_layer": round(us, 2), "gbps": round(kv / us / 1e3, 1),
+            "hbm_peak_frac": round(kv / us / 1e3 / HBM_PEAK_GBPS, 4)}
+
+
 def secondary(args):
     """Kernel measurements on the other batches (one JSON line each; not the headline).
 
@@ -283,6 +316,11 @@ def secondary(args):
            "decode_hbm_peak_frac": round(kv_logical / dec_us / 1e3 / HBM_PEAK_GBPS, 4),
            "decode_tokens_per_s_per_layer": round(len(seqs) / dec_us * 1e6, 1),
            "kernel": "decode_group_mfma_kernel" if 2 <= Hq // Hkv <= 16 else "decode_valu_kernel"}
+    if name in ("gqa", "long"):
+        # the same tables read with nothing computed: the ceiling of this access pattern
+        tr = tile_read_ceiling(pools, tables_h, lens_h, Hkv, stream, reps)
+        res.update({"tile_read_us_per_layer": tr["us_per_layer"], "tile_read_gbps": tr["gbps"],
+                    "decode_frac_of_tile_read": round(tr["us_per_layer"] / dec_us, 4)})
     if name == "gqa":
         # the same batch over float32 pools (2 layers of the same tables): the
         # fp32 matrix-core group kernel, against HBM peak like the bf16 line

@@ -64,7 +64,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;                      // waves of a group-decode workgroup
+constexpr int kGroupThreads = 64 * kWaves;
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -199,7 +200,7 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
     if (!plan_matches(plan, a)) {
       // a plan built for other sizes: every row is NaN
       if (u < a.num_seqs)
-        for (int idx = threadIdx.x; idx < slice_rows * D; idx += 256)
+        for (int idx = threadIdx.x; idx < slice_rows * D; idx += kGroupThreads)
           a.out[(static_cast<int64_t>(u) * Hq + hb) * D + idx] = __builtin_nanf("");
       return;
     }
@@ -210,7 +211,7 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
     ctx = a.context_lens[s];
     if (p < 0) {
       // no attention work: an empty context gives 0, an invalid one NaN
-      for (int idx = threadIdx.x; idx < slice_rows * D; idx += 256)
+      for (int idx = threadIdx.x; idx < slice_rows * D; idx += kGroupThreads)
         a.out[(static_cast<int64_t>(s) * Hq + hb) * D + idx] = ctx == 0 ? 0.f : __builtin_nanf("");
       return;
     }
@@ -482,8 +483,11 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
   if (g == 0) { sm_ml[wave][n][0] = m; sm_ml[wave][n][1] = lsum; }
   if (lane == 0) sm_bad[wave] = bad ? 1 : 0;
   __syncthreads();
-  const bool any_bad = (sm_bad[0] | sm_bad[1] | sm_bad[2] | sm_bad[3]) != 0;
-  for (int idx = threadIdx.x; idx < nrows * D; idx += 256) {
+  int bad_any = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) bad_any |= sm_bad[w];
+  const bool any_bad = bad_any != 0;
+  for (int idx = threadIdx.x; idx < nrows * D; idx += kGroupThreads) {
     const int r = idx / D, d = idx - (idx / D) * D;
     float M = sm_ml[0][r][0];
 #pragma unroll
@@ -511,7 +515,7 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
   if (!shared_unit) {
     const int64_t row0 = static_cast<int64_t>(s0) * Hq + hb;
     if (!pkvd::arrive_last(a.merge_tickets + row0, a.merge_epoch, nslots, &sm_last)) return;
-    for (int idx = threadIdx.x; idx < nrows * D; idx += 256) {
+    for (int idx = threadIdx.x; idx < nrows * D; idx += kGroupThreads) {
       const int64_t prow = (row0 + idx / D) * a.num_partitions;
       const int d = idx - (idx / D) * D;
       a.out[(row0 + idx / D) * D + d] =
@@ -538,7 +542,7 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
     if (!sm_member_last[mi]) continue;
     const int32_t slots = sm_member_slots[mi];
     const int64_t row0 = static_cast<int64_t>(s0 + mi) * Hq + kvh * G;
-    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+    for (int idx = threadIdx.x; idx < G * D; idx += kGroupThreads) {
       const int64_t prow = (row0 + idx / D) * a.num_partitions;
       const int d = idx - (idx / D) * D;
       a.out[(row0 + idx / D) * D + d] =
@@ -550,7 +554,7 @@ __device__ __forceinline__ void decode_group_mfma_body(const pkv_decode_args& a,
 // 8-token blocks take two block ids per tile: three workgroups per CU, so the
 // body keeps its registers
 template <int D, int BS>
-__global__ __launch_bounds__(256, BS == 8 ? 3 : 4) void decode_group_mfma_kernel(pkv_decode_args a) {
+__global__ __launch_bounds__(kGroupThreads, BS == 8 ? 3 : 4) void decode_group_mfma_kernel(pkv_decode_args a) {
   decode_group_mfma_body<D, BS>(a, blockIdx.x, false);
 }
 
@@ -558,7 +562,7 @@ __global__ __launch_bounds__(256, BS == 8 ? 3 : 4) void decode_group_mfma_kernel
 // possible unit and KV head; those past the shared plan's count exit).  The
 // sequences' own units follow in a launch of the plain decode kernels.
 template <int D, int BS>
-__global__ __launch_bounds__(256, BS == 8 ? 3 : 4) void decode_shared_mfma_kernel(pkv_decode_args a) {
+__global__ __launch_bounds__(kGroupThreads, BS == 8 ? 3 : 4) void decode_shared_mfma_kernel(pkv_decode_args a) {
   decode_group_mfma_body<D, BS>(a, blockIdx.x, true);
 }
 
@@ -1439,7 +1443,7 @@ void launch_d_bs(int head_dim, int block_size, dim3 grid, hipStream_t st, Args..
 template <int D, int BS>
 struct GroupDecode {
   static void launch(dim3 grid, hipStream_t st, const pkv_decode_args& a) {
-    hipLaunchKernelGGL((decode_group_mfma_kernel<D, BS>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_group_mfma_kernel<D, BS>), grid, dim3(kGroupThreads), 0, st, a);
   }
 };
 template <int D, int BS>
@@ -1451,7 +1455,7 @@ struct WideGroupDecode {
 template <int D, int BS>
 struct SharedUnits {
   static void launch(dim3 grid, hipStream_t st, const pkv_decode_args& a) {
-    hipLaunchKernelGGL((decode_shared_mfma_kernel<D, BS>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_shared_mfma_kernel<D, BS>), grid, dim3(kGroupThreads), 0, st, a);
   }
 };
 }  // namespace

@@ -15,10 +15,10 @@
 // 0..ctx-n+i.  The rows of KV head kvh are (query i, head kvh*G + r), r < G,
 // numbered token-major; each wave takes one 16-row tile and walks its keys 16
 // at a time (a 16-key tile: two 8-token blocks, one 16-token block or half a
-// 32-token block); a workgroup's four waves take neighbouring tiles of one
-// (sequence, KV head), so they read the same K/V rows close together in time
-// and the repeats hit the CU's cache.  The waves share nothing else: no LDS,
-// no barrier.
+// 32-token block); a workgroup's four waves take neighbouring row tiles of one
+// (sequence, KV head) and share each key tile: its K and V rows are copied
+// once into LDS (a ring of three stages, direct global->LDS copies two tiles
+// ahead, one barrier per tile) and every wave reads its operands from there.
 //
 // Matrix-core layout of v_mfma_f32_16x16x4_f32: lane l, n = l % 16,
 // g = l / 16, supplies A[n][g] and B[g][n] and receives D[4g + j][n] in
@@ -56,16 +56,43 @@ __device__ __forceinline__ float max4(f32x4 v) {
                                        __builtin_elementwise_maximum(v[2], v[3]));
 }
 
+// LDS copy helpers (direct global->LDS, 16 bytes per lane at lds + 16 lane).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
+}
+__device__ __forceinline__ void copy16_to_lds_va(const void* p, const void* lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(p), "{m0}"(lds_addr(lds)) : "memory");
+}
+__device__ __forceinline__ f32x4 lds_read16(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(static_cast<uintptr_t>(addr));
+}
+template <int N> __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+
+// The workgroup's four waves (64 rows) share each 16-key tile: its K and V
+// rows are copied once into a ring of kStages LDS stages, kStages-1 tiles
+// ahead of the tile being computed, and every wave reads its operands from
+// there.  K rows keep their 16-byte slots XOR-swizzled by row (slot ^ row), so
+// that the sixteen rows a K read touches fall in different banks.  Three
+// stages of 16 KiB (head_dim 128) leave room for three workgroups per CU.
 template <int D, int BS>
-// Two waves per SIMD: each wave holds the K and V rows of two tiles (the next
-// one loads while this one is on the matrix cores), 256 registers.
-__global__ __launch_bounds__(64 * kF32Waves, 2) void prefill_chunk_f32_kernel(pkv_prefill_args a) {
+__global__ __launch_bounds__(64 * kF32Waves, 3) void prefill_chunk_f32_kernel(pkv_prefill_args a) {
   constexpr int KQ = D / 16;   // 16-byte pieces of a K or q row per lane
   constexpr int DT = D / 16;   // 16-dim output tiles; a lane holds DT dims of each of its V rows
   constexpr int DV = DT / 4;   // 16-byte pieces of those
+  constexpr int RB = D * 4;    // bytes per K or V row
+  constexpr int kSlots = RB / 16;
+  constexpr int kTileBytes = 16 * RB;
+  constexpr int kTileKiB = kTileBytes / 1024;
+  constexpr int kStageBytes = 2 * kTileBytes;          // K then V
+  constexpr int kThreads = 64 * kF32Waves;
+  constexpr int kCopies = kStageBytes / (16 * kThreads);
+  constexpr int kStages = 3;
   static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
   static_assert(D == 64 || D == 128, "head_dim");
+  static_assert(kStageBytes % (16 * kThreads) == 0 && (kCopies == 2 || kCopies == 4), "stage shape");
+  static_assert(RB * 8 >= 1024, "a 1 KiB copy covers rows of one 8-token block");
   constexpr int64_t kHeadTile = static_cast<int64_t>(BS) * D;   // floats of one (block, head) tile
+  __shared__ __align__(16) char ring[kStages][kStageBytes];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -81,23 +108,28 @@ __global__ __launch_bounds__(64 * kF32Waves, 2) void prefill_chunk_f32_kernel(pk
   if (q0 < 0 || q1 < q0 || q1 > a.num_query_tokens || q1 - q0 > a.max_query_len) return;   // nowhere safe to write
   const int32_t nq = q1 - q0;
   const int32_t rows = nq * G;
-  const int32_t rbase = rt * kPrefillF32RowsPerWg + wave * 16;
-  if (rbase >= rows) return;                   // no barrier below: an idle wave just leaves
-  const int32_t r_end = min(rows, rbase + 16);
+  const int32_t r0 = rt * kPrefillF32RowsPerWg;
+  if (r0 >= rows) return;
+  const int32_t r_end_wg = min(rows, r0 + kPrefillF32RowsPerWg);
+  const int32_t rbase = r0 + wave * 16;
+  const int32_t r_end = min(r_end_wg, rbase + 16);       // <= rbase: a wave without rows
   const int32_t ctx = a.context_lens[s];
   if (ctx < nq || !len_ok(ctx, a.max_context_len, a.max_blocks_per_seq, BS)) {
-    for (int idx = lane; idx < (r_end - rbase) * D; idx += 64) {
-      const int32_t r = rbase + idx / D, d = idx % D;
+    for (int idx = threadIdx.x; idx < (r_end_wg - r0) * D; idx += kThreads) {
+      const int32_t r = r0 + idx / D, d = idx % D;
       a.out[((static_cast<int64_t>(q0) + r / G) * Hq + kvh * G + r % G) * D + d] = __builtin_nanf("");
     }
     return;
   }
   const int32_t first_pos = ctx - nq;          // position of query 0
   const int32_t* __restrict__ table = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq;
-  const int64_t block_stride = static_cast<int64_t>(Hkv) * kHeadTile;
-  const float* __restrict__ kc = static_cast<const float*>(a.k_cache) + kvh * kHeadTile;
-  const float* __restrict__ vc = static_cast<const float*>(a.v_cache) + kvh * kHeadTile;
+  const int64_t block_bytes = static_cast<int64_t>(Hkv) * kHeadTile * 4;
+  const char* __restrict__ kc = reinterpret_cast<const char*>(a.k_cache) + kvh * kHeadTile * 4;
+  const char* __restrict__ vc = reinterpret_cast<const char*>(a.v_cache) + kvh * kHeadTile * 4;
   const int32_t nblk = (ctx + BS - 1) / BS;
+  const int32_t wg_lim = first_pos + (r_end_wg - 1) / G + 1;    // keys the workgroup needs
+  const int32_t ntiles = (wg_lim + 15) / 16;
+  bool bad = false;
 
   // this lane's row; rows past the tile's end get key limit 0 and q = 0 (their
   // results are never written)
@@ -105,8 +137,51 @@ __global__ __launch_bounds__(64 * kF32Waves, 2) void prefill_chunk_f32_kernel(pk
   const bool valid = r < r_end;
   const int32_t i = valid ? r / G : 0;
   const int32_t lim = valid ? first_pos + i + 1 : 0;
-  const int32_t tile_lim = first_pos + (r_end - 1) / G + 1;    // keys any row of the tile needs
-  const int32_t nomask_lim = first_pos + rbase / G + 1;          // keys every row of the tile sees
+  const int32_t tile_lim = r_end > rbase ? first_pos + (r_end - 1) / G + 1 : 0;   // keys any row of the wave needs
+  const int32_t nomask_lim = first_pos + rbase / G + 1;                            // keys every row of the wave sees
+
+  // Copy i of wave w fills KiB kF32Waves*i + w of a stage: tile half t (0: K,
+  // 1: V), rows in lane order; K's LDS slot k holds the row's slot k ^ (row
+  // mod slots).  A 1 KiB copy reads rows of one pool block.
+  uint32_t cp_off[kCopies], cp_off0[kCopies];
+  int32_t cp_key[kCopies];
+#pragma unroll
+  for (int c = 0; c < kCopies; ++c) {
+    const int kib = kF32Waves * c + wave;
+    const int t = kib / kTileKiB;
+    const int off = (kib % kTileKiB) * 1024 + 16 * lane;
+    const int row = off / RB, k = (off % RB) / 16;
+    const int slot = t == 0 ? (k ^ (row % kSlots)) : k;
+    cp_key[c] = row;
+    cp_off[c] = static_cast<uint32_t>((row % BS) * RB + 16 * slot);
+    cp_off0[c] = static_cast<uint32_t>(16 * slot);
+  }
+  // the tile's block ids: the block of its rows 0-7 and of rows 8-15 (the
+  // same unless blocks hold 8 tokens; the second clamped to the last block)
+  auto tile_ids = [&](int32_t tt, int32_t& ida, int32_t& idb) {
+    const int32_t j0 = (16 * tt) / BS;
+    ida = load_block_id(table, __builtin_amdgcn_readfirstlane(j0));
+    idb = ida;
+    if constexpr (BS == 8) idb = load_block_id(table, __builtin_amdgcn_readfirstlane(min(j0 + 1, nblk - 1)));
+  };
+  auto issue = [&](int32_t tt, int32_t ida, int32_t idb, char* stage) {
+    if (static_cast<uint32_t>(ida) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; ida = 0; }
+    if (static_cast<uint32_t>(idb) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; idb = 0; }
+    const int32_t key0 = 16 * tt;
+#pragma unroll
+    for (int c = 0; c < kCopies; ++c) {
+      const int kib = kF32Waves * c + wave;
+      const int t = kib / kTileKiB;
+      const int32_t id = (BS == 8 && cp_key[c] >= 8) ? idb : ida;
+      const char* base = (t == 0 ? kc : vc) + id * block_bytes;
+      // keys past the context read row 0 of the tile (a cached token: finite
+      // data, masked to probability 0)
+      // (a 32-token block holds two tiles: the tile's rows start at key0 mod BS)
+      const char* src = key0 + cp_key[c] < ctx ? base + (key0 % BS) * RB + cp_off[c]
+                                               : (t == 0 ? kc : vc) + ida * block_bytes + (key0 % BS) * RB + cp_off0[c];
+      copy16_to_lds_va(src, stage + kib * 1024);
+    }
+  };
 
   f32x4 qv[KQ];
   {
@@ -126,50 +201,37 @@ __global__ __launch_bounds__(64 * kF32Waves, 2) void prefill_chunk_f32_kernel(pk
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegBig, lsum = 0.f;
-  bool bad = false;
 
-  const int32_t ntiles = (tile_lim + 15) / 16;
-  // the tile's block ids (wave-uniform): its block, or with 8-token blocks its
-  // two (the second clamped to the context's last block: keys past the context
-  // are never read from it); a key past the context reads the tile's first key
-  // instead (a cached token: finite data, masked to probability 0)
-  auto load_tile = [&](int32_t t, f32x4 (&kv)[KQ], f32x4 (&vv)[4][DV]) {
-    const int32_t key0 = 16 * t;
-    const int32_t j0 = key0 / BS;
-    int32_t id_a = load_block_id(table, __builtin_amdgcn_readfirstlane(j0));
-    int32_t id_b = id_a;
-    if constexpr (BS == 8) id_b = load_block_id(table, __builtin_amdgcn_readfirstlane(min(j0 + 1, nblk - 1)));
-    if (static_cast<uint32_t>(id_a) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; id_a = 0; }
-    if (static_cast<uint32_t>(id_b) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; id_b = 0; }
-    auto row_ptr = [&](const float* base, int32_t off) {
-      const int32_t o2 = key0 + off < ctx ? off : 0;
-      const int32_t id = (BS == 8 && o2 >= 8) ? id_b : id_a;
-      return base + id * block_stride + ((key0 + o2) % BS) * D;
-    };
-    {
-      const float* krow = row_ptr(kc, n);
+  // LDS read addresses of stage 0 (the other stages at fixed offsets): K row n,
+  // logical slot 4m + g at its swizzled place; V rows 4g + kk, dims DT n ..
+  const uint32_t ring0 = lds_addr(ring[0]);
+  uint32_t k_addr[KQ];
 #pragma unroll
-      for (int m = 0; m < KQ; ++m) kv[m] = *reinterpret_cast<const f32x4*>(krow + 16 * m + 4 * g);
-    }
+  for (int m = 0; m < KQ; ++m) {
+    k_addr[m] = ring0 + n * RB + 16 * ((4 * m + g) ^ (n % kSlots));
+    asm volatile("" : "+v"(k_addr[m]));
+  }
+  uint32_t v_addr = ring0 + kTileBytes + 4 * g * RB + DT * n * 4;
+  asm volatile("" : "+v"(v_addr));
+
+  auto compute_tile = [&](int32_t tt, uint32_t stage_off) {
+    const int32_t key0 = 16 * tt;
+    f32x4 kv[KQ];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const float* vrow = row_ptr(vc, 4 * g + kk) + DT * n;
-#pragma unroll
-      for (int c = 0; c < DV; ++c) vv[kk][c] = *reinterpret_cast<const f32x4*>(vrow + 4 * c);
-    }
-  };
-  // S^T = K Q^T (two accumulator chains), the online softmax over the tile's
-  // 16 keys (base 2, maximum taken every tile), then O^T += V^T P^T
-  auto compute_tile = [&](int32_t t, const f32x4 (&kv)[KQ], const f32x4 (&vv)[4][DV]) {
-    const int32_t key0 = 16 * t;
+    for (int m = 0; m < KQ; ++m) kv[m] = lds_read16(k_addr[m] + stage_off);
     f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
 #pragma unroll
     for (int m = 0; m < KQ; ++m)
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        if (m & 1) acc1 = mfma4(kv[m][tt], qv[m][tt], acc1);
-        else acc0 = mfma4(kv[m][tt], qv[m][tt], acc0);
+      for (int t4 = 0; t4 < 4; ++t4) {
+        if (m & 1) acc1 = mfma4(kv[m][t4], qv[m][t4], acc1);
+        else acc0 = mfma4(kv[m][t4], qv[m][t4], acc0);
       }
+    f32x4 vv[4][DV];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int c = 0; c < DV; ++c) vv[kk][c] = lds_read16(v_addr + stage_off + kk * RB + 16 * c);
     f32x4 sc = acc0 + acc1;
     if (key0 + 16 > nomask_lim) {
 #pragma unroll
@@ -192,23 +254,48 @@ __global__ __launch_bounds__(64 * kF32Waves, 2) void prefill_chunk_f32_kernel(pk
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) o[dt] = mfma4(vv[kk][dt / 4][dt % 4], p[kk], o[dt]);
   };
-  // two register sets, the loop unrolled by two so that each stays in place
-  f32x4 kA[KQ], vA[4][DV], kB[KQ], vB[4][DV];
-  if (ntiles > 0) load_tile(0, kA, vA);
-  for (int32_t t = 0; t < ntiles; t += 2) {
-    if (t + 1 < ntiles) load_tile(t + 1, kB, vB);
-    compute_tile(t, kA, vA);
-    if (t + 1 >= ntiles) break;
-    if (t + 2 < ntiles) load_tile(t + 2, kA, vA);
-    compute_tile(t + 1, kB, vB);
+
+  // prologue: the first kStages-1 tiles' copies; the ids of the next one
+#pragma unroll
+  for (int tt = 0; tt < kStages - 1; ++tt)
+    if (tt < ntiles) {
+      int32_t ida, idb;
+      tile_ids(tt, ida, idb);
+      issue(tt, ida, idb, ring[tt]);
+    }
+  int32_t nida = 0, nidb = 0;
+  if (kStages - 1 < ntiles) tile_ids(kStages - 1, nida, nidb);
+
+  for (int32_t t0 = 0; t0 < ntiles; t0 += kStages) {
+#pragma unroll
+    for (int st = 0; st < kStages; ++st) {
+      const int32_t tt = t0 + st;
+      if (tt >= ntiles) break;
+      // this tile's copies have landed once at most the later issued tiles'
+      // copies are outstanding (copies complete in issue order)
+      const int32_t ahead = min(kStages - 2, ntiles - 1 - tt);
+      if (ahead >= 2) wait_vm<2 * kCopies>();
+      else if (ahead == 1) wait_vm<kCopies>();
+      else wait_vm<0>();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const int32_t tn = tt + kStages - 1;
+      const int32_t ida = nida, idb = nidb;
+      if (tn + 1 < ntiles) tile_ids(tn + 1, nida, nidb);
+      __builtin_amdgcn_s_barrier();
+      if (16 * tt < tile_lim) compute_tile(tt, static_cast<uint32_t>(st * kStageBytes));
+      // every wave passed the barrier after it finished the tile before this
+      // one, so that tile's stage takes tile tt + kStages - 1
+      if (tn < ntiles) issue(tn, ida, idb, ring[(st + kStages - 1) % kStages]);
+    }
   }
 
   float L = lsum;
   L += __shfl_xor(L, 16);
   L += __shfl_xor(L, 32);
+  // a bad block id in the workgroup's range poisons its rows
+  const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0;
   if (!valid) return;
-  // a bad block id in the tile's range poisons its rows
-  const float inv = bad ? __builtin_nanf("") : 1.f / L;
+  const float inv = any_bad ? __builtin_nanf("") : 1.f / L;
   float* orow = a.out + ((static_cast<int64_t>(q0) + i) * Hq + kvh * G + r % G) * D;
   // lane (n, g) holds dims DT (4g + j) + dt of row n in o[dt][j]
 #pragma unroll

@@ -353,6 +353,22 @@ def secondary(args):
         mq_us = _timed(decode_mqa_all, reps, stream) / len(mpools)
         res.update({"decode_64x1_us_per_layer": round(mq_us, 2),
                     "decode_64x1_kv_gbps": round(kv_logical / Hkv / mq_us / 1e3, 1)})
+        # the same over float32 pools of the one head: the float32 wide group kernel
+        mpools32 = [(torch.randn(NB, 1, P, D, generator=gen, device=dev),
+                     torch.randn(NB, 1, P, D, generator=gen, device=dev)) for _ in range(2)]
+        mplan32 = PK.plan_for(ld, Hq, 1, MB, mcl, PK.PKV_F32)
+
+        def decode_mqa_f32_all():
+            for kp, vp in mpools32:
+                PK.pkv_attention_decode(out32, q32, kp, vp, td, ld, mcl, scale, workspace=ws, plan=mplan32)
+        decode_mqa_f32_all()
+        torch.cuda.synchronize()
+        mq32_us = _timed(decode_mqa_f32_all, reps, stream) / len(mpools32)
+        res.update({"decode_64x1_f32_us_per_layer": round(mq32_us, 2),
+                    "decode_64x1_f32_kv_gbps": round(kv_logical * 2 / Hkv / mq32_us / 1e3, 1),
+                    "decode_64x1_f32_mfma_tflops": round(4 * Hq * D * int(lens_h.sum()) / mq32_us / 1e6, 1),
+                    "decode_64x1_f32_partition_tokens": int(mplan32[16:20].view(torch.int32).item())})
+        del mpools32
         # 16 query heads over the one KV head: 256 (sequence, KV head) pairs,
         # so the library cuts contexts into 1024-token partitions to fill the CUs
         q16 = q[:, :16].contiguous()

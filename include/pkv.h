@@ -152,7 +152,7 @@ pkv_status pkv_swap_blocks(void* dst_k_cache, void* dst_v_cache, int32_t dst_num
  * more heads per KV head run on the matrix cores: bf16 pools with the
  * probabilities carried as a bf16 pair (~16 significant bits), every K/V row
  * read once per group of up to 64 heads (once per 16 heads beyond); float32
- * pools with exact fp32 products, every K/V row read once per 16 heads.  One
+ * pools with exact fp32 products, likewise.  One
  * query head per KV head runs on the vector ALUs, one head per workgroup.
  * max_context_len must be >= every context length (it sizes the context
  * split); a row whose length exceeds it or
@@ -160,7 +160,9 @@ pkv_status pkv_swap_blocks(void* dst_k_cache, void* dst_v_cache, int32_t dst_num
  * [0, num_blocks), is written as NaN.
  * workspace: device scratch of at least pkv_attention_workspace_bytes(...) bytes
  * for the decode plan, the partial results of split contexts (the context is
- * cut into partitions of 1024 tokens, 4096 for the matrix-core group kernels)
+ * cut into partitions of 1024 tokens; 4096, 2048 or 1024 for the
+ * matrix-core group kernels, shorter for batches of fewer (sequence, KV head)
+ * pairs)
  * and one 8-byte merge ticket per (sequence, head): the last partition of a
  * row to finish merges the row's partials in the same launch.  No
  * initialisation is needed (a ticket counts only under the launch's own

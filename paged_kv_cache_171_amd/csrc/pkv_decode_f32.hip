@@ -382,6 +382,305 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void decode_shared_f32_kernel(
   decode_group_f32_body<D, BS>(a, blockIdx.x, true);
 }
 
+// ---------------------------------------------------------------------------
+// Decode for wide query-head groups over float32 pools: 17..64 query heads per
+// KV head.  One workgroup per (unit, KV head) for all the group's 16-row
+// slices: each 16-key tile's K and V rows are copied once into LDS (a ring of
+// three stages, direct global->LDS copies two tiles ahead, one barrier per
+// tile; K rows' 16-byte slots XOR-swizzled by row) and wave w computes slice
+// w from there, so each K/V byte crosses from L2 into the CU once instead of
+// once per slice workgroup.  Scores, softmax (maximum taken every tile) and
+// the merge are those of the group kernel above; the cache write copies token
+// ctx-1's rows into the stage from the step's rows and the workgroup stores
+// them into the pool.  Partitions start at multiples of 1024 tokens (wide
+// groups take no shared prefix).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t lds_addr_f32(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
+}
+__device__ __forceinline__ void copy16_to_lds_f32(const void* p, const void* lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(p), "{m0}"(lds_addr_f32(lds)) : "memory");
+}
+__device__ __forceinline__ f32x4 lds_read16_f32(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(static_cast<uintptr_t>(addr));
+}
+template <int N> __device__ __forceinline__ void wait_vm_f32() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+
+template <int D, int BS>
+__global__ __launch_bounds__(64 * kGroupWaves, 3) void decode_wide_group_f32_kernel(pkv_decode_args a) {
+  constexpr int KQ = D / 16;   // 16-byte pieces of a K or q row per lane
+  constexpr int DT = D / 16;   // 16-dim output tiles; a lane holds DT dims of each of its V rows
+  constexpr int DV = DT / 4;   // 16-byte pieces of those
+  constexpr int RB = D * 4;    // bytes per K or V row
+  constexpr int kSlots = RB / 16;
+  constexpr int kTileBytes = 16 * RB;
+  constexpr int kTileKiB = kTileBytes / 1024;
+  constexpr int kStageBytes = 2 * kTileBytes;          // K then V
+  constexpr int kThreads = 64 * kGroupWaves;
+  constexpr int kCopies = kStageBytes / (16 * kThreads);
+  constexpr int kStages = 3;
+  static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
+  static_assert(D == 64 || D == 128, "head_dim");
+  static_assert(kStageBytes % (16 * kThreads) == 0 && (kCopies == 2 || kCopies == 4), "stage shape");
+  constexpr int64_t kHeadTile = static_cast<int64_t>(BS) * D;   // floats of one (block, head) tile
+  __shared__ __align__(16) char ring[kStages][kStageBytes];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;
+  const int g = lane >> 4;
+
+  const int32_t Hq = a.num_heads, Hkv = a.num_kv_heads, G = Hq / Hkv;
+  const int32_t nsl = (G + 15) / 16;               // 2..4 slices
+  const bool active = wave < nsl;
+  const int32_t R = active ? min(16, G - 16 * wave) : 0;
+  const uint32_t bid = blockIdx.x;
+  const int32_t u = static_cast<int32_t>(bid / static_cast<uint32_t>(Hkv));
+  const int32_t kvh = static_cast<int32_t>(bid - static_cast<uint32_t>(u) * Hkv);
+  const int32_t* plan = a.plan;
+  if (!plan_matches(plan, a)) {
+    // a plan built for other sizes: every row is NaN
+    if (u < a.num_seqs)
+      for (int idx = threadIdx.x; idx < G * D; idx += kThreads)
+        a.out[(static_cast<int64_t>(u) * Hq + kvh * G) * D + idx] = __builtin_nanf("");
+    return;
+  }
+  if (u >= plan[0]) return;
+  const int32_t* units = pkvd::plan_units(plan);
+  const int32_t s = units[2 * u];
+  const int32_t p = units[2 * u + 1];
+  const int32_t ctx = a.context_lens[s];
+  const int64_t grow0 = static_cast<int64_t>(s) * Hq + kvh * G;   // the group's first output row
+  if (p < 0) {
+    // no attention work: an empty context gives 0, an invalid one NaN
+    for (int idx = threadIdx.x; idx < G * D; idx += kThreads)
+      a.out[grow0 * D + idx] = ctx == 0 ? 0.f : __builtin_nanf("");
+    return;
+  }
+  const int32_t part = a.part_tokens;
+  const int32_t np_s = (ctx + part - 1) / part;
+  const int32_t k_begin = p * part;
+  const int32_t k_end = min(ctx, k_begin + part);
+  const int32_t ntiles = (k_end - k_begin + 15) / 16;
+  const bool direct = np_s == 1;
+  const int32_t nblk = (ctx + BS - 1) / BS;
+  const int32_t* __restrict__ table = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq;
+  const int64_t block_bytes = static_cast<int64_t>(Hkv) * kHeadTile * 4;
+  const char* __restrict__ kc = reinterpret_cast<const char*>(a.k_cache) + kvh * kHeadTile * 4;
+  const char* __restrict__ vc = reinterpret_cast<const char*>(a.v_cache) + kvh * kHeadTile * 4;
+  bool bad = false;
+
+  // The step's new token: the unit that holds token ctx-1 checks its slot.
+  const int64_t new_slot = (a.new_slots && k_end == ctx) ? a.new_slots[s] : -1;
+  int32_t new_blk = 0;
+  bool use_new = false;
+  if (new_slot >= 0) {
+    new_blk = load_block_id(table, __builtin_amdgcn_readfirstlane((ctx - 1) / BS));
+    use_new = static_cast<uint32_t>(new_blk) < static_cast<uint32_t>(a.num_blocks) &&
+              new_slot == static_cast<int64_t>(new_blk) * BS + (ctx - 1) % BS;
+    if (!use_new) bad = true;      // not token ctx-1's slot: NaN rows, nothing stored
+  }
+  const char* nk = use_new ? reinterpret_cast<const char*>(a.new_k) + (static_cast<int64_t>(s) * Hkv + kvh) * RB
+                           : nullptr;
+  const char* nv = use_new ? reinterpret_cast<const char*>(a.new_v) + (static_cast<int64_t>(s) * Hkv + kvh) * RB
+                           : nullptr;
+
+  // Copy c of wave w fills KiB kGroupWaves*c + w of a stage: tile half t (0: K,
+  // 1: V), rows in lane order; K's LDS slot k holds the row's slot k ^ (row
+  // mod slots).  A 1 KiB copy reads rows of one pool block.
+  uint32_t cp_off[kCopies], cp_slot[kCopies];
+  int32_t cp_key[kCopies];
+#pragma unroll
+  for (int c = 0; c < kCopies; ++c) {
+    const int kib = kGroupWaves * c + wave;
+    const int t = kib / kTileKiB;
+    const int off = (kib % kTileKiB) * 1024 + 16 * lane;
+    const int row = off / RB, k = (off % RB) / 16;
+    const int slot = t == 0 ? (k ^ (row % kSlots)) : k;
+    cp_key[c] = row;
+    cp_off[c] = static_cast<uint32_t>((row % BS) * RB + 16 * slot);
+    cp_slot[c] = static_cast<uint32_t>(16 * slot);
+  }
+  // the tile's block ids: the block of its rows 0-7 and of rows 8-15 (the
+  // same unless blocks hold 8 tokens; the second clamped to the last block)
+  auto tile_ids = [&](int32_t tt, int32_t& ida, int32_t& idb) {
+    const int32_t j0 = (k_begin + 16 * tt) / BS;
+    ida = load_block_id(table, __builtin_amdgcn_readfirstlane(j0));
+    idb = ida;
+    if constexpr (BS == 8) idb = load_block_id(table, __builtin_amdgcn_readfirstlane(min(j0 + 1, nblk - 1)));
+  };
+  auto issue = [&](int32_t tt, int32_t ida, int32_t idb, char* stage) {
+    if (static_cast<uint32_t>(ida) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; ida = 0; }
+    if (static_cast<uint32_t>(idb) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; idb = 0; }
+    const int32_t key0 = k_begin + 16 * tt;
+#pragma unroll
+    for (int c = 0; c < kCopies; ++c) {
+      const int kib = kGroupWaves * c + wave;
+      const int t = kib / kTileKiB;
+      const int32_t key = key0 + cp_key[c];
+      const int32_t id = (BS == 8 && cp_key[c] >= 8) ? idb : ida;
+      // (a 32-token block holds two tiles: the tile's rows start at key0 mod BS);
+      // keys past the context read row 0 of the tile (finite data, masked)
+      const char* src = key < ctx ? (t == 0 ? kc : vc) + id * block_bytes + (key0 % BS) * RB + cp_off[c]
+                                  : (t == 0 ? kc : vc) + ida * block_bytes + (key0 % BS) * RB + cp_slot[c];
+      if (use_new && key == ctx - 1) src = (t == 0 ? nk : nv) + cp_slot[c];
+      copy16_to_lds_f32(src, stage + kib * 1024);
+    }
+  };
+
+#pragma unroll
+  for (int tt = 0; tt < kStages - 1; ++tt)
+    if (tt < ntiles) {
+      int32_t ida, idb;
+      tile_ids(tt, ida, idb);
+      issue(tt, ida, idb, ring[tt]);
+    }
+  int32_t nida = 0, nidb = 0;
+  if (kStages - 1 < ntiles) tile_ids(kStages - 1, nida, nidb);
+
+  // the wave's query rows as the B operand (rows >= R: q = 0, never written;
+  // a wave without a slice reads the group's first row and zeroes it)
+  f32x4 qv[KQ];
+  {
+    const float* qrow = static_cast<const float*>(a.q) + (grow0 + (n < R ? 16 * wave + n : 0)) * D;
+#pragma unroll
+    for (int m = 0; m < KQ; ++m) {
+      const f32x4 w = *reinterpret_cast<const f32x4*>(qrow + 16 * m + 4 * g);
+      qv[m] = n < R ? w : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  const float c2 = a.scale_log2;               // scale * log2(e), any sign
+  f32x4 o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegBig, lsum = 0.f;
+
+  const uint32_t ring0 = lds_addr_f32(ring[0]);
+  uint32_t k_addr[KQ];
+#pragma unroll
+  for (int m = 0; m < KQ; ++m) {
+    k_addr[m] = ring0 + n * RB + 16 * ((4 * m + g) ^ (n % kSlots));
+    asm volatile("" : "+v"(k_addr[m]));
+  }
+  uint32_t v_addr = ring0 + kTileBytes + 4 * g * RB + DT * n * 4;
+  asm volatile("" : "+v"(v_addr));
+
+  auto compute_tile = [&](int32_t tt, uint32_t stage_off) {
+    const int32_t key0 = k_begin + 16 * tt;
+    f32x4 kv[KQ];
+#pragma unroll
+    for (int m = 0; m < KQ; ++m) kv[m] = lds_read16_f32(k_addr[m] + stage_off);
+    f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+#pragma unroll
+    for (int m = 0; m < KQ; ++m)
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        if (m & 1) acc1 = mfma4(kv[m][t4], qv[m][t4], acc1);
+        else acc0 = mfma4(kv[m][t4], qv[m][t4], acc0);
+      }
+    f32x4 vv[4][DV];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int c = 0; c < DV; ++c) vv[kk][c] = lds_read16_f32(v_addr + stage_off + kk * RB + 16 * c);
+    f32x4 sc = (acc0 + acc1) * c2;               // S[row n][key key0 + 4g + j], base 2
+    if (key0 + 16 > ctx) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (key0 + 4 * g + j >= ctx) sc[j] = -INFINITY;
+    }
+    const float mx = max_over_rows(max4(sc));
+    const float mnew = __builtin_elementwise_maximum(m_run, mx);
+    const float alpha = fast_exp2(m_run - mnew);
+    m_run = mnew;
+    lsum *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    float pr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pr[j] = fast_exp2(sc[j] - m_run);
+    lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) o[dt] = mfma4(vv[kk][dt / 4][dt % 4], pr[kk], o[dt]);
+  };
+
+  for (int32_t t0 = 0; t0 < ntiles; t0 += kStages) {
+#pragma unroll
+    for (int st = 0; st < kStages; ++st) {
+      const int32_t tt = t0 + st;
+      if (tt >= ntiles) break;
+      // this tile's copies have landed once at most the next tile's copies are
+      // outstanding (copies complete in issue order)
+      if (tt + 1 < ntiles) wait_vm_f32<kCopies>();
+      else wait_vm_f32<0>();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const int32_t tn = tt + kStages - 1;
+      const int32_t ida = nida, idb = nidb;
+      if (tn + 1 < ntiles) tile_ids(tn + 1, nida, nidb);
+      __builtin_amdgcn_s_barrier();
+      if (active) compute_tile(tt, static_cast<uint32_t>(st * kStageBytes));
+      if (tn < ntiles) issue(tn, ida, idb, ring[(st + kStages - 1) % kStages]);
+    }
+  }
+
+  // a bad block id anywhere in the unit's range, or a wrong new slot, poisons its rows
+  const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0;
+  if (use_new && threadIdx.x < 2 * RB / 16) {
+    // the new token's K and V rows into the pool (16 bytes per thread)
+    const int half = threadIdx.x / (RB / 16), piece = threadIdx.x % (RB / 16);
+    const char* src = (half == 0 ? nk : nv) + 16 * piece;
+    char* dst = const_cast<char*>(half == 0 ? kc : vc) + new_blk * block_bytes + ((ctx - 1) % BS) * RB + 16 * piece;
+    *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(src);
+  }
+  if (!active) return;
+  float L = lsum;
+  L += __shfl_xor(L, 16);
+  L += __shfl_xor(L, 32);
+  const int64_t row0 = grow0 + 16 * wave;          // the wave's first row
+  // lane (n, g) holds dims DT (4g + j) + dt of row n in o[dt][j]
+  if (direct) {
+    if (n < R) {
+      const float inv = any_bad ? __builtin_nanf("") : 1.f / L;
+      float* orow = a.out + (row0 + n) * D;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int c = 0; c < DV; ++c) {
+          const f32x4 v = f32x4{o[4 * c][j], o[4 * c + 1][j], o[4 * c + 2][j], o[4 * c + 3][j]} * inv;
+          *reinterpret_cast<f32x4*>(orow + DT * (4 * g + j) + 4 * c) = v;
+        }
+    }
+    return;
+  }
+  // a split context: the wave's partial, then one step on its slice's ticket
+  if (n < R) {
+    const int64_t pidx = (row0 + n) * a.num_partitions + p;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        pkvd::store_coherent(a.part_acc + pidx * D + DT * (4 * g + j) + dt, any_bad ? __builtin_nanf("") : o[dt][j]);
+    if (g == 0) {
+      pkvd::store_coherent(a.part_ml + 2 * pidx, m_run);
+      pkvd::store_coherent(a.part_ml + 2 * pidx + 1, any_bad ? __builtin_nanf("") : L);
+    }
+  }
+  pkvd::wait_vmem();
+  int last = 0;
+  if (lane == 0) last = pkvd::ticket_arrive(a.merge_tickets + row0, a.merge_epoch, np_s) ? 1 : 0;
+  last = __shfl(last, 0);
+  if (!last) return;
+  for (int idx = lane; idx < R * D; idx += 64) {
+    const int64_t prow = (row0 + idx / D) * a.num_partitions;
+    const int d = idx - (idx / D) * D;
+    a.out[(row0 + idx / D) * D + d] =
+        pkvd::merge_partials_coherent(a.part_ml + 2 * prow, a.part_acc + prow * D + d, np_s, D);
+  }
+}
+
 template <int D>
 void launch_bs(int block_size, dim3 grid, hipStream_t st, const pkv_decode_args& a, bool shared) {
   if (shared) {
@@ -405,6 +704,22 @@ void launch_bs(int block_size, dim3 grid, hipStream_t st, const pkv_decode_args&
 
 int pkv_launch_decode_group_f32(const pkv_decode_args& a, void* stream) {
   const int64_t np = (a.max_context_len + a.part_tokens - 1) / a.part_tokens;
+  if (pkv_wide_group(a.dtype, a.num_heads, a.num_kv_heads)) {
+    // one workgroup per (unit, KV head) for all the group's slices
+    const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.num_seqs) * (np < 1 ? 1 : np) * a.num_kv_heads));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const dim3 block(64 * kGroupWaves);
+    if (a.head_dim == 128) {
+      if (a.block_size == 8) hipLaunchKernelGGL((decode_wide_group_f32_kernel<128, 8>), grid, block, 0, st, a);
+      else if (a.block_size == 32) hipLaunchKernelGGL((decode_wide_group_f32_kernel<128, 32>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((decode_wide_group_f32_kernel<128, 16>), grid, block, 0, st, a);
+    } else {
+      if (a.block_size == 8) hipLaunchKernelGGL((decode_wide_group_f32_kernel<64, 8>), grid, block, 0, st, a);
+      else if (a.block_size == 32) hipLaunchKernelGGL((decode_wide_group_f32_kernel<64, 32>), grid, block, 0, st, a);
+      else hipLaunchKernelGGL((decode_wide_group_f32_kernel<64, 16>), grid, block, 0, st, a);
+    }
+    return hipGetLastError();
+  }
   const int32_t slices = (a.num_heads / a.num_kv_heads + 15) / 16;
   const int64_t units = static_cast<int64_t>(a.num_seqs) * (np < 1 ? 1 : np) * a.num_kv_heads;
   const int64_t grid = slices == 1 ? units : (units + 7) / 8 * 8 * slices;

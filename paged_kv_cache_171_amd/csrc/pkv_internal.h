@@ -38,7 +38,8 @@ int pkv_launch_swap_blocks(void* k_dst, void* v_dst, int32_t dst_blocks, const v
 // tokens for the VALU kernel; for the MFMA group kernels (which read Hq/Hkv
 // heads per tile and gain more from long units than from balance) the largest
 // of 4096, 2048 and 1024 tokens that still gives a full round of workgroups --
-// four per CU on 256 CUs -- for the call's sizes, so that a batch of few
+// four per CU on 256 CUs (the wide kernels: as many as fit, two for bf16 and
+// three for float32) -- for the call's sizes, so that a batch of few
 // sequences or KV heads gets shorter units instead of idle CUs.
 constexpr int32_t kMinPartTokens = 1024;
 constexpr int32_t kMaxPartTokens = 4096;
@@ -53,12 +54,13 @@ inline bool pkv_uses_mfma(int dtype, int32_t num_heads, int32_t num_kv_heads, in
   (void)block_size;
   return (dtype == PKV_BF16 || dtype == PKV_F32) && group >= 2;
 }
-// Whether a bf16 group of 17..64 query heads per KV head runs on the wide
-// group kernel (one workgroup for all its 16-row slices, K/V staged once in
-// LDS; two workgroups per CU) instead of one workgroup per slice.
+// Whether a group of 17..64 query heads per KV head runs on a wide group
+// kernel (one workgroup for all its 16-row slices, K/V staged once in LDS;
+// two (bf16) or three (float32) workgroups per CU) instead of one workgroup
+// per slice.
 inline bool pkv_wide_group(int dtype, int32_t num_heads, int32_t num_kv_heads) {
   const int32_t group = num_heads / num_kv_heads;
-  return dtype == PKV_BF16 && group > kMaxMfmaGroup && group <= 4 * kMaxMfmaGroup;
+  return (dtype == PKV_BF16 || dtype == PKV_F32) && group > kMaxMfmaGroup && group <= 4 * kMaxMfmaGroup;
 }
 inline int32_t pkv_part_tokens(int dtype, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                int32_t block_size, int32_t max_context_len) {
@@ -68,7 +70,7 @@ inline int32_t pkv_part_tokens(int dtype, int32_t num_seqs, int32_t num_heads, i
   const bool wide = pkv_wide_group(dtype, num_heads, num_kv_heads);
   const int64_t groups = static_cast<int64_t>(num_seqs > 0 ? num_seqs : 0) * num_kv_heads *
                          (wide ? 1 : (num_heads / num_kv_heads + kMaxMfmaGroup - 1) / kMaxMfmaGroup);
-  const int64_t round = wide ? kMfmaRoundWorkgroups / 2 : kMfmaRoundWorkgroups;
+  const int64_t round = wide ? (dtype == PKV_F32 ? 3 : 2) * kMfmaRoundWorkgroups / 4 : kMfmaRoundWorkgroups;
   for (int32_t p = kMaxPartTokens; p > kMinPartTokens; p /= 2) {
     const int64_t parts = (static_cast<int64_t>(max_context_len) + p - 1) / p;
     if (groups * (parts < 1 ? 1 : parts) >= round) return p;

@@ -57,7 +57,8 @@ def _check(w, planned=False):
                                                     ("bf16", 8, 8, 128, 2500), ("bf16", 16, 2, 64, 1500),
                                                     ("bf16", 32, 8, 128, 900), ("bf16", 16, 2, 128, 9000),
                                                     ("bf16", 8, 4, 128, 77), ("bf16", 48, 1, 64, 2100),
-                                                    ("bf16", 64, 2, 128, 1300)])
+                                                    ("bf16", 64, 2, 128, 1300), ("f32", 48, 1, 64, 2100),
+                                                    ("f32", 32, 1, 128, 1300)])
 def test_decode_and_cache_ops(bs, dtype, hq, hkv, d, max_ctx):
     print(f"case: bs={bs} {dtype} {hq}/{hkv} d={d} ctx<={max_ctx}", flush=True)
     w = W.random_small(100 + bs, 9, max_ctx, hq, hkv, d, dtype, block_size=bs)

@@ -92,6 +92,8 @@ def _run(w, seed, no_new=(), wrong=(), planned=False):
     (13, 4, 900, 64, 2, 64, "f32", 8),       # fp32, two slices
     (14, 5, 3000, 64, 1, 128, "bf16", 8),    # wide group kernel (four slices in one workgroup), split contexts
     (15, 6, 700, 24, 1, 64, "bf16", 32),     # wide group kernel, 32-token blocks
+    (16, 5, 3000, 64, 1, 128, "f32", 16),    # float32 wide group kernel, split contexts
+    (17, 6, 700, 32, 1, 64, "f32", 8),       # float32 wide group kernel, 8-token blocks
 ])
 def test_decode_append_matches_write_then_decode(seed, S, max_ctx, hq, hkv, d, dtype, bs):
     print(f"case: decode_append seed={seed} {dtype} {hq}/{hkv} d={d} bs={bs}", flush=True)
@@ -103,7 +105,7 @@ def test_decode_append_matches_write_then_decode(seed, S, max_ctx, hq, hkv, d, d
 @pytest.mark.parametrize("bs", [8, 16, 32])
 def test_no_new_token_and_a_wrong_slot(bs):
     print(f"case: decode_append -1 and wrong slots bs={bs}", flush=True)
-    for hq, hkv, dtype in ((8, 8, "bf16"), (16, 2, "bf16"), (16, 2, "f32"), (32, 1, "bf16")):
+    for hq, hkv, dtype in ((8, 8, "bf16"), (16, 2, "bf16"), (16, 2, "f32"), (32, 1, "bf16"), (32, 1, "f32")):
         w = W.random_small(77, 8, 700, hq, hkv, 128, dtype, block_size=bs)
         _run(w, 9, no_new=(1, 4), wrong=(2, 6))
 

@@ -32,6 +32,7 @@ CASES = [
     (66, 3, 40000, 8, 2, 64, "bf16"),     # MFMA: up to 40 partitions
     (67, 4, 13000, 8, 2, 128, "f32"),     # fp32 MFMA: up to 13 partitions
     (68, 3, 9000, 32, 1, 128, "bf16"),    # wide group kernel: two 16-row slices, each merged on its own ticket
+    (69, 3, 9000, 48, 1, 64, "f32"),      # float32 wide group kernel: three slices
 ]
 
 
@@ -68,7 +69,7 @@ def test_random_workspace_bytes_and_reuse(seed, S, max_ctx, hq, hkv, d, dtype):
     assert np.array_equal(results[0], results[1]) and np.array_equal(results[0], results[2])
 
 
-@pytest.mark.parametrize("seed,S,max_ctx,hq,hkv,d,dtype", [CASES[0], CASES[2], CASES[6]])
+@pytest.mark.parametrize("seed,S,max_ctx,hq,hkv,d,dtype", [CASES[0], CASES[2], CASES[6], CASES[7]])
 def test_graph_replays_match_the_eager_call(seed, S, max_ctx, hq, hkv, d, dtype):
     print(f"case: merge in launch, graph replay seed={seed} {hq}/{hkv} {dtype}", flush=True)
     w, g, ref, x = _setup(seed, S, max_ctx, hq, hkv, d, dtype)

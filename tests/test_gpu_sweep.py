@@ -2,7 +2,7 @@
 
 Sixty draws of batch size (1..12), context lengths (up to past two 1024-token
 partitions, some of 1 token), head layout (MHA; groups of 2..16 query heads per
-KV head; 17..64, the wide group kernel for bf16; beyond 64, 16-row slice
+KV head; 17..64, the wide group kernels; beyond 64, 16-row slice
 workgroups), head_dim 64 or 128, bf16 or float32 pools and block size 8, 16 or
 32.  Each draw goes through pkv_attention_decode (plan built in the call),
 through pkv_decode_plan + pkv_attention_decode_planned (the same bits), and

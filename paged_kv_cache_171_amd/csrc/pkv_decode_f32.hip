@@ -404,6 +404,9 @@ __device__ __forceinline__ void copy16_to_lds_f32(const void* p, const void* lds
 __device__ __forceinline__ f32x4 lds_read16_f32(uint32_t addr) {
   return *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(static_cast<uintptr_t>(addr));
 }
+__device__ __forceinline__ void copy16_to_lds_at_f32(const char* base, uint32_t voff, const void* lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "{m0}"(lds_addr_f32(lds)) : "memory");
+}
 template <int N> __device__ __forceinline__ void wait_vm_f32() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
 
 template <int D, int BS>
@@ -513,6 +516,19 @@ __global__ __launch_bounds__(64 * kGroupWaves, 3) void decode_wide_group_f32_ker
     if (static_cast<uint32_t>(ida) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; ida = 0; }
     if (static_cast<uint32_t>(idb) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; idb = 0; }
     const int32_t key0 = k_begin + 16 * tt;
+    if (key0 + 16 < ctx) {
+      // a tile wholly before token ctx-1: each copy reads rows of one block
+      // (with 8-token blocks: both rows in one half of the tile)
+#pragma unroll
+      for (int c = 0; c < kCopies; ++c) {
+        const int kib = kGroupWaves * c + wave;
+        const int t = kib / kTileKiB;
+        const bool hi = BS == 8 && (kib % kTileKiB) * 1024 / RB >= 8;
+        const char* base = (t == 0 ? kc : vc) + static_cast<int64_t>(hi ? idb : ida) * block_bytes + (key0 % BS) * RB;
+        copy16_to_lds_at_f32(base, cp_off[c], stage + kib * 1024);
+      }
+      return;
+    }
 #pragma unroll
     for (int c = 0; c < kCopies; ++c) {
       const int kib = kGroupWaves * c + wave;
@@ -554,7 +570,7 @@ __global__ __launch_bounds__(64 * kGroupWaves, 3) void decode_wide_group_f32_ker
   f32x4 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegBig, lsum = 0.f;
+  float m_run = kNegBig, thr = kNegBig, lsum = 0.f;
 
   const uint32_t ring0 = lds_addr_f32(ring[0]);
   uint32_t k_addr[KQ];
@@ -563,7 +579,7 @@ __global__ __launch_bounds__(64 * kGroupWaves, 3) void decode_wide_group_f32_ker
     k_addr[m] = ring0 + n * RB + 16 * ((4 * m + g) ^ (n % kSlots));
     asm volatile("" : "+v"(k_addr[m]));
   }
-  uint32_t v_addr = ring0 + kTileBytes + 4 * g * RB + DT * n * 4;
+  uint32_t v_addr = ring0 + kTileBytes + 4 * g * RB + 16 * n;
   asm volatile("" : "+v"(v_addr));
 
   auto compute_tile = [&](int32_t tt, uint32_t stage_off) {
@@ -571,40 +587,51 @@ __global__ __launch_bounds__(64 * kGroupWaves, 3) void decode_wide_group_f32_ker
     f32x4 kv[KQ];
 #pragma unroll
     for (int m = 0; m < KQ; ++m) kv[m] = lds_read16_f32(k_addr[m] + stage_off);
-    f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+    f32x4 acc[4];
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) acc[t4] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < KQ; ++m)
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
-        if (m & 1) acc1 = mfma4(kv[m][t4], qv[m][t4], acc1);
-        else acc0 = mfma4(kv[m][t4], qv[m][t4], acc0);
-      }
+      for (int t4 = 0; t4 < 4; ++t4) acc[t4] = mfma4(kv[m][t4], qv[m][t4], acc[t4]);
+    __builtin_amdgcn_s_setprio(0);
+    const f32x4 acc0 = acc[0] + acc[2], acc1 = acc[1] + acc[3];
     f32x4 vv[4][DV];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int c = 0; c < DV; ++c) vv[kk][c] = lds_read16_f32(v_addr + stage_off + kk * RB + 16 * c);
+      for (int c = 0; c < DV; ++c) vv[kk][c] = lds_read16_f32(v_addr + stage_off + kk * RB + 256 * c);
     f32x4 sc = (acc0 + acc1) * c2;               // S[row n][key key0 + 4g + j], base 2
     if (key0 + 16 > ctx) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (key0 + 4 * g + j >= ctx) sc[j] = -INFINITY;
     }
-    const float mx = max_over_rows(max4(sc));
-    const float mnew = __builtin_elementwise_maximum(m_run, mx);
-    const float alpha = fast_exp2(m_run - mnew);
-    m_run = mnew;
-    lsum *= alpha;
+    const float lane_mx = max4(sc);
+    if (__builtin_amdgcn_ballot_w64(lane_mx > thr)) {
+      // a row's running maximum moves only once a score passes it by 2^8
+      const float mx = max_over_rows(lane_mx);
+      const bool up = mx > thr;
+      const float mnew = up ? mx : m_run;
+      const float alpha = fast_exp2(m_run - mnew);
+      m_run = mnew;
+      thr = up ? mx + 8.f : thr;
+      lsum *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
     float pr[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) pr[j] = fast_exp2(sc[j] - m_run);
     lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) o[dt] = mfma4(vv[kk][dt / 4][dt % 4], pr[kk], o[dt]);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   for (int32_t t0 = 0; t0 < ntiles; t0 += kStages) {
@@ -650,7 +677,7 @@ __global__ __launch_bounds__(64 * kGroupWaves, 3) void decode_wide_group_f32_ker
 #pragma unroll
         for (int c = 0; c < DV; ++c) {
           const f32x4 v = f32x4{o[4 * c][j], o[4 * c + 1][j], o[4 * c + 2][j], o[4 * c + 3][j]} * inv;
-          *reinterpret_cast<f32x4*>(orow + DT * (4 * g + j) + 4 * c) = v;
+          *reinterpret_cast<f32x4*>(orow + 16 * g + 4 * j + 64 * c) = v;
         }
     }
     return;
@@ -662,7 +689,8 @@ __global__ __launch_bounds__(64 * kGroupWaves, 3) void decode_wide_group_f32_ker
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        pkvd::store_coherent(a.part_acc + pidx * D + DT * (4 * g + j) + dt, any_bad ? __builtin_nanf("") : o[dt][j]);
+        pkvd::store_coherent(a.part_acc + pidx * D + 16 * g + 4 * j + 64 * (dt / 4) + dt % 4,
+                             any_bad ? __builtin_nanf("") : o[dt][j]);
     if (g == 0) {
       pkvd::store_coherent(a.part_ml + 2 * pidx, m_run);
       pkvd::store_coherent(a.part_ml + 2 * pidx + 1, any_bad ? __builtin_nanf("") : L);

@@ -389,8 +389,11 @@ __global__ __launch_bounds__(64 * kGroupWaves, 2) void decode_shared_f32_kernel(
 // three stages, direct global->LDS copies two tiles ahead, one barrier per
 // tile; K rows' 16-byte slots XOR-swizzled by row) and wave w computes slice
 // w from there, so each K/V byte crosses from L2 into the CU once instead of
-// once per slice workgroup.  Scores, softmax (maximum taken every tile) and
-// the merge are those of the group kernel above; the cache write copies token
+// once per slice workgroup.  Scores and the merge are those of the group
+// kernel above; a row's running maximum moves only once a score passes it by
+// 2^8 (so most tiles skip the rescale of O), and V is read as each lane's own
+// 16-byte slots (lane n: dims 4n.. and 64 + 4n..), which keeps the 16 lanes
+// of a read in distinct banks.  The cache write copies token
 // ctx-1's rows into the stage from the step's rows and the workgroup stores
 // them into the pool.  Partitions start at multiples of 1024 tokens (wide
 // groups take no shared prefix).
@@ -667,7 +670,7 @@ __global__ __launch_bounds__(64 * kGroupWaves, 3) void decode_wide_group_f32_ker
   L += __shfl_xor(L, 16);
   L += __shfl_xor(L, 32);
   const int64_t row0 = grow0 + 16 * wave;          // the wave's first row
-  // lane (n, g) holds dims DT (4g + j) + dt of row n in o[dt][j]
+  // lane (n, g) holds dims 16g + 4j + 64(dt/4) + dt%4 of row n in o[dt][j]
   if (direct) {
     if (n < R) {
       const float inv = any_bad ? __builtin_nanf("") : 1.f / L;

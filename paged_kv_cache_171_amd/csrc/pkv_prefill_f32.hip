@@ -27,12 +27,14 @@
 //     S^T = K Q^T   k = 4m + t  <->  dim 16m + 4g + t  (lane (n, g) loads
 //                   K[key n] and Q[row n] at dims 16m + 4g .. +3)
 //     O^T += V^T P^T  k = kk  <->  key 4g + kk, and output row i of tile dt
-//                   <->  dim DT i + dt (lane n loads dims DT n .. DT n + DT-1
-//                   of the four V rows 4g .. 4g+3)
+//                   <->  dim 4i + 64(dt/4) + dt%4 (lane n loads its 16-byte
+//                   slots n and 16 + n of the four V rows 4g .. 4g+3, so the
+//                   16 lanes of a read fall in distinct banks)
 // so the S^T result, lane (n, g) holding S[row n][key 4g + j], is already the
 // P^T operand, and every per-row quantity lives in the lanes whose n is the
-// row.  The softmax is the online one in base 2 with the maximum taken every
-// tile: P is exact fp32, so there is nothing to gain from raising it lazily.
+// row.  The softmax is the online one in base 2; a row's running maximum
+// moves only once a score passes it by 2^8 (P stays below 256 and exact
+// fp32), so most tiles skip the rescale of O.
 #include "pkv_device.h"
 
 namespace {
@@ -65,6 +67,9 @@ __device__ __forceinline__ void copy16_to_lds_va(const void* p, const void* lds)
 }
 __device__ __forceinline__ f32x4 lds_read16(uint32_t addr) {
   return *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(static_cast<uintptr_t>(addr));
+}
+__device__ __forceinline__ void copy16_to_lds_at(const char* base, uint32_t voff, const void* lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(base), "{m0}"(lds_addr(lds)) : "memory");
 }
 template <int N> __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
 
@@ -168,6 +173,19 @@ __global__ __launch_bounds__(64 * kF32Waves, 3) void prefill_chunk_f32_kernel(pk
     if (static_cast<uint32_t>(ida) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; ida = 0; }
     if (static_cast<uint32_t>(idb) >= static_cast<uint32_t>(a.num_blocks)) { bad = true; idb = 0; }
     const int32_t key0 = 16 * tt;
+    if (key0 + 16 <= ctx) {
+      // a whole tile: each copy reads rows of one block (with 8-token blocks,
+      // both rows in one half of the tile) at a per-lane offset
+#pragma unroll
+      for (int c = 0; c < kCopies; ++c) {
+        const int kib = kF32Waves * c + wave;
+        const int t = kib / kTileKiB;
+        const bool hi = BS == 8 && (kib % kTileKiB) * 1024 / RB >= 8;
+        const char* base = (t == 0 ? kc : vc) + static_cast<int64_t>(hi ? idb : ida) * block_bytes + (key0 % BS) * RB;
+        copy16_to_lds_at(base, cp_off[c], stage + kib * 1024);
+      }
+      return;
+    }
 #pragma unroll
     for (int c = 0; c < kCopies; ++c) {
       const int kib = kF32Waves * c + wave;
@@ -200,10 +218,11 @@ __global__ __launch_bounds__(64 * kF32Waves, 3) void prefill_chunk_f32_kernel(pk
   f32x4 o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegBig, lsum = 0.f;
+  float m_run = kNegBig, thr = kNegBig, lsum = 0.f;
+  const float rescale_raw = 8.f / c2;          // 2^8 of growth, in raw score units
 
   // LDS read addresses of stage 0 (the other stages at fixed offsets): K row n,
-  // logical slot 4m + g at its swizzled place; V rows 4g + kk, dims DT n ..
+  // logical slot 4m + g at its swizzled place; V rows 4g + kk, slot n ..
   const uint32_t ring0 = lds_addr(ring[0]);
   uint32_t k_addr[KQ];
 #pragma unroll
@@ -211,7 +230,7 @@ __global__ __launch_bounds__(64 * kF32Waves, 3) void prefill_chunk_f32_kernel(pk
     k_addr[m] = ring0 + n * RB + 16 * ((4 * m + g) ^ (n % kSlots));
     asm volatile("" : "+v"(k_addr[m]));
   }
-  uint32_t v_addr = ring0 + kTileBytes + 4 * g * RB + DT * n * 4;
+  uint32_t v_addr = ring0 + kTileBytes + 4 * g * RB + 16 * n;
   asm volatile("" : "+v"(v_addr));
 
   auto compute_tile = [&](int32_t tt, uint32_t stage_off) {
@@ -219,40 +238,51 @@ __global__ __launch_bounds__(64 * kF32Waves, 3) void prefill_chunk_f32_kernel(pk
     f32x4 kv[KQ];
 #pragma unroll
     for (int m = 0; m < KQ; ++m) kv[m] = lds_read16(k_addr[m] + stage_off);
-    f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+    f32x4 acc[4];
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) acc[t4] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < KQ; ++m)
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
-        if (m & 1) acc1 = mfma4(kv[m][t4], qv[m][t4], acc1);
-        else acc0 = mfma4(kv[m][t4], qv[m][t4], acc0);
-      }
+      for (int t4 = 0; t4 < 4; ++t4) acc[t4] = mfma4(kv[m][t4], qv[m][t4], acc[t4]);
+    __builtin_amdgcn_s_setprio(0);
+    const f32x4 acc0 = acc[0] + acc[2], acc1 = acc[1] + acc[3];
     f32x4 vv[4][DV];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int c = 0; c < DV; ++c) vv[kk][c] = lds_read16(v_addr + stage_off + kk * RB + 16 * c);
+      for (int c = 0; c < DV; ++c) vv[kk][c] = lds_read16(v_addr + stage_off + kk * RB + 256 * c);
     f32x4 sc = acc0 + acc1;
     if (key0 + 16 > nomask_lim) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (key0 + 4 * g + j >= lim) sc[j] = -INFINITY;
     }
-    const float mx = max_over_rows(max4(sc));
-    const float mnew = __builtin_elementwise_maximum(m_run, mx * c2);
-    const float alpha = fast_exp2(m_run - mnew);
-    m_run = mnew;
-    lsum *= alpha;
+    const float lane_mx = max4(sc);
+    if (__builtin_amdgcn_ballot_w64(lane_mx > thr)) {
+      // a row's running maximum moves only once a score passes it by 2^8
+      const float mx = max_over_rows(lane_mx);
+      const bool up = mx > thr;
+      const float mnew = up ? mx * c2 : m_run;
+      const float alpha = fast_exp2(m_run - mnew);
+      m_run = mnew;
+      thr = up ? mx + rescale_raw : thr;
+      lsum *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+    }
     float p[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) p[j] = fast_exp2(fmaf(sc[j], c2, -m_run));
     lsum += (p[0] + p[1]) + (p[2] + p[3]);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) o[dt] = mfma4(vv[kk][dt / 4][dt % 4], p[kk], o[dt]);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // prologue: the first kStages-1 tiles' copies; the ids of the next one
@@ -297,13 +327,13 @@ __global__ __launch_bounds__(64 * kF32Waves, 3) void prefill_chunk_f32_kernel(pk
   if (!valid) return;
   const float inv = any_bad ? __builtin_nanf("") : 1.f / L;
   float* orow = a.out + ((static_cast<int64_t>(q0) + i) * Hq + kvh * G + r % G) * D;
-  // lane (n, g) holds dims DT (4g + j) + dt of row n in o[dt][j]
+  // lane (n, g) holds dims 16g + 4j + 64(dt/4) + dt%4 of row n in o[dt][j]
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int c = 0; c < DV; ++c) {
       const f32x4 v = f32x4{o[4 * c][j], o[4 * c + 1][j], o[4 * c + 2][j], o[4 * c + 3][j]} * inv;
-      *reinterpret_cast<f32x4*>(orow + DT * (4 * g + j) + 4 * c) = v;
+      *reinterpret_cast<f32x4*>(orow + 16 * g + 4 * j + 64 * c) = v;
     }
 }
 

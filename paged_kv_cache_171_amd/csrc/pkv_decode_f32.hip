@@ -441,17 +441,25 @@ __global__ __launch_bounds__(64 * kGroupWaves, 3) void decode_wide_group_f32_ker
   const bool active = wave < nsl;
   const int32_t R = active ? min(16, G - 16 * wave) : 0;
   const uint32_t bid = blockIdx.x;
-  const int32_t u = static_cast<int32_t>(bid / static_cast<uint32_t>(Hkv));
-  const int32_t kvh = static_cast<int32_t>(bid - static_cast<uint32_t>(u) * Hkv);
   const int32_t* plan = a.plan;
   if (!plan_matches(plan, a)) {
     // a plan built for other sizes: every row is NaN
-    if (u < a.num_seqs)
+    const int32_t u0 = static_cast<int32_t>(bid / static_cast<uint32_t>(Hkv));
+    const int32_t kvh0 = static_cast<int32_t>(bid - static_cast<uint32_t>(u0) * Hkv);
+    if (u0 < a.num_seqs)
       for (int idx = threadIdx.x; idx < G * D; idx += kThreads)
-        a.out[(static_cast<int64_t>(u) * Hq + kvh * G) * D + idx] = __builtin_nanf("");
+        a.out[(static_cast<int64_t>(u0) * Hq + kvh0 * G) * D + idx] = __builtin_nanf("");
     return;
   }
-  if (u >= plan[0]) return;
+  // rounds of 256 workgroups (one per CU) in alternating order, so that the
+  // longest units (listed first) share a CU with the shortest of the next round
+  const uint32_t live = static_cast<uint32_t>(plan[0]) * static_cast<uint32_t>(Hkv);
+  if (bid >= live) return;
+  const uint32_t rnd = bid / 256u, rk = bid % 256u;
+  const uint32_t nr = min(256u, live - rnd * 256u);
+  const uint32_t b2 = (rnd & 1u) ? rnd * 256u + (nr - 1u - rk) : bid;
+  const int32_t u = static_cast<int32_t>(b2 / static_cast<uint32_t>(Hkv));
+  const int32_t kvh = static_cast<int32_t>(b2 - static_cast<uint32_t>(u) * Hkv);
   const int32_t* units = pkvd::plan_units(plan);
   const int32_t s = units[2 * u];
   const int32_t p = units[2 * u + 1];

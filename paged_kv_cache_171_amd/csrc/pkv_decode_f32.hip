@@ -13,9 +13,11 @@
 //
 // The G query heads of a KV group are the rows of one 16-row MFMA tile, so
 // every K/V row is read once for all of them (the vector-ALU kernel reads it
-// once per query head); a group of more than 16 heads is cut into slices of
-// 16 rows, one workgroup each.  Work units are the plan's (sequence, 4096-token
-// partition) pairs, one workgroup per (unit, KV head, slice); its four waves take the
+// once per query head); a group of more than 64 heads is cut into slices of
+// 16 rows, one workgroup each (17..64 heads: the wide kernel below, one
+// workgroup for all slices).  Work units are the plan's (sequence, partition)
+// pairs (4096, 2048 or 1024 tokens by batch), one workgroup per (unit, KV
+// head, slice); its four waves take the
 // unit's 16-key tiles in turn (a tile: two 8-token blocks, one 16-token block
 // or half a 32-token block) and keep an online softmax per row; the waves are
 // merged through LDS, and the unit writes the output rows or the partials
@@ -30,14 +32,16 @@
 //
 // Matrix-core layout of v_mfma_f32_16x16x4_f32: lane l, n = l % 16,
 // g = l / 16, supplies A[n][g] and B[g][n] and receives D[4g + j][n] in
-// register j.  As in the float32 prefill kernel:
+// register j.  The group kernel loads its operands from memory as:
 //     S^T = K Q^T   k = 4m + t  <->  dim 16m + 4g + t  (lane (n, g) loads
 //                   K[key n] and q[row n] at dims 16m + 4g .. +3)
 //     O^T += V^T P^T  k = kk  <->  key 4g + kk, output row i of tile dt
 //                   <->  dim DT i + dt (lane n loads dims DT n .. DT n + DT-1
 //                   of the four V rows 4g .. 4g+3)
 // so the S^T result is the P^T operand and every per-row quantity lives in
-// the lanes whose n is the row.
+// the lanes whose n is the row.  The wide kernel reads V from LDS as each
+// lane's own 16-byte slots instead (output row i of tile dt <-> dim
+// 4i + 64(dt/4) + dt%4), like the float32 prefill kernel.
 #include "pkv_device.h"
 
 namespace {

@@ -329,6 +329,37 @@ def test_wide_groups_edges_and_bad_rows(dtype):
         assert np.array_equal(out2[i], out[i]), i
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_wide_groups_many_units_all_rows(dtype):
+    """160 sequences of 200..2600 tokens, 64 query heads over 2 KV heads, d 64:
+    about 300 units per KV head (1024-token partitions for float32, 2048 for
+    bf16); for float32 that is two full rounds of one workgroup per CU and a
+    partial third (the kernel deals every other round of 256 workgroups in
+    reverse order).  Every output row against the oracle; the planned call
+    gives the same bits."""
+    print(f"case: wide groups many units 64/2 d=64 {dtype}", flush=True)
+    w = W.random_small(97, 160, 2600, 64, 2, 64, dtype, min_ctx=200)
+    g, r = GpuReplay(w), _oracle(w)
+    out, tables, lens = g.decode()
+    td, ld = torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda()
+    mcl = int(lens.max())
+    plan = PK.plan_for(ld, 64, 2, tables.shape[1], mcl, PK.PKV_BF16 if dtype == "bf16" else PK.PKV_F32)
+    part = int(plan[16:20].view(torch.int32).item())
+    assert part == (1024 if dtype == "f32" else 2048)        # three (two) workgroups per CU fill a round
+    units = sum(-(-int(c) // part) for c in lens)
+    if dtype == "f32":
+        assert units * 2 > 2 * 256 and units * 2 % 256 != 0  # two full rounds and a partial one
+    ref = O.decode_attention(w.q, r.k_pool, r.v_pool, [r.alloc.block_table(s) for s in w.decode_seqs],
+                             [r.alloc.num_tokens(s) for s in w.decode_seqs], w.scale)
+    err = float(np.abs(out - ref).max())
+    assert err <= TOL[dtype], err
+    out2 = torch.full((len(w.decode_seqs), 64, 64), -5.0, dtype=torch.float32, device="cuda")
+    PK.pkv_attention_decode(out2, rows_to_device(w.q, "cuda"), g.k_pool, g.v_pool, td, ld, mcl, float(w.scale),
+                            plan=plan)
+    torch.cuda.synchronize()
+    assert np.array_equal(out2.cpu().numpy(), out)
+
+
 def test_append_skips_negative_and_out_of_pool_slots():
     w = W.random_small(25, 2, 20, 2, 2, 64, "bf16")
     print("case: append skips", flush=True)

@@ -353,6 +353,12 @@ def secondary(args):
         mq_us = _timed(decode_mqa_all, reps, stream) / len(mpools)
         res.update({"decode_64x1_us_per_layer": round(mq_us, 2),
                     "decode_64x1_kv_gbps": round(kv_logical / Hkv / mq_us / 1e3, 1)})
+        # the same tables over the one-head pools read with nothing computed
+        # (4 KiB K and V tiles, one per block: the ceiling of this access pattern)
+        tr1 = tile_read_ceiling(mpools, tables_h, lens_h, 1, stream, reps)
+        res.update({"decode_64x1_tile_read_us_per_layer": tr1["us_per_layer"],
+                    "decode_64x1_tile_read_gbps": tr1["gbps"],
+                    "decode_64x1_frac_of_tile_read": round(tr1["us_per_layer"] / mq_us, 4)})
         # the same over float32 pools of the one head: the float32 wide group kernel
         mpools32 = [(torch.randn(NB, 1, P, D, generator=gen, device=dev),
                      torch.randn(NB, 1, P, D, generator=gen, device=dev)) for _ in range(2)]

@@ -668,8 +668,10 @@ __global__ __launch_bounds__(64 * kGroupWaves, 3) void decode_wide_group_f32_ker
     }
   }
 
-  // a bad block id anywhere in the unit's range, or a wrong new slot, poisons its rows
-  const bool any_bad = __syncthreads_or(bad ? 1 : 0) != 0;
+  // a bad block id anywhere in the unit's range, or a wrong new slot, poisons
+  // its rows (every wave checks the same ids and slot: the flag is the same on
+  // every thread, so no vote through LDS)
+  const bool any_bad = bad;
   if (use_new && threadIdx.x < 2 * RB / 16) {
     // the new token's K and V rows into the pool (16 bytes per thread)
     const int half = threadIdx.x / (RB / 16), piece = threadIdx.x % (RB / 16);

@@ -497,6 +497,27 @@ def secondary(args):
                     "prefill_issued_mfma_tflops": round(1.5 * flops / pf_us / 1e6, 1),
                     "prefill_tokens_per_s_per_layer": round(int(nq.sum()) / pf_us * 1e6, 1),
                     "prefill_kernel": "prefill_chunk_mfma_kernel"})
+        # the step's mix as one pass: each layer's prefill on a second stream,
+        # launched before that layer's decode on this one (the decode units
+        # take the CUs that the prefill workgroups leave as they finish)
+        side = torch.cuda.Stream()
+
+        def mixed_all():
+            start = torch.cuda.Event()
+            start.record(stream)
+            side.wait_event(start)
+            for kp, vp in pools:
+                PK.pkv_attention_prefill_chunk(cout, cq, qsl, int(nq.max()), kp, vp, ctd, cld, int(clens.max()),
+                                               scale, stream=side)
+                PK.pkv_attention_decode(out, q, kp, vp, td, ld, mcl, scale, workspace=ws, plan=plan, stream=stream)
+            done = torch.cuda.Event()
+            done.record(side)
+            stream.wait_event(done)
+        mixed_all()
+        torch.cuda.synchronize()
+        mix_us = _timed(mixed_all, reps, stream) / L
+        res.update({"mixed_step_us_per_layer": round(mix_us, 2),
+                    "mixed_step_over_sequential": round((dec_us + pf_us) / mix_us, 3)})
         # the same chunks over float32 pools (2 layers of the same tables): the
         # fp32 matrix-core kernel, against the fp32 MFMA peak
         fpools = [(torch.randn(NB, Hkv, P, D, generator=gen, device=dev),

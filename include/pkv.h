@@ -170,7 +170,9 @@ pkv_status pkv_swap_blocks(void* dst_k_cache, void* dst_v_cache, int32_t dst_num
  * merging unit sets it back to 0, so a launch captured in a HIP graph can be
  * replayed); the contents are meaningless between calls.
  * Calls that share one workspace must not overlap in time (e.g. run them on
- * one stream).
+ * one stream).  Calls with workspaces of their own may run at once, on
+ * several streams or from several host threads: the library keeps no other
+ * state between calls (the merge tag is drawn from an atomic counter).
  * ------------------------------------------------------------------------ */
 size_t pkv_attention_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                      int32_t max_context_len);
